@@ -1,0 +1,12 @@
+"""Deterministic Split-K LoRA shrink / expand for AMD MI355X (gfx950).
+
+The computation lives in liblora_det.so (hand-written HIP kernels behind the C
+interface of include/lora_det.h); this package is its thin Python binding, with
+one function per C entry point under the same name.  See the header for the
+operand layouts, the determinism contract and the error codes.
+"""
+from ._binding import (  # noqa: F401
+    EXPORTED, LIBRARY_PATH, LoraError, lib, lora_abi_version, lora_expand, lora_sgmv_expand,
+    lora_sgmv_plan, lora_sgmv_plan_bytes, lora_sgmv_shrink, lora_sgmv_workspace_bytes, lora_shrink_plan,
+    lora_shrink_splitk, lora_shrink_splitk_atomic, lora_shrink_workspace_bytes, lora_status_str,
+)

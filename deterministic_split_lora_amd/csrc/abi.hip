@@ -1,0 +1,370 @@
+// C entry points of liblora_det.so (declared in include/lora_det.h).
+//
+// Each entry point checks every scalar and pointer on the host first and
+// returns a status before touching HIP when anything is off; only then does it
+// fill a parameter block and enqueue kernels on the caller's stream.  Nothing
+// here allocates, frees or synchronises.
+#include "../../include/lora_det.h"
+#include "kernels.h"
+
+using namespace lora;
+
+namespace {
+
+constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+
+bool aligned16(const void* p)
+{
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+bool split_ok(int32_t s)
+{
+    return s == 1 || s == 2 || s == 4 || s == 8 || s == 16;
+}
+
+// The static plan: a function of (K, split_k, r) only.
+//   k_chunk = K / S;  n = k_chunk / 32 matrix-core steps per split;
+//   waves   = the largest power of two <= 8 that divides n;
+//   k_steps = n / waves.
+int make_plan(int64_t K, int32_t r, int32_t split_k, lora_shrink_plan_t* pl)
+{
+    if (!split_ok(split_k))
+        return LORA_ERR_UNSUPPORTED;
+    if (r < 1 || r > 64)
+        return LORA_ERR_UNSUPPORTED;
+    if (K <= 0 || K > kMaxDim)
+        return LORA_ERR_SHAPE;
+    if (K % (32 * (int64_t)split_k) != 0)
+        return LORA_ERR_UNSUPPORTED;
+    const int64_t kc = K / split_k;
+    const int64_t n = kc / 32;
+    int w = 8;
+    while (n % w != 0)
+        w >>= 1;
+    pl->split_k = split_k;
+    pl->k_chunk = (int32_t)kc;
+    pl->waves = w;
+    pl->k_steps = (int32_t)(n / w);
+    pl->rank_tiles = (r + 15) / 16;
+    pl->row_block = kRowBlock;
+    return LORA_OK;
+}
+
+int launch_status(hipError_t e)
+{
+    return e == hipSuccess ? LORA_OK : LORA_ERR_LAUNCH;
+}
+
+// Checks shared by the single-adapter shrinks.
+int check_shrink(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a, const float* h,
+                 int64_t ld_h, int64_t M, int64_t K, int32_t r, int32_t split_k, lora_shrink_plan_t* pl)
+{
+    if (M < 0 || M > kMaxDim)
+        return LORA_ERR_SHAPE;
+    int st = make_plan(K, r, split_k, pl);
+    if (st != LORA_OK)
+        return st;
+    if (M == 0)
+        return LORA_OK;
+    if (!x || !A || !h)
+        return LORA_ERR_NULL;
+    if (ld_x < K || ld_a < K || ld_h < r)
+        return LORA_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(A) || (reinterpret_cast<uintptr_t>(h) & 3u) || ld_x % 8 || ld_a % 8)
+        return LORA_ERR_ALIGN;
+    return LORA_OK;
+}
+
+ShrinkParams shrink_params(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a, int64_t M,
+                           int32_t r, const lora_shrink_plan_t& pl, float scale)
+{
+    ShrinkParams p{};
+    p.x = x;
+    p.ld_x = ld_x;
+    p.A = A;
+    p.ld_a = ld_a;
+    p.M = M;
+    p.r = r;
+    p.r_max = r;
+    p.k_chunk = pl.k_chunk;
+    p.k_steps = pl.k_steps;
+    p.split_k = pl.split_k;
+    p.scale = scale;
+    return p;
+}
+
+size_t workspace_bytes(int64_t M, int32_t cols, int32_t split_k)
+{
+    if (M < 0 || M > kMaxDim || cols < 1 || cols > 64 || !split_ok(split_k))
+        return 0;
+    return (size_t)split_k * (size_t)M * (size_t)cols * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int lora_abi_version(void)
+{
+    return LORA_DET_ABI_VERSION;
+}
+
+const char* lora_status_str(int status)
+{
+    switch (status) {
+    case LORA_OK: return "ok";
+    case LORA_ERR_NULL: return "null pointer";
+    case LORA_ERR_SHAPE: return "bad shape or leading dimension";
+    case LORA_ERR_UNSUPPORTED: return "unsupported rank, split count or K";
+    case LORA_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
+    case LORA_ERR_WORKSPACE: return "workspace or plan buffer too small";
+    case LORA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+int lora_shrink_plan(int64_t K, int32_t r, int32_t split_k, lora_shrink_plan_t* plan)
+{
+    if (!plan)
+        return LORA_ERR_NULL;
+    lora_shrink_plan_t pl;
+    const int st = make_plan(K, r, split_k, &pl);
+    if (st == LORA_OK)
+        *plan = pl;
+    return st;
+}
+
+size_t lora_shrink_workspace_bytes(int64_t M, int32_t r, int32_t split_k)
+{
+    if (split_k == 1)
+        return 0;
+    return workspace_bytes(M, r, split_k);
+}
+
+int lora_shrink_splitk(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a, float* h,
+                       int64_t ld_h, int64_t M, int64_t K, int32_t r, int32_t split_k, float scale,
+                       void* workspace, size_t ws_bytes, void* stream)
+{
+    lora_shrink_plan_t pl;
+    int st = check_shrink(x, ld_x, A, ld_a, h, ld_h, M, K, r, split_k, &pl);
+    if (st != LORA_OK || M == 0)
+        return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    ShrinkParams p = shrink_params(x, ld_x, A, ld_a, M, r, pl, scale);
+    if (split_k == 1) {
+        p.out = h;
+        p.ld_out = ld_h;
+        return launch_status(launch_shrink_partial_direct(p, pl.waves, pl.rank_tiles, s));
+    }
+    const size_t need = lora_shrink_workspace_bytes(M, r, split_k);
+    if (!workspace)
+        return LORA_ERR_NULL;
+    if (!aligned16(workspace))
+        return LORA_ERR_ALIGN;
+    if (ws_bytes < need)
+        return LORA_ERR_WORKSPACE;
+    p.out = static_cast<float*>(workspace);
+    p.ld_out = r;
+    p.split_stride = M * r;
+    st = launch_status(launch_shrink_partial_ws(p, pl.waves, pl.rank_tiles, s));
+    if (st != LORA_OK)
+        return st;
+    TreeParams t{};
+    t.ws = static_cast<const float*>(workspace);
+    t.split_stride = M * r;
+    t.ldw = r;
+    t.h = h;
+    t.ld_h = ld_h;
+    t.M = M;
+    t.ncols = r;
+    t.scale = scale;
+    return launch_status(launch_splitk_tree(t, split_k, false, s));
+}
+
+int lora_shrink_splitk_atomic(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a, float* h,
+                              int64_t ld_h, int64_t M, int64_t K, int32_t r, int32_t split_k, float scale,
+                              void* stream)
+{
+    lora_shrink_plan_t pl;
+    int st = check_shrink(x, ld_x, A, ld_a, h, ld_h, M, K, r, split_k, &pl);
+    if (st != LORA_OK || M == 0)
+        return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = launch_status(launch_fill_zero(h, ld_h, M, r, s));
+    if (st != LORA_OK)
+        return st;
+    ShrinkParams p = shrink_params(x, ld_x, A, ld_a, M, r, pl, scale);
+    p.out = h;
+    p.ld_out = ld_h;
+    return launch_status(launch_shrink_partial_atomic(p, pl.waves, pl.rank_tiles, s));
+}
+
+int lora_expand(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b, uint16_t* y, int64_t ld_y,
+                int64_t M, int32_t r, int64_t N, float scale, void* stream)
+{
+    if (M < 0 || M > kMaxDim || N < 0 || N > kMaxDim)
+        return LORA_ERR_SHAPE;
+    if (r < 1 || r > 64)
+        return LORA_ERR_UNSUPPORTED;
+    if (N % 8 != 0)
+        return LORA_ERR_UNSUPPORTED;
+    if ((M + kRowBlock - 1) / kRowBlock > 0x7FFFFFFF || (N + kExpandCols - 1) / kExpandCols > 65535)
+        return LORA_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return LORA_OK;
+    if (!h || !B || !y)
+        return LORA_ERR_NULL;
+    if (ld_h < r || ld_b < r || ld_y < N)
+        return LORA_ERR_SHAPE;
+    if (!aligned16(h) || !aligned16(B) || !aligned16(y) || ld_h % 4 || ld_b % 8 || ld_y % 8)
+        return LORA_ERR_ALIGN;
+    ExpandParams p{};
+    p.h = h;
+    p.ld_h = ld_h;
+    p.B = B;
+    p.ld_b = ld_b;
+    p.y = y;
+    p.ld_y = ld_y;
+    p.M = M;
+    p.N = N;
+    p.r = r;
+    p.r_max = r;
+    p.scale = scale;
+    return launch_status(launch_expand(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t lora_sgmv_plan_bytes(int64_t M)
+{
+    if (M < 0 || M > kMaxDim)
+        return 0;
+    return (size_t)kPlanHeaderInts * 4 + (size_t)12 * (size_t)M;
+}
+
+int lora_sgmv_plan(const int32_t* token_adapter, int64_t M, int32_t n_adapters, void* plan,
+                   size_t plan_bytes, void* stream)
+{
+    if (M < 0 || M > kMaxDim)
+        return LORA_ERR_SHAPE;
+    if (n_adapters < 1)
+        return LORA_ERR_SHAPE;
+    if (!plan)
+        return LORA_ERR_NULL;
+    if (!aligned16(plan))
+        return LORA_ERR_ALIGN;
+    if (plan_bytes < lora_sgmv_plan_bytes(M))
+        return LORA_ERR_WORKSPACE;
+    if (M > 0 && !token_adapter)
+        return LORA_ERR_NULL;
+    return launch_status(launch_sgmv_plan(token_adapter, M, n_adapters, static_cast<int32_t*>(plan),
+                                          static_cast<hipStream_t>(stream)));
+}
+
+size_t lora_sgmv_workspace_bytes(int64_t M, int32_t r_max, int32_t split_k)
+{
+    return workspace_bytes(M, r_max, split_k);
+}
+
+int lora_sgmv_shrink(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_ptrs, int64_t ld_a,
+                     const int32_t* ranks, const float* scales, const int32_t* token_adapter, int32_t n_adapters,
+                     const void* plan, size_t plan_bytes, float* h, int64_t ld_h, int64_t M, int64_t K,
+                     int32_t r_max, int32_t split_k, void* workspace, size_t ws_bytes, void* stream)
+{
+    if (M < 0 || M > kMaxDim || n_adapters < 1)
+        return LORA_ERR_SHAPE;
+    lora_shrink_plan_t pl;
+    int st = make_plan(K, r_max, split_k, &pl);
+    if (st != LORA_OK)
+        return st;
+    if (M == 0)
+        return LORA_OK;
+    if (!x || !A_ptrs || !ranks || !token_adapter || !plan || !h || !workspace)
+        return LORA_ERR_NULL;
+    if (ld_x < K || ld_a < K || ld_h < r_max)
+        return LORA_ERR_SHAPE;
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(h) & 3u) || !aligned16(plan) || !aligned16(workspace) ||
+        ld_x % 8 || ld_a % 8)
+        return LORA_ERR_ALIGN;
+    if (plan_bytes < lora_sgmv_plan_bytes(M) || ws_bytes < workspace_bytes(M, r_max, split_k))
+        return LORA_ERR_WORKSPACE;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    ShrinkParams p{};
+    p.x = x;
+    p.ld_x = ld_x;
+    p.ld_a = ld_a;
+    p.A_ptrs = A_ptrs;
+    p.ranks = ranks;
+    p.tiles = static_cast<const int32_t*>(plan);
+    p.out = static_cast<float*>(workspace);
+    p.ld_out = r_max;
+    p.split_stride = M * r_max;
+    p.M = M;
+    p.r = r_max;
+    p.r_max = r_max;
+    p.k_chunk = pl.k_chunk;
+    p.k_steps = pl.k_steps;
+    p.split_k = split_k;
+    p.n_adapters = n_adapters;
+    p.scale = 1.0f;
+    // Tiles never exceed M; the grid is a fixed bound, idle workgroups exit.
+    const int64_t items_bound = M * split_k;
+    const int grid = (int)(items_bound < 2048 ? items_bound : 2048);
+    st = launch_status(launch_sgmv_shrink_partial(p, pl.waves, grid, s));
+    if (st != LORA_OK)
+        return st;
+    TreeParams t{};
+    t.ws = static_cast<const float*>(workspace);
+    t.split_stride = M * r_max;
+    t.ldw = r_max;
+    t.h = h;
+    t.ld_h = ld_h;
+    t.M = M;
+    t.ncols = r_max;
+    t.scale = 1.0f;
+    t.ids = token_adapter;
+    t.ranks = ranks;
+    t.scales = scales;
+    t.n_adapters = n_adapters;
+    return launch_status(launch_splitk_tree(t, split_k, true, s));
+}
+
+int lora_sgmv_expand(const float* h, int64_t ld_h, const uint16_t* const* B_ptrs, const int32_t* ranks,
+                     const float* scales, int32_t n_adapters, const void* plan, size_t plan_bytes, uint16_t* y,
+                     int64_t ld_y, int64_t M, int64_t N, int32_t r_max, void* stream)
+{
+    if (M < 0 || M > kMaxDim || N < 0 || N > kMaxDim || n_adapters < 1)
+        return LORA_ERR_SHAPE;
+    if (r_max < 1 || r_max > 64 || N % 8 != 0)
+        return LORA_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0)
+        return LORA_OK;
+    if (!h || !B_ptrs || !ranks || !plan || !y)
+        return LORA_ERR_NULL;
+    if (ld_h < r_max || ld_y < N)
+        return LORA_ERR_SHAPE;
+    if (!aligned16(h) || !aligned16(y) || !aligned16(plan) || ld_h % 4 || ld_y % 8)
+        return LORA_ERR_ALIGN;
+    if (plan_bytes < lora_sgmv_plan_bytes(M))
+        return LORA_ERR_WORKSPACE;
+    ExpandParams p{};
+    p.h = h;
+    p.ld_h = ld_h;
+    p.B_ptrs = B_ptrs;
+    p.ranks = ranks;
+    p.scales = scales;
+    p.tiles = static_cast<const int32_t*>(plan);
+    p.y = y;
+    p.ld_y = ld_y;
+    p.M = M;
+    p.N = N;
+    p.r = r_max;
+    p.r_max = r_max;
+    p.n_adapters = n_adapters;
+    p.scale = 1.0f;
+    const int64_t nblocks = (N + kExpandCols - 1) / kExpandCols;
+    const int64_t items_bound = M * nblocks;
+    const int grid = (int)(items_bound < 8192 ? items_bound : 8192);
+    return launch_status(launch_sgmv_expand(p, grid, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Internal interface between the C entry points (abi.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace lora {
+
+constexpr int kRowBlock = 16;                // tokens per matrix-core tile
+
+// Plan buffer: int32 header [ntiles, M, n_adapters, magic], then ntiles
+// triples (first token, token count 1..16, adapter id).
+constexpr int kPlanHeaderInts = 4;
+constexpr int32_t kPlanMagic = 0x4C6F5241;   // "LoRA"
+
+struct ShrinkParams {
+    const uint16_t* x;
+    int64_t ld_x;
+    const uint16_t* A;              // single adapter: [r][ld_a]
+    int64_t ld_a;                   // row stride of A (every adapter for sgmv)
+    const uint16_t* const* A_ptrs;  // sgmv: device array of adapter pointers
+    const int32_t* ranks;           // sgmv: device ranks
+    const int32_t* tiles;           // sgmv: plan buffer
+    float* out;                     // workspace or h
+    int64_t ld_out;                 // row stride of out
+    int64_t split_stride;           // floats between workspace slices
+    int64_t M;
+    int32_t r;                      // single adapter rank
+    int32_t r_max;                  // sgmv rank bound
+    int32_t k_chunk;                // K / split_k
+    int32_t k_steps;                // matrix-core steps per wave
+    int32_t split_k;
+    int32_t n_adapters;             // sgmv
+    float scale;
+};
+
+struct TreeParams {
+    const float* ws;
+    int64_t split_stride;
+    int64_t ldw;
+    float* h;
+    int64_t ld_h;
+    int64_t M;
+    int32_t ncols;                  // r (single) or r_max (sgmv)
+    float scale;                    // single adapter
+    const int32_t* ids;             // sgmv
+    const int32_t* ranks;           // sgmv
+    const float* scales;            // sgmv (may be null: 1)
+    int32_t n_adapters;
+};
+
+struct ExpandParams {
+    const float* h;
+    int64_t ld_h;
+    const uint16_t* B;              // single adapter: [N][ld_b]
+    int64_t ld_b;
+    const uint16_t* const* B_ptrs;  // sgmv
+    const int32_t* ranks;           // sgmv
+    const float* scales;            // sgmv (may be null: 1)
+    const int32_t* tiles;           // sgmv plan
+    uint16_t* y;
+    int64_t ld_y;
+    int64_t M;
+    int64_t N;
+    int32_t r;
+    int32_t r_max;
+    int32_t n_adapters;             // sgmv
+    float scale;
+};
+
+// Number of tiles of a plan buffer, or 0 when the buffer was not built by
+// lora_sgmv_plan for these M and n_adapters (the kernels then do nothing
+// rather than follow stale entries).
+__device__ __forceinline__ int plan_tiles(const int32_t* plan, int64_t M, int32_t n_adapters)
+{
+    if (plan[3] != kPlanMagic || plan[1] != (int32_t)M || plan[2] != n_adapters)
+        return 0;
+    const int n = plan[0];
+    return n < 0 ? 0 : (n > M ? (int)M : n);
+}
+
+// A tile entry is used only if it lies inside [0, M) and names a valid adapter.
+__device__ __forceinline__ bool tile_ok(const int32_t* t, int64_t M, int32_t n_adapters)
+{
+    return t[0] >= 0 && t[1] >= 1 && t[1] <= kRowBlock && (int64_t)t[0] + t[1] <= M && t[2] >= 0 &&
+           t[2] < n_adapters;
+}
+
+hipError_t launch_shrink_partial_ws(const ShrinkParams& p, int waves, int rank_tiles, hipStream_t st);
+hipError_t launch_shrink_partial_direct(const ShrinkParams& p, int waves, int rank_tiles, hipStream_t st);
+hipError_t launch_shrink_partial_atomic(const ShrinkParams& p, int waves, int rank_tiles, hipStream_t st);
+hipError_t launch_sgmv_shrink_partial(const ShrinkParams& p, int waves, int grid, hipStream_t st);
+hipError_t launch_splitk_tree(const TreeParams& p, int split_k, bool sgmv, hipStream_t st);
+hipError_t launch_fill_zero(float* h, int64_t ld_h, int64_t M, int ncols, hipStream_t st);
+
+hipError_t launch_expand(const ExpandParams& p, hipStream_t st);
+hipError_t launch_sgmv_expand(const ExpandParams& p, int grid, hipStream_t st);
+
+hipError_t launch_sgmv_plan(const int32_t* ids, int64_t M, int32_t n_adapters, int32_t* plan,
+                            hipStream_t st);
+
+// Columns of y one expand workgroup covers (4 waves x 64).
+constexpr int kExpandCols = 256;
+
+}  // namespace lora

@@ -1,0 +1,210 @@
+/*
+ * lora_det.h - deterministic Split-K LoRA shrink / expand for AMD MI355X (gfx950).
+ *
+ * A plain C interface: host scalars and device pointers only, no HIP or
+ * framework types.  bf16 tensors are passed as `uint16_t*` (the IEEE binary32
+ * upper half), fp32 as `float*`, a HIP stream as `void*` (NULL = the default
+ * stream).
+ *
+ * The operation is the LoRA term of a linear layer, Eq. 1 of "Reproducible LoRA
+ * Inference Through Deterministic Split-K Reduction" (Balusamy & Mohan):
+ *     Y = X W^T + s (X A^T) B^T
+ * split into the shrink  h = X A^T  (section 2: a narrow GEMM, H -> r) and the
+ * expand  Y += s h B^T.  The shrink is parallelised with Split-K (section 2.1,
+ * Eq. 3) and its partials are combined in a fixed order (section 4.3) so that
+ * every output bit is reproducible.
+ *
+ * OPERAND LAYOUTS (row-major, element strides `ld_*`, innermost stride 1):
+ *   x  bf16 [M][ld_x]   tokens x hidden; columns [0, K) used
+ *   A  bf16 [r][ld_a]   the adapter's down projection stored as in Eq. 1
+ *                       (A in R^{r x H}): row j holds rank j's K weights
+ *   h  fp32 [M][ld_h]   shrink output; columns [0, r) written
+ *   B  bf16 [N][ld_b]   the up projection as in Eq. 1 (B in R^{H_out x r})
+ *   y  bf16 [M][ld_y]   updated in place; columns [0, N) touched
+ * (As a math matrix, the product x.A of "hidden x rank" shape is x times the
+ * transpose of this A; the two describe the same numbers.)
+ *
+ * OWNERSHIP.  Every tensor, workspace and plan buffer is allocated and owned by
+ * the caller.  The library never allocates, frees or synchronises; it only
+ * enqueues kernels on `stream` and returns.  Calls on one stream execute in
+ * order; a workspace or plan buffer must not be shared by calls that may run
+ * concurrently.  Outputs must not alias inputs or workspaces.
+ *
+ * ERRORS.  Every entry point returns LORA_OK (0) or a positive lora_status.
+ * All argument checks happen on the host before any HIP call; on any error
+ * nothing is enqueued.  M == 0 (or N == 0 for the expand) is a successful no-op.
+ * LORA_ERR_LAUNCH reports a launch the HIP runtime refused.  No entry point
+ * prints, aborts or throws.
+ *
+ * DETERMINISM.  For the deterministic entry points (everything except
+ * lora_shrink_splitk_atomic) each output element's bits depend only on that
+ * token's own input row, the adapter, K, r, split_k and the scale: not on M,
+ * on the row's position in the batch, on other rows, on the stream or on
+ * timing.  The Split-K plan (lora_shrink_plan) is a function of (K, split_k)
+ * alone.
+ *
+ * SUPPORTED (otherwise LORA_ERR_UNSUPPORTED / LORA_ERR_ALIGN):
+ *   1 <= r <= 64;  split_k in {1, 2, 4, 8, 16};  K % (32 * split_k) == 0;
+ *   x, A, B, y, workspace: 16-byte aligned, ld_x, ld_a, ld_b, ld_y multiples of 8;
+ *   h as written by the shrinks: 4-byte aligned, any ld_h >= r;
+ *   h as read by the expands: 16-byte aligned, ld_h a multiple of 4;
+ *   N a multiple of 8;
+ *   M, K, N < 2^31.
+ */
+#ifndef LORA_DET_H
+#define LORA_DET_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LORA_DET_ABI_VERSION 1
+
+enum lora_status {
+    LORA_OK = 0,
+    LORA_ERR_NULL = 1,        /* a required pointer is NULL */
+    LORA_ERR_SHAPE = 2,       /* negative size, or a leading dimension below the row width */
+    LORA_ERR_UNSUPPORTED = 3, /* rank, split count or K divisibility outside the supported set */
+    LORA_ERR_ALIGN = 4,       /* pointer or leading dimension breaks the 16-byte rule */
+    LORA_ERR_WORKSPACE = 5,   /* workspace or plan buffer smaller than required */
+    LORA_ERR_LAUNCH = 6       /* the HIP runtime refused a kernel launch */
+};
+
+/* Returns LORA_DET_ABI_VERSION of the built library. */
+int lora_abi_version(void);
+
+/* Static text for a status code ("ok", "null pointer", ...); never NULL. */
+const char* lora_status_str(int status);
+
+/*
+ * The static Split-K plan (host only, no HIP call).  Section 2.1 / Eq. 3 of
+ * the paper split the reduction dimension into S subsets; here they are S
+ * contiguous chunks of k_chunk = K / S (as Fig. 1 draws K0..K7).  Inside a
+ * chunk, `waves` wavefronts each own k_chunk / waves consecutive k and run
+ * `k_steps` 16x16x32 bf16 matrix-core steps over them in ascending k with an
+ * fp32 accumulator; the wave results are added along a fixed pairwise tree.
+ * The plan depends on (K, split_k) only - never on M.  rank_tiles = ceil(r/16),
+ * row_block = 16 tokens per workgroup.
+ * Returns LORA_ERR_NULL / LORA_ERR_UNSUPPORTED / LORA_ERR_SHAPE on bad input.
+ */
+typedef struct lora_shrink_plan_s {
+    int32_t split_k;
+    int32_t k_chunk;
+    int32_t waves;
+    int32_t k_steps;
+    int32_t rank_tiles;
+    int32_t row_block;
+} lora_shrink_plan_t;
+
+int lora_shrink_plan(int64_t K, int32_t r, int32_t split_k, lora_shrink_plan_t* plan);
+
+/*
+ * Bytes of fp32 workspace lora_shrink_splitk needs: split_k * M * r * 4
+ * (0 when split_k == 1: that path writes h directly).  Layout, part of the ABI:
+ * ws[s][i][j] at float offset (s * M + i) * r + j holds split s's partial sum
+ * for token i, rank j.  No initialisation needed.  Returns 0 for invalid input.
+ */
+size_t lora_shrink_workspace_bytes(int64_t M, int32_t r, int32_t split_k);
+
+/*
+ * Deterministic Split-K shrink (paper section 4.3, Eq. 3):
+ *     h[i][j] = scale * T( P_0[i][j], ..., P_{S-1}[i][j] )
+ *     P_s[i][j] = sum over k in chunk s of x[i][k] * A[j][k]   (fp32)
+ * where T is the fixed pairwise tree: (P0+P1), (P2+P3), ... then neighbours of
+ * those, level by level, in fp32 - the order the paper's earlier two-kernel
+ * deterministic design used - followed by one fp32 multiply by `scale`.
+ * Two launches: the partial kernel writes ws, a second kernel applies T.
+ * With split_k == 1 one launch writes h = scale * P_0 directly.
+ * workspace: >= lora_shrink_workspace_bytes(M, r, split_k) bytes (may be NULL
+ * when that is 0).
+ */
+int lora_shrink_splitk(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a,
+                       float* h, int64_t ld_h, int64_t M, int64_t K, int32_t r,
+                       int32_t split_k, float scale, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * Atomic Split-K shrink, kept only as the nondeterministic contrast of paper
+ * section 4.1: h is zeroed by a fill kernel (the output initialisation the
+ * paper counts in its latency), then each split adds scale * P_s into h with
+ * hardware fp32 atomic adds, in whatever order the splits finish.  The value
+ * agrees with lora_shrink_splitk to rounding; the bits may differ between runs.
+ */
+int lora_shrink_splitk_atomic(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a,
+                              float* h, int64_t ld_h, int64_t M, int64_t K, int32_t r,
+                              int32_t split_k, float scale, void* stream);
+
+/*
+ * Expand (paper Eq. 1, the s (X A^T) B^T term added into Y):
+ *     hb = bf16_rne(h[i][j])   (section 6.2: shrink outputs meet B as bf16)
+ *     acc = sum_{j<r} hb[i][j] * B[n][j]      fp32 accumulation, matrix cores
+ *     y[i][n] = bf16_rne( fma(scale, acc, y[i][n]) )
+ * One launch, y updated in place.
+ */
+int lora_expand(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b,
+                uint16_t* y, int64_t ld_y, int64_t M, int32_t r, int64_t N, float scale,
+                void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Multi-adapter (SGMV) variants.  The paper replays shrink operations with the
+ * mapping of tokens to adapters (section 5.2); here each token i carries an
+ * adapter id token_adapter[i].  Ids outside [0, n_adapters) mean "no LoRA":
+ * the h row is written as zeros and the y row is left untouched.
+ *
+ * Adapter a has rank ranks[a] (1..r_max), weights A_ptrs[a] -> bf16
+ * [ranks[a]][ld_a] and B_ptrs[a] -> bf16 [N][rb_a] with row stride
+ * rb_a = ranks[a] rounded up to a multiple of 8 (contiguous when the rank is a
+ * multiple of 8), and scale scales[a] (scales == NULL means 1).  A_ptrs, B_ptrs,
+ * ranks, scales and token_adapter are DEVICE arrays; their contents are read by
+ * the kernels, so the caller guarantees 1 <= ranks[a] <= r_max and valid,
+ * 16-byte aligned weight pointers.  Each token's bits equal those of the
+ * single-adapter call with that token's adapter.
+ * ------------------------------------------------------------------------- */
+
+/* Bytes of the plan buffer for M tokens: 16 + 12 * M. */
+size_t lora_sgmv_plan_bytes(int64_t M);
+
+/*
+ * Builds the work list from the per-token ids, on the device and without a
+ * host synchronisation: tokens are grouped into runs of equal id, each run is
+ * cut into tiles of at most 16 consecutive tokens, tiles of invalid ids are
+ * dropped.  One launch of one workgroup.  The plan buffer (16-byte aligned) is
+ * opaque; it stays valid for later sgmv calls with the same ids, M and
+ * n_adapters and may be reused by both sgmv_shrink and sgmv_expand.
+ */
+int lora_sgmv_plan(const int32_t* token_adapter, int64_t M, int32_t n_adapters,
+                   void* plan, size_t plan_bytes, void* stream);
+
+/* Workspace bytes for lora_sgmv_shrink: split_k * M * r_max * 4 (layout as
+   for the single-adapter shrink with r_max columns).  0 for invalid input. */
+size_t lora_sgmv_workspace_bytes(int64_t M, int32_t r_max, int32_t split_k);
+
+/*
+ * Multi-adapter deterministic Split-K shrink: per token, the single-adapter
+ * shrink with its adapter's A, rank and scale; h columns in [rank, r_max) and
+ * rows of tokens without an adapter are written as 0.  Two launches (partials
+ * over the plan's tiles, then the fixed tree) for every split_k, including 1.
+ */
+int lora_sgmv_shrink(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_ptrs, int64_t ld_a,
+                     const int32_t* ranks, const float* scales, const int32_t* token_adapter,
+                     int32_t n_adapters, const void* plan, size_t plan_bytes,
+                     float* h, int64_t ld_h, int64_t M, int64_t K, int32_t r_max, int32_t split_k,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Multi-adapter expand: per token with an adapter, lora_expand with that
+ * adapter's B, rank and scale; other rows of y untouched.  One launch.
+ */
+int lora_sgmv_expand(const float* h, int64_t ld_h, const uint16_t* const* B_ptrs,
+                     const int32_t* ranks, const float* scales, int32_t n_adapters,
+                     const void* plan, size_t plan_bytes, uint16_t* y, int64_t ld_y,
+                     int64_t M, int64_t N, int32_t r_max, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_DET_H */

@@ -1,0 +1,224 @@
+"""The C-ABI library on the host: it loads, exports every function the header
+declares, computes the static plan from (K, split_k) alone, and rejects bad
+arguments with the documented status before any HIP call.  No test here
+launches a kernel: every call below carries at least one defect that the host
+checks catch (or is an M == 0 no-op), so fake device addresses are never
+dereferenced."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import deterministic_split_lora_amd as dsl
+from deterministic_split_lora_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "lora_det.h")
+
+FAKE = 0x100000          # a 16-byte aligned address that is never dereferenced
+FAKE_MIS = 0x100002      # misaligned
+
+
+def header_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(lora_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_function():
+    L = dsl.lib()
+    declared = header_functions()
+    assert len(declared) >= 12
+    for name in declared:
+        assert hasattr(L, name), f"{name} declared in lora_det.h but not exported"
+    assert sorted(B.EXPORTED) == declared
+
+
+def test_abi_version_and_status_strings():
+    assert dsl.lora_abi_version() == 1
+    seen = set()
+    for s in range(0, 7):
+        t = dsl.lora_status_str(s)
+        assert t and t != "unknown status"
+        seen.add(t)
+    assert len(seen) == 7
+    assert dsl.lora_status_str(99) == "unknown status"
+
+
+@pytest.mark.parametrize("K,S,chunk,waves,steps", [
+    (1024, 8, 128, 4, 1),      # single-adapter shrink, 8 tokens x 1024, 128-wide chunks
+    (4096, 8, 512, 8, 2),      # q_proj-shaped 4096 hidden
+    (14336, 8, 1792, 8, 7),    # MLP down-projection shape
+    (8192, 16, 512, 8, 2),     # 8192 hidden, Split-K 16
+    (8192, 8, 1024, 8, 4),
+    (3072, 8, 384, 4, 3),      # the paper's decode example (hidden 3072)
+    (4096, 1, 4096, 8, 16),
+    (64, 2, 32, 1, 1),
+])
+def test_static_plan(K, S, chunk, waves, steps):
+    p = dsl.lora_shrink_plan(K, 16, S)
+    assert p == {"split_k": S, "k_chunk": chunk, "waves": waves, "k_steps": steps,
+                 "rank_tiles": 1, "row_block": 16}
+    assert waves * steps * 32 == chunk and chunk * S == K
+    for r, rt in [(1, 1), (8, 1), (16, 1), (17, 2), (32, 2), (33, 3), (64, 4)]:
+        assert dsl.lora_shrink_plan(K, r, S)["rank_tiles"] == rt
+
+
+def test_plan_rejects():
+    L = dsl.lib()
+    p = B.ShrinkPlan()
+    assert L.lora_shrink_plan(4096, 16, 3, ctypes.byref(p)) == B.LORA_ERR_UNSUPPORTED
+    assert L.lora_shrink_plan(4096, 16, 32, ctypes.byref(p)) == B.LORA_ERR_UNSUPPORTED
+    assert L.lora_shrink_plan(4096, 0, 8, ctypes.byref(p)) == B.LORA_ERR_UNSUPPORTED
+    assert L.lora_shrink_plan(4096, 65, 8, ctypes.byref(p)) == B.LORA_ERR_UNSUPPORTED
+    assert L.lora_shrink_plan(4000, 16, 8, ctypes.byref(p)) == B.LORA_ERR_UNSUPPORTED
+    assert L.lora_shrink_plan(0, 16, 8, ctypes.byref(p)) == B.LORA_ERR_SHAPE
+    assert L.lora_shrink_plan(4096, 16, 8, None) == B.LORA_ERR_NULL
+
+
+def test_workspace_and_plan_sizes():
+    assert dsl.lora_shrink_workspace_bytes(256, 16, 8) == 8 * 256 * 16 * 4
+    assert dsl.lora_shrink_workspace_bytes(256, 16, 1) == 0
+    assert dsl.lora_shrink_workspace_bytes(-1, 16, 8) == 0
+    assert dsl.lora_shrink_workspace_bytes(256, 0, 8) == 0
+    assert dsl.lora_shrink_workspace_bytes(256, 16, 3) == 0
+    assert dsl.lora_sgmv_workspace_bytes(512, 64, 8) == 8 * 512 * 64 * 4
+    assert dsl.lora_sgmv_workspace_bytes(512, 64, 1) == 512 * 64 * 4
+    assert dsl.lora_sgmv_plan_bytes(512) == 16 + 12 * 512
+    assert dsl.lora_sgmv_plan_bytes(-3) == 0
+
+
+def _shrink(**kw):
+    a = dict(x=FAKE, ld_x=4096, A=FAKE, ld_a=4096, h=FAKE, ld_h=16, M=4, K=4096, r=16, S=8, scale=1.0,
+             ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return dsl.lib().lora_shrink_splitk(a["x"], a["ld_x"], a["A"], a["ld_a"], a["h"], a["ld_h"], a["M"], a["K"],
+                                        a["r"], a["S"], a["scale"], a["ws"], a["wsb"], a["stream"])
+
+
+def _atomic(**kw):
+    a = dict(x=FAKE, ld_x=4096, A=FAKE, ld_a=4096, h=FAKE, ld_h=16, M=4, K=4096, r=16, S=8, scale=1.0)
+    a.update(kw)
+    return dsl.lib().lora_shrink_splitk_atomic(a["x"], a["ld_x"], a["A"], a["ld_a"], a["h"], a["ld_h"], a["M"],
+                                               a["K"], a["r"], a["S"], a["scale"], None)
+
+
+def _expand(**kw):
+    a = dict(h=FAKE, ld_h=16, B=FAKE, ld_b=16, y=FAKE, ld_y=4096, M=4, r=16, N=4096, scale=2.0)
+    a.update(kw)
+    return dsl.lib().lora_expand(a["h"], a["ld_h"], a["B"], a["ld_b"], a["y"], a["ld_y"], a["M"], a["r"], a["N"],
+                                 a["scale"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), B.LORA_ERR_NULL),
+    (dict(A=None), B.LORA_ERR_NULL),
+    (dict(h=None), B.LORA_ERR_NULL),
+    (dict(ws=None), B.LORA_ERR_NULL),
+    (dict(M=-1), B.LORA_ERR_SHAPE),
+    (dict(r=0), B.LORA_ERR_UNSUPPORTED),
+    (dict(r=65), B.LORA_ERR_UNSUPPORTED),
+    (dict(S=3), B.LORA_ERR_UNSUPPORTED),
+    (dict(S=32), B.LORA_ERR_UNSUPPORTED),
+    (dict(K=4000, ld_x=4000, ld_a=4000), B.LORA_ERR_UNSUPPORTED),
+    (dict(K=0), B.LORA_ERR_SHAPE),
+    (dict(ld_x=4088), B.LORA_ERR_SHAPE),
+    (dict(ld_a=4000), B.LORA_ERR_SHAPE),
+    (dict(ld_h=8), B.LORA_ERR_SHAPE),
+    (dict(x=FAKE_MIS), B.LORA_ERR_ALIGN),
+    (dict(A=FAKE_MIS), B.LORA_ERR_ALIGN),
+    (dict(h=FAKE + 2), B.LORA_ERR_ALIGN),
+    (dict(ws=FAKE + 8), B.LORA_ERR_ALIGN),
+    (dict(ld_x=4100), B.LORA_ERR_ALIGN),
+    (dict(ld_a=4100), B.LORA_ERR_ALIGN),
+    (dict(wsb=8 * 4 * 16 * 4 - 1), B.LORA_ERR_WORKSPACE),
+])
+def test_shrink_rejects(kw, status):
+    assert _shrink(**kw) == status
+
+
+def test_shrink_zero_rows_is_noop():
+    # M == 0 succeeds without touching any pointer (and without a GPU)
+    assert _shrink(M=0, x=None, A=None, h=None, ws=None) == B.LORA_OK
+    assert _atomic(M=0, x=None, A=None, h=None) == B.LORA_OK
+    assert _expand(M=0, h=None, B=None, y=None) == B.LORA_OK
+    assert _expand(N=0, h=None, B=None, y=None) == B.LORA_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), B.LORA_ERR_NULL),
+    (dict(S=5), B.LORA_ERR_UNSUPPORTED),
+    (dict(r=100), B.LORA_ERR_UNSUPPORTED),
+    (dict(ld_a=8), B.LORA_ERR_SHAPE),
+    (dict(A=FAKE_MIS), B.LORA_ERR_ALIGN),
+])
+def test_atomic_rejects(kw, status):
+    assert _atomic(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(h=None), B.LORA_ERR_NULL),
+    (dict(B=None), B.LORA_ERR_NULL),
+    (dict(y=None), B.LORA_ERR_NULL),
+    (dict(M=-2), B.LORA_ERR_SHAPE),
+    (dict(r=0), B.LORA_ERR_UNSUPPORTED),
+    (dict(r=80), B.LORA_ERR_UNSUPPORTED),
+    (dict(N=4092, ld_y=4096), B.LORA_ERR_UNSUPPORTED),
+    (dict(ld_y=4088), B.LORA_ERR_SHAPE),
+    (dict(ld_b=8), B.LORA_ERR_SHAPE),
+    (dict(ld_b=20), B.LORA_ERR_ALIGN),
+    (dict(y=FAKE_MIS), B.LORA_ERR_ALIGN),
+    (dict(h=FAKE + 8), B.LORA_ERR_ALIGN),
+    (dict(N=256 * 65536, ld_y=256 * 65536), B.LORA_ERR_SHAPE),
+])
+def test_expand_rejects(kw, status):
+    assert _expand(**kw) == status
+
+
+def test_sgmv_rejects():
+    L = dsl.lib()
+    pb = dsl.lora_sgmv_plan_bytes(64)
+    # plan
+    assert L.lora_sgmv_plan(FAKE, 64, 4, None, pb, None) == B.LORA_ERR_NULL
+    assert L.lora_sgmv_plan(None, 64, 4, FAKE, pb, None) == B.LORA_ERR_NULL
+    assert L.lora_sgmv_plan(FAKE, 64, 0, FAKE, pb, None) == B.LORA_ERR_SHAPE
+    assert L.lora_sgmv_plan(FAKE, 64, 4, FAKE, pb - 1, None) == B.LORA_ERR_WORKSPACE
+    assert L.lora_sgmv_plan(FAKE, 64, 4, FAKE + 4, pb, None) == B.LORA_ERR_ALIGN
+    assert L.lora_sgmv_plan(FAKE, -1, 4, FAKE, pb, None) == B.LORA_ERR_SHAPE
+    wsb = dsl.lora_sgmv_workspace_bytes(64, 64, 8)
+
+    def shrink(**kw):
+        a = dict(x=FAKE, ld_x=4096, Ap=FAKE, ld_a=4096, ranks=FAKE, scales=None, ids=FAKE, n=4, plan=FAKE,
+                 pb=pb, h=FAKE, ld_h=64, M=64, K=4096, r_max=64, S=8, ws=FAKE, wsb=wsb)
+        a.update(kw)
+        return L.lora_sgmv_shrink(a["x"], a["ld_x"], a["Ap"], a["ld_a"], a["ranks"], a["scales"], a["ids"], a["n"],
+                                  a["plan"], a["pb"], a["h"], a["ld_h"], a["M"], a["K"], a["r_max"], a["S"],
+                                  a["ws"], a["wsb"], None)
+    assert shrink(Ap=None) == B.LORA_ERR_NULL
+    assert shrink(ranks=None) == B.LORA_ERR_NULL
+    assert shrink(ids=None) == B.LORA_ERR_NULL
+    assert shrink(n=0) == B.LORA_ERR_SHAPE
+    assert shrink(r_max=65) == B.LORA_ERR_UNSUPPORTED
+    assert shrink(S=6) == B.LORA_ERR_UNSUPPORTED
+    assert shrink(ld_h=32) == B.LORA_ERR_SHAPE
+    assert shrink(ld_a=4092) == B.LORA_ERR_SHAPE
+    assert shrink(ld_a=4100) == B.LORA_ERR_ALIGN
+    assert shrink(wsb=wsb - 4) == B.LORA_ERR_WORKSPACE
+    assert shrink(pb=pb - 4) == B.LORA_ERR_WORKSPACE
+    assert shrink(M=0, x=None) == B.LORA_OK
+
+    def expand(**kw):
+        a = dict(h=FAKE, ld_h=64, Bp=FAKE, ranks=FAKE, scales=None, n=4, plan=FAKE, pb=pb, y=FAKE, ld_y=4096,
+                 M=64, N=4096, r_max=64)
+        a.update(kw)
+        return L.lora_sgmv_expand(a["h"], a["ld_h"], a["Bp"], a["ranks"], a["scales"], a["n"], a["plan"], a["pb"],
+                                  a["y"], a["ld_y"], a["M"], a["N"], a["r_max"], None)
+    assert expand(Bp=None) == B.LORA_ERR_NULL
+    assert expand(plan=None) == B.LORA_ERR_NULL
+    assert expand(N=4090) == B.LORA_ERR_UNSUPPORTED
+    assert expand(r_max=0) == B.LORA_ERR_UNSUPPORTED
+    assert expand(ld_y=2048) == B.LORA_ERR_SHAPE
+    assert expand(y=FAKE_MIS) == B.LORA_ERR_ALIGN
+    assert expand(pb=16) == B.LORA_ERR_WORKSPACE
+    assert expand(M=0, h=None) == B.LORA_OK

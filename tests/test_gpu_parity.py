@@ -1,0 +1,534 @@
+"""GPU path vs the CPU oracle, through the C-ABI library (MI355X / gfx950).
+
+Floating-point results are compared element by element within the tolerances
+written in tests/helpers.py; integer-valued inputs, the crafted Split-K
+partials and the fixed-order combine are compared bit for bit.  Self-
+comparisons (repeats, batch sizes, scale placement, multi-adapter vs single)
+compare raw bits, never float ==.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import deterministic_split_lora_amd as dsl
+import oracle
+from synth import integer_bf16, normal_bf16, single_adapter_case, sgmv_case, segments_to_ids
+from tests.helpers import (bf16_from_gpu, bf16_to_gpu, check_expand, check_shrink, f32_bits, f32_to_gpu,
+                           gpu_available, torch, workspace)
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def run_shrink(x, A, S, scale=1.0, atomic=False):
+    t = torch()
+    M, K = x.shape
+    r = A.shape[0]
+    xg, Ag = bf16_to_gpu(x), bf16_to_gpu(A)
+    h = t.full((M, r), float("nan"), dtype=t.float32, device="cuda")
+    if atomic:
+        dsl.lora_shrink_splitk_atomic(xg, Ag, h, split_k=S, scale=scale)
+    else:
+        ws = workspace(dsl.lora_shrink_workspace_bytes(M, r, S))
+        dsl.lora_shrink_splitk(xg, Ag, h, ws if S > 1 else None, split_k=S, scale=scale)
+    t.cuda.synchronize()
+    return h.cpu().numpy()
+
+
+# ---------------------------------------------------------------------------
+# shrink parity
+# ---------------------------------------------------------------------------
+SHRINK_CASES = [
+    # (M, K, r, S, scale, label)
+    (8, 1024, 8, 8, 1.0, "single adapter 8x1024 rank 8, 128-wide chunks"),
+    (1, 4096, 16, 8, 1.0, "q_proj M=1"),
+    (16, 4096, 16, 8, 1.0, "q_proj M=16"),
+    (64, 4096, 16, 8, 1.0, "q_proj M=64"),
+    (256, 4096, 16, 8, 2.0, "q_proj M=256 scale 2"),
+    (17, 4096, 16, 8, 1.0, "ragged M"),
+    (33, 1024, 5, 4, 1.0, "rank 5"),
+    (3, 2048, 64, 16, 1.0, "rank 64, S=16"),
+    (40, 3072, 24, 8, 0.5, "rank 24, hidden 3072"),
+    (5, 4096, 33, 2, 1.0, "rank 33, S=2"),
+    (100, 4096, 48, 1, 1.0, "S=1 direct"),
+    (1, 8192, 64, 16, 2.0, "decode rank 64 S=16"),
+    (300, 14336, 32, 8, 1.0, "down-proj shape, 7 steps per wave"),
+]
+
+
+@pytest.mark.parametrize("M,K,r,S,scale,label", SHRINK_CASES)
+def test_shrink_parity(M, K, r, S, scale, label):
+    _say(f"shrink parity: {label} M={M} K={K} r={r} S={S}")
+    c = single_adapter_case(M, K, r, 0, split_k=S, scale=scale, seed=M + K + r)
+    h = run_shrink(c.x, c.A, S, scale)
+    plan = dsl.lora_shrink_plan(K, r, S)
+    a, b = check_shrink(h, c.x, c.A, scale, plan, label)
+    _say(f"  max err / stated tol {a:.3g}, / rounding bound {b:.3g}")
+
+
+@pytest.mark.parametrize("M,K,r,S", [(8, 1024, 8, 8), (19, 4096, 16, 8), (5, 2048, 40, 16), (33, 1024, 64, 1)])
+def test_shrink_integer_inputs_bit_exact(M, K, r, S):
+    """Integer inputs with every partial sum below 2^24: any summation order is
+    exact, so deterministic, atomic and split_k == 1 all equal the oracle
+    bit for bit; a wrong index or layout cannot hide."""
+    _say(f"integer shrink M={M} K={K} r={r} S={S}")
+    x = integer_bf16((M, K), -3, 3, 1, "ix")
+    A = integer_bf16((r, K), -3, 3, 1, "iA")
+    ref = oracle.shrink(x, A, 2.0)
+    assert np.all(np.abs(ref) < 2 ** 23)
+    for atomic in (False, True):
+        h = run_shrink(x, A, S, 2.0, atomic)
+        assert np.array_equal(h.astype(np.float64), ref), f"atomic={atomic}"
+    h1 = run_shrink(x, A, 1, 2.0)
+    assert np.array_equal(h1.astype(np.float64), ref)
+
+
+def _crafted_x_A(K, S, r, values, seed):
+    """One nonzero product per split: split s gets x[0, s*K/S + off_s] = a_s and
+    A[j, same k] = b_s[j], so its fp32 partial is exactly a_s * b_s[j] (a bf16
+    x bf16 product is exact in fp32) whatever order the hardware sums in."""
+    rng = np.random.default_rng(seed)
+    Kc = K // S
+    x = np.zeros((1, K), dtype=np.uint16)
+    A = np.zeros((r, K), dtype=np.uint16)
+    for s in range(S):
+        k = s * Kc + int(rng.integers(0, Kc))
+        xa, Ab = values(s, rng)
+        x[0, k] = xa
+        A[:, k] = Ab
+    return x, A
+
+
+def test_fixed_order_combine_crafted_partials():
+    """P = (2^100, 1, -2^100, 1, 0, 0, 0, 0): the neighbour pairwise tree gives
+    0, the increasing-order fold 1, a stride-paired tree 2 (hand-derived in
+    tests/golden/crafted_partials.json).  The GPU must give exactly 0."""
+    K, S, r = 1024, 8, 8
+    two50 = 0x5880      # bf16 bits of 2^50
+    one = 0x3F80
+    vals = {0: (two50, two50), 1: (one, one), 2: (two50, 0xD880), 3: (one, one)}
+
+    def v(s, rng):
+        return vals.get(s, (0, 0))
+    x, A = _crafted_x_A(K, S, r, v, 5)
+    P = oracle.split_partials(x, A, S)
+    assert P[0, 0, 0] == 2.0 ** 100 and P[2, 0, 0] == -2.0 ** 100
+    want = oracle.combine_tree_f32(P.astype(np.float32), 1.0)
+    assert np.all(want == 0.0)
+    h = run_shrink(x, A, S, 1.0)
+    assert np.array_equal(f32_bits_np(h), f32_bits_np(want))
+    assert np.all(oracle.combine_sequential_f32(P.astype(np.float32)) == 1.0)
+
+
+def f32_bits_np(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.int32)
+
+
+@pytest.mark.parametrize("S", [2, 4, 8, 16])
+def test_fixed_order_combine_random_exponents(S):
+    """Partials with random signs and exponents spread over 2^-40..2^40: their
+    fp32 sum rounds differently for almost every order, so bit equality with
+    the oracle's fixed pairwise tree pins the combine order and the single
+    scale multiply."""
+    K, r = 32 * S * 8, 16
+
+    def v(s, rng):
+        ea = int(rng.integers(-20, 21))
+        xa = np.float32(rng.uniform(1, 2) * 2.0 ** ea * rng.choice([-1, 1]))
+        b = (rng.uniform(1, 2, r) * 2.0 ** rng.integers(-20, 21, r) * rng.choice([-1, 1], r)).astype(np.float32)
+        return (oracle.bf16_rne([xa])[0], oracle.bf16_rne(b))
+    differs_from_fold = 0
+    for seed in range(4):
+        x, A = _crafted_x_A(K, S, r, v, 100 * S + seed)
+        P = oracle.split_partials(x, A, S).astype(np.float32)   # exact
+        for scale in (1.0, 0.75):
+            want = oracle.combine_tree_f32(P, scale)
+            h = run_shrink(x, A, S, scale)
+            assert np.array_equal(f32_bits_np(h), f32_bits_np(want)), (seed, scale)
+            seq = oracle.combine_sequential_f32(P, scale)
+            differs_from_fold += int(np.sum(f32_bits_np(seq) != f32_bits_np(want)))
+    if S >= 4:
+        # the inputs do discriminate between summation orders
+        assert differs_from_fold > 0
+
+
+@pytest.mark.parametrize("M,K,r,S", [(8, 1024, 8, 8), (64, 4096, 16, 8), (7, 8192, 64, 16)])
+def test_atomic_parity(M, K, r, S):
+    _say(f"atomic shrink parity M={M} K={K} r={r} S={S}")
+    c = single_adapter_case(M, K, r, 0, split_k=S, seed=3)
+    h = run_shrink(c.x, c.A, S, 2.0, atomic=True)
+    check_shrink(h, c.x, c.A, 2.0, dsl.lora_shrink_plan(K, r, S), "atomic")
+
+
+# ---------------------------------------------------------------------------
+# expand parity
+# ---------------------------------------------------------------------------
+EXPAND_CASES = [
+    (1, 16, 4096, 2.0), (16, 16, 4096, 2.0), (64, 16, 4096, 2.0), (256, 16, 4096, 2.0),
+    (17, 1, 264, 2.0), (9, 8, 520, 1.0), (33, 24, 1000, 2.0), (5, 40, 4096, 0.5), (20, 64, 6144, 2.0),
+    (3, 37, 8, 2.0),
+]
+
+
+@pytest.mark.parametrize("M,r,N,scale", EXPAND_CASES)
+def test_expand_parity(M, r, N, scale):
+    _say(f"expand parity M={M} r={r} N={N}")
+    t = torch()
+    rng = np.random.default_rng(M * 7 + r)
+    h = (rng.standard_normal((M, r)) * 1.3).astype(np.float32)
+    B = normal_bf16((N, r), 0.02, 1, f"eB{r}")
+    y = normal_bf16((M, N), 1.0, 1, f"ey{M}")
+    # B rows padded to a multiple of 8 columns as the ABI requires
+    ldb = (r + 7) // 8 * 8
+    Bp = np.zeros((N, ldb), dtype=np.uint16)
+    Bp[:, :r] = B
+    hp = np.zeros((M, (r + 3) // 4 * 4), dtype=np.float32)
+    hp[:, :r] = h
+    yg = bf16_to_gpu(y)
+    dsl.lora_expand(f32_to_gpu(hp), bf16_to_gpu(Bp), yg, scale, r=r)
+    t.cuda.synchronize()
+    got = bf16_from_gpu(yg)
+    yo, e, ab = oracle.expand(h, B, y, scale)
+    frac = check_expand(got, yo, e, ab, y, f"M={M} r={r} N={N}")
+    _say(f"  fraction differing from the correctly rounded value: {frac:.2e}")
+
+
+def test_expand_B_zero_leaves_y_bitwise():
+    t = torch()
+    M, r, N = 40, 16, 1024
+    y = normal_bf16((M, N), 1.0, 2, "y0")
+    yg = bf16_to_gpu(y)
+    h = f32_to_gpu(np.random.default_rng(1).standard_normal((M, r)).astype(np.float32))
+    dsl.lora_expand(h, t.zeros((N, r), dtype=t.bfloat16, device="cuda"), yg, 2.0)
+    t.cuda.synchronize()
+    assert np.array_equal(bf16_from_gpu(yg), y)
+
+
+def test_expand_integer_bit_exact_and_h_rounding():
+    t = torch()
+    M, r, N = 20, 32, 512
+    rng = np.random.default_rng(9)
+    h = rng.integers(-4, 5, (M, r)).astype(np.float32)
+    B = integer_bf16((N, r), -3, 3, 9, "iB")
+    y = integer_bf16((M, N), -50, 50, 9, "iy")
+    yg = bf16_to_gpu(y)
+    dsl.lora_expand(f32_to_gpu(h), bf16_to_gpu(B), yg, 2.0)
+    t.cuda.synchronize()
+    yo, _, _ = oracle.expand(h, B, y, 2.0)
+    assert np.array_equal(bf16_from_gpu(yg), yo)
+    # the paper's midpoint value must be rounded to bf16 before meeting B
+    h2 = np.zeros((1, 8), np.float32)
+    h2[0, 0] = 0.010345458984375
+    B2 = np.zeros((8, 8), np.uint16)
+    B2[:, 0] = 0x3F80
+    y2 = np.zeros((1, 8), np.uint16)
+    yg2 = bf16_to_gpu(y2)
+    dsl.lora_expand(f32_to_gpu(h2), bf16_to_gpu(B2), yg2, 3.0)
+    t.cuda.synchronize()
+    assert np.all(oracle.bf16_to_f64(bf16_from_gpu(yg2)) == 255 * 2.0 ** -13)
+
+
+def test_scale_placement_bitwise():
+    """scale 2 in the shrink or in the expand: multiplying by a power of two
+    is exact, so both pipelines give the same bits."""
+    t = torch()
+    c = single_adapter_case(64, 4096, 16, 4096, seed=4)
+    xg, Ag, Bg = bf16_to_gpu(c.x), bf16_to_gpu(c.A), bf16_to_gpu(c.B)
+    ws = workspace(dsl.lora_shrink_workspace_bytes(64, 16, 8))
+    outs = []
+    for s_shrink, s_expand in ((1.0, 2.0), (2.0, 1.0)):
+        h = t.empty((64, 16), dtype=t.float32, device="cuda")
+        dsl.lora_shrink_splitk(xg, Ag, h, ws, 8, s_shrink)
+        yg = bf16_to_gpu(c.y)
+        dsl.lora_expand(h, Bg, yg, s_expand)
+        t.cuda.synchronize()
+        outs.append(bf16_from_gpu(yg))
+    assert np.array_equal(outs[0], outs[1])
+
+
+# ---------------------------------------------------------------------------
+# determinism: repeats and batch sizes
+# ---------------------------------------------------------------------------
+def test_repeat_1000_bitwise():
+    t = torch()
+    M, K, r, N, S = 64, 4096, 16, 4096, 8
+    c = single_adapter_case(M, K, r, N, seed=6)
+    xg, Ag, Bg = bf16_to_gpu(c.x), bf16_to_gpu(c.A), bf16_to_gpu(c.B)
+    ws = workspace(dsl.lora_shrink_workspace_bytes(M, r, S))
+    h = t.empty((M, r), dtype=t.float32, device="cuda")
+    y0 = bf16_to_gpu(c.y)
+    hs, ys = [], []
+    for rep in range(1000):
+        dsl.lora_shrink_splitk(xg, Ag, h, ws, S, 1.0)
+        yg = y0.clone()
+        dsl.lora_expand(h, Bg, yg, 2.0)
+        hs.append(h.view(t.int32).clone())
+        ys.append(yg.view(t.int16))
+    t.cuda.synchronize()
+    H = t.stack(hs)
+    Y = t.stack(ys)
+    assert bool((H == H[0]).all()) and bool((Y == Y[0]).all())
+    check_shrink(hs[0].view(t.float32).cpu().numpy(), c.x, c.A, 1.0, dsl.lora_shrink_plan(K, r, S), "repeat")
+
+
+def test_batch_invariance_sweep():
+    """16 probe rows of the MLP down-projection shape (K=14336, r=32, N=4096,
+    S=8) placed at random positions among N(0,1) filler rows in batches of
+    1, 2, 4, ..., 1024 tokens (four layouts per size, the first launched 1000
+    times): every probe row's h (fp32 bits) and y (bf16 bits) must be
+    identical across repeats, positions and batch sizes."""
+    t = torch()
+    K, r, N, S, P = 14336, 32, 4096, 8, 16
+    probe = normal_bf16((P, K), 1.0, 0, "probe_x")
+    A = normal_bf16((r, K), 0.02, 0, "probe_A")
+    B = normal_bf16((N, r), 0.02, 0, "probe_B")
+    ybase = normal_bf16((P, N), 1.0, 0, "probe_y")
+    Ag, Bg = bf16_to_gpu(A), bf16_to_gpu(B)
+    ref_h = ref_y = None
+    rng = np.random.default_rng(0)
+    for b in [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024]:
+        for layout in range(4):
+            # which probe rows go in this batch and where
+            groups = [list(range(i, i + b)) for i in range(0, P, b)] if b < P else [list(range(P))]
+            for grp in groups:
+                M = max(b, len(grp))
+                x = normal_bf16((M, K), 1.0, 1000 * b + layout, "filler")
+                y = normal_bf16((M, N), 1.0, 1000 * b + layout, "filler_y")
+                pos = rng.choice(M, size=len(grp), replace=False)
+                x[pos] = probe[grp]
+                y[pos] = ybase[grp]
+                xg, yg = bf16_to_gpu(x), bf16_to_gpu(y)
+                h = t.empty((M, r), dtype=t.float32, device="cuda")
+                ws = workspace(dsl.lora_shrink_workspace_bytes(M, r, S))
+                yw = yg.clone()
+                dsl.lora_shrink_splitk(xg, Ag, h, ws, S, 1.0)
+                dsl.lora_expand(h, Bg, yw, 2.0)
+                h0, y0 = h.view(t.int32).clone(), yw.view(t.int16).clone()
+                # the first layout of each batch size is launched 1000 times,
+                # every repeat compared on the GPU with the first
+                bad = t.zeros((), dtype=t.int64, device="cuda")
+                for _ in range(999 if layout == 0 else 0):
+                    yw = yg.clone()
+                    dsl.lora_shrink_splitk(xg, Ag, h, ws, S, 1.0)
+                    dsl.lora_expand(h, Bg, yw, 2.0)
+                    bad += (h.view(t.int32) != h0).sum() + (yw.view(t.int16) != y0).sum()
+                assert int(bad) == 0, f"batch {b}: repeats differ"
+                hb = f32_bits(h)[pos]
+                yb = bf16_from_gpu(yw)[pos]
+                if ref_h is None:
+                    ref_h = np.zeros((P, r), np.int32)
+                    ref_y = np.zeros((P, N), np.uint16)
+                    seen = np.zeros(P, bool)
+                for k, gi in enumerate(grp):
+                    if not seen[gi]:
+                        ref_h[gi], ref_y[gi], seen[gi] = hb[k], yb[k], True
+                    else:
+                        assert np.array_equal(hb[k], ref_h[gi]), f"h of probe {gi} changed at batch {b}"
+                        assert np.array_equal(yb[k], ref_y[gi]), f"y of probe {gi} changed at batch {b}"
+        _say(f"  batch {b}: probe rows identical")
+    # and the probe rows are right
+    check_shrink(ref_h.view(np.float32), probe, A, 1.0, dsl.lora_shrink_plan(K, r, S), "probe")
+    yo, e, ab = oracle.expand(ref_h.view(np.float32), B, ybase, 2.0)
+    check_expand(ref_y, yo, e, ab, ybase, "probe expand")
+
+
+def test_atomic_variant_varies_on_crafted_input():
+    """The atomic variant's result depends on the order its splits land.  With
+    P = (2^100, 1, -2^100, 1, 0...) every order gives 0, 1 or 2.  The
+    deterministic path gives 0 every time.  Reports how many distinct atomic
+    results 2000 launches produced."""
+    t = torch()
+    K, S, r = 1024, 8, 8
+    two50, one = 0x5880, 0x3F80
+    vals = {0: (two50, two50), 1: (one, one), 2: (two50, 0xD880), 3: (one, one)}
+    x, A = _crafted_x_A(K, S, r, lambda s, rng: vals.get(s, (0, 0)), 5)
+    xg, Ag = bf16_to_gpu(x), bf16_to_gpu(A)
+    h = t.empty((1, r), dtype=t.float32, device="cuda")
+    ws = workspace(dsl.lora_shrink_workspace_bytes(1, r, S))
+    det, atom = [], []
+    for _ in range(2000):
+        dsl.lora_shrink_splitk(xg, Ag, h, ws, S, 1.0)
+        det.append(h.clone())
+        dsl.lora_shrink_splitk_atomic(xg, Ag, h, S, 1.0)
+        atom.append(h.clone())
+    t.cuda.synchronize()
+    D = t.stack(det).cpu().numpy()
+    Aa = t.stack(atom).cpu().numpy()
+    assert np.all(D == 0.0)
+    vals_seen = sorted(set(Aa.reshape(-1).tolist()))
+    assert set(vals_seen) <= {0.0, 1.0, 2.0}
+    _say(f"  atomic results seen over 2000 launches x {r} columns: {vals_seen}")
+
+
+# ---------------------------------------------------------------------------
+# multi-adapter
+# ---------------------------------------------------------------------------
+def _plan_reference(ids, n):
+    tiles = []
+    M = len(ids)
+    i = 0
+    norm = [a if 0 <= a < n else -1 for a in ids]
+    while i < M:
+        j = i
+        while j < M and norm[j] == norm[i]:
+            j += 1
+        if norm[i] >= 0:
+            for s in range(i, j, 16):
+                tiles.append((s, min(16, j - s), norm[i]))
+        i = j
+    return tiles
+
+
+def _build_plan(ids, n):
+    t = torch()
+    M = len(ids)
+    idg = t.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).cuda()
+    plan = t.zeros(dsl.lora_sgmv_plan_bytes(M), dtype=t.uint8, device="cuda")
+    dsl.lora_sgmv_plan(idg, n, plan)
+    return idg, plan
+
+
+@pytest.mark.parametrize("case", ["segments", "singletons", "invalid", "long", "one_adapter", "large"])
+def test_sgmv_plan_tiles(case):
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
+    if case == "segments":
+        ids, n = segments_to_ids(512, [(s, l, a) for s, l, a in _segs(512, 1, 64, 4, rng)]), 4
+    elif case == "singletons":
+        ids, n = rng.integers(0, 32, 37).astype(np.int32), 32
+    elif case == "invalid":
+        ids, n = rng.choice([-1, 0, 1, 2, 7, -5], 300).astype(np.int32), 3
+    elif case == "long":
+        ids, n = segments_to_ids(5000, [(s, l, a) for s, l, a in _segs(5000, 32, 512, 32, rng)]), 32
+    elif case == "one_adapter":
+        ids, n = np.zeros(1025, np.int32), 1
+    else:
+        ids, n = rng.integers(0, 2, 20000).astype(np.int32), 2
+    _say(f"plan {case}: M={len(ids)}")
+    _, plan = _build_plan(ids, n)
+    torch().cuda.synchronize()
+    raw = plan.cpu().numpy().view(np.int32)
+    ref = _plan_reference(ids.tolist(), n)
+    assert raw[0] == len(ref) and raw[1] == len(ids) and raw[2] == n
+    got = [tuple(raw[4 + 3 * k: 7 + 3 * k]) for k in range(raw[0])]
+    assert got == ref
+
+
+def _segs(M, lo, hi, n, rng):
+    out, s = [], 0
+    while s < M:
+        ln = min(int(rng.integers(lo, hi + 1)), M - s)
+        out.append((s, ln, int(rng.integers(0, n))))
+        s += ln
+    return out
+
+
+def _sgmv_gpu(c, plan_ids=None):
+    t = torch()
+    n = len(c.ranks)
+    K = c.K
+    As = [bf16_to_gpu(a) for a in c.As]
+    Bs = []
+    for b in c.Bs:
+        r = b.shape[1]
+        rb = (r + 7) // 8 * 8
+        bp = np.zeros((c.N, rb), np.uint16)
+        bp[:, :r] = b
+        Bs.append(bf16_to_gpu(bp))
+    Ap = t.tensor([a.data_ptr() for a in As], dtype=t.int64, device="cuda")
+    Bp = t.tensor([b.data_ptr() for b in Bs], dtype=t.int64, device="cuda")
+    ranks = t.from_numpy(c.ranks).cuda()
+    scales = t.from_numpy(c.scales).cuda()
+    idg, plan = _build_plan(c.ids, n)
+    xg = bf16_to_gpu(c.x)
+    h = t.full((c.M, c.r_max), float("nan"), dtype=t.float32, device="cuda")
+    ws = workspace(dsl.lora_sgmv_workspace_bytes(c.M, c.r_max, c.split_k))
+    dsl.lora_sgmv_shrink(xg, Ap, K, ranks, scales, idg, n, plan, h, c.r_max, c.split_k, ws)
+    yg = bf16_to_gpu(c.y)
+    dsl.lora_sgmv_expand(h, Bp, ranks, scales, n, plan, yg, c.r_max)
+    t.cuda.synchronize()
+    return h.cpu().numpy(), bf16_from_gpu(yg), (As, Bs)
+
+
+def _check_sgmv(c, h, y, rows, label):
+    """Per-token comparison with the oracle on the given rows."""
+    n = len(c.ranks)
+    ids = c.ids[rows]
+    for k, i in enumerate(rows):
+        a = ids[k]
+        if a < 0 or a >= n:
+            assert np.all(h[i] == 0.0) and np.array_equal(y[i], c.y[i]), f"{label}: row {i} without adapter"
+            continue
+        r = int(c.ranks[a])
+        assert np.all(h[i, r:] == 0.0)
+        check_shrink(h[i:i + 1, :r], c.x[i:i + 1], c.As[a], float(c.scales[a]),
+                     dsl.lora_shrink_plan(c.K, r, c.split_k), f"{label} row {i}")
+    yo, e, ab = oracle.sgmv_expand(h[rows], c.Bs, c.ranks, c.scales, c.ids[rows], c.y[rows])
+    return check_expand(y[rows], yo, e, ab, c.y[rows], label)
+
+
+def test_sgmv_fused_qkv_parity():
+    """4 adapters of rank 64, x [512 x 4096], segments of 1..64 tokens, B [64 x 6144], S=8."""
+    c = sgmv_case(512, 4096, 6144, [64, 64, 64, 64], 1, 64, 8, seed=0, tag="cfg3")
+    _say(f"sgmv 512x4096 -> 6144, {len(c.segs)} segments")
+    h, y, _ = _sgmv_gpu(c)
+    frac = _check_sgmv(c, h, y, list(range(512)), "sgmv qkv")
+    _say(f"  fraction of y differing from the correctly rounded value: {frac:.2e}")
+
+
+def test_sgmv_mixed_ranks_and_invalid_ids():
+    ranks = [8, 16, 32, 64, 24, 5]
+    rng = np.random.default_rng(11)
+    M = 300
+    ids = rng.choice([-1, 0, 1, 2, 3, 4, 5, 9], M).astype(np.int32)
+    ids[100:180] = 3
+    c = sgmv_case(M, 2048, 520, ranks, 0, 0, 4, seed=1, tag="mix", ids=ids)
+    h, y, _ = _sgmv_gpu(c)
+    _check_sgmv(c, h, y, list(range(M)), "sgmv mixed")
+
+
+def test_sgmv_equals_single_adapter_bitwise():
+    """All tokens on one adapter: the multi-adapter path must reproduce the
+    single-adapter calls bit for bit (same per-token arithmetic)."""
+    t = torch()
+    for r in (16, 64):
+        M, K, N, S = 77, 4096, 1024, 8
+        c = sgmv_case(M, K, N, [r], 0, 0, S, seed=2, tag=f"one{r}", ids=np.zeros(M, np.int32))
+        h, y, (As, Bs) = _sgmv_gpu(c)
+        xg = bf16_to_gpu(c.x)
+        hs = t.empty((M, r), dtype=t.float32, device="cuda")
+        dsl.lora_shrink_splitk(xg, As[0], hs, workspace(dsl.lora_shrink_workspace_bytes(M, r, S)), S, 2.0)
+        ys = bf16_to_gpu(c.y)
+        dsl.lora_expand(hs, Bs[0], ys, 2.0, r=r)
+        t.cuda.synchronize()
+        assert np.array_equal(f32_bits(hs), f32_bits_np(h[:, :r]))
+        assert np.array_equal(bf16_from_gpu(ys), y)
+
+
+def test_sgmv_permuting_segments_keeps_token_bits():
+    ranks = [16, 32, 64]
+    M = 200
+    c = sgmv_case(M, 4096, 512, ranks, 1, 40, 8, seed=5, tag="perm")
+    h1, y1, _ = _sgmv_gpu(c)
+    # reverse the order of the segments (tokens move with their ids, x and y)
+    order = np.concatenate([np.arange(s, s + l) for s, l, _ in reversed(c.segs)])
+    c2 = sgmv_case(M, 4096, 512, ranks, 1, 40, 8, seed=5, tag="perm")
+    c2.x, c2.y, c2.ids = c.x[order], c.y[order], c.ids[order]
+    h2, y2, _ = _sgmv_gpu(c2)
+    assert np.array_equal(f32_bits_np(h2), f32_bits_np(h1[order]))
+    assert np.array_equal(y2, y1[order])
+
+
+def test_sgmv_prefill_full_size_sampled():
+    """32 adapters with ranks cycling 8, 16, 32, 64, x [4096 x 8192], segments
+    of 32..512 tokens, B_i [r_i x 28672], S=16, at full size; the oracle checks
+    64 sampled tokens (and untouched rows are checked by value)."""
+    c = sgmv_case(4096, 8192, 28672, [8, 16, 32, 64] * 8, 32, 512, 16, seed=0, tag="cfg5")
+    _say(f"sgmv prefill 4096x8192 -> 28672, {len(c.segs)} segments")
+    h, y, _ = _sgmv_gpu(c)
+    rows = sorted(np.random.default_rng(3).choice(4096, 64, replace=False).tolist())
+    _check_sgmv(c, h, y, rows, "sgmv prefill")
