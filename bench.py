@@ -1,0 +1,360 @@
+"""Benchmark: deterministic vs atomic Split-K LoRA shrink + expand on one MI355X.
+
+Workload (one "step"): the q_proj-shaped single-adapter LoRA of an
+8B-parameter Llama-3 layer - x bf16 [M x 4096] ~ N(0,1), A bf16 [16 x 4096]
+and B bf16 [4096 x 16] ~ N(0, 0.02), base y bf16 [M x 4096] ~ N(0,1),
+scale 2.0, Split-K 8 - run once at each batch size M in {1, 16, 64, 256}:
+deterministic shrink (split partials + fixed-tree combine) then expand into y.
+`value` is the mean microseconds per shrink+expand call over the four batch
+sizes.  The atomic Split-K contrast (zero fill + atomic partials + expand) is
+timed the same way.
+
+Timing: each step is captured once per input copy in a HIP graph (the paper
+times shrink latency under CUDA graphs); the timed region replays K steps,
+rotating over enough input copies (>= 1 GiB) that no step finds its inputs
+in the 256 MB last-level cache.  Inputs are resident in HBM before timing.
+HIP events are recorded on the stream the kernels run on.
+
+Also reported: per-batch-size numbers, hot-cache numbers, the roofline of the
+dominant kernel (the tree + expand kernel of the deterministic pipeline), a decode
+bandwidth probe (32 tokens, each with its own rank-64 adapter, hidden 8192,
+multi-adapter shrink) and the CPU oracle timed on the host cores.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "shrink+expand µs/call & HBM GB/s (% peak), deterministic vs atomic Split-K=8"
+HBM_PEAK_GBS = 8000.0
+M_LIST = (1, 16, 64, 256)
+K_HID, RANK, N_OUT, SPLIT, SCALE = 4096, 16, 4096, 8, 2.0
+ROTATE_BYTES = 1 << 30
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def shrink_bytes(M, K, r):
+    """Algorithmic bytes of a shrink: read x and A once, write h."""
+    return 2 * M * K + 2 * K * r + 4 * M * r
+
+
+def expand_bytes(M, r, N):
+    """Algorithmic bytes of an expand: read h and B once, read and write y."""
+    return 4 * M * r + 2 * r * N + 4 * M * N
+
+
+def combine_bytes(M, r, N, S):
+    """Algorithmic bytes of the tree + expand kernel: read the S workspace
+    slices once, write h, read B once, read and write y."""
+    return 4 * S * M * r + 4 * M * r + 2 * r * N + 4 * M * N
+
+
+class Bench:
+    def __init__(self, args):
+        import torch
+        import deterministic_split_lora_amd as dsl
+        from synth import single_adapter_case
+        self.t, self.dsl, self.args = torch, dsl, args
+        self.dev = torch.device("cuda:0")
+        torch.cuda.set_device(self.dev)
+
+        def g(a):
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(self.dev)
+
+        # one seeded input set per batch size, then device copies for rotation
+        base = {M: single_adapter_case(M, K_HID, RANK, N_OUT, SPLIT, SCALE, seed=0) for M in M_LIST}
+        self.ws_bytes = {M: dsl.lora_shrink_expand_workspace_bytes(M, RANK, SPLIT) for M in M_LIST}
+        per_set = sum(2 * M * K_HID + 2 * M * N_OUT + 4 * RANK * K_HID + 4 * M * RANK * (SPLIT + 1)
+                      for M in M_LIST)
+        self.copies = max(2, math.ceil(ROTATE_BYTES / per_set)) if not args.hot else 1
+        self.sets = []
+        for c in range(self.copies):
+            s = {}
+            for M in M_LIST:
+                b = base[M]
+                s[M] = dict(x=g(b.x), A=g(b.A), B=g(b.B), y=g(b.y),
+                            h=torch.empty((M, RANK), dtype=torch.float32, device=self.dev),
+                            ws=torch.empty(self.ws_bytes[M], dtype=torch.uint8, device=self.dev))
+            self.sets.append(s)
+        torch.cuda.synchronize()
+        log(f"bench: {self.copies} input copies ({self.copies * per_set / 2**30:.2f} GiB)")
+
+    # -- one call of each variant on one input set ---------------------------
+    def det(self, s, M):
+        """Deterministic shrink + expand (lora_shrink_expand: one launch for
+        small M, two otherwise; the same bits either way)."""
+        self.dsl.lora_shrink_expand(s["x"], s["A"], s["B"], s["y"], s["ws"], SPLIT, 1.0, SCALE, h=s["h"])
+
+    def det_two_launch(self, s, M):
+        """Split partials, then tree + expand (2 launches)."""
+        d = self.dsl
+        d.lora_shrink_partials(s["x"], s["A"], s["ws"], SPLIT)
+        d.lora_expand_combine(s["ws"], s["B"], s["y"], SPLIT, 1.0, SCALE, h=s["h"])
+
+    def det_one_launch(self, s, M):
+        self.dsl.lora_shrink_expand_fused(s["x"], s["A"], s["B"], s["y"], SPLIT, 1.0, SCALE, h=s["h"])
+
+    def det_two_call(self, s, M):
+        """Deterministic shrink (partials + tree kernel) then expand (3 launches)."""
+        d = self.dsl
+        d.lora_shrink_splitk(s["x"], s["A"], s["h"], s["ws"], SPLIT, 1.0)
+        d.lora_expand(s["h"], s["B"], s["y"], SCALE)
+
+    def atomic(self, s, M):
+        """Atomic contrast: zero fill + atomic partials, then expand (3 launches)."""
+        d = self.dsl
+        d.lora_shrink_splitk_atomic(s["x"], s["A"], s["h"], SPLIT, 1.0)
+        d.lora_expand(s["h"], s["B"], s["y"], SCALE)
+
+    def combine_only(self, s, M):
+        self.dsl.lora_expand_combine(s["ws"], s["B"], s["y"], SPLIT, 1.0, SCALE, h=s["h"])
+
+    def capture(self, fn, Ms, per_graph=1):
+        """HIP graphs that each run fn(set, M) for M in Ms on `per_graph`
+        consecutive input copies; together the graphs cover every copy."""
+        t = self.t
+        side = t.cuda.Stream()
+        side.wait_stream(t.cuda.current_stream())
+        with t.cuda.stream(side):
+            for M in Ms:
+                fn(self.sets[0][M], M)          # first launch outside capture
+        t.cuda.current_stream().wait_stream(side)
+        t.cuda.synchronize()
+        C = len(self.sets)
+        graphs = []
+        for c0 in range(0, C, per_graph):
+            gr = t.cuda.CUDAGraph()
+            with t.cuda.graph(gr):
+                for q in range(per_graph):
+                    s = self.sets[(c0 + q) % C]
+                    for M in Ms:
+                        fn(s[M], M)
+            graphs.append(gr)
+        t.cuda.synchronize()
+        return graphs
+
+    def time_graphs(self, graphs, replays, warmup):
+        t = self.t
+        n = len(graphs)
+        for i in range(warmup):
+            graphs[i % n].replay()
+        t.cuda.synchronize()
+        e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(replays):
+            graphs[i % n].replay()
+        e1.record()
+        t.cuda.synchronize()
+        return e0.elapsed_time(e1) / replays          # ms per replay
+
+    def per_call_us(self, fn, Ms, per_graph, calls):
+        g = self.capture(fn, Ms, per_graph)
+        reps = max(1, calls // per_graph)
+        ms = self.time_graphs(g, reps, max(2, self.args.warmup // per_graph))
+        del g
+        return ms * 1000 / per_graph                  # us per pass over Ms
+
+    def run(self):
+        a = self.args
+        K, W = a.steps, a.warmup
+        res = {}
+        # the timed step: the four batch sizes back to back, one graph per copy
+        det_g = self.capture(self.det, M_LIST)
+        ms_det = self.time_graphs(det_g, K, W)
+        del det_g
+        res["ms_per_step"] = ms_det
+        res["us_per_call"] = ms_det * 1000 / len(M_LIST)
+        res["atomic_us_per_call"] = self.per_call_us(self.atomic, M_LIST, 1, K) / len(M_LIST)
+        res["det_two_call_us_per_call"] = self.per_call_us(self.det_two_call, M_LIST, 1, K) / len(M_LIST)
+        # per batch size: 8 calls per graph on 8 copies keep graph-launch cost out
+        per_m = {}
+        for M in M_LIST:
+            ud = self.per_call_us(self.det, (M,), 8, K)
+            ua = self.per_call_us(self.atomic, (M,), 8, K)
+            u3 = self.per_call_us(self.det_two_call, (M,), 8, K)
+            u2 = self.per_call_us(self.det_two_launch, (M,), 8, K)
+            u1 = self.per_call_us(self.det_one_launch, (M,), 8, K)
+            byt = shrink_bytes(M, K_HID, RANK) + expand_bytes(M, RANK, N_OUT)
+            per_m[str(M)] = {"det_us": round(ud, 3), "atomic_us": round(ua, 3),
+                             "det_launches": self.dsl.lora_shrink_expand_launches(M, K_HID, RANK, N_OUT, SPLIT),
+                             "det_one_launch_us": round(u1, 3), "det_two_launch_us": round(u2, 3),
+                             "det_three_launch_us": round(u3, 3),
+                             "det_over_atomic": round(ud / ua, 4), "bytes": byt,
+                             "workspace_bytes": 8 * SPLIT * M * RANK,
+                             "det_GBps": round(byt / ud / 1e3, 1),
+                             "det_pct_hbm_peak": round(100 * byt / ud / 1e3 / HBM_PEAK_GBS, 2)}
+        res["per_m"] = per_m
+        # roofline of the dominant kernel of the step, timed alone over the
+        # batch sizes at which the step launches it, 8 launches per graph
+        one = tuple(M for M in M_LIST if self.dsl.lora_shrink_expand_launches(M, K_HID, RANK, N_OUT, SPLIT) == 1)
+        two = tuple(M for M in M_LIST if M not in one)
+        cand = []
+        if one:
+            us = self.per_call_us(self.det_one_launch, one, 8, K)
+            byt = sum(shrink_bytes(M, K_HID, RANK) + expand_bytes(M, RANK, N_OUT) for M in one)
+            cand.append((us, len(one), byt, "k_shrink_expand_fused<2,8,8> (lora_shrink_expand_fused: Split-K "
+                         "shrink recomputed per 512 columns, fixed trees, expand; r=16, N=4096, M=" +
+                         "/".join(map(str, one)) + ")"))
+        if two:
+            us = self.per_call_us(self.combine_only, two, 8, K)
+            byt = sum(combine_bytes(M, RANK, N_OUT, SPLIT) for M in two)
+            cand.append((us, len(two), byt, "k_expand_combine<1,8> (lora_expand_combine: fixed tree over the "
+                         "Split-K workspace + expand; r=16, N=4096, M=" + "/".join(map(str, two)) + ")"))
+        us, n, byt, name = max(cand)
+        avg_launch_us = us / n
+        avg_bytes = byt / n
+        ach = avg_bytes / avg_launch_us / 1e3
+        res["roofline"] = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
+                           "avg_launch_us": round(avg_launch_us, 3), "algorithmic_bytes_per_launch": avg_bytes}
+        return res
+
+
+def decode_probe(args):
+    """32 decode tokens, each with its own rank-64 adapter, hidden 8192, Split-K 8:
+    the multi-adapter deterministic shrink (partials + fixed tree) on a prebuilt
+    plan, cold cache.  Algorithmic bytes: x, every adapter's A once, h."""
+    import torch
+    import deterministic_split_lora_amd as dsl
+    from synth import normal_bf16
+    dev = torch.device("cuda:0")
+    M, K, r, S, n = 32, 8192, 64, 8, 32
+
+    def g(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    x = normal_bf16((M, K), 1.0, 0, "probe_x")
+    As = [normal_bf16((r, K), 0.02, 0, f"probe_A{a}") for a in range(n)]
+    byt = 2 * M * K + 2 * K * r * n + 4 * M * r
+    copies = 1 if args.hot else max(2, math.ceil(ROTATE_BYTES / byt))
+    ids = torch.arange(M, dtype=torch.int32, device=dev)
+    ranks = torch.full((n,), r, dtype=torch.int32, device=dev)
+    plan = torch.empty(dsl.lora_sgmv_plan_bytes(M), dtype=torch.uint8, device=dev)
+    dsl.lora_sgmv_plan(ids, n, plan)
+    sets = []
+    for c in range(copies):
+        Ag = [g(a) for a in As]
+        sets.append(dict(x=g(x), A=Ag, Ap=torch.tensor([t.data_ptr() for t in Ag], dtype=torch.int64, device=dev),
+                         h=torch.empty((M, r), dtype=torch.float32, device=dev),
+                         ws=torch.empty(dsl.lora_sgmv_workspace_bytes(M, r, S), dtype=torch.uint8, device=dev)))
+    torch.cuda.synchronize()
+
+    def call(s):
+        dsl.lora_sgmv_shrink(s["x"], s["Ap"], K, ranks, None, ids, n, plan, s["h"], r, S, s["ws"])
+    call(sets[0])
+    torch.cuda.synchronize()
+    per_graph = 8
+    graphs = []
+    for c0 in range(0, copies, per_graph):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for q in range(per_graph):
+                call(sets[(c0 + q) % copies])
+        graphs.append(gr)
+    for i in range(max(2, args.warmup // per_graph)):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    replays = max(args.steps // per_graph, 8)
+    e0.record()
+    for i in range(replays):
+        graphs[i % len(graphs)].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000 / (replays * per_graph)
+    return {"workload": "32 tokens x hidden 8192, 32 adapters of rank 64 (one per token), Split-K 8, "
+                        "multi-adapter deterministic shrink (partials + tree)",
+            "us_per_call": round(us, 3), "bytes": byt, "GBps": round(byt / us / 1e3, 1),
+            "pct_hbm_peak": round(100 * byt / us / 1e3 / HBM_PEAK_GBS, 2), "copies": copies}
+
+
+def cpu_baseline(seconds: float):
+    """The CPU oracle (fp64 C, OpenMP) on the same workload: full steps (four
+    batch sizes, shrink + expand each) repeated for about `seconds`."""
+    import oracle
+    from synth import single_adapter_case
+    cases = {M: single_adapter_case(M, K_HID, RANK, N_OUT, SPLIT, SCALE, seed=0) for M in M_LIST}
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for M, c in cases.items():
+            h = oracle.shrink(c.x, c.A, 1.0)
+            oracle.expand(h.astype(np.float32), c.B, c.y, SCALE)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(el / (n * len(M_LIST)) * 1e6, 1), "unit": "us/call", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{n} full steps (M = 1, 16, 64, 256; fp64 shrink + expand each) in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--hot", action="store_true", help="no input rotation (inputs may sit in cache)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the deterministic shrink/expand needs no collective; "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    b = Bench(args)
+    res = b.run()
+    log("bench: main timing done")
+    probe = None if args.no_probe else decode_probe(args)
+    cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
+    import torch
+    out = {
+        "metric": METRIC,
+        "value": round(res["us_per_call"], 3),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_per_step"], 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "single-adapter LoRA, q_proj shape of an 8B Llama-3 layer: x [M x 4096], "
+                               "A [16 x 4096], B [4096 x 16], y [M x 4096] bf16, scale 2, Split-K 8, "
+                               "M = 1, 16, 64, 256 per step",
+                   "cache": "hot" if args.hot else f"cold: rotating {b.copies} input copies (>= 1 GiB)",
+                   "timing": "HIP graph replay, HIP events on the launch stream",
+                   "det_pipeline": "lora_shrink_expand (1 launch for M <= 64, 2 above; identical bits)",
+                   "atomic_pipeline": "lora_shrink_splitk_atomic (fill + atomic partials) + lora_expand (3 launches)"},
+        "atomic_us_per_call": round(res["atomic_us_per_call"], 3),
+        "det_two_call_us_per_call": round(res["det_two_call_us_per_call"], 3),
+        "det_over_atomic": round(res["us_per_call"] / res["atomic_us_per_call"], 4),
+        "per_m": res["per_m"],
+        "roofline": res["roofline"],
+        "cpu_baseline": cpu,
+        "decode_bandwidth_probe": probe,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -27,6 +27,8 @@ EXPORTED = [
     "lora_abi_version", "lora_status_str", "lora_shrink_plan", "lora_shrink_workspace_bytes",
     "lora_shrink_splitk", "lora_shrink_splitk_atomic", "lora_expand", "lora_sgmv_plan_bytes",
     "lora_sgmv_plan", "lora_sgmv_workspace_bytes", "lora_sgmv_shrink", "lora_sgmv_expand",
+    "lora_shrink_expand_workspace_bytes", "lora_shrink_expand", "lora_shrink_partials", "lora_expand_combine",
+    "lora_shrink_expand_fused", "lora_shrink_expand_launches",
 ]
 
 
@@ -76,6 +78,21 @@ def lib():
                                                 _f32, _vp]
         L.lora_expand.restype = ctypes.c_int
         L.lora_expand.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i32, _i64, _f32, _vp]
+        L.lora_shrink_expand_workspace_bytes.restype = _sz
+        L.lora_shrink_expand_workspace_bytes.argtypes = [_i64, _i32, _i32]
+        L.lora_shrink_expand.restype = ctypes.c_int
+        L.lora_shrink_expand.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32,
+                                         _i64, _i32, _f32, _f32, _vp, _sz, _vp]
+        L.lora_shrink_expand_launches.restype = ctypes.c_int
+        L.lora_shrink_expand_launches.argtypes = [_i64, _i64, _i32, _i64, _i32]
+        L.lora_shrink_expand_fused.restype = ctypes.c_int
+        L.lora_shrink_expand_fused.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
+                                               _i32, _i64, _i32, _f32, _f32, _vp]
+        L.lora_shrink_partials.restype = ctypes.c_int
+        L.lora_shrink_partials.argtypes = [_vp, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _vp, _sz, _vp]
+        L.lora_expand_combine.restype = ctypes.c_int
+        L.lora_expand_combine.argtypes = [_vp, _sz, _i32, _f32, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i32, _i64,
+                                          _f32, _vp]
         L.lora_sgmv_plan_bytes.restype = _sz
         L.lora_sgmv_plan_bytes.argtypes = [_i64]
         L.lora_sgmv_plan.restype = ctypes.c_int
@@ -200,6 +217,85 @@ def lora_expand(h, B, y, scale: float, r: int | None = None, stream=None):
     st = lib().lora_expand(_ptr(h), _ld(h, "h"), _ptr(B), _ld(B, "B"), _ptr(y), _ld(y, "y"), M, r, N, scale,
                            _stream(stream, y))
     _check(st, "lora_expand")
+    return y
+
+
+def lora_shrink_expand_workspace_bytes(M: int, r: int, split_k: int) -> int:
+    return int(lib().lora_shrink_expand_workspace_bytes(M, r, split_k))
+
+
+def lora_shrink_expand(x, A, B, y, workspace, split_k: int = 8, shrink_scale: float = 1.0,
+                       expand_scale: float = 1.0, h=None, stream=None):
+    """Deterministic shrink then expand in two launches; y updated in place,
+    h (optional, fp32 [M, >= r]) receives the shrink output."""
+    import torch
+    _dtype(x, torch.bfloat16, "x"); _dtype(A, torch.bfloat16, "A")
+    _dtype(B, torch.bfloat16, "B"); _dtype(y, torch.bfloat16, "y")
+    if h is not None:
+        _dtype(h, torch.float32, "h")
+    M, K = x.shape
+    r = A.shape[0]
+    N = y.shape[1]
+    if y.shape[0] != M:
+        raise ValueError("x and y must have the same number of rows")
+    st = lib().lora_shrink_expand(_ptr(x), _ld(x, "x"), _ptr(A), _ld(A, "A"), _ptr(B), _ld(B, "B"), _ptr(h),
+                                  _ld(h, "h") if h is not None else 0, _ptr(y), _ld(y, "y"), M, K, r, N, split_k,
+                                  shrink_scale, expand_scale, _ptr(workspace), _nbytes(workspace),
+                                  _stream(stream, x))
+    _check(st, "lora_shrink_expand")
+    return y
+
+
+def lora_shrink_expand_launches(M: int, K: int, r: int, N: int, split_k: int) -> int:
+    return int(lib().lora_shrink_expand_launches(M, K, r, N, split_k))
+
+
+def lora_shrink_expand_fused(x, A, B, y, split_k: int = 8, shrink_scale: float = 1.0, expand_scale: float = 1.0,
+                             h=None, stream=None):
+    """Deterministic shrink then expand in one launch (no workspace); y in place."""
+    import torch
+    _dtype(x, torch.bfloat16, "x"); _dtype(A, torch.bfloat16, "A")
+    _dtype(B, torch.bfloat16, "B"); _dtype(y, torch.bfloat16, "y")
+    if h is not None:
+        _dtype(h, torch.float32, "h")
+    M, K = x.shape
+    r = A.shape[0]
+    N = y.shape[1]
+    if y.shape[0] != M:
+        raise ValueError("x and y must have the same number of rows")
+    st = lib().lora_shrink_expand_fused(_ptr(x), _ld(x, "x"), _ptr(A), _ld(A, "A"), _ptr(B), _ld(B, "B"), _ptr(h),
+                                        _ld(h, "h") if h is not None else 0, _ptr(y), _ld(y, "y"), M, K, r, N,
+                                        split_k, shrink_scale, expand_scale, _stream(stream, x))
+    _check(st, "lora_shrink_expand_fused")
+    return y
+
+
+def lora_shrink_partials(x, A, workspace, split_k: int = 8, stream=None):
+    """workspace[s][i][j] = split s's fp32 partial of x @ A^T (one launch)."""
+    import torch
+    _dtype(x, torch.bfloat16, "x"); _dtype(A, torch.bfloat16, "A")
+    M, K = x.shape
+    r = A.shape[0]
+    st = lib().lora_shrink_partials(_ptr(x), _ld(x, "x"), _ptr(A), _ld(A, "A"), M, K, r, split_k,
+                                    _ptr(workspace), _nbytes(workspace), _stream(stream, x))
+    _check(st, "lora_shrink_partials")
+    return workspace
+
+
+def lora_expand_combine(workspace, B, y, split_k: int = 8, shrink_scale: float = 1.0, expand_scale: float = 1.0,
+                        h=None, r: int | None = None, stream=None):
+    """Fixed-tree combine of the workspace, then the expand into y (one launch)."""
+    import torch
+    _dtype(B, torch.bfloat16, "B"); _dtype(y, torch.bfloat16, "y")
+    if h is not None:
+        _dtype(h, torch.float32, "h")
+    M, N = y.shape
+    if r is None:
+        r = B.shape[1]
+    st = lib().lora_expand_combine(_ptr(workspace), _nbytes(workspace), split_k, shrink_scale, _ptr(B), _ld(B, "B"),
+                                   _ptr(h), _ld(h, "h") if h is not None else 0, _ptr(y), _ld(y, "y"), M, r, N,
+                                   expand_scale, _stream(stream, y))
+    _check(st, "lora_expand_combine")
     return y
 
 

@@ -12,7 +12,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblora_det.so")
-SOURCES = ["abi.hip", "shrink.hip", "expand.hip", "sgmv_plan.hip"]
+SOURCES = ["abi.hip", "shrink.hip", "expand.hip", "fused.hip", "sgmv_plan.hip"]
 HEADERS = ["device.h", "kernels.h"]
 
 HIPCC_FLAGS = [

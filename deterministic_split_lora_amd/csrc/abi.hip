@@ -101,6 +101,69 @@ size_t workspace_bytes(int64_t M, int32_t cols, int32_t split_k)
     return (size_t)split_k * (size_t)M * (size_t)cols * sizeof(float);
 }
 
+// Checks shared by the single-adapter shrink + expand entry points.
+int check_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a, const uint16_t* B,
+                        int64_t ld_b, const float* h, int64_t ld_h, const uint16_t* y, int64_t ld_y, int64_t M,
+                        int64_t K, int32_t r, int64_t N, int32_t split_k, lora_shrink_plan_t* pl)
+{
+    if (M < 0 || M > kMaxDim || N < 0 || N > kMaxDim)
+        return LORA_ERR_SHAPE;
+    int st = make_plan(K, r, split_k, pl);
+    if (st != LORA_OK)
+        return st;
+    if (N % 8 != 0)
+        return LORA_ERR_UNSUPPORTED;
+    if ((N + kExpandCols - 1) / kExpandCols > 65535 || (M + kRowBlock - 1) / kRowBlock > 0x7FFFFFFF)
+        return LORA_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return LORA_OK;
+    if (!x || !A || !B || !y)
+        return LORA_ERR_NULL;
+    if (ld_x < K || ld_a < K || ld_b < r || ld_y < N || (h && ld_h < r))
+        return LORA_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) ||
+        (reinterpret_cast<uintptr_t>(h) & 3u) || ld_x % 8 || ld_a % 8 || ld_b % 8 || ld_y % 8)
+        return LORA_ERR_ALIGN;
+    return LORA_OK;
+}
+
+// Which schedule lora_shrink_expand runs.  Both give the same bits (same
+// chunks, chains, trees and expand arithmetic).  The single launch makes every
+// workgroup (16 tokens x 512 columns) re-read the whole of A, K * r * 2 bytes,
+// through one compute unit; that beats a second dependent launch only while A
+// is small (measured on MI355X: at K = 4096, r = 16, i.e. 128 KiB, the two
+// launches are faster at every M).
+bool use_single_launch(int64_t M, int64_t K, int32_t r, int64_t N)
+{
+    (void)N;
+    return M <= 64 && K * r * 2 <= 32 * 1024;
+}
+
+int launch_fused(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a, const uint16_t* B,
+                 int64_t ld_b, float* h, int64_t ld_h, uint16_t* y, int64_t ld_y, int64_t M, int32_t r, int64_t N,
+                 const lora_shrink_plan_t& pl, float shrink_scale, float expand_scale, void* stream)
+{
+    FusedParams p{};
+    p.x = x;
+    p.ld_x = ld_x;
+    p.A = A;
+    p.ld_a = ld_a;
+    p.B = B;
+    p.ld_b = ld_b;
+    p.h = h;
+    p.ld_h = ld_h;
+    p.y = y;
+    p.ld_y = ld_y;
+    p.M = M;
+    p.N = N;
+    p.r = r;
+    p.k_chunk = pl.k_chunk;
+    p.k_steps = pl.k_steps;
+    p.shrink_scale = shrink_scale;
+    p.expand_scale = expand_scale;
+    return launch_status(launch_shrink_expand_fused(p, pl.split_k, pl.waves, static_cast<hipStream_t>(stream)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -232,6 +295,141 @@ int lora_expand(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b, u
     p.r_max = r;
     p.scale = scale;
     return launch_status(launch_expand(p, static_cast<hipStream_t>(stream)));
+}
+
+size_t lora_shrink_expand_workspace_bytes(int64_t M, int32_t r, int32_t split_k)
+{
+    return workspace_bytes(M, r, split_k);
+}
+
+int lora_shrink_partials(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a, int64_t M, int64_t K,
+                         int32_t r, int32_t split_k, void* workspace, size_t ws_bytes, void* stream)
+{
+    if (M < 0 || M > kMaxDim)
+        return LORA_ERR_SHAPE;
+    lora_shrink_plan_t pl;
+    int st = make_plan(K, r, split_k, &pl);
+    if (st != LORA_OK)
+        return st;
+    if (M == 0)
+        return LORA_OK;
+    if (!x || !A || !workspace)
+        return LORA_ERR_NULL;
+    if (ld_x < K || ld_a < K)
+        return LORA_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(A) || !aligned16(workspace) || ld_x % 8 || ld_a % 8)
+        return LORA_ERR_ALIGN;
+    if (ws_bytes < workspace_bytes(M, r, split_k))
+        return LORA_ERR_WORKSPACE;
+    ShrinkParams sp = shrink_params(x, ld_x, A, ld_a, M, r, pl, 1.0f);
+    sp.out = static_cast<float*>(workspace);
+    sp.ld_out = r;
+    sp.split_stride = M * r;
+    return launch_status(launch_shrink_partial_ws(sp, pl.waves, pl.rank_tiles, static_cast<hipStream_t>(stream)));
+}
+
+int lora_expand_combine(const void* workspace, size_t ws_bytes, int32_t split_k, float shrink_scale,
+                        const uint16_t* B, int64_t ld_b, float* h, int64_t ld_h, uint16_t* y, int64_t ld_y,
+                        int64_t M, int32_t r, int64_t N, float expand_scale, void* stream)
+{
+    if (M < 0 || M > kMaxDim || N < 0 || N > kMaxDim)
+        return LORA_ERR_SHAPE;
+    if (!split_ok(split_k) || r < 1 || r > 64 || N % 8 != 0)
+        return LORA_ERR_UNSUPPORTED;
+    if ((N + kExpandCols - 1) / kExpandCols > 65535)
+        return LORA_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return LORA_OK;
+    if (!workspace || !B || !y)
+        return LORA_ERR_NULL;
+    if (ld_b < r || ld_y < N || (h && ld_h < r))
+        return LORA_ERR_SHAPE;
+    if (!aligned16(workspace) || !aligned16(B) || !aligned16(y) || (reinterpret_cast<uintptr_t>(h) & 3u) ||
+        ld_b % 8 || ld_y % 8)
+        return LORA_ERR_ALIGN;
+    if (ws_bytes < workspace_bytes(M, r, split_k))
+        return LORA_ERR_WORKSPACE;
+    TreeParams t{};
+    t.ws = static_cast<const float*>(workspace);
+    t.split_stride = M * r;
+    t.ldw = r;
+    t.h = h;
+    t.ld_h = ld_h;
+    t.M = M;
+    t.ncols = r;
+    t.scale = shrink_scale;
+    ExpandParams ep{};
+    ep.B = B;
+    ep.ld_b = ld_b;
+    ep.y = y;
+    ep.ld_y = ld_y;
+    ep.M = M;
+    ep.N = N;
+    ep.r = r;
+    ep.r_max = r;
+    ep.scale = expand_scale;
+    return launch_status(launch_expand_combine(ep, t, split_k, static_cast<hipStream_t>(stream)));
+}
+
+int lora_shrink_expand_launches(int64_t M, int64_t K, int32_t r, int64_t N, int32_t split_k)
+{
+    lora_shrink_plan_t pl;
+    if (M < 0 || N < 0 || make_plan(K, r, split_k, &pl) != LORA_OK)
+        return -LORA_ERR_UNSUPPORTED;
+    if (M == 0 || N == 0)
+        return 0;
+    return use_single_launch(M, K, r, N) ? 1 : 2;
+}
+
+int lora_shrink_expand_fused(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a, const uint16_t* B,
+                             int64_t ld_b, float* h, int64_t ld_h, uint16_t* y, int64_t ld_y, int64_t M, int64_t K,
+                             int32_t r, int64_t N, int32_t split_k, float shrink_scale, float expand_scale,
+                             void* stream)
+{
+    lora_shrink_plan_t pl;
+    const int st = check_shrink_expand(x, ld_x, A, ld_a, B, ld_b, h, ld_h, y, ld_y, M, K, r, N, split_k, &pl);
+    if (st != LORA_OK || M == 0 || N == 0)
+        return st;
+    return launch_fused(x, ld_x, A, ld_a, B, ld_b, h, ld_h, y, ld_y, M, r, N, pl, shrink_scale, expand_scale,
+                        stream);
+}
+
+int lora_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a, const uint16_t* B,
+                       int64_t ld_b, float* h, int64_t ld_h, uint16_t* y, int64_t ld_y, int64_t M, int64_t K,
+                       int32_t r, int64_t N, int32_t split_k, float shrink_scale, float expand_scale,
+                       void* workspace, size_t ws_bytes, void* stream)
+{
+    // all checks of both halves before the first launch
+    if (M < 0 || M > kMaxDim || N < 0 || N > kMaxDim)
+        return LORA_ERR_SHAPE;
+    lora_shrink_plan_t pl;
+    int st = make_plan(K, r, split_k, &pl);
+    if (st != LORA_OK)
+        return st;
+    if (N % 8 != 0)
+        return LORA_ERR_UNSUPPORTED;
+    if ((N + kExpandCols - 1) / kExpandCols > 65535)
+        return LORA_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return LORA_OK;
+    if (!x || !A || !B || !y || !workspace)
+        return LORA_ERR_NULL;
+    if (ld_x < K || ld_a < K || ld_b < r || ld_y < N || (h && ld_h < r))
+        return LORA_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) || !aligned16(workspace) ||
+        (reinterpret_cast<uintptr_t>(h) & 3u) || ld_x % 8 || ld_a % 8 || ld_b % 8 || ld_y % 8)
+        return LORA_ERR_ALIGN;
+    if (ws_bytes < workspace_bytes(M, r, split_k))
+        return LORA_ERR_WORKSPACE;
+    if (use_single_launch(M, K, r, N)) {
+        return launch_fused(x, ld_x, A, ld_a, B, ld_b, h, ld_h, y, ld_y, M, r, N, pl, shrink_scale, expand_scale,
+                            stream);
+    }
+    st = lora_shrink_partials(x, ld_x, A, ld_a, M, K, r, split_k, workspace, ws_bytes, stream);
+    if (st != LORA_OK)
+        return st;
+    return lora_expand_combine(workspace, ws_bytes, split_k, shrink_scale, B, ld_b, h, ld_h, y, ld_y, M, r, N,
+                               expand_scale, stream);
 }
 
 size_t lora_sgmv_plan_bytes(int64_t M)

@@ -65,6 +65,124 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
+// bf16(h[row][j0 .. j0+7]) with columns >= r read as 0.
+__device__ __forceinline__ bf16x8 load_h_as_bf16(const float* hp, int j0, int r)
+{
+    float f[8];
+    if (j0 + 8 <= r) {
+        const float4 a = *reinterpret_cast<const float4*>(hp);
+        const float4 b = *reinterpret_cast<const float4*>(hp + 4);
+        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
+        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            f[e] = (j0 + e < r) ? hp[e] : 0.0f;
+    }
+    u16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        v[e] = f32_to_bf16_bits(f[e]);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// ---------------------------------------------------------------------------
+// Expand tile, shared by every kernel that expands (so the per-element
+// arithmetic is literally the same code): a wavefront owns 16 tokens x 64
+// output columns.  The matrix-core "row" operand is B (a row per output column)
+// and the "column" operand is bf16(h) (a column per token); accumulator
+// register v of lane (li, g) is output row 4g+v of column li.  Operand row m of
+// tile t (0..3) stands for column  n_base + 16 (m / 4) + 4 t + (m % 4),  so lane
+// (li, g) collects columns n_base + 16 g + 4 t + v - a contiguous run of 16 -
+// for token li, and y moves with 16-byte loads and stores straight from the
+// accumulators.  Per element: one matrix-core step over j < 32 (r <= 32) or two
+// (r <= 64) with zero-padded reduction slots, then fma(scale, acc, y) and one
+// rounding to bf16.
+// ---------------------------------------------------------------------------
+struct ExpandLane {
+    int64_t row;        // this lane's token (clamped into the block)
+    int64_t n_base;     // first column of this wave
+    int li, g;
+    bool row_ok;
+};
+
+__device__ __forceinline__ ExpandLane expand_lane(int64_t row0, int nrows, int64_t col0)
+{
+    ExpandLane L;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    L.li = lane & 15;
+    L.g = lane >> 4;
+    L.row_ok = L.li < nrows;
+    L.row = row0 + (L.row_ok ? L.li : 0);
+    L.n_base = col0 + wave * 64;
+    return L;
+}
+
+// Loads this lane's 16 y values and its B operand rows (KS steps of 32 over r).
+template <int KS>
+__device__ __forceinline__ void expand_load(const ExpandLane& L, const uint16_t* y, int64_t ld_y, int64_t N,
+                                            const uint16_t* __restrict__ B, int64_t ld_b, int r, u16x8 (&yv)[2],
+                                            bf16x8 (&bop)[4][KS])
+{
+    const int64_t n0 = L.n_base + 16 * L.g;
+    const uint16_t* yp = y + L.row * ld_y + n0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+        yv[half] = (L.row_ok && n0 + half * 8 < N) ? *reinterpret_cast<const u16x8*>(yp + half * 8)
+                                                  : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int64_t n = L.n_base + (L.li >> 2) * 16 + t * 4 + (L.li & 3);
+        const bool n_ok = n < N;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int j0 = ks * kKStep + 8 * L.g;
+            bop[t][ks] = (n_ok && j0 < r) ? load_bf16x8_partial(B + n * ld_b + j0, r - j0) : bf16x8_zero();
+        }
+    }
+}
+
+// bf16(h) of the block's token rows (hrows: row 0 of the block, stride ld_hr),
+// the matrix-core steps, and the y update.  N % 8 == 0, so 8-column chunks
+// are whole.
+template <int KS>
+__device__ __forceinline__ void expand_finish(const ExpandLane& L, uint16_t* y, int64_t ld_y, int64_t N,
+                                              const float* hrows, int64_t ld_hr, int r, float scale,
+                                              const u16x8 (&yv)[2], const bf16x8 (&bop)[4][KS])
+{
+    bf16x8 hb[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int j0 = ks * kKStep + 8 * L.g;
+        hb[ks] = (L.row_ok && j0 < r) ? load_h_as_bf16(hrows + L.li * ld_hr + j0, j0, r) : bf16x8_zero();
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+            acc[t] = mfma_16x16x32(bop[t][ks], hb[ks], acc[t]);
+    }
+    if (!L.row_ok)
+        return;
+    const int64_t n0 = L.n_base + 16 * L.g;
+    uint16_t* yp = y + L.row * ld_y + n0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        if (n0 + half * 8 < N) {
+            u16x8 o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int idx = half * 8 + e;
+                o[e] = f32_to_bf16_bits(__builtin_fmaf(scale, acc[idx >> 2][idx & 3], bf16_bits_to_f32(yv[half][e])));
+            }
+            *reinterpret_cast<u16x8*>(yp + half * 8) = o;
+        }
+    }
+}
+
 // Fixed pairwise tree over N values: v[0]+v[1], v[2]+v[3], ... then the same on
 // the results, level by level; every add is one fp32 rounding.  N is a power
 // of two.  The result is left in v[0].

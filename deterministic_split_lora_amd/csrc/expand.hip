@@ -25,94 +25,64 @@ namespace lora {
 
 namespace {
 
-// bf16(h[row][j0 .. j0+7]) with columns >= r read as 0.
-__device__ __forceinline__ bf16x8 load_h_as_bf16(const float* hp, int j0, int r)
-{
-    float f[8];
-    if (j0 + 8 <= r) {
-        const float4 a = *reinterpret_cast<const float4*>(hp);
-        const float4 b = *reinterpret_cast<const float4*>(hp + 4);
-        f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w;
-        f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            f[e] = (j0 + e < r) ? hp[e] : 0.0f;
-    }
-    u16x8 v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-        v[e] = f32_to_bf16_bits(f[e]);
-    return __builtin_bit_cast(bf16x8, v);
-}
-
-// Tokens row0 .. row0+nrows-1 (nrows <= 16) x columns [256 cb, 256 cb + 256).
-// KS = matrix-core steps over the rank: 1 for r <= 32, 2 for r <= 64.
-template <int KS>
-__device__ __forceinline__ void expand_tile(const ExpandParams& p, int64_t row0, int nrows,
-                                            const uint16_t* __restrict__ B, int64_t ld_b, int r,
-                                            float scale, int64_t cb)
-{
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int li = lane & 15;
-    const int g = lane >> 4;
-    const int64_t n_base = cb * kExpandCols + wave * 64;
-    if (n_base >= p.N)
-        return;
-    const bool row_ok = li < nrows;
-    const int64_t row = row0 + (row_ok ? li : 0);
-
-    bf16x8 hb[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const int j0 = ks * kKStep + 8 * g;
-        hb[ks] = (row_ok && j0 < r) ? load_h_as_bf16(p.h + row * p.ld_h + j0, j0, r) : bf16x8_zero();
-    }
-
-    f32x4 acc[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int64_t n = n_base + (li >> 2) * 16 + t * 4 + (li & 3);
-        const bool n_ok = n < p.N;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int j0 = ks * kKStep + 8 * g;
-            const bf16x8 bv = (n_ok && j0 < r) ? load_bf16x8_partial(B + n * ld_b + j0, r - j0)
-                                               : bf16x8_zero();
-            acc[t] = mfma_16x16x32(bv, hb[ks], acc[t]);
-        }
-    }
-
-    if (!row_ok)
-        return;
-    const int64_t n0 = n_base + 16 * g;
-    uint16_t* yp = p.y + row * p.ld_y + n0;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        if (n0 + half * 8 < p.N) {                 // N % 8 == 0: chunks are whole
-            u16x8* q = reinterpret_cast<u16x8*>(yp + half * 8);
-            const u16x8 yv = *q;
-            u16x8 o;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int idx = half * 8 + e;
-                o[e] = f32_to_bf16_bits(__builtin_fmaf(scale, acc[idx >> 2][idx & 3], bf16_bits_to_f32(yv[e])));
-            }
-            *q = o;
-        }
-    }
-}
-
-// Single adapter: grid (ceil(M/16), ceil(N/256)), 4 waves.
+// Single adapter: grid (ceil(M/16), ceil(N/256)), 4 waves of 64 columns.
 template <int KS>
 __global__ __launch_bounds__(256) void k_expand(ExpandParams p)
 {
     const int64_t row0 = (int64_t)blockIdx.x * kRowBlock;
     const int64_t left = p.M - row0;
     const int nrows = left < kRowBlock ? (int)left : kRowBlock;
-    expand_tile<KS>(p, row0, nrows, p.B, p.ld_b, p.r, p.scale, blockIdx.y);
+    ExpandLane L = expand_lane(row0, nrows, (int64_t)blockIdx.y * kExpandCols);
+    if (L.n_base >= p.N)
+        return;
+    u16x8 yv[2];
+    bf16x8 bop[4][KS];
+    expand_load<KS>(L, p.y, p.ld_y, p.N, p.B, p.ld_b, p.r, yv, bop);
+    expand_finish<KS>(L, p.y, p.ld_y, p.N, p.h + row0 * p.ld_h, p.ld_h, p.r, p.scale, yv, bop);
+}
+
+// Fused: the fixed pairwise tree over the Split-K workspace for this row block
+// (exactly the second pass of the deterministic shrink: tree, then one
+// multiply by the shrink scale) is evaluated into an LDS tile, written out as
+// h by the first column block, and fed to the expand without a round trip
+// through a separate kernel.  Same bits as shrink then expand.
+constexpr int kHTileStride = 68;          // floats per LDS row (64 + 4 padding)
+
+template <int KS, int S>
+__global__ __launch_bounds__(256) void k_expand_combine(ExpandParams p, TreeParams c)
+{
+    __shared__ __align__(16) float hs[kRowBlock * kHTileStride];
+    const int64_t row0 = (int64_t)blockIdx.x * kRowBlock;
+    const int64_t left = p.M - row0;
+    const int nrows = left < kRowBlock ? (int)left : kRowBlock;
+    const int r = p.r;
+    // y and B first: they do not depend on the workspace
+    ExpandLane L = expand_lane(row0, nrows, (int64_t)blockIdx.y * kExpandCols);
+    const bool active = L.n_base < p.N;
+    u16x8 yv[2];
+    bf16x8 bop[4][KS];
+    if (active)
+        expand_load<KS>(L, p.y, p.ld_y, p.N, p.B, p.ld_b, r, yv, bop);
+    const bool write_h = c.h != nullptr && blockIdx.y == 0;
+    for (int e = threadIdx.x; e < kRowBlock * r; e += 256) {
+        const int row = e / r;
+        const int col = e - row * r;
+        if (row < nrows) {
+            float v[S];
+            const float* w = c.ws + (row0 + row) * c.ldw + col;
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+                v[s] = w[(int64_t)s * c.split_stride];
+            const float hv = __fmul_rn(pairwise_tree<S>(v), c.scale);
+            hs[row * kHTileStride + col] = hv;
+            if (write_h)
+                c.h[(row0 + row) * c.ld_h + col] = hv;
+        }
+    }
+    __syncthreads();
+    if (!active)
+        return;
+    expand_finish<KS>(L, p.y, p.ld_y, p.N, hs, kHTileStride, r, p.scale, yv, bop);
 }
 
 // Multi-adapter: a fixed grid walks the plan's (tile, column block) items.
@@ -132,10 +102,20 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(ExpandParams p)
         ra = ra < 0 ? 0 : (ra > p.r_max ? p.r_max : ra);
         const float scale = p.scales ? p.scales[a] : 1.0f;
         const int64_t ld_b = (ra + 7) & ~7;
-        if (ra > 32)
-            expand_tile<2>(p, t[0], t[1], p.B_ptrs[a], ld_b, ra, scale, cb);
-        else
-            expand_tile<1>(p, t[0], t[1], p.B_ptrs[a], ld_b, ra, scale, cb);
+        ExpandLane L = expand_lane(t[0], t[1], cb * kExpandCols);
+        if (L.n_base >= p.N)
+            continue;
+        const float* hrows = p.h + (int64_t)t[0] * p.ld_h;
+        u16x8 yv[2];
+        if (ra > 32) {
+            bf16x8 bop[4][2];
+            expand_load<2>(L, p.y, p.ld_y, p.N, p.B_ptrs[a], ld_b, ra, yv, bop);
+            expand_finish<2>(L, p.y, p.ld_y, p.N, hrows, p.ld_h, ra, scale, yv, bop);
+        } else {
+            bf16x8 bop[4][1];
+            expand_load<1>(L, p.y, p.ld_y, p.N, p.B_ptrs[a], ld_b, ra, yv, bop);
+            expand_finish<1>(L, p.y, p.ld_y, p.N, hrows, p.ld_h, ra, scale, yv, bop);
+        }
     }
 }
 
@@ -150,6 +130,26 @@ hipError_t launch_expand(const ExpandParams& p, hipStream_t st)
     else
         hipLaunchKernelGGL(k_expand<1>, grid, block, 0, st, p);
     return hipGetLastError();
+}
+
+template <int KS>
+hipError_t launch_expand_combine_ks(const ExpandParams& p, const TreeParams& c, int S, dim3 grid, hipStream_t st)
+{
+    switch (S) {
+    case 1: hipLaunchKernelGGL((k_expand_combine<KS, 1>), grid, dim3(256), 0, st, p, c); break;
+    case 2: hipLaunchKernelGGL((k_expand_combine<KS, 2>), grid, dim3(256), 0, st, p, c); break;
+    case 4: hipLaunchKernelGGL((k_expand_combine<KS, 4>), grid, dim3(256), 0, st, p, c); break;
+    case 8: hipLaunchKernelGGL((k_expand_combine<KS, 8>), grid, dim3(256), 0, st, p, c); break;
+    default: hipLaunchKernelGGL((k_expand_combine<KS, 16>), grid, dim3(256), 0, st, p, c); break;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st)
+{
+    dim3 grid((unsigned)((p.M + kRowBlock - 1) / kRowBlock), (unsigned)((p.N + kExpandCols - 1) / kExpandCols));
+    return p.r > 32 ? launch_expand_combine_ks<2>(p, c, split_k, grid, st)
+                    : launch_expand_combine_ks<1>(p, c, split_k, grid, st);
 }
 
 hipError_t launch_sgmv_expand(const ExpandParams& p, int grid, hipStream_t st)

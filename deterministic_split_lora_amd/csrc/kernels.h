@@ -86,6 +86,26 @@ __device__ __forceinline__ bool tile_ok(const int32_t* t, int64_t M, int32_t n_a
            t[2] < n_adapters;
 }
 
+struct FusedParams {
+    const uint16_t* x;
+    int64_t ld_x;
+    const uint16_t* A;
+    int64_t ld_a;
+    const uint16_t* B;
+    int64_t ld_b;
+    float* h;                       // may be null
+    int64_t ld_h;
+    uint16_t* y;
+    int64_t ld_y;
+    int64_t M;
+    int64_t N;
+    int32_t r;
+    int32_t k_chunk;
+    int32_t k_steps;
+    float shrink_scale;
+    float expand_scale;
+};
+
 hipError_t launch_shrink_partial_ws(const ShrinkParams& p, int waves, int rank_tiles, hipStream_t st);
 hipError_t launch_shrink_partial_direct(const ShrinkParams& p, int waves, int rank_tiles, hipStream_t st);
 hipError_t launch_shrink_partial_atomic(const ShrinkParams& p, int waves, int rank_tiles, hipStream_t st);
@@ -94,7 +114,9 @@ hipError_t launch_splitk_tree(const TreeParams& p, int split_k, bool sgmv, hipSt
 hipError_t launch_fill_zero(float* h, int64_t ld_h, int64_t M, int ncols, hipStream_t st);
 
 hipError_t launch_expand(const ExpandParams& p, hipStream_t st);
+hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st);
 hipError_t launch_sgmv_expand(const ExpandParams& p, int grid, hipStream_t st);
+hipError_t launch_shrink_expand_fused(const FusedParams& p, int split_k, int waves, hipStream_t st);
 
 hipError_t launch_sgmv_plan(const int32_t* ids, int64_t M, int32_t n_adapters, int32_t* plan,
                             hipStream_t st);

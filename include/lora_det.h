@@ -148,6 +148,65 @@ int lora_expand(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b,
                 uint16_t* y, int64_t ld_y, int64_t M, int32_t r, int64_t N, float scale,
                 void* stream);
 
+/*
+ * The two halves of the deterministic pipeline, one launch each.
+ *
+ * lora_shrink_partials: the Split-K partial kernel of lora_shrink_splitk on its
+ * own.  It writes ws[s][i][j] = P_s[i][j] (unscaled fp32 partial sums, layout
+ * as documented for lora_shrink_workspace_bytes) and nothing else.  The
+ * partials are the unit a row-parallel layer would exchange between devices
+ * before the fixed-order combine.
+ *
+ * lora_expand_combine: for each 16-token block, evaluates the same fixed
+ * pairwise tree over the split_k workspace slices and the multiply by
+ * shrink_scale that lora_shrink_splitk's second pass applies, writes the
+ * result to h when h is not NULL, and feeds it (rounded to bf16) into the
+ * expand of lora_expand with expand_scale.  The workspace must hold split_k
+ * slices of M x r floats.
+ *
+ * lora_shrink_expand: h and y bit for bit those of lora_shrink_splitk followed
+ * by lora_expand, in fewer launches: either the two calls above in order on
+ * one stream, or (small M) the single launch of lora_shrink_expand_fused.
+ *
+ * workspace: >= lora_shrink_expand_workspace_bytes(M, r, split_k) bytes =
+ * split_k * M * r * 4, also for split_k == 1.  Requirements: those of
+ * lora_shrink_splitk and lora_expand together.
+ */
+size_t lora_shrink_expand_workspace_bytes(int64_t M, int32_t r, int32_t split_k);
+
+int lora_shrink_partials(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a,
+                         int64_t M, int64_t K, int32_t r, int32_t split_k,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+int lora_expand_combine(const void* workspace, size_t workspace_bytes, int32_t split_k,
+                        float shrink_scale, const uint16_t* B, int64_t ld_b, float* h, int64_t ld_h,
+                        uint16_t* y, int64_t ld_y, int64_t M, int32_t r, int64_t N,
+                        float expand_scale, void* stream);
+
+/*
+ * lora_shrink_expand_fused: the same h and y in ONE launch and without a
+ * workspace.  Each workgroup owns a 16-token block and 512 output columns and
+ * recomputes that block's deterministic Split-K shrink - the same chunks,
+ * matrix-core chains, wave tree and split tree as lora_shrink_splitk, held in
+ * registers and LDS - before expanding it, so no workgroup depends on another.
+ * lora_shrink_expand runs this schedule when it is the faster one (small M).
+ */
+/* Host only: how many kernel launches lora_shrink_expand makes for these sizes
+   (1: the single-launch schedule, 2: partials then tree + expand, 0: nothing
+   to do), or -LORA_ERR_UNSUPPORTED for sizes it rejects. */
+int lora_shrink_expand_launches(int64_t M, int64_t K, int32_t r, int64_t N, int32_t split_k);
+
+int lora_shrink_expand_fused(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a,
+                             const uint16_t* B, int64_t ld_b, float* h, int64_t ld_h,
+                             uint16_t* y, int64_t ld_y, int64_t M, int64_t K, int32_t r, int64_t N,
+                             int32_t split_k, float shrink_scale, float expand_scale, void* stream);
+
+int lora_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a,
+                       const uint16_t* B, int64_t ld_b, float* h, int64_t ld_h,
+                       uint16_t* y, int64_t ld_y, int64_t M, int64_t K, int32_t r, int64_t N,
+                       int32_t split_k, float shrink_scale, float expand_scale,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Multi-adapter (SGMV) variants.  The paper replays shrink operations with the
  * mapping of tokens to adapters (section 5.2); here each token i carries an

@@ -222,3 +222,95 @@ def test_sgmv_rejects():
     assert expand(y=FAKE_MIS) == B.LORA_ERR_ALIGN
     assert expand(pb=16) == B.LORA_ERR_WORKSPACE
     assert expand(M=0, h=None) == B.LORA_OK
+
+
+def test_shrink_expand_rejects():
+    L = dsl.lib()
+    wsb = dsl.lora_shrink_expand_workspace_bytes(4, 16, 8)
+    assert wsb == 8 * 4 * 16 * 4
+    assert dsl.lora_shrink_expand_workspace_bytes(4, 16, 1) == 4 * 16 * 4
+
+    def call(**kw):
+        a = dict(x=FAKE, ld_x=4096, A=FAKE, ld_a=4096, B=FAKE, ld_b=16, h=FAKE, ld_h=16, y=FAKE, ld_y=4096, M=4,
+                 K=4096, r=16, N=4096, S=8, ss=1.0, es=2.0, ws=FAKE, wsb=wsb)
+        a.update(kw)
+        return L.lora_shrink_expand(a["x"], a["ld_x"], a["A"], a["ld_a"], a["B"], a["ld_b"], a["h"], a["ld_h"],
+                                    a["y"], a["ld_y"], a["M"], a["K"], a["r"], a["N"], a["S"], a["ss"], a["es"],
+                                    a["ws"], a["wsb"], None)
+    assert call(x=None) == B.LORA_ERR_NULL
+    assert call(B=None) == B.LORA_ERR_NULL
+    assert call(y=None) == B.LORA_ERR_NULL
+    assert call(ws=None) == B.LORA_ERR_NULL
+    assert call(S=3) == B.LORA_ERR_UNSUPPORTED
+    assert call(r=0) == B.LORA_ERR_UNSUPPORTED
+    assert call(N=4090) == B.LORA_ERR_UNSUPPORTED
+    assert call(K=4000, ld_x=4000, ld_a=4000) == B.LORA_ERR_UNSUPPORTED
+    assert call(ld_b=8) == B.LORA_ERR_SHAPE
+    assert call(ld_h=8) == B.LORA_ERR_SHAPE
+    assert call(h=None, ld_h=8, ld_y=100) == B.LORA_ERR_SHAPE
+    assert call(M=-1) == B.LORA_ERR_SHAPE
+    assert call(y=FAKE_MIS) == B.LORA_ERR_ALIGN
+    assert call(h=FAKE + 2) == B.LORA_ERR_ALIGN
+    assert call(ld_b=20) == B.LORA_ERR_ALIGN
+    assert call(wsb=wsb - 1) == B.LORA_ERR_WORKSPACE
+    assert call(M=0, x=None, ws=None) == B.LORA_OK
+
+
+def test_partials_and_combine_reject():
+    L = dsl.lib()
+    wsb = dsl.lora_shrink_expand_workspace_bytes(4, 16, 8)
+    assert L.lora_shrink_partials(None, 4096, FAKE, 4096, 4, 4096, 16, 8, FAKE, wsb, None) == B.LORA_ERR_NULL
+    assert L.lora_shrink_partials(FAKE, 4096, FAKE, 4096, 4, 4096, 16, 8, None, wsb, None) == B.LORA_ERR_NULL
+    assert L.lora_shrink_partials(FAKE, 4096, FAKE, 4096, 4, 4096, 16, 6, FAKE, wsb, None) == B.LORA_ERR_UNSUPPORTED
+    assert L.lora_shrink_partials(FAKE, 4096, FAKE, 4096, 4, 4096, 16, 8, FAKE, wsb - 4, None) == B.LORA_ERR_WORKSPACE
+    assert L.lora_shrink_partials(FAKE_MIS, 4096, FAKE, 4096, 4, 4096, 16, 8, FAKE, wsb, None) == B.LORA_ERR_ALIGN
+    assert L.lora_shrink_partials(FAKE, 2048, FAKE, 4096, 4, 4096, 16, 8, FAKE, wsb, None) == B.LORA_ERR_SHAPE
+    assert L.lora_shrink_partials(None, 4096, None, 4096, 0, 4096, 16, 8, None, 0, None) == B.LORA_OK
+
+    def comb(**kw):
+        a = dict(ws=FAKE, wsb=wsb, S=8, ss=1.0, B=FAKE, ld_b=16, h=None, ld_h=0, y=FAKE, ld_y=4096, M=4, r=16,
+                 N=4096, es=2.0)
+        a.update(kw)
+        return L.lora_expand_combine(a["ws"], a["wsb"], a["S"], a["ss"], a["B"], a["ld_b"], a["h"], a["ld_h"],
+                                     a["y"], a["ld_y"], a["M"], a["r"], a["N"], a["es"], None)
+    assert comb(ws=None) == B.LORA_ERR_NULL
+    assert comb(B=None) == B.LORA_ERR_NULL
+    assert comb(S=12) == B.LORA_ERR_UNSUPPORTED
+    assert comb(r=65) == B.LORA_ERR_UNSUPPORTED
+    assert comb(N=12) == B.LORA_ERR_UNSUPPORTED
+    assert comb(wsb=wsb - 1) == B.LORA_ERR_WORKSPACE
+    assert comb(h=FAKE, ld_h=8) == B.LORA_ERR_SHAPE
+    assert comb(ld_y=8) == B.LORA_ERR_SHAPE
+    assert comb(ws=FAKE + 4) == B.LORA_ERR_ALIGN
+    assert comb(h=FAKE + 1, ld_h=16) == B.LORA_ERR_ALIGN
+    assert comb(M=0, ws=None, B=None, y=None) == B.LORA_OK
+
+
+def test_shrink_expand_fused_rejects():
+    L = dsl.lib()
+
+    def call(**kw):
+        a = dict(x=FAKE, ld_x=4096, A=FAKE, ld_a=4096, B=FAKE, ld_b=16, h=FAKE, ld_h=16, y=FAKE, ld_y=4096, M=4,
+                 K=4096, r=16, N=4096, S=8, ss=1.0, es=2.0)
+        a.update(kw)
+        return L.lora_shrink_expand_fused(a["x"], a["ld_x"], a["A"], a["ld_a"], a["B"], a["ld_b"], a["h"],
+                                          a["ld_h"], a["y"], a["ld_y"], a["M"], a["K"], a["r"], a["N"], a["S"],
+                                          a["ss"], a["es"], None)
+    assert call(x=None) == B.LORA_ERR_NULL
+    assert call(A=None) == B.LORA_ERR_NULL
+    assert call(S=32) == B.LORA_ERR_UNSUPPORTED
+    assert call(r=70) == B.LORA_ERR_UNSUPPORTED
+    assert call(N=100, ld_y=4096) == B.LORA_ERR_UNSUPPORTED
+    assert call(ld_x=2048) == B.LORA_ERR_SHAPE
+    assert call(x=FAKE_MIS) == B.LORA_ERR_ALIGN
+    assert call(h=FAKE + 1) == B.LORA_ERR_ALIGN
+    assert call(M=0, x=None, A=None) == B.LORA_OK
+
+
+def test_shrink_expand_launch_count():
+    assert dsl.lora_shrink_expand_launches(1, 1024, 8, 4096, 8) == 1
+    assert dsl.lora_shrink_expand_launches(64, 1024, 16, 4096, 8) == 1
+    assert dsl.lora_shrink_expand_launches(65, 1024, 16, 4096, 8) == 2
+    assert dsl.lora_shrink_expand_launches(1, 4096, 16, 4096, 8) == 2
+    assert dsl.lora_shrink_expand_launches(0, 4096, 16, 4096, 8) == 0
+    assert dsl.lora_shrink_expand_launches(8, 4000, 16, 4096, 8) < 0

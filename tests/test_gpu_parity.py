@@ -309,6 +309,12 @@ def test_batch_invariance_sweep():
                 dsl.lora_shrink_splitk(xg, Ag, h, ws, S, 1.0)
                 dsl.lora_expand(h, Bg, yw, 2.0)
                 h0, y0 = h.view(t.int32).clone(), yw.view(t.int16).clone()
+                # the same through lora_shrink_expand (whose schedule depends on M)
+                hf = t.empty_like(h)
+                yf = yg.clone()
+                dsl.lora_shrink_expand(xg, Ag, Bg, yf, workspace(dsl.lora_shrink_expand_workspace_bytes(M, r, S)),
+                                       S, 1.0, 2.0, h=hf)
+                assert t.equal(hf.view(t.int32), h0) and t.equal(yf.view(t.int16), y0), f"batch {b}"
                 # the first layout of each batch size is launched 1000 times,
                 # every repeat compared on the GPU with the first
                 bad = t.zeros((), dtype=t.int64, device="cuda")
@@ -532,3 +538,186 @@ def test_sgmv_prefill_full_size_sampled():
     h, y, _ = _sgmv_gpu(c)
     rows = sorted(np.random.default_rng(3).choice(4096, 64, replace=False).tolist())
     _check_sgmv(c, h, y, rows, "sgmv prefill")
+
+
+# ---------------------------------------------------------------------------
+# fused shrink + expand (two launches) and HIP graph capture
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,r,N,S", [(1, 4096, 16, 4096, 8), (16, 4096, 16, 4096, 8), (256, 4096, 16, 4096, 8),
+                                       (37, 8192, 64, 1032, 16), (5, 1024, 8, 512, 1), (70, 2048, 40, 264, 4),
+                                       (3, 3072, 1, 8, 2), (64, 14336, 32, 4096, 8), (65, 4096, 24, 1000, 8),
+                                       (9, 1024, 33, 520, 4), (2, 16384, 64, 512, 16)])
+def test_shrink_expand_fused_bitwise(M, K, r, N, S):
+    """Every schedule of the deterministic shrink + expand - lora_shrink_splitk
+    then lora_expand (three launches), lora_shrink_partials then
+    lora_expand_combine (two), lora_shrink_expand_fused (one) and
+    lora_shrink_expand (which picks by M) - gives the same h and y bits, and
+    y agrees with the oracle."""
+    _say(f"fused shrink+expand M={M} K={K} r={r} N={N} S={S}")
+    t = torch()
+    c = single_adapter_case(M, K, r, N, split_k=S, seed=M + r)
+    ldb = (r + 7) // 8 * 8
+    Bp = np.zeros((N, ldb), np.uint16)
+    Bp[:, :r] = c.B
+    xg, Ag, Bg = bf16_to_gpu(c.x), bf16_to_gpu(c.A), bf16_to_gpu(Bp)
+    # two calls
+    h1 = t.empty((M, r), dtype=t.float32, device="cuda")
+    ws1 = workspace(dsl.lora_shrink_workspace_bytes(M, r, S))
+    dsl.lora_shrink_splitk(xg, Ag, h1, ws1 if S > 1 else None, S, 1.0)
+    hpad = t.zeros((M, (r + 3) // 4 * 4), dtype=t.float32, device="cuda")
+    hpad[:, :r] = h1
+    y1 = bf16_to_gpu(c.y)
+    dsl.lora_expand(hpad, Bg, y1, 2.0, r=r)
+    # fused, with and without h
+    ws2 = workspace(dsl.lora_shrink_expand_workspace_bytes(M, r, S))
+    h2 = t.full((M, r), float("nan"), dtype=t.float32, device="cuda")
+    y2 = bf16_to_gpu(c.y)
+    dsl.lora_shrink_expand(xg, Ag, Bg, y2, ws2, S, 1.0, 2.0, h=h2)
+    y3 = bf16_to_gpu(c.y)
+    dsl.lora_shrink_expand(xg, Ag, Bg, y3, ws2, S, 1.0, 2.0)
+    # the two schedules explicitly: two launches, and the single launch
+    h4 = t.full((M, r), float("nan"), dtype=t.float32, device="cuda")
+    y4 = bf16_to_gpu(c.y)
+    dsl.lora_shrink_partials(xg, Ag, ws2, S)
+    dsl.lora_expand_combine(ws2, Bg, y4, S, 1.0, 2.0, h=h4, r=r)
+    h5 = t.full((M, r), float("nan"), dtype=t.float32, device="cuda")
+    y5 = bf16_to_gpu(c.y)
+    dsl.lora_shrink_expand_fused(xg, Ag, Bg, y5, S, 1.0, 2.0, h=h5)
+    y6 = bf16_to_gpu(c.y)
+    dsl.lora_shrink_expand_fused(xg, Ag, Bg, y6, S, 1.0, 2.0)
+    t.cuda.synchronize()
+    for hh_ in (h2, h4, h5):
+        assert np.array_equal(f32_bits(h1), f32_bits(hh_))
+    for yy in (y2, y3, y4, y5, y6):
+        assert np.array_equal(bf16_from_gpu(y1), bf16_from_gpu(yy))
+    hh = h2.cpu().numpy()
+    check_shrink(hh, c.x, c.A, 1.0, dsl.lora_shrink_plan(K, r, S), "fused h")
+    yo, e, ab = oracle.expand(hh, c.B, c.y, 2.0)
+    check_expand(bf16_from_gpu(y2), yo, e, ab, c.y, "fused y")
+
+
+def test_graph_capture_replays_match_eager():
+    """The deterministic pipeline captured in a HIP graph: several replays, with
+    eager work and synchronisations in between, each equal to the eager bits."""
+    t = torch()
+    M, K, r, N, S = 64, 4096, 16, 4096, 8
+    c = single_adapter_case(M, K, r, N, seed=12)
+    xg, Ag, Bg = bf16_to_gpu(c.x), bf16_to_gpu(c.A), bf16_to_gpu(c.B)
+    y0 = bf16_to_gpu(c.y)
+    ws = workspace(dsl.lora_shrink_expand_workspace_bytes(M, r, S))
+    wsa = workspace(dsl.lora_shrink_workspace_bytes(M, r, S))
+    h = t.empty((M, r), dtype=t.float32, device="cuda")
+    ha = t.empty((M, r), dtype=t.float32, device="cuda")
+    y = y0.clone()
+    ya = y0.clone()
+
+    def step():
+        y.copy_(y0)
+        dsl.lora_shrink_expand(xg, Ag, Bg, y, ws, S, 1.0, 2.0, h=h)
+        dsl.lora_shrink_splitk(xg, Ag, ha, wsa, S, 1.0)
+        ya.copy_(y0)
+        dsl.lora_expand(ha, Bg, ya, 2.0)
+    step()
+    t.cuda.synchronize()
+    ref = (f32_bits(h), bf16_from_gpu(y), f32_bits(ha), bf16_from_gpu(ya))
+    assert np.array_equal(ref[1], ref[3])
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        step()
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        step()
+    for rep in range(5):
+        h.fill_(float("nan")); y.zero_(); ha.fill_(float("nan")); ya.zero_()
+        junk = t.randn(1 << 20, device="cuda") * 3.0        # eager work between replays
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        got = (f32_bits(h), bf16_from_gpu(y), f32_bits(ha), bf16_from_gpu(ya))
+        for a, b in zip(got, ref):
+            assert np.array_equal(a, b), f"replay {rep}"
+        del junk
+
+
+@pytest.mark.parametrize("S", [1, 2, 4, 8, 16])
+def test_expand_combine_on_given_workspace(S):
+    """lora_expand_combine on a workspace filled with seeded fp32 values of
+    widely spread exponents: h must equal the oracle's fixed pairwise tree
+    (then x shrink_scale) bit for bit, and y the oracle's expand of that h."""
+    t = torch()
+    M, r, N = 45, 24, 520
+    rng = np.random.default_rng(77 + S)
+    P = (rng.uniform(-1, 1, (S, M, r)) * 2.0 ** rng.integers(-30, 30, (S, M, r))).astype(np.float32)
+    B = normal_bf16((N, r), 0.02, S, "cwB")
+    y = normal_bf16((M, N), 1.0, S, "cwy")
+    h = t.full((M, r), float("nan"), dtype=t.float32, device="cuda")
+    yg = bf16_to_gpu(y)
+    dsl.lora_expand_combine(f32_to_gpu(P.reshape(-1)), bf16_to_gpu(B), yg, S, 0.75, 2.0, h=h)
+    t.cuda.synchronize()
+    want_h = oracle.combine_tree_f32(P, 0.75)
+    assert np.array_equal(f32_bits(h), f32_bits_np(want_h))
+    yo, e, ab = oracle.expand(want_h, B, y, 2.0)
+    check_expand(bf16_from_gpu(yg), yo, e, ab, y, f"combine S={S}")
+
+
+@pytest.mark.parametrize("M,K,r,S", [(1, 4096, 16, 8), (33, 8192, 64, 16), (20, 1024, 8, 8)])
+def test_shrink_partials_match_oracle(M, K, r, S):
+    """Each split's fp32 partial P_s (read back from the documented workspace
+    layout) agrees with the oracle's Eq. 3 partial for that chunk."""
+    t = torch()
+    c = single_adapter_case(M, K, r, 0, split_k=S, seed=21)
+    ws = workspace(dsl.lora_shrink_expand_workspace_bytes(M, r, S))
+    dsl.lora_shrink_partials(bf16_to_gpu(c.x), bf16_to_gpu(c.A), ws, S)
+    t.cuda.synchronize()
+    P = ws[: S * M * r * 4].view(t.float32).cpu().numpy().reshape(S, M, r)
+    ref = oracle.split_partials(c.x, c.A, S)
+    plan = dsl.lora_shrink_plan(K, r, S)
+    # per chunk: one matrix-core step per 32 k, k_steps deep, log2(waves)-level tree
+    Kc = K // S
+    xs = oracle.bf16_to_f64(c.x)
+    As = oracle.bf16_to_f64(c.A)
+    for s in range(S):
+        absum = np.abs(xs[:, s * Kc:(s + 1) * Kc]) @ np.abs(As[:, s * Kc:(s + 1) * Kc]).T
+        depth = 32 + plan["k_steps"] + int(np.log2(plan["waves"])) + 1
+        assert np.all(np.abs(P[s] - ref[s]) <= depth * 2.0 ** -24 * absum + 1e-30), f"split {s}"
+
+
+def test_batch_invariance_across_schedule_switch():
+    """A shape whose A is small enough (1024 x 8) for lora_shrink_expand to use
+    the single-launch schedule up to 64 tokens and two launches above: 16
+    probe rows at random positions in batches of 1 .. 512 give the same bits
+    as each other and as lora_shrink_splitk + lora_expand."""
+    t = torch()
+    K, r, N, S, P = 1024, 8, 1024, 8, 16
+    assert dsl.lora_shrink_expand_launches(64, K, r, N, S) == 1
+    assert dsl.lora_shrink_expand_launches(65, K, r, N, S) == 2
+    probe = normal_bf16((P, K), 1.0, 3, "sw_x")
+    A = normal_bf16((r, K), 0.02, 3, "sw_A")
+    B = normal_bf16((N, r), 0.02, 3, "sw_B")
+    ybase = normal_bf16((P, N), 1.0, 3, "sw_y")
+    Ag, Bg = bf16_to_gpu(A), bf16_to_gpu(B)
+    xg0, yg0 = bf16_to_gpu(probe), bf16_to_gpu(ybase)
+    h0 = t.empty((P, r), dtype=t.float32, device="cuda")
+    dsl.lora_shrink_splitk(xg0, Ag, h0, workspace(dsl.lora_shrink_workspace_bytes(P, r, S)), S, 1.0)
+    dsl.lora_expand(h0, Bg, yg0, 2.0)
+    ref_h, ref_y = f32_bits(h0), bf16_from_gpu(yg0)
+    rng = np.random.default_rng(5)
+    for b in [1, 2, 4, 8, 16, 32, 64, 65, 128, 512]:
+        groups = [list(range(i, min(i + b, P))) for i in range(0, P, b)] if b < P else [list(range(P))]
+        for grp in groups:
+            M = max(b, len(grp))
+            x = normal_bf16((M, K), 1.0, 50 + b, "sw_f")
+            y = normal_bf16((M, N), 1.0, 50 + b, "sw_fy")
+            pos = rng.choice(M, size=len(grp), replace=False)
+            x[pos] = probe[grp]
+            y[pos] = ybase[grp]
+            h = t.empty((M, r), dtype=t.float32, device="cuda")
+            yg = bf16_to_gpu(y)
+            dsl.lora_shrink_expand(bf16_to_gpu(x), Ag, Bg, yg, workspace(dsl.lora_shrink_expand_workspace_bytes(M, r, S)),
+                                   S, 1.0, 2.0, h=h)
+            t.cuda.synchronize()
+            assert np.array_equal(f32_bits(h)[pos], ref_h[grp]), f"h at batch {b}"
+            assert np.array_equal(bf16_from_gpu(yg)[pos], ref_y[grp]), f"y at batch {b}"
