@@ -28,7 +28,8 @@ EXPORTED = [
     "lora_shrink_splitk", "lora_shrink_splitk_atomic", "lora_expand", "lora_sgmv_plan_bytes",
     "lora_sgmv_plan", "lora_sgmv_workspace_bytes", "lora_sgmv_shrink", "lora_sgmv_expand",
     "lora_shrink_expand_workspace_bytes", "lora_shrink_expand", "lora_shrink_partials", "lora_expand_combine",
-    "lora_shrink_expand_fused", "lora_shrink_expand_launches",
+    "lora_shrink_expand_fused", "lora_shrink_expand_launches", "lora_shrink_counter_bytes",
+    "lora_shrink_splitk_counted", "lora_sgmv_counter_bytes", "lora_sgmv_shrink_counted",
 ]
 
 
@@ -83,6 +84,16 @@ def lib():
         L.lora_shrink_expand.restype = ctypes.c_int
         L.lora_shrink_expand.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32,
                                          _i64, _i32, _f32, _f32, _vp, _sz, _vp]
+        L.lora_shrink_counter_bytes.restype = _sz
+        L.lora_shrink_counter_bytes.argtypes = [_i64]
+        L.lora_sgmv_counter_bytes.restype = _sz
+        L.lora_sgmv_counter_bytes.argtypes = [_i64]
+        L.lora_shrink_splitk_counted.restype = ctypes.c_int
+        L.lora_shrink_splitk_counted.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32, _i32, _f32,
+                                                 _vp, _sz, _vp, _sz, _vp]
+        L.lora_sgmv_shrink_counted.restype = ctypes.c_int
+        L.lora_sgmv_shrink_counted.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _i32, _vp, _sz, _vp, _i64, _i64,
+                                               _i64, _i32, _i32, _vp, _sz, _vp, _sz, _vp]
         L.lora_shrink_expand_launches.restype = ctypes.c_int
         L.lora_shrink_expand_launches.argtypes = [_i64, _i64, _i32, _i64, _i32]
         L.lora_shrink_expand_fused.restype = ctypes.c_int
@@ -193,6 +204,30 @@ def lora_shrink_splitk(x, A, h, workspace=None, split_k: int = 8, scale: float =
     st = lib().lora_shrink_splitk(_ptr(x), _ld(x, "x"), _ptr(A), _ld(A, "A"), _ptr(h), _ld(h, "h"), M, K, r,
                                   split_k, scale, _ptr(workspace), _nbytes(workspace), _stream(stream, x))
     _check(st, "lora_shrink_splitk")
+    return h
+
+
+def lora_shrink_counter_bytes(M: int) -> int:
+    return int(lib().lora_shrink_counter_bytes(M))
+
+
+def lora_sgmv_counter_bytes(M: int) -> int:
+    return int(lib().lora_sgmv_counter_bytes(M))
+
+
+def lora_shrink_splitk_counted(x, A, h, workspace, counters, split_k: int = 8, scale: float = 1.0, stream=None):
+    """Single-launch deterministic shrink; counters: zero-initialised int32 GPU tensor
+    of lora_shrink_counter_bytes(M) / 4 elements (left zero)."""
+    import torch
+    _dtype(x, torch.bfloat16, "x"); _dtype(A, torch.bfloat16, "A"); _dtype(h, torch.float32, "h")
+    if counters is not None:
+        _dtype(counters, torch.int32, "counters")
+    M, K = x.shape
+    r = A.shape[0]
+    st = lib().lora_shrink_splitk_counted(_ptr(x), _ld(x, "x"), _ptr(A), _ld(A, "A"), _ptr(h), _ld(h, "h"), M, K,
+                                          r, split_k, scale, _ptr(workspace), _nbytes(workspace), _ptr(counters),
+                                          _nbytes(counters), _stream(stream, x))
+    _check(st, "lora_shrink_splitk_counted")
     return h
 
 
@@ -323,6 +358,23 @@ def lora_sgmv_shrink(x, A_ptrs, ld_a: int, ranks, scales, token_adapter, n_adapt
                                 _ptr(token_adapter), n_adapters, _ptr(plan), _nbytes(plan), _ptr(h), _ld(h, "h"),
                                 M, K, r_max, split_k, _ptr(workspace), _nbytes(workspace), _stream(stream, x))
     _check(st, "lora_sgmv_shrink")
+    return h
+
+
+def lora_sgmv_shrink_counted(x, A_ptrs, ld_a: int, ranks, scales, n_adapters: int, plan, h, r_max: int,
+                             split_k: int, workspace, counters, stream=None):
+    import torch
+    _dtype(x, torch.bfloat16, "x"); _dtype(h, torch.float32, "h")
+    _dtype(A_ptrs, torch.int64, "A_ptrs"); _dtype(ranks, torch.int32, "ranks")
+    _dtype(counters, torch.int32, "counters")
+    if scales is not None:
+        _dtype(scales, torch.float32, "scales")
+    M, K = x.shape
+    st = lib().lora_sgmv_shrink_counted(_ptr(x), _ld(x, "x"), _ptr(A_ptrs), ld_a, _ptr(ranks), _ptr(scales),
+                                        n_adapters, _ptr(plan), _nbytes(plan), _ptr(h), _ld(h, "h"), M, K, r_max,
+                                        split_k, _ptr(workspace), _nbytes(workspace), _ptr(counters),
+                                        _nbytes(counters), _stream(stream, x))
+    _check(st, "lora_sgmv_shrink_counted")
     return h
 
 

@@ -12,6 +12,7 @@ using namespace lora;
 namespace {
 
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
+constexpr int64_t kMaxGrid = (int64_t{1} << 31) - 1;     // workgroups of a 1-D launch
 
 bool aligned16(const void* p)
 {
@@ -51,6 +52,38 @@ int make_plan(int64_t K, int32_t r, int32_t split_k, lora_shrink_plan_t* pl)
     return LORA_OK;
 }
 
+// Rank tiles per shrink workgroup.  Per-element arithmetic does not depend on
+// it; small calls give every 16-wide rank tile its own workgroup (more loads in
+// flight across the chip), large ones keep a row block's rank tiles together
+// so its x rows are read once.
+int group_tiles_for(int64_t M, int32_t split_k, int rank_tiles)
+{
+    const int64_t wgs = ((M + kRowBlock - 1) / kRowBlock) * split_k * rank_tiles;
+    return wgs <= 2048 ? 1 : rank_tiles;
+}
+
+// Multi-adapter: 1 or 4 rank tiles per workgroup, by the same rule with M
+// standing in for the (device-side) tile count.
+int sgmv_group_tiles(int64_t M, int32_t split_k, int32_t r_max)
+{
+    return group_tiles_for(M, split_k, (r_max + 15) / 16) == 1 ? 1 : kMaxRankTiles;
+}
+
+// Persistent grid: never more workgroups than items can exist (tiles <= M).
+// Work items of the multi-adapter kernels are counted in 32 bits.
+bool sgmv_items_fit(int64_t M, int32_t split_k, int64_t N)
+{
+    const int64_t nblocks = (N + kExpandCols - 1) / kExpandCols;
+    return M * split_k * kMaxRankTiles <= kMaxGrid && M * nblocks <= kMaxGrid;
+}
+
+int sgmv_grid(int64_t M, int32_t split_k, int32_t r_max, int group_tiles)
+{
+    const int64_t groups = ((r_max + 15) / 16 + group_tiles - 1) / group_tiles;
+    const int64_t bound = M * split_k * groups;
+    return (int)(bound < 4096 ? bound : 4096);
+}
+
 int launch_status(hipError_t e)
 {
     return e == hipSuccess ? LORA_OK : LORA_ERR_LAUNCH;
@@ -65,6 +98,8 @@ int check_shrink(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_
     int st = make_plan(K, r, split_k, pl);
     if (st != LORA_OK)
         return st;
+    if (((M + kRowBlock - 1) / kRowBlock) * split_k * pl->rank_tiles > kMaxGrid)
+        return LORA_ERR_SHAPE;
     if (M == 0)
         return LORA_OK;
     if (!x || !A || !h)
@@ -113,7 +148,8 @@ int check_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* A, int6
         return st;
     if (N % 8 != 0)
         return LORA_ERR_UNSUPPORTED;
-    if ((N + kExpandCols - 1) / kExpandCols > 65535 || (M + kRowBlock - 1) / kRowBlock > 0x7FFFFFFF)
+    if (((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols) > kMaxGrid ||
+        ((M + kRowBlock - 1) / kRowBlock) * split_k * pl->rank_tiles > kMaxGrid)
         return LORA_ERR_SHAPE;
     if (M == 0 || N == 0)
         return LORA_OK;
@@ -218,7 +254,7 @@ int lora_shrink_splitk(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64
     if (split_k == 1) {
         p.out = h;
         p.ld_out = ld_h;
-        return launch_status(launch_shrink_partial_direct(p, pl.waves, pl.rank_tiles, s));
+        return launch_status(launch_shrink_partial_direct(p, pl.waves, pl.rank_tiles, group_tiles_for(M, split_k, pl.rank_tiles), s));
     }
     const size_t need = lora_shrink_workspace_bytes(M, r, split_k);
     if (!workspace)
@@ -230,7 +266,7 @@ int lora_shrink_splitk(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64
     p.out = static_cast<float*>(workspace);
     p.ld_out = r;
     p.split_stride = M * r;
-    st = launch_status(launch_shrink_partial_ws(p, pl.waves, pl.rank_tiles, s));
+    st = launch_status(launch_shrink_partial_ws(p, pl.waves, pl.rank_tiles, group_tiles_for(M, split_k, pl.rank_tiles), s));
     if (st != LORA_OK)
         return st;
     TreeParams t{};
@@ -260,7 +296,7 @@ int lora_shrink_splitk_atomic(const uint16_t* x, int64_t ld_x, const uint16_t* A
     ShrinkParams p = shrink_params(x, ld_x, A, ld_a, M, r, pl, scale);
     p.out = h;
     p.ld_out = ld_h;
-    return launch_status(launch_shrink_partial_atomic(p, pl.waves, pl.rank_tiles, s));
+    return launch_status(launch_shrink_partial_atomic(p, pl.waves, pl.rank_tiles, group_tiles_for(M, split_k, pl.rank_tiles), s));
 }
 
 int lora_expand(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b, uint16_t* y, int64_t ld_y,
@@ -272,7 +308,7 @@ int lora_expand(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b, u
         return LORA_ERR_UNSUPPORTED;
     if (N % 8 != 0)
         return LORA_ERR_UNSUPPORTED;
-    if ((M + kRowBlock - 1) / kRowBlock > 0x7FFFFFFF || (N + kExpandCols - 1) / kExpandCols > 65535)
+    if (((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols) > kMaxGrid)
         return LORA_ERR_SHAPE;
     if (M == 0 || N == 0)
         return LORA_OK;
@@ -311,6 +347,8 @@ int lora_shrink_partials(const uint16_t* x, int64_t ld_x, const uint16_t* A, int
     int st = make_plan(K, r, split_k, &pl);
     if (st != LORA_OK)
         return st;
+    if (((M + kRowBlock - 1) / kRowBlock) * split_k * pl.rank_tiles > kMaxGrid)
+        return LORA_ERR_SHAPE;
     if (M == 0)
         return LORA_OK;
     if (!x || !A || !workspace)
@@ -325,7 +363,8 @@ int lora_shrink_partials(const uint16_t* x, int64_t ld_x, const uint16_t* A, int
     sp.out = static_cast<float*>(workspace);
     sp.ld_out = r;
     sp.split_stride = M * r;
-    return launch_status(launch_shrink_partial_ws(sp, pl.waves, pl.rank_tiles, static_cast<hipStream_t>(stream)));
+    return launch_status(launch_shrink_partial_ws(sp, pl.waves, pl.rank_tiles, group_tiles_for(M, split_k, pl.rank_tiles),
+                                                          static_cast<hipStream_t>(stream)));
 }
 
 int lora_expand_combine(const void* workspace, size_t ws_bytes, int32_t split_k, float shrink_scale,
@@ -336,7 +375,7 @@ int lora_expand_combine(const void* workspace, size_t ws_bytes, int32_t split_k,
         return LORA_ERR_SHAPE;
     if (!split_ok(split_k) || r < 1 || r > 64 || N % 8 != 0)
         return LORA_ERR_UNSUPPORTED;
-    if ((N + kExpandCols - 1) / kExpandCols > 65535)
+    if (((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols) > kMaxGrid)
         return LORA_ERR_SHAPE;
     if (M == 0 || N == 0)
         return LORA_OK;
@@ -408,7 +447,7 @@ int lora_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64
         return st;
     if (N % 8 != 0)
         return LORA_ERR_UNSUPPORTED;
-    if ((N + kExpandCols - 1) / kExpandCols > 65535)
+    if (((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols) > kMaxGrid)
         return LORA_ERR_SHAPE;
     if (M == 0 || N == 0)
         return LORA_OK;
@@ -430,6 +469,106 @@ int lora_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64
         return st;
     return lora_expand_combine(workspace, ws_bytes, split_k, shrink_scale, B, ld_b, h, ld_h, y, ld_y, M, r, N,
                                expand_scale, stream);
+}
+
+size_t lora_shrink_counter_bytes(int64_t M)
+{
+    if (M < 0 || M > kMaxDim)
+        return 0;
+    return (size_t)4 * kMaxRankTiles * (size_t)((M + kRowBlock - 1) / kRowBlock);
+}
+
+int lora_shrink_splitk_counted(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a, float* h,
+                               int64_t ld_h, int64_t M, int64_t K, int32_t r, int32_t split_k, float scale,
+                               void* workspace, size_t ws_bytes, int32_t* counters, size_t counter_bytes,
+                               void* stream)
+{
+    lora_shrink_plan_t pl;
+    int st = check_shrink(x, ld_x, A, ld_a, h, ld_h, M, K, r, split_k, &pl);
+    if (st != LORA_OK || M == 0)
+        return st;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    ShrinkParams p = shrink_params(x, ld_x, A, ld_a, M, r, pl, scale);
+    if (split_k == 1) {                         // one split: it is its own last arrival
+        p.out = h;
+        p.ld_out = ld_h;
+        return launch_status(launch_shrink_partial_direct(p, pl.waves, pl.rank_tiles, group_tiles_for(M, split_k, pl.rank_tiles), s));
+    }
+    if (!workspace || !counters)
+        return LORA_ERR_NULL;
+    if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(counters) & 3u))
+        return LORA_ERR_ALIGN;
+    if (ws_bytes < workspace_bytes(M, r, split_k) || counter_bytes < lora_shrink_counter_bytes(M))
+        return LORA_ERR_WORKSPACE;
+    p.out = static_cast<float*>(workspace);
+    p.ld_out = r;
+    p.split_stride = M * r;
+    CounterParams c{};
+    c.counters = counters;
+    c.h = h;
+    c.ld_h = ld_h;
+    return launch_status(launch_shrink_counted(p, c, pl.waves, pl.rank_tiles, group_tiles_for(M, split_k, pl.rank_tiles), s));
+}
+
+size_t lora_sgmv_counter_bytes(int64_t M)
+{
+    if (M < 0 || M > kMaxDim)
+        return 0;
+    return (size_t)4 * kMaxRankTiles * (size_t)(M > 0 ? M : 1);
+}
+
+int lora_sgmv_shrink_counted(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_ptrs, int64_t ld_a,
+                             const int32_t* ranks, const float* scales, int32_t n_adapters, const void* plan,
+                             size_t plan_bytes, float* h, int64_t ld_h, int64_t M, int64_t K, int32_t r_max,
+                             int32_t split_k, void* workspace, size_t ws_bytes, int32_t* counters,
+                             size_t counter_bytes, void* stream)
+{
+    if (M < 0 || M > kMaxDim || n_adapters < 1)
+        return LORA_ERR_SHAPE;
+    lora_shrink_plan_t pl;
+    int st = make_plan(K, r_max, split_k, &pl);
+    if (st != LORA_OK)
+        return st;
+    if (!sgmv_items_fit(M, split_k, 0))
+        return LORA_ERR_SHAPE;
+    if (M == 0)
+        return LORA_OK;
+    if (!x || !A_ptrs || !ranks || !plan || !h || !workspace || !counters)
+        return LORA_ERR_NULL;
+    if (ld_x < K || ld_a < K || ld_h < r_max)
+        return LORA_ERR_SHAPE;
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(h) & 3u) || !aligned16(plan) || !aligned16(workspace) ||
+        (reinterpret_cast<uintptr_t>(counters) & 3u) || ld_x % 8 || ld_a % 8)
+        return LORA_ERR_ALIGN;
+    if (plan_bytes < lora_sgmv_plan_bytes(M) || ws_bytes < workspace_bytes(M, r_max, split_k) ||
+        counter_bytes < lora_sgmv_counter_bytes(M))
+        return LORA_ERR_WORKSPACE;
+    ShrinkParams p{};
+    p.x = x;
+    p.ld_x = ld_x;
+    p.ld_a = ld_a;
+    p.A_ptrs = A_ptrs;
+    p.ranks = ranks;
+    p.tiles = static_cast<const int32_t*>(plan);
+    p.out = static_cast<float*>(workspace);
+    p.ld_out = r_max;
+    p.split_stride = M * r_max;
+    p.M = M;
+    p.r = r_max;
+    p.r_max = r_max;
+    p.k_chunk = pl.k_chunk;
+    p.k_steps = pl.k_steps;
+    p.split_k = split_k;
+    p.n_adapters = n_adapters;
+    p.scale = 1.0f;
+    CounterParams c{};
+    c.counters = counters;
+    c.h = h;
+    c.ld_h = ld_h;
+    c.scales = scales;
+    const int gt = sgmv_group_tiles(M, split_k, r_max);
+    const int grid = sgmv_grid(M, split_k, r_max, gt);
+    return launch_status(launch_sgmv_shrink_counted(p, c, pl.waves, gt, grid, static_cast<hipStream_t>(stream)));
 }
 
 size_t lora_sgmv_plan_bytes(int64_t M)
@@ -474,6 +613,8 @@ int lora_sgmv_shrink(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_p
     int st = make_plan(K, r_max, split_k, &pl);
     if (st != LORA_OK)
         return st;
+    if (!sgmv_items_fit(M, split_k, 0))
+        return LORA_ERR_SHAPE;
     if (M == 0)
         return LORA_OK;
     if (!x || !A_ptrs || !ranks || !token_adapter || !plan || !h || !workspace)
@@ -505,9 +646,9 @@ int lora_sgmv_shrink(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_p
     p.n_adapters = n_adapters;
     p.scale = 1.0f;
     // Tiles never exceed M; the grid is a fixed bound, idle workgroups exit.
-    const int64_t items_bound = M * split_k;
-    const int grid = (int)(items_bound < 2048 ? items_bound : 2048);
-    st = launch_status(launch_sgmv_shrink_partial(p, pl.waves, grid, s));
+    const int gt = sgmv_group_tiles(M, split_k, r_max);
+    const int grid = sgmv_grid(M, split_k, r_max, gt);
+    st = launch_status(launch_sgmv_shrink_partial(p, pl.waves, gt, grid, s));
     if (st != LORA_OK)
         return st;
     TreeParams t{};
@@ -534,6 +675,8 @@ int lora_sgmv_expand(const float* h, int64_t ld_h, const uint16_t* const* B_ptrs
         return LORA_ERR_SHAPE;
     if (r_max < 1 || r_max > 64 || N % 8 != 0)
         return LORA_ERR_UNSUPPORTED;
+    if (!sgmv_items_fit(M, 1, N))
+        return LORA_ERR_SHAPE;
     if (M == 0 || N == 0)
         return LORA_OK;
     if (!h || !B_ptrs || !ranks || !plan || !y)

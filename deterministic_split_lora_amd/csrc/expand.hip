@@ -25,14 +25,34 @@ namespace lora {
 
 namespace {
 
-// Single adapter: grid (ceil(M/16), ceil(N/256)), 4 waves of 64 columns.
+// (row block, column block) of a 1-D grid, column block fastest: consecutive
+// workgroups, which land on different XCDs, cover adjacent stretches of the
+// same y rows.
+struct ExpandItem {
+    int64_t row0;
+    int64_t cb;
+    int nrows;
+};
+
+__device__ __forceinline__ ExpandItem expand_item(int64_t M, int64_t N)
+{
+    ExpandItem q;                                 // 32-bit: the grid is below 2^31
+    const uint32_t nblocks = (uint32_t)((N + kExpandCols - 1) / kExpandCols);
+    q.cb = blockIdx.x % nblocks;
+    q.row0 = (int64_t)(blockIdx.x / nblocks) * kRowBlock;
+    const int64_t left = M - q.row0;
+    q.nrows = left < kRowBlock ? (int)left : kRowBlock;
+    return q;
+}
+
+// Single adapter: 4 waves of 64 columns per workgroup.
 template <int KS>
 __global__ __launch_bounds__(256) void k_expand(ExpandParams p)
 {
-    const int64_t row0 = (int64_t)blockIdx.x * kRowBlock;
-    const int64_t left = p.M - row0;
-    const int nrows = left < kRowBlock ? (int)left : kRowBlock;
-    ExpandLane L = expand_lane(row0, nrows, (int64_t)blockIdx.y * kExpandCols);
+    const ExpandItem q = expand_item(p.M, p.N);
+    const int64_t row0 = q.row0;
+    const int nrows = q.nrows;
+    ExpandLane L = expand_lane(row0, nrows, q.cb * kExpandCols);
     if (L.n_base >= p.N)
         return;
     u16x8 yv[2];
@@ -52,18 +72,18 @@ template <int KS, int S>
 __global__ __launch_bounds__(256) void k_expand_combine(ExpandParams p, TreeParams c)
 {
     __shared__ __align__(16) float hs[kRowBlock * kHTileStride];
-    const int64_t row0 = (int64_t)blockIdx.x * kRowBlock;
-    const int64_t left = p.M - row0;
-    const int nrows = left < kRowBlock ? (int)left : kRowBlock;
+    const ExpandItem q = expand_item(p.M, p.N);
+    const int64_t row0 = q.row0;
+    const int nrows = q.nrows;
     const int r = p.r;
     // y and B first: they do not depend on the workspace
-    ExpandLane L = expand_lane(row0, nrows, (int64_t)blockIdx.y * kExpandCols);
+    ExpandLane L = expand_lane(row0, nrows, q.cb * kExpandCols);
     const bool active = L.n_base < p.N;
     u16x8 yv[2];
     bf16x8 bop[4][KS];
     if (active)
         expand_load<KS>(L, p.y, p.ld_y, p.N, p.B, p.ld_b, r, yv, bop);
-    const bool write_h = c.h != nullptr && blockIdx.y == 0;
+    const bool write_h = c.h != nullptr && q.cb == 0;
     for (int e = threadIdx.x; e < kRowBlock * r; e += 256) {
         const int row = e / r;
         const int col = e - row * r;
@@ -89,11 +109,11 @@ __global__ __launch_bounds__(256) void k_expand_combine(ExpandParams p, TreePara
 __global__ __launch_bounds__(256) void k_sgmv_expand(ExpandParams p)
 {
     const int ntiles = plan_tiles(p.tiles, p.M, p.n_adapters);
-    const int64_t nblocks = (p.N + kExpandCols - 1) / kExpandCols;
-    const int64_t items = (int64_t)ntiles * nblocks;
-    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const uint32_t nblocks = (uint32_t)((p.N + kExpandCols - 1) / kExpandCols);
+    const uint32_t items = (uint32_t)ntiles * nblocks;
+    for (uint32_t it = blockIdx.x; it < items; it += gridDim.x) {
         const int tile = (int)(it / nblocks);
-        const int64_t cb = it - (int64_t)tile * nblocks;
+        const int64_t cb = it - (uint32_t)tile * nblocks;
         const int32_t* t = p.tiles + kPlanHeaderInts + 3 * tile;
         if (!tile_ok(t, p.M, p.n_adapters))
             continue;
@@ -121,9 +141,14 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(ExpandParams p)
 
 }  // namespace
 
+inline dim3 expand_grid(int64_t M, int64_t N)
+{
+    return dim3((unsigned)(((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols)));
+}
+
 hipError_t launch_expand(const ExpandParams& p, hipStream_t st)
 {
-    dim3 grid((unsigned)((p.M + kRowBlock - 1) / kRowBlock), (unsigned)((p.N + kExpandCols - 1) / kExpandCols));
+    const dim3 grid = expand_grid(p.M, p.N);
     dim3 block(256);
     if (p.r > 32)
         hipLaunchKernelGGL(k_expand<2>, grid, block, 0, st, p);
@@ -147,7 +172,7 @@ hipError_t launch_expand_combine_ks(const ExpandParams& p, const TreeParams& c, 
 
 hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st)
 {
-    dim3 grid((unsigned)((p.M + kRowBlock - 1) / kRowBlock), (unsigned)((p.N + kExpandCols - 1) / kExpandCols));
+    const dim3 grid = expand_grid(p.M, p.N);
     return p.r > 32 ? launch_expand_combine_ks<2>(p, c, split_k, grid, st)
                     : launch_expand_combine_ks<1>(p, c, split_k, grid, st);
 }

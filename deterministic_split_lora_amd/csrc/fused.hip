@@ -182,14 +182,17 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_shrink_expand_fused(FusedP
     const int li = lane & 15;
     const int g = lane >> 4;
     const int r = p.r;
-    const int64_t row0 = (int64_t)blockIdx.x * kRowBlock;
+    // 1-D grid, column block fastest (see the expand kernels)
+    const uint32_t nblocks = (uint32_t)((p.N + kFusedCols - 1) / kFusedCols);
+    const int64_t cb = blockIdx.x % nblocks;
+    const int64_t row0 = (int64_t)(blockIdx.x / nblocks) * kRowBlock;
     const int64_t left = p.M - row0;
     const int nrows = left < kRowBlock ? (int)left : kRowBlock;
     const bool row_ok = li < nrows;
     const int64_t row = row0 + (row_ok ? li : 0);
 
     // ---- expand operands first: y and B do not depend on the shrink -------
-    ExpandLane L = expand_lane(row0, nrows, (int64_t)blockIdx.y * kFusedCols);
+    ExpandLane L = expand_lane(row0, nrows, cb * kFusedCols);
     const bool cols_ok = L.n_base < p.N;
     u16x8 yv[2];
     bf16x8 bop[4][KS];
@@ -222,7 +225,7 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_shrink_expand_fused(FusedP
 
     // ---- pairwise tree over the S split partials, times the shrink scale --
     const int ncols = r < 16 * RTMAX ? r : 16 * RTMAX;
-    const bool write_h = p.h != nullptr && blockIdx.y == 0;
+    const bool write_h = p.h != nullptr && cb == 0;
     for (int e = threadIdx.x; e < 16 * ncols; e += kFusedWaves * 64) {
         const int rr = e / ncols;
         const int cc = e - rr * ncols;
@@ -272,7 +275,7 @@ hipError_t launch_rt(const FusedParams& p, int split_k, int waves, dim3 grid, hi
 
 hipError_t launch_shrink_expand_fused(const FusedParams& p, int split_k, int waves, hipStream_t st)
 {
-    dim3 grid((unsigned)((p.M + kRowBlock - 1) / kRowBlock), (unsigned)((p.N + kFusedCols - 1) / kFusedCols));
+    dim3 grid((unsigned)(((p.M + kRowBlock - 1) / kRowBlock) * ((p.N + kFusedCols - 1) / kFusedCols)));
     return p.r > 32 ? launch_rt<4>(p, split_k, waves, grid, st) : launch_rt<2>(p, split_k, waves, grid, st);
 }
 

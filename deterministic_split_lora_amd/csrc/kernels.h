@@ -7,9 +7,11 @@
 namespace lora {
 
 constexpr int kRowBlock = 16;                // tokens per matrix-core tile
+constexpr int kMaxRankTiles = 4;             // 16-wide rank tiles of a rank <= 64
 
 // Plan buffer: int32 header [ntiles, M, n_adapters, magic], then ntiles
-// triples (first token, token count 1..16, adapter id).
+// triples (first token, token count 1..16, adapter id or -1 for tokens
+// without an adapter).
 constexpr int kPlanHeaderInts = 4;
 constexpr int32_t kPlanMagic = 0x4C6F5241;   // "LoRA"
 
@@ -79,12 +81,26 @@ __device__ __forceinline__ int plan_tiles(const int32_t* plan, int64_t M, int32_
     return n < 0 ? 0 : (n > M ? (int)M : n);
 }
 
-// A tile entry is used only if it lies inside [0, M) and names a valid adapter.
+// A tile entry covers 1..16 rows inside [0, M) ...
+__device__ __forceinline__ bool tile_rows_ok(const int32_t* t, int64_t M)
+{
+    return t[0] >= 0 && t[1] >= 1 && t[1] <= kRowBlock && (int64_t)t[0] + t[1] <= M;
+}
+
+// ... and is computed on only if it also names a valid adapter (tiles of
+// tokens without an adapter carry -1).
 __device__ __forceinline__ bool tile_ok(const int32_t* t, int64_t M, int32_t n_adapters)
 {
-    return t[0] >= 0 && t[1] >= 1 && t[1] <= kRowBlock && (int64_t)t[0] + t[1] <= M && t[2] >= 0 &&
-           t[2] < n_adapters;
+    return tile_rows_ok(t, M) && t[2] >= 0 && t[2] < n_adapters;
 }
+
+// Single-launch shrink: the per-tile arrival counters and the h it writes.
+struct CounterParams {
+    int32_t* counters;              // kMaxRankTiles per row block / plan tile, 0 between calls
+    float* h;
+    int64_t ld_h;
+    const float* scales;            // sgmv (may be null: 1)
+};
 
 struct FusedParams {
     const uint16_t* x;
@@ -106,10 +122,18 @@ struct FusedParams {
     float expand_scale;
 };
 
-hipError_t launch_shrink_partial_ws(const ShrinkParams& p, int waves, int rank_tiles, hipStream_t st);
-hipError_t launch_shrink_partial_direct(const ShrinkParams& p, int waves, int rank_tiles, hipStream_t st);
-hipError_t launch_shrink_partial_atomic(const ShrinkParams& p, int waves, int rank_tiles, hipStream_t st);
-hipError_t launch_sgmv_shrink_partial(const ShrinkParams& p, int waves, int grid, hipStream_t st);
+// group_tiles: rank tiles per workgroup (1 .. rank_tiles; the sgmv kernels take 1 or 4).
+hipError_t launch_shrink_partial_ws(const ShrinkParams& p, int waves, int rank_tiles, int group_tiles,
+                                    hipStream_t st);
+hipError_t launch_shrink_partial_direct(const ShrinkParams& p, int waves, int rank_tiles, int group_tiles,
+                                        hipStream_t st);
+hipError_t launch_shrink_partial_atomic(const ShrinkParams& p, int waves, int rank_tiles, int group_tiles,
+                                        hipStream_t st);
+hipError_t launch_sgmv_shrink_partial(const ShrinkParams& p, int waves, int group_tiles, int grid, hipStream_t st);
+hipError_t launch_shrink_counted(const ShrinkParams& p, const CounterParams& c, int waves, int rank_tiles,
+                                 int group_tiles, hipStream_t st);
+hipError_t launch_sgmv_shrink_counted(const ShrinkParams& p, const CounterParams& c, int waves, int group_tiles,
+                                      int grid, hipStream_t st);
 hipError_t launch_splitk_tree(const TreeParams& p, int split_k, bool sgmv, hipStream_t st);
 hipError_t launch_fill_zero(float* h, int64_t ld_h, int64_t M, int ncols, hipStream_t st);
 

@@ -5,7 +5,8 @@
 // adapter for all its tokens, so the ids are turned into tiles of at most 16
 // consecutive tokens with equal id: a run of L tokens becomes ceil(L/16)
 // tiles starting at run offsets 0, 16, 32, ...; runs of ids outside
-// [0, n_adapters) produce no tile.  Tiles are listed in token order.
+// [0, n_adapters) become tiles with adapter -1, which the shrinks zero and
+// everything else skips.  Tiles are listed in token order.
 //
 // One workgroup of 1024 threads walks the ids in chunks of 1024.  Per chunk:
 // a run starts at token i when its id differs from token i-1's; an inclusive
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_sgmv_plan(const int32_t* __res
         }
         start = start > v ? start : v;
 
-        const bool opens = in && a >= 0 && ((i - start) % kRowBlock == 0);
+        const bool opens = in && ((i - start) % kRowBlock == 0);
         const int c = opens ? 1 : 0;
         int incl = c;
 #pragma unroll

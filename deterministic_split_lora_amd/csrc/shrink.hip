@@ -2,20 +2,23 @@
 //
 // The shrink h = x A^T (paper Eq. 1) is a narrow GEMM: K = hidden size is long,
 // r <= 64 is short.  Split-K (section 2.1, Eq. 3) cuts K into S contiguous
-// chunks so S workgroups share one output tile.  One workgroup owns one
-// (16-token row block, split) pair and W wavefronts; wave w walks
-// k_steps * 32 consecutive k of the split's chunk with matrix-core steps, the
-// bf16 operands streamed straight from HBM into registers with 16-byte loads
-// (x rows and A rows are both k-contiguous, which is exactly the per-lane
-// operand layout, so no LDS transpose is needed and every byte is loaded once
-// per workgroup).  The W wave results meet in LDS and are added along a fixed
-// pairwise tree.  The split's fp32 partial then goes to the workspace
-// (deterministic path), straight to h (split_k == 1), or is atomically added
-// to h (the nondeterministic contrast of section 4.1).
+// chunks so S workgroups share one output tile.  A workgroup owns one
+// (16-token row block, split, group of RT 16-wide rank tiles) and W
+// wavefronts; wave w walks k_steps * 32 consecutive k of the split's chunk
+// with matrix-core steps, the bf16 operands streamed straight from HBM into
+// registers with 16-byte loads (x rows and A rows are both k-contiguous, which
+// is exactly the per-lane operand layout, so no LDS transpose is needed).  The
+// W wave results meet in LDS and are added along a fixed pairwise tree.  The
+// split's fp32 partial then goes to the workspace (deterministic paths),
+// straight to h (split_k == 1), or is atomically added to h (the
+// nondeterministic contrast of section 4.1).
 //
 // Every element's arithmetic - which k each matrix-core step covers, the step
-// order, the wave tree, the split tree - is fixed by (K, split_k) alone, so a
-// token's bits do not depend on M or on its neighbours in the batch.
+// order, the wave tree, the split tree - is fixed by (K, split_k) alone, and
+// each rank column's chain is independent of the others, so neither M, a
+// token's neighbours, nor how rank tiles are grouped into workgroups changes a
+// single bit.  Small calls spread their rank tiles over more workgroups (more
+// memory parallelism); large calls keep them together (x is read once).
 #include "device.h"
 #include "kernels.h"
 
@@ -23,16 +26,30 @@ namespace lora {
 
 namespace {
 
-enum ShrinkMode { kToWorkspace = 0, kToOutputScaled = 1, kAtomicScaled = 2 };
+enum ShrinkMode { kToWorkspace = 0, kToOutputScaled = 1, kAtomicScaled = 2, kToWorkspaceCoherent = 3 };
+
+// Agent-scope atomic store / load: performed at the device-wide coherence
+// point, past the per-XCD L2 caches (used for the single-launch combine).
+__device__ __forceinline__ void store_coherent(float* p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_coherent(const float* p)
+{
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // Output element (row, col) of the tile: write / atomically add.
 template <int MODE>
-__device__ __forceinline__ void shrink_store(const ShrinkParams& p, int64_t row0, int s, int row,
-                                             int col, float v, float scale)
+__device__ __forceinline__ void shrink_store(const ShrinkParams& p, int64_t row0, int s, int row, int col, float v,
+                                             float scale)
 {
     const int64_t rr = row0 + row;
     if (MODE == kToWorkspace) {
         p.out[(int64_t)s * p.split_stride + rr * p.ld_out + col] = v;
+    } else if (MODE == kToWorkspaceCoherent) {
+        store_coherent(&p.out[(int64_t)s * p.split_stride + rr * p.ld_out + col], v);
     } else if (MODE == kToOutputScaled) {
         p.out[rr * p.ld_out + col] = __fmul_rn(v, scale);
     } else {
@@ -40,18 +57,19 @@ __device__ __forceinline__ void shrink_store(const ShrinkParams& p, int64_t row0
     }
 }
 
-// One (row block, split) work item.  RT = number of 16-wide rank tiles the
-// kernel is built for; r <= 16 * RT is the rank actually used.
+// One work item: rows row0 .. row0+nrows-1, split s, rank columns col0 ..
+// col0 + 16 RT - 1 (those below r).  A is the adapter's row 0.
 template <int RT, int W, int MODE>
 __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0, int nrows,
-                                            const uint16_t* __restrict__ A, int r, int s,
-                                            float scale, float* red)
+                                            const uint16_t* __restrict__ A, int r, int col0, int s, float scale,
+                                            float* red)
 {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int li = lane & 15;
     const int g = lane >> 4;
     const int steps = p.k_steps;
+    const int rg = r - col0;                 // rank columns left from col0
 
     // Reduction slots 8g..8g+7 of step t hold k = kbase + 32 t + (0..7).
     const int64_t kbase = (int64_t)s * p.k_chunk + (int64_t)wave * steps * kKStep + g * 8;
@@ -62,8 +80,8 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0,
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int j = rt * 16 + li;
-        a_ok[rt] = j < r;
-        ap[rt] = A + (int64_t)(a_ok[rt] ? j : 0) * p.ld_a + kbase;
+        a_ok[rt] = j < rg;
+        ap[rt] = A + (int64_t)(col0 + (a_ok[rt] ? j : 0)) * p.ld_a + kbase;
     }
 
     f32x4 acc[RT];
@@ -83,7 +101,7 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0,
                 xa[u] = row_ok ? load_bf16x8(xp + off) : bf16x8_zero();
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
-                    b[u][rt] = (rt * 16 < r && a_ok[rt]) ? load_bf16x8(ap[rt] + off) : bf16x8_zero();
+                    b[u][rt] = (rt * 16 < rg && a_ok[rt]) ? load_bf16x8(ap[rt] + off) : bf16x8_zero();
             }
         }
 #pragma unroll
@@ -91,21 +109,21 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0,
             if (t0 + u < steps) {
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
-                    if (rt * 16 < r)
+                    if (rt * 16 < rg)
                         acc[rt] = mfma_16x16x32(xa[u], b[u][rt], acc[rt]);
             }
         }
     }
 
-    // acc[rt][v] is the wave's sum for token row 4g+v, rank column 16 rt + li.
+    // acc[rt][v] is the wave's sum for token row 4g+v, rank column col0 + 16 rt + li.
     if constexpr (W == 1) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int row = 4 * g + v, col = rt * 16 + li;
-                if (row < nrows && col < r)
-                    shrink_store<MODE>(p, row0, s, row, col, acc[rt][v], scale);
+                if (row < nrows && col < rg)
+                    shrink_store<MODE>(p, row0, s, row, col0 + col, acc[rt][v], scale);
             }
     } else {
         constexpr int RS = 16 * RT + 4;          // padded LDS row stride (floats)
@@ -115,7 +133,7 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0,
             for (int v = 0; v < 4; ++v)
                 red[(wave * 16 + 4 * g + v) * RS + rt * 16 + li] = acc[rt][v];
         __syncthreads();
-        const int ncols = r < 16 * RT ? r : 16 * RT;
+        const int ncols = rg < 16 * RT ? rg : 16 * RT;
         for (int e = threadIdx.x; e < 16 * 16 * RT; e += W * kWave) {
             const int row = e / (16 * RT);
             const int col = e - row * (16 * RT);
@@ -124,7 +142,7 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0,
 #pragma unroll
                 for (int w = 0; w < W; ++w)
                     v[w] = red[(w * 16 + row) * RS + col];
-                shrink_store<MODE>(p, row0, s, row, col, pairwise_tree<W>(v), scale);
+                shrink_store<MODE>(p, row0, s, row, col0 + col, pairwise_tree<W>(v), scale);
             }
         }
         __syncthreads();                          // LDS is reused by the next item
@@ -137,43 +155,230 @@ constexpr int red_floats()
     return W > 1 ? W * 16 * (16 * RT + 4) : 1;
 }
 
-// Single adapter: grid (ceil(M/16), split_k), W waves.
-template <int RT, int W, int MODE>
-__global__ __launch_bounds__(W * 64) void k_shrink_partial(ShrinkParams p)
+// ---------------------------------------------------------------------------
+// Single-launch combine (the completion-counter protocol of the paper's
+// section 4.3 / Alg. 1, with the pairwise tree of the two-pass path as the
+// fixed order).
+//
+// The XCDs of an MI355X each have their own L2, so a partial written by one
+// workgroup must reach the device-wide coherence point before another XCD can
+// read it.  A release fence at agent scope would write back this XCD's entire
+// L2 and an acquire would invalidate it - costly at one pair per workgroup.
+// Instead the partials are moved with agent-scope atomic stores and loads,
+// which the hardware performs at the agent coherence point, and ordering is
+// enforced where the fence would enforce it:
+//   writer: agent-scope stores of its partial; wait until every one of them
+//           has completed (s_waitcnt 0); workgroup barrier; one thread adds 1
+//           to the tile's counter (agent-scope integer atomic).
+//   reader: the workgroup whose add returned split_k - 1 arrived last; only
+//           then does it load the S partials (agent-scope loads), evaluate the
+//           same pairwise tree and multiply as the second-pass kernel, write h
+//           and put the counter back to 0 for the next call.
+// Integer atomics only order the arrivals; the floating-point sum has one
+// fixed order whichever workgroup is last.  No workgroup waits for another.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool arrived_last(int32_t* counter, int split_k, int* flag)
 {
-    __shared__ float red[red_floats<RT, W>()];
-    const int64_t row0 = (int64_t)blockIdx.x * kRowBlock;
-    const int64_t left = p.M - row0;
-    const int nrows = left < kRowBlock ? (int)left : kRowBlock;
-    shrink_tile<RT, W, MODE>(p, row0, nrows, p.A, p.r, (int)blockIdx.y, p.scale, red);
+    __builtin_amdgcn_s_waitcnt(0);            // this thread's partial stores are complete
+    __syncthreads();
+    if (threadIdx.x == 0)
+        *flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    return *flag == split_k - 1;
 }
 
-// Multi-adapter: a fixed grid walks the plan's (tile, split) items with a
-// static stride; every wave of a workgroup sees the same item count and
-// leaves the loop together.
-template <int W>
-__global__ __launch_bounds__(W * 64) void k_sgmv_shrink_partial(ShrinkParams p)
+template <int S>
+__device__ __forceinline__ float tree_of_splits(const float* w, int64_t split_stride)
 {
-    __shared__ float red[red_floats<4, W>()];
-    const int ntiles = plan_tiles(p.tiles, p.M, p.n_adapters);
-    const int S = p.split_k;
-    const int64_t items = (int64_t)ntiles * S;
-    for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-        const int tile = (int)(it / S);
-        const int s = (int)(it - (int64_t)tile * S);
-        const int32_t* t = p.tiles + kPlanHeaderInts + 3 * tile;
-        if (!tile_ok(t, p.M, p.n_adapters))      // uniform across the workgroup
-            continue;
-        const int64_t row0 = t[0];
-        const int nrows = t[1];
-        const int a = t[2];
-        int ra = p.ranks[a];
-        ra = ra < 0 ? 0 : (ra > p.r_max ? p.r_max : ra);
-        shrink_tile<4, W, kToWorkspace>(p, row0, nrows, p.A_ptrs[a], ra, s, 1.0f, red);
+    float v[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+        v[s] = load_coherent(w + (int64_t)s * split_stride);
+    return pairwise_tree<S>(v);
+}
+
+// h rows row0 .. row0+nrows-1, columns [c0, c_zero): scale * tree over the S
+// workspace slices for columns below c_data, zeros from c_data on.
+__device__ __forceinline__ void combine_tile(const ShrinkParams& p, int64_t row0, int nrows, int c0, int c_data,
+                                             int c_zero, float scale, float* h, int64_t ld_h)
+{
+    const int ncols = c_zero - c0;
+    for (int e = threadIdx.x; e < nrows * ncols; e += blockDim.x) {
+        const int row = e / ncols;
+        const int col = c0 + (e - row * ncols);
+        float val = 0.0f;
+        if (col < c_data) {
+            const float* w = p.out + (row0 + row) * p.ld_out + col;
+            float t;
+            switch (p.split_k) {
+            case 1: t = tree_of_splits<1>(w, p.split_stride); break;
+            case 2: t = tree_of_splits<2>(w, p.split_stride); break;
+            case 4: t = tree_of_splits<4>(w, p.split_stride); break;
+            case 8: t = tree_of_splits<8>(w, p.split_stride); break;
+            default: t = tree_of_splits<16>(w, p.split_stride); break;
+            }
+            val = __fmul_rn(t, scale);
+        }
+        h[(row0 + row) * ld_h + col] = val;
     }
 }
 
-// h = scale * tree(ws[0..S-1]) elementwise.
+// ---------------------------------------------------------------------------
+// Single adapter.  A 1-D grid of (row block, rank group, split) items with the
+// split index fastest.  Consecutive workgroup ids go to different XCDs, so
+// this order makes the XCDs stream adjacent pieces of the same rows at the
+// same time; measured on MI355X, it reads the same bytes ~25% faster than
+// the row-block-fastest order (which leaves each XCD a strided subset).
+// ---------------------------------------------------------------------------
+struct SingleItem {
+    int64_t row0;
+    int nrows;
+    int s;
+    int grp;
+    int64_t mb;
+};
+
+__device__ __forceinline__ SingleItem single_item(const ShrinkParams& p, int groups)
+{
+    SingleItem q;                                 // 32-bit: the grid is below 2^31
+    const uint32_t bid = blockIdx.x;
+    const uint32_t S = (uint32_t)p.split_k;
+    q.s = (int)(bid % S);
+    const uint32_t rest = bid / S;
+    q.grp = (int)(rest % (uint32_t)groups);
+    q.mb = rest / (uint32_t)groups;
+    q.row0 = q.mb * kRowBlock;
+    const int64_t left = p.M - q.row0;
+    q.nrows = left < kRowBlock ? (int)left : kRowBlock;
+    return q;
+}
+
+template <int RT, int W, int MODE>
+__global__ __launch_bounds__(W * 64) void k_shrink_partial(ShrinkParams p, int groups)
+{
+    __shared__ float red[red_floats<RT, W>()];
+    const SingleItem q = single_item(p, groups);
+    shrink_tile<RT, W, MODE>(p, q.row0, q.nrows, p.A, p.r, q.grp * 16 * RT, q.s, p.scale, red);
+}
+
+// Single launch: the last split of each (row block, rank group) writes h.
+template <int RT, int W>
+__global__ __launch_bounds__(W * 64) void k_shrink_counted(ShrinkParams p, CounterParams c, int groups)
+{
+    __shared__ float red[red_floats<RT, W>()];
+    __shared__ int flag;
+    const SingleItem q = single_item(p, groups);
+    const int64_t row0 = q.row0;
+    const int nrows = q.nrows;
+    const int col0 = q.grp * 16 * RT;
+    shrink_tile<RT, W, kToWorkspaceCoherent>(p, row0, nrows, p.A, p.r, col0, q.s, 1.0f, red);
+    int32_t* counter = c.counters + q.mb * kMaxRankTiles + q.grp;
+    if (arrived_last(counter, p.split_k, &flag)) {
+        const int cend = col0 + 16 * RT < p.r ? col0 + 16 * RT : p.r;
+        combine_tile(p, row0, nrows, col0, cend, cend, p.scale, c.h, c.ld_h);
+        if (threadIdx.x == 0)
+            __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Multi-adapter.  A fixed grid walks the plan's (tile, split, rank group)
+// items with a static stride; every wave of a workgroup sees the same item
+// count and leaves the loop together.  Items of rank groups beyond the tile's
+// adapter rank are skipped.
+// ---------------------------------------------------------------------------
+struct SgmvItem {
+    int64_t row0;
+    int nrows;
+    int a;           // adapter, -1 for tokens without one
+    int s;
+    int grp;
+    int tile;
+    bool ok;         // rows inside [0, M), adapter -1 or valid
+};
+
+__device__ __forceinline__ SgmvItem sgmv_item(const ShrinkParams& p, uint32_t it, int groups)
+{
+    SgmvItem q;                                   // order: tile, rank group, split (fastest)
+    const uint32_t S = (uint32_t)p.split_k;
+    q.s = (int)(it % S);
+    const uint32_t rest = it / S;
+    q.grp = (int)(rest % (uint32_t)groups);
+    q.tile = (int)(rest / (uint32_t)groups);
+    const int32_t* t = p.tiles + kPlanHeaderInts + 3 * q.tile;
+    q.ok = tile_rows_ok(t, p.M) && t[2] >= -1 && t[2] < p.n_adapters;
+    q.row0 = t[0];
+    q.nrows = t[1];
+    q.a = t[2];
+    return q;
+}
+
+__device__ __forceinline__ int adapter_rank(const ShrinkParams& p, int a)
+{
+    int ra = p.ranks[a];
+    return ra < 0 ? 0 : (ra > p.r_max ? p.r_max : ra);
+}
+
+template <int RT, int W>
+__global__ __launch_bounds__(W * 64) void k_sgmv_shrink_partial(ShrinkParams p)
+{
+    __shared__ float red[red_floats<RT, W>()];
+    const int groups = (p.r_max + 16 * RT - 1) / (16 * RT);
+    const uint32_t items = (uint32_t)plan_tiles(p.tiles, p.M, p.n_adapters) * p.split_k * groups;
+    for (uint32_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const SgmvItem q = sgmv_item(p, it, groups);
+        if (!q.ok || q.a < 0)                     // uniform across the workgroup
+            continue;
+        const int ra = adapter_rank(p, q.a);
+        const int col0 = q.grp * 16 * RT;
+        if (col0 >= ra)
+            continue;
+        shrink_tile<RT, W, kToWorkspace>(p, q.row0, q.nrows, p.A_ptrs[q.a], ra, col0, q.s, 1.0f, red);
+    }
+}
+
+// Single launch: the last split of each (tile, rank group) writes its h
+// columns; the group holding the adapter's last rank column also zeroes the
+// columns from the rank up to r_max; tiles of tokens without an adapter are
+// zeroed by their (split 0, group 0) workgroup.
+template <int RT, int W>
+__global__ __launch_bounds__(W * 64) void k_sgmv_shrink_counted(ShrinkParams p, CounterParams c)
+{
+    __shared__ float red[red_floats<RT, W>()];
+    __shared__ int flag;
+    const int groups = (p.r_max + 16 * RT - 1) / (16 * RT);
+    const uint32_t items = (uint32_t)plan_tiles(p.tiles, p.M, p.n_adapters) * p.split_k * groups;
+    for (uint32_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const SgmvItem q = sgmv_item(p, it, groups);
+        if (!q.ok)
+            continue;
+        if (q.a < 0) {
+            if (q.s == 0 && q.grp == 0)
+                for (int e = threadIdx.x; e < q.nrows * p.r_max; e += blockDim.x)
+                    c.h[(q.row0 + e / p.r_max) * c.ld_h + e % p.r_max] = 0.0f;
+            continue;
+        }
+        const int ra = adapter_rank(p, q.a);
+        const int col0 = q.grp * 16 * RT;
+        if (col0 >= ra)
+            continue;
+        shrink_tile<RT, W, kToWorkspaceCoherent>(p, q.row0, q.nrows, p.A_ptrs[q.a], ra, col0, q.s, 1.0f, red);
+        int32_t* counter = c.counters + (int64_t)q.tile * kMaxRankTiles + q.grp;
+        if (arrived_last(counter, p.split_k, &flag)) {
+            const float scale = c.scales ? c.scales[q.a] : 1.0f;
+            const int cend = col0 + 16 * RT < ra ? col0 + 16 * RT : ra;
+            const int czero = cend == ra ? p.r_max : cend;
+            combine_tile(p, q.row0, q.nrows, col0, cend, czero, scale, c.h, c.ld_h);
+            if (threadIdx.x == 0)
+                __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();                          // flag is reused by the next item
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Second pass of the two-pass shrink: h = scale * tree(ws[0..S-1]).
+// ---------------------------------------------------------------------------
 template <int S, bool SGMV>
 __global__ __launch_bounds__(256) void k_splitk_tree(TreeParams p)
 {
@@ -215,29 +420,80 @@ __global__ __launch_bounds__(256) void k_fill_zero(float* h, int64_t ld_h, int64
     h[i * ld_h + (e - i * ncols)] = 0.0f;
 }
 
-template <int MODE, int W>
-hipError_t launch_partial_w(const ShrinkParams& p, int rt, hipStream_t st)
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+inline dim3 single_grid(const ShrinkParams& p, int groups)
 {
-    dim3 grid((unsigned)((p.M + kRowBlock - 1) / kRowBlock), (unsigned)p.split_k);
-    dim3 block(W * 64);
-    switch (rt) {
-    case 1: hipLaunchKernelGGL((k_shrink_partial<1, W, MODE>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((k_shrink_partial<2, W, MODE>), grid, block, 0, st, p); break;
-    case 3: hipLaunchKernelGGL((k_shrink_partial<3, W, MODE>), grid, block, 0, st, p); break;
-    default: hipLaunchKernelGGL((k_shrink_partial<4, W, MODE>), grid, block, 0, st, p); break;
+    return dim3((unsigned)(((p.M + kRowBlock - 1) / kRowBlock) * p.split_k * groups));
+}
+
+template <int MODE, int RT, int W>
+void launch_partial_rw(const ShrinkParams& p, int groups, hipStream_t st)
+{
+    hipLaunchKernelGGL((k_shrink_partial<RT, W, MODE>), single_grid(p, groups), dim3(W * 64), 0, st, p, groups);
+}
+
+template <int MODE, int RT>
+void launch_partial_r(const ShrinkParams& p, int waves, int groups, hipStream_t st)
+{
+    switch (waves) {
+    case 1: launch_partial_rw<MODE, RT, 1>(p, groups, st); break;
+    case 2: launch_partial_rw<MODE, RT, 2>(p, groups, st); break;
+    case 4: launch_partial_rw<MODE, RT, 4>(p, groups, st); break;
+    default: launch_partial_rw<MODE, RT, 8>(p, groups, st); break;
+    }
+}
+
+// group_tiles: rank tiles per workgroup (1 .. rank_tiles).
+template <int MODE>
+hipError_t launch_partial(const ShrinkParams& p, int waves, int rank_tiles, int group_tiles, hipStream_t st)
+{
+    const int groups = (rank_tiles + group_tiles - 1) / group_tiles;
+    switch (group_tiles) {
+    case 1: launch_partial_r<MODE, 1>(p, waves, groups, st); break;
+    case 2: launch_partial_r<MODE, 2>(p, waves, groups, st); break;
+    case 3: launch_partial_r<MODE, 3>(p, waves, groups, st); break;
+    default: launch_partial_r<MODE, 4>(p, waves, groups, st); break;
     }
     return hipGetLastError();
 }
 
-template <int MODE>
-hipError_t launch_partial(const ShrinkParams& p, int waves, int rt, hipStream_t st)
+template <int RT, int W>
+void launch_counted_rw(const ShrinkParams& p, const CounterParams& c, int groups, hipStream_t st)
+{
+    hipLaunchKernelGGL((k_shrink_counted<RT, W>), single_grid(p, groups), dim3(W * 64), 0, st, p, c, groups);
+}
+
+template <int RT>
+void launch_counted_r(const ShrinkParams& p, const CounterParams& c, int waves, int groups, hipStream_t st)
 {
     switch (waves) {
-    case 1: return launch_partial_w<MODE, 1>(p, rt, st);
-    case 2: return launch_partial_w<MODE, 2>(p, rt, st);
-    case 4: return launch_partial_w<MODE, 4>(p, rt, st);
-    default: return launch_partial_w<MODE, 8>(p, rt, st);
+    case 1: launch_counted_rw<RT, 1>(p, c, groups, st); break;
+    case 2: launch_counted_rw<RT, 2>(p, c, groups, st); break;
+    case 4: launch_counted_rw<RT, 4>(p, c, groups, st); break;
+    default: launch_counted_rw<RT, 8>(p, c, groups, st); break;
     }
+}
+
+template <int RT, bool COUNTED>
+void launch_sgmv_r(const ShrinkParams& p, const CounterParams& c, int waves, int grid, hipStream_t st)
+{
+    dim3 g((unsigned)grid);
+#define LORA_SGMV_LAUNCH(W_)                                                                   \
+    do {                                                                                       \
+        if (COUNTED)                                                                           \
+            hipLaunchKernelGGL((k_sgmv_shrink_counted<RT, W_>), g, dim3(W_ * 64), 0, st, p, c); \
+        else                                                                                   \
+            hipLaunchKernelGGL((k_sgmv_shrink_partial<RT, W_>), g, dim3(W_ * 64), 0, st, p);    \
+    } while (0)
+    switch (waves) {
+    case 1: LORA_SGMV_LAUNCH(1); break;
+    case 2: LORA_SGMV_LAUNCH(2); break;
+    case 4: LORA_SGMV_LAUNCH(4); break;
+    default: LORA_SGMV_LAUNCH(8); break;
+    }
+#undef LORA_SGMV_LAUNCH
 }
 
 template <bool SGMV>
@@ -257,30 +513,54 @@ hipError_t launch_tree_t(const TreeParams& p, int S, hipStream_t st)
 
 }  // namespace
 
-hipError_t launch_shrink_partial_ws(const ShrinkParams& p, int waves, int rank_tiles, hipStream_t st)
+hipError_t launch_shrink_partial_ws(const ShrinkParams& p, int waves, int rank_tiles, int group_tiles,
+                                    hipStream_t st)
 {
-    return launch_partial<kToWorkspace>(p, waves, rank_tiles, st);
+    return launch_partial<kToWorkspace>(p, waves, rank_tiles, group_tiles, st);
 }
 
-hipError_t launch_shrink_partial_direct(const ShrinkParams& p, int waves, int rank_tiles, hipStream_t st)
+hipError_t launch_shrink_partial_direct(const ShrinkParams& p, int waves, int rank_tiles, int group_tiles,
+                                        hipStream_t st)
 {
-    return launch_partial<kToOutputScaled>(p, waves, rank_tiles, st);
+    return launch_partial<kToOutputScaled>(p, waves, rank_tiles, group_tiles, st);
 }
 
-hipError_t launch_shrink_partial_atomic(const ShrinkParams& p, int waves, int rank_tiles, hipStream_t st)
+hipError_t launch_shrink_partial_atomic(const ShrinkParams& p, int waves, int rank_tiles, int group_tiles,
+                                        hipStream_t st)
 {
-    return launch_partial<kAtomicScaled>(p, waves, rank_tiles, st);
+    return launch_partial<kAtomicScaled>(p, waves, rank_tiles, group_tiles, st);
 }
 
-hipError_t launch_sgmv_shrink_partial(const ShrinkParams& p, int waves, int grid, hipStream_t st)
+hipError_t launch_shrink_counted(const ShrinkParams& p, const CounterParams& c, int waves, int rank_tiles,
+                                 int group_tiles, hipStream_t st)
 {
-    dim3 g((unsigned)grid), b(waves * 64);
-    switch (waves) {
-    case 1: hipLaunchKernelGGL((k_sgmv_shrink_partial<1>), g, b, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((k_sgmv_shrink_partial<2>), g, b, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((k_sgmv_shrink_partial<4>), g, b, 0, st, p); break;
-    default: hipLaunchKernelGGL((k_sgmv_shrink_partial<8>), g, b, 0, st, p); break;
+    const int groups = (rank_tiles + group_tiles - 1) / group_tiles;
+    switch (group_tiles) {
+    case 1: launch_counted_r<1>(p, c, waves, groups, st); break;
+    case 2: launch_counted_r<2>(p, c, waves, groups, st); break;
+    case 3: launch_counted_r<3>(p, c, waves, groups, st); break;
+    default: launch_counted_r<4>(p, c, waves, groups, st); break;
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_sgmv_shrink_partial(const ShrinkParams& p, int waves, int group_tiles, int grid, hipStream_t st)
+{
+    const CounterParams none{};
+    if (group_tiles == 1)
+        launch_sgmv_r<1, false>(p, none, waves, grid, st);
+    else
+        launch_sgmv_r<4, false>(p, none, waves, grid, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_sgmv_shrink_counted(const ShrinkParams& p, const CounterParams& c, int waves, int group_tiles,
+                                      int grid, hipStream_t st)
+{
+    if (group_tiles == 1)
+        launch_sgmv_r<1, true>(p, c, waves, grid, st);
+    else
+        launch_sgmv_r<4, true>(p, c, waves, grid, st);
     return hipGetLastError();
 }
 

@@ -149,6 +149,29 @@ int lora_expand(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b,
                 void* stream);
 
 /*
+ * Single-launch deterministic Split-K shrink: the paper's final design
+ * (section 4.3, Alg. 1).  Each split's workgroup stores its fp32 partial to
+ * the workspace, makes it visible device-wide (agent-scope release fence),
+ * and adds 1 to its row block's integer counter with an agent-scope atomic;
+ * the workgroup that sees split_k - 1 arrived last, acquires, and applies the
+ * same fixed pairwise tree and scale as lora_shrink_splitk, writes h and
+ * resets the counter to 0.  Bit for bit the same h as lora_shrink_splitk, in
+ * one launch.  No workgroup waits for another.
+ * counters: int32 [lora_shrink_counter_bytes(M) / 4] (4 per 16-token block, one
+ * per 16-wide rank tile), 4-byte aligned, ALL ZERO
+ * before the first call; every completed call leaves them zero again, so one
+ * zero-initialised buffer serves any number of calls on one stream (not
+ * concurrent calls).  workspace as for lora_shrink_splitk.  split_k == 1 needs
+ * neither workspace nor counters.
+ */
+size_t lora_shrink_counter_bytes(int64_t M);
+
+int lora_shrink_splitk_counted(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a,
+                               float* h, int64_t ld_h, int64_t M, int64_t K, int32_t r,
+                               int32_t split_k, float scale, void* workspace, size_t workspace_bytes,
+                               int32_t* counters, size_t counter_bytes, void* stream);
+
+/*
  * The two halves of the deterministic pipeline, one launch each.
  *
  * lora_shrink_partials: the Split-K partial kernel of lora_shrink_splitk on its
@@ -229,8 +252,8 @@ size_t lora_sgmv_plan_bytes(int64_t M);
 /*
  * Builds the work list from the per-token ids, on the device and without a
  * host synchronisation: tokens are grouped into runs of equal id, each run is
- * cut into tiles of at most 16 consecutive tokens, tiles of invalid ids are
- * dropped.  One launch of one workgroup.  The plan buffer (16-byte aligned) is
+ * cut into tiles of at most 16 consecutive tokens (tiles of tokens without a
+ * valid adapter are kept, marked -1).  One launch of one workgroup.  The plan buffer (16-byte aligned) is
  * opaque; it stays valid for later sgmv calls with the same ids, M and
  * n_adapters and may be reused by both sgmv_shrink and sgmv_expand.
  */
@@ -252,6 +275,23 @@ int lora_sgmv_shrink(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_p
                      int32_t n_adapters, const void* plan, size_t plan_bytes,
                      float* h, int64_t ld_h, int64_t M, int64_t K, int32_t r_max, int32_t split_k,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Multi-adapter single-launch shrink: lora_sgmv_shrink's result (same bits) in
+ * one launch with the completion-counter combine of lora_shrink_splitk_counted,
+ * one counter per plan tile.  The plan must come from lora_sgmv_plan with the
+ * same M and n_adapters (token ids are read from the plan).
+ * counters: int32 [lora_sgmv_counter_bytes(M) / 4] (4 per possible tile), all
+ * zero before the first call, left zero.
+ */
+size_t lora_sgmv_counter_bytes(int64_t M);
+
+int lora_sgmv_shrink_counted(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_ptrs,
+                             int64_t ld_a, const int32_t* ranks, const float* scales,
+                             int32_t n_adapters, const void* plan, size_t plan_bytes,
+                             float* h, int64_t ld_h, int64_t M, int64_t K, int32_t r_max,
+                             int32_t split_k, void* workspace, size_t workspace_bytes,
+                             int32_t* counters, size_t counter_bytes, void* stream);
 
 /*
  * Multi-adapter expand: per token with an adapter, lora_expand with that

@@ -170,7 +170,7 @@ def test_atomic_rejects(kw, status):
     (dict(ld_b=20), B.LORA_ERR_ALIGN),
     (dict(y=FAKE_MIS), B.LORA_ERR_ALIGN),
     (dict(h=FAKE + 8), B.LORA_ERR_ALIGN),
-    (dict(N=256 * 65536, ld_y=256 * 65536), B.LORA_ERR_SHAPE),
+    (dict(M=(1 << 31) - 1, N=(1 << 31) - 8, ld_y=(1 << 31)), B.LORA_ERR_SHAPE),
 ])
 def test_expand_rejects(kw, status):
     assert _expand(**kw) == status
@@ -314,3 +314,42 @@ def test_shrink_expand_launch_count():
     assert dsl.lora_shrink_expand_launches(1, 4096, 16, 4096, 8) == 2
     assert dsl.lora_shrink_expand_launches(0, 4096, 16, 4096, 8) == 0
     assert dsl.lora_shrink_expand_launches(8, 4000, 16, 4096, 8) < 0
+
+
+def test_counted_rejects():
+    L = dsl.lib()
+    assert dsl.lora_shrink_counter_bytes(1) == 16
+    assert dsl.lora_shrink_counter_bytes(33) == 48
+    assert dsl.lora_sgmv_counter_bytes(33) == 528
+    wsb = dsl.lora_shrink_workspace_bytes(4, 16, 8)
+
+    def call(**kw):
+        a = dict(x=FAKE, ld_x=4096, A=FAKE, ld_a=4096, h=FAKE, ld_h=16, M=4, K=4096, r=16, S=8, scale=1.0,
+                 ws=FAKE, wsb=wsb, cnt=FAKE, cb=16)
+        a.update(kw)
+        return L.lora_shrink_splitk_counted(a["x"], a["ld_x"], a["A"], a["ld_a"], a["h"], a["ld_h"], a["M"],
+                                            a["K"], a["r"], a["S"], a["scale"], a["ws"], a["wsb"], a["cnt"], a["cb"],
+                                            None)
+    assert call(cnt=None) == B.LORA_ERR_NULL
+    assert call(ws=None) == B.LORA_ERR_NULL
+    assert call(cnt=FAKE + 2) == B.LORA_ERR_ALIGN
+    assert call(cb=0) == B.LORA_ERR_WORKSPACE
+    assert call(wsb=wsb - 4) == B.LORA_ERR_WORKSPACE
+    assert call(S=5) == B.LORA_ERR_UNSUPPORTED
+    assert call(M=0, x=None, cnt=None) == B.LORA_OK
+    pb = dsl.lora_sgmv_plan_bytes(64)
+    wsg = dsl.lora_sgmv_workspace_bytes(64, 64, 8)
+
+    def sg(**kw):
+        a = dict(x=FAKE, ld_x=4096, Ap=FAKE, ld_a=4096, ranks=FAKE, scales=None, n=4, plan=FAKE, pb=pb, h=FAKE,
+                 ld_h=64, M=64, K=4096, r_max=64, S=8, ws=FAKE, wsb=wsg, cnt=FAKE, cb=1024)
+        a.update(kw)
+        return L.lora_sgmv_shrink_counted(a["x"], a["ld_x"], a["Ap"], a["ld_a"], a["ranks"], a["scales"], a["n"],
+                                          a["plan"], a["pb"], a["h"], a["ld_h"], a["M"], a["K"], a["r_max"], a["S"],
+                                          a["ws"], a["wsb"], a["cnt"], a["cb"], None)
+    assert sg(cnt=None) == B.LORA_ERR_NULL
+    assert sg(plan=None) == B.LORA_ERR_NULL
+    assert sg(cb=1020) == B.LORA_ERR_WORKSPACE
+    assert sg(n=0) == B.LORA_ERR_SHAPE
+    assert sg(cnt=FAKE + 1) == B.LORA_ERR_ALIGN
+    assert sg(M=0, x=None) == B.LORA_OK

@@ -383,9 +383,8 @@ def _plan_reference(ids, n):
         j = i
         while j < M and norm[j] == norm[i]:
             j += 1
-        if norm[i] >= 0:
-            for s in range(i, j, 16):
-                tiles.append((s, min(16, j - s), norm[i]))
+        for s in range(i, j, 16):
+            tiles.append((s, min(16, j - s), norm[i]))
         i = j
     return tiles
 
@@ -721,3 +720,153 @@ def test_batch_invariance_across_schedule_switch():
             t.cuda.synchronize()
             assert np.array_equal(f32_bits(h)[pos], ref_h[grp]), f"h at batch {b}"
             assert np.array_equal(bf16_from_gpu(yg)[pos], ref_y[grp]), f"y at batch {b}"
+
+
+# ---------------------------------------------------------------------------
+# single-launch shrink with completion counters (the paper's final design)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,r,S", [(1, 4096, 16, 8), (8, 1024, 8, 8), (64, 4096, 16, 8), (256, 4096, 16, 8),
+                                     (37, 8192, 64, 16), (100, 2048, 40, 4), (19, 14336, 32, 8), (5, 1024, 5, 2),
+                                     (40, 4096, 16, 1)])
+def test_shrink_counted_bitwise(M, K, r, S):
+    """lora_shrink_splitk_counted (one launch, the last-arriving split
+    combines) gives lora_shrink_splitk's bits, leaves its counters at zero,
+    and repeats bit for bit on the same counters."""
+    t = torch()
+    c = single_adapter_case(M, K, r, 0, split_k=S, seed=31 + M)
+    xg, Ag = bf16_to_gpu(c.x), bf16_to_gpu(c.A)
+    ws = workspace(dsl.lora_shrink_workspace_bytes(M, r, S))
+    h1 = t.empty((M, r), dtype=t.float32, device="cuda")
+    dsl.lora_shrink_splitk(xg, Ag, h1, ws if S > 1 else None, S, 2.0)
+    cnt = t.zeros(max(1, dsl.lora_shrink_counter_bytes(M) // 4), dtype=t.int32, device="cuda")
+    ws2 = workspace(dsl.lora_shrink_workspace_bytes(M, r, S))
+    outs = []
+    for rep in range(20):
+        h2 = t.full((M, r), float("nan"), dtype=t.float32, device="cuda")
+        dsl.lora_shrink_splitk_counted(xg, Ag, h2, ws2 if S > 1 else None, cnt if S > 1 else None, S, 2.0)
+        outs.append(h2)
+    t.cuda.synchronize()
+    ref = f32_bits(h1)
+    for h2 in outs:
+        assert np.array_equal(f32_bits(h2), ref)
+    assert int(cnt.abs().sum()) == 0
+    check_shrink(outs[0].cpu().numpy(), c.x, c.A, 2.0, dsl.lora_shrink_plan(K, r, S), "counted")
+
+
+def test_shrink_counted_in_graph_replays():
+    t = torch()
+    M, K, r, S = 48, 4096, 16, 8
+    c = single_adapter_case(M, K, r, 0, split_k=S, seed=8)
+    xg, Ag = bf16_to_gpu(c.x), bf16_to_gpu(c.A)
+    ws = workspace(dsl.lora_shrink_workspace_bytes(M, r, S))
+    cnt = t.zeros(dsl.lora_shrink_counter_bytes(M) // 4, dtype=t.int32, device="cuda")
+    h = t.empty((M, r), dtype=t.float32, device="cuda")
+    dsl.lora_shrink_splitk_counted(xg, Ag, h, ws, cnt, S, 1.0)
+    t.cuda.synchronize()
+    ref = f32_bits(h)
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        dsl.lora_shrink_splitk_counted(xg, Ag, h, ws, cnt, S, 1.0)
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        for _ in range(3):
+            dsl.lora_shrink_splitk_counted(xg, Ag, h, ws, cnt, S, 1.0)
+    for rep in range(5):
+        h.fill_(float("nan"))
+        junk = t.randn(1 << 18, device="cuda").sum()
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        assert np.array_equal(f32_bits(h), ref), f"replay {rep}"
+        assert int(cnt.abs().sum()) == 0
+        del junk
+
+
+@pytest.mark.parametrize("case", ["qkv", "mixed", "decode_probe"])
+def test_sgmv_counted_bitwise(case):
+    """lora_sgmv_shrink_counted gives lora_sgmv_shrink's bits (rows without an
+    adapter and columns beyond a rank zeroed) in one launch."""
+    t = torch()
+    if case == "qkv":
+        c = sgmv_case(512, 4096, 64, [64, 64, 64, 64], 1, 64, 8, seed=0, tag="cq")
+    elif case == "mixed":
+        rng = np.random.default_rng(4)
+        ids = rng.choice([-1, 0, 1, 2, 3, 17], 333).astype(np.int32)
+        ids[50:150] = 2
+        c = sgmv_case(333, 2048, 64, [8, 16, 32, 64], 0, 0, 16, seed=1, tag="cm", ids=ids)
+    else:
+        c = sgmv_case(32, 8192, 64, [64] * 32, 0, 0, 8, seed=2, tag="cd", ids=np.arange(32, dtype=np.int32))
+    n = len(c.ranks)
+    As = [bf16_to_gpu(a) for a in c.As]
+    Ap = t.tensor([a.data_ptr() for a in As], dtype=t.int64, device="cuda")
+    ranks = t.from_numpy(c.ranks).cuda()
+    scales = t.from_numpy(c.scales).cuda()
+    idg, plan = _build_plan(c.ids, n)
+    xg = bf16_to_gpu(c.x)
+    h1 = t.full((c.M, c.r_max), float("nan"), dtype=t.float32, device="cuda")
+    ws = workspace(dsl.lora_sgmv_workspace_bytes(c.M, c.r_max, c.split_k))
+    dsl.lora_sgmv_shrink(xg, Ap, c.K, ranks, scales, idg, n, plan, h1, c.r_max, c.split_k, ws)
+    cnt = t.zeros(dsl.lora_sgmv_counter_bytes(c.M) // 4, dtype=t.int32, device="cuda")
+    ws2 = workspace(dsl.lora_sgmv_workspace_bytes(c.M, c.r_max, c.split_k))
+    hs = []
+    for rep in range(5):
+        h2 = t.full((c.M, c.r_max), float("nan"), dtype=t.float32, device="cuda")
+        dsl.lora_sgmv_shrink_counted(xg, Ap, c.K, ranks, scales, n, plan, h2, c.r_max, c.split_k, ws2, cnt)
+        hs.append(h2)
+    t.cuda.synchronize()
+    for h2 in hs:
+        assert np.array_equal(f32_bits(h2), f32_bits(h1))
+    assert int(cnt.abs().sum()) == 0
+    hh = hs[0].cpu().numpy()
+    for i in range(0, c.M, max(1, c.M // 40)):
+        a = int(c.ids[i])
+        if a < 0 or a >= n:
+            assert np.all(hh[i] == 0.0)
+            continue
+        r = int(c.ranks[a])
+        assert np.all(hh[i, r:] == 0.0)
+        check_shrink(hh[i:i + 1, :r], c.x[i:i + 1], c.As[a], float(c.scales[a]),
+                     dsl.lora_shrink_plan(c.K, r, c.split_k), f"{case} row {i}")
+
+
+def test_counted_shrinks_stress_repeats():
+    """Back-to-back launches of the single-launch shrinks (single adapter and
+    32 one-token adapters of rank 64), each compared bit for bit on the GPU
+    with the two-pass result: a partial read before it was visible would show
+    up as a mismatch."""
+    t = torch()
+    M, K, r, S = 64, 4096, 16, 8
+    c = single_adapter_case(M, K, r, 0, split_k=S, seed=90)
+    xg, Ag = bf16_to_gpu(c.x), bf16_to_gpu(c.A)
+    ref = t.empty((M, r), dtype=t.float32, device="cuda")
+    dsl.lora_shrink_splitk(xg, Ag, ref, workspace(dsl.lora_shrink_workspace_bytes(M, r, S)), S, 1.0)
+    ws = workspace(dsl.lora_shrink_workspace_bytes(M, r, S))
+    cnt = t.zeros(dsl.lora_shrink_counter_bytes(M) // 4, dtype=t.int32, device="cuda")
+    h = t.empty_like(ref)
+    bad = t.zeros((), dtype=t.int64, device="cuda")
+    for _ in range(500):
+        h.fill_(float("nan"))
+        dsl.lora_shrink_splitk_counted(xg, Ag, h, ws, cnt, S, 1.0)
+        bad += (h.view(t.int32) != ref.view(t.int32)).sum()
+    c2 = sgmv_case(32, 8192, 64, [64] * 32, 0, 0, 8, seed=91, tag="st", ids=np.arange(32, dtype=np.int32))
+    As = [bf16_to_gpu(a) for a in c2.As]
+    Ap = t.tensor([a.data_ptr() for a in As], dtype=t.int64, device="cuda")
+    ranks = t.from_numpy(c2.ranks).cuda()
+    idg, plan = _build_plan(c2.ids, 32)
+    x2 = bf16_to_gpu(c2.x)
+    ref2 = t.empty((32, 64), dtype=t.float32, device="cuda")
+    dsl.lora_sgmv_shrink(x2, Ap, 8192, ranks, None, idg, 32, plan, ref2, 64, 8,
+                         workspace(dsl.lora_sgmv_workspace_bytes(32, 64, 8)))
+    ws2 = workspace(dsl.lora_sgmv_workspace_bytes(32, 64, 8))
+    cnt2 = t.zeros(dsl.lora_sgmv_counter_bytes(32) // 4, dtype=t.int32, device="cuda")
+    h2 = t.empty_like(ref2)
+    for _ in range(500):
+        h2.fill_(float("nan"))
+        dsl.lora_sgmv_shrink_counted(x2, Ap, 8192, ranks, None, 32, plan, h2, 64, 8, ws2, cnt2)
+        bad += (h2.view(t.int32) != ref2.view(t.int32)).sum()
+    t.cuda.synchronize()
+    assert int(bad) == 0
+    assert int(cnt.abs().sum()) == 0 and int(cnt2.abs().sum()) == 0
