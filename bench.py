@@ -234,15 +234,39 @@ class Bench:
         return res
 
 
-def decode_probe(args):
-    """32 decode tokens, each with its own rank-64 adapter, hidden 8192, Split-K 8:
+def copy_roofline(args, nbytes_list):
+    """Device-to-device copy of known sizes on rotating buffers (>= 1 GiB), HIP
+    graphs + events: the practical bandwidth ceiling at these sizes, and the
+    plain copy of known size the hardware byte counters are calibrated with."""
+    import torch
+    dev = torch.device("cuda:0")
+    out = {}
+    for nb in nbytes_list:
+        n = nb // 2
+        copies = max(2, math.ceil(ROTATE_BYTES / (2 * nb)))
+        src = [torch.empty(n, dtype=torch.bfloat16, device=dev).fill_(1.0) for _ in range(copies)]
+        dst = [torch.empty_like(t) for t in src]
+        sets = [dict(s=a, d=b) for a, b in zip(src, dst)]
+
+        def call(st):
+            st["d"].copy_(st["s"])
+        us = _time_rotating(call, sets, args)
+        out[str(nb)] = {"us": round(us, 3), "GBps_read_plus_write": round(2 * nb / us / 1e3, 1),
+                        "pct_hbm_peak": round(100 * 2 * nb / us / 1e3 / HBM_PEAK_GBS, 2)}
+        del src, dst, sets
+        torch.cuda.empty_cache()
+    return out
+
+
+def decode_probe(args, M=32):
+    """M decode tokens, each with its own rank-64 adapter, hidden 8192, Split-K 8:
     the multi-adapter deterministic shrink (partials + fixed tree) on a prebuilt
     plan, cold cache.  Algorithmic bytes: x, every adapter's A once, h."""
     import torch
     import deterministic_split_lora_amd as dsl
     from synth import normal_bf16
     dev = torch.device("cuda:0")
-    M, K, r, S, n = 32, 8192, 64, 8, 32
+    K, r, S, n = 8192, 64, 8, M
 
     def g(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -270,7 +294,7 @@ def decode_probe(args):
     def counted(s):
         dsl.lora_sgmv_shrink_counted(s["x"], s["Ap"], K, ranks, None, n, plan, s["h"], r, S, s["ws"], cnt)
 
-    out = {"workload": "32 tokens x hidden 8192, 32 adapters of rank 64 (one per token), Split-K 8, "
+    out = {"workload": f"{M} tokens x hidden 8192, {M} adapters of rank 64 (one per token), Split-K 8, "
                        "multi-adapter deterministic shrink", "bytes": byt, "copies": copies}
     for name, call in (("two_launch", two_launch), ("single_launch", counted)):
         us = _time_rotating(call, sets, args)
@@ -347,7 +371,12 @@ def main():
     b = Bench(args)
     res = b.run()
     log("bench: main timing done")
-    probe = None if args.no_probe else decode_probe(args)
+    probe = wide = roof = None
+    if not args.no_probe:
+        probe = decode_probe(args, 32)
+        wide = decode_probe(args, 128)
+        roof = copy_roofline(args, [probe["bytes"], wide["bytes"], 64 << 20])
+        log("bench: probes done")
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
     import torch
     out = {
@@ -377,6 +406,8 @@ def main():
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
         "decode_bandwidth_probe": probe,
+        "decode_bandwidth_probe_wide": wide,
+        "copy_roofline": roof,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)
