@@ -15,12 +15,15 @@ rotating over enough input copies (>= 1 GiB) that no step finds its inputs
 in the 256 MB last-level cache.  Inputs are resident in HBM before timing.
 HIP events are recorded on the stream the kernels run on.
 
-Also reported: per-batch-size numbers, hot-cache numbers, the roofline of the
-dominant kernel (the tree + expand kernel of the deterministic pipeline), a decode
-bandwidth probe (32 tokens, each with its own rank-64 adapter, hidden 8192,
-multi-adapter shrink) and the CPU oracle timed on the host cores.
+Also reported: per-batch-size numbers, the roofline of the dominant kernel
+(the tree + expand kernel of the deterministic pipeline, with the HBM bytes
+the hardware counters recorded for it when its sources are unchanged since),
+two decode bandwidth probes (32 and 128 tokens, each with its own rank-64
+adapter, hidden 8192, multi-adapter shrink), device-copy ceilings at the
+probes' sizes, and the CPU oracle timed on the host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py --counters      # eager pass for rocprofv3 --pmc runs
 """
 from __future__ import annotations
 
@@ -65,7 +68,7 @@ def combine_bytes(M, r, N, S):
 
 
 class Bench:
-    def __init__(self, args):
+    def __init__(self, args, copies=None):
         import torch
         import deterministic_split_lora_amd as dsl
         from synth import single_adapter_case
@@ -82,6 +85,8 @@ class Bench:
         per_set = sum(2 * M * K_HID + 2 * M * N_OUT + 4 * RANK * K_HID + 4 * M * RANK * (SPLIT + 1)
                       for M in M_LIST)
         self.copies = max(2, math.ceil(ROTATE_BYTES / per_set)) if not args.hot else 1
+        if copies is not None:
+            self.copies = copies
         self.sets = []
         for c in range(self.copies):
             s = {}
@@ -199,6 +204,7 @@ class Bench:
             u1 = self.per_call_us(self.det_one_launch, (M,), 8, K)
             uc = self.per_call_us(self.det_counted, (M,), 8, K)
             byt = shrink_bytes(M, K_HID, RANK) + expand_bytes(M, RANK, N_OUT)
+            log(f"bench: M={M} timed")
             per_m[str(M)] = {"det_us": round(ud, 3), "atomic_us": round(ua, 3),
                              "det_launches": self.dsl.lora_shrink_expand_launches(M, K_HID, RANK, N_OUT, SPLIT),
                              "det_one_launch_us": round(u1, 3), "det_two_launch_us": round(u2, 3),
@@ -220,18 +226,79 @@ class Bench:
                          "shrink recomputed per 512 columns, fixed trees, expand; r=16, N=4096, M=" +
                          "/".join(map(str, one)) + ")"))
         if two:
-            us = self.per_call_us(self.combine_only, two, 8, K)
+            per = {M: self.per_call_us(self.combine_only, (M,), 8, K) for M in two}
             byt = sum(combine_bytes(M, RANK, N_OUT, SPLIT) for M in two)
-            cand.append((us, len(two), byt, "k_expand_combine<1,8> (lora_expand_combine: fixed tree over the "
-                         "Split-K workspace + expand; r=16, N=4096, M=" + "/".join(map(str, two)) + ")"))
-        us, n, byt, name = max(cand)
+            cand.append((sum(per.values()), len(two), byt, COMBINE_KERNEL + " (lora_expand_combine: fixed tree "
+                         "over the Split-K workspace + expand; r=16, N=4096, M=" + "/".join(map(str, two)) + ")",
+                         {str(M): round(u, 3) for M, u in per.items()}))
+        us, n, byt, name, per = max(cand, key=lambda c: c[0])
         avg_launch_us = us / n
         avg_bytes = byt / n
         ach = avg_bytes / avg_launch_us / 1e3
+        traffic = recorded_traffic(COMBINE_KERNEL, two) if name.startswith(COMBINE_KERNEL) else None
         res["roofline"] = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None,
-                           "avg_launch_us": round(avg_launch_us, 3), "algorithmic_bytes_per_launch": avg_bytes}
+                           "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
+                           "avg_launch_us": round(avg_launch_us, 3), "launch_us_per_m": per,
+                           "algorithmic_bytes_per_launch": avg_bytes,
+                           "timing": "8 back-to-back launches per HIP graph on 8 input copies; a launch's time "
+                                     "includes the gap to the next dispatch"}
         return res
+
+
+COMBINE_KERNEL = "k_expand_combine<1,8>"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_expand_combine_qproj_r16_s8_traffic.md")
+KERNEL_SOURCES = ["deterministic_split_lora_amd/csrc/expand.hip", "deterministic_split_lora_amd/csrc/device.h",
+                  "deterministic_split_lora_amd/csrc/kernels.h"]
+
+
+def kernel_source_hash():
+    """sha256 over the sources the tree + expand kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel, Ms):
+    """HBM bytes per launch of `kernel`, averaged over batch sizes Ms, from the
+    hardware-counter summary under profiles/ (FETCH_SIZE + WRITE_SIZE, each
+    scaled by the factor a plain copy of known size gives).  None when there is
+    no summary or the kernel's sources have changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if line.startswith("source_hash:"):
+                rec["hash"] = line.split(":", 1)[1].strip()
+            elif line.startswith("hbm_bytes M="):
+                k, v = line[len("hbm_bytes M="):].split(":")
+                rec[int(k)] = float(v)
+    if rec.get("hash") != kernel_source_hash() or not all(M in rec for M in Ms):
+        return None
+    return round(sum(rec[M] for M in Ms) / len(Ms), 1)
+
+
+def counter_pass(args):
+    """Driver for hardware-counter runs (rocprofv3 --pmc): the deterministic
+    step at every batch size on 8 distinct input copies, eagerly, then four
+    copies of 64 MiB (the plain copy of known size the counters are scaled by)."""
+    import torch
+    b = Bench(args, copies=8)
+    for c in range(8):
+        for M in M_LIST:
+            b.det(b.sets[c][M], M)
+    torch.cuda.synchronize()
+    n = (64 << 20) // 2
+    src = [torch.ones(n, dtype=torch.bfloat16, device=b.dev) for _ in range(4)]
+    dst = [torch.empty_like(t) for t in src]
+    torch.cuda.synchronize()
+    for a, d in zip(src, dst):
+        d.copy_(a)
+    torch.cuda.synchronize()
+    log("bench: counter pass done")
 
 
 def copy_roofline(args, nbytes_list):
@@ -359,15 +426,20 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--hot", action="store_true", help="no input rotation (inputs may sit in cache)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="only run the step eagerly for a hardware-counter profile; prints no JSON")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the deterministic shrink/expand needs no collective; "
               "run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
+    if args.counters:
+        counter_pass(args)
+        return
     b = Bench(args)
     res = b.run()
     log("bench: main timing done")
@@ -397,7 +469,8 @@ def main():
                                "M = 1, 16, 64, 256 per step",
                    "cache": "hot" if args.hot else f"cold: rotating {b.copies} input copies (>= 1 GiB)",
                    "timing": "HIP graph replay, HIP events on the launch stream",
-                   "det_pipeline": "lora_shrink_expand (1 launch for M <= 64, 2 above; identical bits)",
+                   "det_pipeline": "lora_shrink_expand (split partials, then tree + expand: 2 launches at every M "
+                                   "of this shape; identical bits to every other schedule)",
                    "atomic_pipeline": "lora_shrink_splitk_atomic (fill + atomic partials) + lora_expand (3 launches)"},
         "atomic_us_per_call": round(res["atomic_us_per_call"], 3),
         "det_two_call_us_per_call": round(res["det_two_call_us_per_call"], 3),
