@@ -9,11 +9,12 @@ deterministic shrink (split partials + fixed-tree combine) then expand into y.
 sizes.  The atomic Split-K contrast (zero fill + atomic partials + expand) is
 timed the same way.
 
-Timing: each step is captured once per input copy in a HIP graph (the paper
-times shrink latency under CUDA graphs); the timed region replays K steps,
-rotating over enough input copies (>= 1 GiB) that no step finds its inputs
-in the 256 MB last-level cache.  Inputs are resident in HBM before timing.
-HIP events are recorded on the stream the kernels run on.
+Timing: steps are captured in HIP graphs, 8 consecutive steps on 8 input
+copies per graph (the paper times shrink latency under CUDA graphs); the
+timed region replays K / 8 graphs, i.e. exactly K steps, rotating over enough
+input copies (>= 1 GiB) that no step finds its inputs in the 256 MB
+last-level cache.  Inputs are resident in HBM before timing.  HIP events are
+recorded on the stream the kernels run on.
 
 Also reported: per-batch-size numbers, the roofline of the dominant kernel
 (the tree + expand kernel of the deterministic pipeline, with the HBM bytes
@@ -45,6 +46,7 @@ HBM_PEAK_GBS = 8000.0
 M_LIST = (1, 16, 64, 256)
 K_HID, RANK, N_OUT, SPLIT, SCALE = 4096, 16, 4096, 8, 2.0
 ROTATE_BYTES = 1 << 30
+STEPS_PER_GRAPH = 8
 
 
 def log(*a):
@@ -98,6 +100,9 @@ class Bench:
                             cnt=torch.zeros(max(1, dsl.lora_shrink_counter_bytes(M) // 4), dtype=torch.int32,
                                             device=self.dev))
             self.sets.append(s)
+        # one arrival-counter buffer serves every call: the calls run one after another
+        self.cnt_se = torch.zeros(dsl.lora_shrink_expand_counter_bytes(max(M_LIST)) // 4, dtype=torch.int32,
+                                  device=self.dev)
         torch.cuda.synchronize()
         log(f"bench: {self.copies} input copies ({self.copies * per_set / 2**30:.2f} GiB)")
 
@@ -118,6 +123,11 @@ class Bench:
         d = self.dsl
         d.lora_shrink_splitk_counted(s["x"], s["A"], s["h"], s["ws"], s["cnt"], SPLIT, 1.0)
         d.lora_expand(s["h"], s["B"], s["y"], SCALE)
+
+    def det_counted_one_launch(self, s, M):
+        """Shrink and expand in one launch with arrival counters."""
+        self.dsl.lora_shrink_expand_counted(s["x"], s["A"], s["B"], s["y"], s["ws"], self.cnt_se, SPLIT, 1.0, SCALE,
+                                            h=s["h"])
 
     def det_one_launch(self, s, M):
         self.dsl.lora_shrink_expand_fused(s["x"], s["A"], s["B"], s["y"], SPLIT, 1.0, SCALE, h=s["h"])
@@ -186,14 +196,18 @@ class Bench:
         a = self.args
         K, W = a.steps, a.warmup
         res = {}
-        # the timed step: the four batch sizes back to back, one graph per copy
-        det_g = self.capture(self.det, M_LIST)
-        ms_det = self.time_graphs(det_g, K, W)
+        # the timed steps: the four batch sizes back to back; each HIP graph
+        # holds SPG consecutive steps on SPG input copies, replayed K / SPG
+        # times, so exactly K steps run in the timed region
+        spg = STEPS_PER_GRAPH if K % STEPS_PER_GRAPH == 0 else 1
+        det_g = self.capture(self.det, M_LIST, spg)
+        ms_det = self.time_graphs(det_g, K // spg, max(1, W // spg)) / spg
         del det_g
         res["ms_per_step"] = ms_det
         res["us_per_call"] = ms_det * 1000 / len(M_LIST)
-        res["atomic_us_per_call"] = self.per_call_us(self.atomic, M_LIST, 1, K) / len(M_LIST)
-        res["det_two_call_us_per_call"] = self.per_call_us(self.det_two_call, M_LIST, 1, K) / len(M_LIST)
+        res["steps_per_graph"] = spg
+        res["atomic_us_per_call"] = self.per_call_us(self.atomic, M_LIST, spg, K) / len(M_LIST)
+        res["det_two_call_us_per_call"] = self.per_call_us(self.det_two_call, M_LIST, spg, K) / len(M_LIST)
         # per batch size: 8 calls per graph on 8 copies keep graph-launch cost out
         per_m = {}
         for M in M_LIST:
@@ -203,12 +217,14 @@ class Bench:
             u2 = self.per_call_us(self.det_two_launch, (M,), 8, K)
             u1 = self.per_call_us(self.det_one_launch, (M,), 8, K)
             uc = self.per_call_us(self.det_counted, (M,), 8, K)
+            uq = self.per_call_us(self.det_counted_one_launch, (M,), 8, K)
             byt = shrink_bytes(M, K_HID, RANK) + expand_bytes(M, RANK, N_OUT)
             log(f"bench: M={M} timed")
             per_m[str(M)] = {"det_us": round(ud, 3), "atomic_us": round(ua, 3),
                              "det_launches": self.dsl.lora_shrink_expand_launches(M, K_HID, RANK, N_OUT, SPLIT),
                              "det_one_launch_us": round(u1, 3), "det_two_launch_us": round(u2, 3),
                              "det_three_launch_us": round(u3, 3), "det_counted_shrink_then_expand_us": round(uc, 3),
+                             "det_counted_one_launch_us": round(uq, 3),
                              "det_over_atomic": round(ud / ua, 4), "bytes": byt,
                              "workspace_bytes": 8 * SPLIT * M * RANK,
                              "det_GBps": round(byt / ud / 1e3, 1),
@@ -325,6 +341,172 @@ def copy_roofline(args, nbytes_list):
     return out
 
 
+def launch_floor(args):
+    """Per-launch floor on this GPU and stream, timed like everything else
+    (8 launches per HIP graph): an empty kernel, and a one-workgroup kernel
+    that writes 64 bytes."""
+    import torch
+    tiny = [torch.zeros(16, dtype=torch.float32, device="cuda") for _ in range(8)]
+    sets = [dict(t=t) for t in tiny]
+    empty = _time_rotating(lambda st: torch.cuda._sleep(0), sets, args)
+    one_wg = _time_rotating(lambda st: st["t"].zero_(), sets, args)
+    return {"empty_kernel_us": round(empty, 3), "one_workgroup_kernel_us": round(one_wg, 3)}
+
+
+def gpu_tensor(a, dev):
+    return torch_from_bf16(a).to(dev)
+
+
+def torch_from_bf16(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+
+
+def shrink_only_bench(args):
+    """The shrink alone at the small correctness shape (M=8, K=1024, r=8,
+    Split-K 8, scale 1): deterministic two launches (partials, tree),
+    deterministic single launch (arrival counters) and atomic (fill + atomic
+    partials)."""
+    import torch
+    import deterministic_split_lora_amd as dsl
+    from synth import single_adapter_case
+    M, K, r, S = 8, 1024, 8, 8
+    c = single_adapter_case(M, K, r, 0, split_k=S, scale=1.0, seed=0)
+    dev = torch.device("cuda:0")
+    per = 2 * M * K + 2 * K * r
+    copies = max(8, math.ceil(ROTATE_BYTES / 64 / per))
+    sets = [dict(x=gpu_tensor(c.x, dev), A=gpu_tensor(c.A, dev),
+                 h=torch.empty((M, r), dtype=torch.float32, device=dev),
+                 ws=torch.empty(dsl.lora_shrink_workspace_bytes(M, r, S), dtype=torch.uint8, device=dev))
+            for _ in range(copies)]
+    cnt = torch.zeros(dsl.lora_shrink_counter_bytes(M) // 4, dtype=torch.int32, device=dev)
+    out = {"workload": "shrink only: x [8 x 1024], A [8 x 1024] bf16, Split-K 8, scale 1",
+           "bytes": shrink_bytes(M, K, r), "copies": copies}
+    calls = {
+        "det_two_launch": lambda st: dsl.lora_shrink_splitk(st["x"], st["A"], st["h"], st["ws"], S, 1.0),
+        "det_one_launch": lambda st: dsl.lora_shrink_splitk_counted(st["x"], st["A"], st["h"], st["ws"], cnt, S,
+                                                                    1.0),
+        "atomic": lambda st: dsl.lora_shrink_splitk_atomic(st["x"], st["A"], st["h"], S, 1.0),
+    }
+    for name, call in calls.items():
+        out[name + "_us"] = round(_time_rotating(call, sets, args), 3)
+    out["det_over_atomic"] = round(min(out["det_two_launch_us"], out["det_one_launch_us"]) / out["atomic_us"], 4)
+    return out
+
+
+def batch_sweep_bench(args):
+    """Deterministic shrink + expand vs the atomic contrast for batch sizes
+    1 .. 1024 at the MLP down-projection shape (K=14336, r=32, N=4096,
+    Split-K 8, scale 2): the cost of a plan that never depends on M."""
+    import torch
+    import deterministic_split_lora_amd as dsl
+    from synth import single_adapter_case
+    K, r, N, S, Mmax = 14336, 32, 4096, 8, 1024
+    c = single_adapter_case(Mmax, K, r, N, split_k=S, seed=0)
+    dev = torch.device("cuda:0")
+    per = 2 * Mmax * K + 2 * Mmax * N + 4 * K * r
+    copies = max(8, math.ceil(ROTATE_BYTES / per))
+    base = dict(x=gpu_tensor(c.x, dev), A=gpu_tensor(c.A, dev), B=gpu_tensor(c.B, dev), y=gpu_tensor(c.y, dev))
+    sets = [dict({k: v.clone() for k, v in base.items()},
+                 h=torch.empty((Mmax, r), dtype=torch.float32, device=dev),
+                 ws=torch.empty(dsl.lora_shrink_expand_workspace_bytes(Mmax, r, S), dtype=torch.uint8, device=dev))
+            for _ in range(copies)]
+    del base
+    out = {"workload": "x [b x 14336], A [32 x 14336], B [4096 x 32], y [b x 4096] bf16, Split-K 8, scale 2",
+           "copies": copies, "points": {}}
+    b = 1
+    while b <= Mmax:
+        def det(st, b=b):
+            dsl.lora_shrink_expand(st["x"][:b], st["A"], st["B"], st["y"][:b], st["ws"], S, 1.0, SCALE,
+                                   h=st["h"][:b])
+
+        def atomic(st, b=b):
+            dsl.lora_shrink_splitk_atomic(st["x"][:b], st["A"], st["h"][:b], S, 1.0)
+            dsl.lora_expand(st["h"][:b], st["B"], st["y"][:b], SCALE)
+        ud = _time_rotating(det, sets, args)
+        ua = _time_rotating(atomic, sets, args)
+        byt = shrink_bytes(b, K, r) + expand_bytes(b, r, N)
+        out["points"][str(b)] = {"det_us": round(ud, 3), "atomic_us": round(ua, 3),
+                                 "det_over_atomic": round(ud / ua, 4), "bytes": byt,
+                                 "det_pct_hbm_peak": round(100 * byt / ud / 1e3 / HBM_PEAK_GBS, 2)}
+        b *= 2
+    return out
+
+
+def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S):
+    """Multi-adapter shrink and expand on a prebuilt plan, cold cache.
+    Compulsory bytes count only the adapters some token uses, at their own
+    rank: shrink 2MK + 2K sum(r) + 4 M r_max (h), expand 4 sum_i r_(a_i) (h)
+    + 2N sum(r) + 4 M' N (y read and written for the M' tokens with an
+    adapter)."""
+    import torch
+    import deterministic_split_lora_amd as dsl
+    from synth import sgmv_case
+    c = sgmv_case(M, K, N, ranks, seg_lo, seg_hi, S, seed=0, tag=label)
+    dev = torch.device("cuda:0")
+    n = len(c.ranks)
+    valid = (c.ids >= 0) & (c.ids < n)
+    touched = sorted(set(int(a) for a in c.ids[valid]))
+    sum_r = sum(int(c.ranks[a]) for a in touched)
+    sh_bytes = 2 * M * K + 2 * K * sum_r + 4 * M * c.r_max
+    ex_bytes = 4 * int(sum(int(c.ranks[a]) for a in c.ids[valid])) + 2 * N * sum_r + 4 * int(valid.sum()) * N
+    per = sh_bytes + ex_bytes
+    copies = max(2, math.ceil(ROTATE_BYTES / per))
+    base_x, base_y = gpu_tensor(c.x, dev), gpu_tensor(c.y, dev)
+    base_A = [gpu_tensor(a, dev) for a in c.As]
+    base_B = [gpu_tensor(b, dev) for b in c.Bs]
+    ranks_g = torch.from_numpy(c.ranks).to(dev)
+    scales_g = torch.from_numpy(c.scales).to(dev)
+    ids_g = torch.from_numpy(c.ids).to(dev)
+    plan = torch.empty(dsl.lora_sgmv_plan_bytes(M), dtype=torch.uint8, device=dev)
+    dsl.lora_sgmv_plan(ids_g, n, plan)
+    cnt = torch.zeros(dsl.lora_sgmv_counter_bytes(M) // 4, dtype=torch.int32, device=dev)
+    sets = []
+    for i in range(copies):
+        As = [a.clone() for a in base_A] if i else base_A
+        Bs = [b.clone() for b in base_B] if i else base_B
+        sets.append(dict(x=base_x.clone() if i else base_x, y=base_y.clone() if i else base_y, A=As, B=Bs,
+                         Ap=torch.tensor([a.data_ptr() for a in As], dtype=torch.int64, device=dev),
+                         Bp=torch.tensor([b.data_ptr() for b in Bs], dtype=torch.int64, device=dev),
+                         h=torch.empty((M, c.r_max), dtype=torch.float32, device=dev),
+                         ws=torch.empty(dsl.lora_sgmv_workspace_bytes(M, c.r_max, S), dtype=torch.uint8,
+                                        device=dev)))
+    torch.cuda.synchronize()
+
+    def shrink(st):
+        dsl.lora_sgmv_shrink(st["x"], st["Ap"], K, ranks_g, scales_g, ids_g, n, plan, st["h"], c.r_max, S, st["ws"])
+
+    def shrink_counted(st):
+        dsl.lora_sgmv_shrink_counted(st["x"], st["Ap"], K, ranks_g, scales_g, n, plan, st["h"], c.r_max, S,
+                                     st["ws"], cnt)
+
+    def expand(st):
+        dsl.lora_sgmv_expand(st["h"], st["Bp"], ranks_g, scales_g, ids_g, n, st["y"], c.r_max)
+
+    def both(st):
+        shrink(st)
+        expand(st)
+
+    def plan_only(st):
+        dsl.lora_sgmv_plan(ids_g, n, plan)
+
+    out = {"workload": f"M={M}, K={K}, N={N}, {n} adapters of ranks {sorted(set(int(v) for v in c.ranks))}, "
+                       f"segments {seg_lo}..{seg_hi} tokens, Split-K {S}",
+           "segments": len(c.segs), "touched_adapters": len(touched), "shrink_bytes": sh_bytes,
+           "expand_bytes": ex_bytes, "workspace_bytes": 8 * S * M * c.r_max, "copies": copies}
+    for name, call, byt in (("shrink", shrink, sh_bytes), ("shrink_one_launch", shrink_counted, sh_bytes),
+                            ("expand", expand, ex_bytes), ("shrink_expand", both, sh_bytes + ex_bytes),
+                            ("plan", plan_only, 0)):
+        us = _time_rotating(call, sets, args)
+        out[name] = {"us": round(us, 3)}
+        if byt:
+            out[name]["GBps"] = round(byt / us / 1e3, 1)
+            out[name]["pct_hbm_peak"] = round(100 * byt / us / 1e3 / HBM_PEAK_GBS, 2)
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
 def decode_probe(args, M=32):
     """M decode tokens, each with its own rank-64 adapter, hidden 8192, Split-K 8:
     the multi-adapter deterministic shrink (partials + fixed tree) on a prebuilt
@@ -429,6 +611,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-configs", action="store_true", help="skip the other shapes (sweep, multi-adapter)")
     ap.add_argument("--counters", action="store_true",
                     help="only run the step eagerly for a hardware-counter profile; prints no JSON")
     args = ap.parse_args()
@@ -443,12 +626,24 @@ def main():
     b = Bench(args)
     res = b.run()
     log("bench: main timing done")
-    probe = wide = roof = None
+    probe = wide = roof = floor = extra = None
     if not args.no_probe:
         probe = decode_probe(args, 32)
         wide = decode_probe(args, 128)
-        roof = copy_roofline(args, [probe["bytes"], wide["bytes"], 64 << 20])
+        avg = int(res["roofline"]["algorithmic_bytes_per_launch"]) // 2 // 16 * 16
+        roof = copy_roofline(args, [avg, probe["bytes"], wide["bytes"], 64 << 20])
+        floor = launch_floor(args)
         log("bench: probes done")
+    if not args.no_configs:
+        extra = {"shrink_only_m8_k1024_r8": shrink_only_bench(args)}
+        log("bench: shrink-only shape done")
+        extra["batch_sweep_k14336_r32_n4096"] = batch_sweep_bench(args)
+        log("bench: batch sweep done")
+        extra["sgmv_m512_k4096_n6144_4x_r64"] = sgmv_bench(args, "b3", 512, 4096, 6144, [64] * 4, 1, 64, 8)
+        log("bench: sgmv 512 done")
+        extra["sgmv_prefill_m4096_k8192_n28672_32_adapters"] = sgmv_bench(args, "b5", 4096, 8192, 28672,
+                                                                          [8, 16, 32, 64] * 8, 32, 512, 16)
+        log("bench: sgmv prefill done")
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
     import torch
     out = {
@@ -481,6 +676,8 @@ def main():
         "decode_bandwidth_probe": probe,
         "decode_bandwidth_probe_wide": wide,
         "copy_roofline": roof,
+        "launch_floor": floor,
+        "other_shapes": extra,
         "device": torch.cuda.get_device_name(0),
     }
     print(json.dumps(out), flush=True)

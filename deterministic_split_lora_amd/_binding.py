@@ -30,6 +30,7 @@ EXPORTED = [
     "lora_shrink_expand_workspace_bytes", "lora_shrink_expand", "lora_shrink_partials", "lora_expand_combine",
     "lora_shrink_expand_fused", "lora_shrink_expand_launches", "lora_shrink_counter_bytes",
     "lora_shrink_splitk_counted", "lora_sgmv_counter_bytes", "lora_sgmv_shrink_counted",
+    "lora_shrink_expand_counter_bytes", "lora_shrink_expand_counted",
 ]
 
 
@@ -84,6 +85,11 @@ def lib():
         L.lora_shrink_expand.restype = ctypes.c_int
         L.lora_shrink_expand.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32,
                                          _i64, _i32, _f32, _f32, _vp, _sz, _vp]
+        L.lora_shrink_expand_counter_bytes.restype = _sz
+        L.lora_shrink_expand_counter_bytes.argtypes = [_i64]
+        L.lora_shrink_expand_counted.restype = ctypes.c_int
+        L.lora_shrink_expand_counted.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
+                                                 _i32, _i64, _i32, _f32, _f32, _vp, _sz, _vp, _sz, _vp]
         L.lora_shrink_counter_bytes.restype = _sz
         L.lora_shrink_counter_bytes.argtypes = [_i64]
         L.lora_sgmv_counter_bytes.restype = _sz
@@ -114,8 +120,7 @@ def lib():
         L.lora_sgmv_shrink.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _sz, _vp, _i64, _i64,
                                        _i64, _i32, _i32, _vp, _sz, _vp]
         L.lora_sgmv_expand.restype = ctypes.c_int
-        L.lora_sgmv_expand.argtypes = [_vp, _i64, _vp, _vp, _vp, _i32, _vp, _sz, _vp, _i64, _i64, _i64, _i32,
-                                       _vp]
+        L.lora_sgmv_expand.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _i32, _vp]
         _lib = L
     return _lib
 
@@ -281,6 +286,35 @@ def lora_shrink_expand(x, A, B, y, workspace, split_k: int = 8, shrink_scale: fl
     return y
 
 
+def lora_shrink_expand_counter_bytes(M: int) -> int:
+    return int(lib().lora_shrink_expand_counter_bytes(M))
+
+
+def lora_shrink_expand_counted(x, A, B, y, workspace, counters, split_k: int = 8, shrink_scale: float = 1.0,
+                               expand_scale: float = 1.0, h=None, stream=None):
+    """Deterministic shrink then expand in one launch; counters: zero-initialised
+    int32 GPU tensor of lora_shrink_expand_counter_bytes(M) / 4 elements
+    (element 0 is the status word, 0 after a complete call)."""
+    import torch
+    _dtype(x, torch.bfloat16, "x"); _dtype(A, torch.bfloat16, "A")
+    _dtype(B, torch.bfloat16, "B"); _dtype(y, torch.bfloat16, "y")
+    if h is not None:
+        _dtype(h, torch.float32, "h")
+    if counters is not None:
+        _dtype(counters, torch.int32, "counters")
+    M, K = x.shape
+    r = A.shape[0]
+    N = y.shape[1]
+    if y.shape[0] != M:
+        raise ValueError("x and y must have the same number of rows")
+    st = lib().lora_shrink_expand_counted(_ptr(x), _ld(x, "x"), _ptr(A), _ld(A, "A"), _ptr(B), _ld(B, "B"),
+                                          _ptr(h), _ld(h, "h") if h is not None else 0, _ptr(y), _ld(y, "y"), M, K,
+                                          r, N, split_k, shrink_scale, expand_scale, _ptr(workspace),
+                                          _nbytes(workspace), _ptr(counters), _nbytes(counters), _stream(stream, x))
+    _check(st, "lora_shrink_expand_counted")
+    return y
+
+
 def lora_shrink_expand_launches(M: int, K: int, r: int, N: int, split_k: int) -> int:
     return int(lib().lora_shrink_expand_launches(M, K, r, N, split_k))
 
@@ -378,15 +412,12 @@ def lora_sgmv_shrink_counted(x, A_ptrs, ld_a: int, ranks, scales, n_adapters: in
     return h
 
 
-def lora_sgmv_expand(h, B_ptrs, ranks, scales, n_adapters: int, plan, y, r_max: int, stream=None):
-    """B_ptrs: int64 GPU tensor of adapter weight addresses ([N][round_up(r_a, 8)] bf16 each)."""
+def lora_sgmv_expand(h, B_ptrs, ranks, scales, token_adapter, n_adapters: int, y, r_max: int, stream=None):
+    """Multi-adapter expand, y updated in place for tokens with an adapter."""
     import torch
-    _dtype(h, torch.float32, "h"); _dtype(y, torch.bfloat16, "y")
-    _dtype(B_ptrs, torch.int64, "B_ptrs"); _dtype(ranks, torch.int32, "ranks")
-    if scales is not None:
-        _dtype(scales, torch.float32, "scales")
+    _dtype(h, torch.float32, "h"); _dtype(y, torch.bfloat16, "y"); _dtype(token_adapter, torch.int32, "ids")
     M, N = y.shape
-    st = lib().lora_sgmv_expand(_ptr(h), _ld(h, "h"), _ptr(B_ptrs), _ptr(ranks), _ptr(scales), n_adapters,
-                                _ptr(plan), _nbytes(plan), _ptr(y), _ld(y, "y"), M, N, r_max, _stream(stream, y))
+    st = lib().lora_sgmv_expand(_ptr(h), _ld(h, "h"), _ptr(B_ptrs), _ptr(ranks), _ptr(scales), _ptr(token_adapter),
+                                n_adapters, _ptr(y), _ld(y, "y"), M, N, r_max, _stream(stream, y))
     _check(st, "lora_sgmv_expand")
     return y

@@ -12,8 +12,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "liblora_det.so")
-SOURCES = ["abi.hip", "shrink.hip", "expand.hip", "fused.hip", "sgmv_plan.hip"]
-HEADERS = ["device.h", "kernels.h"]
+SOURCES = ["abi.hip", "shrink.hip", "expand.hip", "fused.hip", "streamed.hip", "sgmv_plan.hip"]
+HEADERS = ["device.h", "kernels.h", "shrink_tile.h"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

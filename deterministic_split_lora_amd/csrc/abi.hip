@@ -179,6 +179,8 @@ int launch_fused(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_
                  int64_t ld_b, float* h, int64_t ld_h, uint16_t* y, int64_t ld_y, int64_t M, int32_t r, int64_t N,
                  const lora_shrink_plan_t& pl, float shrink_scale, float expand_scale, void* stream)
 {
+    if (fused_grid(M, N) > kMaxGrid)
+        return LORA_ERR_SHAPE;
     FusedParams p{};
     p.x = x;
     p.ld_x = ld_x;
@@ -471,6 +473,69 @@ int lora_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64
                                expand_scale, stream);
 }
 
+size_t lora_shrink_expand_counter_bytes(int64_t M)
+{
+    if (M < 0 || M > kMaxDim)
+        return 0;
+    return 16 + (size_t)8 * (size_t)((M + kRowBlock - 1) / kRowBlock);
+}
+
+int lora_shrink_expand_counted(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a, const uint16_t* B,
+                               int64_t ld_b, float* h, int64_t ld_h, uint16_t* y, int64_t ld_y, int64_t M,
+                               int64_t K, int32_t r, int64_t N, int32_t split_k, float shrink_scale,
+                               float expand_scale, void* workspace, size_t ws_bytes, int32_t* counters,
+                               size_t counter_bytes, void* stream)
+{
+    lora_shrink_plan_t pl;
+    int st = check_shrink_expand(x, ld_x, A, ld_a, B, ld_b, h, ld_h, y, ld_y, M, K, r, N, split_k, &pl);
+    if (st != LORA_OK)
+        return st;
+    // per row block: split_k x groups shrink workgroups, then one expand
+    // workgroup per waves x 64 columns
+    const int gt = group_tiles_for(M, split_k, pl.rank_tiles);
+    const int64_t producers = (int64_t)split_k * ((pl.rank_tiles + gt - 1) / gt);
+    const int64_t consumers = (N + pl.waves * 64 - 1) / (pl.waves * 64);
+    if (((M + kRowBlock - 1) / kRowBlock) * (producers + consumers) > kMaxGrid)
+        return LORA_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return LORA_OK;
+    if (!workspace || !counters)
+        return LORA_ERR_NULL;
+    if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(counters) & 3u))
+        return LORA_ERR_ALIGN;
+    if (ws_bytes < workspace_bytes(M, r, split_k) || counter_bytes < lora_shrink_expand_counter_bytes(M))
+        return LORA_ERR_WORKSPACE;
+    ShrinkParams sp = shrink_params(x, ld_x, A, ld_a, M, r, pl, 1.0f);
+    sp.out = static_cast<float*>(workspace);
+    sp.ld_out = r;
+    sp.split_stride = M * r;
+    TreeParams t{};
+    t.ws = static_cast<const float*>(workspace);
+    t.split_stride = M * r;
+    t.ldw = r;
+    t.h = h;
+    t.ld_h = ld_h;
+    t.M = M;
+    t.ncols = r;
+    t.scale = shrink_scale;
+    ExpandParams ep{};
+    ep.B = B;
+    ep.ld_b = ld_b;
+    ep.y = y;
+    ep.ld_y = ld_y;
+    ep.M = M;
+    ep.N = N;
+    ep.r = r;
+    ep.r_max = r;
+    ep.scale = expand_scale;
+    StreamParams q{};
+    q.status = counters;
+    q.counters = counters + 4;
+    q.producers = (int32_t)producers;
+    q.consumers = (int32_t)consumers;
+    return launch_status(launch_shrink_expand_counted(sp, ep, t, q, pl.waves, gt, static_cast<hipStream_t>(stream)));
+}
+
 size_t lora_shrink_counter_bytes(int64_t M)
 {
     if (M < 0 || M > kMaxDim)
@@ -668,32 +733,30 @@ int lora_sgmv_shrink(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_p
 }
 
 int lora_sgmv_expand(const float* h, int64_t ld_h, const uint16_t* const* B_ptrs, const int32_t* ranks,
-                     const float* scales, int32_t n_adapters, const void* plan, size_t plan_bytes, uint16_t* y,
+                     const float* scales, const int32_t* token_adapter, int32_t n_adapters, uint16_t* y,
                      int64_t ld_y, int64_t M, int64_t N, int32_t r_max, void* stream)
 {
     if (M < 0 || M > kMaxDim || N < 0 || N > kMaxDim || n_adapters < 1)
         return LORA_ERR_SHAPE;
     if (r_max < 1 || r_max > 64 || N % 8 != 0)
         return LORA_ERR_UNSUPPORTED;
-    if (!sgmv_items_fit(M, 1, N))
+    if (((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols) > kMaxGrid)
         return LORA_ERR_SHAPE;
     if (M == 0 || N == 0)
         return LORA_OK;
-    if (!h || !B_ptrs || !ranks || !plan || !y)
+    if (!h || !B_ptrs || !ranks || !token_adapter || !y)
         return LORA_ERR_NULL;
     if (ld_h < r_max || ld_y < N)
         return LORA_ERR_SHAPE;
-    if (!aligned16(h) || !aligned16(y) || !aligned16(plan) || ld_h % 4 || ld_y % 8)
+    if (!aligned16(h) || !aligned16(y) || ld_h % 4 || ld_y % 8)
         return LORA_ERR_ALIGN;
-    if (plan_bytes < lora_sgmv_plan_bytes(M))
-        return LORA_ERR_WORKSPACE;
     ExpandParams p{};
     p.h = h;
     p.ld_h = ld_h;
     p.B_ptrs = B_ptrs;
     p.ranks = ranks;
     p.scales = scales;
-    p.tiles = static_cast<const int32_t*>(plan);
+    p.ids = token_adapter;
     p.y = y;
     p.ld_y = ld_y;
     p.M = M;
@@ -702,10 +765,7 @@ int lora_sgmv_expand(const float* h, int64_t ld_h, const uint16_t* const* B_ptrs
     p.r_max = r_max;
     p.n_adapters = n_adapters;
     p.scale = 1.0f;
-    const int64_t nblocks = (N + kExpandCols - 1) / kExpandCols;
-    const int64_t items_bound = M * nblocks;
-    const int grid = (int)(items_bound < 8192 ? items_bound : 8192);
-    return launch_status(launch_sgmv_expand(p, grid, static_cast<hipStream_t>(stream)));
+    return launch_status(launch_sgmv_expand(p, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

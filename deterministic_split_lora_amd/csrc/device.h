@@ -119,11 +119,9 @@ __device__ __forceinline__ ExpandLane expand_lane(int64_t row0, int nrows, int64
     return L;
 }
 
-// Loads this lane's 16 y values and its B operand rows (KS steps of 32 over r).
-template <int KS>
-__device__ __forceinline__ void expand_load(const ExpandLane& L, const uint16_t* y, int64_t ld_y, int64_t N,
-                                            const uint16_t* __restrict__ B, int64_t ld_b, int r, u16x8 (&yv)[2],
-                                            bf16x8 (&bop)[4][KS])
+// This lane's 16 y values (zeros for a row outside the block).
+__device__ __forceinline__ void expand_load_y(const ExpandLane& L, const uint16_t* y, int64_t ld_y, int64_t N,
+                                              u16x8 (&yv)[2])
 {
     const int64_t n0 = L.n_base + 16 * L.g;
     const uint16_t* yp = y + L.row * ld_y + n0;
@@ -131,6 +129,13 @@ __device__ __forceinline__ void expand_load(const ExpandLane& L, const uint16_t*
     for (int half = 0; half < 2; ++half)
         yv[half] = (L.row_ok && n0 + half * 8 < N) ? *reinterpret_cast<const u16x8*>(yp + half * 8)
                                                   : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+}
+
+// This lane's B operand rows (KS steps of 32 over r; zeros past r and N).
+template <int KS>
+__device__ __forceinline__ void expand_load_b(const ExpandLane& L, int64_t N, const uint16_t* __restrict__ B,
+                                              int64_t ld_b, int r, bf16x8 (&bop)[4][KS])
+{
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
         const int64_t n = L.n_base + (L.li >> 2) * 16 + t * 4 + (L.li & 3);
@@ -143,20 +148,23 @@ __device__ __forceinline__ void expand_load(const ExpandLane& L, const uint16_t*
     }
 }
 
-// bf16(h) of the block's token rows (hrows: row 0 of the block, stride ld_hr),
-// the matrix-core steps, and the y update.  N % 8 == 0, so 8-column chunks
-// are whole.
+// Loads this lane's 16 y values and its B operand rows.
 template <int KS>
-__device__ __forceinline__ void expand_finish(const ExpandLane& L, uint16_t* y, int64_t ld_y, int64_t N,
-                                              const float* hrows, int64_t ld_hr, int r, float scale,
-                                              const u16x8 (&yv)[2], const bf16x8 (&bop)[4][KS])
+__device__ __forceinline__ void expand_load(const ExpandLane& L, const uint16_t* y, int64_t ld_y, int64_t N,
+                                            const uint16_t* __restrict__ B, int64_t ld_b, int r, u16x8 (&yv)[2],
+                                            bf16x8 (&bop)[4][KS])
 {
-    bf16x8 hb[KS];
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const int j0 = ks * kKStep + 8 * L.g;
-        hb[ks] = (L.row_ok && j0 < r) ? load_h_as_bf16(hrows + L.li * ld_hr + j0, j0, r) : bf16x8_zero();
-    }
+    expand_load_y(L, y, ld_y, N, yv);
+    expand_load_b<KS>(L, N, B, ld_b, r, bop);
+}
+
+// The matrix-core steps and the y update, given this lane's bf16(h) operand
+// (its token's h[j], j = 32 ks + 8 g .. + 7, zeros from r on).
+template <int KS>
+__device__ __forceinline__ void expand_mma_store(const ExpandLane& L, uint16_t* y, int64_t ld_y, int64_t N,
+                                                 const bf16x8 (&hb)[KS], float scale, const u16x8 (&yv)[2],
+                                                 const bf16x8 (&bop)[4][KS])
+{
     f32x4 acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -180,6 +188,91 @@ __device__ __forceinline__ void expand_finish(const ExpandLane& L, uint16_t* y, 
             }
             *reinterpret_cast<u16x8*>(yp + half * 8) = o;
         }
+    }
+}
+
+// bf16(h) of the block's token rows (hrows: row 0 of the block, stride ld_hr),
+// the matrix-core steps, and the y update.  N % 8 == 0, so 8-column chunks
+// are whole.
+template <int KS>
+__device__ __forceinline__ void expand_finish(const ExpandLane& L, uint16_t* y, int64_t ld_y, int64_t N,
+                                              const float* hrows, int64_t ld_hr, int r, float scale,
+                                              const u16x8 (&yv)[2], const bf16x8 (&bop)[4][KS])
+{
+    bf16x8 hb[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int j0 = ks * kKStep + 8 * L.g;
+        hb[ks] = (L.row_ok && j0 < r) ? load_h_as_bf16(hrows + L.li * ld_hr + j0, j0, r) : bf16x8_zero();
+    }
+    expand_mma_store<KS>(L, y, ld_y, N, hb, scale, yv, bop);
+}
+
+// ---------------------------------------------------------------------------
+// Staging of an h tile for the expands that walk several 16-token tiles per
+// workgroup: 16 rows x round_up(r, 8) columns of bf16(h) in LDS (row stride
+// kHbStride), zeros past r and for rows outside the tile.  Each of the first
+// 16 * round_up(r, 8) / 4 threads converts one group of 4 columns, read with
+// one 16-byte load (h is 16-byte aligned with ld_h % 4 == 0, so a group that
+// starts below r ends inside the row's ld_h).
+// ---------------------------------------------------------------------------
+constexpr int kHbStride = 72;             // bf16 per LDS row (64 + 8 padding)
+
+struct HStageSlot {
+    int row;
+    int col;
+    bool on;
+};
+
+__device__ __forceinline__ HStageSlot h_stage_slot(int r)
+{
+    const int q = ((r + 7) & ~7) / 4;     // 4-column groups per row, 2 .. 16
+    HStageSlot s;
+    s.row = (int)threadIdx.x / q;
+    s.col = ((int)threadIdx.x - s.row * q) * 4;
+    s.on = s.row < 16;
+    return s;
+}
+
+__device__ __forceinline__ void h_stage(const HStageSlot& s, const float* h, int64_t ld_h, int64_t row0, int nrows,
+                                        int r, uint16_t* tile)
+{
+    if (!s.on)
+        return;
+    float f[4] = {0.f, 0.f, 0.f, 0.f};
+    if (s.row < nrows && s.col < r) {
+        const float4 v = *reinterpret_cast<const float4*>(h + (row0 + s.row) * ld_h + s.col);
+        f[0] = v.x;
+        f[1] = s.col + 1 < r ? v.y : 0.f;
+        f[2] = s.col + 2 < r ? v.z : 0.f;
+        f[3] = s.col + 3 < r ? v.w : 0.f;
+    }
+    uint16_t* d = tile + s.row * kHbStride + s.col;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        d[e] = f32_to_bf16_bits(f[e]);
+}
+
+// This lane's bf16(h) operand from a staged tile, zeros from column `r` on
+// (r may be below the staged width: a lower adapter rank).
+template <int KS>
+__device__ __forceinline__ void hb_from_tile(const ExpandLane& L, const uint16_t* tile, int r, bf16x8 (&hb)[KS])
+{
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int j0 = ks * kKStep + 8 * L.g;
+        if (!L.row_ok || j0 >= r) {
+            hb[ks] = bf16x8_zero();
+            continue;
+        }
+        u16x8 v = *reinterpret_cast<const u16x8*>(tile + L.li * kHbStride + j0);
+        if (j0 + 8 > r) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (j0 + e >= r)
+                    v[e] = 0;
+        }
+        hb[ks] = __builtin_bit_cast(bf16x8, v);
     }
 }
 

@@ -61,6 +61,56 @@ __global__ __launch_bounds__(256) void k_expand(ExpandParams p)
     expand_finish<KS>(L, p.y, p.ld_y, p.N, p.h + row0 * p.ld_h, p.ld_h, p.r, p.scale, yv, bop);
 }
 
+// Single adapter, large M: a workgroup walks R consecutive 16-token tiles of
+// one 256-column block.  Its B operands are loaded once and stay in
+// registers; each tile's h rows are converted to bf16 once into LDS (double
+// buffered, one barrier per tile) instead of once per wave; the next tile's y
+// is loaded before the current one is finished.  Per element this is the
+// arithmetic of k_expand (same operands, steps and epilogue code); it only
+// reads B and h fewer times, which is what limits the one-tile-per-workgroup
+// kernel once M x N is large (its B and h loads keep the address units busy).
+__device__ __forceinline__ int tile_rows(int64_t M, int64_t row0)
+{
+    const int64_t left = M - row0;
+    return left < kRowBlock ? (int)left : kRowBlock;
+}
+
+template <int KS>
+__global__ __launch_bounds__(256) void k_expand_rows(ExpandParams p, int R)
+{
+    __shared__ __align__(16) uint16_t hs[2][kRowBlock * kHbStride];
+    const uint32_t nblocks = (uint32_t)((p.N + kExpandCols - 1) / kExpandCols);
+    const int64_t col0 = (int64_t)(blockIdx.x % nblocks) * kExpandCols;
+    const int64_t row_base = (int64_t)(blockIdx.x / nblocks) * kRowBlock * R;
+    const int64_t left = (p.M - row_base + kRowBlock - 1) / kRowBlock;
+    const int tiles = left < R ? (int)left : R;
+    const HStageSlot slot = h_stage_slot(p.r);
+    ExpandLane L = expand_lane(row_base, tile_rows(p.M, row_base), col0);
+    u16x8 yv[2];
+    bf16x8 bop[4][KS];
+    expand_load<KS>(L, p.y, p.ld_y, p.N, p.B, p.ld_b, p.r, yv, bop);
+    h_stage(slot, p.h, p.ld_h, row_base, tile_rows(p.M, row_base), p.r, hs[0]);
+    for (int i = 0; i < tiles; ++i) {
+        __syncthreads();                 // tile i staged; the other buffer is free
+        ExpandLane Ln = L;
+        u16x8 yn[2] = {u16x8{0, 0, 0, 0, 0, 0, 0, 0}, u16x8{0, 0, 0, 0, 0, 0, 0, 0}};
+        if (i + 1 < tiles) {
+            const int64_t r1 = row_base + (int64_t)kRowBlock * (i + 1);
+            Ln = expand_lane(r1, tile_rows(p.M, r1), col0);
+            expand_load_y(Ln, p.y, p.ld_y, p.N, yn);
+            h_stage(slot, p.h, p.ld_h, r1, tile_rows(p.M, r1), p.r, hs[(i + 1) & 1]);
+        }
+        if (L.n_base < p.N) {
+            bf16x8 hb[KS];
+            hb_from_tile<KS>(L, hs[i & 1], p.r, hb);
+            expand_mma_store<KS>(L, p.y, p.ld_y, p.N, hb, p.scale, yv, bop);
+        }
+        L = Ln;
+        yv[0] = yn[0];
+        yv[1] = yn[1];
+    }
+}
+
 // Fused: the fixed pairwise tree over the Split-K workspace for this row block
 // (exactly the second pass of the deterministic shrink: tree, then one
 // multiply by the shrink scale) is evaluated into an LDS tile, written out as
@@ -105,37 +155,156 @@ __global__ __launch_bounds__(256) void k_expand_combine(ExpandParams p, TreePara
     expand_finish<KS>(L, p.y, p.ld_y, p.N, hs, kHTileStride, r, p.scale, yv, bop);
 }
 
-// Multi-adapter: a fixed grid walks the plan's (tile, column block) items.
+// Multi-adapter: the single-adapter expand's grid, one workgroup per
+// (16-token row block, 256 columns), every wave on its own.  Each lane reads
+// its token's adapter id; tokens without one (id outside [0, n_adapters))
+// are neither read nor written.  A matrix-core step shares its B operand
+// across the 16 tokens, so the wave makes one pass per distinct adapter among
+// its tokens (in the order of their first token; one pass when the block lies
+// inside one run of equal ids): the pass loads that adapter's B rows and
+// feeds only its own tokens' h rows (the others read as zeros and are not
+// stored).  A token's output column depends only on its own h row, so each
+// token gets exactly the single-adapter expand's arithmetic with its
+// adapter's rank and scale.  The grid is exact (no persistent loop), so the
+// hardware keeps as many y tiles in flight as occupancy allows.
+template <int KS>
+__device__ __forceinline__ void sgmv_pass(const ExpandParams& p, const ExpandLane& L, const float* hrows, int a,
+                                          const u16x8 (&yv)[2])
+{
+    int ra = p.ranks[a];
+    ra = ra < 0 ? 0 : (ra > p.r_max ? p.r_max : ra);
+    const float scale = p.scales ? p.scales[a] : 1.0f;
+    const int64_t ld_b = (ra + 7) & ~7;
+    u16x8 unused[2];
+    ExpandLane Lb = L;
+    Lb.row_ok = false;                               // B rows only
+    if (ra > 32 || KS == 1) {
+        bf16x8 bop[4][KS];
+        expand_load<KS>(Lb, p.y, p.ld_y, p.N, p.B_ptrs[a], ld_b, ra, unused, bop);
+        expand_finish<KS>(L, p.y, p.ld_y, p.N, hrows, p.ld_h, ra, scale, yv, bop);
+    } else {
+        bf16x8 bop[4][1];
+        expand_load<1>(Lb, p.y, p.ld_y, p.N, p.B_ptrs[a], ld_b, ra, unused, bop);
+        expand_finish<1>(L, p.y, p.ld_y, p.N, hrows, p.ld_h, ra, scale, yv, bop);
+    }
+}
+
+// Multi-adapter, large M: as k_expand_rows, the workgroup walking R tiles of
+// one column block, with k_sgmv_expand's passes per distinct adapter.  Each
+// wave keeps the B operands of the last adapter it used and reloads them only
+// when a pass needs another one (tokens of one adapter are usually
+// contiguous); the staged h tile holds r_max columns and every pass masks it
+// to its adapter's rank.  y is read for every token of a tile but written only
+// for tokens with an adapter.
+template <int KS>
+__global__ __launch_bounds__(256) void k_sgmv_expand_rows(ExpandParams p, int R)
+{
+    __shared__ __align__(16) uint16_t hs[2][kRowBlock * kHbStride];
+    const uint32_t nblocks = (uint32_t)((p.N + kExpandCols - 1) / kExpandCols);
+    const int64_t col0 = (int64_t)(blockIdx.x % nblocks) * kExpandCols;
+    const int64_t row_base = (int64_t)(blockIdx.x / nblocks) * kRowBlock * R;
+    const int64_t left = (p.M - row_base + kRowBlock - 1) / kRowBlock;
+    const int tiles = left < R ? (int)left : R;
+    const HStageSlot slot = h_stage_slot(p.r_max);
+    ExpandLane L = expand_lane(row_base, tile_rows(p.M, row_base), col0);
+    auto token_id = [&](const ExpandLane& X) {
+        int a = X.row_ok ? p.ids[X.row] : -1;
+        return (a < 0 || a >= p.n_adapters) ? -1 : a;
+    };
+    int id = token_id(L);
+    u16x8 yv[2];
+    expand_load_y(L, p.y, p.ld_y, p.N, yv);
+    h_stage(slot, p.h, p.ld_h, row_base, tile_rows(p.M, row_base), p.r_max, hs[0]);
+    int cur = -1;                        // adapter whose B operands this wave holds
+    int ra = 0;
+    float scale = 1.0f;
+    bf16x8 bop[4][KS];
+    for (int i = 0; i < tiles; ++i) {
+        __syncthreads();
+        ExpandLane Ln = L;
+        int idn = -1;
+        u16x8 yn[2] = {u16x8{0, 0, 0, 0, 0, 0, 0, 0}, u16x8{0, 0, 0, 0, 0, 0, 0, 0}};
+        if (i + 1 < tiles) {
+            const int64_t r1 = row_base + (int64_t)kRowBlock * (i + 1);
+            Ln = expand_lane(r1, tile_rows(p.M, r1), col0);
+            idn = token_id(Ln);
+            expand_load_y(Ln, p.y, p.ld_y, p.N, yn);
+            h_stage(slot, p.h, p.ld_h, r1, tile_rows(p.M, r1), p.r_max, hs[(i + 1) & 1]);
+        }
+        if (L.n_base < p.N) {
+            bool done = !(L.row_ok && id >= 0);
+            for (;;) {
+                const uint64_t pending = __ballot(!done);
+                if (pending == 0)
+                    break;
+                const int a = __shfl(id, __builtin_ctzll(pending));     // wave-uniform
+                if (a != cur) {
+                    cur = a;
+                    ra = p.ranks[a];
+                    ra = ra < 0 ? 0 : (ra > p.r_max ? p.r_max : ra);
+                    scale = p.scales ? p.scales[a] : 1.0f;
+                    expand_load_b<KS>(L, p.N, p.B_ptrs[a], (ra + 7) & ~7, ra, bop);
+                }
+                const bool mine = !done && id == a;
+                ExpandLane La = L;
+                La.row_ok = mine;
+                if (KS == 2 && ra > 32) {
+                    bf16x8 hb[KS];
+                    hb_from_tile<KS>(La, hs[i & 1], ra, hb);
+                    expand_mma_store<KS>(La, p.y, p.ld_y, p.N, hb, scale, yv, bop);
+                } else {
+                    bf16x8 hb[1];
+                    bf16x8 b1[4][1];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        b1[t][0] = bop[t][0];
+                    hb_from_tile<1>(La, hs[i & 1], ra, hb);
+                    expand_mma_store<1>(La, p.y, p.ld_y, p.N, hb, scale, yv, b1);
+                }
+                done = done || mine;
+            }
+        }
+        L = Ln;
+        id = idn;
+        yv[0] = yn[0];
+        yv[1] = yn[1];
+    }
+}
+
+// KS: matrix-core steps the kernel is built for (1: r_max <= 32, 2: r_max <= 64).
+template <int KS>
 __global__ __launch_bounds__(256) void k_sgmv_expand(ExpandParams p)
 {
-    const int ntiles = plan_tiles(p.tiles, p.M, p.n_adapters);
-    const uint32_t nblocks = (uint32_t)((p.N + kExpandCols - 1) / kExpandCols);
-    const uint32_t items = (uint32_t)ntiles * nblocks;
-    for (uint32_t it = blockIdx.x; it < items; it += gridDim.x) {
-        const int tile = (int)(it / nblocks);
-        const int64_t cb = it - (uint32_t)tile * nblocks;
-        const int32_t* t = p.tiles + kPlanHeaderInts + 3 * tile;
-        if (!tile_ok(t, p.M, p.n_adapters))
-            continue;
-        const int a = t[2];
-        int ra = p.ranks[a];
-        ra = ra < 0 ? 0 : (ra > p.r_max ? p.r_max : ra);
-        const float scale = p.scales ? p.scales[a] : 1.0f;
-        const int64_t ld_b = (ra + 7) & ~7;
-        ExpandLane L = expand_lane(t[0], t[1], cb * kExpandCols);
-        if (L.n_base >= p.N)
-            continue;
-        const float* hrows = p.h + (int64_t)t[0] * p.ld_h;
-        u16x8 yv[2];
-        if (ra > 32) {
-            bf16x8 bop[4][2];
-            expand_load<2>(L, p.y, p.ld_y, p.N, p.B_ptrs[a], ld_b, ra, yv, bop);
-            expand_finish<2>(L, p.y, p.ld_y, p.N, hrows, p.ld_h, ra, scale, yv, bop);
-        } else {
-            bf16x8 bop[4][1];
-            expand_load<1>(L, p.y, p.ld_y, p.N, p.B_ptrs[a], ld_b, ra, yv, bop);
-            expand_finish<1>(L, p.y, p.ld_y, p.N, hrows, p.ld_h, ra, scale, yv, bop);
-        }
+    const ExpandItem q = expand_item(p.M, p.N);
+    ExpandLane L = expand_lane(q.row0, q.nrows, q.cb * kExpandCols);
+    if (L.n_base >= p.N)
+        return;                                      // per wave: no workgroup barrier here
+    int id = -1;
+    if (L.row_ok) {
+        id = p.ids[L.row];
+        id = (id < 0 || id >= p.n_adapters) ? -1 : id;
+    }
+    ExpandLane Ly = L;
+    Ly.row_ok = L.row_ok && id >= 0;
+    u16x8 yv[2];
+    const int64_t n0 = L.n_base + 16 * L.g;
+    const uint16_t* yp = p.y + L.row * p.ld_y + n0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+        yv[half] = (Ly.row_ok && n0 + half * 8 < p.N) ? *reinterpret_cast<const u16x8*>(yp + half * 8)
+                                                     : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    const float* hrows = p.h + q.row0 * p.ld_h;
+    bool done = !Ly.row_ok;
+    for (;;) {
+        const uint64_t pending = __ballot(!done);
+        if (pending == 0)
+            break;
+        const int a = __shfl(id, __builtin_ctzll(pending));     // wave-uniform
+        const bool mine = !done && id == a;
+        ExpandLane La = L;
+        La.row_ok = mine;
+        sgmv_pass<KS>(p, La, hrows, a, yv);
+        done = done || mine;
     }
 }
 
@@ -146,10 +315,37 @@ inline dim3 expand_grid(int64_t M, int64_t N)
     return dim3((unsigned)(((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols)));
 }
 
+// Tiles per workgroup for the expands: one while the one-tile grid leaves
+// fewer than ~4096 workgroups (small and medium M: no reuse is needed and the
+// parallelism is), else enough to bring the grid down to ~2048, at most 16.
+int expand_tiles_per_wg(int64_t M, int64_t N)
+{
+    const int64_t wgs = ((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols);
+    if (wgs < 4096)
+        return 1;
+    const int64_t R = wgs / 2048;
+    return (int)(R > 16 ? 16 : R);
+}
+
+inline dim3 expand_rows_grid(int64_t M, int64_t N, int R)
+{
+    const int64_t tiles = (M + kRowBlock - 1) / kRowBlock;
+    return dim3((unsigned)(((tiles + R - 1) / R) * ((N + kExpandCols - 1) / kExpandCols)));
+}
+
 hipError_t launch_expand(const ExpandParams& p, hipStream_t st)
 {
-    const dim3 grid = expand_grid(p.M, p.N);
     dim3 block(256);
+    const int R = expand_tiles_per_wg(p.M, p.N);
+    if (R > 1) {
+        const dim3 grid = expand_rows_grid(p.M, p.N, R);
+        if (p.r > 32)
+            hipLaunchKernelGGL(k_expand_rows<2>, grid, block, 0, st, p, R);
+        else
+            hipLaunchKernelGGL(k_expand_rows<1>, grid, block, 0, st, p, R);
+        return hipGetLastError();
+    }
+    const dim3 grid = expand_grid(p.M, p.N);
     if (p.r > 32)
         hipLaunchKernelGGL(k_expand<2>, grid, block, 0, st, p);
     else
@@ -177,9 +373,22 @@ hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int
                     : launch_expand_combine_ks<1>(p, c, split_k, grid, st);
 }
 
-hipError_t launch_sgmv_expand(const ExpandParams& p, int grid, hipStream_t st)
+hipError_t launch_sgmv_expand(const ExpandParams& p, hipStream_t st)
 {
-    hipLaunchKernelGGL(k_sgmv_expand, dim3((unsigned)grid), dim3(256), 0, st, p);
+    const int R = expand_tiles_per_wg(p.M, p.N);
+    if (R > 1) {
+        const dim3 grid = expand_rows_grid(p.M, p.N, R);
+        if (p.r_max > 32)
+            hipLaunchKernelGGL(k_sgmv_expand_rows<2>, grid, dim3(256), 0, st, p, R);
+        else
+            hipLaunchKernelGGL(k_sgmv_expand_rows<1>, grid, dim3(256), 0, st, p, R);
+        return hipGetLastError();
+    }
+    const dim3 grid = expand_grid(p.M, p.N);
+    if (p.r_max > 32)
+        hipLaunchKernelGGL(k_sgmv_expand<2>, grid, dim3(256), 0, st, p);
+    else
+        hipLaunchKernelGGL(k_sgmv_expand<1>, grid, dim3(256), 0, st, p);
     return hipGetLastError();
 }
 

@@ -166,8 +166,39 @@ __device__ __forceinline__ void split_partial(const ChainOperands<RTMAX>& c, f32
     }
 }
 
-// RTMAX: rank tiles the kernel is built for (2: r <= 32, one expand step;
-// 4: r <= 64, two expand steps).  S: split count.  W: chains per split.
+// Which (row block, column block) a workgroup owns.  Every workgroup of a row
+// block re-reads that block's x rows and all of A, so with at least 8 row
+// blocks the 1-D grid keeps all column blocks of a row block on one XCD
+// (workgroup ids go round-robin over the 8 XCDs, each with its own L2): XCD x
+// takes row blocks x, x + 8, ...; ids past the last row block exit at once.
+// With fewer row blocks the column blocks are spread over the XCDs instead.
+struct FusedItem {
+    int64_t mb;
+    int64_t cb;
+    bool ok;
+};
+
+__device__ __forceinline__ FusedItem fused_item(int64_t M, int64_t N)
+{
+    FusedItem q;
+    const uint32_t nblocks = (uint32_t)((N + kFusedCols - 1) / kFusedCols);
+    const uint32_t mbs = (uint32_t)((M + kRowBlock - 1) / kRowBlock);
+    const uint32_t b = blockIdx.x;
+    if (mbs >= kXcds) {
+        const uint32_t slot = b / kXcds;
+        q.mb = (b % kXcds) + kXcds * (slot / nblocks);
+        q.cb = slot % nblocks;
+    } else {
+        q.mb = b / nblocks;
+        q.cb = b % nblocks;
+    }
+    q.ok = q.mb < mbs;
+    return q;
+}
+
+// RTMAX: rank tiles the kernel is built for (1: r <= 16, 2: r <= 32, one
+// expand step; 4: r <= 64, two expand steps).  S: split count.  W: chains
+// per split.
 template <int RTMAX, int S, int W>
 __global__ __launch_bounds__(kFusedWaves * 64) void k_shrink_expand_fused(FusedParams p)
 {
@@ -182,10 +213,11 @@ __global__ __launch_bounds__(kFusedWaves * 64) void k_shrink_expand_fused(FusedP
     const int li = lane & 15;
     const int g = lane >> 4;
     const int r = p.r;
-    // 1-D grid, column block fastest (see the expand kernels)
-    const uint32_t nblocks = (uint32_t)((p.N + kFusedCols - 1) / kFusedCols);
-    const int64_t cb = blockIdx.x % nblocks;
-    const int64_t row0 = (int64_t)(blockIdx.x / nblocks) * kRowBlock;
+    const FusedItem item = fused_item(p.M, p.N);
+    if (!item.ok)
+        return;                                   // uniform: the whole workgroup leaves
+    const int64_t cb = item.cb;
+    const int64_t row0 = item.mb * kRowBlock;
     const int64_t left = p.M - row0;
     const int nrows = left < kRowBlock ? (int)left : kRowBlock;
     const bool row_ok = li < nrows;
@@ -273,10 +305,21 @@ hipError_t launch_rt(const FusedParams& p, int split_k, int waves, dim3 grid, hi
 
 }  // namespace
 
+int64_t fused_grid(int64_t M, int64_t N)
+{
+    const int64_t mbs = (M + kRowBlock - 1) / kRowBlock;
+    const int64_t nblocks = (N + kFusedCols - 1) / kFusedCols;
+    return (mbs >= kXcds ? (mbs + kXcds - 1) / kXcds * kXcds : mbs) * nblocks;
+}
+
 hipError_t launch_shrink_expand_fused(const FusedParams& p, int split_k, int waves, hipStream_t st)
 {
-    dim3 grid((unsigned)(((p.M + kRowBlock - 1) / kRowBlock) * ((p.N + kFusedCols - 1) / kFusedCols)));
-    return p.r > 32 ? launch_rt<4>(p, split_k, waves, grid, st) : launch_rt<2>(p, split_k, waves, grid, st);
+    const dim3 grid((unsigned)fused_grid(p.M, p.N));
+    if (p.r > 32)
+        return launch_rt<4>(p, split_k, waves, grid, st);
+    if (p.r > 16)
+        return launch_rt<2>(p, split_k, waves, grid, st);
+    return launch_rt<1>(p, split_k, waves, grid, st);
 }
 
 }  // namespace lora

@@ -59,7 +59,7 @@ struct ExpandParams {
     const uint16_t* const* B_ptrs;  // sgmv
     const int32_t* ranks;           // sgmv
     const float* scales;            // sgmv (may be null: 1)
-    const int32_t* tiles;           // sgmv plan
+    const int32_t* ids;             // sgmv: per-token adapter ids
     uint16_t* y;
     int64_t ld_y;
     int64_t M;
@@ -102,6 +102,15 @@ struct CounterParams {
     const float* scales;            // sgmv (may be null: 1)
 };
 
+// Single-launch shrink + expand: per 16-token block, `producers` shrink
+// workgroups (split_k x rank groups) then `consumers` expand workgroups.
+struct StreamParams {
+    int32_t* counters;              // (arrivals, departures) per row block, 0 between calls
+    int32_t* status;                // set to 1 when an expand workgroup stops waiting
+    int32_t producers;
+    int32_t consumers;
+};
+
 struct FusedParams {
     const uint16_t* x;
     int64_t ld_x;
@@ -139,13 +148,24 @@ hipError_t launch_fill_zero(float* h, int64_t ld_h, int64_t M, int ncols, hipStr
 
 hipError_t launch_expand(const ExpandParams& p, hipStream_t st);
 hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st);
-hipError_t launch_sgmv_expand(const ExpandParams& p, int grid, hipStream_t st);
+hipError_t launch_sgmv_expand(const ExpandParams& p, hipStream_t st);
 hipError_t launch_shrink_expand_fused(const FusedParams& p, int split_k, int waves, hipStream_t st);
+hipError_t launch_shrink_expand_counted(const ShrinkParams& p, const ExpandParams& e, const TreeParams& c,
+                                        const StreamParams& q, int waves, int group_tiles, hipStream_t st);
 
 hipError_t launch_sgmv_plan(const int32_t* ids, int64_t M, int32_t n_adapters, int32_t* plan,
                             hipStream_t st);
 
 // Columns of y one expand workgroup covers (4 waves x 64).
 constexpr int kExpandCols = 256;
+
+// 16-token tiles one expand workgroup walks (1: one tile per workgroup).
+int expand_tiles_per_wg(int64_t M, int64_t N);
+
+// XCDs of an MI355X; consecutive workgroup ids of a launch go to different ones.
+constexpr int kXcds = 8;
+
+// Workgroups of the single-launch recompute kernel for M tokens, N columns.
+int64_t fused_grid(int64_t M, int64_t N);
 
 }  // namespace lora

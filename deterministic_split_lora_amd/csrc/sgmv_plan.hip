@@ -9,13 +9,15 @@
 // everything else skips.  Tiles are listed in token order.
 //
 // One workgroup of 1024 threads walks the ids in chunks of 1024.  Per chunk:
-// a run starts at token i when its id differs from token i-1's; an inclusive
-// max-scan of "i if a run starts at i" gives each token its run start (carried
-// across chunks); tokens whose offset in the run is a multiple of 16 open a
-// tile; an exclusive sum-scan of those flags gives the tile's slot.  Both scans
-// use wavefront shuffles, then LDS across the 16 waves.  No host
-// synchronisation is needed, so the plan can be built inside a captured
-// stream and reused by every layer of a batch.
+// the chunk's ids (normalised, plus the one before and the 15 after) are
+// staged in LDS; a run starts at token i when its id differs from token
+// i-1's; an inclusive max-scan of "i if a run starts at i" gives each token
+// its run start (carried across chunks); tokens whose offset in the run is a
+// multiple of 16 open a tile, whose length is read from the staged ids; an
+// exclusive sum-scan of the openers gives the tile's slot.  Both scans use
+// wavefront shuffles, then LDS across the 16 waves.  No host synchronisation
+// is needed, so the plan can be built inside a captured stream and reused by
+// every layer of a batch.
 #include "device.h"
 #include "kernels.h"
 
@@ -38,6 +40,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_sgmv_plan(const int32_t* __res
     __shared__ int32_t s_cnt[kPlanWaves];
     __shared__ int32_t s_carry_start;
     __shared__ int32_t s_carry_tiles;
+    // ids[base - 1 .. base + 1024 + 15), normalised; slot 0 is token base - 1
+    __shared__ int32_t s_ids[kPlanThreads + kRowBlock];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
@@ -49,10 +53,15 @@ __global__ __launch_bounds__(kPlanThreads) void k_sgmv_plan(const int32_t* __res
     int32_t* tiles = plan + kPlanHeaderInts;
 
     for (int64_t base = 0; base < M; base += kPlanThreads) {
+        for (int e = tid; e < kPlanThreads + kRowBlock; e += kPlanThreads) {
+            const int64_t k = base - 1 + e;
+            s_ids[e] = (k >= 0 && k < M) ? norm_id(ids[k], n_adapters) : -2;   // -2: outside [0, M)
+        }
+        __syncthreads();
         const int i = (int)(base + tid);
         const bool in = i < M;
-        const int a = in ? norm_id(ids[i], n_adapters) : -1;
-        const bool run_start = in && (i == 0 || a != norm_id(ids[i - 1], n_adapters));
+        const int a = in ? s_ids[tid + 1] : -1;
+        const bool run_start = in && (i == 0 || a != s_ids[tid]);
 
         // inclusive max-scan of run starts
         int v = run_start ? i : -1;
@@ -95,13 +104,13 @@ __global__ __launch_bounds__(kPlanThreads) void k_sgmv_plan(const int32_t* __res
         if (opens) {
             const int slot = s_carry_tiles + before + incl - c;
             int n = 1;
-            while (n < kRowBlock && (int64_t)i + n < M && norm_id(ids[i + n], n_adapters) == a)
+            while (n < kRowBlock && s_ids[tid + 1 + n] == a)    // -2 past the end never matches
                 ++n;
             tiles[3 * slot + 0] = i;
             tiles[3 * slot + 1] = n;
             tiles[3 * slot + 2] = a;
         }
-        __syncthreads();                 // all reads of the carries are done
+        __syncthreads();                 // all reads of the carries and staged ids are done
         if (tid == 0) {
             s_carry_start = chunk_max;
             s_carry_tiles += total;

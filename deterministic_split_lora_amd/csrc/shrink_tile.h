@@ -1,0 +1,167 @@
+// The Split-K shrink work item shared by the shrink kernels and the
+// single-launch shrink + expand: one (16-token row block, split, group of RT
+// 16-wide rank tiles) computed by W wavefronts with matrix-core steps, the
+// wave results added along a fixed pairwise tree, the split's fp32 partial
+// stored, scaled, or atomically added.
+#pragma once
+
+#include "device.h"
+#include "kernels.h"
+
+namespace lora {
+
+enum ShrinkMode { kToWorkspace = 0, kToOutputScaled = 1, kAtomicScaled = 2, kToWorkspaceCoherent = 3 };
+
+// Agent-scope atomic store / load: performed at the device-wide coherence
+// point, past the per-XCD L2 caches (used for the single-launch combine).
+__device__ __forceinline__ void store_coherent(float* p, float v)
+{
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float load_coherent(const float* p)
+{
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Output element (row, col) of the tile: write / atomically add.
+template <int MODE>
+__device__ __forceinline__ void shrink_store(const ShrinkParams& p, int64_t row0, int s, int row, int col, float v,
+                                             float scale)
+{
+    const int64_t rr = row0 + row;
+    if (MODE == kToWorkspace) {
+        p.out[(int64_t)s * p.split_stride + rr * p.ld_out + col] = v;
+    } else if (MODE == kToWorkspaceCoherent) {
+        store_coherent(&p.out[(int64_t)s * p.split_stride + rr * p.ld_out + col], v);
+    } else if (MODE == kToOutputScaled) {
+        p.out[rr * p.ld_out + col] = __fmul_rn(v, scale);
+    } else {
+        unsafeAtomicAdd(&p.out[rr * p.ld_out + col], __fmul_rn(v, scale));
+    }
+}
+
+// One work item: rows row0 .. row0+nrows-1, split s, rank columns col0 ..
+// col0 + 16 RT - 1 (those below r).  A is the adapter's row 0.
+template <int RT, int W, int MODE>
+__device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0, int nrows,
+                                            const uint16_t* __restrict__ A, int r, int col0, int s, float scale,
+                                            float* red)
+{
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 15;
+    const int g = lane >> 4;
+    const int steps = p.k_steps;
+    const int rg = r - col0;                 // rank columns left from col0
+
+    // Reduction slots 8g..8g+7 of step t hold k = kbase + 32 t + (0..7).
+    const int64_t kbase = (int64_t)s * p.k_chunk + (int64_t)wave * steps * kKStep + g * 8;
+    const bool row_ok = li < nrows;
+    const uint16_t* xp = p.x + (row0 + (row_ok ? li : 0)) * p.ld_x + kbase;
+    const uint16_t* ap[RT];
+    bool a_ok[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int j = rt * 16 + li;
+        a_ok[rt] = j < rg;
+        ap[rt] = A + (int64_t)(col0 + (a_ok[rt] ? j : 0)) * p.ld_a + kbase;
+    }
+
+    f32x4 acc[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+        acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // Groups of up to 4 steps: issue all loads of the group, then the
+    // matrix-core steps in ascending k.
+    for (int t0 = 0; t0 < steps; t0 += 4) {
+        bf16x8 xa[4];
+        bf16x8 b[4][RT];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (t0 + u < steps) {
+                const int off = (t0 + u) * kKStep;
+                xa[u] = row_ok ? load_bf16x8(xp + off) : bf16x8_zero();
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    b[u][rt] = (rt * 16 < rg && a_ok[rt]) ? load_bf16x8(ap[rt] + off) : bf16x8_zero();
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            if (t0 + u < steps) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    if (rt * 16 < rg)
+                        acc[rt] = mfma_16x16x32(xa[u], b[u][rt], acc[rt]);
+            }
+        }
+    }
+
+    // acc[rt][v] is the wave's sum for token row 4g+v, rank column col0 + 16 rt + li.
+    if constexpr (W == 1) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int row = 4 * g + v, col = rt * 16 + li;
+                if (row < nrows && col < rg)
+                    shrink_store<MODE>(p, row0, s, row, col0 + col, acc[rt][v], scale);
+            }
+    } else {
+        constexpr int RS = 16 * RT + 4;          // padded LDS row stride (floats)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                red[(wave * 16 + 4 * g + v) * RS + rt * 16 + li] = acc[rt][v];
+        __syncthreads();
+        const int ncols = rg < 16 * RT ? rg : 16 * RT;
+        for (int e = threadIdx.x; e < 16 * 16 * RT; e += W * kWave) {
+            const int row = e / (16 * RT);
+            const int col = e - row * (16 * RT);
+            if (row < nrows && col < ncols) {
+                float v[W];
+#pragma unroll
+                for (int w = 0; w < W; ++w)
+                    v[w] = red[(w * 16 + row) * RS + col];
+                shrink_store<MODE>(p, row0, s, row, col0 + col, pairwise_tree<W>(v), scale);
+            }
+        }
+        __syncthreads();                          // LDS is reused by the next item
+    }
+}
+
+template <int RT, int W>
+constexpr int red_floats()
+{
+    return W > 1 ? W * 16 * (16 * RT + 4) : 1;
+}
+
+// Fixed pairwise tree over the S workspace slices of one element, read with
+// agent-scope loads (the slices may have been written by other XCDs during
+// the same launch).
+template <int S>
+__device__ __forceinline__ float tree_of_splits(const float* w, int64_t split_stride)
+{
+    float v[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+        v[s] = load_coherent(w + (int64_t)s * split_stride);
+    return pairwise_tree<S>(v);
+}
+
+// The same for a split count known at run time (1, 2, 4, 8 or 16).
+__device__ __forceinline__ float split_tree(const float* w, int64_t split_stride, int split_k)
+{
+    switch (split_k) {
+    case 1: return tree_of_splits<1>(w, split_stride);
+    case 2: return tree_of_splits<2>(w, split_stride);
+    case 4: return tree_of_splits<4>(w, split_stride);
+    case 8: return tree_of_splits<8>(w, split_stride);
+    default: return tree_of_splits<16>(w, split_stride);
+    }
+}
+
+}  // namespace lora

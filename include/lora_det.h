@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define LORA_DET_ABI_VERSION 1
+#define LORA_DET_ABI_VERSION 2
 
 enum lora_status {
     LORA_OK = 0,
@@ -151,11 +151,12 @@ int lora_expand(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b,
 /*
  * Single-launch deterministic Split-K shrink: the paper's final design
  * (section 4.3, Alg. 1).  Each split's workgroup stores its fp32 partial to
- * the workspace, makes it visible device-wide (agent-scope release fence),
+ * the workspace with agent-scope stores (performed at the device-wide
+ * coherence point, past the per-XCD L2 caches), waits for them to complete,
  * and adds 1 to its row block's integer counter with an agent-scope atomic;
- * the workgroup that sees split_k - 1 arrived last, acquires, and applies the
- * same fixed pairwise tree and scale as lora_shrink_splitk, writes h and
- * resets the counter to 0.  Bit for bit the same h as lora_shrink_splitk, in
+ * the workgroup that sees split_k - 1 arrived last loads the partials with
+ * agent-scope loads, applies the same fixed pairwise tree and scale as
+ * lora_shrink_splitk, writes h and resets the counter to 0.  Bit for bit the same h as lora_shrink_splitk, in
  * one launch.  No workgroup waits for another.
  * counters: int32 [lora_shrink_counter_bytes(M) / 4] (4 per 16-token block, one
  * per 16-wide rank tile), 4-byte aligned, ALL ZERO
@@ -230,6 +231,39 @@ int lora_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64
                        int32_t split_k, float shrink_scale, float expand_scale,
                        void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * lora_shrink_expand_counted: the same h and y as lora_shrink_expand in ONE
+ * launch, with a workspace and a counter buffer.  The grid holds, for each
+ * 16-token block, its Split-K shrink workgroups (the partial kernel of
+ * lora_shrink_partials, stores made device-visible as in
+ * lora_shrink_splitk_counted, then one agent-scope add to the block's arrival
+ * counter) followed by its expand workgroups, which load their y tile and B
+ * rows, wait until the block's counter shows every partial, then evaluate the
+ * tree + expand of lora_expand_combine.  The wait is bounded; workgroups are
+ * dispatched in increasing id and every shrink workgroup of a block precedes
+ * the block's expand workgroups, so the wait ends once they have run.
+ *
+ * counters: int32 [lora_shrink_expand_counter_bytes(M) / 4], 4-byte aligned,
+ * ALL ZERO before the first call.  Layout: counters[0] is a status word,
+ * counters[1..3] are unused, then two counters (arrivals, departures) per
+ * 16-token block.  Every completed call leaves the block counters zero, so one
+ * buffer serves any number of calls, of any M up to the one it was sized for,
+ * on one stream; calls that share a buffer must not overlap.  An expand
+ * workgroup that waited too long (not expected) sets counters[0] to 1 and
+ * leaves its part of y unchanged; the results of that call are then
+ * incomplete and the whole buffer must be zeroed again before the next call.
+ * workspace: as for lora_shrink_expand.  Other requirements: those of
+ * lora_shrink_expand.
+ */
+size_t lora_shrink_expand_counter_bytes(int64_t M);
+
+int lora_shrink_expand_counted(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a,
+                               const uint16_t* B, int64_t ld_b, float* h, int64_t ld_h,
+                               uint16_t* y, int64_t ld_y, int64_t M, int64_t K, int32_t r, int64_t N,
+                               int32_t split_k, float shrink_scale, float expand_scale,
+                               void* workspace, size_t workspace_bytes, int32_t* counters,
+                               size_t counter_bytes, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Multi-adapter (SGMV) variants.  The paper replays shrink operations with the
  * mapping of tokens to adapters (section 5.2); here each token i carries an
@@ -294,12 +328,20 @@ int lora_sgmv_shrink_counted(const uint16_t* x, int64_t ld_x, const uint16_t* co
                              int32_t* counters, size_t counter_bytes, void* stream);
 
 /*
- * Multi-adapter expand: per token with an adapter, lora_expand with that
- * adapter's B, rank and scale; other rows of y untouched.  One launch.
+ * Multi-adapter expand: per token i with an adapter (a = token_adapter[i] in
+ * [0, n_adapters)), lora_expand with B_a, rank r_a and scale scales[a] (1 when
+ * scales is NULL); rows of other tokens are neither read nor written.  One
+ * launch, one workgroup per 16 tokens x 256 columns; a block whose tokens use
+ * several adapters makes one matrix-core pass per adapter.  Each token's bits
+ * equal the single-adapter lora_expand's with its adapter (they do not depend
+ * on M, the token's neighbours or their adapters).
+ * h: fp32 [M][ld_h], 16-byte aligned, ld_h % 4 == 0, columns < r_a read.
+ * B_ptrs: device array of n_adapters pointers, B_a bf16 [N][round_up(r_a, 8)],
+ * 16-byte aligned.  token_adapter: device int32 [M].
  */
 int lora_sgmv_expand(const float* h, int64_t ld_h, const uint16_t* const* B_ptrs,
-                     const int32_t* ranks, const float* scales, int32_t n_adapters,
-                     const void* plan, size_t plan_bytes, uint16_t* y, int64_t ld_y,
+                     const int32_t* ranks, const float* scales, const int32_t* token_adapter,
+                     int32_t n_adapters, uint16_t* y, int64_t ld_y,
                      int64_t M, int64_t N, int32_t r_max, void* stream);
 
 #ifdef __cplusplus

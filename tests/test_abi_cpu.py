@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert dsl.lora_abi_version() == 1
+    assert dsl.lora_abi_version() == 2
     seen = set()
     for s in range(0, 7):
         t = dsl.lora_status_str(s)
@@ -209,18 +209,21 @@ def test_sgmv_rejects():
     assert shrink(M=0, x=None) == B.LORA_OK
 
     def expand(**kw):
-        a = dict(h=FAKE, ld_h=64, Bp=FAKE, ranks=FAKE, scales=None, n=4, plan=FAKE, pb=pb, y=FAKE, ld_y=4096,
+        a = dict(h=FAKE, ld_h=64, Bp=FAKE, ranks=FAKE, scales=None, ids=FAKE, n=4, y=FAKE, ld_y=4096,
                  M=64, N=4096, r_max=64)
         a.update(kw)
-        return L.lora_sgmv_expand(a["h"], a["ld_h"], a["Bp"], a["ranks"], a["scales"], a["n"], a["plan"], a["pb"],
+        return L.lora_sgmv_expand(a["h"], a["ld_h"], a["Bp"], a["ranks"], a["scales"], a["ids"], a["n"],
                                   a["y"], a["ld_y"], a["M"], a["N"], a["r_max"], None)
     assert expand(Bp=None) == B.LORA_ERR_NULL
-    assert expand(plan=None) == B.LORA_ERR_NULL
+    assert expand(ids=None) == B.LORA_ERR_NULL
+    assert expand(ranks=None) == B.LORA_ERR_NULL
+    assert expand(n=0) == B.LORA_ERR_SHAPE
+    assert expand(ld_h=60) == B.LORA_ERR_SHAPE
+    assert expand(h=FAKE + 4) == B.LORA_ERR_ALIGN
     assert expand(N=4090) == B.LORA_ERR_UNSUPPORTED
     assert expand(r_max=0) == B.LORA_ERR_UNSUPPORTED
     assert expand(ld_y=2048) == B.LORA_ERR_SHAPE
     assert expand(y=FAKE_MIS) == B.LORA_ERR_ALIGN
-    assert expand(pb=16) == B.LORA_ERR_WORKSPACE
     assert expand(M=0, h=None) == B.LORA_OK
 
 
@@ -353,3 +356,37 @@ def test_counted_rejects():
     assert sg(n=0) == B.LORA_ERR_SHAPE
     assert sg(cnt=FAKE + 1) == B.LORA_ERR_ALIGN
     assert sg(M=0, x=None) == B.LORA_OK
+
+
+def test_shrink_expand_counted_rejects():
+    L = dsl.lib()
+    assert dsl.lora_shrink_expand_counter_bytes(1) == 16 + 8
+    assert dsl.lora_shrink_expand_counter_bytes(33) == 16 + 3 * 8
+    assert dsl.lora_shrink_expand_counter_bytes(0) == 16
+    assert dsl.lora_shrink_expand_counter_bytes(-1) == 0
+    wsb = dsl.lora_shrink_expand_workspace_bytes(4, 16, 8)
+    cbytes = dsl.lora_shrink_expand_counter_bytes(4)
+
+    def call(**kw):
+        a = dict(x=FAKE, ld_x=4096, A=FAKE, ld_a=4096, B=FAKE, ld_b=16, h=FAKE, ld_h=16, y=FAKE, ld_y=4096, M=4,
+                 K=4096, r=16, N=4096, S=8, ss=1.0, es=2.0, ws=FAKE, wsb=wsb, cnt=FAKE, cb=cbytes)
+        a.update(kw)
+        return L.lora_shrink_expand_counted(a["x"], a["ld_x"], a["A"], a["ld_a"], a["B"], a["ld_b"], a["h"],
+                                            a["ld_h"], a["y"], a["ld_y"], a["M"], a["K"], a["r"], a["N"], a["S"],
+                                            a["ss"], a["es"], a["ws"], a["wsb"], a["cnt"], a["cb"], None)
+    assert call(x=None) == B.LORA_ERR_NULL
+    assert call(B=None) == B.LORA_ERR_NULL
+    assert call(ws=None) == B.LORA_ERR_NULL
+    assert call(cnt=None) == B.LORA_ERR_NULL
+    assert call(S=3) == B.LORA_ERR_UNSUPPORTED
+    assert call(r=65) == B.LORA_ERR_UNSUPPORTED
+    assert call(N=4092) == B.LORA_ERR_UNSUPPORTED
+    assert call(ld_h=8) == B.LORA_ERR_SHAPE
+    assert call(M=-5) == B.LORA_ERR_SHAPE
+    assert call(y=FAKE_MIS) == B.LORA_ERR_ALIGN
+    assert call(ws=FAKE + 8) == B.LORA_ERR_ALIGN
+    assert call(cnt=FAKE + 2) == B.LORA_ERR_ALIGN
+    assert call(wsb=wsb - 4) == B.LORA_ERR_WORKSPACE
+    assert call(cb=cbytes - 1) == B.LORA_ERR_WORKSPACE
+    assert call(M=0, x=None, ws=None, cnt=None) == B.LORA_OK
+    assert call(N=0, ws=None, cnt=None) == B.LORA_OK

@@ -454,7 +454,7 @@ def _sgmv_gpu(c, plan_ids=None):
     ws = workspace(dsl.lora_sgmv_workspace_bytes(c.M, c.r_max, c.split_k))
     dsl.lora_sgmv_shrink(xg, Ap, K, ranks, scales, idg, n, plan, h, c.r_max, c.split_k, ws)
     yg = bf16_to_gpu(c.y)
-    dsl.lora_sgmv_expand(h, Bp, ranks, scales, n, plan, yg, c.r_max)
+    dsl.lora_sgmv_expand(h, Bp, ranks, scales, idg, n, yg, c.r_max)
     t.cuda.synchronize()
     return h.cpu().numpy(), bf16_from_gpu(yg), (As, Bs)
 
@@ -549,7 +549,8 @@ def test_sgmv_prefill_full_size_sampled():
 def test_shrink_expand_fused_bitwise(M, K, r, N, S):
     """Every schedule of the deterministic shrink + expand - lora_shrink_splitk
     then lora_expand (three launches), lora_shrink_partials then
-    lora_expand_combine (two), lora_shrink_expand_fused (one) and
+    lora_expand_combine (two), lora_shrink_expand_fused (one),
+    lora_shrink_expand_counted (one, with arrival counters) and
     lora_shrink_expand (which picks by M) - gives the same h and y bits, and
     y agrees with the oracle."""
     _say(f"fused shrink+expand M={M} K={K} r={r} N={N} S={S}")
@@ -584,10 +585,18 @@ def test_shrink_expand_fused_bitwise(M, K, r, N, S):
     dsl.lora_shrink_expand_fused(xg, Ag, Bg, y5, S, 1.0, 2.0, h=h5)
     y6 = bf16_to_gpu(c.y)
     dsl.lora_shrink_expand_fused(xg, Ag, Bg, y6, S, 1.0, 2.0)
+    # one launch with arrival counters, twice on the same counters
+    cnt = t.zeros(dsl.lora_shrink_expand_counter_bytes(M) // 4, dtype=t.int32, device="cuda")
+    h7 = t.full((M, r), float("nan"), dtype=t.float32, device="cuda")
+    y7 = bf16_to_gpu(c.y)
+    dsl.lora_shrink_expand_counted(xg, Ag, Bg, y7, ws2, cnt, S, 1.0, 2.0, h=h7)
+    y8 = bf16_to_gpu(c.y)
+    dsl.lora_shrink_expand_counted(xg, Ag, Bg, y8, ws2, cnt, S, 1.0, 2.0)
     t.cuda.synchronize()
-    for hh_ in (h2, h4, h5):
+    assert int(cnt.abs().sum()) == 0
+    for hh_ in (h2, h4, h5, h7):
         assert np.array_equal(f32_bits(h1), f32_bits(hh_))
-    for yy in (y2, y3, y4, y5, y6):
+    for yy in (y2, y3, y4, y5, y6, y7, y8):
         assert np.array_equal(bf16_from_gpu(y1), bf16_from_gpu(yy))
     hh = h2.cpu().numpy()
     check_shrink(hh, c.x, c.A, 1.0, dsl.lora_shrink_plan(K, r, S), "fused h")
@@ -870,3 +879,152 @@ def test_counted_shrinks_stress_repeats():
     t.cuda.synchronize()
     assert int(bad) == 0
     assert int(cnt.abs().sum()) == 0 and int(cnt2.abs().sum()) == 0
+
+
+# ---------------------------------------------------------------------------
+# single-launch shrink + expand with arrival counters
+# ---------------------------------------------------------------------------
+def test_shrink_expand_counted_stress_and_graph():
+    """Back-to-back launches of lora_shrink_expand_counted at several M on one
+    counter buffer (sized for the largest M), each compared bit for bit on the
+    GPU with the two-launch result; then the same calls captured in a HIP
+    graph and replayed with eager work in between.  A partial read before it
+    was visible, or a counter left non-zero, would show up as a mismatch."""
+    t = torch()
+    K, r, N, S = 4096, 16, 4096, 8
+    Ms = (1, 16, 64, 256, 33)
+    cnt = t.zeros(dsl.lora_shrink_expand_counter_bytes(max(Ms)) // 4, dtype=t.int32, device="cuda")
+    bad = t.zeros((), dtype=t.int64, device="cuda")
+    cases = []
+    for M in Ms:
+        _say(f"counted shrink+expand stress M={M}")
+        c = single_adapter_case(M, K, r, N, split_k=S, seed=300 + M)
+        xg, Ag, Bg, y0 = bf16_to_gpu(c.x), bf16_to_gpu(c.A), bf16_to_gpu(c.B), bf16_to_gpu(c.y)
+        ws = workspace(dsl.lora_shrink_expand_workspace_bytes(M, r, S))
+        href = t.empty((M, r), dtype=t.float32, device="cuda")
+        yref = y0.clone()
+        dsl.lora_shrink_partials(xg, Ag, ws, S)
+        dsl.lora_expand_combine(ws, Bg, yref, S, 1.0, 2.0, h=href, r=r)
+        h = t.empty_like(href)
+        y = t.empty_like(y0)
+        cases.append((M, xg, Ag, Bg, y0, ws, href, yref, h, y))
+        for _ in range(200):
+            y.copy_(y0)
+            h.fill_(float("nan"))
+            dsl.lora_shrink_expand_counted(xg, Ag, Bg, y, ws, cnt, S, 1.0, 2.0, h=h)
+            bad += (h.view(t.int32) != href.view(t.int32)).sum() + (y.view(t.int16) != yref.view(t.int16)).sum()
+    t.cuda.synchronize()
+    assert int(bad) == 0
+    assert int(cnt.abs().sum()) == 0
+
+    def step():
+        for (M, xg, Ag, Bg, y0, ws, href, yref, h, y) in cases:
+            y.copy_(y0)
+            dsl.lora_shrink_expand_counted(xg, Ag, Bg, y, ws, cnt, S, 1.0, 2.0, h=h)
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        step()
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        step()
+    for rep in range(5):
+        for case in cases:
+            case[8].fill_(float("nan"))
+            case[9].zero_()
+        junk = t.randn(1 << 18, device="cuda") * 2.0
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        for (M, xg, Ag, Bg, y0, ws, href, yref, h, y) in cases:
+            assert np.array_equal(f32_bits(h), f32_bits(href)), f"replay {rep} M={M} h"
+            assert np.array_equal(bf16_from_gpu(y), bf16_from_gpu(yref)), f"replay {rep} M={M} y"
+        assert int(cnt.abs().sum()) == 0
+        del junk
+
+
+# ---------------------------------------------------------------------------
+# expands that walk several 16-token tiles per workgroup (large M x N)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("r", [5, 16, 37, 64])
+def test_expand_large_m_tiles_bitwise(r):
+    """At M x N large enough that lora_expand walks several tiles per
+    workgroup (B kept in registers, h staged in LDS), every row equals the
+    one-tile-per-workgroup result of a small call on the same rows bit for
+    bit, and sampled rows agree with the oracle.  Ragged M and N."""
+    t = torch()
+    M, N = 4100, 4104
+    _say(f"large-M expand r={r} M={M} N={N}")
+    ldh = (r + 3) // 4 * 4
+    ldb = (r + 7) // 8 * 8
+    rng = np.random.default_rng(40 + r)
+    h = np.zeros((M, ldh), np.float32)
+    h[:, :r] = rng.normal(0, 0.5, (M, r)).astype(np.float32)
+    h[:, r:] = np.nan                         # padding must never be read
+    Bm = normal_bf16((N, r), 0.02, r, "lmB")
+    Bp = np.zeros((N, ldb), np.uint16)
+    Bp[:, :r] = Bm
+    y = normal_bf16((M, N), 1.0, r, "lmy")
+    hg, Bg = f32_to_gpu(h), bf16_to_gpu(Bp)
+    yg = bf16_to_gpu(y)
+    dsl.lora_expand(hg, Bg, yg, 2.0, r=r)
+    got = bf16_from_gpu(yg)
+    for r0 in (0, 1008, 4096 - 16, 4100 - 37):
+        n = min(64, M - r0)
+        ys = bf16_to_gpu(y[r0:r0 + n])
+        dsl.lora_expand(hg[r0:r0 + n], Bg, ys, 2.0, r=r)
+        assert np.array_equal(bf16_from_gpu(ys), got[r0:r0 + n]), f"rows {r0}.."
+    rows = sorted(set([0, 15, 16, 2047, 4095, 4096, 4099] + rng.choice(M, 24, replace=False).tolist()))
+    yo, e, ab = oracle.expand(h[rows, :r], Bm, y[rows], 2.0)
+    check_expand(got[rows], yo, e, ab, y[rows], f"large-M expand r={r}")
+
+
+def test_sgmv_expand_large_m_tiles_bitwise():
+    """Multi-adapter expand at a size that walks several tiles per workgroup:
+    ids in runs (including -1 and out-of-range ids, runs that straddle tiles),
+    ranks 5 / 16 / 37 / 64.  Each token's y bits equal the single-adapter
+    lora_expand of its adapter on its rows; tokens without an adapter keep y."""
+    t = torch()
+    M, N = 4100, 4104
+    ranks = [5, 16, 37, 64]
+    n = len(ranks)
+    rng = np.random.default_rng(9)
+    ids = np.empty(M, np.int32)
+    pos = 0
+    while pos < M:
+        run = int(rng.integers(1, 300))
+        ids[pos:pos + run] = rng.choice([-1, 0, 1, 2, 3, 9])
+        pos += run
+    r_max = 64
+    h = rng.normal(0, 0.5, (M, r_max)).astype(np.float32)
+    y = normal_bf16((M, N), 1.0, 1, "slmy")
+    Bs, Bg = [], []
+    for a, r in enumerate(ranks):
+        ldb = (r + 7) // 8 * 8
+        Bm = normal_bf16((N, r), 0.02, a, "slmB")
+        Bp = np.zeros((N, ldb), np.uint16)
+        Bp[:, :r] = Bm
+        Bs.append(Bm)
+        Bg.append(bf16_to_gpu(Bp))
+    scales = np.array([2.0, 0.5, 1.0, 2.0], np.float32)
+    Bptr = t.tensor([b.data_ptr() for b in Bg], dtype=t.int64, device="cuda")
+    hg = f32_to_gpu(h)
+    yg = bf16_to_gpu(y)
+    dsl.lora_sgmv_expand(hg, Bptr, t.from_numpy(np.array(ranks, np.int32)).cuda(), t.from_numpy(scales).cuda(),
+                         t.from_numpy(ids).cuda(), n, yg, r_max)
+    got = bf16_from_gpu(yg)
+    none = (ids < 0) | (ids >= n)
+    assert np.array_equal(got[none], y[none])
+    for a, r in enumerate(ranks):
+        sel = np.nonzero(ids == a)[0]
+        if len(sel) == 0:
+            continue
+        hs = np.ascontiguousarray(h[sel])
+        ys = bf16_to_gpu(y[sel])
+        dsl.lora_expand(f32_to_gpu(hs), Bg[a], ys, float(scales[a]), r=r)
+        assert np.array_equal(bf16_from_gpu(ys), got[sel]), f"adapter {a}"
+        pick = sel[rng.choice(len(sel), min(8, len(sel)), replace=False)]
+        yo, e, ab = oracle.expand(h[pick, :r], Bs[a], y[pick], float(scales[a]))
+        check_expand(got[pick], yo, e, ab, y[pick], f"sgmv large-M adapter {a}")
