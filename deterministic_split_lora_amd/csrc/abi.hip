@@ -62,6 +62,18 @@ int group_tiles_for(int64_t M, int32_t split_k, int rank_tiles)
     return wgs <= 2048 ? 1 : rank_tiles;
 }
 
+// Row blocks per shrink workgroup in the two-pass paths (all rank tiles
+// together when above 1).  A workgroup reads its rows' x and the split's
+// chunk of A; sharing the A loads between 2 or 4 row blocks cuts the
+// traffic through the compute units once the grid is large, while small
+// grids keep one row block (and one rank tile) per workgroup for memory
+// parallelism.  Per-element arithmetic does not depend on it.
+int shrink_tiles_per_wg(int64_t M, int32_t split_k)
+{
+    const int64_t wgs = ((M + kRowBlock - 1) / kRowBlock) * split_k;
+    return wgs >= 2048 ? 4 : (wgs >= 512 ? 2 : 1);
+}
+
 // Multi-adapter: 1 or 4 rank tiles per workgroup, by the same rule with M
 // standing in for the (device-side) tile count.
 int sgmv_group_tiles(int64_t M, int32_t split_k, int32_t r_max)
@@ -87,6 +99,16 @@ int sgmv_grid(int64_t M, int32_t split_k, int32_t r_max, int group_tiles)
 int launch_status(hipError_t e)
 {
     return e == hipSuccess ? LORA_OK : LORA_ERR_LAUNCH;
+}
+
+// The Split-K partial kernel of the deterministic two-pass paths.
+hipError_t launch_partials(const ShrinkParams& p, const lora_shrink_plan_t& pl, int64_t M, int32_t split_k,
+                           hipStream_t st)
+{
+    const int T = shrink_tiles_per_wg(M, split_k);
+    if (T > 1)
+        return launch_shrink_partial_multi(p, pl.waves, pl.rank_tiles, T, st);
+    return launch_shrink_partial_ws(p, pl.waves, pl.rank_tiles, group_tiles_for(M, split_k, pl.rank_tiles), st);
 }
 
 // Checks shared by the single-adapter shrinks.
@@ -268,7 +290,7 @@ int lora_shrink_splitk(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64
     p.out = static_cast<float*>(workspace);
     p.ld_out = r;
     p.split_stride = M * r;
-    st = launch_status(launch_shrink_partial_ws(p, pl.waves, pl.rank_tiles, group_tiles_for(M, split_k, pl.rank_tiles), s));
+    st = launch_status(launch_partials(p, pl, M, split_k, s));
     if (st != LORA_OK)
         return st;
     TreeParams t{};
@@ -365,8 +387,7 @@ int lora_shrink_partials(const uint16_t* x, int64_t ld_x, const uint16_t* A, int
     sp.out = static_cast<float*>(workspace);
     sp.ld_out = r;
     sp.split_stride = M * r;
-    return launch_status(launch_shrink_partial_ws(sp, pl.waves, pl.rank_tiles, group_tiles_for(M, split_k, pl.rank_tiles),
-                                                          static_cast<hipStream_t>(stream)));
+    return launch_status(launch_partials(sp, pl, M, split_k, static_cast<hipStream_t>(stream)));
 }
 
 int lora_expand_combine(const void* workspace, size_t ws_bytes, int32_t split_k, float shrink_scale,
@@ -711,9 +732,15 @@ int lora_sgmv_shrink(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_p
     p.n_adapters = n_adapters;
     p.scale = 1.0f;
     // Tiles never exceed M; the grid is a fixed bound, idle workgroups exit.
-    const int gt = sgmv_group_tiles(M, split_k, r_max);
-    const int grid = sgmv_grid(M, split_k, r_max, gt);
-    st = launch_status(launch_sgmv_shrink_partial(p, pl.waves, gt, grid, s));
+    const int T = shrink_tiles_per_wg(M, split_k);
+    if (T > 1) {
+        const int64_t bound = (M + T - 1) / T * split_k;
+        st = launch_status(launch_sgmv_shrink_partial_multi(p, pl.waves, T, (int)(bound < 2048 ? bound : 2048), s));
+    } else {
+        const int gt = sgmv_group_tiles(M, split_k, r_max);
+        const int grid = sgmv_grid(M, split_k, r_max, gt);
+        st = launch_status(launch_sgmv_shrink_partial(p, pl.waves, gt, grid, s));
+    }
     if (st != LORA_OK)
         return st;
     TreeParams t{};

@@ -139,6 +139,11 @@ hipError_t launch_shrink_partial_direct(const ShrinkParams& p, int waves, int ra
 hipError_t launch_shrink_partial_atomic(const ShrinkParams& p, int waves, int rank_tiles, int group_tiles,
                                         hipStream_t st);
 hipError_t launch_sgmv_shrink_partial(const ShrinkParams& p, int waves, int group_tiles, int grid, hipStream_t st);
+// tiles_per_wg 2 or 4: row blocks (plan tiles) per workgroup, all rank tiles together
+hipError_t launch_shrink_partial_multi(const ShrinkParams& p, int waves, int rank_tiles, int tiles_per_wg,
+                                       hipStream_t st);
+hipError_t launch_sgmv_shrink_partial_multi(const ShrinkParams& p, int waves, int tiles_per_wg, int grid,
+                                            hipStream_t st);
 hipError_t launch_shrink_counted(const ShrinkParams& p, const CounterParams& c, int waves, int rank_tiles,
                                  int group_tiles, hipStream_t st);
 hipError_t launch_sgmv_shrink_counted(const ShrinkParams& p, const CounterParams& c, int waves, int group_tiles,

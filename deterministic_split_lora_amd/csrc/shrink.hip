@@ -115,6 +115,28 @@ __global__ __launch_bounds__(W * 64) void k_shrink_partial(ShrinkParams p, int g
     shrink_tile<RT, W, MODE>(p, q.row0, q.nrows, p.A, p.r, q.grp * 16 * RT, q.s, p.scale, red);
 }
 
+// Large M: T consecutive row blocks per workgroup, all rank tiles together,
+// split index fastest in the 1-D grid.  The row blocks share the A loads (see
+// shrink_tiles); partials and their bits are those of k_shrink_partial.
+template <int RT, int W, int T>
+__global__ __launch_bounds__(W * 64) void k_shrink_partial_multi(ShrinkParams p)
+{
+    __shared__ float red[red_floats<RT, W>()];
+    const uint32_t S = (uint32_t)p.split_k;
+    const int s = (int)(blockIdx.x % S);
+    const int64_t first = (int64_t)(blockIdx.x / S) * T * kRowBlock;
+    int64_t row0[T];
+    int nrows[T];
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+        const int64_t r0 = first + (int64_t)u * kRowBlock;
+        const int64_t left = p.M - r0;
+        nrows[u] = left <= 0 ? 0 : (left < kRowBlock ? (int)left : kRowBlock);
+        row0[u] = nrows[u] > 0 ? r0 : first;      // empty tiles keep a valid base address
+    }
+    shrink_tiles<RT, W, kToWorkspace, T>(p, row0, nrows, p.A, p.r, 0, s, 1.0f, red);
+}
+
 // Single launch: the last split of each (row block, rank group) writes h.
 template <int RT, int W>
 __global__ __launch_bounds__(W * 64) void k_shrink_counted(ShrinkParams p, CounterParams c, int groups)
@@ -188,6 +210,50 @@ __global__ __launch_bounds__(W * 64) void k_sgmv_shrink_partial(ShrinkParams p)
         if (col0 >= ra)
             continue;
         shrink_tile<RT, W, kToWorkspace>(p, q.row0, q.nrows, p.A_ptrs[q.a], ra, col0, q.s, 1.0f, red);
+    }
+}
+
+// Large M: items are (chunk of T consecutive plan tiles, split), split
+// fastest; in a chunk, each stretch of consecutive tiles with one adapter
+// goes through shrink_tiles together (tiles of one adapter are consecutive
+// in the plan, so a chunk is usually one stretch).  All rank tiles of r_max
+// in one workgroup.  Same partials, same bits as k_sgmv_shrink_partial.
+template <int RT, int W, int T>
+__global__ __launch_bounds__(W * 64) void k_sgmv_shrink_partial_multi(ShrinkParams p)
+{
+    __shared__ float red[red_floats<RT, W>()];
+    const int ntiles = plan_tiles(p.tiles, p.M, p.n_adapters);
+    const uint32_t S = (uint32_t)p.split_k;
+    const uint32_t items = (uint32_t)((ntiles + T - 1) / T) * S;
+    const int32_t* plan = p.tiles + kPlanHeaderInts;
+    for (uint32_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int s = (int)(it % S);
+        const int c0 = (int)(it / S) * T;
+        const int c1 = c0 + T < ntiles ? c0 + T : ntiles;
+        int j = c0;
+        while (j < c1) {                          // uniform: plan data only
+            const int32_t* t = plan + 3 * j;
+            if (!tile_ok(t, p.M, p.n_adapters)) {
+                ++j;
+                continue;
+            }
+            const int a = t[2];
+            int64_t row0[T];
+            int nrows[T];
+            int n = 0;
+#pragma unroll
+            for (int u = 0; u < T; ++u) {
+                const int32_t* tu = plan + 3 * (j + u);
+                const bool take = n == u && j + u < c1 && tile_ok(tu, p.M, p.n_adapters) && tu[2] == a;
+                row0[u] = take ? tu[0] : t[0];
+                nrows[u] = take ? tu[1] : 0;
+                n += take ? 1 : 0;
+            }
+            const int ra = adapter_rank(p, a);
+            if (ra > 0)
+                shrink_tiles<RT, W, kToWorkspace, T>(p, row0, nrows, p.A_ptrs[a], ra, 0, s, 1.0f, red);
+            j += n;
+        }
     }
 }
 
@@ -371,6 +437,63 @@ hipError_t launch_shrink_partial_ws(const ShrinkParams& p, int waves, int rank_t
                                     hipStream_t st)
 {
     return launch_partial<kToWorkspace>(p, waves, rank_tiles, group_tiles, st);
+}
+
+namespace {
+
+template <int RT, int T>
+void launch_multi_rt(const ShrinkParams& p, int waves, dim3 grid, bool sgmv, hipStream_t st)
+{
+#define LORA_MULTI(W_)                                                                                   \
+    do {                                                                                                 \
+        if (sgmv)                                                                                        \
+            hipLaunchKernelGGL((k_sgmv_shrink_partial_multi<RT, W_, T>), grid, dim3(W_ * 64), 0, st, p); \
+        else                                                                                             \
+            hipLaunchKernelGGL((k_shrink_partial_multi<RT, W_, T>), grid, dim3(W_ * 64), 0, st, p);      \
+    } while (0)
+    switch (waves) {
+    case 1: LORA_MULTI(1); break;
+    case 2: LORA_MULTI(2); break;
+    case 4: LORA_MULTI(4); break;
+    default: LORA_MULTI(8); break;
+    }
+#undef LORA_MULTI
+}
+
+template <int T>
+void launch_multi_t(const ShrinkParams& p, int waves, int rank_tiles, dim3 grid, bool sgmv, hipStream_t st)
+{
+    if (rank_tiles == 1)
+        launch_multi_rt<1, T>(p, waves, grid, sgmv, st);
+    else if (rank_tiles == 2)
+        launch_multi_rt<2, T>(p, waves, grid, sgmv, st);
+    else
+        launch_multi_rt<4, T>(p, waves, grid, sgmv, st);
+}
+
+}  // namespace
+
+hipError_t launch_shrink_partial_multi(const ShrinkParams& p, int waves, int rank_tiles, int tiles_per_wg,
+                                       hipStream_t st)
+{
+    const int64_t mbs = (p.M + kRowBlock - 1) / kRowBlock;
+    const dim3 grid((unsigned)(((mbs + tiles_per_wg - 1) / tiles_per_wg) * p.split_k));
+    if (tiles_per_wg == 2)
+        launch_multi_t<2>(p, waves, rank_tiles, grid, false, st);
+    else
+        launch_multi_t<4>(p, waves, rank_tiles, grid, false, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_sgmv_shrink_partial_multi(const ShrinkParams& p, int waves, int tiles_per_wg, int grid,
+                                            hipStream_t st)
+{
+    const int rank_tiles = (p.r_max + 15) / 16;
+    if (tiles_per_wg == 2)
+        launch_multi_t<2>(p, waves, rank_tiles, dim3((unsigned)grid), true, st);
+    else
+        launch_multi_t<4>(p, waves, rank_tiles, dim3((unsigned)grid), true, st);
+    return hipGetLastError();
 }
 
 hipError_t launch_shrink_partial_direct(const ShrinkParams& p, int waves, int rank_tiles, int group_tiles,

@@ -41,6 +41,10 @@ __device__ __forceinline__ void shrink_store(const ShrinkParams& p, int64_t row0
     }
 }
 
+template <int RT, int W, int MODE>
+__device__ __forceinline__ void wave_tree_store(const ShrinkParams& p, int64_t row0, int nrows, int rg, int col0,
+                                                int s, float scale, float* red, const f32x4 (&acc)[RT]);
+
 // One work item: rows row0 .. row0+nrows-1, split s, rank columns col0 ..
 // col0 + 16 RT - 1 (those below r).  A is the adapter's row 0.
 template <int RT, int W, int MODE>
@@ -99,7 +103,95 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0,
         }
     }
 
-    // acc[rt][v] is the wave's sum for token row 4g+v, rank column col0 + 16 rt + li.
+    wave_tree_store<RT, W, MODE>(p, row0, nrows, rg, col0, s, scale, red, acc);
+}
+
+// Several row tiles that share one adapter and rank columns: T 16-row tiles
+// (row0[u], nrows[u]; a tile with nrows 0 is skipped) against the same A
+// operands, loaded once per matrix-core step for all T tiles.  Each (tile,
+// rank tile) accumulator sees the same steps in the same ascending k order as
+// in shrink_tile, and the wave tree is the same, so every partial has the same
+// bits; only the A loads are shared.  Steps go in groups of two.
+template <int RT, int W, int MODE, int T>
+__device__ __forceinline__ void shrink_tiles(const ShrinkParams& p, const int64_t (&row0)[T], const int (&nrows)[T],
+                                             const uint16_t* __restrict__ A, int r, int col0, int s, float scale,
+                                             float* red)
+{
+    constexpr int G = 2;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 15;
+    const int g = lane >> 4;
+    const int steps = p.k_steps;
+    const int rg = r - col0;
+
+    const int64_t kbase = (int64_t)s * p.k_chunk + (int64_t)wave * steps * kKStep + g * 8;
+    const uint16_t* xp[T];
+    bool row_ok[T];
+#pragma unroll
+    for (int u = 0; u < T; ++u) {
+        row_ok[u] = li < nrows[u];
+        xp[u] = p.x + (row0[u] + (row_ok[u] ? li : 0)) * p.ld_x + kbase;
+    }
+    const uint16_t* ap[RT];
+    bool a_ok[RT];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+        const int j = rt * 16 + li;
+        a_ok[rt] = j < rg;
+        ap[rt] = A + (int64_t)(col0 + (a_ok[rt] ? j : 0)) * p.ld_a + kbase;
+    }
+    f32x4 acc[T][RT];
+#pragma unroll
+    for (int u = 0; u < T; ++u)
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+            acc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int t0 = 0; t0 < steps; t0 += G) {
+        bf16x8 xa[G][T];
+        bf16x8 b[G][RT];
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            if (t0 + q < steps) {
+                const int off = (t0 + q) * kKStep;
+#pragma unroll
+                for (int u = 0; u < T; ++u)
+                    xa[q][u] = row_ok[u] ? load_bf16x8(xp[u] + off) : bf16x8_zero();
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+                    b[q][rt] = (rt * 16 < rg && a_ok[rt]) ? load_bf16x8(ap[rt] + off) : bf16x8_zero();
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            if (t0 + q < steps) {
+#pragma unroll
+                for (int u = 0; u < T; ++u)
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+                        if (rt * 16 < rg)
+                            acc[u][rt] = mfma_16x16x32(xa[q][u], b[q][rt], acc[u][rt]);
+            }
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < T; ++u)
+        if (nrows[u] > 0)                         // uniform across the workgroup
+            wave_tree_store<RT, W, MODE>(p, row0[u], nrows[u], rg, col0, s, scale, red, acc[u]);
+}
+
+// acc[rt][v] is the wave's sum for token row 4g+v, rank column col0 + 16 rt + li:
+// with W waves, the W wave sums meet in LDS and are added along the fixed
+// pairwise tree; then the split's partial is stored.
+template <int RT, int W, int MODE>
+__device__ __forceinline__ void wave_tree_store(const ShrinkParams& p, int64_t row0, int nrows, int rg, int col0,
+                                                int s, float scale, float* red, const f32x4 (&acc)[RT])
+{
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 15;
+    const int g = lane >> 4;
     if constexpr (W == 1) {
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)

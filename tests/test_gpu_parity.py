@@ -736,11 +736,14 @@ def test_batch_invariance_across_schedule_switch():
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("M,K,r,S", [(1, 4096, 16, 8), (8, 1024, 8, 8), (64, 4096, 16, 8), (256, 4096, 16, 8),
                                      (37, 8192, 64, 16), (100, 2048, 40, 4), (19, 14336, 32, 8), (5, 1024, 5, 2),
-                                     (40, 4096, 16, 1)])
+                                     (40, 4096, 16, 1), (1100, 2048, 40, 8), (4100, 1024, 64, 8),
+                                     (4100, 2048, 16, 8), (2000, 1024, 24, 16)])
 def test_shrink_counted_bitwise(M, K, r, S):
     """lora_shrink_splitk_counted (one launch, the last-arriving split
-    combines) gives lora_shrink_splitk's bits, leaves its counters at zero,
-    and repeats bit for bit on the same counters."""
+    combines, one row block per workgroup) gives lora_shrink_splitk's bits
+    (which shares A loads between 2 or 4 row blocks per workgroup at the
+    larger M here), leaves its counters at zero, and repeats bit for bit on
+    the same counters."""
     t = torch()
     c = single_adapter_case(M, K, r, 0, split_k=S, seed=31 + M)
     xg, Ag = bf16_to_gpu(c.x), bf16_to_gpu(c.A)
@@ -794,12 +797,22 @@ def test_shrink_counted_in_graph_replays():
         del junk
 
 
-@pytest.mark.parametrize("case", ["qkv", "mixed", "decode_probe"])
+@pytest.mark.parametrize("case", ["qkv", "mixed", "decode_probe", "prefill"])
 def test_sgmv_counted_bitwise(case):
     """lora_sgmv_shrink_counted gives lora_sgmv_shrink's bits (rows without an
-    adapter and columns beyond a rank zeroed) in one launch."""
+    adapter and columns beyond a rank zeroed) in one launch; in the prefill
+    case the two-pass shrink shares A loads between 4 plan tiles."""
     t = torch()
-    if case == "qkv":
+    if case == "prefill":
+        rng = np.random.default_rng(6)
+        ids = np.empty(2048, np.int32)
+        pos = 0
+        while pos < 2048:
+            run = int(rng.integers(5, 300))
+            ids[pos:pos + run] = rng.choice([-1, 0, 1, 2, 3, 4, 5, 6, 7])
+            pos += run
+        c = sgmv_case(2048, 2048, 64, [8, 16, 32, 64, 5, 37, 64, 16], 0, 0, 16, seed=3, tag="cp", ids=ids)
+    elif case == "qkv":
         c = sgmv_case(512, 4096, 64, [64, 64, 64, 64], 1, 64, 8, seed=0, tag="cq")
     elif case == "mixed":
         rng = np.random.default_rng(4)
