@@ -433,6 +433,93 @@ def batch_sweep_bench(args):
     return out
 
 
+def split_sweep_bench(args):
+    """Split count S in {1, 2, 4, 8, 16}:
+    - the one-token decode shrink over three fused QKV slices (hidden 3072,
+      rank 16 per slice; the slices' A rows stacked into one rank-48 operand,
+      so each slice is its own 16-wide output tile: 3 x S workgroups) -
+      deterministic two launches, deterministic single launch, atomic;
+    - deterministic shrink + expand at the q_proj shape (M = 1, 16, 256) and
+      at the MLP down-projection shape (K=14336, r=32; M = 1, 16, 256)."""
+    import torch
+    import deterministic_split_lora_amd as dsl
+    from synth import single_adapter_case
+    dev = torch.device("cuda:0")
+    splits = (1, 2, 4, 8, 16)
+    out = {"splits": list(splits)}
+    # fused QKV decode shrink
+    K, r = 3072, 48
+    c = single_adapter_case(1, K, r, 0, split_k=8, scale=1.0, seed=0)
+    copies = 256
+    sets = [dict(x=gpu_tensor(c.x, dev), A=gpu_tensor(c.A, dev), h=torch.empty((1, r), device=dev),
+                 ws=torch.empty(dsl.lora_shrink_workspace_bytes(1, r, 16), dtype=torch.uint8, device=dev))
+            for _ in range(copies)]
+    cnt = torch.zeros(dsl.lora_shrink_counter_bytes(1) // 4, dtype=torch.int32, device=dev)
+    qkv = {"workload": "decode shrink, 1 token, hidden 3072, 3 fused QKV slices of rank 16 (A stacked: r = 48)"}
+    for S in splits:
+        row = {}
+        row["det_two_launch_us"] = round(_time_rotating(
+            lambda st, S=S: dsl.lora_shrink_splitk(st["x"], st["A"], st["h"], st["ws"], S, 1.0), sets, args), 3)
+        row["det_one_launch_us"] = round(_time_rotating(
+            lambda st, S=S: dsl.lora_shrink_splitk_counted(st["x"], st["A"], st["h"], st["ws"], cnt, S, 1.0), sets,
+            args), 3)
+        row["atomic_us"] = round(_time_rotating(
+            lambda st, S=S: dsl.lora_shrink_splitk_atomic(st["x"], st["A"], st["h"], S, 1.0), sets, args), 3)
+        row["workgroups"] = 3 * S
+        qkv[str(S)] = row
+    best1 = min(qkv["1"]["det_two_launch_us"], qkv["1"]["det_one_launch_us"])
+    for S in splits:
+        b = min(qkv[str(S)]["det_two_launch_us"], qkv[str(S)]["det_one_launch_us"])
+        qkv[str(S)]["det_speedup_vs_split1"] = round(best1 / b, 3)
+    out["decode_qkv_shrink"] = qkv
+    del sets
+    # shrink + expand at two shapes
+    for label, K, r, N in (("q_proj_k4096_r16_n4096", 4096, 16, 4096), ("down_k14336_r32_n4096", 14336, 32, 4096)):
+        tab = {}
+        for M in (1, 16, 256):
+            cc = single_adapter_case(M, K, r, N, split_k=8, seed=0)
+            per = 2 * M * K + 4 * M * N + 4 * K * r
+            copies = max(8, math.ceil(ROTATE_BYTES / 4 / per))
+            sets = [dict(x=gpu_tensor(cc.x, dev), A=gpu_tensor(cc.A, dev), B=gpu_tensor(cc.B, dev),
+                         y=gpu_tensor(cc.y, dev), h=torch.empty((M, r), device=dev),
+                         ws=torch.empty(dsl.lora_shrink_expand_workspace_bytes(M, r, 16), dtype=torch.uint8,
+                                        device=dev))
+                    for _ in range(copies)]
+            tab[str(M)] = {str(S): round(_time_rotating(
+                lambda st, S=S: dsl.lora_shrink_expand(st["x"], st["A"], st["B"], st["y"], st["ws"], S, 1.0, SCALE,
+                                                       h=st["h"]), sets, args), 3) for S in splits}
+            del sets
+        out[label + "_det_us"] = tab
+    torch.cuda.empty_cache()
+    return out
+
+
+def compensated_bench(args):
+    """lora_expand vs lora_expand_compensated (two matrix-core passes, hi and
+    lo of h) at N = 4096, r = 16 and 64, M = 1, 256, 4096: the cost of
+    consuming 16 instead of 8 significant bits of h."""
+    import torch
+    import deterministic_split_lora_amd as dsl
+    from synth import normal_bf16
+    dev = torch.device("cuda:0")
+    out = {"workload": "expand only: h fp32 [M x r], B [4096 x r], y [M x 4096] bf16, scale 2"}
+    N = 4096
+    for r in (16, 64):
+        for M in (1, 256, 4096):
+            per = 4 * M * N + 2 * N * r + 4 * M * r
+            copies = max(8, math.ceil(ROTATE_BYTES / 4 / per))
+            Bm = gpu_tensor(normal_bf16((N, r), 0.02, 0, "cbB"), dev)
+            y0 = gpu_tensor(normal_bf16((M, N), 1.0, 0, "cby"), dev)
+            sets = [dict(h=torch.randn((M, r), device=dev) * 0.5, B=Bm.clone(), y=y0.clone()) for _ in range(copies)]
+            up = _time_rotating(lambda st: dsl.lora_expand(st["h"], st["B"], st["y"], SCALE), sets, args)
+            uc = _time_rotating(lambda st: dsl.lora_expand_compensated(st["h"], st["B"], st["y"], SCALE), sets, args)
+            out[f"r{r}_m{M}"] = {"plain_us": round(up, 3), "compensated_us": round(uc, 3),
+                                 "ratio": round(uc / up, 3), "bytes": per}
+            del sets
+    torch.cuda.empty_cache()
+    return out
+
+
 def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S):
     """Multi-adapter shrink and expand on a prebuilt plan, cold cache.
     Compulsory bytes count only the adapters some token uses, at their own
@@ -639,6 +726,10 @@ def main():
         log("bench: shrink-only shape done")
         extra["batch_sweep_k14336_r32_n4096"] = batch_sweep_bench(args)
         log("bench: batch sweep done")
+        extra["split_sweep"] = split_sweep_bench(args)
+        log("bench: split sweep done")
+        extra["compensated_expand"] = compensated_bench(args)
+        log("bench: compensated expand done")
         extra["sgmv_m512_k4096_n6144_4x_r64"] = sgmv_bench(args, "b3", 512, 4096, 6144, [64] * 4, 1, 64, 8)
         log("bench: sgmv 512 done")
         extra["sgmv_prefill_m4096_k8192_n28672_32_adapters"] = sgmv_bench(args, "b5", 4096, 8192, 28672,

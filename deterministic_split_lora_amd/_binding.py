@@ -30,7 +30,7 @@ EXPORTED = [
     "lora_shrink_expand_workspace_bytes", "lora_shrink_expand", "lora_shrink_partials", "lora_expand_combine",
     "lora_shrink_expand_fused", "lora_shrink_expand_launches", "lora_shrink_counter_bytes",
     "lora_shrink_splitk_counted", "lora_sgmv_counter_bytes", "lora_sgmv_shrink_counted",
-    "lora_shrink_expand_counter_bytes", "lora_shrink_expand_counted",
+    "lora_shrink_expand_counter_bytes", "lora_shrink_expand_counted", "lora_expand_compensated",
 ]
 
 
@@ -80,6 +80,8 @@ def lib():
                                                 _f32, _vp]
         L.lora_expand.restype = ctypes.c_int
         L.lora_expand.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i32, _i64, _f32, _vp]
+        L.lora_expand_compensated.restype = ctypes.c_int
+        L.lora_expand_compensated.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i32, _i64, _f32, _vp]
         L.lora_shrink_expand_workspace_bytes.restype = _sz
         L.lora_shrink_expand_workspace_bytes.argtypes = [_i64, _i32, _i32]
         L.lora_shrink_expand.restype = ctypes.c_int
@@ -257,6 +259,19 @@ def lora_expand(h, B, y, scale: float, r: int | None = None, stream=None):
     st = lib().lora_expand(_ptr(h), _ld(h, "h"), _ptr(B), _ld(B, "B"), _ptr(y), _ld(y, "y"), M, r, N, scale,
                            _stream(stream, y))
     _check(st, "lora_expand")
+    return y
+
+
+def lora_expand_compensated(h, B, y, scale: float, r: int | None = None, stream=None):
+    """Like lora_expand, with h split into bf16 hi + bf16 lo (two matrix-core passes)."""
+    import torch
+    _dtype(h, torch.float32, "h"); _dtype(B, torch.bfloat16, "B"); _dtype(y, torch.bfloat16, "y")
+    M, N = y.shape
+    if r is None:
+        r = B.shape[1]
+    st = lib().lora_expand_compensated(_ptr(h), _ld(h, "h"), _ptr(B), _ld(B, "B"), _ptr(y), _ld(y, "y"), M, r, N,
+                                       scale, _stream(stream, y))
+    _check(st, "lora_expand_compensated")
     return y
 
 

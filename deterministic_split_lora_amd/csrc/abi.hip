@@ -323,8 +323,10 @@ int lora_shrink_splitk_atomic(const uint16_t* x, int64_t ld_x, const uint16_t* A
     return launch_status(launch_shrink_partial_atomic(p, pl.waves, pl.rank_tiles, group_tiles_for(M, split_k, pl.rank_tiles), s));
 }
 
-int lora_expand(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b, uint16_t* y, int64_t ld_y,
-                int64_t M, int32_t r, int64_t N, float scale, void* stream)
+namespace {
+
+int expand_entry(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b, uint16_t* y, int64_t ld_y,
+                 int64_t M, int32_t r, int64_t N, float scale, bool compensated, void* stream)
 {
     if (M < 0 || M > kMaxDim || N < 0 || N > kMaxDim)
         return LORA_ERR_SHAPE;
@@ -354,7 +356,22 @@ int lora_expand(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b, u
     p.r = r;
     p.r_max = r;
     p.scale = scale;
-    return launch_status(launch_expand(p, static_cast<hipStream_t>(stream)));
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    return launch_status(compensated ? launch_expand_compensated(p, st) : launch_expand(p, st));
+}
+
+}  // namespace
+
+int lora_expand(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b, uint16_t* y, int64_t ld_y,
+                int64_t M, int32_t r, int64_t N, float scale, void* stream)
+{
+    return expand_entry(h, ld_h, B, ld_b, y, ld_y, M, r, N, scale, false, stream);
+}
+
+int lora_expand_compensated(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b, uint16_t* y,
+                            int64_t ld_y, int64_t M, int32_t r, int64_t N, float scale, void* stream)
+{
+    return expand_entry(h, ld_h, B, ld_b, y, ld_y, M, r, N, scale, true, stream);
 }
 
 size_t lora_shrink_expand_workspace_bytes(int64_t M, int32_t r, int32_t split_k)

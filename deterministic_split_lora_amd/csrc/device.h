@@ -65,10 +65,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f)
     return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
-// bf16(h[row][j0 .. j0+7]) with columns >= r read as 0.
-__device__ __forceinline__ bf16x8 load_h_as_bf16(const float* hp, int j0, int r)
+// h[row][j0 .. j0+7] with columns >= r read as 0.
+__device__ __forceinline__ void load_h8(const float* hp, int j0, int r, float (&f)[8])
 {
-    float f[8];
     if (j0 + 8 <= r) {
         const float4 a = *reinterpret_cast<const float4*>(hp);
         const float4 b = *reinterpret_cast<const float4*>(hp + 4);
@@ -79,6 +78,13 @@ __device__ __forceinline__ bf16x8 load_h_as_bf16(const float* hp, int j0, int r)
         for (int e = 0; e < 8; ++e)
             f[e] = (j0 + e < r) ? hp[e] : 0.0f;
     }
+}
+
+// bf16(h[row][j0 .. j0+7]) with columns >= r read as 0.
+__device__ __forceinline__ bf16x8 load_h_as_bf16(const float* hp, int j0, int r)
+{
+    float f[8];
+    load_h8(hp, j0, r, f);
     u16x8 v;
 #pragma unroll
     for (int e = 0; e < 8; ++e)
@@ -206,6 +212,64 @@ __device__ __forceinline__ void expand_finish(const ExpandLane& L, uint16_t* y, 
         hb[ks] = (L.row_ok && j0 < r) ? load_h_as_bf16(hrows + L.li * ld_hr + j0, j0, r) : bf16x8_zero();
     }
     expand_mma_store<KS>(L, y, ld_y, N, hb, scale, yv, bop);
+}
+
+// Compensated expand: h is split into hi = bf16(h) and lo = bf16(h - hi)
+// (h - hi is exact in fp32), both go through the matrix-core steps with the
+// same B operands, and the two fp32 results are added before the epilogue:
+//   acc = acc(hi) + acc(lo);  y = bf16(fma(scale, acc, y)).
+template <int KS>
+__device__ __forceinline__ void expand_finish_comp(const ExpandLane& L, uint16_t* y, int64_t ld_y, int64_t N,
+                                                   const float* hrows, int64_t ld_hr, int r, float scale,
+                                                   const u16x8 (&yv)[2], const bf16x8 (&bop)[4][KS])
+{
+    bf16x8 hi[KS], lo[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+        const int j0 = ks * kKStep + 8 * L.g;
+        u16x8 vh = {0, 0, 0, 0, 0, 0, 0, 0}, vl = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (L.row_ok && j0 < r) {
+            float f[8];
+            load_h8(hrows + L.li * ld_hr + j0, j0, r, f);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                vh[e] = f32_to_bf16_bits(f[e]);
+                vl[e] = f32_to_bf16_bits(__fsub_rn(f[e], bf16_bits_to_f32(vh[e])));
+            }
+        }
+        hi[ks] = __builtin_bit_cast(bf16x8, vh);
+        lo[ks] = __builtin_bit_cast(bf16x8, vl);
+    }
+    f32x4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f32x4 ah = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 al = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            ah = mfma_16x16x32(bop[t][ks], hi[ks], ah);
+            al = mfma_16x16x32(bop[t][ks], lo[ks], al);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            acc[t][v] = __fadd_rn(ah[v], al[v]);
+    }
+    if (!L.row_ok)
+        return;
+    const int64_t n0 = L.n_base + 16 * L.g;
+    uint16_t* yp = y + L.row * ld_y + n0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+        if (n0 + half * 8 < N) {
+            u16x8 o;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int idx = half * 8 + e;
+                o[e] = f32_to_bf16_bits(__builtin_fmaf(scale, acc[idx >> 2][idx & 3], bf16_bits_to_f32(yv[half][e])));
+            }
+            *reinterpret_cast<u16x8*>(yp + half * 8) = o;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -61,6 +61,21 @@ __global__ __launch_bounds__(256) void k_expand(ExpandParams p)
     expand_finish<KS>(L, p.y, p.ld_y, p.N, p.h + row0 * p.ld_h, p.ld_h, p.r, p.scale, yv, bop);
 }
 
+// Compensated single-adapter expand: the grid and loads of k_expand, the
+// arithmetic of expand_finish_comp (two matrix-core passes, hi and lo of h).
+template <int KS>
+__global__ __launch_bounds__(256) void k_expand_comp(ExpandParams p)
+{
+    const ExpandItem q = expand_item(p.M, p.N);
+    ExpandLane L = expand_lane(q.row0, q.nrows, q.cb * kExpandCols);
+    if (L.n_base >= p.N)
+        return;
+    u16x8 yv[2];
+    bf16x8 bop[4][KS];
+    expand_load<KS>(L, p.y, p.ld_y, p.N, p.B, p.ld_b, p.r, yv, bop);
+    expand_finish_comp<KS>(L, p.y, p.ld_y, p.N, p.h + q.row0 * p.ld_h, p.ld_h, p.r, p.scale, yv, bop);
+}
+
 // Single adapter, large M: a workgroup walks R consecutive 16-token tiles of
 // one 256-column block.  Its B operands are loaded once and stay in
 // registers; each tile's h rows are converted to bf16 once into LDS (double
@@ -331,6 +346,16 @@ inline dim3 expand_rows_grid(int64_t M, int64_t N, int R)
 {
     const int64_t tiles = (M + kRowBlock - 1) / kRowBlock;
     return dim3((unsigned)(((tiles + R - 1) / R) * ((N + kExpandCols - 1) / kExpandCols)));
+}
+
+hipError_t launch_expand_compensated(const ExpandParams& p, hipStream_t st)
+{
+    const dim3 grid = expand_grid(p.M, p.N);
+    if (p.r > 32)
+        hipLaunchKernelGGL(k_expand_comp<2>, grid, dim3(256), 0, st, p);
+    else
+        hipLaunchKernelGGL(k_expand_comp<1>, grid, dim3(256), 0, st, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_expand(const ExpandParams& p, hipStream_t st)

@@ -152,6 +152,7 @@ hipError_t launch_splitk_tree(const TreeParams& p, int split_k, bool sgmv, hipSt
 hipError_t launch_fill_zero(float* h, int64_t ld_h, int64_t M, int ncols, hipStream_t st);
 
 hipError_t launch_expand(const ExpandParams& p, hipStream_t st);
+hipError_t launch_expand_compensated(const ExpandParams& p, hipStream_t st);
 hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st);
 hipError_t launch_sgmv_expand(const ExpandParams& p, hipStream_t st);
 hipError_t launch_shrink_expand_fused(const FusedParams& p, int split_k, int waves, hipStream_t st);

@@ -149,6 +149,23 @@ int lora_expand(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b,
                 void* stream);
 
 /*
+ * Compensated expand (the GEMM compensation of "Demystifying Numerical
+ * Instability in LLM Inference ... with HEAL", section 3, Eq. 10, with bf16
+ * halves): h is split into hi = bf16_rne(h) and lo = bf16_rne(h - hi), both
+ * are multiplied by B on the matrix cores, and the two fp32 results are added
+ * before the update:
+ *     acc = sum_j hi[i][j] B[n][j]  +  sum_j lo[i][j] B[n][j]
+ *     y[i][n] = bf16_rne( fma(scale, acc, y[i][n]) )
+ * The product then sees about 16 significant bits of h instead of 8, so two
+ * fp32 shrink values that round to different bf16 values no longer give y
+ * values 1 bf16 step apart.  Twice the matrix-core work of lora_expand, the
+ * same memory traffic.  Arguments, layouts and errors as for lora_expand.
+ */
+int lora_expand_compensated(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b,
+                            uint16_t* y, int64_t ld_y, int64_t M, int32_t r, int64_t N, float scale,
+                            void* stream);
+
+/*
  * Single-launch deterministic Split-K shrink: the paper's final design
  * (section 4.3, Alg. 1).  Each split's workgroup stores its fp32 partial to
  * the workspace with agent-scope stores (performed at the device-wide

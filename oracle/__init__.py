@@ -28,6 +28,13 @@ the tests live in ``tests/test_oracle.py``):
                         h pinned by the paper's midpoint value.
 * ``sgmv_*``          - per-token equality with the single-adapter functions,
                         invalid ids leave rows untouched.
+* ``expand_compensated`` - exact rational brute force (``exact.py``); the
+                        hand-derived cases of tests/golden/compensated_expand.json
+                        (where it and the plain expand differ); hi + lo equals h
+                        for every h with at most 16 significant bits; equal to
+                        ``expand`` when h is already bf16.  Follows the HEAL page
+                        ("Demystifying Numerical Instability in LLM Inference"),
+                        section 3, Eq. 10, read with bf16 halves.
 """
 from __future__ import annotations
 
@@ -81,6 +88,8 @@ def lib():
         L.oracle_combine_sequential_f32.argtypes = [_f32p, _i64, _i64, ctypes.c_float, _f32p]
         L.oracle_expand.argtypes = [_f32p, _u16p, _u16p, _i64, _i64, _i64, ctypes.c_double,
                                     _f64p, _u16p, _f64p]
+        L.oracle_expand_compensated.argtypes = [_f32p, _u16p, _u16p, _i64, _i64, _i64, ctypes.c_double,
+                                                _f64p, _u16p, _f64p]
         L.oracle_sgmv_shrink.argtypes = [_u16p, ctypes.POINTER(_u16p), _i32p, _f32p, _i32p,
                                          ctypes.c_int32, _i64, _i64, _i64, _f64p]
         L.oracle_sgmv_expand.argtypes = [_f32p, ctypes.POINTER(_u16p), _i32p, _f32p, _i32p,
@@ -193,6 +202,23 @@ def expand(h, B, y, scale: float):
     ab = np.empty((M, N), dtype=np.float64)
     lib().oracle_expand(_p(h, _f32p), _p(B, _u16p), _p(y, _u16p), M, r, N, float(scale),
                         _p(e, _f64p), _p(yo, _u16p), _p(ab, _f64p))
+    return yo, e, ab
+
+
+def expand_compensated(h, B, y, scale: float):
+    """The compensated expand (h split into bf16 hi + bf16 lo of the residual,
+    the two products summed); returns (y_out, e, sum|s (hi + lo) B|) like
+    expand()."""
+    h = np.ascontiguousarray(h, dtype=np.float32)
+    B, y = _u16(B), _u16(y)
+    M, r = h.shape
+    N = B.shape[0]
+    assert B.shape[1] == r and y.shape == (M, N)
+    e = np.empty((M, N), dtype=np.float64)
+    yo = np.empty((M, N), dtype=np.uint16)
+    ab = np.empty((M, N), dtype=np.float64)
+    lib().oracle_expand_compensated(_p(h, _f32p), _p(B, _u16p), _p(y, _u16p), M, r, N, float(scale),
+                                    _p(e, _f64p), _p(yo, _u16p), _p(ab, _f64p))
     return yo, e, ab
 
 

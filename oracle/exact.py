@@ -109,3 +109,29 @@ def expand(h_f32, B_bits, y_bits, scale):
         E.append(erow)
         O.append(orow)
     return O, E
+
+
+def expand_compensated(h_f32, B_bits, y_bits, scale):
+    """Exact compensated expand: hi = rne_bf16(h), lo = rne_bf16(h - hi),
+    e = y + scale * sum_j (hi + lo) B[n][j], and its bf16 rounding (the HEAL
+    page, section 3, Eq. 10, with bf16 halves)."""
+    h_f32 = np.asarray(h_f32, dtype=np.float32)
+    B_bits = np.asarray(B_bits)
+    y_bits = np.asarray(y_bits)
+    M, r = h_f32.shape
+    N = B_bits.shape[0]
+    sc = Fraction(float(np.float32(scale))) if not isinstance(scale, Fraction) else scale
+    E, O = [], []
+    for i in range(M):
+        hv = [f32_to_fraction(h_f32[i, j]) for j in range(r)]
+        hi = [rne_bf16(v) for v in hv]
+        lo = [rne_bf16(v - a) for v, a in zip(hv, hi)]
+        erow, orow = [], []
+        for n in range(N):
+            s = sum(((hi[j] + lo[j]) * bf16_bits_to_fraction(B_bits[n, j]) for j in range(r)), Fraction(0))
+            e = bf16_bits_to_fraction(y_bits[i, n]) + sc * s
+            erow.append(e)
+            orow.append(fraction_to_bf16_bits(rne_bf16(e)))
+        E.append(erow)
+        O.append(orow)
+    return O, E

@@ -247,6 +247,45 @@ void oracle_expand(const float* h, const uint16_t* B, const uint16_t* y_in, int6
 }
 
 /* ------------------------------------------------------------------------ */
+/* Compensated expand ("Demystifying Numerical Instability in LLM Inference  */
+/* ... with HEAL", section 3, GEMM algebraic compensation, Eq. 10): the      */
+/* fp32 input of a 16-bit product is written as a leading 16-bit value plus  */
+/* a 16-bit residual, and the product is the sum of the two products.  Read  */
+/* here with bf16 halves (bf16 has the fp32 exponent range, so the residual  */
+/* needs no 2^10 shift):                                                     */
+/*   hi = bf16_rne(h),  lo = bf16_rne(h - hi)      (h - hi is exact)          */
+/*   e[i][n]  = y[i][n] + scale * sum_{j<r} (hi_j + lo_j) * B[n][j]  (double) */
+/*   out[i][n] = bf16_rne(e[i][n])                                           */
+/* Also returns sum_j (|hi B| + |lo B|) per element for error bounds.       */
+/* ------------------------------------------------------------------------ */
+void oracle_expand_compensated(const float* h, const uint16_t* B, const uint16_t* y_in, int64_t M, int64_t r,
+                               int64_t N, double scale, double* e_out, uint16_t* y_out, double* abs_sum)
+{
+    #pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < M; ++i) {
+        double hi[256], lo[256];
+        for (int64_t j = 0; j < r; ++j) {
+            const double hv = (double)h[i * r + j];
+            hi[j] = oracle_bf16_to_double(oracle_bf16_rne_from_float(h[i * r + j]));
+            lo[j] = oracle_bf16_to_double(oracle_bf16_rne_from_double(hv - hi[j]));
+        }
+        for (int64_t n = 0; n < N; ++n) {
+            double acc = 0.0, aacc = 0.0;
+            for (int64_t j = 0; j < r; ++j) {
+                const double b = oracle_bf16_to_double(B[n * r + j]);
+                acc += hi[j] * b + lo[j] * b;
+                aacc += fabs(hi[j] * b) + fabs(lo[j] * b);
+            }
+            double e = oracle_bf16_to_double(y_in[i * N + n]) + scale * acc;
+            e_out[i * N + n] = e;
+            y_out[i * N + n] = oracle_bf16_rne_from_double(e);
+            if (abs_sum)
+                abs_sum[i * N + n] = fabs(scale) * aacc;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Multi-adapter (SGMV) shrink and expand.  RLI section 5.2 replays shrink   */
 /* operations together with the token-to-adapter mapping: which adapter each */
 /* token uses.  Per token i with a = ids[i]:                                 */

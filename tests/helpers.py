@@ -41,19 +41,22 @@ def workspace(nbytes: int):
     return t.empty(max(int(nbytes), 16), dtype=t.uint8, device="cuda")
 
 
-def check_shrink(h_gpu: np.ndarray, x, A, scale: float, plan: dict, what: str = ""):
+def check_shrink(h_gpu: np.ndarray, x, A, scale: float, plan: dict, what: str = "", atomic: bool = False):
     """Two bounds, both per element:
     * the stated tolerance: |h - ref| <= 1e-3 |scale| ||x_i|| ||A_j||;
     * a rounding bound from the arithmetic: every element is the result of
       one 32-product matrix-core step per step, k_steps accumulating steps, a
       log2(waves)-level and a log2(split_k)-level fp32 tree and one multiply,
-      so |h - ref| <= (32 + k_steps + log2 W + log2 S + 2) 2^-24 |scale| sum|x A|.
+      so |h - ref| <= (32 + k_steps + log2 W + log2 S + 2) 2^-24 |scale| sum|x A|;
+      the atomic variant adds its S scaled partials one after another in any
+      order, which takes S instead of log2 S + 1 in that count.
     Returns (max error / stated tolerance, max error / rounding bound)."""
     ref = oracle.shrink(x, A, scale)
     absum, xn, an = oracle.shrink_bounds(x, A)
     err = np.abs(h_gpu.astype(np.float64) - ref)
     tol = 1e-3 * abs(scale) * np.outer(xn, an)
-    depth = 32 + plan["k_steps"] + int(np.log2(plan["waves"])) + int(np.log2(plan["split_k"])) + 2
+    split_depth = plan["split_k"] if atomic else int(np.log2(plan["split_k"])) + 1
+    depth = 32 + plan["k_steps"] + int(np.log2(plan["waves"])) + split_depth + 1
     rb = depth * 2.0 ** -24 * abs(scale) * absum + 1e-30
     assert np.all(err <= tol), f"{what}: shrink beyond stated tolerance, worst {np.max(err / tol):.3g}"
     assert np.all(err <= rb), f"{what}: shrink beyond rounding bound, worst {np.max(err / rb):.3g}"

@@ -104,11 +104,11 @@ def _atomic(**kw):
                                                a["K"], a["r"], a["S"], a["scale"], None)
 
 
-def _expand(**kw):
+def _expand(fn="lora_expand", **kw):
     a = dict(h=FAKE, ld_h=16, B=FAKE, ld_b=16, y=FAKE, ld_y=4096, M=4, r=16, N=4096, scale=2.0)
     a.update(kw)
-    return dsl.lib().lora_expand(a["h"], a["ld_h"], a["B"], a["ld_b"], a["y"], a["ld_y"], a["M"], a["r"], a["N"],
-                                 a["scale"], None)
+    return getattr(dsl.lib(), fn)(a["h"], a["ld_h"], a["B"], a["ld_b"], a["y"], a["ld_y"], a["M"], a["r"], a["N"],
+                                  a["scale"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -144,6 +144,7 @@ def test_shrink_zero_rows_is_noop():
     assert _atomic(M=0, x=None, A=None, h=None) == B.LORA_OK
     assert _expand(M=0, h=None, B=None, y=None) == B.LORA_OK
     assert _expand(N=0, h=None, B=None, y=None) == B.LORA_OK
+    assert _expand(fn="lora_expand_compensated", M=0, h=None, B=None, y=None) == B.LORA_OK
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -174,6 +175,7 @@ def test_atomic_rejects(kw, status):
 ])
 def test_expand_rejects(kw, status):
     assert _expand(**kw) == status
+    assert _expand(fn="lora_expand_compensated", **kw) == status
 
 
 def test_sgmv_rejects():

@@ -162,7 +162,7 @@ def test_atomic_parity(M, K, r, S):
     _say(f"atomic shrink parity M={M} K={K} r={r} S={S}")
     c = single_adapter_case(M, K, r, 0, split_k=S, seed=3)
     h = run_shrink(c.x, c.A, S, 2.0, atomic=True)
-    check_shrink(h, c.x, c.A, 2.0, dsl.lora_shrink_plan(K, r, S), "atomic")
+    check_shrink(h, c.x, c.A, 2.0, dsl.lora_shrink_plan(K, r, S), "atomic", atomic=True)
 
 
 # ---------------------------------------------------------------------------
@@ -1041,3 +1041,107 @@ def test_sgmv_expand_large_m_tiles_bitwise():
         pick = sel[rng.choice(len(sel), min(8, len(sel)), replace=False)]
         yo, e, ab = oracle.expand(h[pick, :r], Bs[a], y[pick], float(scales[a]))
         check_expand(got[pick], yo, e, ab, y[pick], f"sgmv large-M adapter {a}")
+
+
+# ---------------------------------------------------------------------------
+# the pages' decode shape: one token, hidden 3072, three fused QKV slices
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("S", [1, 2, 4, 8, 16])
+def test_fused_qkv_decode_slices(S):
+    """Three QKV slices of rank 16 on one token, K = 3072: the rank-48 shrink
+    over the stacked A rows gives each slice the bits of its own rank-16
+    shrink (rank columns are independent chains), for the two-launch and
+    single-launch deterministic shrinks; h agrees with the oracle, and the
+    atomic variant agrees within the stated tolerance."""
+    t = torch()
+    K = 3072
+    for M in (1, 5):
+        c = single_adapter_case(M, K, 48, 0, split_k=S, scale=1.0, seed=70 + M)
+        xg, Ag = bf16_to_gpu(c.x), bf16_to_gpu(c.A)
+        ws = workspace(dsl.lora_shrink_workspace_bytes(M, 48, S))
+        h48 = t.full((M, 48), float("nan"), dtype=t.float32, device="cuda")
+        dsl.lora_shrink_splitk(xg, Ag, h48, ws if S > 1 else None, S, 1.0)
+        cnt = t.zeros(dsl.lora_shrink_counter_bytes(M) // 4, dtype=t.int32, device="cuda")
+        h1 = t.full((M, 48), float("nan"), dtype=t.float32, device="cuda")
+        dsl.lora_shrink_splitk_counted(xg, Ag, h1, ws if S > 1 else None, cnt if S > 1 else None, S, 1.0)
+        ha = t.full((M, 48), float("nan"), dtype=t.float32, device="cuda")
+        dsl.lora_shrink_splitk_atomic(xg, Ag, ha, S, 1.0)
+        slices = []
+        for q in range(3):
+            hq = t.full((M, 16), float("nan"), dtype=t.float32, device="cuda")
+            dsl.lora_shrink_splitk(xg, bf16_to_gpu(np.ascontiguousarray(c.A[16 * q:16 * q + 16])), hq,
+                                   ws if S > 1 else None, S, 1.0)
+            slices.append(hq)
+        t.cuda.synchronize()
+        b48 = f32_bits(h48)
+        for q in range(3):
+            assert np.array_equal(b48[:, 16 * q:16 * q + 16], f32_bits(slices[q])), f"slice {q}"
+        assert np.array_equal(f32_bits(h1), b48)
+        plan = dsl.lora_shrink_plan(K, 48, S)
+        check_shrink(h48.cpu().numpy(), c.x, c.A, 1.0, plan, f"qkv S={S} M={M}")
+        check_shrink(ha.cpu().numpy(), c.x, c.A, 1.0, plan, f"qkv atomic S={S} M={M}", atomic=True)
+
+
+# ---------------------------------------------------------------------------
+# compensated expand (h as bf16 hi + bf16 lo)
+# ---------------------------------------------------------------------------
+def test_expand_compensated_golden_bitwise():
+    """The hand-derived cases, on the GPU: bit for bit the oracle's outputs,
+    which keep the residual of h that lora_expand drops."""
+    import json
+    import os
+    t = torch()
+    gold = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "compensated_expand.json")))
+    for c in gold["cases"]:
+        h = np.array(c["h"], dtype=np.float32)
+        r = h.shape[1]
+        ldh = (r + 3) // 4 * 4
+        hp = np.zeros((h.shape[0], ldh), np.float32)
+        hp[:, :r] = h
+        Bv = np.array(c["B"], dtype=np.float32)
+        yv = np.array(c["y"], dtype=np.float32)
+        N = Bv.shape[0]
+        Np = (N + 7) // 8 * 8                     # N % 8 == 0; extra columns of B are 0, of y are 0
+        ldb = (r + 7) // 8 * 8
+        Bb = np.zeros((Np, ldb), np.uint16)
+        Bb[:N, :r] = (Bv.view(np.uint32) >> 16).astype(np.uint16)
+        yb = np.zeros((h.shape[0], Np), np.uint16)
+        yb[:, :N] = (yv.view(np.uint32) >> 16).astype(np.uint16)
+        for fn, key in ((dsl.lora_expand_compensated, "compensated_out"), (dsl.lora_expand, "plain_out")):
+            yg = bf16_to_gpu(yb)
+            fn(f32_to_gpu(hp), bf16_to_gpu(Bb), yg, c["scale"], r=r)
+            t.cuda.synchronize()
+            got = oracle.bf16_to_f64(bf16_from_gpu(yg))[:, :N]
+            assert np.array_equal(got, np.array(c[key])), (c["name"], key, got)
+
+
+@pytest.mark.parametrize("M,r,N", [(1, 16, 4096), (37, 5, 1032), (64, 64, 520), (300, 33, 2048)])
+def test_expand_compensated_parity(M, r, N):
+    """Random fp32 h (full 24-bit significands): the compensated expand agrees
+    with the oracle's compensated definition within 1 bf16 ulp (plus the fp32
+    accumulation floor); it matches the correctly rounded product of the fp32
+    h far more often than lora_expand does."""
+    t = torch()
+    rng = np.random.default_rng(300 + r)
+    ldh = (r + 3) // 4 * 4
+    h = np.zeros((M, ldh), np.float32)
+    h[:, :r] = (rng.standard_normal((M, r)) * 0.5).astype(np.float32)
+    Bm = normal_bf16((N, r), 0.05, r, "cpB")
+    ldb = (r + 7) // 8 * 8
+    Bp = np.zeros((N, ldb), np.uint16)
+    Bp[:, :r] = Bm
+    y = np.zeros((M, N), np.uint16)               # y = 0: the output is the product itself
+    yc = bf16_to_gpu(y)
+    dsl.lora_expand_compensated(f32_to_gpu(h), bf16_to_gpu(Bp), yc, 2.0, r=r)
+    yp = bf16_to_gpu(y)
+    dsl.lora_expand(f32_to_gpu(h), bf16_to_gpu(Bp), yp, 2.0, r=r)
+    t.cuda.synchronize()
+    gc, gp = bf16_from_gpu(yc), bf16_from_gpu(yp)
+    yo, e, ab = oracle.expand_compensated(h[:, :r], Bm, y, 2.0)
+    check_expand(gc, yo, e, ab, y, f"compensated M={M} r={r}")
+    # correctly rounded product with the fp32 h itself (no conversion of h)
+    exact = 2.0 * (h[:, :r].astype(np.float64) @ oracle.bf16_to_f64(Bm).T)
+    want = oracle.bf16_rne(exact)
+    match_c = float(np.mean(gc == want))
+    match_p = float(np.mean(gp == want))
+    assert match_c > 0.97 and match_c > match_p, (match_c, match_p)

@@ -320,3 +320,85 @@ def test_sgmv_matches_single_adapter_per_token():
         ys, es, _ = oracle.expand(hf[i:i + 1, :r], Bs[a], y[i:i + 1], float(scales[a]))
         assert np.array_equal(yo[i], ys[0])
         assert np.array_equal(e[i], es[0])
+
+
+# ---------------------------------------------------------------------------
+# compensated expand (h split into bf16 hi + bf16 lo of the residual)
+# ---------------------------------------------------------------------------
+def _exact_bf16_bits(vals):
+    """bf16 bits of values that are exactly bf16 numbers (checked)."""
+    a = np.asarray(vals, dtype=np.float32)
+    u = a.view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0)
+    return (u >> 16).astype(np.uint16)
+
+
+def test_expand_compensated_golden_cases():
+    """The hand-derived cases: the compensated expand keeps the residual of h
+    that the plain expand drops when h is rounded to bf16."""
+    for c in _gold("compensated_expand.json")["cases"]:
+        h = np.array(c["h"], dtype=np.float32)
+        B = _exact_bf16_bits(c["B"])
+        y = _exact_bf16_bits(c["y"])
+        yo, e, _ = oracle.expand_compensated(h, B, y, c["scale"])
+        assert np.array_equal(_bits_to_f64(yo), np.array(c["compensated_out"])), c["name"]
+        assert np.array_equal(e, np.array(c["compensated_out"])), c["name"]
+        yp, _, _ = oracle.expand(h, B, y, c["scale"])
+        assert np.array_equal(_bits_to_f64(yp), np.array(c["plain_out"])), c["name"]
+        O, E = exact.expand_compensated(h, B, y, c["scale"])
+        assert O == yo.tolist() and float(E[0][0]) == c["compensated_out"][0][0], c["name"]
+
+
+@pytest.mark.parametrize("M,r,N,seed", [(1, 1, 3, 0), (2, 4, 5, 1), (3, 8, 4, 2)])
+def test_expand_compensated_against_exact_rationals(M, r, N, seed):
+    rng = np.random.default_rng(100 + seed)
+    h = (rng.standard_normal((M, r)) * 0.3).astype(np.float32)      # full 24-bit significands
+    B = normal_bf16((N, r), 0.5, seed, "cB")
+    y = normal_bf16((M, N), 1.0, seed, "cy")
+    yo, e, _ = oracle.expand_compensated(h, B, y, 2.0)
+    O, E = exact.expand_compensated(h, B, y, 2.0)
+    assert yo.tolist() == O
+    for i in range(M):
+        for n in range(N):
+            assert abs(Fraction(float(e[i, n])) - E[i][n]) <= abs(E[i][n]) * Fraction(2 * r + 2, 2 ** 52) + \
+                Fraction(1, 2 ** 200)
+
+
+def test_expand_compensated_recovers_16_bit_inputs_exactly():
+    """With B = 1, y = 0 and scale 1 the compensated expand returns hi + lo
+    before rounding.  That sum equals h for every h with at most 16
+    significant bits (the residual of an 8-bit rounding then has at most 8
+    bits), and is within 2^-16 relative of h for full fp32 h; the plain
+    expand is only within 2^-8."""
+    rng = np.random.default_rng(7)
+    n = 4000
+    sig = rng.integers(2 ** 15, 2 ** 16, n)                     # exactly 16 significant bits
+    ex = rng.integers(-40, 20, n)
+    sign = rng.choice([-1.0, 1.0], n)
+    h16 = (sign * sig * np.exp2(ex - 15.0)).astype(np.float32)
+    assert np.all(h16.astype(np.float64) == sign * sig * np.exp2(ex - 15.0))
+    one = _exact_bf16_bits([[1.0]])
+    zero = np.zeros((1, 1), np.uint16)
+    for v in h16[:600]:
+        _, e, _ = oracle.expand_compensated(np.array([[v]], np.float32), one, zero, 1.0)
+        assert e[0, 0] == float(v)
+    hf = (rng.standard_normal(600) * np.exp2(rng.integers(-30, 30, 600))).astype(np.float32)
+    worst_c = worst_p = 0.0
+    for v in hf:
+        _, ec, _ = oracle.expand_compensated(np.array([[v]], np.float32), one, zero, 1.0)
+        _, ep, _ = oracle.expand(np.array([[v]], np.float32), one, zero, 1.0)
+        worst_c = max(worst_c, abs(ec[0, 0] - float(v)) / abs(float(v)))
+        worst_p = max(worst_p, abs(ep[0, 0] - float(v)) / abs(float(v)))
+    assert worst_c <= 2.0 ** -16 and worst_p <= 2.0 ** -8 and worst_c < worst_p / 64
+
+
+def test_expand_compensated_equals_plain_for_bf16_inputs():
+    """When h is already a bf16 value the residual is 0 and both expands agree."""
+    M, r, N = 3, 16, 40
+    hb = normal_bf16((M, r), 0.5, 9, "ch")
+    h = bf16_bits_to_f32(hb).astype(np.float32)
+    B = normal_bf16((N, r), 0.02, 9, "cB2")
+    y = normal_bf16((M, N), 1.0, 9, "cy2")
+    a, ea, _ = oracle.expand_compensated(h, B, y, 2.0)
+    b, eb, _ = oracle.expand(h, B, y, 2.0)
+    assert np.array_equal(a, b) and np.array_equal(ea, eb)
