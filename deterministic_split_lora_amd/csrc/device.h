@@ -28,10 +28,15 @@ __device__ __forceinline__ bf16x8 bf16x8_zero()
     return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 }
 
-// 16-byte load of 8 bf16 (the address is 16-byte aligned by the host checks).
+// 16-byte load of 8 bf16 from device memory (the address is 16-byte aligned by
+// the host checks).  The pointer is used as a global-memory pointer, so an
+// adapter pointer read from a device array still gets a global load rather
+// than a flat one.
+typedef __attribute__((address_space(1))) const u32x4 global_u32x4;
+
 __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p)
 {
-    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+    return __builtin_bit_cast(bf16x8, *(const global_u32x4*)(p));
 }
 
 // 8 bf16 starting at p of which only the first n exist (n < 8 only at a

@@ -118,8 +118,10 @@ __global__ __launch_bounds__(W * 64) void k_shrink_partial(ShrinkParams p, int g
 // Large M: T consecutive row blocks per workgroup, all rank tiles together,
 // split index fastest in the 1-D grid.  The row blocks share the A loads (see
 // shrink_tiles); partials and their bits are those of k_shrink_partial.
+// Two 8-wave workgroups per compute unit (4 waves per SIMD, <= 128 VGPRs):
+// one workgroup's loads are in flight while the other runs its trees.
 template <int RT, int W, int T>
-__global__ __launch_bounds__(W * 64) void k_shrink_partial_multi(ShrinkParams p)
+__global__ __launch_bounds__(W * 64, 4) void k_shrink_partial_multi(ShrinkParams p)
 {
     __shared__ float red[red_floats<RT, W>()];
     const uint32_t S = (uint32_t)p.split_k;
@@ -219,7 +221,7 @@ __global__ __launch_bounds__(W * 64) void k_sgmv_shrink_partial(ShrinkParams p)
 // in the plan, so a chunk is usually one stretch).  All rank tiles of r_max
 // in one workgroup.  Same partials, same bits as k_sgmv_shrink_partial.
 template <int RT, int W, int T>
-__global__ __launch_bounds__(W * 64) void k_sgmv_shrink_partial_multi(ShrinkParams p)
+__global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_partial_multi(ShrinkParams p)
 {
     __shared__ float red[red_floats<RT, W>()];
     const int ntiles = plan_tiles(p.tiles, p.M, p.n_adapters);
@@ -489,7 +491,9 @@ hipError_t launch_sgmv_shrink_partial_multi(const ShrinkParams& p, int waves, in
                                             hipStream_t st)
 {
     const int rank_tiles = (p.r_max + 15) / 16;
-    if (tiles_per_wg == 2)
+    // with 3-4 rank tiles, four plan tiles per workgroup do not fit in the
+    // 128 registers of two workgroups per compute unit: take two
+    if (tiles_per_wg == 2 || rank_tiles > 2)
         launch_multi_t<2>(p, waves, rank_tiles, dim3((unsigned)grid), true, st);
     else
         launch_multi_t<4>(p, waves, rank_tiles, dim3((unsigned)grid), true, st);

@@ -45,13 +45,70 @@ template <int RT, int W, int MODE>
 __device__ __forceinline__ void wave_tree_store(const ShrinkParams& p, int64_t row0, int nrows, int rg, int col0,
                                                 int s, float scale, float* red, const f32x4 (&acc)[RT]);
 
-// One work item: rows row0 .. row0+nrows-1, split s, rank columns col0 ..
-// col0 + 16 RT - 1 (those below r).  A is the adapter's row 0.
-template <int RT, int W, int MODE>
-__device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0, int nrows,
-                                            const uint16_t* __restrict__ A, int r, int col0, int s, float scale,
-                                            float* red)
+// The matrix-core chains of one wave: T row tiles (x row pointers xp[u]) times
+// NRT rank tiles (A row pointers ap[rt]), `steps` steps of 32 k from the
+// pointers on, each accumulator in ascending k.  Steps go in groups of G with
+// all loads of a group issued before its matrix-core steps, without any guard;
+// the steps left over after the last full group go one at a time.  Lanes whose token row or rank column lies outside
+// the tile load from a clamped, valid row: matrix-core output (i, j) depends
+// only on row i of the first operand and column j of the second, and outputs
+// of such lanes are never stored, so no operand needs to be zeroed.
+template <int NRT, int RT, int T, int G>
+__device__ __forceinline__ void mfma_chains(const uint16_t* const (&xp)[T], const uint16_t* const (&ap)[RT], int steps,
+                                            f32x4 (&acc)[T][RT])
 {
+    int t = 0;
+    for (; t + G <= steps; t += G) {
+        bf16x8 xa[G][T];
+        bf16x8 b[G][NRT];
+#pragma unroll
+        for (int q = 0; q < G; ++q) {
+            const int off = (t + q) * kKStep;
+#pragma unroll
+            for (int u = 0; u < T; ++u)
+                xa[q][u] = load_bf16x8(xp[u] + off);
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt)
+                b[q][rt] = load_bf16x8(ap[rt] + off);
+        }
+#pragma unroll
+        for (int q = 0; q < G; ++q)
+#pragma unroll
+            for (int u = 0; u < T; ++u)
+#pragma unroll
+                for (int rt = 0; rt < NRT; ++rt)
+                    acc[u][rt] = mfma_16x16x32(xa[q][u], b[q][rt], acc[u][rt]);
+    }
+    for (; t < steps; ++t) {
+        const int off = t * kKStep;
+        bf16x8 xa[T];
+        bf16x8 b[NRT];
+#pragma unroll
+        for (int u = 0; u < T; ++u)
+            xa[u] = load_bf16x8(xp[u] + off);
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+            b[rt] = load_bf16x8(ap[rt] + off);
+#pragma unroll
+        for (int u = 0; u < T; ++u)
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt)
+                acc[u][rt] = mfma_16x16x32(xa[u], b[rt], acc[u][rt]);
+    }
+}
+
+// T row tiles (row0[u], nrows[u]; a tile with nrows 0 is skipped) that share
+// one adapter, split s and rank columns col0 .. col0 + 16 RT - 1 (those below
+// r): every (tile, rank tile) accumulator gets its chain over the wave's k
+// range, the A loads shared by the T tiles, then the wave tree and the store.
+// Per element the arithmetic depends only on (K, split_k): the tiles a
+// workgroup holds and the rank tiles grouped with it change no bit.
+template <int RT, int W, int MODE, int T>
+__device__ __forceinline__ void shrink_tiles(const ShrinkParams& p, const int64_t (&row0)[T], const int (&nrows)[T],
+                                             const uint16_t* __restrict__ A, int r, int col0, int s, float scale,
+                                             float* red)
+{
+    constexpr int G = T == 1 ? 4 : 2;
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int li = lane & 15;
@@ -61,85 +118,15 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0,
 
     // Reduction slots 8g..8g+7 of step t hold k = kbase + 32 t + (0..7).
     const int64_t kbase = (int64_t)s * p.k_chunk + (int64_t)wave * steps * kKStep + g * 8;
-    const bool row_ok = li < nrows;
-    const uint16_t* xp = p.x + (row0 + (row_ok ? li : 0)) * p.ld_x + kbase;
-    const uint16_t* ap[RT];
-    bool a_ok[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-        const int j = rt * 16 + li;
-        a_ok[rt] = j < rg;
-        ap[rt] = A + (int64_t)(col0 + (a_ok[rt] ? j : 0)) * p.ld_a + kbase;
-    }
-
-    f32x4 acc[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-        acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    // Groups of up to 4 steps: issue all loads of the group, then the
-    // matrix-core steps in ascending k.
-    for (int t0 = 0; t0 < steps; t0 += 4) {
-        bf16x8 xa[4];
-        bf16x8 b[4][RT];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (t0 + u < steps) {
-                const int off = (t0 + u) * kKStep;
-                xa[u] = row_ok ? load_bf16x8(xp + off) : bf16x8_zero();
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-                    b[u][rt] = (rt * 16 < rg && a_ok[rt]) ? load_bf16x8(ap[rt] + off) : bf16x8_zero();
-            }
-        }
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            if (t0 + u < steps) {
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-                    if (rt * 16 < rg)
-                        acc[rt] = mfma_16x16x32(xa[u], b[u][rt], acc[rt]);
-            }
-        }
-    }
-
-    wave_tree_store<RT, W, MODE>(p, row0, nrows, rg, col0, s, scale, red, acc);
-}
-
-// Several row tiles that share one adapter and rank columns: T 16-row tiles
-// (row0[u], nrows[u]; a tile with nrows 0 is skipped) against the same A
-// operands, loaded once per matrix-core step for all T tiles.  Each (tile,
-// rank tile) accumulator sees the same steps in the same ascending k order as
-// in shrink_tile, and the wave tree is the same, so every partial has the same
-// bits; only the A loads are shared.  Steps go in groups of two.
-template <int RT, int W, int MODE, int T>
-__device__ __forceinline__ void shrink_tiles(const ShrinkParams& p, const int64_t (&row0)[T], const int (&nrows)[T],
-                                             const uint16_t* __restrict__ A, int r, int col0, int s, float scale,
-                                             float* red)
-{
-    constexpr int G = 2;
-    const int wave = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
-    const int li = lane & 15;
-    const int g = lane >> 4;
-    const int steps = p.k_steps;
-    const int rg = r - col0;
-
-    const int64_t kbase = (int64_t)s * p.k_chunk + (int64_t)wave * steps * kKStep + g * 8;
     const uint16_t* xp[T];
-    bool row_ok[T];
 #pragma unroll
-    for (int u = 0; u < T; ++u) {
-        row_ok[u] = li < nrows[u];
-        xp[u] = p.x + (row0[u] + (row_ok[u] ? li : 0)) * p.ld_x + kbase;
-    }
+    for (int u = 0; u < T; ++u)
+        xp[u] = p.x + (row0[u] + (li < nrows[u] ? li : 0)) * p.ld_x + kbase;
     const uint16_t* ap[RT];
-    bool a_ok[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int j = rt * 16 + li;
-        a_ok[rt] = j < rg;
-        ap[rt] = A + (int64_t)(col0 + (a_ok[rt] ? j : 0)) * p.ld_a + kbase;
+        ap[rt] = A + (int64_t)(col0 + (j < rg ? j : 0)) * p.ld_a + kbase;
     }
     f32x4 acc[T][RT];
 #pragma unroll
@@ -148,37 +135,36 @@ __device__ __forceinline__ void shrink_tiles(const ShrinkParams& p, const int64_
         for (int rt = 0; rt < RT; ++rt)
             acc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int t0 = 0; t0 < steps; t0 += G) {
-        bf16x8 xa[G][T];
-        bf16x8 b[G][RT];
-#pragma unroll
-        for (int q = 0; q < G; ++q) {
-            if (t0 + q < steps) {
-                const int off = (t0 + q) * kKStep;
-#pragma unroll
-                for (int u = 0; u < T; ++u)
-                    xa[q][u] = row_ok[u] ? load_bf16x8(xp[u] + off) : bf16x8_zero();
-#pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
-                    b[q][rt] = (rt * 16 < rg && a_ok[rt]) ? load_bf16x8(ap[rt] + off) : bf16x8_zero();
-            }
-        }
-#pragma unroll
-        for (int q = 0; q < G; ++q) {
-            if (t0 + q < steps) {
-#pragma unroll
-                for (int u = 0; u < T; ++u)
-#pragma unroll
-                    for (int rt = 0; rt < RT; ++rt)
-                        if (rt * 16 < rg)
-                            acc[u][rt] = mfma_16x16x32(xa[q][u], b[q][rt], acc[u][rt]);
-            }
+    // rank tiles with at least one column below r (uniform)
+    const int nrt = (rg + 15) / 16 < RT ? (rg + 15) / 16 : RT;
+    if (nrt >= RT)
+        mfma_chains<RT, RT, T, G>(xp, ap, steps, acc);
+    else if constexpr (RT >= 2) {
+        if (nrt == 1)
+            mfma_chains<1, RT, T, G>(xp, ap, steps, acc);
+        else if constexpr (RT >= 3) {
+            if (nrt == 2)
+                mfma_chains<2, RT, T, G>(xp, ap, steps, acc);
+            else if constexpr (RT >= 4)
+                mfma_chains<3, RT, T, G>(xp, ap, steps, acc);
         }
     }
 #pragma unroll
     for (int u = 0; u < T; ++u)
         if (nrows[u] > 0)                         // uniform across the workgroup
             wave_tree_store<RT, W, MODE>(p, row0[u], nrows[u], rg, col0, s, scale, red, acc[u]);
+}
+
+// One work item: rows row0 .. row0+nrows-1, split s, rank columns col0 ..
+// col0 + 16 RT - 1 (those below r).  A is the adapter's row 0.
+template <int RT, int W, int MODE>
+__device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0, int nrows,
+                                            const uint16_t* __restrict__ A, int r, int col0, int s, float scale,
+                                            float* red)
+{
+    const int64_t rows[1] = {row0};
+    const int n[1] = {nrows};
+    shrink_tiles<RT, W, MODE, 1>(p, rows, n, A, r, col0, s, scale, red);
 }
 
 // acc[rt][v] is the wave's sum for token row 4g+v, rank column col0 + 16 rt + li:
