@@ -81,12 +81,11 @@ int sgmv_group_tiles(int64_t M, int32_t split_k, int32_t r_max)
     return group_tiles_for(M, split_k, (r_max + 15) / 16) == 1 ? 1 : kMaxRankTiles;
 }
 
-// Persistent grid: never more workgroups than items can exist (tiles <= M).
-// Work items of the multi-adapter kernels are counted in 32 bits.
-bool sgmv_items_fit(int64_t M, int32_t split_k, int64_t N)
+// Work items of the multi-adapter shrinks (at most M tiles x split_k x
+// kMaxRankTiles) are counted in 32 bits.
+bool sgmv_items_fit(int64_t M, int32_t split_k)
 {
-    const int64_t nblocks = (N + kExpandCols - 1) / kExpandCols;
-    return M * split_k * kMaxRankTiles <= kMaxGrid && M * nblocks <= kMaxGrid;
+    return M * split_k * kMaxRankTiles <= kMaxGrid;
 }
 
 int sgmv_grid(int64_t M, int32_t split_k, int32_t r_max, int group_tiles)
@@ -278,7 +277,8 @@ int lora_shrink_splitk(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64
     if (split_k == 1) {
         p.out = h;
         p.ld_out = ld_h;
-        return launch_status(launch_shrink_partial_direct(p, pl.waves, pl.rank_tiles, group_tiles_for(M, split_k, pl.rank_tiles), s));
+        return launch_status(launch_shrink_partial_direct(p, pl.waves, pl.rank_tiles,
+                                                          group_tiles_for(M, split_k, pl.rank_tiles), s));
     }
     const size_t need = lora_shrink_workspace_bytes(M, r, split_k);
     if (!workspace)
@@ -320,7 +320,8 @@ int lora_shrink_splitk_atomic(const uint16_t* x, int64_t ld_x, const uint16_t* A
     ShrinkParams p = shrink_params(x, ld_x, A, ld_a, M, r, pl, scale);
     p.out = h;
     p.ld_out = ld_h;
-    return launch_status(launch_shrink_partial_atomic(p, pl.waves, pl.rank_tiles, group_tiles_for(M, split_k, pl.rank_tiles), s));
+    return launch_status(launch_shrink_partial_atomic(p, pl.waves, pl.rank_tiles,
+                                                      group_tiles_for(M, split_k, pl.rank_tiles), s));
 }
 
 namespace {
@@ -595,7 +596,8 @@ int lora_shrink_splitk_counted(const uint16_t* x, int64_t ld_x, const uint16_t* 
     if (split_k == 1) {                         // one split: it is its own last arrival
         p.out = h;
         p.ld_out = ld_h;
-        return launch_status(launch_shrink_partial_direct(p, pl.waves, pl.rank_tiles, group_tiles_for(M, split_k, pl.rank_tiles), s));
+        return launch_status(launch_shrink_partial_direct(p, pl.waves, pl.rank_tiles,
+                                                          group_tiles_for(M, split_k, pl.rank_tiles), s));
     }
     if (!workspace || !counters)
         return LORA_ERR_NULL;
@@ -610,7 +612,8 @@ int lora_shrink_splitk_counted(const uint16_t* x, int64_t ld_x, const uint16_t* 
     c.counters = counters;
     c.h = h;
     c.ld_h = ld_h;
-    return launch_status(launch_shrink_counted(p, c, pl.waves, pl.rank_tiles, group_tiles_for(M, split_k, pl.rank_tiles), s));
+    return launch_status(launch_shrink_counted(p, c, pl.waves, pl.rank_tiles,
+                                               group_tiles_for(M, split_k, pl.rank_tiles), s));
 }
 
 size_t lora_sgmv_counter_bytes(int64_t M)
@@ -632,7 +635,7 @@ int lora_sgmv_shrink_counted(const uint16_t* x, int64_t ld_x, const uint16_t* co
     int st = make_plan(K, r_max, split_k, &pl);
     if (st != LORA_OK)
         return st;
-    if (!sgmv_items_fit(M, split_k, 0))
+    if (!sgmv_items_fit(M, split_k))
         return LORA_ERR_SHAPE;
     if (M == 0)
         return LORA_OK;
@@ -716,7 +719,7 @@ int lora_sgmv_shrink(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_p
     int st = make_plan(K, r_max, split_k, &pl);
     if (st != LORA_OK)
         return st;
-    if (!sgmv_items_fit(M, split_k, 0))
+    if (!sgmv_items_fit(M, split_k))
         return LORA_ERR_SHAPE;
     if (M == 0)
         return LORA_OK;

@@ -58,6 +58,10 @@ SHRINK_CASES = [
     (100, 4096, 48, 1, 1.0, "S=1 direct"),
     (1, 8192, 64, 16, 2.0, "decode rank 64 S=16"),
     (300, 14336, 32, 8, 1.0, "down-proj shape, 7 steps per wave"),
+    (3, 32, 16, 1, 1.0, "minimal K: one step, one wave"),
+    (17, 64, 64, 2, 1.0, "minimal K per split, S=2"),
+    (1, 512, 7, 16, 2.0, "minimal K per split, S=16"),
+    (33, 96, 5, 1, 1.0, "three steps on one wave (odd step count)"),
 ]
 
 
@@ -542,7 +546,8 @@ def test_sgmv_prefill_full_size_sampled():
 # ---------------------------------------------------------------------------
 # fused shrink + expand (two launches) and HIP graph capture
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("M,K,r,N,S", [(1, 4096, 16, 4096, 8), (16, 4096, 16, 4096, 8), (256, 4096, 16, 4096, 8),
+@pytest.mark.parametrize("M,K,r,N,S", [(1, 4096, 16, 4096, 8), (16, 4096, 16, 4096, 8), (64, 4096, 16, 4096, 8),
+                                       (256, 4096, 16, 4096, 8), (1, 32, 16, 256, 1), (20, 1024, 64, 8, 16),
                                        (37, 8192, 64, 1032, 16), (5, 1024, 8, 512, 1), (70, 2048, 40, 264, 4),
                                        (3, 3072, 1, 8, 2), (64, 14336, 32, 4096, 8), (65, 4096, 24, 1000, 8),
                                        (9, 1024, 33, 520, 4), (2, 16384, 64, 512, 16)])
@@ -724,8 +729,8 @@ def test_batch_invariance_across_schedule_switch():
             y[pos] = ybase[grp]
             h = t.empty((M, r), dtype=t.float32, device="cuda")
             yg = bf16_to_gpu(y)
-            dsl.lora_shrink_expand(bf16_to_gpu(x), Ag, Bg, yg, workspace(dsl.lora_shrink_expand_workspace_bytes(M, r, S)),
-                                   S, 1.0, 2.0, h=h)
+            ws = workspace(dsl.lora_shrink_expand_workspace_bytes(M, r, S))
+            dsl.lora_shrink_expand(bf16_to_gpu(x), Ag, Bg, yg, ws, S, 1.0, 2.0, h=h)
             t.cuda.synchronize()
             assert np.array_equal(f32_bits(h)[pos], ref_h[grp]), f"h at batch {b}"
             assert np.array_equal(bf16_from_gpu(yg)[pos], ref_y[grp]), f"y at batch {b}"

@@ -251,7 +251,8 @@ def test_expand_against_exact_rationals(M, r, N, seed):
     assert yo.tolist() == O
     for i in range(M):
         for n in range(N):
-            assert abs(Fraction(float(e[i, n])) - E[i][n]) <= abs(E[i][n]) * Fraction(r + 2, 2 ** 52) + Fraction(1, 2 ** 200)
+            assert abs(Fraction(float(e[i, n])) - E[i][n]) <= \
+                abs(E[i][n]) * Fraction(r + 2, 2 ** 52) + Fraction(1, 2 ** 200)
 
 
 def test_expand_B_zero_leaves_y_bitwise():
