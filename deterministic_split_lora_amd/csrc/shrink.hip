@@ -446,12 +446,15 @@ namespace {
 template <int RT, int T>
 void launch_multi_rt(const ShrinkParams& p, int waves, dim3 grid, bool sgmv, hipStream_t st)
 {
-#define LORA_MULTI(W_)                                                                                   \
-    do {                                                                                                 \
-        if (sgmv)                                                                                        \
-            hipLaunchKernelGGL((k_sgmv_shrink_partial_multi<RT, W_, T>), grid, dim3(W_ * 64), 0, st, p); \
-        else                                                                                             \
-            hipLaunchKernelGGL((k_shrink_partial_multi<RT, W_, T>), grid, dim3(W_ * 64), 0, st, p);      \
+    // the multi-adapter kernel takes at most two tiles with 3-4 rank tiles
+    // (four do not fit in 128 registers), so that variant is not built
+    constexpr int TS = (RT > 2 && T > 2) ? 2 : T;
+#define LORA_MULTI(W_)                                                                                    \
+    do {                                                                                                  \
+        if (sgmv)                                                                                         \
+            hipLaunchKernelGGL((k_sgmv_shrink_partial_multi<RT, W_, TS>), grid, dim3(W_ * 64), 0, st, p); \
+        else                                                                                              \
+            hipLaunchKernelGGL((k_shrink_partial_multi<RT, W_, T>), grid, dim3(W_ * 64), 0, st, p);       \
     } while (0)
     switch (waves) {
     case 1: LORA_MULTI(1); break;

@@ -53,8 +53,21 @@ __device__ __forceinline__ void wave_tree_store(const ShrinkParams& p, int64_t r
 // the tile load from a clamped, valid row: matrix-core output (i, j) depends
 // only on row i of the first operand and column j of the second, and outputs
 // of such lanes are never stored, so no operand needs to be zeroed.
-template <int NRT, int RT, int T, int G>
-__device__ __forceinline__ void mfma_chains(const uint16_t* const (&xp)[T], const uint16_t* const (&ap)[RT], int steps,
+template <bool MASK>
+__device__ __forceinline__ bf16x8 operand_load(const uint16_t* p, bool ok)
+{
+    if constexpr (MASK)
+        return ok ? load_bf16x8(p) : bf16x8_zero();
+    else
+        return load_bf16x8(p);
+}
+
+// MASK: lanes outside the tile skip their loads (fewer addresses for the
+// texture units when a tile has few rows, e.g. one decode token); their
+// operands are then zeros instead of a clamped row - again never stored.
+template <int NRT, int RT, int T, int G, bool MASK>
+__device__ __forceinline__ void mfma_chains(const uint16_t* const (&xp)[T], const bool (&x_ok)[T],
+                                            const uint16_t* const (&ap)[RT], const bool (&a_ok)[RT], int steps,
                                             f32x4 (&acc)[T][RT])
 {
     int t = 0;
@@ -66,10 +79,10 @@ __device__ __forceinline__ void mfma_chains(const uint16_t* const (&xp)[T], cons
             const int off = (t + q) * kKStep;
 #pragma unroll
             for (int u = 0; u < T; ++u)
-                xa[q][u] = load_bf16x8(xp[u] + off);
+                xa[q][u] = operand_load<MASK>(xp[u] + off, x_ok[u]);
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt)
-                b[q][rt] = load_bf16x8(ap[rt] + off);
+                b[q][rt] = operand_load<MASK>(ap[rt] + off, a_ok[rt]);
         }
 #pragma unroll
         for (int q = 0; q < G; ++q)
@@ -85,15 +98,35 @@ __device__ __forceinline__ void mfma_chains(const uint16_t* const (&xp)[T], cons
         bf16x8 b[NRT];
 #pragma unroll
         for (int u = 0; u < T; ++u)
-            xa[u] = load_bf16x8(xp[u] + off);
+            xa[u] = operand_load<MASK>(xp[u] + off, x_ok[u]);
 #pragma unroll
         for (int rt = 0; rt < NRT; ++rt)
-            b[rt] = load_bf16x8(ap[rt] + off);
+            b[rt] = operand_load<MASK>(ap[rt] + off, a_ok[rt]);
 #pragma unroll
         for (int u = 0; u < T; ++u)
 #pragma unroll
             for (int rt = 0; rt < NRT; ++rt)
                 acc[u][rt] = mfma_16x16x32(xa[u], b[rt], acc[u][rt]);
+    }
+}
+
+// The chains for nrt (1 .. RT) active rank tiles.
+template <int RT, int T, int G, bool MASK>
+__device__ __forceinline__ void mfma_dispatch(int nrt, const uint16_t* const (&xp)[T], const bool (&x_ok)[T],
+                                              const uint16_t* const (&ap)[RT], const bool (&a_ok)[RT], int steps,
+                                              f32x4 (&acc)[T][RT])
+{
+    if (nrt >= RT)
+        mfma_chains<RT, RT, T, G, MASK>(xp, x_ok, ap, a_ok, steps, acc);
+    else if constexpr (RT >= 2) {
+        if (nrt == 1)
+            mfma_chains<1, RT, T, G, MASK>(xp, x_ok, ap, a_ok, steps, acc);
+        else if constexpr (RT >= 3) {
+            if (nrt == 2)
+                mfma_chains<2, RT, T, G, MASK>(xp, x_ok, ap, a_ok, steps, acc);
+            else if constexpr (RT >= 4)
+                mfma_chains<3, RT, T, G, MASK>(xp, x_ok, ap, a_ok, steps, acc);
+        }
     }
 }
 
@@ -119,14 +152,21 @@ __device__ __forceinline__ void shrink_tiles(const ShrinkParams& p, const int64_
     // Reduction slots 8g..8g+7 of step t hold k = kbase + 32 t + (0..7).
     const int64_t kbase = (int64_t)s * p.k_chunk + (int64_t)wave * steps * kKStep + g * 8;
     const uint16_t* xp[T];
+    bool x_ok[T];
+    bool full = true;                        // every tile has 16 rows (uniform)
 #pragma unroll
-    for (int u = 0; u < T; ++u)
-        xp[u] = p.x + (row0[u] + (li < nrows[u] ? li : 0)) * p.ld_x + kbase;
+    for (int u = 0; u < T; ++u) {
+        x_ok[u] = li < nrows[u];
+        full = full && (nrows[u] == kRowBlock || nrows[u] == 0);
+        xp[u] = p.x + (row0[u] + (x_ok[u] ? li : 0)) * p.ld_x + kbase;
+    }
     const uint16_t* ap[RT];
+    bool a_ok[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
         const int j = rt * 16 + li;
-        ap[rt] = A + (int64_t)(col0 + (j < rg ? j : 0)) * p.ld_a + kbase;
+        a_ok[rt] = j < rg;
+        ap[rt] = A + (int64_t)(col0 + (a_ok[rt] ? j : 0)) * p.ld_a + kbase;
     }
     f32x4 acc[T][RT];
 #pragma unroll
@@ -135,20 +175,14 @@ __device__ __forceinline__ void shrink_tiles(const ShrinkParams& p, const int64_
         for (int rt = 0; rt < RT; ++rt)
             acc[u][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // rank tiles with at least one column below r (uniform)
+    // rank tiles with at least one column below r (uniform); masked loads
+    // only for a single tile with padding rows or padding rank columns (the
+    // several-tile kernels are register-bound and see full tiles almost only)
     const int nrt = (rg + 15) / 16 < RT ? (rg + 15) / 16 : RT;
-    if (nrt >= RT)
-        mfma_chains<RT, RT, T, G>(xp, ap, steps, acc);
-    else if constexpr (RT >= 2) {
-        if (nrt == 1)
-            mfma_chains<1, RT, T, G>(xp, ap, steps, acc);
-        else if constexpr (RT >= 3) {
-            if (nrt == 2)
-                mfma_chains<2, RT, T, G>(xp, ap, steps, acc);
-            else if constexpr (RT >= 4)
-                mfma_chains<3, RT, T, G>(xp, ap, steps, acc);
-        }
-    }
+    if (T > 1 || (full && rg >= 16 * nrt))
+        mfma_dispatch<RT, T, G, false>(nrt, xp, x_ok, ap, a_ok, steps, acc);
+    else if constexpr (T == 1)
+        mfma_dispatch<RT, T, G, true>(nrt, xp, x_ok, ap, a_ok, steps, acc);
 #pragma unroll
     for (int u = 0; u < T; ++u)
         if (nrows[u] > 0)                         // uniform across the workgroup
