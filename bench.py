@@ -561,10 +561,10 @@ def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S):
     torch.cuda.synchronize()
 
     def shrink(st):
-        dsl.lora_sgmv_shrink(st["x"], st["Ap"], K, ranks_g, scales_g, ids_g, n, plan, st["h"], c.r_max, S, st["ws"])
+        dsl.lora_sgmv_shrink(st["x"], st["Ap"], K, ranks_g, None, ids_g, n, plan, st["h"], c.r_max, S, st["ws"])
 
     def shrink_counted(st):
-        dsl.lora_sgmv_shrink_counted(st["x"], st["Ap"], K, ranks_g, scales_g, n, plan, st["h"], c.r_max, S,
+        dsl.lora_sgmv_shrink_counted(st["x"], st["Ap"], K, ranks_g, None, n, plan, st["h"], c.r_max, S,
                                      st["ws"], cnt)
 
     def expand(st):
@@ -573,6 +573,10 @@ def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S):
     def both(st):
         shrink(st)
         expand(st)
+
+    def pipeline(st):
+        dsl.lora_sgmv_shrink_expand(st["x"], st["Ap"], K, st["Bp"], ranks_g, None, scales_g, ids_g, n, plan, st["y"],
+                                    c.r_max, S, st["ws"], h=st["h"])
 
     def plan_only(st):
         dsl.lora_sgmv_plan(ids_g, n, plan)
@@ -583,6 +587,7 @@ def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S):
            "expand_bytes": ex_bytes, "workspace_bytes": 8 * S * M * c.r_max, "copies": copies}
     for name, call, byt in (("shrink", shrink, sh_bytes), ("shrink_one_launch", shrink_counted, sh_bytes),
                             ("expand", expand, ex_bytes), ("shrink_expand", both, sh_bytes + ex_bytes),
+                            ("shrink_expand_pipeline", pipeline, sh_bytes + ex_bytes),
                             ("plan", plan_only, 0)):
         us = _time_rotating(call, sets, args)
         out[name] = {"us": round(us, 3)}

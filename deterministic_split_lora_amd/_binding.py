@@ -31,6 +31,7 @@ EXPORTED = [
     "lora_shrink_expand_fused", "lora_shrink_expand_launches", "lora_shrink_counter_bytes",
     "lora_shrink_splitk_counted", "lora_sgmv_counter_bytes", "lora_sgmv_shrink_counted",
     "lora_shrink_expand_counter_bytes", "lora_shrink_expand_counted", "lora_expand_compensated",
+    "lora_sgmv_shrink_expand",
 ]
 
 
@@ -123,6 +124,9 @@ def lib():
                                        _i64, _i32, _i32, _vp, _sz, _vp]
         L.lora_sgmv_expand.restype = ctypes.c_int
         L.lora_sgmv_expand.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _i64, _i64, _i64, _i32, _vp]
+        L.lora_sgmv_shrink_expand.restype = ctypes.c_int
+        L.lora_sgmv_shrink_expand.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp,
+                                              _i64, _vp, _i64, _i64, _i64, _i64, _i32, _i32, _vp, _sz, _vp]
         _lib = L
     return _lib
 
@@ -425,6 +429,27 @@ def lora_sgmv_shrink_counted(x, A_ptrs, ld_a: int, ranks, scales, n_adapters: in
                                         _nbytes(counters), _stream(stream, x))
     _check(st, "lora_sgmv_shrink_counted")
     return h
+
+
+def lora_sgmv_shrink_expand(x, A_ptrs, ld_a: int, B_ptrs, ranks, shrink_scales, expand_scales, token_adapter,
+                            n_adapters: int, plan, y, r_max: int, split_k: int, workspace, h=None, stream=None):
+    """Multi-adapter shrink + expand in two launches (expand reads the Split-K
+    workspace); y updated in place, h (optional) receives the shrink output."""
+    import torch
+    _dtype(x, torch.bfloat16, "x"); _dtype(y, torch.bfloat16, "y"); _dtype(token_adapter, torch.int32, "ids")
+    if h is not None:
+        _dtype(h, torch.float32, "h")
+    M, K = x.shape
+    N = y.shape[1]
+    if y.shape[0] != M:
+        raise ValueError("x and y must have the same number of rows")
+    st = lib().lora_sgmv_shrink_expand(_ptr(x), _ld(x, "x"), _ptr(A_ptrs), ld_a, _ptr(B_ptrs), _ptr(ranks),
+                                       _ptr(shrink_scales), _ptr(expand_scales), _ptr(token_adapter), n_adapters,
+                                       _ptr(plan), _nbytes(plan), _ptr(h), _ld(h, "h") if h is not None else 0,
+                                       _ptr(y), _ld(y, "y"), M, K, N, r_max, split_k, _ptr(workspace),
+                                       _nbytes(workspace), _stream(stream, x))
+    _check(st, "lora_sgmv_shrink_expand")
+    return y
 
 
 def lora_sgmv_expand(h, B_ptrs, ranks, scales, token_adapter, n_adapters: int, y, r_max: int, stream=None):

@@ -223,6 +223,62 @@ int launch_fused(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_
     return launch_status(launch_shrink_expand_fused(p, pl.split_k, pl.waves, static_cast<hipStream_t>(stream)));
 }
 
+// The partial kernel of the multi-adapter two-pass shrink (arguments checked).
+int launch_sgmv_partials(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_ptrs, int64_t ld_a,
+                         const int32_t* ranks, int32_t n_adapters, const void* plan, int64_t M, int32_t r_max,
+                         const lora_shrink_plan_t& pl, void* workspace, hipStream_t s)
+{
+    ShrinkParams p{};
+    p.x = x;
+    p.ld_x = ld_x;
+    p.ld_a = ld_a;
+    p.A_ptrs = A_ptrs;
+    p.ranks = ranks;
+    p.tiles = static_cast<const int32_t*>(plan);
+    p.out = static_cast<float*>(workspace);
+    p.ld_out = r_max;
+    p.split_stride = M * r_max;
+    p.M = M;
+    p.r = r_max;
+    p.r_max = r_max;
+    p.k_chunk = pl.k_chunk;
+    p.k_steps = pl.k_steps;
+    p.split_k = pl.split_k;
+    p.n_adapters = n_adapters;
+    p.scale = 1.0f;
+    // Tiles never exceed M; the grid is a fixed bound, idle workgroups exit.
+    const int T = shrink_tiles_per_wg(M, pl.split_k);
+    if (T > 1) {
+        const int64_t bound = (M + T - 1) / T * pl.split_k;
+        return launch_status(
+            launch_sgmv_shrink_partial_multi(p, pl.waves, T, (int)(bound < 2048 ? bound : 2048), s));
+    }
+    const int gt = sgmv_group_tiles(M, pl.split_k, r_max);
+    const int grid = sgmv_grid(M, pl.split_k, r_max, gt);
+    return launch_status(launch_sgmv_shrink_partial(p, pl.waves, gt, grid, s));
+}
+
+// Second pass of the multi-adapter shrink over a [split_k][M][r_max] workspace.
+TreeParams sgmv_tree_params(void* workspace, int64_t M, int32_t r_max, float* h, int64_t ld_h,
+                            const int32_t* token_adapter, const int32_t* ranks, const float* scales,
+                            int32_t n_adapters)
+{
+    TreeParams t{};
+    t.ws = static_cast<const float*>(workspace);
+    t.split_stride = M * r_max;
+    t.ldw = r_max;
+    t.h = h;
+    t.ld_h = ld_h;
+    t.M = M;
+    t.ncols = r_max;
+    t.scale = 1.0f;
+    t.ids = token_adapter;
+    t.ranks = ranks;
+    t.scales = scales;
+    t.n_adapters = n_adapters;
+    return t;
+}
+
 }  // namespace
 
 extern "C" {
@@ -733,50 +789,79 @@ int lora_sgmv_shrink(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_p
     if (plan_bytes < lora_sgmv_plan_bytes(M) || ws_bytes < workspace_bytes(M, r_max, split_k))
         return LORA_ERR_WORKSPACE;
     const hipStream_t s = static_cast<hipStream_t>(stream);
-    ShrinkParams p{};
-    p.x = x;
-    p.ld_x = ld_x;
-    p.ld_a = ld_a;
-    p.A_ptrs = A_ptrs;
-    p.ranks = ranks;
-    p.tiles = static_cast<const int32_t*>(plan);
-    p.out = static_cast<float*>(workspace);
-    p.ld_out = r_max;
-    p.split_stride = M * r_max;
-    p.M = M;
-    p.r = r_max;
-    p.r_max = r_max;
-    p.k_chunk = pl.k_chunk;
-    p.k_steps = pl.k_steps;
-    p.split_k = split_k;
-    p.n_adapters = n_adapters;
-    p.scale = 1.0f;
-    // Tiles never exceed M; the grid is a fixed bound, idle workgroups exit.
-    const int T = shrink_tiles_per_wg(M, split_k);
-    if (T > 1) {
-        const int64_t bound = (M + T - 1) / T * split_k;
-        st = launch_status(launch_sgmv_shrink_partial_multi(p, pl.waves, T, (int)(bound < 2048 ? bound : 2048), s));
-    } else {
-        const int gt = sgmv_group_tiles(M, split_k, r_max);
-        const int grid = sgmv_grid(M, split_k, r_max, gt);
-        st = launch_status(launch_sgmv_shrink_partial(p, pl.waves, gt, grid, s));
-    }
+    st = launch_sgmv_partials(x, ld_x, A_ptrs, ld_a, ranks, n_adapters, plan, M, r_max, pl, workspace, s);
     if (st != LORA_OK)
         return st;
-    TreeParams t{};
-    t.ws = static_cast<const float*>(workspace);
-    t.split_stride = M * r_max;
-    t.ldw = r_max;
-    t.h = h;
-    t.ld_h = ld_h;
-    t.M = M;
-    t.ncols = r_max;
-    t.scale = 1.0f;
-    t.ids = token_adapter;
-    t.ranks = ranks;
-    t.scales = scales;
-    t.n_adapters = n_adapters;
+    const TreeParams t = sgmv_tree_params(workspace, M, r_max, h, ld_h, token_adapter, ranks, scales, n_adapters);
     return launch_status(launch_splitk_tree(t, split_k, true, s));
+}
+
+int lora_sgmv_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_ptrs, int64_t ld_a,
+                            const uint16_t* const* B_ptrs, const int32_t* ranks, const float* shrink_scales,
+                            const float* expand_scales, const int32_t* token_adapter, int32_t n_adapters,
+                            const void* plan, size_t plan_bytes, float* h, int64_t ld_h, uint16_t* y, int64_t ld_y,
+                            int64_t M, int64_t K, int64_t N, int32_t r_max, int32_t split_k, void* workspace,
+                            size_t ws_bytes, void* stream)
+{
+    if (M < 0 || M > kMaxDim || N < 0 || N > kMaxDim || n_adapters < 1)
+        return LORA_ERR_SHAPE;
+    lora_shrink_plan_t pl;
+    int st = make_plan(K, r_max, split_k, &pl);
+    if (st != LORA_OK)
+        return st;
+    if (N % 8 != 0)
+        return LORA_ERR_UNSUPPORTED;
+    if (!sgmv_items_fit(M, split_k) ||
+        ((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols) > kMaxGrid)
+        return LORA_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return LORA_OK;
+    if (!x || !A_ptrs || !B_ptrs || !ranks || !token_adapter || !plan || !y || !workspace)
+        return LORA_ERR_NULL;
+    if (ld_x < K || ld_a < K || ld_y < N || (h && ld_h < r_max))
+        return LORA_ERR_SHAPE;
+    if (!aligned16(x) || !aligned16(y) || (reinterpret_cast<uintptr_t>(h) & 3u) || !aligned16(plan) ||
+        !aligned16(workspace) || ld_x % 8 || ld_a % 8 || ld_y % 8)
+        return LORA_ERR_ALIGN;
+    if (plan_bytes < lora_sgmv_plan_bytes(M) || ws_bytes < workspace_bytes(M, r_max, split_k))
+        return LORA_ERR_WORKSPACE;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = launch_sgmv_partials(x, ld_x, A_ptrs, ld_a, ranks, n_adapters, plan, M, r_max, pl, workspace, s);
+    if (st != LORA_OK)
+        return st;
+    // Every column block of the expand evaluates its rows' tree again, so the
+    // tree goes into the expand only while column blocks x splits is small;
+    // otherwise the tree kernel writes h once (into the caller's h, or in
+    // place into workspace slice 0, each element read then written by one
+    // thread) and the expand reads it.  The bits are the same either way.
+    const int64_t nblocks = (N + kExpandCols - 1) / kExpandCols;
+    float* hh = h ? h : static_cast<float*>(workspace);
+    const int64_t ldh = h ? ld_h : r_max;
+    const bool h_readable = aligned16(hh) && ldh % 4 == 0;
+    const bool fuse = nblocks * split_k <= 256 || !h_readable;
+    const TreeParams t = sgmv_tree_params(workspace, M, r_max, fuse ? h : hh, fuse ? ld_h : ldh, token_adapter,
+                                          ranks, shrink_scales, n_adapters);
+    ExpandParams e{};
+    e.B_ptrs = B_ptrs;
+    e.ranks = ranks;
+    e.scales = expand_scales;
+    e.ids = token_adapter;
+    e.y = y;
+    e.ld_y = ld_y;
+    e.M = M;
+    e.N = N;
+    e.r = r_max;
+    e.r_max = r_max;
+    e.n_adapters = n_adapters;
+    e.scale = 1.0f;
+    if (fuse)
+        return launch_status(launch_sgmv_expand_combine(e, t, split_k, s));
+    st = launch_status(launch_splitk_tree(t, split_k, true, s));
+    if (st != LORA_OK)
+        return st;
+    e.h = hh;
+    e.ld_h = ldh;
+    return launch_status(launch_sgmv_expand(e, s));
 }
 
 int lora_sgmv_expand(const float* h, int64_t ld_h, const uint16_t* const* B_ptrs, const int32_t* ranks,

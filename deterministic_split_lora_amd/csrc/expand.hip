@@ -183,8 +183,8 @@ __global__ __launch_bounds__(256) void k_expand_combine(ExpandParams p, TreePara
 // adapter's rank and scale.  The grid is exact (no persistent loop), so the
 // hardware keeps as many y tiles in flight as occupancy allows.
 template <int KS>
-__device__ __forceinline__ void sgmv_pass(const ExpandParams& p, const ExpandLane& L, const float* hrows, int a,
-                                          const u16x8 (&yv)[2])
+__device__ __forceinline__ void sgmv_pass(const ExpandParams& p, const ExpandLane& L, const float* hrows,
+                                          int64_t ld_hr, int a, const u16x8 (&yv)[2])
 {
     int ra = p.ranks[a];
     ra = ra < 0 ? 0 : (ra > p.r_max ? p.r_max : ra);
@@ -196,12 +196,84 @@ __device__ __forceinline__ void sgmv_pass(const ExpandParams& p, const ExpandLan
     if (ra > 32 || KS == 1) {
         bf16x8 bop[4][KS];
         expand_load<KS>(Lb, p.y, p.ld_y, p.N, p.B_ptrs[a], ld_b, ra, unused, bop);
-        expand_finish<KS>(L, p.y, p.ld_y, p.N, hrows, p.ld_h, ra, scale, yv, bop);
+        expand_finish<KS>(L, p.y, p.ld_y, p.N, hrows, ld_hr, ra, scale, yv, bop);
     } else {
         bf16x8 bop[4][1];
         expand_load<1>(Lb, p.y, p.ld_y, p.N, p.B_ptrs[a], ld_b, ra, unused, bop);
-        expand_finish<1>(L, p.y, p.ld_y, p.N, hrows, p.ld_h, ra, scale, yv, bop);
+        expand_finish<1>(L, p.y, p.ld_y, p.N, hrows, ld_hr, ra, scale, yv, bop);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Multi-adapter combine: h of one token and rank column evaluated from the
+// Split-K workspace exactly as the second pass of lora_sgmv_shrink does it
+// (zero for tokens without an adapter and for columns from the adapter's rank
+// on; otherwise the fixed pairwise tree over the S slices, then one multiply
+// by the adapter's shrink scale).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float splits_tree(const float* w, int64_t stride, int split_k)
+{
+    float v[16];
+    switch (split_k) {
+    case 1: return w[0];
+    case 2:
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            v[s] = w[s * stride];
+        return pairwise_tree<2>(v);
+    case 4:
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            v[s] = w[s * stride];
+        return pairwise_tree<4>(v);
+    case 8:
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            v[s] = w[s * stride];
+        return pairwise_tree<8>(v);
+    default:
+#pragma unroll
+        for (int s = 0; s < 16; ++s)
+            v[s] = w[s * stride];
+        return pairwise_tree<16>(v);
+    }
+}
+
+__device__ __forceinline__ float sgmv_h_value(const TreeParams& c, int64_t row, int col, int split_k)
+{
+    const int a = c.ids[row];
+    if (a < 0 || a >= c.n_adapters)
+        return 0.0f;
+    int ra = c.ranks[a];
+    ra = ra < 0 ? 0 : (ra > c.ncols ? c.ncols : ra);
+    if (col >= ra)
+        return 0.0f;
+    const float scale = c.scales ? c.scales[a] : 1.0f;
+    return __fmul_rn(splits_tree(c.ws + row * c.ldw + col, c.split_stride, split_k), scale);
+}
+
+// h_stage with the tile's h computed from the workspace (and written to c.h
+// when write_h).
+__device__ __forceinline__ void h_stage_tree(const HStageSlot& s, const TreeParams& c, int64_t row0, int nrows,
+                                             int r, int split_k, bool write_h, uint16_t* tile)
+{
+    if (!s.on)
+        return;
+    float f[4] = {0.f, 0.f, 0.f, 0.f};
+    if (s.row < nrows) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (s.col + e < r) {
+                f[e] = sgmv_h_value(c, row0 + s.row, s.col + e, split_k);
+                if (write_h)
+                    c.h[(row0 + s.row) * c.ld_h + s.col + e] = f[e];
+            }
+        }
+    }
+    uint16_t* d = tile + s.row * kHbStride + s.col;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+        d[e] = f32_to_bf16_bits(f[e]);
 }
 
 // Multi-adapter, large M: as k_expand_rows, the workgroup walking R tiles of
@@ -211,8 +283,10 @@ __device__ __forceinline__ void sgmv_pass(const ExpandParams& p, const ExpandLan
 // contiguous); the staged h tile holds r_max columns and every pass masks it
 // to its adapter's rank.  y is read for every token of a tile but written only
 // for tokens with an adapter.
-template <int KS>
-__global__ __launch_bounds__(256) void k_sgmv_expand_rows(ExpandParams p, int R)
+// COMBINE: h comes from the Split-K workspace (sgmv_h_value), the first
+// column block also writes it out.
+template <int KS, bool COMBINE>
+__global__ __launch_bounds__(256) void k_sgmv_expand_rows(ExpandParams p, TreeParams c, int R, int split_k)
 {
     __shared__ __align__(16) uint16_t hs[2][kRowBlock * kHbStride];
     const uint32_t nblocks = (uint32_t)((p.N + kExpandCols - 1) / kExpandCols);
@@ -226,10 +300,17 @@ __global__ __launch_bounds__(256) void k_sgmv_expand_rows(ExpandParams p, int R)
         int a = X.row_ok ? p.ids[X.row] : -1;
         return (a < 0 || a >= p.n_adapters) ? -1 : a;
     };
+    const bool write_h = COMBINE && c.h != nullptr && col0 == 0;
+    auto stage = [&](int64_t r0, uint16_t* tile) {
+        if constexpr (COMBINE)
+            h_stage_tree(slot, c, r0, tile_rows(p.M, r0), p.r_max, split_k, write_h, tile);
+        else
+            h_stage(slot, p.h, p.ld_h, r0, tile_rows(p.M, r0), p.r_max, tile);
+    };
     int id = token_id(L);
     u16x8 yv[2];
     expand_load_y(L, p.y, p.ld_y, p.N, yv);
-    h_stage(slot, p.h, p.ld_h, row_base, tile_rows(p.M, row_base), p.r_max, hs[0]);
+    stage(row_base, hs[0]);
     int cur = -1;                        // adapter whose B operands this wave holds
     int ra = 0;
     float scale = 1.0f;
@@ -244,7 +325,7 @@ __global__ __launch_bounds__(256) void k_sgmv_expand_rows(ExpandParams p, int R)
             Ln = expand_lane(r1, tile_rows(p.M, r1), col0);
             idn = token_id(Ln);
             expand_load_y(Ln, p.y, p.ld_y, p.N, yn);
-            h_stage(slot, p.h, p.ld_h, r1, tile_rows(p.M, r1), p.r_max, hs[(i + 1) & 1]);
+            stage(r1, hs[(i + 1) & 1]);
         }
         if (L.n_base < p.N) {
             bool done = !(L.row_ok && id >= 0);
@@ -287,13 +368,15 @@ __global__ __launch_bounds__(256) void k_sgmv_expand_rows(ExpandParams p, int R)
 }
 
 // KS: matrix-core steps the kernel is built for (1: r_max <= 32, 2: r_max <= 64).
-template <int KS>
-__global__ __launch_bounds__(256) void k_sgmv_expand(ExpandParams p)
+// COMBINE: the block's h rows are evaluated from the Split-K workspace into
+// LDS first (the first column block also writes them out).
+template <int KS, bool COMBINE>
+__global__ __launch_bounds__(256) void k_sgmv_expand(ExpandParams p, TreeParams c, int split_k)
 {
+    __shared__ __align__(16) float hs[COMBINE ? kRowBlock * kHTileStride : 1];
     const ExpandItem q = expand_item(p.M, p.N);
     ExpandLane L = expand_lane(q.row0, q.nrows, q.cb * kExpandCols);
-    if (L.n_base >= p.N)
-        return;                                      // per wave: no workgroup barrier here
+    const bool active = L.n_base < p.N;              // per wave
     int id = -1;
     if (L.row_ok) {
         id = p.ids[L.row];
@@ -301,14 +384,29 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(ExpandParams p)
     }
     ExpandLane Ly = L;
     Ly.row_ok = L.row_ok && id >= 0;
-    u16x8 yv[2];
-    const int64_t n0 = L.n_base + 16 * L.g;
-    const uint16_t* yp = p.y + L.row * p.ld_y + n0;
-#pragma unroll
-    for (int half = 0; half < 2; ++half)
-        yv[half] = (Ly.row_ok && n0 + half * 8 < p.N) ? *reinterpret_cast<const u16x8*>(yp + half * 8)
-                                                     : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+    u16x8 yv[2] = {u16x8{0, 0, 0, 0, 0, 0, 0, 0}, u16x8{0, 0, 0, 0, 0, 0, 0, 0}};
+    if (active)
+        expand_load_y(Ly, p.y, p.ld_y, p.N, yv);
     const float* hrows = p.h + q.row0 * p.ld_h;
+    int64_t ld_hr = p.ld_h;
+    if constexpr (COMBINE) {
+        const bool write_h = c.h != nullptr && q.cb == 0;
+        for (int e = threadIdx.x; e < kRowBlock * p.r_max; e += 256) {
+            const int row = e / p.r_max;
+            const int col = e - row * p.r_max;
+            if (row < q.nrows) {
+                const float v = sgmv_h_value(c, q.row0 + row, col, split_k);
+                hs[row * kHTileStride + col] = v;
+                if (write_h)
+                    c.h[(q.row0 + row) * c.ld_h + col] = v;
+            }
+        }
+        __syncthreads();
+        hrows = hs;
+        ld_hr = kHTileStride;
+    }
+    if (!active)
+        return;
     bool done = !Ly.row_ok;
     for (;;) {
         const uint64_t pending = __ballot(!done);
@@ -318,7 +416,7 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(ExpandParams p)
         const bool mine = !done && id == a;
         ExpandLane La = L;
         La.row_ok = mine;
-        sgmv_pass<KS>(p, La, hrows, a, yv);
+        sgmv_pass<KS>(p, La, hrows, ld_hr, a, yv);
         done = done || mine;
     }
 }
@@ -398,22 +496,34 @@ hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int
                     : launch_expand_combine_ks<1>(p, c, split_k, grid, st);
 }
 
-hipError_t launch_sgmv_expand(const ExpandParams& p, hipStream_t st)
+template <bool COMBINE>
+void launch_sgmv_expand_t(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st)
 {
     const int R = expand_tiles_per_wg(p.M, p.N);
     if (R > 1) {
         const dim3 grid = expand_rows_grid(p.M, p.N, R);
         if (p.r_max > 32)
-            hipLaunchKernelGGL(k_sgmv_expand_rows<2>, grid, dim3(256), 0, st, p, R);
+            hipLaunchKernelGGL((k_sgmv_expand_rows<2, COMBINE>), grid, dim3(256), 0, st, p, c, R, split_k);
         else
-            hipLaunchKernelGGL(k_sgmv_expand_rows<1>, grid, dim3(256), 0, st, p, R);
-        return hipGetLastError();
+            hipLaunchKernelGGL((k_sgmv_expand_rows<1, COMBINE>), grid, dim3(256), 0, st, p, c, R, split_k);
+        return;
     }
     const dim3 grid = expand_grid(p.M, p.N);
     if (p.r_max > 32)
-        hipLaunchKernelGGL(k_sgmv_expand<2>, grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL((k_sgmv_expand<2, COMBINE>), grid, dim3(256), 0, st, p, c, split_k);
     else
-        hipLaunchKernelGGL(k_sgmv_expand<1>, grid, dim3(256), 0, st, p);
+        hipLaunchKernelGGL((k_sgmv_expand<1, COMBINE>), grid, dim3(256), 0, st, p, c, split_k);
+}
+
+hipError_t launch_sgmv_expand(const ExpandParams& p, hipStream_t st)
+{
+    launch_sgmv_expand_t<false>(p, TreeParams{}, 1, st);
+    return hipGetLastError();
+}
+
+hipError_t launch_sgmv_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st)
+{
+    launch_sgmv_expand_t<true>(p, c, split_k, st);
     return hipGetLastError();
 }
 

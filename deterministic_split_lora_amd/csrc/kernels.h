@@ -155,6 +155,7 @@ hipError_t launch_expand(const ExpandParams& p, hipStream_t st);
 hipError_t launch_expand_compensated(const ExpandParams& p, hipStream_t st);
 hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st);
 hipError_t launch_sgmv_expand(const ExpandParams& p, hipStream_t st);
+hipError_t launch_sgmv_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st);
 hipError_t launch_shrink_expand_fused(const FusedParams& p, int split_k, int waves, hipStream_t st);
 hipError_t launch_shrink_expand_counted(const ShrinkParams& p, const ExpandParams& e, const TreeParams& c,
                                         const StreamParams& q, int waves, int group_tiles, hipStream_t st);

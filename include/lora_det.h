@@ -345,6 +345,30 @@ int lora_sgmv_shrink_counted(const uint16_t* x, int64_t ld_x, const uint16_t* co
                              int32_t* counters, size_t counter_bytes, void* stream);
 
 /*
+ * Multi-adapter shrink + expand: the partial kernel of lora_sgmv_shrink, then
+ * either (two launches) an expand that evaluates each token's h from the
+ * Split-K workspace (the same fixed tree and shrink_scales[a] multiply as
+ * lora_sgmv_shrink's second pass, zeros past the adapter's rank), writes it
+ * to h when h is not NULL and applies lora_sgmv_expand's update with
+ * expand_scales[a]; or (three launches, when ceil(N / 256) * split_k > 256,
+ * where every column block re-evaluating the tree would cost more than a
+ * launch) the tree kernel, then lora_sgmv_expand's kernel.  Without h the
+ * three-launch schedule keeps h in workspace slice 0 (when r_max % 4 == 0,
+ * else it takes the two-launch schedule).  Either way h and y are bit for bit
+ * those of lora_sgmv_shrink(scales = shrink_scales) followed by
+ * lora_sgmv_expand(scales = expand_scales); either scale array may be NULL
+ * (all 1).  Arguments and requirements as for those two calls; h is
+ * optional here (4-byte aligned, ld_h >= r_max when given); the workspace
+ * content is undefined afterwards.
+ */
+int lora_sgmv_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_ptrs, int64_t ld_a,
+                            const uint16_t* const* B_ptrs, const int32_t* ranks, const float* shrink_scales,
+                            const float* expand_scales, const int32_t* token_adapter, int32_t n_adapters,
+                            const void* plan, size_t plan_bytes, float* h, int64_t ld_h,
+                            uint16_t* y, int64_t ld_y, int64_t M, int64_t K, int64_t N, int32_t r_max,
+                            int32_t split_k, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Multi-adapter expand: per token i with an adapter (a = token_adapter[i] in
  * [0, n_adapters)), lora_expand with B_a, rank r_a and scale scales[a] (1 when
  * scales is NULL); rows of other tokens are neither read nor written.  One

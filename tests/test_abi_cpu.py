@@ -392,3 +392,33 @@ def test_shrink_expand_counted_rejects():
     assert call(cb=cbytes - 1) == B.LORA_ERR_WORKSPACE
     assert call(M=0, x=None, ws=None, cnt=None) == B.LORA_OK
     assert call(N=0, ws=None, cnt=None) == B.LORA_OK
+
+
+def test_sgmv_shrink_expand_rejects():
+    L = dsl.lib()
+    pb = dsl.lora_sgmv_plan_bytes(64)
+    wsb = dsl.lora_sgmv_workspace_bytes(64, 64, 8)
+
+    def call(**kw):
+        a = dict(x=FAKE, ld_x=4096, Ap=FAKE, ld_a=4096, Bp=FAKE, ranks=FAKE, ss=None, es=None, ids=FAKE, n=4,
+                 plan=FAKE, pb=pb, h=None, ld_h=0, y=FAKE, ld_y=6144, M=64, K=4096, N=6144, r_max=64, S=8, ws=FAKE,
+                 wsb=wsb)
+        a.update(kw)
+        return L.lora_sgmv_shrink_expand(a["x"], a["ld_x"], a["Ap"], a["ld_a"], a["Bp"], a["ranks"], a["ss"], a["es"],
+                                         a["ids"], a["n"], a["plan"], a["pb"], a["h"], a["ld_h"], a["y"], a["ld_y"],
+                                         a["M"], a["K"], a["N"], a["r_max"], a["S"], a["ws"], a["wsb"], None)
+    assert call(x=None) == B.LORA_ERR_NULL
+    assert call(Bp=None) == B.LORA_ERR_NULL
+    assert call(ids=None) == B.LORA_ERR_NULL
+    assert call(ws=None) == B.LORA_ERR_NULL
+    assert call(n=0) == B.LORA_ERR_SHAPE
+    assert call(S=3) == B.LORA_ERR_UNSUPPORTED
+    assert call(r_max=65) == B.LORA_ERR_UNSUPPORTED
+    assert call(N=6140, ld_y=6144) == B.LORA_ERR_UNSUPPORTED
+    assert call(ld_y=4096) == B.LORA_ERR_SHAPE
+    assert call(h=FAKE, ld_h=32) == B.LORA_ERR_SHAPE
+    assert call(h=FAKE + 2, ld_h=64) == B.LORA_ERR_ALIGN
+    assert call(y=FAKE_MIS) == B.LORA_ERR_ALIGN
+    assert call(pb=pb - 4) == B.LORA_ERR_WORKSPACE
+    assert call(wsb=wsb - 4) == B.LORA_ERR_WORKSPACE
+    assert call(M=0, x=None, ws=None) == B.LORA_OK

@@ -1150,3 +1150,75 @@ def test_expand_compensated_parity(M, r, N):
     match_c = float(np.mean(gc == want))
     match_p = float(np.mean(gp == want))
     assert match_c > 0.97 and match_c > match_p, (match_c, match_p)
+
+
+# ---------------------------------------------------------------------------
+# multi-adapter shrink + expand in two launches (expand reads the workspace)
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("case", ["qkv", "mixed", "decode", "large", "large_s16"])
+def test_sgmv_shrink_expand_bitwise(case):
+    """lora_sgmv_shrink_expand gives the h and y bits of lora_sgmv_shrink
+    (with the shrink scales) followed by lora_sgmv_expand (with the expand
+    scales): tokens without an adapter keep y, ranks below r_max and not a
+    multiple of 8 included; the large cases walk several tiles per expand
+    workgroup, the last one takes the three-launch schedule (with h, and with
+    h kept in the workspace).  Sampled rows agree with the oracle."""
+    t = torch()
+    if case == "qkv":
+        c = sgmv_case(512, 4096, 6144, [64, 64, 64, 64], 1, 64, 8, seed=11, tag="se_q")
+    elif case == "mixed":
+        rng = np.random.default_rng(12)
+        ids = rng.choice([-1, 0, 1, 2, 3, 7], 333).astype(np.int32)
+        ids[40:140] = 1
+        c = sgmv_case(333, 2048, 520, [5, 16, 37, 64], 0, 0, 16, seed=12, tag="se_m", ids=ids)
+    elif case == "decode":
+        c = sgmv_case(24, 8192, 1024, [64, 8, 32, 16] * 6, 0, 0, 8, seed=13, tag="se_d",
+                      ids=np.arange(24, dtype=np.int32))
+    elif case == "large":
+        c = sgmv_case(4100, 1024, 4104, [8, 16, 32, 64, 5, 40], 16, 300, 4, seed=14, tag="se_l")
+    else:                                          # 17 column blocks x 16 splits: tree kernel, then expand
+        c = sgmv_case(4100, 1024, 4104, [8, 16, 32, 64, 5, 40], 16, 300, 16, seed=15, tag="se_l16")
+    _say(f"sgmv shrink+expand {case} M={c.M} N={c.N}")
+    n = len(c.ranks)
+    As = [bf16_to_gpu(a) for a in c.As]
+    Bs = []
+    for b in c.Bs:
+        r = b.shape[1]
+        bp = np.zeros((c.N, (r + 7) // 8 * 8), np.uint16)
+        bp[:, :r] = b
+        Bs.append(bf16_to_gpu(bp))
+    Ap = t.tensor([a.data_ptr() for a in As], dtype=t.int64, device="cuda")
+    Bp = t.tensor([b.data_ptr() for b in Bs], dtype=t.int64, device="cuda")
+    ranks = t.from_numpy(c.ranks).cuda()
+    sh = np.array([0.5, 2.0, 1.0, 0.25] * ((n + 3) // 4), np.float32)[:n]
+    ex = np.array([2.0, 1.0, 0.5, 3.0] * ((n + 3) // 4), np.float32)[:n]
+    shg, exg = t.from_numpy(sh).cuda(), t.from_numpy(ex).cuda()
+    idg, plan = _build_plan(c.ids, n)
+    xg = bf16_to_gpu(c.x)
+    ws = workspace(dsl.lora_sgmv_workspace_bytes(c.M, c.r_max, c.split_k))
+    h1 = t.full((c.M, c.r_max), float("nan"), dtype=t.float32, device="cuda")
+    dsl.lora_sgmv_shrink(xg, Ap, c.K, ranks, shg, idg, n, plan, h1, c.r_max, c.split_k, ws)
+    y1 = bf16_to_gpu(c.y)
+    dsl.lora_sgmv_expand(h1, Bp, ranks, exg, idg, n, y1, c.r_max)
+    ws2 = workspace(dsl.lora_sgmv_workspace_bytes(c.M, c.r_max, c.split_k))
+    h2 = t.full((c.M, c.r_max), float("nan"), dtype=t.float32, device="cuda")
+    y2 = bf16_to_gpu(c.y)
+    dsl.lora_sgmv_shrink_expand(xg, Ap, c.K, Bp, ranks, shg, exg, idg, n, plan, y2, c.r_max, c.split_k, ws2, h=h2)
+    y3 = bf16_to_gpu(c.y)
+    dsl.lora_sgmv_shrink_expand(xg, Ap, c.K, Bp, ranks, shg, exg, idg, n, plan, y3, c.r_max, c.split_k, ws2)
+    t.cuda.synchronize()
+    assert np.array_equal(f32_bits(h1), f32_bits(h2))
+    g1 = bf16_from_gpu(y1)
+    assert np.array_equal(g1, bf16_from_gpu(y2)) and np.array_equal(g1, bf16_from_gpu(y3))
+    hh = h2.cpu().numpy()
+    rng = np.random.default_rng(5)
+    for i in sorted(rng.choice(c.M, min(12, c.M), replace=False).tolist()):
+        a = int(c.ids[i])
+        if a < 0 or a >= n:
+            assert np.all(hh[i] == 0.0) and np.array_equal(g1[i], c.y[i])
+            continue
+        r = int(c.ranks[a])
+        check_shrink(hh[i:i + 1, :r], c.x[i:i + 1], c.As[a], float(sh[a]),
+                     dsl.lora_shrink_plan(c.K, r, c.split_k), f"{case} h row {i}")
+        yo, e, ab = oracle.expand(hh[i:i + 1, :r], c.Bs[a], c.y[i:i + 1], float(ex[a]))
+        check_expand(g1[i:i + 1], yo, e, ab, c.y[i:i + 1], f"{case} y row {i}")
