@@ -564,8 +564,29 @@ int lora_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64
     st = lora_shrink_partials(x, ld_x, A, ld_a, M, K, r, split_k, workspace, ws_bytes, stream);
     if (st != LORA_OK)
         return st;
-    return lora_expand_combine(workspace, ws_bytes, split_k, shrink_scale, B, ld_b, h, ld_h, y, ld_y, M, r, N,
-                               expand_scale, stream);
+    // As in lora_sgmv_shrink_expand: the tree goes into the expand only while
+    // column blocks x splits is small (every column block evaluates its rows'
+    // tree again); otherwise the tree kernel writes h once - into the caller's
+    // h, or in place into workspace slice 0 - and the expand reads it.
+    const int64_t nblocks = (N + kExpandCols - 1) / kExpandCols;
+    float* hh = h ? h : static_cast<float*>(workspace);
+    const int64_t ldh = h ? ld_h : r;
+    if (nblocks * split_k <= 256 || !aligned16(hh) || ldh % 4 != 0)
+        return lora_expand_combine(workspace, ws_bytes, split_k, shrink_scale, B, ld_b, h, ld_h, y, ld_y, M, r, N,
+                                   expand_scale, stream);
+    TreeParams t{};
+    t.ws = static_cast<const float*>(workspace);
+    t.split_stride = M * r;
+    t.ldw = r;
+    t.h = hh;
+    t.ld_h = ldh;
+    t.M = M;
+    t.ncols = r;
+    t.scale = shrink_scale;
+    st = launch_status(launch_splitk_tree(t, split_k, false, static_cast<hipStream_t>(stream)));
+    if (st != LORA_OK)
+        return st;
+    return lora_expand(hh, ldh, B, ld_b, y, ld_y, M, r, N, expand_scale, stream);
 }
 
 size_t lora_shrink_expand_counter_bytes(int64_t M)

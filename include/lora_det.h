@@ -206,8 +206,12 @@ int lora_shrink_splitk_counted(const uint16_t* x, int64_t ld_x, const uint16_t* 
  * slices of M x r floats.
  *
  * lora_shrink_expand: h and y bit for bit those of lora_shrink_splitk followed
- * by lora_expand, in fewer launches: either the two calls above in order on
- * one stream, or (small M) the single launch of lora_shrink_expand_fused.
+ * by lora_expand, in fewer launches: the two calls above in order on one
+ * stream; or (small M and A) the single launch of lora_shrink_expand_fused; or,
+ * when ceil(N / 256) * split_k > 256 (every column block re-evaluating the
+ * tree would cost more than a launch), the partials, the tree kernel and the
+ * expand kernel - without h, h is then kept in workspace slice 0 (when
+ * r % 4 == 0).  The workspace content is undefined afterwards.
  *
  * workspace: >= lora_shrink_expand_workspace_bytes(M, r, split_k) bytes =
  * split_k * M * r * 4, also for split_k == 1.  Requirements: those of

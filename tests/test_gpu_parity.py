@@ -550,7 +550,8 @@ def test_sgmv_prefill_full_size_sampled():
                                        (256, 4096, 16, 4096, 8), (1, 32, 16, 256, 1), (20, 1024, 64, 8, 16),
                                        (37, 8192, 64, 1032, 16), (5, 1024, 8, 512, 1), (70, 2048, 40, 264, 4),
                                        (3, 3072, 1, 8, 2), (64, 14336, 32, 4096, 8), (65, 4096, 24, 1000, 8),
-                                       (9, 1024, 33, 520, 4), (2, 16384, 64, 512, 16)])
+                                       (9, 1024, 33, 520, 4), (2, 16384, 64, 512, 16),
+                                       (300, 2048, 64, 8200, 16), (40, 1024, 24, 16384, 8)])
 def test_shrink_expand_fused_bitwise(M, K, r, N, S):
     """Every schedule of the deterministic shrink + expand - lora_shrink_splitk
     then lora_expand (three launches), lora_shrink_partials then
