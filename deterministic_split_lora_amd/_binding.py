@@ -56,6 +56,9 @@ _i32 = ctypes.c_int32
 _f32 = ctypes.c_float
 _sz = ctypes.c_size_t
 
+# LORA_DET_ABI_VERSION of include/lora_det.h that these signatures follow.
+ABI_VERSION = 2
+
 
 def lib():
     """The loaded library; raises ImportError when it has not been built."""
@@ -67,6 +70,9 @@ def lib():
         L = ctypes.CDLL(LIBRARY_PATH)
         L.lora_abi_version.restype = ctypes.c_int
         L.lora_abi_version.argtypes = []
+        if L.lora_abi_version() != ABI_VERSION:
+            raise ImportError(f"{LIBRARY_PATH} has ABI version {L.lora_abi_version()}, the binding "
+                              f"expects {ABI_VERSION}: rebuild it")
         L.lora_status_str.restype = ctypes.c_char_p
         L.lora_status_str.argtypes = [ctypes.c_int]
         L.lora_shrink_plan.restype = ctypes.c_int

@@ -169,12 +169,12 @@ __device__ __forceinline__ void expand_load(const ExpandLane& L, const uint16_t*
     expand_load_b<KS>(L, N, B, ld_b, r, bop);
 }
 
-// The matrix-core steps and the y update, given this lane's bf16(h) operand
-// (its token's h[j], j = 32 ks + 8 g .. + 7, zeros from r on).
+// The matrix-core steps and the updated y values of this lane's 16 columns,
+// given its bf16(h) operand (its token's h[j], j = 32 ks + 8 g .. + 7, zeros
+// from r on):  o = bf16(fma(scale, sum_j bf16(h[j]) B[n][j], y)).
 template <int KS>
-__device__ __forceinline__ void expand_mma_store(const ExpandLane& L, uint16_t* y, int64_t ld_y, int64_t N,
-                                                 const bf16x8 (&hb)[KS], float scale, const u16x8 (&yv)[2],
-                                                 const bf16x8 (&bop)[4][KS])
+__device__ __forceinline__ void expand_mma(const bf16x8 (&hb)[KS], float scale, const u16x8 (&yv)[2],
+                                           const bf16x8 (&bop)[4][KS], u16x8 (&o)[2])
 {
     f32x4 acc[4];
 #pragma unroll
@@ -184,22 +184,31 @@ __device__ __forceinline__ void expand_mma_store(const ExpandLane& L, uint16_t* 
         for (int ks = 0; ks < KS; ++ks)
             acc[t] = mfma_16x16x32(bop[t][ks], hb[ks], acc[t]);
     }
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int idx = half * 8 + e;
+            o[half][e] = f32_to_bf16_bits(__builtin_fmaf(scale, acc[idx >> 2][idx & 3], bf16_bits_to_f32(yv[half][e])));
+        }
+}
+
+// expand_mma, then the lane's 16 y values stored straight to y.
+template <int KS>
+__device__ __forceinline__ void expand_mma_store(const ExpandLane& L, uint16_t* y, int64_t ld_y, int64_t N,
+                                                 const bf16x8 (&hb)[KS], float scale, const u16x8 (&yv)[2],
+                                                 const bf16x8 (&bop)[4][KS])
+{
+    u16x8 o[2];
+    expand_mma<KS>(hb, scale, yv, bop, o);
     if (!L.row_ok)
         return;
     const int64_t n0 = L.n_base + 16 * L.g;
     uint16_t* yp = y + L.row * ld_y + n0;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        if (n0 + half * 8 < N) {
-            u16x8 o;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int idx = half * 8 + e;
-                o[e] = f32_to_bf16_bits(__builtin_fmaf(scale, acc[idx >> 2][idx & 3], bf16_bits_to_f32(yv[half][e])));
-            }
-            *reinterpret_cast<u16x8*>(yp + half * 8) = o;
-        }
-    }
+    for (int half = 0; half < 2; ++half)
+        if (n0 + half * 8 < N)
+            *reinterpret_cast<u16x8*>(yp + half * 8) = o[half];
 }
 
 // bf16(h) of the block's token rows (hrows: row 0 of the block, stride ld_hr),
@@ -303,19 +312,25 @@ __device__ __forceinline__ HStageSlot h_stage_slot(int r)
     return s;
 }
 
-__device__ __forceinline__ void h_stage(const HStageSlot& s, const float* h, int64_t ld_h, int64_t row0, int nrows,
-                                        int r, uint16_t* tile)
+// The slot's 4 h values (zeros past r and for rows outside the tile) ...
+__device__ __forceinline__ void h_load(const HStageSlot& s, const float* h, int64_t ld_h, int64_t row0, int nrows,
+                                       int r, float (&f)[4])
+{
+    f[0] = f[1] = f[2] = f[3] = 0.f;
+    if (!s.on || s.row >= nrows || s.col >= r)
+        return;
+    const float4 v = *reinterpret_cast<const float4*>(h + (row0 + s.row) * ld_h + s.col);
+    f[0] = v.x;
+    f[1] = s.col + 1 < r ? v.y : 0.f;
+    f[2] = s.col + 2 < r ? v.z : 0.f;
+    f[3] = s.col + 3 < r ? v.w : 0.f;
+}
+
+// ... and their bf16 roundings put into the LDS tile.
+__device__ __forceinline__ void h_put(const HStageSlot& s, const float (&f)[4], uint16_t* tile)
 {
     if (!s.on)
         return;
-    float f[4] = {0.f, 0.f, 0.f, 0.f};
-    if (s.row < nrows && s.col < r) {
-        const float4 v = *reinterpret_cast<const float4*>(h + (row0 + s.row) * ld_h + s.col);
-        f[0] = v.x;
-        f[1] = s.col + 1 < r ? v.y : 0.f;
-        f[2] = s.col + 2 < r ? v.z : 0.f;
-        f[3] = s.col + 3 < r ? v.w : 0.f;
-    }
     uint16_t* d = tile + s.row * kHbStride + s.col;
 #pragma unroll
     for (int e = 0; e < 4; ++e)

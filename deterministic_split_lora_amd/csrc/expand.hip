@@ -78,52 +78,142 @@ __global__ __launch_bounds__(256) void k_expand_comp(ExpandParams p)
 
 // Single adapter, large M: a workgroup walks R consecutive 16-token tiles of
 // one 256-column block.  Its B operands are loaded once and stay in
-// registers; each tile's h rows are converted to bf16 once into LDS (double
-// buffered, one barrier per tile) instead of once per wave; the next tile's y
-// is loaded before the current one is finished.  Per element this is the
-// arithmetic of k_expand (same operands, steps and epilogue code); it only
-// reads B and h fewer times, which is what limits the one-tile-per-workgroup
-// kernel once M x N is large (its B and h loads keep the address units busy).
+// registers; each tile's h rows are converted to bf16 once into LDS instead
+// of once per wave.  y moves through LDS: it is read and written row by row
+// (thread t moves the 16-byte chunk t % 32 of rows t / 32 and t / 32 + 8, so
+// a wave covers two whole 512-byte row segments per access) and each lane
+// takes its 16 matrix-core-layout values from the LDS tile and puts its
+// results back in their place.  Loads run one tile ahead, stores one tile
+// behind: while tile i is computed, tile i + 1's y and h are in flight and
+// tile i - 1 is being written out, with one barrier per tile (y and h tiles
+// double buffered).  Per element this is the arithmetic of k_expand (same
+// operands, steps and epilogue code); only the data movement differs.
 __device__ __forceinline__ int tile_rows(int64_t M, int64_t row0)
 {
     const int64_t left = M - row0;
     return left < kRowBlock ? (int)left : kRowBlock;
 }
 
+constexpr int kYStride = kExpandCols + 8;     // bf16 per LDS row of a y tile (528 bytes)
+
+struct YChunk {
+    int row;                                  // first of the thread's rows; the other is row + 8
+    int col;                                  // first of its 8 columns
+};
+
+__device__ __forceinline__ YChunk y_chunk()
+{
+    return YChunk{(int)threadIdx.x >> 5, ((int)threadIdx.x & 31) * 8};
+}
+
+// ok bit e: the thread's row e (row + 8 e) is read / written.
+__device__ __forceinline__ void y_chunk_load(const YChunk& c, const uint16_t* y, int64_t ld_y, int64_t row0,
+                                             int64_t col0, unsigned ok, u16x8 (&g)[2])
+{
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+        g[e] = (ok >> e & 1u) ? *reinterpret_cast<const u16x8*>(y + (row0 + c.row + 8 * e) * ld_y + col0 + c.col)
+                              : u16x8{0, 0, 0, 0, 0, 0, 0, 0};
+}
+
+__device__ __forceinline__ void y_chunk_put(const YChunk& c, const u16x8 (&g)[2], uint16_t* tile)
+{
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+        *reinterpret_cast<u16x8*>(tile + (c.row + 8 * e) * kYStride + c.col) = g[e];
+}
+
+__device__ __forceinline__ void y_chunk_store(const YChunk& c, const uint16_t* tile, uint16_t* y, int64_t ld_y,
+                                              int64_t row0, int64_t col0, unsigned ok)
+{
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+        if (ok >> e & 1u)
+            *reinterpret_cast<u16x8*>(y + (row0 + c.row + 8 * e) * ld_y + col0 + c.col) =
+                *reinterpret_cast<const u16x8*>(tile + (c.row + 8 * e) * kYStride + c.col);
+}
+
+// Rows of the thread's chunk inside a tile of nrows rows (and N, when the
+// chunk's columns are inside N).
+__device__ __forceinline__ unsigned y_chunk_rows(const YChunk& c, int nrows, bool col_ok)
+{
+    return col_ok ? (unsigned)(c.row < nrows) | (unsigned)(c.row + 8 < nrows) << 1 : 0u;
+}
+
+// This lane's 16 values in the LDS y tile: row li, columns 64 wave + 16 g ..
+__device__ __forceinline__ uint16_t* y_lane(const ExpandLane& L, uint16_t* tile)
+{
+    return tile + L.li * kYStride + (int)(threadIdx.x >> 6) * 64 + 16 * L.g;
+}
+
+// The expand of one lane's 16 values held in the LDS y tile, written back in place.
+template <int KS>
+__device__ __forceinline__ void expand_in_tile(uint16_t* yl, const bf16x8 (&hb)[KS], float scale,
+                                               const bf16x8 (&bop)[4][KS])
+{
+    u16x8 yv[2], o[2];
+    yv[0] = *reinterpret_cast<const u16x8*>(yl);
+    yv[1] = *reinterpret_cast<const u16x8*>(yl + 8);
+    expand_mma<KS>(hb, scale, yv, bop, o);
+    *reinterpret_cast<u16x8*>(yl) = o[0];
+    *reinterpret_cast<u16x8*>(yl + 8) = o[1];
+}
+
 template <int KS>
 __global__ __launch_bounds__(256) void k_expand_rows(ExpandParams p, int R)
 {
     __shared__ __align__(16) uint16_t hs[2][kRowBlock * kHbStride];
+    __shared__ __align__(16) uint16_t ys[2][kRowBlock * kYStride];
     const uint32_t nblocks = (uint32_t)((p.N + kExpandCols - 1) / kExpandCols);
     const int64_t col0 = (int64_t)(blockIdx.x % nblocks) * kExpandCols;
     const int64_t row_base = (int64_t)(blockIdx.x / nblocks) * kRowBlock * R;
     const int64_t left = (p.M - row_base + kRowBlock - 1) / kRowBlock;
     const int tiles = left < R ? (int)left : R;
     const HStageSlot slot = h_stage_slot(p.r);
-    ExpandLane L = expand_lane(row_base, tile_rows(p.M, row_base), col0);
-    u16x8 yv[2];
+    const YChunk yc = y_chunk();
+    const bool col_ok = col0 + yc.col < p.N;
+    const unsigned full = y_chunk_rows(yc, kRowBlock, col_ok);
+    ExpandLane L = expand_lane(row_base, kRowBlock, col0);
+    const bool active = L.n_base < p.N;
     bf16x8 bop[4][KS];
-    expand_load<KS>(L, p.y, p.ld_y, p.N, p.B, p.ld_b, p.r, yv, bop);
-    h_stage(slot, p.h, p.ld_h, row_base, tile_rows(p.M, row_base), p.r, hs[0]);
+    expand_load_b<KS>(L, p.N, p.B, p.ld_b, p.r, bop);
+    u16x8 g[2];
+    float f[4];
+    int nr = tile_rows(p.M, row_base);
+    unsigned ok = y_chunk_rows(yc, nr, col_ok);
+    y_chunk_load(yc, p.y, p.ld_y, row_base, col0, ok, g);
+    h_load(slot, p.h, p.ld_h, row_base, nr, p.r, f);
+    y_chunk_put(yc, g, ys[0]);
+    h_put(slot, f, hs[0]);
+    __syncthreads();
     for (int i = 0; i < tiles; ++i) {
-        __syncthreads();                 // tile i staged; the other buffer is free
-        ExpandLane Ln = L;
-        u16x8 yn[2] = {u16x8{0, 0, 0, 0, 0, 0, 0, 0}, u16x8{0, 0, 0, 0, 0, 0, 0, 0}};
-        if (i + 1 < tiles) {
-            const int64_t r1 = row_base + (int64_t)kRowBlock * (i + 1);
-            Ln = expand_lane(r1, tile_rows(p.M, r1), col0);
-            expand_load_y(Ln, p.y, p.ld_y, p.N, yn);
-            h_stage(slot, p.h, p.ld_h, r1, tile_rows(p.M, r1), p.r, hs[(i + 1) & 1]);
+        const int64_t row0 = row_base + (int64_t)kRowBlock * i;
+        const bool next = i + 1 < tiles;
+        const int nr1 = next ? tile_rows(p.M, row0 + kRowBlock) : 0;
+        const unsigned ok1 = y_chunk_rows(yc, nr1, col_ok);
+        if (next) {
+            y_chunk_load(yc, p.y, p.ld_y, row0 + kRowBlock, col0, ok1, g);
+            h_load(slot, p.h, p.ld_h, row0 + kRowBlock, nr1, p.r, f);
         }
-        if (L.n_base < p.N) {
+        if (i > 0)                                   // tile i - 1 is whole
+            y_chunk_store(yc, ys[(i - 1) & 1], p.y, p.ld_y, row0 - kRowBlock, col0, full);
+        if (active) {
+            L.row_ok = L.li < nr;
             bf16x8 hb[KS];
             hb_from_tile<KS>(L, hs[i & 1], p.r, hb);
-            expand_mma_store<KS>(L, p.y, p.ld_y, p.N, hb, p.scale, yv, bop);
+            expand_in_tile<KS>(y_lane(L, ys[i & 1]), hb, p.scale, bop);
         }
-        L = Ln;
-        yv[0] = yn[0];
-        yv[1] = yn[1];
+        if (next) {
+            y_chunk_put(yc, g, ys[(i + 1) & 1]);
+            h_put(slot, f, hs[(i + 1) & 1]);
+        }
+        __syncthreads();
+        if (next) {
+            nr = nr1;
+            ok = ok1;
+        }
     }
+    y_chunk_store(yc, ys[(tiles - 1) & 1], p.y, p.ld_y, row_base + (int64_t)kRowBlock * (tiles - 1), col0, ok);
 }
 
 // Fused: the fixed pairwise tree over the Split-K workspace for this row block
@@ -252,88 +342,106 @@ __device__ __forceinline__ float sgmv_h_value(const TreeParams& c, int64_t row, 
     return __fmul_rn(splits_tree(c.ws + row * c.ldw + col, c.split_stride, split_k), scale);
 }
 
-// h_stage with the tile's h computed from the workspace (and written to c.h
-// when write_h).
-__device__ __forceinline__ void h_stage_tree(const HStageSlot& s, const TreeParams& c, int64_t row0, int nrows,
-                                             int r, int split_k, bool write_h, uint16_t* tile)
+// The slot's 4 h values computed from the workspace (and written to c.h when
+// write_h), for h_put.
+__device__ __forceinline__ void h_tree(const HStageSlot& s, const TreeParams& c, int64_t row0, int nrows, int r,
+                                       int split_k, bool write_h, float (&f)[4])
 {
-    if (!s.on)
+    f[0] = f[1] = f[2] = f[3] = 0.f;
+    if (!s.on || s.row >= nrows)
         return;
-    float f[4] = {0.f, 0.f, 0.f, 0.f};
-    if (s.row < nrows) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (s.col + e < r) {
-                f[e] = sgmv_h_value(c, row0 + s.row, s.col + e, split_k);
-                if (write_h)
-                    c.h[(row0 + s.row) * c.ld_h + s.col + e] = f[e];
-            }
+    for (int e = 0; e < 4; ++e) {
+        if (s.col + e < r) {
+            f[e] = sgmv_h_value(c, row0 + s.row, s.col + e, split_k);
+            if (write_h)
+                c.h[(row0 + s.row) * c.ld_h + s.col + e] = f[e];
         }
     }
-    uint16_t* d = tile + s.row * kHbStride + s.col;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-        d[e] = f32_to_bf16_bits(f[e]);
 }
 
-// Multi-adapter, large M: as k_expand_rows, the workgroup walking R tiles of
-// one column block, with k_sgmv_expand's passes per distinct adapter.  Each
-// wave keeps the B operands of the last adapter it used and reloads them only
-// when a pass needs another one (tokens of one adapter are usually
-// contiguous); the staged h tile holds r_max columns and every pass masks it
-// to its adapter's rank.  y is read for every token of a tile but written only
+// Multi-adapter, large M: k_expand_rows' tile walk and y movement, with
+// k_sgmv_expand's passes per distinct adapter.  Each wave keeps the B
+// operands of the last adapter it used and reloads them only when a pass
+// needs another one (tokens of one adapter are usually contiguous); the
+// staged h tile holds r_max columns and every pass masks it to its adapter's
+// rank.  A lane's result goes back into the LDS y tile only in the pass of its
+// token's adapter; y rows are read for every token of a tile but written only
 // for tokens with an adapter.
 // COMBINE: h comes from the Split-K workspace (sgmv_h_value), the first
 // column block also writes it out.
+// (at most 128 VGPRs: four workgroups per CU)
 template <int KS, bool COMBINE>
-__global__ __launch_bounds__(256) void k_sgmv_expand_rows(ExpandParams p, TreeParams c, int R, int split_k)
+__global__ __launch_bounds__(256, 4) void k_sgmv_expand_rows(ExpandParams p, TreeParams c, int R, int split_k)
 {
     __shared__ __align__(16) uint16_t hs[2][kRowBlock * kHbStride];
+    __shared__ __align__(16) uint16_t ys[2][kRowBlock * kYStride];
     const uint32_t nblocks = (uint32_t)((p.N + kExpandCols - 1) / kExpandCols);
     const int64_t col0 = (int64_t)(blockIdx.x % nblocks) * kExpandCols;
     const int64_t row_base = (int64_t)(blockIdx.x / nblocks) * kRowBlock * R;
     const int64_t left = (p.M - row_base + kRowBlock - 1) / kRowBlock;
     const int tiles = left < R ? (int)left : R;
     const HStageSlot slot = h_stage_slot(p.r_max);
-    ExpandLane L = expand_lane(row_base, tile_rows(p.M, row_base), col0);
-    auto token_id = [&](const ExpandLane& X) {
-        int a = X.row_ok ? p.ids[X.row] : -1;
-        return (a < 0 || a >= p.n_adapters) ? -1 : a;
-    };
+    const YChunk yc = y_chunk();
+    const bool col_ok = col0 + yc.col < p.N;
+    ExpandLane L = expand_lane(row_base, kRowBlock, col0);
+    const bool active = L.n_base < p.N;
     const bool write_h = COMBINE && c.h != nullptr && col0 == 0;
-    auto stage = [&](int64_t r0, uint16_t* tile) {
-        if constexpr (COMBINE)
-            h_stage_tree(slot, c, r0, tile_rows(p.M, r0), p.r_max, split_k, write_h, tile);
-        else
-            h_stage(slot, p.h, p.ld_h, r0, tile_rows(p.M, r0), p.r_max, tile);
+    // raw adapter id of a row of the tile at r0 (-1 outside the tile)
+    auto raw_id = [&](int64_t r0, int nrows, int row) { return row < nrows ? p.ids[r0 + row] : -1; };
+    auto valid = [&](int a) { return a >= 0 && a < p.n_adapters; };
+    // the tile at r0: its y chunk rows, h slot and this lane's token id in flight
+    u16x8 g[2];
+    float f[4];
+    int ca[2];                                   // adapter ids of the chunk's rows
+    auto fetch = [&](int64_t r0, int nrows, int& lane_id) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+            ca[e] = col_ok ? raw_id(r0, nrows, yc.row + 8 * e) : -1;
+        lane_id = raw_id(r0, nrows, L.li);
+        y_chunk_load(yc, p.y, p.ld_y, r0, col0, y_chunk_rows(yc, nrows, col_ok), g);
+        if constexpr (!COMBINE)
+            h_load(slot, p.h, p.ld_h, r0, nrows, p.r_max, f);
     };
-    int id = token_id(L);
-    u16x8 yv[2];
-    expand_load_y(L, p.y, p.ld_y, p.N, yv);
-    stage(row_base, hs[0]);
-    int cur = -1;                        // adapter whose B operands this wave holds
+    // ... put into LDS buffer b; returns the chunk rows to be written back
+    auto put = [&](int64_t r0, int nrows, int b) {
+        if constexpr (COMBINE)
+            h_tree(slot, c, r0, nrows, p.r_max, split_k, write_h, f);
+        y_chunk_put(yc, g, ys[b]);
+        h_put(slot, f, hs[b]);
+        return (unsigned)valid(ca[0]) | (unsigned)valid(ca[1]) << 1;
+    };
+    int id;
+    int nr = tile_rows(p.M, row_base);
+    fetch(row_base, nr, id);
+    unsigned w_prev = 0;
+    unsigned w_cur = put(row_base, nr, 0);
+    __syncthreads();
+    int cur = -1;                                // adapter whose B operands this wave holds
     int ra = 0;
     float scale = 1.0f;
     bf16x8 bop[4][KS];
     for (int i = 0; i < tiles; ++i) {
-        __syncthreads();
-        ExpandLane Ln = L;
+        const int64_t row0 = row_base + (int64_t)kRowBlock * i;
+        const bool next = i + 1 < tiles;
+        const int nr1 = next ? tile_rows(p.M, row0 + kRowBlock) : 0;
         int idn = -1;
-        u16x8 yn[2] = {u16x8{0, 0, 0, 0, 0, 0, 0, 0}, u16x8{0, 0, 0, 0, 0, 0, 0, 0}};
-        if (i + 1 < tiles) {
-            const int64_t r1 = row_base + (int64_t)kRowBlock * (i + 1);
-            Ln = expand_lane(r1, tile_rows(p.M, r1), col0);
-            idn = token_id(Ln);
-            expand_load_y(Ln, p.y, p.ld_y, p.N, yn);
-            stage(r1, hs[(i + 1) & 1]);
-        }
-        if (L.n_base < p.N) {
-            bool done = !(L.row_ok && id >= 0);
+        if (next)
+            fetch(row0 + kRowBlock, nr1, idn);
+        if (i > 0)
+            y_chunk_store(yc, ys[(i - 1) & 1], p.y, p.ld_y, row0 - kRowBlock, col0, w_prev);
+        if (active) {
+            const int lid = valid(id) ? id : -1;
+            uint16_t* yl = y_lane(L, ys[i & 1]);
+            u16x8 yv[2];
+            yv[0] = *reinterpret_cast<const u16x8*>(yl);
+            yv[1] = *reinterpret_cast<const u16x8*>(yl + 8);
+            bool done = lid < 0;
             for (;;) {
                 const uint64_t pending = __ballot(!done);
                 if (pending == 0)
                     break;
-                const int a = __shfl(id, __builtin_ctzll(pending));     // wave-uniform
+                const int a = __shfl(lid, __builtin_ctzll(pending));    // wave-uniform
                 if (a != cur) {
                     cur = a;
                     ra = p.ranks[a];
@@ -341,13 +449,14 @@ __global__ __launch_bounds__(256) void k_sgmv_expand_rows(ExpandParams p, TreePa
                     scale = p.scales ? p.scales[a] : 1.0f;
                     expand_load_b<KS>(L, p.N, p.B_ptrs[a], (ra + 7) & ~7, ra, bop);
                 }
-                const bool mine = !done && id == a;
+                const bool mine = !done && lid == a;
                 ExpandLane La = L;
                 La.row_ok = mine;
+                u16x8 o[2];
                 if (KS == 2 && ra > 32) {
                     bf16x8 hb[KS];
                     hb_from_tile<KS>(La, hs[i & 1], ra, hb);
-                    expand_mma_store<KS>(La, p.y, p.ld_y, p.N, hb, scale, yv, bop);
+                    expand_mma<KS>(hb, scale, yv, bop, o);
                 } else {
                     bf16x8 hb[1];
                     bf16x8 b1[4][1];
@@ -355,16 +464,24 @@ __global__ __launch_bounds__(256) void k_sgmv_expand_rows(ExpandParams p, TreePa
                     for (int t = 0; t < 4; ++t)
                         b1[t][0] = bop[t][0];
                     hb_from_tile<1>(La, hs[i & 1], ra, hb);
-                    expand_mma_store<1>(La, p.y, p.ld_y, p.N, hb, scale, yv, b1);
+                    expand_mma<1>(hb, scale, yv, b1, o);
+                }
+                if (mine) {
+                    *reinterpret_cast<u16x8*>(yl) = o[0];
+                    *reinterpret_cast<u16x8*>(yl + 8) = o[1];
                 }
                 done = done || mine;
             }
         }
-        L = Ln;
+        unsigned w_next = 0;
+        if (next)
+            w_next = put(row0 + kRowBlock, nr1, (i + 1) & 1);
+        __syncthreads();
+        w_prev = w_cur;
+        w_cur = w_next;
         id = idn;
-        yv[0] = yn[0];
-        yv[1] = yn[1];
     }
+    y_chunk_store(yc, ys[(tiles - 1) & 1], p.y, p.ld_y, row_base + (int64_t)kRowBlock * (tiles - 1), col0, w_prev);
 }
 
 // KS: matrix-core steps the kernel is built for (1: r_max <= 32, 2: r_max <= 64).
