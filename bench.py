@@ -537,8 +537,11 @@ def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S):
     sum_r = sum(int(c.ranks[a]) for a in touched)
     sh_bytes = 2 * M * K + 2 * K * sum_r + 4 * M * c.r_max
     ex_bytes = 4 * int(sum(int(c.ranks[a]) for a in c.ids[valid])) + 2 * N * sum_r + 4 * int(valid.sum()) * N
-    per = sh_bytes + ex_bytes
-    copies = max(2, math.ceil(ROTATE_BYTES / per))
+    # each variant rotates over >= 1 GiB of its own operands: the shrink's
+    # (x, A) and the expand's (y, B, h) copies are counted separately
+    copies_sh = max(2, math.ceil(ROTATE_BYTES / sh_bytes))
+    copies_ex = max(2, math.ceil(ROTATE_BYTES / ex_bytes))
+    copies = max(copies_sh, copies_ex)
     base_x, base_y = gpu_tensor(c.x, dev), gpu_tensor(c.y, dev)
     base_A = [gpu_tensor(a, dev) for a in c.As]
     base_B = [gpu_tensor(b, dev) for b in c.Bs]
@@ -548,14 +551,18 @@ def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S):
     plan = torch.empty(dsl.lora_sgmv_plan_bytes(M), dtype=torch.uint8, device=dev)
     dsl.lora_sgmv_plan(ids_g, n, plan)
     cnt = torch.zeros(dsl.lora_sgmv_counter_bytes(M) // 4, dtype=torch.int32, device=dev)
+    xs = [base_x] + [base_x.clone() for _ in range(copies_sh - 1)]
+    Ass = [base_A] + [[a.clone() for a in base_A] for _ in range(copies_sh - 1)]
+    ys = [base_y] + [base_y.clone() for _ in range(copies_ex - 1)]
+    Bss = [base_B] + [[b.clone() for b in base_B] for _ in range(copies_ex - 1)]
+    hs = [torch.empty((M, c.r_max), dtype=torch.float32, device=dev) for _ in range(copies_ex)]
     sets = []
     for i in range(copies):
-        As = [a.clone() for a in base_A] if i else base_A
-        Bs = [b.clone() for b in base_B] if i else base_B
-        sets.append(dict(x=base_x.clone() if i else base_x, y=base_y.clone() if i else base_y, A=As, B=Bs,
+        As, Bs = Ass[i % copies_sh], Bss[i % copies_ex]
+        sets.append(dict(x=xs[i % copies_sh], y=ys[i % copies_ex], A=As, B=Bs,
                          Ap=torch.tensor([a.data_ptr() for a in As], dtype=torch.int64, device=dev),
                          Bp=torch.tensor([b.data_ptr() for b in Bs], dtype=torch.int64, device=dev),
-                         h=torch.empty((M, c.r_max), dtype=torch.float32, device=dev),
+                         h=hs[i % copies_ex],
                          ws=torch.empty(dsl.lora_sgmv_workspace_bytes(M, c.r_max, S), dtype=torch.uint8,
                                         device=dev)))
     torch.cuda.synchronize()
@@ -584,7 +591,8 @@ def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S):
     out = {"workload": f"M={M}, K={K}, N={N}, {n} adapters of ranks {sorted(set(int(v) for v in c.ranks))}, "
                        f"segments {seg_lo}..{seg_hi} tokens, Split-K {S}",
            "segments": len(c.segs), "touched_adapters": len(touched), "shrink_bytes": sh_bytes,
-           "expand_bytes": ex_bytes, "workspace_bytes": 8 * S * M * c.r_max, "copies": copies}
+           "expand_bytes": ex_bytes, "workspace_bytes": 8 * S * M * c.r_max,
+           "copies": {"x_A": copies_sh, "y_B_h": copies_ex}}
     for name, call, byt in (("shrink", shrink, sh_bytes), ("shrink_one_launch", shrink_counted, sh_bytes),
                             ("expand", expand, ex_bytes), ("shrink_expand", both, sh_bytes + ex_bytes),
                             ("shrink_expand_pipeline", pipeline, sh_bytes + ex_bytes),
@@ -647,11 +655,16 @@ def decode_probe(args, M=32):
 
 
 def _time_rotating(call, sets, args):
-    """us per call: 8 calls on 8 input copies per HIP graph, graphs replayed."""
+    """us per call: 8 calls on 8 input copies per HIP graph, graphs replayed.
+    Under --counters: two eager calls, no timing (returns NaN)."""
     import torch
     copies = len(sets)
     call(sets[0])
     torch.cuda.synchronize()
+    if getattr(args, "counters", False):
+        call(sets[1 % copies])
+        torch.cuda.synchronize()
+        return float("nan")
     per_graph = 8
     graphs = []
     for c0 in range(0, copies, per_graph):
@@ -694,6 +707,14 @@ def cpu_baseline(seconds: float):
             "sample": f"{n} full steps (M = 1, 16, 64, 256; fp64 shrink + expand each) in {el:.1f} s"}
 
 
+# Workloads bench.py can time on their own (--only).
+ONLY = {
+    "sgmv_qkv": lambda a: sgmv_bench(a, "b3", 512, 4096, 6144, [64] * 4, 1, 64, 8),
+    "sgmv_prefill": lambda a: sgmv_bench(a, "b5", 4096, 8192, 28672, [8, 16, 32, 64] * 8, 32, 512, 16),
+    "decode_probe": lambda a: decode_probe(a, 128),
+}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -704,6 +725,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the other shapes (sweep, multi-adapter)")
+    ap.add_argument("--only", choices=sorted(ONLY),
+                    help="time one workload and print its JSON only (a target for a profiler run)")
     ap.add_argument("--counters", action="store_true",
                     help="only run the step eagerly for a hardware-counter profile; prints no JSON")
     args = ap.parse_args()
@@ -713,7 +736,13 @@ def main():
         sys.exit(2)
 
     if args.counters:
-        counter_pass(args)
+        if args.only:
+            ONLY[args.only](args)             # eager calls, no timing (see _time_rotating)
+        else:
+            counter_pass(args)
+        return
+    if args.only:
+        print(json.dumps({args.only: ONLY[args.only](args)}), flush=True)
         return
     b = Bench(args)
     res = b.run()
@@ -735,10 +764,9 @@ def main():
         log("bench: split sweep done")
         extra["compensated_expand"] = compensated_bench(args)
         log("bench: compensated expand done")
-        extra["sgmv_m512_k4096_n6144_4x_r64"] = sgmv_bench(args, "b3", 512, 4096, 6144, [64] * 4, 1, 64, 8)
+        extra["sgmv_m512_k4096_n6144_4x_r64"] = ONLY["sgmv_qkv"](args)
         log("bench: sgmv 512 done")
-        extra["sgmv_prefill_m4096_k8192_n28672_32_adapters"] = sgmv_bench(args, "b5", 4096, 8192, 28672,
-                                                                          [8, 16, 32, 64] * 8, 32, 512, 16)
+        extra["sgmv_prefill_m4096_k8192_n28672_32_adapters"] = ONLY["sgmv_prefill"](args)
         log("bench: sgmv prefill done")
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
     import torch
