@@ -100,10 +100,27 @@ int launch_status(hipError_t e)
     return e == hipSuccess ? LORA_OK : LORA_ERR_LAUNCH;
 }
 
+// Row blocks per item of the A-in-registers partial kernel, or 0 when it is
+// not used: it needs short wave chains (shrink_stream_fits) and at least 2048
+// (row block, split) pairs, and takes about 512 items.  Per-element
+// arithmetic does not depend on it.
+int stream_rows_per_item(int64_t tiles, const lora_shrink_plan_t& pl)
+{
+    if (!shrink_stream_fits(pl.waves, pl.k_steps, pl.rank_tiles) || tiles * pl.split_k < 2048)
+        return 0;
+    const int64_t R = (tiles * pl.split_k + 511) / 512;
+    return R < 4 ? 4 : (R > 16 ? 16 : (int)R);
+}
+
 // The Split-K partial kernel of the deterministic two-pass paths.
 hipError_t launch_partials(const ShrinkParams& p, const lora_shrink_plan_t& pl, int64_t M, int32_t split_k,
                            hipStream_t st)
 {
+    const int64_t tiles = (M + kRowBlock - 1) / kRowBlock;
+    const int R = stream_rows_per_item(tiles, pl);
+    if (R > 0)
+        return launch_shrink_stream(p, pl.waves, pl.k_steps, pl.rank_tiles, R,
+                                    (int)((tiles + R - 1) / R * split_k), false, st);
     const int T = shrink_tiles_per_wg(M, split_k);
     if (T > 1)
         return launch_shrink_partial_multi(p, pl.waves, pl.rank_tiles, T, st);
@@ -247,6 +264,19 @@ int launch_sgmv_partials(const uint16_t* x, int64_t ld_x, const uint16_t* const*
     p.n_adapters = n_adapters;
     p.scale = 1.0f;
     // Tiles never exceed M; the grid is a fixed bound, idle workgroups exit.
+    // The A-in-registers kernel is sized for about M / 16 + n_adapters tiles
+    // (runs of one adapter); its workgroups take further items when the plan
+    // has more.
+    const int64_t est = (M + kRowBlock - 1) / kRowBlock + n_adapters;
+    lora_shrink_plan_t ps = pl;
+    ps.rank_tiles = (r_max + 15) / 16;
+    const int R = stream_rows_per_item(est, ps);
+    if (R > 0) {
+        const int64_t grid = (est + R - 1) / R * pl.split_k;
+        return launch_status(launch_shrink_stream(p, pl.waves, pl.k_steps, ps.rank_tiles, R,
+                                                  (int)(grid < 65536 ? grid : 65536 / pl.split_k * pl.split_k),
+                                                  true, s));
+    }
     const int T = shrink_tiles_per_wg(M, pl.split_k);
     if (T > 1) {
         const int64_t bound = (M + T - 1) / T * pl.split_k;

@@ -144,6 +144,13 @@ hipError_t launch_shrink_partial_multi(const ShrinkParams& p, int waves, int ran
                                        hipStream_t st);
 hipError_t launch_sgmv_shrink_partial_multi(const ShrinkParams& p, int waves, int tiles_per_wg, int grid,
                                             hipStream_t st);
+// A-in-registers partial kernel for large M: R row blocks (plan tiles) per
+// workgroup item; usable when shrink_stream_fits (waves 4 or 8, k_steps 1, 2
+// or 4, at most 32 registers of A operands per wave).
+constexpr int kStreamMaxRows = 16;             // row blocks per item, at most
+bool shrink_stream_fits(int waves, int k_steps, int rank_tiles);
+hipError_t launch_shrink_stream(const ShrinkParams& p, int waves, int k_steps, int rank_tiles, int R, int grid,
+                                bool sgmv, hipStream_t st);
 hipError_t launch_shrink_counted(const ShrinkParams& p, const CounterParams& c, int waves, int rank_tiles,
                                  int group_tiles, hipStream_t st);
 hipError_t launch_sgmv_shrink_counted(const ShrinkParams& p, const CounterParams& c, int waves, int group_tiles,

@@ -259,6 +259,171 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_partial_multi(ShrinkP
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large M with short wave chains (the 16 RT rank rows x k_steps operands of a
+// wave's k range fit in 32 registers): a workgroup takes one split and R
+// consecutive row blocks (plan tiles for the multi-adapter shrink).  Each wave
+// loads its k range of the adapter's A once - again only when the adapter
+// changes - and keeps it in registers while it walks the row blocks; the x
+// operands of a block are loaded two blocks ahead; the wave sums of a block
+// meet in LDS (two buffers, one barrier per block) and are added along the
+// fixed pairwise tree while the other waves run the next block's
+// matrix-core steps.  Per element this is the arithmetic of shrink_tiles: the
+// same chains in the same k order, the same wave tree, the same partial
+// stored to the workspace.  What changes is the traffic: A is read once per
+// workgroup instead of once per few row blocks.
+// ---------------------------------------------------------------------------
+template <int RT, int W, int STEPS, bool SGMV>
+__global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int R)
+{
+    constexpr int RS = 16 * RT + 4;               // padded LDS row stride (floats)
+    __shared__ __align__(16) float red[2][W * 16 * RS];
+    __shared__ int32_t tl[3 * kStreamMaxRows];    // the item's plan entries
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int li = lane & 15;
+    const int g = lane >> 4;
+    const int32_t* plan = p.tiles + kPlanHeaderInts;
+    const int64_t ntiles = SGMV ? plan_tiles(p.tiles, p.M, p.n_adapters) : (p.M + kRowBlock - 1) / kRowBlock;
+    const uint32_t S = (uint32_t)p.split_k;
+    const uint32_t items = (uint32_t)((ntiles + R - 1) / R) * S;
+    // tile j (the item's u-th): first row, row count (0: nothing to compute)
+    // and adapter; plan entries come from LDS, so reading them never waits
+    // for the x loads in flight
+    auto tile = [&](int64_t j, int u, int64_t& row0, int& nrows, int& a) {
+        if constexpr (SGMV) {
+            const int32_t* t = tl + 3 * u;
+            const bool ok = tile_ok(t, p.M, p.n_adapters);
+            row0 = ok ? t[0] : 0;
+            nrows = ok ? t[1] : 0;
+            a = ok ? t[2] : -1;
+        } else {
+            row0 = j * kRowBlock;
+            nrows = p.M - row0 < kRowBlock ? (int)(p.M - row0) : kRowBlock;
+            a = 0;
+        }
+    };
+    uint32_t k = 0;                               // blocks walked: selects the LDS buffer
+    for (uint32_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int s = (int)(it % S);
+        const int64_t c0 = (int64_t)(it / S) * R;
+        const int cnt = ntiles - c0 < R ? (int)(ntiles - c0) : R;
+        if constexpr (SGMV) {
+            __syncthreads();                      // the previous item's entries are no longer read
+            if ((int)threadIdx.x < 3 * cnt)
+                tl[threadIdx.x] = plan[3 * c0 + threadIdx.x];
+            __syncthreads();
+        }
+        // reduction slots 8g..8g+7 of step t hold k = kbase + 32 t + (0..7)
+        const int64_t kbase = (int64_t)s * p.k_chunk + (int64_t)wave * STEPS * kKStep + g * 8;
+        auto xload = [&](int u, bf16x8 (&dst)[STEPS]) {
+            int64_t row0;
+            int nrows, a;
+            tile(c0 + u, u, row0, nrows, a);
+            const uint16_t* xp = p.x + (row0 + (li < nrows ? li : 0)) * p.ld_x + kbase;
+#pragma unroll
+            for (int t = 0; t < STEPS; ++t)
+                dst[t] = load_bf16x8(xp + t * kKStep);
+        };
+        bf16x8 x0[STEPS], x1[STEPS], x2[STEPS];
+        bf16x8 aop[STEPS][RT];
+        // runs of blocks with one adapter: the run's first two x blocks and
+        // its A chunk are loaded at the start of the run and waited for there,
+        // so the loop over the run's blocks waits only for the x operands it
+        // is about to use
+        int u = 0;
+        while (u < cnt) {
+            int64_t row0;
+            int nrows, a;
+            tile(c0 + u, u, row0, nrows, a);      // uniform: plan data only
+            int u1 = u + 1;
+            if constexpr (SGMV) {
+                while (u1 < cnt) {
+                    int64_t r1;
+                    int n1, a1;
+                    tile(c0 + u1, u1, r1, n1, a1);
+                    if (a1 != a)
+                        break;
+                    ++u1;
+                }
+            } else {
+                u1 = cnt;
+            }
+            const int ra = a < 0 ? 0 : (SGMV ? adapter_rank(p, a) : p.r);
+            const int nrt = (ra + 15) / 16 < RT ? (ra + 15) / 16 : RT;
+            xload(u, x0);
+            xload(u + 1 < u1 ? u + 1 : u, x1);
+            if (ra > 0) {
+                const uint16_t* A = SGMV ? p.A_ptrs[a] : p.A;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    if (rt < nrt) {
+                        const int j = rt * 16 + li;
+                        const uint16_t* ap = A + (int64_t)(j < ra ? j : 0) * p.ld_a + kbase;
+#pragma unroll
+                        for (int t = 0; t < STEPS; ++t)
+                            aop[t][rt] = load_bf16x8(ap + t * kKStep);
+                    }
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0);
+            // the run's i-th block uses buffer i % 3 and loads block i + 2
+            // into buffer (i + 2) % 3 (loop unrolled by three: no register is
+            // copied while its load is in flight)
+            auto block = [&](const bf16x8 (&xc)[STEPS], bf16x8 (&xn)[STEPS]) {
+                xload(u + 2 < u1 ? u + 2 : u1 - 1, xn);   // unconditional: no branch-dependent buffer
+                tile(c0 + u, u, row0, nrows, a);
+                const bool on = nrows > 0 && ra > 0;
+                float* rb = red[k & 1];
+                if (on) {
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) {
+                        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if (rt < nrt) {
+#pragma unroll
+                            for (int t = 0; t < STEPS; ++t)
+                                acc = mfma_16x16x32(xc[t], aop[t][rt], acc);
+                        }
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            rb[(wave * 16 + 4 * g + v) * RS + rt * 16 + li] = acc[v];
+                    }
+                }
+                __syncthreads();
+                if (on) {
+                    const int ncols = ra < 16 * RT ? ra : 16 * RT;
+                    for (int e = threadIdx.x; e < 16 * 16 * RT; e += W * kWave) {
+                        const int row = e / (16 * RT);
+                        const int col = e - row * (16 * RT);
+                        if (row < nrows && col < ncols) {
+                            float v[W];
+#pragma unroll
+                            for (int w = 0; w < W; ++w)
+                                v[w] = rb[(w * 16 + row) * RS + col];
+                            p.out[(int64_t)s * p.split_stride + (row0 + row) * p.ld_out + col] =
+                                pairwise_tree<W>(v);
+                        }
+                    }
+                }
+            };
+            for (;;) {
+                block(x0, x2);
+                ++k;
+                if (++u >= u1)
+                    break;
+                block(x1, x0);
+                ++k;
+                if (++u >= u1)
+                    break;
+                block(x2, x1);
+                ++k;
+                if (++u >= u1)
+                    break;
+            }
+        }
+    }
+}
+
 // Single launch: the last split of each (tile, rank group) writes its h
 // columns; the group holding the adapter's last rank column also zeroes the
 // columns from the rank up to r_max; tiles of tokens without an adapter are
@@ -501,6 +666,55 @@ hipError_t launch_sgmv_shrink_partial_multi(const ShrinkParams& p, int waves, in
     else
         launch_multi_t<4>(p, waves, rank_tiles, dim3((unsigned)grid), true, st);
     return hipGetLastError();
+}
+
+namespace {
+
+template <int RT, int W, bool SGMV>
+hipError_t launch_stream_rws(const ShrinkParams& p, int steps, int R, dim3 grid, hipStream_t st)
+{
+    switch (steps) {
+    case 1: hipLaunchKernelGGL((k_shrink_stream<RT, W, 1, SGMV>), grid, dim3(W * 64), 0, st, p, R); break;
+    case 2: hipLaunchKernelGGL((k_shrink_stream<RT, W, 2, SGMV>), grid, dim3(W * 64), 0, st, p, R); break;
+    default:
+        if constexpr (RT <= 2)
+            hipLaunchKernelGGL((k_shrink_stream<RT, W, 4, SGMV>), grid, dim3(W * 64), 0, st, p, R);
+        else
+            return hipErrorInvalidValue;
+        break;
+    }
+    return hipGetLastError();
+}
+
+template <int RT, bool SGMV>
+hipError_t launch_stream_r(const ShrinkParams& p, int waves, int steps, int R, dim3 grid, hipStream_t st)
+{
+    return waves == 8 ? launch_stream_rws<RT, 8, SGMV>(p, steps, R, grid, st)
+                      : launch_stream_rws<RT, 4, SGMV>(p, steps, R, grid, st);
+}
+
+}  // namespace
+
+bool shrink_stream_fits(int waves, int k_steps, int rank_tiles)
+{
+    const int rt = rank_tiles <= 1 ? 1 : (rank_tiles == 2 ? 2 : 4);
+    return (waves == 4 || waves == 8) && (k_steps == 1 || k_steps == 2 || k_steps == 4) && rt * k_steps <= 8;
+}
+
+hipError_t launch_shrink_stream(const ShrinkParams& p, int waves, int k_steps, int rank_tiles, int R, int grid,
+                                bool sgmv, hipStream_t st)
+{
+    if (!shrink_stream_fits(waves, k_steps, rank_tiles) || R < 1 || R > kStreamMaxRows || grid < 1)
+        return hipErrorInvalidValue;
+    const dim3 g((unsigned)grid);
+    if (rank_tiles <= 1)
+        return sgmv ? launch_stream_r<1, true>(p, waves, k_steps, R, g, st)
+                    : launch_stream_r<1, false>(p, waves, k_steps, R, g, st);
+    if (rank_tiles == 2)
+        return sgmv ? launch_stream_r<2, true>(p, waves, k_steps, R, g, st)
+                    : launch_stream_r<2, false>(p, waves, k_steps, R, g, st);
+    return sgmv ? launch_stream_r<4, true>(p, waves, k_steps, R, g, st)
+                : launch_stream_r<4, false>(p, waves, k_steps, R, g, st);
 }
 
 hipError_t launch_shrink_partial_direct(const ShrinkParams& p, int waves, int rank_tiles, int group_tiles,

@@ -965,6 +965,31 @@ def test_shrink_expand_counted_stress_and_graph():
 
 
 # ---------------------------------------------------------------------------
+# shrinks whose partial kernel keeps A in registers and walks row blocks
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,r,S", [(4100, 8192, 64, 16), (4100, 4096, 24, 8), (2100, 16384, 32, 16),
+                                     (4100, 1024, 5, 8), (2100, 2048, 37, 16)])
+def test_shrink_stream_rows_bitwise(M, K, r, S):
+    """At M large enough (at least 2048 row block x split pairs, short wave
+    chains) for the partial kernel that keeps each wave's A operands in
+    registers while it walks several row blocks, every row's h equals that of
+    a small call on the same rows (one-tile kernels) bit for bit, and sampled
+    rows agree with the oracle.  Plans with 1, 2 and 4 steps per wave, 4 and 8
+    waves, 1 to 4 rank tiles; ragged M and ranks."""
+    _say(f"stream shrink M={M} K={K} r={r} S={S}")
+    x = normal_bf16((M, K), 1.0, r, "ssx")
+    A = normal_bf16((r, K), 0.02, r, "ssA")
+    h = run_shrink(x, A, S, 2.0)
+    for r0 in (0, 1008, M - 37):
+        n = min(64, M - r0)
+        hs = run_shrink(np.ascontiguousarray(x[r0:r0 + n]), A, S, 2.0)
+        assert np.array_equal(hs.view(np.int32), h[r0:r0 + n].view(np.int32)), f"rows {r0}.."
+    rng = np.random.default_rng(r)
+    rows = sorted(set([0, 15, 16, M - 1] + rng.choice(M, 16, replace=False).tolist()))
+    check_shrink(h[rows], x[rows], A, 2.0, dsl.lora_shrink_plan(K, r, S), f"stream shrink M={M} K={K} r={r}")
+
+
+# ---------------------------------------------------------------------------
 # expands that walk several 16-token tiles per workgroup (large M x N)
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("r", [5, 16, 37, 64])
