@@ -32,7 +32,7 @@ int make_plan(int64_t K, int32_t r, int32_t split_k, lora_shrink_plan_t* pl)
 {
     if (!split_ok(split_k))
         return LORA_ERR_UNSUPPORTED;
-    if (r < 1 || r > 64)
+    if (r < 1 || r > kMaxRank)
         return LORA_ERR_UNSUPPORTED;
     if (K <= 0 || K > kMaxDim)
         return LORA_ERR_SHAPE;
@@ -54,12 +54,12 @@ int make_plan(int64_t K, int32_t r, int32_t split_k, lora_shrink_plan_t* pl)
 
 // Rank tiles per shrink workgroup.  Per-element arithmetic does not depend on
 // it; small calls give every 16-wide rank tile its own workgroup (more loads in
-// flight across the chip), large ones keep a row block's rank tiles together
-// so its x rows are read once.
+// flight across the chip), large ones keep up to kGroupTiles of a row block's
+// rank tiles together so its x rows are read once (twice above rank 64).
 int group_tiles_for(int64_t M, int32_t split_k, int rank_tiles)
 {
     const int64_t wgs = ((M + kRowBlock - 1) / kRowBlock) * split_k * rank_tiles;
-    return wgs <= 2048 ? 1 : rank_tiles;
+    return wgs <= 2048 ? 1 : (rank_tiles < kGroupTiles ? rank_tiles : kGroupTiles);
 }
 
 // Row blocks per shrink workgroup in the two-pass paths (all rank tiles
@@ -78,7 +78,7 @@ int shrink_tiles_per_wg(int64_t M, int32_t split_k)
 // standing in for the (device-side) tile count.
 int sgmv_group_tiles(int64_t M, int32_t split_k, int32_t r_max)
 {
-    return group_tiles_for(M, split_k, (r_max + 15) / 16) == 1 ? 1 : kMaxRankTiles;
+    return group_tiles_for(M, split_k, (r_max + 15) / 16) == 1 ? 1 : kGroupTiles;
 }
 
 // Work items of the multi-adapter shrinks (at most M tiles x split_k x
@@ -121,7 +121,8 @@ hipError_t launch_partials(const ShrinkParams& p, const lora_shrink_plan_t& pl, 
     if (R > 0)
         return launch_shrink_stream(p, pl.waves, pl.k_steps, pl.rank_tiles, R,
                                     (int)((tiles + R - 1) / R * split_k), false, st);
-    const int T = shrink_tiles_per_wg(M, split_k);
+    // several row blocks per workgroup hold all rank tiles at once: ranks <= 64
+    const int T = pl.rank_tiles <= kGroupTiles ? shrink_tiles_per_wg(M, split_k) : 1;
     if (T > 1)
         return launch_shrink_partial_multi(p, pl.waves, pl.rank_tiles, T, st);
     return launch_shrink_partial_ws(p, pl.waves, pl.rank_tiles, group_tiles_for(M, split_k, pl.rank_tiles), st);
@@ -169,7 +170,7 @@ ShrinkParams shrink_params(const uint16_t* x, int64_t ld_x, const uint16_t* A, i
 
 size_t workspace_bytes(int64_t M, int32_t cols, int32_t split_k)
 {
-    if (M < 0 || M > kMaxDim || cols < 1 || cols > 64 || !split_ok(split_k))
+    if (M < 0 || M > kMaxDim || cols < 1 || cols > kMaxRank || !split_ok(split_k))
         return 0;
     return (size_t)split_k * (size_t)M * (size_t)cols * sizeof(float);
 }
@@ -210,7 +211,7 @@ int check_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* A, int6
 bool use_single_launch(int64_t M, int64_t K, int32_t r, int64_t N)
 {
     (void)N;
-    return M <= 64 && K * r * 2 <= 32 * 1024;
+    return M <= 64 && r <= kFusedMaxRank && K * r * 2 <= 32 * 1024;
 }
 
 int launch_fused(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a, const uint16_t* B,
@@ -277,7 +278,7 @@ int launch_sgmv_partials(const uint16_t* x, int64_t ld_x, const uint16_t* const*
                                                   (int)(grid < 65536 ? grid : 65536 / pl.split_k * pl.split_k),
                                                   true, s));
     }
-    const int T = shrink_tiles_per_wg(M, pl.split_k);
+    const int T = r_max <= 16 * kGroupTiles ? shrink_tiles_per_wg(M, pl.split_k) : 1;
     if (T > 1) {
         const int64_t bound = (M + T - 1) / T * pl.split_k;
         return launch_status(
@@ -417,7 +418,7 @@ int expand_entry(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b, 
 {
     if (M < 0 || M > kMaxDim || N < 0 || N > kMaxDim)
         return LORA_ERR_SHAPE;
-    if (r < 1 || r > 64)
+    if (r < 1 || r > kMaxRank)
         return LORA_ERR_UNSUPPORTED;
     if (N % 8 != 0)
         return LORA_ERR_UNSUPPORTED;
@@ -500,7 +501,7 @@ int lora_expand_combine(const void* workspace, size_t ws_bytes, int32_t split_k,
 {
     if (M < 0 || M > kMaxDim || N < 0 || N > kMaxDim)
         return LORA_ERR_SHAPE;
-    if (!split_ok(split_k) || r < 1 || r > 64 || N % 8 != 0)
+    if (!split_ok(split_k) || r < 1 || r > kMaxRank || N % 8 != 0)
         return LORA_ERR_UNSUPPORTED;
     if (((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols) > kMaxGrid)
         return LORA_ERR_SHAPE;
@@ -552,6 +553,8 @@ int lora_shrink_expand_fused(const uint16_t* x, int64_t ld_x, const uint16_t* A,
                              int32_t r, int64_t N, int32_t split_k, float shrink_scale, float expand_scale,
                              void* stream)
 {
+    if (r > kFusedMaxRank)
+        return LORA_ERR_UNSUPPORTED;
     lora_shrink_plan_t pl;
     const int st = check_shrink_expand(x, ld_x, A, ld_a, B, ld_b, h, ld_h, y, ld_y, M, K, r, N, split_k, &pl);
     if (st != LORA_OK || M == 0 || N == 0)
@@ -921,7 +924,7 @@ int lora_sgmv_expand(const float* h, int64_t ld_h, const uint16_t* const* B_ptrs
 {
     if (M < 0 || M > kMaxDim || N < 0 || N > kMaxDim || n_adapters < 1)
         return LORA_ERR_SHAPE;
-    if (r_max < 1 || r_max > 64 || N % 8 != 0)
+    if (r_max < 1 || r_max > kMaxRank || N % 8 != 0)
         return LORA_ERR_UNSUPPORTED;
     if (((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols) > kMaxGrid)
         return LORA_ERR_SHAPE;

@@ -106,10 +106,23 @@ __device__ __forceinline__ bf16x8 load_h_as_bf16(const float* hp, int j0, int r)
 // tile t (0..3) stands for column  n_base + 16 (m / 4) + 4 t + (m % 4),  so lane
 // (li, g) collects columns n_base + 16 g + 4 t + v - a contiguous run of 16 -
 // for token li, and y moves with 16-byte loads and stores straight from the
-// accumulators.  Per element: one matrix-core step over j < 32 (r <= 32) or two
-// (r <= 64) with zero-padded reduction slots, then fma(scale, acc, y) and one
-// rounding to bf16.
+// accumulators.  Per element: one matrix-core step over j < 32 (r <= 32), two
+// (r <= 64) or four (r <= 128) with zero-padded reduction slots, then
+// fma(scale, acc, y) and one rounding to bf16.
 // ---------------------------------------------------------------------------
+// Matrix-core steps of 32 the expand takes at rank r: 1 (r <= 32), 2 (r <= 64)
+// or 4 (r <= 128).  Every expand kernel takes exactly this many for a token of
+// rank r, whatever rank bound it was built for, so their bits agree.
+__host__ __device__ constexpr int expand_steps(int r)
+{
+    return r <= 32 ? 1 : (r <= 64 ? 2 : 4);
+}
+
+template <int N>
+struct Steps {
+    static constexpr int value = N;
+};
+
 struct ExpandLane {
     int64_t row;        // this lane's token (clamped into the block)
     int64_t n_base;     // first column of this wave
@@ -290,11 +303,12 @@ __device__ __forceinline__ void expand_finish_comp(const ExpandLane& L, uint16_t
 // Staging of an h tile for the expands that walk several 16-token tiles per
 // workgroup: 16 rows x round_up(r, 8) columns of bf16(h) in LDS (row stride
 // kHbStride), zeros past r and for rows outside the tile.  Each of the first
-// 16 * round_up(r, 8) / 4 threads converts one group of 4 columns, read with
-// one 16-byte load (h is 16-byte aligned with ld_h % 4 == 0, so a group that
-// starts below r ends inside the row's ld_h).
+// 16 * round_up(r, 8) / HC threads converts one group of HC (4 or 8) columns,
+// read with 16-byte loads (h is 16-byte aligned with ld_h % 4 == 0, so a
+// 4-column part that starts below r ends inside the row's ld_h).  HC = 4
+// covers ranks <= 64 with 256 threads, HC = 8 ranks <= 128.
 // ---------------------------------------------------------------------------
-constexpr int kHbStride = 72;             // bf16 per LDS row (64 + 8 padding)
+constexpr int kHbStride = 136;            // bf16 per LDS row (128 + 8 padding)
 
 struct HStageSlot {
     int row;
@@ -302,38 +316,53 @@ struct HStageSlot {
     bool on;
 };
 
+template <int HC>
 __device__ __forceinline__ HStageSlot h_stage_slot(int r)
 {
-    const int q = ((r + 7) & ~7) / 4;     // 4-column groups per row, 2 .. 16
+    const int q = ((r + 7) & ~7) / HC;    // column groups per row
     HStageSlot s;
     s.row = (int)threadIdx.x / q;
-    s.col = ((int)threadIdx.x - s.row * q) * 4;
+    s.col = ((int)threadIdx.x - s.row * q) * HC;
     s.on = s.row < 16;
     return s;
 }
 
-// The slot's 4 h values (zeros past r and for rows outside the tile) ...
+// The slot's HC h values (zeros past r and for rows outside the tile) ...
+template <int HC>
 __device__ __forceinline__ void h_load(const HStageSlot& s, const float* h, int64_t ld_h, int64_t row0, int nrows,
-                                       int r, float (&f)[4])
+                                       int r, float (&f)[HC])
 {
-    f[0] = f[1] = f[2] = f[3] = 0.f;
+#pragma unroll
+    for (int e = 0; e < HC; ++e)
+        f[e] = 0.f;
     if (!s.on || s.row >= nrows || s.col >= r)
         return;
-    const float4 v = *reinterpret_cast<const float4*>(h + (row0 + s.row) * ld_h + s.col);
+    const float* hp = h + (row0 + s.row) * ld_h + s.col;
+    const float4 v = *reinterpret_cast<const float4*>(hp);
     f[0] = v.x;
     f[1] = s.col + 1 < r ? v.y : 0.f;
     f[2] = s.col + 2 < r ? v.z : 0.f;
     f[3] = s.col + 3 < r ? v.w : 0.f;
+    if constexpr (HC == 8) {
+        if (s.col + 4 < r) {
+            const float4 w = *reinterpret_cast<const float4*>(hp + 4);
+            f[4] = w.x;
+            f[5] = s.col + 5 < r ? w.y : 0.f;
+            f[6] = s.col + 6 < r ? w.z : 0.f;
+            f[7] = s.col + 7 < r ? w.w : 0.f;
+        }
+    }
 }
 
 // ... and their bf16 roundings put into the LDS tile.
-__device__ __forceinline__ void h_put(const HStageSlot& s, const float (&f)[4], uint16_t* tile)
+template <int HC>
+__device__ __forceinline__ void h_put(const HStageSlot& s, const float (&f)[HC], uint16_t* tile)
 {
     if (!s.on)
         return;
     uint16_t* d = tile + s.row * kHbStride + s.col;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < HC; ++e)
         d[e] = f32_to_bf16_bits(f[e]);
 }
 

@@ -169,7 +169,8 @@ __global__ __launch_bounds__(256) void k_expand_rows(ExpandParams p, int R)
     const int64_t row_base = (int64_t)(blockIdx.x / nblocks) * kRowBlock * R;
     const int64_t left = (p.M - row_base + kRowBlock - 1) / kRowBlock;
     const int tiles = left < R ? (int)left : R;
-    const HStageSlot slot = h_stage_slot(p.r);
+    constexpr int HC = KS == 4 ? 8 : 4;          // h columns each staging thread converts
+    const HStageSlot slot = h_stage_slot<HC>(p.r);
     const YChunk yc = y_chunk();
     const bool col_ok = col0 + yc.col < p.N;
     const unsigned full = y_chunk_rows(yc, kRowBlock, col_ok);
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(256) void k_expand_rows(ExpandParams p, int R)
     bf16x8 bop[4][KS];
     expand_load_b<KS>(L, p.N, p.B, p.ld_b, p.r, bop);
     u16x8 g[2];
-    float f[4];
+    float f[HC];
     int nr = tile_rows(p.M, row_base);
     unsigned ok = y_chunk_rows(yc, nr, col_ok);
     y_chunk_load(yc, p.y, p.ld_y, row_base, col0, ok, g);
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(256) void k_expand_rows(ExpandParams p, int R)
 // multiply by the shrink scale) is evaluated into an LDS tile, written out as
 // h by the first column block, and fed to the expand without a round trip
 // through a separate kernel.  Same bits as shrink then expand.
-constexpr int kHTileStride = 68;          // floats per LDS row (64 + 4 padding)
+constexpr int kHTileStride = 132;         // floats per LDS row (128 + 4 padding)
 
 template <int KS, int S>
 __global__ __launch_bounds__(256) void k_expand_combine(ExpandParams p, TreeParams c)
@@ -283,15 +284,27 @@ __device__ __forceinline__ void sgmv_pass(const ExpandParams& p, const ExpandLan
     u16x8 unused[2];
     ExpandLane Lb = L;
     Lb.row_ok = false;                               // B rows only
-    if (ra > 32 || KS == 1) {
-        bf16x8 bop[4][KS];
-        expand_load<KS>(Lb, p.y, p.ld_y, p.N, p.B_ptrs[a], ld_b, ra, unused, bop);
-        expand_finish<KS>(L, p.y, p.ld_y, p.N, hrows, ld_hr, ra, scale, yv, bop);
-    } else {
-        bf16x8 bop[4][1];
-        expand_load<1>(Lb, p.y, p.ld_y, p.N, p.B_ptrs[a], ld_b, ra, unused, bop);
-        expand_finish<1>(L, p.y, p.ld_y, p.N, hrows, ld_hr, ra, scale, yv, bop);
+    // the steps the single-adapter expand takes at this rank
+    auto pass = [&](auto steps) {
+        constexpr int K2 = decltype(steps)::value;
+        bf16x8 bop[4][K2];
+        expand_load<K2>(Lb, p.y, p.ld_y, p.N, p.B_ptrs[a], ld_b, ra, unused, bop);
+        expand_finish<K2>(L, p.y, p.ld_y, p.N, hrows, ld_hr, ra, scale, yv, bop);
+    };
+    const int need = expand_steps(ra);
+    if constexpr (KS >= 4) {
+        if (need == 4) {
+            pass(Steps<4>{});
+            return;
+        }
     }
+    if constexpr (KS >= 2) {
+        if (need == 2) {
+            pass(Steps<2>{});
+            return;
+        }
+    }
+    pass(Steps<1>{});
 }
 
 // ---------------------------------------------------------------------------
@@ -344,14 +357,17 @@ __device__ __forceinline__ float sgmv_h_value(const TreeParams& c, int64_t row, 
 
 // The slot's 4 h values computed from the workspace (and written to c.h when
 // write_h), for h_put.
+template <int HC>
 __device__ __forceinline__ void h_tree(const HStageSlot& s, const TreeParams& c, int64_t row0, int nrows, int r,
-                                       int split_k, bool write_h, float (&f)[4])
+                                       int split_k, bool write_h, float (&f)[HC])
 {
-    f[0] = f[1] = f[2] = f[3] = 0.f;
+#pragma unroll
+    for (int e = 0; e < HC; ++e)
+        f[e] = 0.f;
     if (!s.on || s.row >= nrows)
         return;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
+    for (int e = 0; e < HC; ++e) {
         if (s.col + e < r) {
             f[e] = sgmv_h_value(c, row0 + s.row, s.col + e, split_k);
             if (write_h)
@@ -370,9 +386,9 @@ __device__ __forceinline__ void h_tree(const HStageSlot& s, const TreeParams& c,
 // for tokens with an adapter.
 // COMBINE: h comes from the Split-K workspace (sgmv_h_value), the first
 // column block also writes it out.
-// (at most 128 VGPRs: four workgroups per CU)
+// (at most 128 VGPRs below rank 64: four workgroups per CU)
 template <int KS, bool COMBINE>
-__global__ __launch_bounds__(256, 4) void k_sgmv_expand_rows(ExpandParams p, TreeParams c, int R, int split_k)
+__global__ __launch_bounds__(256, KS == 4 ? 2 : 4) void k_sgmv_expand_rows(ExpandParams p, TreeParams c, int R, int split_k)
 {
     __shared__ __align__(16) uint16_t hs[2][kRowBlock * kHbStride];
     __shared__ __align__(16) uint16_t ys[2][kRowBlock * kYStride];
@@ -381,7 +397,8 @@ __global__ __launch_bounds__(256, 4) void k_sgmv_expand_rows(ExpandParams p, Tre
     const int64_t row_base = (int64_t)(blockIdx.x / nblocks) * kRowBlock * R;
     const int64_t left = (p.M - row_base + kRowBlock - 1) / kRowBlock;
     const int tiles = left < R ? (int)left : R;
-    const HStageSlot slot = h_stage_slot(p.r_max);
+    constexpr int HC = KS == 4 ? 8 : 4;          // h columns each staging thread converts
+    const HStageSlot slot = h_stage_slot<HC>(p.r_max);
     const YChunk yc = y_chunk();
     const bool col_ok = col0 + yc.col < p.N;
     ExpandLane L = expand_lane(row_base, kRowBlock, col0);
@@ -392,7 +409,7 @@ __global__ __launch_bounds__(256, 4) void k_sgmv_expand_rows(ExpandParams p, Tre
     auto valid = [&](int a) { return a >= 0 && a < p.n_adapters; };
     // the tile at r0: its y chunk rows, h slot and this lane's token id in flight
     u16x8 g[2];
-    float f[4];
+    float f[HC];
     int ca[2];                                   // adapter ids of the chunk's rows
     auto fetch = [&](int64_t r0, int nrows, int& lane_id) {
 #pragma unroll
@@ -453,7 +470,32 @@ __global__ __launch_bounds__(256, 4) void k_sgmv_expand_rows(ExpandParams p, Tre
                 ExpandLane La = L;
                 La.row_ok = mine;
                 u16x8 o[2];
-                if (KS == 2 && ra > 32) {
+                // the steps the single-adapter expand takes at this rank
+                auto mma = [&](auto steps) {
+                    constexpr int K2 = decltype(steps)::value;
+                    bf16x8 hb[K2];
+                    hb_from_tile<K2>(La, hs[i & 1], ra, hb);
+                    if constexpr (K2 == KS) {
+                        expand_mma<KS>(hb, scale, yv, bop, o);
+                    } else {
+                        bf16x8 b2[4][K2];
+#pragma unroll
+                        for (int t = 0; t < 4; ++t)
+#pragma unroll
+                            for (int ks = 0; ks < K2; ++ks)
+                                b2[t][ks] = bop[t][ks];
+                        expand_mma<K2>(hb, scale, yv, b2, o);
+                    }
+                };
+                if constexpr (KS == 4) {
+                    const int need = expand_steps(ra);
+                    if (need == 4)
+                        mma(Steps<4>{});
+                    else if (need == 2)
+                        mma(Steps<2>{});
+                    else
+                        mma(Steps<1>{});
+                } else if (KS == 2 && ra > 32) {            // KS 2: ra <= r_max <= 64
                     bf16x8 hb[KS];
                     hb_from_tile<KS>(La, hs[i & 1], ra, hb);
                     expand_mma<KS>(hb, scale, yv, bop, o);
@@ -566,10 +608,11 @@ inline dim3 expand_rows_grid(int64_t M, int64_t N, int R)
 hipError_t launch_expand_compensated(const ExpandParams& p, hipStream_t st)
 {
     const dim3 grid = expand_grid(p.M, p.N);
-    if (p.r > 32)
-        hipLaunchKernelGGL(k_expand_comp<2>, grid, dim3(256), 0, st, p);
-    else
-        hipLaunchKernelGGL(k_expand_comp<1>, grid, dim3(256), 0, st, p);
+    switch (expand_steps(p.r)) {
+    case 4: hipLaunchKernelGGL(k_expand_comp<4>, grid, dim3(256), 0, st, p); break;
+    case 2: hipLaunchKernelGGL(k_expand_comp<2>, grid, dim3(256), 0, st, p); break;
+    default: hipLaunchKernelGGL(k_expand_comp<1>, grid, dim3(256), 0, st, p); break;
+    }
     return hipGetLastError();
 }
 
@@ -579,17 +622,19 @@ hipError_t launch_expand(const ExpandParams& p, hipStream_t st)
     const int R = expand_tiles_per_wg(p.M, p.N);
     if (R > 1) {
         const dim3 grid = expand_rows_grid(p.M, p.N, R);
-        if (p.r > 32)
-            hipLaunchKernelGGL(k_expand_rows<2>, grid, block, 0, st, p, R);
-        else
-            hipLaunchKernelGGL(k_expand_rows<1>, grid, block, 0, st, p, R);
+        switch (expand_steps(p.r)) {
+        case 4: hipLaunchKernelGGL(k_expand_rows<4>, grid, block, 0, st, p, R); break;
+        case 2: hipLaunchKernelGGL(k_expand_rows<2>, grid, block, 0, st, p, R); break;
+        default: hipLaunchKernelGGL(k_expand_rows<1>, grid, block, 0, st, p, R); break;
+        }
         return hipGetLastError();
     }
     const dim3 grid = expand_grid(p.M, p.N);
-    if (p.r > 32)
-        hipLaunchKernelGGL(k_expand<2>, grid, block, 0, st, p);
-    else
-        hipLaunchKernelGGL(k_expand<1>, grid, block, 0, st, p);
+    switch (expand_steps(p.r)) {
+    case 4: hipLaunchKernelGGL(k_expand<4>, grid, block, 0, st, p); break;
+    case 2: hipLaunchKernelGGL(k_expand<2>, grid, block, 0, st, p); break;
+    default: hipLaunchKernelGGL(k_expand<1>, grid, block, 0, st, p); break;
+    }
     return hipGetLastError();
 }
 
@@ -609,8 +654,11 @@ hipError_t launch_expand_combine_ks(const ExpandParams& p, const TreeParams& c, 
 hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st)
 {
     const dim3 grid = expand_grid(p.M, p.N);
-    return p.r > 32 ? launch_expand_combine_ks<2>(p, c, split_k, grid, st)
-                    : launch_expand_combine_ks<1>(p, c, split_k, grid, st);
+    switch (expand_steps(p.r)) {
+    case 4: return launch_expand_combine_ks<4>(p, c, split_k, grid, st);
+    case 2: return launch_expand_combine_ks<2>(p, c, split_k, grid, st);
+    default: return launch_expand_combine_ks<1>(p, c, split_k, grid, st);
+    }
 }
 
 template <bool COMBINE>
@@ -619,17 +667,19 @@ void launch_sgmv_expand_t(const ExpandParams& p, const TreeParams& c, int split_
     const int R = expand_tiles_per_wg(p.M, p.N);
     if (R > 1) {
         const dim3 grid = expand_rows_grid(p.M, p.N, R);
-        if (p.r_max > 32)
-            hipLaunchKernelGGL((k_sgmv_expand_rows<2, COMBINE>), grid, dim3(256), 0, st, p, c, R, split_k);
-        else
-            hipLaunchKernelGGL((k_sgmv_expand_rows<1, COMBINE>), grid, dim3(256), 0, st, p, c, R, split_k);
+        switch (expand_steps(p.r_max)) {
+        case 4: hipLaunchKernelGGL((k_sgmv_expand_rows<4, COMBINE>), grid, dim3(256), 0, st, p, c, R, split_k); break;
+        case 2: hipLaunchKernelGGL((k_sgmv_expand_rows<2, COMBINE>), grid, dim3(256), 0, st, p, c, R, split_k); break;
+        default: hipLaunchKernelGGL((k_sgmv_expand_rows<1, COMBINE>), grid, dim3(256), 0, st, p, c, R, split_k); break;
+        }
         return;
     }
     const dim3 grid = expand_grid(p.M, p.N);
-    if (p.r_max > 32)
-        hipLaunchKernelGGL((k_sgmv_expand<2, COMBINE>), grid, dim3(256), 0, st, p, c, split_k);
-    else
-        hipLaunchKernelGGL((k_sgmv_expand<1, COMBINE>), grid, dim3(256), 0, st, p, c, split_k);
+    switch (expand_steps(p.r_max)) {
+    case 4: hipLaunchKernelGGL((k_sgmv_expand<4, COMBINE>), grid, dim3(256), 0, st, p, c, split_k); break;
+    case 2: hipLaunchKernelGGL((k_sgmv_expand<2, COMBINE>), grid, dim3(256), 0, st, p, c, split_k); break;
+    default: hipLaunchKernelGGL((k_sgmv_expand<1, COMBINE>), grid, dim3(256), 0, st, p, c, split_k); break;
+    }
 }
 
 hipError_t launch_sgmv_expand(const ExpandParams& p, hipStream_t st)

@@ -314,6 +314,8 @@ int64_t fused_grid(int64_t M, int64_t N)
 
 hipError_t launch_shrink_expand_fused(const FusedParams& p, int split_k, int waves, hipStream_t st)
 {
+    if (p.r > kFusedMaxRank)
+        return hipErrorInvalidValue;
     const dim3 grid((unsigned)fused_grid(p.M, p.N));
     if (p.r > 32)
         return launch_rt<4>(p, split_k, waves, grid, st);

@@ -7,7 +7,10 @@
 namespace lora {
 
 constexpr int kRowBlock = 16;                // tokens per matrix-core tile
-constexpr int kMaxRankTiles = 4;             // 16-wide rank tiles of a rank <= 64
+constexpr int kMaxRank = 128;                // largest adapter rank
+constexpr int kMaxRankTiles = 8;             // 16-wide rank tiles of a rank <= kMaxRank
+constexpr int kGroupTiles = 4;               // rank tiles one shrink workgroup computes, at most
+constexpr int kFusedMaxRank = 64;            // rank bound of the single-launch recompute kernel
 
 // Plan buffer: int32 header [ntiles, M, n_adapters, magic], then ntiles
 // triples (first token, token count 1..16, adapter id or -1 for tokens

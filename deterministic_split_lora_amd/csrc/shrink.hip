@@ -536,6 +536,8 @@ void launch_partial_r(const ShrinkParams& p, int waves, int groups, hipStream_t 
 template <int MODE>
 hipError_t launch_partial(const ShrinkParams& p, int waves, int rank_tiles, int group_tiles, hipStream_t st)
 {
+    if (group_tiles < 1 || group_tiles > kGroupTiles)
+        return hipErrorInvalidValue;
     const int groups = (rank_tiles + group_tiles - 1) / group_tiles;
     switch (group_tiles) {
     case 1: launch_partial_r<MODE, 1>(p, waves, groups, st); break;
@@ -646,6 +648,8 @@ void launch_multi_t(const ShrinkParams& p, int waves, int rank_tiles, dim3 grid,
 hipError_t launch_shrink_partial_multi(const ShrinkParams& p, int waves, int rank_tiles, int tiles_per_wg,
                                        hipStream_t st)
 {
+    if (rank_tiles < 1 || rank_tiles > kGroupTiles)
+        return hipErrorInvalidValue;
     const int64_t mbs = (p.M + kRowBlock - 1) / kRowBlock;
     const dim3 grid((unsigned)(((mbs + tiles_per_wg - 1) / tiles_per_wg) * p.split_k));
     if (tiles_per_wg == 2)
@@ -659,6 +663,8 @@ hipError_t launch_sgmv_shrink_partial_multi(const ShrinkParams& p, int waves, in
                                             hipStream_t st)
 {
     const int rank_tiles = (p.r_max + 15) / 16;
+    if (rank_tiles > kGroupTiles)
+        return hipErrorInvalidValue;
     // with 3-4 rank tiles, four plan tiles per workgroup do not fit in the
     // 128 registers of two workgroups per compute unit: take two
     if (tiles_per_wg == 2 || rank_tiles > 2)
@@ -697,6 +703,8 @@ hipError_t launch_stream_r(const ShrinkParams& p, int waves, int steps, int R, d
 
 bool shrink_stream_fits(int waves, int k_steps, int rank_tiles)
 {
+    if (rank_tiles < 1 || rank_tiles > kGroupTiles)
+        return false;
     const int rt = rank_tiles <= 1 ? 1 : (rank_tiles == 2 ? 2 : 4);
     return (waves == 4 || waves == 8) && (k_steps == 1 || k_steps == 2 || k_steps == 4) && rt * k_steps <= 8;
 }
@@ -732,6 +740,8 @@ hipError_t launch_shrink_partial_atomic(const ShrinkParams& p, int waves, int ra
 hipError_t launch_shrink_counted(const ShrinkParams& p, const CounterParams& c, int waves, int rank_tiles,
                                  int group_tiles, hipStream_t st)
 {
+    if (group_tiles < 1 || group_tiles > kGroupTiles)
+        return hipErrorInvalidValue;
     const int groups = (rank_tiles + group_tiles - 1) / group_tiles;
     switch (group_tiles) {
     case 1: launch_counted_r<1>(p, c, waves, groups, st); break;

@@ -47,7 +47,7 @@ namespace lora {
 
 namespace {
 
-constexpr int kHTileStride = 68;          // floats per LDS row of the h tile (64 + 4 padding)
+constexpr int kHTileStride = 132;         // floats per LDS row of the h tile (128 + 4 padding)
 constexpr int kSpinLimit = 1 << 21;       // polls before an expand workgroup gives up
 
 template <int RT, int W>
@@ -139,10 +139,11 @@ template <int RT, int W>
 void launch_rw(const ShrinkParams& p, const ExpandParams& e, const TreeParams& c, const StreamParams& q,
                dim3 grid, hipStream_t st)
 {
-    if (e.r > 32)
-        hipLaunchKernelGGL((k_shrink_expand_counted<RT, W, 2>), grid, dim3(W * 64), 0, st, p, e, c, q);
-    else
-        hipLaunchKernelGGL((k_shrink_expand_counted<RT, W, 1>), grid, dim3(W * 64), 0, st, p, e, c, q);
+    switch (expand_steps(e.r)) {
+    case 4: hipLaunchKernelGGL((k_shrink_expand_counted<RT, W, 4>), grid, dim3(W * 64), 0, st, p, e, c, q); break;
+    case 2: hipLaunchKernelGGL((k_shrink_expand_counted<RT, W, 2>), grid, dim3(W * 64), 0, st, p, e, c, q); break;
+    default: hipLaunchKernelGGL((k_shrink_expand_counted<RT, W, 1>), grid, dim3(W * 64), 0, st, p, e, c, q); break;
+    }
 }
 
 template <int RT>

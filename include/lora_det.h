@@ -44,7 +44,8 @@
  * alone.
  *
  * SUPPORTED (otherwise LORA_ERR_UNSUPPORTED / LORA_ERR_ALIGN):
- *   1 <= r <= 64;  split_k in {1, 2, 4, 8, 16};  K % (32 * split_k) == 0;
+ *   1 <= r <= 128 (lora_shrink_expand_fused: r <= 64);  split_k in {1, 2, 4, 8, 16};
+ *   K % (32 * split_k) == 0;
  *   x, A, B, y, workspace: 16-byte aligned, ld_x, ld_a, ld_b, ld_y multiples of 8;
  *   h as written by the shrinks: 4-byte aligned, any ld_h >= r;
  *   h as read by the expands: 16-byte aligned, ld_h a multiple of 4;
@@ -61,7 +62,7 @@
 extern "C" {
 #endif
 
-#define LORA_DET_ABI_VERSION 2
+#define LORA_DET_ABI_VERSION 3
 
 enum lora_status {
     LORA_OK = 0,
@@ -175,8 +176,8 @@ int lora_expand_compensated(const float* h, int64_t ld_h, const uint16_t* B, int
  * agent-scope loads, applies the same fixed pairwise tree and scale as
  * lora_shrink_splitk, writes h and resets the counter to 0.  Bit for bit the same h as lora_shrink_splitk, in
  * one launch.  No workgroup waits for another.
- * counters: int32 [lora_shrink_counter_bytes(M) / 4] (4 per 16-token block, one
- * per 16-wide rank tile), 4-byte aligned, ALL ZERO
+ * counters: int32 [lora_shrink_counter_bytes(M) / 4] (8 per 16-token block, one
+ * per 16-wide rank tile of a rank <= 128), 4-byte aligned, ALL ZERO
  * before the first call; every completed call leaves them zero again, so one
  * zero-initialised buffer serves any number of calls on one stream (not
  * concurrent calls).  workspace as for lora_shrink_splitk.  split_k == 1 needs
@@ -235,6 +236,8 @@ int lora_expand_combine(const void* workspace, size_t workspace_bytes, int32_t s
  * matrix-core chains, wave tree and split tree as lora_shrink_splitk, held in
  * registers and LDS - before expanding it, so no workgroup depends on another.
  * lora_shrink_expand runs this schedule when it is the faster one (small M).
+ * Ranks above 64 return LORA_ERR_UNSUPPORTED here (lora_shrink_expand takes
+ * another schedule for them).
  */
 /* Host only: how many kernel launches lora_shrink_expand makes for these sizes
    (1: the single-launch schedule, 2: partials then tree + expand, 0: nothing
@@ -336,7 +339,7 @@ int lora_sgmv_shrink(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_p
  * one launch with the completion-counter combine of lora_shrink_splitk_counted,
  * one counter per plan tile.  The plan must come from lora_sgmv_plan with the
  * same M and n_adapters (token ids are read from the plan).
- * counters: int32 [lora_sgmv_counter_bytes(M) / 4] (4 per possible tile), all
+ * counters: int32 [lora_sgmv_counter_bytes(M) / 4] (8 per possible tile), all
  * zero before the first call, left zero.
  */
 size_t lora_sgmv_counter_bytes(int64_t M);

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert dsl.lora_abi_version() == 2
+    assert dsl.lora_abi_version() == 3
     seen = set()
     for s in range(0, 7):
         t = dsl.lora_status_str(s)
@@ -61,7 +61,7 @@ def test_static_plan(K, S, chunk, waves, steps):
     assert p == {"split_k": S, "k_chunk": chunk, "waves": waves, "k_steps": steps,
                  "rank_tiles": 1, "row_block": 16}
     assert waves * steps * 32 == chunk and chunk * S == K
-    for r, rt in [(1, 1), (8, 1), (16, 1), (17, 2), (32, 2), (33, 3), (64, 4)]:
+    for r, rt in [(1, 1), (8, 1), (16, 1), (17, 2), (32, 2), (33, 3), (64, 4), (65, 5), (96, 6), (128, 8)]:
         assert dsl.lora_shrink_plan(K, r, S)["rank_tiles"] == rt
 
 
@@ -71,7 +71,7 @@ def test_plan_rejects():
     assert L.lora_shrink_plan(4096, 16, 3, ctypes.byref(p)) == B.LORA_ERR_UNSUPPORTED
     assert L.lora_shrink_plan(4096, 16, 32, ctypes.byref(p)) == B.LORA_ERR_UNSUPPORTED
     assert L.lora_shrink_plan(4096, 0, 8, ctypes.byref(p)) == B.LORA_ERR_UNSUPPORTED
-    assert L.lora_shrink_plan(4096, 65, 8, ctypes.byref(p)) == B.LORA_ERR_UNSUPPORTED
+    assert L.lora_shrink_plan(4096, 129, 8, ctypes.byref(p)) == B.LORA_ERR_UNSUPPORTED
     assert L.lora_shrink_plan(4000, 16, 8, ctypes.byref(p)) == B.LORA_ERR_UNSUPPORTED
     assert L.lora_shrink_plan(0, 16, 8, ctypes.byref(p)) == B.LORA_ERR_SHAPE
     assert L.lora_shrink_plan(4096, 16, 8, None) == B.LORA_ERR_NULL
@@ -118,7 +118,7 @@ def _expand(fn="lora_expand", **kw):
     (dict(ws=None), B.LORA_ERR_NULL),
     (dict(M=-1), B.LORA_ERR_SHAPE),
     (dict(r=0), B.LORA_ERR_UNSUPPORTED),
-    (dict(r=65), B.LORA_ERR_UNSUPPORTED),
+    (dict(r=129), B.LORA_ERR_UNSUPPORTED),
     (dict(S=3), B.LORA_ERR_UNSUPPORTED),
     (dict(S=32), B.LORA_ERR_UNSUPPORTED),
     (dict(K=4000, ld_x=4000, ld_a=4000), B.LORA_ERR_UNSUPPORTED),
@@ -150,7 +150,7 @@ def test_shrink_zero_rows_is_noop():
 @pytest.mark.parametrize("kw,status", [
     (dict(x=None), B.LORA_ERR_NULL),
     (dict(S=5), B.LORA_ERR_UNSUPPORTED),
-    (dict(r=100), B.LORA_ERR_UNSUPPORTED),
+    (dict(r=200), B.LORA_ERR_UNSUPPORTED),
     (dict(ld_a=8), B.LORA_ERR_SHAPE),
     (dict(A=FAKE_MIS), B.LORA_ERR_ALIGN),
 ])
@@ -164,7 +164,7 @@ def test_atomic_rejects(kw, status):
     (dict(y=None), B.LORA_ERR_NULL),
     (dict(M=-2), B.LORA_ERR_SHAPE),
     (dict(r=0), B.LORA_ERR_UNSUPPORTED),
-    (dict(r=80), B.LORA_ERR_UNSUPPORTED),
+    (dict(r=129), B.LORA_ERR_UNSUPPORTED),
     (dict(N=4092, ld_y=4096), B.LORA_ERR_UNSUPPORTED),
     (dict(ld_y=4088), B.LORA_ERR_SHAPE),
     (dict(ld_b=8), B.LORA_ERR_SHAPE),
@@ -201,7 +201,7 @@ def test_sgmv_rejects():
     assert shrink(ranks=None) == B.LORA_ERR_NULL
     assert shrink(ids=None) == B.LORA_ERR_NULL
     assert shrink(n=0) == B.LORA_ERR_SHAPE
-    assert shrink(r_max=65) == B.LORA_ERR_UNSUPPORTED
+    assert shrink(r_max=129) == B.LORA_ERR_UNSUPPORTED
     assert shrink(S=6) == B.LORA_ERR_UNSUPPORTED
     assert shrink(ld_h=32) == B.LORA_ERR_SHAPE
     assert shrink(ld_a=4092) == B.LORA_ERR_SHAPE
@@ -281,7 +281,7 @@ def test_partials_and_combine_reject():
     assert comb(ws=None) == B.LORA_ERR_NULL
     assert comb(B=None) == B.LORA_ERR_NULL
     assert comb(S=12) == B.LORA_ERR_UNSUPPORTED
-    assert comb(r=65) == B.LORA_ERR_UNSUPPORTED
+    assert comb(r=129) == B.LORA_ERR_UNSUPPORTED
     assert comb(N=12) == B.LORA_ERR_UNSUPPORTED
     assert comb(wsb=wsb - 1) == B.LORA_ERR_WORKSPACE
     assert comb(h=FAKE, ld_h=8) == B.LORA_ERR_SHAPE
@@ -323,14 +323,15 @@ def test_shrink_expand_launch_count():
 
 def test_counted_rejects():
     L = dsl.lib()
-    assert dsl.lora_shrink_counter_bytes(1) == 16
-    assert dsl.lora_shrink_counter_bytes(33) == 48
-    assert dsl.lora_sgmv_counter_bytes(33) == 528
+    # one int32 per 16-wide rank tile of a rank <= 128, per row block / per plan tile
+    assert dsl.lora_shrink_counter_bytes(1) == 32
+    assert dsl.lora_shrink_counter_bytes(33) == 96
+    assert dsl.lora_sgmv_counter_bytes(33) == 1056
     wsb = dsl.lora_shrink_workspace_bytes(4, 16, 8)
 
     def call(**kw):
         a = dict(x=FAKE, ld_x=4096, A=FAKE, ld_a=4096, h=FAKE, ld_h=16, M=4, K=4096, r=16, S=8, scale=1.0,
-                 ws=FAKE, wsb=wsb, cnt=FAKE, cb=16)
+                 ws=FAKE, wsb=wsb, cnt=FAKE, cb=32)
         a.update(kw)
         return L.lora_shrink_splitk_counted(a["x"], a["ld_x"], a["A"], a["ld_a"], a["h"], a["ld_h"], a["M"],
                                             a["K"], a["r"], a["S"], a["scale"], a["ws"], a["wsb"], a["cnt"], a["cb"],
@@ -381,7 +382,7 @@ def test_shrink_expand_counted_rejects():
     assert call(ws=None) == B.LORA_ERR_NULL
     assert call(cnt=None) == B.LORA_ERR_NULL
     assert call(S=3) == B.LORA_ERR_UNSUPPORTED
-    assert call(r=65) == B.LORA_ERR_UNSUPPORTED
+    assert call(r=129) == B.LORA_ERR_UNSUPPORTED
     assert call(N=4092) == B.LORA_ERR_UNSUPPORTED
     assert call(ld_h=8) == B.LORA_ERR_SHAPE
     assert call(M=-5) == B.LORA_ERR_SHAPE
@@ -413,7 +414,7 @@ def test_sgmv_shrink_expand_rejects():
     assert call(ws=None) == B.LORA_ERR_NULL
     assert call(n=0) == B.LORA_ERR_SHAPE
     assert call(S=3) == B.LORA_ERR_UNSUPPORTED
-    assert call(r_max=65) == B.LORA_ERR_UNSUPPORTED
+    assert call(r_max=129) == B.LORA_ERR_UNSUPPORTED
     assert call(N=6140, ld_y=6144) == B.LORA_ERR_UNSUPPORTED
     assert call(ld_y=4096) == B.LORA_ERR_SHAPE
     assert call(h=FAKE, ld_h=32) == B.LORA_ERR_SHAPE

@@ -62,6 +62,11 @@ SHRINK_CASES = [
     (17, 64, 64, 2, 1.0, "minimal K per split, S=2"),
     (1, 512, 7, 16, 2.0, "minimal K per split, S=16"),
     (33, 96, 5, 1, 1.0, "three steps on one wave (odd step count)"),
+    (20, 4096, 128, 8, 1.0, "rank 128: two groups of four rank tiles"),
+    (33, 2048, 96, 16, 2.0, "rank 96, S=16"),
+    (7, 4096, 65, 1, 1.0, "rank 65, S=1 direct"),
+    (2100, 4096, 128, 8, 1.0, "rank 128 at large M: rank groups, one row block per workgroup"),
+    (1, 8192, 112, 8, 2.0, "decode rank 112"),
 ]
 
 
@@ -75,7 +80,8 @@ def test_shrink_parity(M, K, r, S, scale, label):
     _say(f"  max err / stated tol {a:.3g}, / rounding bound {b:.3g}")
 
 
-@pytest.mark.parametrize("M,K,r,S", [(8, 1024, 8, 8), (19, 4096, 16, 8), (5, 2048, 40, 16), (33, 1024, 64, 1)])
+@pytest.mark.parametrize("M,K,r,S", [(8, 1024, 8, 8), (19, 4096, 16, 8), (5, 2048, 40, 16), (33, 1024, 64, 1),
+                                     (9, 2048, 128, 8), (18, 1024, 77, 4)])
 def test_shrink_integer_inputs_bit_exact(M, K, r, S):
     """Integer inputs with every partial sum below 2^24: any summation order is
     exact, so deterministic, atomic and split_k == 1 all equal the oracle
@@ -161,7 +167,7 @@ def test_fixed_order_combine_random_exponents(S):
         assert differs_from_fold > 0
 
 
-@pytest.mark.parametrize("M,K,r,S", [(8, 1024, 8, 8), (64, 4096, 16, 8), (7, 8192, 64, 16)])
+@pytest.mark.parametrize("M,K,r,S", [(8, 1024, 8, 8), (64, 4096, 16, 8), (7, 8192, 64, 16), (5, 4096, 128, 8)])
 def test_atomic_parity(M, K, r, S):
     _say(f"atomic shrink parity M={M} K={K} r={r} S={S}")
     c = single_adapter_case(M, K, r, 0, split_k=S, seed=3)
@@ -175,7 +181,7 @@ def test_atomic_parity(M, K, r, S):
 EXPAND_CASES = [
     (1, 16, 4096, 2.0), (16, 16, 4096, 2.0), (64, 16, 4096, 2.0), (256, 16, 4096, 2.0),
     (17, 1, 264, 2.0), (9, 8, 520, 1.0), (33, 24, 1000, 2.0), (5, 40, 4096, 0.5), (20, 64, 6144, 2.0),
-    (3, 37, 8, 2.0),
+    (3, 37, 8, 2.0), (37, 128, 1032, 2.0), (6, 65, 264, 1.0), (300, 100, 2048, 2.0), (1, 128, 4096, 2.0),
 ]
 
 
@@ -198,7 +204,7 @@ def test_expand_parity(M, r, N, scale):
     t.cuda.synchronize()
     got = bf16_from_gpu(yg)
     yo, e, ab = oracle.expand(h, B, y, scale)
-    frac = check_expand(got, yo, e, ab, y, f"M={M} r={r} N={N}")
+    frac = check_expand(got, yo, e, ab, y, f"M={M} r={r} N={N}", r=r)
     _say(f"  fraction differing from the correctly rounded value: {frac:.2e}")
 
 
@@ -477,7 +483,7 @@ def _check_sgmv(c, h, y, rows, label):
         check_shrink(h[i:i + 1, :r], c.x[i:i + 1], c.As[a], float(c.scales[a]),
                      dsl.lora_shrink_plan(c.K, r, c.split_k), f"{label} row {i}")
     yo, e, ab = oracle.sgmv_expand(h[rows], c.Bs, c.ranks, c.scales, c.ids[rows], c.y[rows])
-    return check_expand(y[rows], yo, e, ab, c.y[rows], label)
+    return check_expand(y[rows], yo, e, ab, c.y[rows], label, r=int(c.r_max))
 
 
 def test_sgmv_fused_qkv_parity():
@@ -500,11 +506,32 @@ def test_sgmv_mixed_ranks_and_invalid_ids():
     _check_sgmv(c, h, y, list(range(M)), "sgmv mixed")
 
 
+def test_sgmv_ranks_above_64():
+    """Ranks 65..128 next to small ones (r_max 128: two groups of four rank
+    tiles in the shrink, four matrix-core steps in the expand), -1 and
+    out-of-range ids; at a small M and at a large one that walks several
+    tiles per expand workgroup."""
+    ranks = [128, 65, 8, 100, 16, 96]
+    for M, K, N, S in ((300, 2048, 520, 8), (2100, 1024, 4104, 4)):
+        rng = np.random.default_rng(M)
+        ids = np.empty(M, np.int32)
+        pos = 0
+        while pos < M:
+            run = int(rng.integers(1, 200))
+            ids[pos:pos + run] = rng.choice([-1, 0, 1, 2, 3, 4, 5, 11])
+            pos += run
+        c = sgmv_case(M, K, N, ranks, 0, 0, S, seed=M, tag=f"r128_{M}", ids=ids)
+        _say(f"sgmv ranks up to 128: M={M} K={K} N={N} S={S}")
+        h, y, _ = _sgmv_gpu(c)
+        rows = list(range(M)) if M <= 300 else sorted(rng.choice(M, 60, replace=False).tolist())
+        _check_sgmv(c, h, y, rows, f"sgmv r<=128 M={M}")
+
+
 def test_sgmv_equals_single_adapter_bitwise():
     """All tokens on one adapter: the multi-adapter path must reproduce the
     single-adapter calls bit for bit (same per-token arithmetic)."""
     t = torch()
-    for r in (16, 64):
+    for r in (16, 64, 128):
         M, K, N, S = 77, 4096, 1024, 8
         c = sgmv_case(M, K, N, [r], 0, 0, S, seed=2, tag=f"one{r}", ids=np.zeros(M, np.int32))
         h, y, (As, Bs) = _sgmv_gpu(c)
@@ -551,7 +578,9 @@ def test_sgmv_prefill_full_size_sampled():
                                        (37, 8192, 64, 1032, 16), (5, 1024, 8, 512, 1), (70, 2048, 40, 264, 4),
                                        (3, 3072, 1, 8, 2), (64, 14336, 32, 4096, 8), (65, 4096, 24, 1000, 8),
                                        (9, 1024, 33, 520, 4), (2, 16384, 64, 512, 16),
-                                       (300, 2048, 64, 8200, 16), (40, 1024, 24, 16384, 8)])
+                                       (300, 2048, 64, 8200, 16), (40, 1024, 24, 16384, 8),
+                                       (1, 4096, 128, 4096, 8), (20, 1024, 96, 1032, 16),
+                                       (300, 2048, 128, 8200, 16), (33, 2048, 72, 264, 1)])
 def test_shrink_expand_fused_bitwise(M, K, r, N, S):
     """Every schedule of the deterministic shrink + expand - lora_shrink_splitk
     then lora_expand (three launches), lora_shrink_partials then
@@ -588,9 +617,14 @@ def test_shrink_expand_fused_bitwise(M, K, r, N, S):
     dsl.lora_expand_combine(ws2, Bg, y4, S, 1.0, 2.0, h=h4, r=r)
     h5 = t.full((M, r), float("nan"), dtype=t.float32, device="cuda")
     y5 = bf16_to_gpu(c.y)
-    dsl.lora_shrink_expand_fused(xg, Ag, Bg, y5, S, 1.0, 2.0, h=h5)
     y6 = bf16_to_gpu(c.y)
-    dsl.lora_shrink_expand_fused(xg, Ag, Bg, y6, S, 1.0, 2.0)
+    if r <= 64:
+        dsl.lora_shrink_expand_fused(xg, Ag, Bg, y5, S, 1.0, 2.0, h=h5)
+        dsl.lora_shrink_expand_fused(xg, Ag, Bg, y6, S, 1.0, 2.0)
+    else:                                          # the recompute kernel stops at rank 64
+        with pytest.raises(RuntimeError):
+            dsl.lora_shrink_expand_fused(xg, Ag, Bg, y5, S, 1.0, 2.0, h=h5)
+        h5, y5, y6 = h2, y2, y3
     # one launch with arrival counters, twice on the same counters
     cnt = t.zeros(dsl.lora_shrink_expand_counter_bytes(M) // 4, dtype=t.int32, device="cuda")
     h7 = t.full((M, r), float("nan"), dtype=t.float32, device="cuda")
@@ -607,7 +641,7 @@ def test_shrink_expand_fused_bitwise(M, K, r, N, S):
     hh = h2.cpu().numpy()
     check_shrink(hh, c.x, c.A, 1.0, dsl.lora_shrink_plan(K, r, S), "fused h")
     yo, e, ab = oracle.expand(hh, c.B, c.y, 2.0)
-    check_expand(bf16_from_gpu(y2), yo, e, ab, c.y, "fused y")
+    check_expand(bf16_from_gpu(y2), yo, e, ab, c.y, "fused y", r=r)
 
 
 def test_graph_capture_replays_match_eager():
@@ -743,7 +777,8 @@ def test_batch_invariance_across_schedule_switch():
 @pytest.mark.parametrize("M,K,r,S", [(1, 4096, 16, 8), (8, 1024, 8, 8), (64, 4096, 16, 8), (256, 4096, 16, 8),
                                      (37, 8192, 64, 16), (100, 2048, 40, 4), (19, 14336, 32, 8), (5, 1024, 5, 2),
                                      (40, 4096, 16, 1), (1100, 2048, 40, 8), (4100, 1024, 64, 8),
-                                     (4100, 2048, 16, 8), (2000, 1024, 24, 16)])
+                                     (4100, 2048, 16, 8), (2000, 1024, 24, 16), (37, 4096, 128, 8),
+                                     (2100, 1024, 100, 8)])
 def test_shrink_counted_bitwise(M, K, r, S):
     """lora_shrink_splitk_counted (one launch, the last-arriving split
     combines, one row block per workgroup) gives lora_shrink_splitk's bits
@@ -803,7 +838,7 @@ def test_shrink_counted_in_graph_replays():
         del junk
 
 
-@pytest.mark.parametrize("case", ["qkv", "mixed", "decode_probe", "prefill"])
+@pytest.mark.parametrize("case", ["qkv", "mixed", "decode_probe", "prefill", "rank128"])
 def test_sgmv_counted_bitwise(case):
     """lora_sgmv_shrink_counted gives lora_sgmv_shrink's bits (rows without an
     adapter and columns beyond a rank zeroed) in one launch; in the prefill
@@ -820,6 +855,11 @@ def test_sgmv_counted_bitwise(case):
         c = sgmv_case(2048, 2048, 64, [8, 16, 32, 64, 5, 37, 64, 16], 0, 0, 16, seed=3, tag="cp", ids=ids)
     elif case == "qkv":
         c = sgmv_case(512, 4096, 64, [64, 64, 64, 64], 1, 64, 8, seed=0, tag="cq")
+    elif case == "rank128":
+        rng = np.random.default_rng(8)
+        ids = rng.choice([-1, 0, 1, 2, 3], 150).astype(np.int32)
+        ids[20:90] = 0
+        c = sgmv_case(150, 2048, 64, [128, 72, 16, 100], 0, 0, 8, seed=4, tag="c128", ids=ids)
     elif case == "mixed":
         rng = np.random.default_rng(4)
         ids = rng.choice([-1, 0, 1, 2, 3, 17], 333).astype(np.int32)
@@ -992,7 +1032,7 @@ def test_shrink_stream_rows_bitwise(M, K, r, S):
 # ---------------------------------------------------------------------------
 # expands that walk several 16-token tiles per workgroup (large M x N)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("r", [5, 16, 37, 64])
+@pytest.mark.parametrize("r", [5, 16, 37, 64, 100, 128])
 def test_expand_large_m_tiles_bitwise(r):
     """At M x N large enough that lora_expand walks several tiles per
     workgroup (B kept in registers, h staged in LDS), every row equals the
@@ -1022,7 +1062,7 @@ def test_expand_large_m_tiles_bitwise(r):
         assert np.array_equal(bf16_from_gpu(ys), got[r0:r0 + n]), f"rows {r0}.."
     rows = sorted(set([0, 15, 16, 2047, 4095, 4096, 4099] + rng.choice(M, 24, replace=False).tolist()))
     yo, e, ab = oracle.expand(h[rows, :r], Bm, y[rows], 2.0)
-    check_expand(got[rows], yo, e, ab, y[rows], f"large-M expand r={r}")
+    check_expand(got[rows], yo, e, ab, y[rows], f"large-M expand r={r}", r=r)
 
 
 def test_sgmv_expand_large_m_tiles_bitwise():
@@ -1146,7 +1186,7 @@ def test_expand_compensated_golden_bitwise():
             assert np.array_equal(got, np.array(c[key])), (c["name"], key, got)
 
 
-@pytest.mark.parametrize("M,r,N", [(1, 16, 4096), (37, 5, 1032), (64, 64, 520), (300, 33, 2048)])
+@pytest.mark.parametrize("M,r,N", [(1, 16, 4096), (37, 5, 1032), (64, 64, 520), (300, 33, 2048), (40, 128, 1032)])
 def test_expand_compensated_parity(M, r, N):
     """Random fp32 h (full 24-bit significands): the compensated expand agrees
     with the oracle's compensated definition within 1 bf16 ulp (plus the fp32
@@ -1169,7 +1209,7 @@ def test_expand_compensated_parity(M, r, N):
     t.cuda.synchronize()
     gc, gp = bf16_from_gpu(yc), bf16_from_gpu(yp)
     yo, e, ab = oracle.expand_compensated(h[:, :r], Bm, y, 2.0)
-    check_expand(gc, yo, e, ab, y, f"compensated M={M} r={r}")
+    check_expand(gc, yo, e, ab, y, f"compensated M={M} r={r}", r=r)
     # correctly rounded product with the fp32 h itself (no conversion of h)
     exact = 2.0 * (h[:, :r].astype(np.float64) @ oracle.bf16_to_f64(Bm).T)
     want = oracle.bf16_rne(exact)
@@ -1181,7 +1221,7 @@ def test_expand_compensated_parity(M, r, N):
 # ---------------------------------------------------------------------------
 # multi-adapter shrink + expand in two launches (expand reads the workspace)
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("case", ["qkv", "mixed", "decode", "large", "large_s16"])
+@pytest.mark.parametrize("case", ["qkv", "mixed", "decode", "large", "large_s16", "rank128"])
 def test_sgmv_shrink_expand_bitwise(case):
     """lora_sgmv_shrink_expand gives the h and y bits of lora_sgmv_shrink
     (with the shrink scales) followed by lora_sgmv_expand (with the expand
@@ -1202,6 +1242,8 @@ def test_sgmv_shrink_expand_bitwise(case):
                       ids=np.arange(24, dtype=np.int32))
     elif case == "large":
         c = sgmv_case(4100, 1024, 4104, [8, 16, 32, 64, 5, 40], 16, 300, 4, seed=14, tag="se_l")
+    elif case == "rank128":
+        c = sgmv_case(1100, 1024, 2056, [128, 8, 65, 96], 1, 200, 8, seed=16, tag="se_r")
     else:                                          # 17 column blocks x 16 splits: tree kernel, then expand
         c = sgmv_case(4100, 1024, 4104, [8, 16, 32, 64, 5, 40], 16, 300, 16, seed=15, tag="se_l16")
     _say(f"sgmv shrink+expand {case} M={c.M} N={c.N}")
@@ -1247,4 +1289,4 @@ def test_sgmv_shrink_expand_bitwise(case):
         check_shrink(hh[i:i + 1, :r], c.x[i:i + 1], c.As[a], float(sh[a]),
                      dsl.lora_shrink_plan(c.K, r, c.split_k), f"{case} h row {i}")
         yo, e, ab = oracle.expand(hh[i:i + 1, :r], c.Bs[a], c.y[i:i + 1], float(ex[a]))
-        check_expand(g1[i:i + 1], yo, e, ab, c.y[i:i + 1], f"{case} y row {i}")
+        check_expand(g1[i:i + 1], yo, e, ab, c.y[i:i + 1], f"{case} y row {i}", r=r)
