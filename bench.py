@@ -21,7 +21,9 @@ Also reported: per-batch-size numbers, the roofline of the dominant kernel
 the hardware counters recorded for it when its sources are unchanged since),
 two decode bandwidth probes (32 and 128 tokens, each with its own rank-64
 adapter, hidden 8192, multi-adapter shrink), device-copy ceilings at the
-probes' sizes, and the CPU oracle timed on the host cores.
+probes' sizes, identical-input replay statistics of the deterministic and
+atomic pipelines (1000 launches per batch size), and the CPU oracle timed on
+the host cores.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
     python bench.py --counters      # eager pass for rocprofv3 --pmc runs
@@ -174,7 +176,9 @@ class Bench:
     def time_graphs(self, graphs, replays, warmup):
         t = self.t
         n = len(graphs)
-        for i in range(warmup):
+        # the warm-up replays every graph at least once, so the timed region
+        # never meets an input copy (or a graph) for the first time
+        for i in range(max(warmup, n)):
             graphs[i % n].replay()
         t.cuda.synchronize()
         e0, e1 = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
@@ -351,6 +355,67 @@ def launch_floor(args):
     empty = _time_rotating(lambda st: torch.cuda._sleep(0), sets, args)
     one_wg = _time_rotating(lambda st: st["t"].zero_(), sets, args)
     return {"empty_kernel_us": round(empty, 3), "one_workgroup_kernel_us": round(one_wg, 3)}
+
+
+def replay_variability(args, repeats=1000):
+    """Identical-input replay (the pages' experiment that finds 97.61% of
+    atomic Split-K=8 shrink comparisons differing): at the q_proj shape, each
+    batch size's shrink is launched `repeats` times on the same inputs, the
+    deterministic pipeline and the atomic contrast alike, and every launch's
+    fp32 h (and the bf16 y its expand produces) is compared bit for bit with
+    the first launch's.  Reported: fraction of comparisons with any differing
+    element, fraction of differing elements, mean and max |difference| over
+    the differing elements, distinct outputs."""
+    import torch
+    import deterministic_split_lora_amd as dsl
+    from synth import single_adapter_case
+    dev = torch.device("cuda:0")
+    out = {"workload": f"q_proj shape (K={K_HID}, r={RANK}, N={N_OUT}, Split-K {SPLIT}, scale {SCALE}), "
+                       f"{repeats} launches per batch size on identical inputs, each compared with launch 0"}
+
+    def stats(H, ref):
+        """H: [n, ...] outputs as raw bits; ref: the same as values (float64)."""
+        n = H.shape[0]
+        flat = H.reshape(n, -1)
+        diff = flat[1:] != flat[0:1]
+        per = diff.any(dim=1)
+        vals = ref.reshape(n, -1)
+        ad = (vals[1:] - vals[0:1]).abs()[diff]
+        return {"comparisons": n - 1, "differing_comparisons": int(per.sum()),
+                "differing_comparisons_pct": round(100.0 * float(per.float().mean()), 2),
+                "differing_elements_pct": round(100.0 * float(diff.float().mean()), 4),
+                "mean_abs_diff": float(ad.mean()) if ad.numel() else 0.0,
+                "max_abs_diff": float(ad.max()) if ad.numel() else 0.0,
+                "distinct_outputs": distinct(flat)}
+
+    def distinct(flat):
+        """Distinct rows, by a 64-bit multiplicative hash of each row's bits."""
+        g = torch.Generator(device=flat.device).manual_seed(1)
+        w = torch.randint(1, 2 ** 62, (flat.shape[1],), generator=g, device=flat.device, dtype=torch.int64) | 1
+        hsh = (flat.to(torch.int64) * w).sum(dim=1)
+        return int(torch.unique(hsh).numel())
+
+    for M in M_LIST:
+        c = single_adapter_case(M, K_HID, RANK, N_OUT, SPLIT, SCALE, seed=0)
+        x, A, B, y0 = (gpu_tensor(a, dev) for a in (c.x, c.A, c.B, c.y))
+        ws = torch.empty(dsl.lora_shrink_workspace_bytes(M, RANK, SPLIT), dtype=torch.uint8, device=dev)
+        row = {}
+        for name in ("deterministic", "atomic"):
+            H = torch.empty((repeats, M, RANK), dtype=torch.float32, device=dev)
+            Y = torch.empty((repeats, M, N_OUT), dtype=torch.bfloat16, device=dev)
+            for i in range(repeats):
+                if name == "atomic":
+                    dsl.lora_shrink_splitk_atomic(x, A, H[i], SPLIT, 1.0)
+                else:
+                    dsl.lora_shrink_splitk(x, A, H[i], ws, SPLIT, 1.0)
+                Y[i].copy_(y0)
+                dsl.lora_expand(H[i], B, Y[i], SCALE)
+            torch.cuda.synchronize()
+            row[name] = {"h_fp32": stats(H.view(torch.int32), H.double()),
+                         "y_bf16": stats(Y.view(torch.int16), Y.double())}
+            del H, Y
+        out[f"M={M}"] = row
+    return out
 
 
 def gpu_tensor(a, dev):
@@ -673,7 +738,7 @@ def _time_rotating(call, sets, args):
             for q in range(per_graph):
                 call(sets[(c0 + q) % copies])
         graphs.append(gr)
-    for i in range(max(2, args.warmup // per_graph)):
+    for i in range(max(2, args.warmup // per_graph, len(graphs))):
         graphs[i % len(graphs)].replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -709,6 +774,7 @@ def cpu_baseline(seconds: float):
 
 # Workloads bench.py can time on their own (--only).
 ONLY = {
+    "replay": replay_variability,
     "sgmv_qkv": lambda a: sgmv_bench(a, "b3", 512, 4096, 6144, [64] * 4, 1, 64, 8),
     "sgmv_prefill": lambda a: sgmv_bench(a, "b5", 4096, 8192, 28672, [8, 16, 32, 64] * 8, 32, 512, 16),
     "decode_probe": lambda a: decode_probe(a, 128),
@@ -747,7 +813,7 @@ def main():
     b = Bench(args)
     res = b.run()
     log("bench: main timing done")
-    probe = wide = roof = floor = extra = None
+    probe = wide = roof = floor = extra = replay = None
     if not args.no_probe:
         probe = decode_probe(args, 32)
         wide = decode_probe(args, 128)
@@ -755,6 +821,8 @@ def main():
         roof = copy_roofline(args, [avg, probe["bytes"], wide["bytes"], 64 << 20])
         floor = launch_floor(args)
         log("bench: probes done")
+        replay = replay_variability(args)
+        log("bench: replay variability done")
     if not args.no_configs:
         extra = {"shrink_only_m8_k1024_r8": shrink_only_bench(args)}
         log("bench: shrink-only shape done")
@@ -801,6 +869,7 @@ def main():
         "decode_bandwidth_probe_wide": wide,
         "copy_roofline": roof,
         "launch_floor": floor,
+        "replay_variability": replay,
         "other_shapes": extra,
         "device": torch.cuda.get_device_name(0),
     }
