@@ -778,6 +778,8 @@ ONLY = {
     "sgmv_qkv": lambda a: sgmv_bench(a, "b3", 512, 4096, 6144, [64] * 4, 1, 64, 8),
     "sgmv_prefill": lambda a: sgmv_bench(a, "b5", 4096, 8192, 28672, [8, 16, 32, 64] * 8, 32, 512, 16),
     "decode_probe": lambda a: decode_probe(a, 128),
+    "decode_probe32": lambda a: decode_probe(a, 32),
+    "batch_sweep": batch_sweep_bench,
 }
 
 

@@ -39,6 +39,23 @@ __device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t* p)
     return __builtin_bit_cast(bf16x8, *(const global_u32x4*)(p));
 }
 
+// Raw buffer resource over `bytes` bytes from `base` (stride 0: offsets are
+// byte offsets; stores at or past `bytes` are dropped by the hardware), and a
+// 4-byte store through it at a per-lane byte offset.  The resource lives in
+// scalar registers.
+typedef __amdgpu_buffer_rsrc_t BufferRsrc;
+constexpr int kBufferRsrcWord3 = 0x00020000;   // raw 32-bit data, CDNA buffer format
+
+__device__ __forceinline__ BufferRsrc buffer_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferRsrcWord3);
+}
+
+__device__ __forceinline__ void buffer_store_f32(float v, BufferRsrc r, uint32_t byte_offset)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, (int)byte_offset, 0, 0);
+}
+
 // 8 bf16 starting at p of which only the first n exist (n < 8 only at a
 // rank edge that is not a multiple of 8); missing ones read as +0 so that
 // padded reduction slots contribute exact zeros.

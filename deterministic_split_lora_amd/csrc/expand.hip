@@ -587,16 +587,29 @@ inline dim3 expand_grid(int64_t M, int64_t N)
     return dim3((unsigned)(((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols)));
 }
 
-// Tiles per workgroup for the expands: one while the one-tile grid leaves
-// fewer than ~4096 workgroups (small and medium M: no reuse is needed and the
-// parallelism is), else enough to bring the grid down to ~2048, at most 16.
-int expand_tiles_per_wg(int64_t M, int64_t N)
+// Tiles per workgroup for the expands, from the one-tile grid size and the
+// rank (any choice gives the same bits).  One tile per workgroup keeps small
+// grids parallel; walking tiles saves the per-workgroup B loads (16 r bytes
+// per column) and moves y row-contiguously through LDS.  The more B a
+// workgroup holds, the more tiles pay: measured on MI355X (cold inputs),
+// ranks <= 32 are fastest with 2 tiles once the grid exceeds ~1024
+// workgroups (4096 x 28672 at rank 16: 88.9 us against 115 us for one tile
+// and 106 us for 16), ranks <= 64 with 2 from ~512 workgroups, 3 from ~1536
+// and 6 from ~3072 (rank 64, 4096 x 4096: 19.0 us against 34.1 us for one
+// tile), ranks <= 128 with up to 8.
+int expand_tiles_per_wg(int64_t M, int64_t N, int r)
 {
     const int64_t wgs = ((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols);
-    if (wgs < 4096)
+    const int steps = expand_steps(r);
+    if (steps == 1)
+        return wgs <= 1024 ? 1 : 2;
+    if (wgs < 512)
         return 1;
-    const int64_t R = wgs / 2048;
-    return (int)(R > 16 ? 16 : R);
+    if (wgs < 1536)
+        return 2;
+    if (wgs < 3072)
+        return steps == 2 ? 3 : 4;
+    return steps == 2 ? 6 : 8;
 }
 
 inline dim3 expand_rows_grid(int64_t M, int64_t N, int R)
@@ -616,10 +629,10 @@ hipError_t launch_expand_compensated(const ExpandParams& p, hipStream_t st)
     return hipGetLastError();
 }
 
-hipError_t launch_expand(const ExpandParams& p, hipStream_t st)
+hipError_t launch_expand(const ExpandParams& p, hipStream_t st, int tiles_per_wg)
 {
     dim3 block(256);
-    const int R = expand_tiles_per_wg(p.M, p.N);
+    const int R = tiles_per_wg > 0 ? tiles_per_wg : expand_tiles_per_wg(p.M, p.N, p.r);
     if (R > 1) {
         const dim3 grid = expand_rows_grid(p.M, p.N, R);
         switch (expand_steps(p.r)) {
@@ -661,10 +674,29 @@ hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int
     }
 }
 
-template <bool COMBINE>
-void launch_sgmv_expand_t(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st)
+// Tiles per workgroup for the multi-adapter expands.  Measured on MI355X:
+// the plain expand takes the single-adapter choice up to ~4096 one-tile
+// workgroups and up to 16 tiles beyond (4096 x 28672, 32 adapters of ranks 8
+// to 64: 16 tiles 106 us, 6 tiles 108 us, 2 tiles 119 us); the expand that
+// also evaluates each row's Split-K tree keeps one tile per workgroup below
+// ~4096 workgroups, where the staging threads' tree over the workspace would
+// serialise more of it (512 x 6144, rank 64, Split-K 8: 2 tiles 28.3 us per
+// shrink + expand against 23.5 us).
+static int sgmv_tiles_per_wg(int64_t M, int64_t N, int r_max, bool combine)
 {
-    const int R = expand_tiles_per_wg(p.M, p.N);
+    const int64_t wgs = ((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols);
+    const int wide = wgs < 4096 ? 1 : (int)(wgs / 2048 > 16 ? 16 : wgs / 2048);
+    if (combine)
+        return wide;
+    const int single = expand_tiles_per_wg(M, N, r_max);
+    return single > wide ? single : wide;
+}
+
+template <bool COMBINE>
+void launch_sgmv_expand_t(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st, int R = 0)
+{
+    if (R <= 0)
+        R = sgmv_tiles_per_wg(p.M, p.N, p.r_max, COMBINE);
     if (R > 1) {
         const dim3 grid = expand_rows_grid(p.M, p.N, R);
         switch (expand_steps(p.r_max)) {
@@ -682,9 +714,9 @@ void launch_sgmv_expand_t(const ExpandParams& p, const TreeParams& c, int split_
     }
 }
 
-hipError_t launch_sgmv_expand(const ExpandParams& p, hipStream_t st)
+hipError_t launch_sgmv_expand(const ExpandParams& p, hipStream_t st, int tiles_per_wg)
 {
-    launch_sgmv_expand_t<false>(p, TreeParams{}, 1, st);
+    launch_sgmv_expand_t<false>(p, TreeParams{}, 1, st, tiles_per_wg);
     return hipGetLastError();
 }
 

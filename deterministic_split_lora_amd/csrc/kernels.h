@@ -161,10 +161,12 @@ hipError_t launch_sgmv_shrink_counted(const ShrinkParams& p, const CounterParams
 hipError_t launch_splitk_tree(const TreeParams& p, int split_k, bool sgmv, hipStream_t st);
 hipError_t launch_fill_zero(float* h, int64_t ld_h, int64_t M, int ncols, hipStream_t st);
 
-hipError_t launch_expand(const ExpandParams& p, hipStream_t st);
+// tiles_per_wg: 16-token tiles per expand workgroup, 0 = expand_tiles_per_wg(M, N)
+// (any value gives the same bits).
+hipError_t launch_expand(const ExpandParams& p, hipStream_t st, int tiles_per_wg = 0);
 hipError_t launch_expand_compensated(const ExpandParams& p, hipStream_t st);
 hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st);
-hipError_t launch_sgmv_expand(const ExpandParams& p, hipStream_t st);
+hipError_t launch_sgmv_expand(const ExpandParams& p, hipStream_t st, int tiles_per_wg = 0);
 hipError_t launch_sgmv_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st);
 hipError_t launch_shrink_expand_fused(const FusedParams& p, int split_k, int waves, hipStream_t st);
 hipError_t launch_shrink_expand_counted(const ShrinkParams& p, const ExpandParams& e, const TreeParams& c,
@@ -176,8 +178,9 @@ hipError_t launch_sgmv_plan(const int32_t* ids, int64_t M, int32_t n_adapters, i
 // Columns of y one expand workgroup covers (4 waves x 64).
 constexpr int kExpandCols = 256;
 
-// 16-token tiles one expand workgroup walks (1: one tile per workgroup).
-int expand_tiles_per_wg(int64_t M, int64_t N);
+// 16-token tiles one expand workgroup walks (1: one tile per workgroup) for
+// rank (bound) r.
+int expand_tiles_per_wg(int64_t M, int64_t N, int r);
 
 // XCDs of an MI355X; consecutive workgroup ids of a launch go to different ones.
 constexpr int kXcds = 8;

@@ -276,6 +276,10 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_partial_multi(ShrinkP
 template <int RT, int W, int STEPS, bool SGMV>
 __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int R)
 {
+    // x buffers in rotation: blocks are loaded NB - 1 = 2 ahead (measured on
+    // MI355X: loading 3 ahead makes the 4096 x 8192 multi-adapter partials no
+    // faster)
+    constexpr int NB = 3;
     constexpr int RS = 16 * RT + 4;               // padded LDS row stride (floats)
     __shared__ __align__(16) float red[2][W * 16 * RS];
     __shared__ int32_t tl[3 * kStreamMaxRows];    // the item's plan entries
@@ -292,7 +296,10 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
     // for the x loads in flight
     auto tile = [&](int64_t j, int u, int64_t& row0, int& nrows, int& a) {
         if constexpr (SGMV) {
-            const int32_t* t = tl + 3 * u;
+            // uniform by construction: scalar registers
+            const int32_t t[3] = {__builtin_amdgcn_readfirstlane(tl[3 * u]),
+                                  __builtin_amdgcn_readfirstlane(tl[3 * u + 1]),
+                                  __builtin_amdgcn_readfirstlane(tl[3 * u + 2])};
             const bool ok = tile_ok(t, p.M, p.n_adapters);
             row0 = ok ? t[0] : 0;
             nrows = ok ? t[1] : 0;
@@ -303,6 +310,30 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
             a = 0;
         }
     };
+    // this thread's elements of a block's 16 x 16 RT partial tile: row, column
+    // and byte offset inside the block's workspace rows (erow = 16 for the
+    // threads left over: never stored).  A workspace store's source registers
+    // must not be reused until the store has completed, which the compiler
+    // enforces by waiting for every memory operation issued before it; with
+    // offsets that stay put and the block's base in scalar registers only the
+    // stored value is such a register.
+    constexpr int EPT = (16 * 16 * RT + W * kWave - 1) / (W * kWave);
+    int erow[EPT], ecol[EPT];
+    uint32_t voff[EPT];
+#pragma unroll
+    for (int q = 0; q < EPT; ++q) {
+        const int e = (int)threadIdx.x + q * W * kWave;
+        erow[q] = e < 16 * 16 * RT ? e / (16 * RT) : 16;
+        ecol[q] = e % (16 * RT);
+        voff[q] = (uint32_t)((erow[q] * p.ld_out + ecol[q]) * 4);
+    }
+    // registers of the values stored by the NB unrolled blocks (see block)
+    float kept[NB][EPT];
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int q = 0; q < EPT; ++q)
+            kept[b][q] = 0.0f;
     uint32_t k = 0;                               // blocks walked: selects the LDS buffer
     for (uint32_t it = blockIdx.x; it < items; it += gridDim.x) {
         const int s = (int)(it % S);
@@ -325,7 +356,7 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
             for (int t = 0; t < STEPS; ++t)
                 dst[t] = load_bf16x8(xp + t * kKStep);
         };
-        bf16x8 x0[STEPS], x1[STEPS], x2[STEPS];
+        bf16x8 xb[NB][STEPS];
         bf16x8 aop[STEPS][RT];
         // runs of blocks with one adapter: the run's first two x blocks and
         // its A chunk are loaded at the start of the run and waited for there,
@@ -351,8 +382,9 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
             }
             const int ra = a < 0 ? 0 : (SGMV ? adapter_rank(p, a) : p.r);
             const int nrt = (ra + 15) / 16 < RT ? (ra + 15) / 16 : RT;
-            xload(u, x0);
-            xload(u + 1 < u1 ? u + 1 : u, x1);
+#pragma unroll
+            for (int q = 0; q + 1 < NB; ++q)
+                xload(u + q < u1 ? u + q : u1 - 1, xb[q]);
             if (ra > 0) {
                 const uint16_t* A = SGMV ? p.A_ptrs[a] : p.A;
 #pragma unroll
@@ -367,58 +399,74 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
                 }
             }
             __builtin_amdgcn_s_waitcnt(0);
-            // the run's i-th block uses buffer i % 3 and loads block i + 2
-            // into buffer (i + 2) % 3 (loop unrolled by three: no register is
-            // copied while its load is in flight)
-            auto block = [&](const bf16x8 (&xc)[STEPS], bf16x8 (&xn)[STEPS]) {
-                xload(u + 2 < u1 ? u + 2 : u1 - 1, xn);   // unconditional: no branch-dependent buffer
+            // the run's i-th block uses buffer i % NB and loads block
+            // i + NB - 1 into buffer (i + NB - 1) % NB (loop unrolled by NB:
+            // no register is copied while its load is in flight).  The matrix-core steps run
+            // on every path - also for rank tiles past the adapter's rank and
+            // for blocks without rows, whose results are never stored - so
+            // that every buffer is known to have landed once its block is
+            // done and its registers can be reused without draining the
+            // loads in flight.
+            auto block = [&](const bf16x8 (&xc)[STEPS], bf16x8 (&xn)[STEPS], float (&kept)[EPT]) {
+                xload(u + NB - 1 < u1 ? u + NB - 1 : u1 - 1, xn);   // unconditional: no branch-dependent buffer
                 tile(c0 + u, u, row0, nrows, a);
                 const bool on = nrows > 0 && ra > 0;
                 float* rb = red[k & 1];
+                f32x4 acc[RT];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int t = 0; t < STEPS; ++t)
+                        acc[rt] = mfma_16x16x32(xc[t], aop[t][rt], acc[rt]);
+                }
                 if (on) {
 #pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) {
-                        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-                        if (rt < nrt) {
-#pragma unroll
-                            for (int t = 0; t < STEPS; ++t)
-                                acc = mfma_16x16x32(xc[t], aop[t][rt], acc);
-                        }
+                    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                         for (int v = 0; v < 4; ++v)
-                            rb[(wave * 16 + 4 * g + v) * RS + rt * 16 + li] = acc[v];
-                    }
+                            rb[(wave * 16 + 4 * g + v) * RS + rt * 16 + li] = acc[rt][v];
                 }
                 __syncthreads();
                 if (on) {
                     const int ncols = ra < 16 * RT ? ra : 16 * RT;
-                    for (int e = threadIdx.x; e < 16 * 16 * RT; e += W * kWave) {
-                        const int row = e / (16 * RT);
-                        const int col = e - row * (16 * RT);
-                        if (row < nrows && col < ncols) {
+                    // the block's 16 workspace rows, addressed from scalar
+                    // registers; the per-lane offsets never change
+                    const BufferRsrc ws = buffer_rsrc(p.out + (int64_t)s * p.split_stride + row0 * p.ld_out,
+                                                      (uint32_t)(16 * p.ld_out * 4));
+#pragma unroll
+                    for (int q = 0; q < EPT; ++q) {
+                        const bool mine = erow[q] < nrows && ecol[q] < ncols;
+                        float val = 0.0f;
+                        if (mine) {
                             float v[W];
 #pragma unroll
                             for (int w = 0; w < W; ++w)
-                                v[w] = rb[(w * 16 + row) * RS + col];
-                            p.out[(int64_t)s * p.split_stride + (row0 + row) * p.ld_out + col] =
-                                pairwise_tree<W>(v);
+                                v[w] = rb[(w * 16 + erow[q]) * RS + ecol[q]];
+                            val = pairwise_tree<W>(v);
                         }
+                        // the value this slot stored NB blocks ago stays
+                        // in its register until here; the new one is stored
+                        // from the register it then keeps (the empty asm
+                        // statements pin both)
+                        asm volatile("" : "+v"(kept[q]));
+                        kept[q] = val;
+                        asm volatile("" : "+v"(kept[q]));
+                        if (mine)
+                            buffer_store_f32(kept[q], ws, voff[q]);
                     }
                 }
             };
-            for (;;) {
-                block(x0, x2);
-                ++k;
-                if (++u >= u1)
-                    break;
-                block(x1, x0);
-                ++k;
-                if (++u >= u1)
-                    break;
-                block(x2, x1);
-                ++k;
-                if (++u >= u1)
-                    break;
+            bool more = true;
+            while (more) {
+#pragma unroll
+                for (int q = 0; q < NB; ++q) {
+                    if (more) {                   // uniform
+                        block(xb[q], xb[(q + NB - 1) % NB], kept[q]);
+                        ++k;
+                        more = ++u < u1;
+                    }
+                }
             }
         }
     }
