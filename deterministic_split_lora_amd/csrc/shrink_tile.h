@@ -49,10 +49,11 @@ __device__ __forceinline__ void wave_tree_store(const ShrinkParams& p, int64_t r
 // NRT rank tiles (A row pointers ap[rt]), `steps` steps of 32 k from the
 // pointers on, each accumulator in ascending k.  Steps go in groups of G with
 // all loads of a group issued before its matrix-core steps, without any guard;
-// the steps left over after the last full group go one at a time.  Lanes whose token row or rank column lies outside
-// the tile load from a clamped, valid row: matrix-core output (i, j) depends
-// only on row i of the first operand and column j of the second, and outputs
-// of such lanes are never stored, so no operand needs to be zeroed.
+// the steps left over after the last full group form one more, smaller group.
+// Lanes whose token row or rank column lies outside the tile load from a
+// clamped, valid row: matrix-core output (i, j) depends only on row i of the
+// first operand and column j of the second, and outputs of such lanes are
+// never stored, so no operand needs to be zeroed.
 template <bool MASK>
 __device__ __forceinline__ bf16x8 operand_load(const uint16_t* p, bool ok)
 {
@@ -62,52 +63,59 @@ __device__ __forceinline__ bf16x8 operand_load(const uint16_t* p, bool ok)
         return load_bf16x8(p);
 }
 
+// One group: the loads of steps t .. t + G - 1, then their matrix-core steps.
 // MASK: lanes outside the tile skip their loads (fewer addresses for the
 // texture units when a tile has few rows, e.g. one decode token); their
 // operands are then zeros instead of a clamped row - again never stored.
+template <int NRT, int RT, int T, int G, bool MASK>
+__device__ __forceinline__ void mfma_group(const uint16_t* const (&xp)[T], const bool (&x_ok)[T],
+                                           const uint16_t* const (&ap)[RT], const bool (&a_ok)[RT], int t,
+                                           f32x4 (&acc)[T][RT])
+{
+    bf16x8 xa[G][T];
+    bf16x8 b[G][NRT];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        const int off = (t + q) * kKStep;
+#pragma unroll
+        for (int u = 0; u < T; ++u)
+            xa[q][u] = operand_load<MASK>(xp[u] + off, x_ok[u]);
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+            b[q][rt] = operand_load<MASK>(ap[rt] + off, a_ok[rt]);
+    }
+#pragma unroll
+    for (int q = 0; q < G; ++q)
+#pragma unroll
+        for (int u = 0; u < T; ++u)
+#pragma unroll
+            for (int rt = 0; rt < NRT; ++rt)
+                acc[u][rt] = mfma_16x16x32(xa[q][u], b[q][rt], acc[u][rt]);
+}
+
 template <int NRT, int RT, int T, int G, bool MASK>
 __device__ __forceinline__ void mfma_chains(const uint16_t* const (&xp)[T], const bool (&x_ok)[T],
                                             const uint16_t* const (&ap)[RT], const bool (&a_ok)[RT], int steps,
                                             f32x4 (&acc)[T][RT])
 {
     int t = 0;
-    for (; t + G <= steps; t += G) {
-        bf16x8 xa[G][T];
-        bf16x8 b[G][NRT];
-#pragma unroll
-        for (int q = 0; q < G; ++q) {
-            const int off = (t + q) * kKStep;
-#pragma unroll
-            for (int u = 0; u < T; ++u)
-                xa[q][u] = operand_load<MASK>(xp[u] + off, x_ok[u]);
-#pragma unroll
-            for (int rt = 0; rt < NRT; ++rt)
-                b[q][rt] = operand_load<MASK>(ap[rt] + off, a_ok[rt]);
+    for (; t + G <= steps; t += G)
+        mfma_group<NRT, RT, T, G, MASK>(xp, x_ok, ap, a_ok, t, acc);
+    const int left = steps - t;                   // 0 .. G - 1, uniform
+    if constexpr (G >= 4) {
+        if (left == 3) {
+            mfma_group<NRT, RT, T, 3, MASK>(xp, x_ok, ap, a_ok, t, acc);
+            return;
         }
-#pragma unroll
-        for (int q = 0; q < G; ++q)
-#pragma unroll
-            for (int u = 0; u < T; ++u)
-#pragma unroll
-                for (int rt = 0; rt < NRT; ++rt)
-                    acc[u][rt] = mfma_16x16x32(xa[q][u], b[q][rt], acc[u][rt]);
     }
-    for (; t < steps; ++t) {
-        const int off = t * kKStep;
-        bf16x8 xa[T];
-        bf16x8 b[NRT];
-#pragma unroll
-        for (int u = 0; u < T; ++u)
-            xa[u] = operand_load<MASK>(xp[u] + off, x_ok[u]);
-#pragma unroll
-        for (int rt = 0; rt < NRT; ++rt)
-            b[rt] = operand_load<MASK>(ap[rt] + off, a_ok[rt]);
-#pragma unroll
-        for (int u = 0; u < T; ++u)
-#pragma unroll
-            for (int rt = 0; rt < NRT; ++rt)
-                acc[u][rt] = mfma_16x16x32(xa[u], b[rt], acc[u][rt]);
+    if constexpr (G >= 3) {
+        if (left == 2) {
+            mfma_group<NRT, RT, T, 2, MASK>(xp, x_ok, ap, a_ok, t, acc);
+            return;
+        }
     }
+    if (left == 1)
+        mfma_group<NRT, RT, T, 1, MASK>(xp, x_ok, ap, a_ok, t, acc);
 }
 
 // The chains for nrt (1 .. RT) active rank tiles.
