@@ -312,11 +312,10 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
     };
     // this thread's elements of a block's 16 x 16 RT partial tile: row, column
     // and byte offset inside the block's workspace rows (erow = 16 for the
-    // threads left over: never stored).  A workspace store's source registers
-    // must not be reused until the store has completed, which the compiler
-    // enforces by waiting for every memory operation issued before it; with
-    // offsets that stay put and the block's base in scalar registers only the
-    // stored value is such a register.
+    // threads left over: never stored).  The offsets are computed once and the
+    // block's base goes into scalar registers, so the per-block stores need no
+    // fresh address registers (with addresses recomputed each block, the
+    // compiled loop waited for all loads in flight more often).
     constexpr int EPT = (16 * 16 * RT + W * kWave - 1) / (W * kWave);
     int erow[EPT], ecol[EPT];
     uint32_t voff[EPT];
@@ -446,7 +445,9 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
                             val = pairwise_tree<W>(v);
                         }
                         // the value this slot stored NB blocks ago stays
-                        // in its register until here; the new one is stored
+                        // in its register until here, so no later
+                        // instruction of the loop overwrites a register a
+                        // recent store still reads; the new one is stored
                         // from the register it then keeps (the empty asm
                         // statements pin both)
                         asm volatile("" : "+v"(kept[q]));
