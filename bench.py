@@ -780,6 +780,7 @@ ONLY = {
     "decode_probe": lambda a: decode_probe(a, 128),
     "decode_probe32": lambda a: decode_probe(a, 32),
     "batch_sweep": batch_sweep_bench,
+    "compensated": compensated_bench,
 }
 
 

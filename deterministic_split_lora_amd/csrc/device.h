@@ -262,6 +262,42 @@ __device__ __forceinline__ void expand_finish(const ExpandLane& L, uint16_t* y, 
 // (h - hi is exact in fp32), both go through the matrix-core steps with the
 // same B operands, and the two fp32 results are added before the epilogue:
 //   acc = acc(hi) + acc(lo);  y = bf16(fma(scale, acc, y)).
+__device__ __forceinline__ void split_hi_lo(float f, uint16_t& hi, uint16_t& lo)
+{
+    hi = f32_to_bf16_bits(f);
+    lo = f32_to_bf16_bits(__fsub_rn(f, bf16_bits_to_f32(hi)));
+}
+
+// The matrix-core steps and updated y values of this lane's 16 columns, given
+// its hi and lo operands (zeros from r on) - every compensated expand kernel
+// runs exactly this code.
+template <int KS>
+__device__ __forceinline__ void expand_mma_comp(const bf16x8 (&hi)[KS], const bf16x8 (&lo)[KS], float scale,
+                                                const u16x8 (&yv)[2], const bf16x8 (&bop)[4][KS], u16x8 (&o)[2])
+{
+    f32x4 acc[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        f32x4 ah = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 al = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            ah = mfma_16x16x32(bop[t][ks], hi[ks], ah);
+            al = mfma_16x16x32(bop[t][ks], lo[ks], al);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            acc[t][v] = __fadd_rn(ah[v], al[v]);
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int idx = half * 8 + e;
+            o[half][e] = f32_to_bf16_bits(__builtin_fmaf(scale, acc[idx >> 2][idx & 3], bf16_bits_to_f32(yv[half][e])));
+        }
+}
+
 template <int KS>
 __device__ __forceinline__ void expand_finish_comp(const ExpandLane& L, uint16_t* y, int64_t ld_y, int64_t N,
                                                    const float* hrows, int64_t ld_hr, int r, float scale,
@@ -277,43 +313,25 @@ __device__ __forceinline__ void expand_finish_comp(const ExpandLane& L, uint16_t
             load_h8(hrows + L.li * ld_hr + j0, j0, r, f);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                vh[e] = f32_to_bf16_bits(f[e]);
-                vl[e] = f32_to_bf16_bits(__fsub_rn(f[e], bf16_bits_to_f32(vh[e])));
+                uint16_t a, b;
+                split_hi_lo(f[e], a, b);
+                vh[e] = a;
+                vl[e] = b;
             }
         }
         hi[ks] = __builtin_bit_cast(bf16x8, vh);
         lo[ks] = __builtin_bit_cast(bf16x8, vl);
     }
-    f32x4 acc[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        f32x4 ah = f32x4{0.f, 0.f, 0.f, 0.f};
-        f32x4 al = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            ah = mfma_16x16x32(bop[t][ks], hi[ks], ah);
-            al = mfma_16x16x32(bop[t][ks], lo[ks], al);
-        }
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-            acc[t][v] = __fadd_rn(ah[v], al[v]);
-    }
+    u16x8 o[2];
+    expand_mma_comp<KS>(hi, lo, scale, yv, bop, o);
     if (!L.row_ok)
         return;
     const int64_t n0 = L.n_base + 16 * L.g;
     uint16_t* yp = y + L.row * ld_y + n0;
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-        if (n0 + half * 8 < N) {
-            u16x8 o;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int idx = half * 8 + e;
-                o[e] = f32_to_bf16_bits(__builtin_fmaf(scale, acc[idx >> 2][idx & 3], bf16_bits_to_f32(yv[half][e])));
-            }
-            *reinterpret_cast<u16x8*>(yp + half * 8) = o;
-        }
-    }
+    for (int half = 0; half < 2; ++half)
+        if (n0 + half * 8 < N)
+            *reinterpret_cast<u16x8*>(yp + half * 8) = o[half];
 }
 
 // ---------------------------------------------------------------------------
@@ -381,6 +399,25 @@ __device__ __forceinline__ void h_put(const HStageSlot& s, const float (&f)[HC],
 #pragma unroll
     for (int e = 0; e < HC; ++e)
         d[e] = f32_to_bf16_bits(f[e]);
+}
+
+// ... or, for the compensated expand, the hi and lo halves of each value put
+// into two LDS tiles.
+template <int HC>
+__device__ __forceinline__ void h_put_comp(const HStageSlot& s, const float (&f)[HC], uint16_t* hi_tile,
+                                           uint16_t* lo_tile)
+{
+    if (!s.on)
+        return;
+    uint16_t* dh = hi_tile + s.row * kHbStride + s.col;
+    uint16_t* dl = lo_tile + s.row * kHbStride + s.col;
+#pragma unroll
+    for (int e = 0; e < HC; ++e) {
+        uint16_t vh, vl;
+        split_hi_lo(f[e], vh, vl);
+        dh[e] = vh;
+        dl[e] = vl;
+    }
 }
 
 // This lane's bf16(h) operand from a staged tile, zeros from column `r` on

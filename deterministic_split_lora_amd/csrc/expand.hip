@@ -217,6 +217,75 @@ __global__ __launch_bounds__(256) void k_expand_rows(ExpandParams p, int R)
     y_chunk_store(yc, ys[(tiles - 1) & 1], p.y, p.ld_y, row_base + (int64_t)kRowBlock * (tiles - 1), col0, ok);
 }
 
+// Compensated expand, large M: the data movement of k_expand_rows with the
+// arithmetic of k_expand_comp - each tile's h is staged as its bf16 hi and lo
+// halves in two LDS tiles and both pass through expand_mma_comp.
+template <int KS>
+__global__ __launch_bounds__(256) void k_expand_comp_rows(ExpandParams p, int R)
+{
+    __shared__ __align__(16) uint16_t hs[2][kRowBlock * kHbStride];
+    __shared__ __align__(16) uint16_t hl[2][kRowBlock * kHbStride];
+    __shared__ __align__(16) uint16_t ys[2][kRowBlock * kYStride];
+    const uint32_t nblocks = (uint32_t)((p.N + kExpandCols - 1) / kExpandCols);
+    const int64_t col0 = (int64_t)(blockIdx.x % nblocks) * kExpandCols;
+    const int64_t row_base = (int64_t)(blockIdx.x / nblocks) * kRowBlock * R;
+    const int64_t left = (p.M - row_base + kRowBlock - 1) / kRowBlock;
+    const int tiles = left < R ? (int)left : R;
+    constexpr int HC = KS == 4 ? 8 : 4;          // h columns each staging thread converts
+    const HStageSlot slot = h_stage_slot<HC>(p.r);
+    const YChunk yc = y_chunk();
+    const bool col_ok = col0 + yc.col < p.N;
+    const unsigned full = y_chunk_rows(yc, kRowBlock, col_ok);
+    ExpandLane L = expand_lane(row_base, kRowBlock, col0);
+    const bool active = L.n_base < p.N;
+    bf16x8 bop[4][KS];
+    expand_load_b<KS>(L, p.N, p.B, p.ld_b, p.r, bop);
+    u16x8 g[2];
+    float f[HC];
+    int nr = tile_rows(p.M, row_base);
+    unsigned ok = y_chunk_rows(yc, nr, col_ok);
+    y_chunk_load(yc, p.y, p.ld_y, row_base, col0, ok, g);
+    h_load(slot, p.h, p.ld_h, row_base, nr, p.r, f);
+    y_chunk_put(yc, g, ys[0]);
+    h_put_comp(slot, f, hs[0], hl[0]);
+    __syncthreads();
+    for (int i = 0; i < tiles; ++i) {
+        const int64_t row0 = row_base + (int64_t)kRowBlock * i;
+        const bool next = i + 1 < tiles;
+        const int nr1 = next ? tile_rows(p.M, row0 + kRowBlock) : 0;
+        const unsigned ok1 = y_chunk_rows(yc, nr1, col_ok);
+        if (next) {
+            y_chunk_load(yc, p.y, p.ld_y, row0 + kRowBlock, col0, ok1, g);
+            h_load(slot, p.h, p.ld_h, row0 + kRowBlock, nr1, p.r, f);
+        }
+        if (i > 0)                                   // tile i - 1 is whole
+            y_chunk_store(yc, ys[(i - 1) & 1], p.y, p.ld_y, row0 - kRowBlock, col0, full);
+        if (active) {
+            L.row_ok = L.li < nr;
+            bf16x8 hi[KS], lo[KS];
+            hb_from_tile<KS>(L, hs[i & 1], p.r, hi);
+            hb_from_tile<KS>(L, hl[i & 1], p.r, lo);
+            uint16_t* yl = y_lane(L, ys[i & 1]);
+            u16x8 yv[2], o[2];
+            yv[0] = *reinterpret_cast<const u16x8*>(yl);
+            yv[1] = *reinterpret_cast<const u16x8*>(yl + 8);
+            expand_mma_comp<KS>(hi, lo, p.scale, yv, bop, o);
+            *reinterpret_cast<u16x8*>(yl) = o[0];
+            *reinterpret_cast<u16x8*>(yl + 8) = o[1];
+        }
+        if (next) {
+            y_chunk_put(yc, g, ys[(i + 1) & 1]);
+            h_put_comp(slot, f, hs[(i + 1) & 1], hl[(i + 1) & 1]);
+        }
+        __syncthreads();
+        if (next) {
+            nr = nr1;
+            ok = ok1;
+        }
+    }
+    y_chunk_store(yc, ys[(tiles - 1) & 1], p.y, p.ld_y, row_base + (int64_t)kRowBlock * (tiles - 1), col0, ok);
+}
+
 // Fused: the fixed pairwise tree over the Split-K workspace for this row block
 // (exactly the second pass of the deterministic shrink: tree, then one
 // multiply by the shrink scale) is evaluated into an LDS tile, written out as
@@ -618,8 +687,18 @@ inline dim3 expand_rows_grid(int64_t M, int64_t N, int R)
     return dim3((unsigned)(((tiles + R - 1) / R) * ((N + kExpandCols - 1) / kExpandCols)));
 }
 
-hipError_t launch_expand_compensated(const ExpandParams& p, hipStream_t st)
+hipError_t launch_expand_compensated(const ExpandParams& p, hipStream_t st, int tiles_per_wg)
 {
+    const int R = tiles_per_wg > 0 ? tiles_per_wg : expand_tiles_per_wg(p.M, p.N, p.r);
+    if (R > 1) {
+        const dim3 grid = expand_rows_grid(p.M, p.N, R);
+        switch (expand_steps(p.r)) {
+        case 4: hipLaunchKernelGGL(k_expand_comp_rows<4>, grid, dim3(256), 0, st, p, R); break;
+        case 2: hipLaunchKernelGGL(k_expand_comp_rows<2>, grid, dim3(256), 0, st, p, R); break;
+        default: hipLaunchKernelGGL(k_expand_comp_rows<1>, grid, dim3(256), 0, st, p, R); break;
+        }
+        return hipGetLastError();
+    }
     const dim3 grid = expand_grid(p.M, p.N);
     switch (expand_steps(p.r)) {
     case 4: hipLaunchKernelGGL(k_expand_comp<4>, grid, dim3(256), 0, st, p); break;

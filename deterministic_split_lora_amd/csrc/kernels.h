@@ -164,7 +164,7 @@ hipError_t launch_fill_zero(float* h, int64_t ld_h, int64_t M, int ncols, hipStr
 // tiles_per_wg: 16-token tiles per expand workgroup, 0 = expand_tiles_per_wg(M, N)
 // (any value gives the same bits).
 hipError_t launch_expand(const ExpandParams& p, hipStream_t st, int tiles_per_wg = 0);
-hipError_t launch_expand_compensated(const ExpandParams& p, hipStream_t st);
+hipError_t launch_expand_compensated(const ExpandParams& p, hipStream_t st, int tiles_per_wg = 0);
 hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st);
 hipError_t launch_sgmv_expand(const ExpandParams& p, hipStream_t st, int tiles_per_wg = 0);
 hipError_t launch_sgmv_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st);

@@ -1218,6 +1218,38 @@ def test_expand_compensated_parity(M, r, N):
     assert match_c > 0.97 and match_c > match_p, (match_c, match_p)
 
 
+@pytest.mark.parametrize("r", [16, 37, 64, 128])
+def test_expand_compensated_large_m_tiles_bitwise(r):
+    """At M x N large enough that lora_expand_compensated walks several tiles
+    per workgroup (hi and lo halves of h staged in LDS), every row equals the
+    one-tile-per-workgroup result of a small call on the same rows bit for
+    bit, and sampled rows agree with the oracle's compensated expand."""
+    M, N = 4100, 4104
+    _say(f"large-M compensated expand r={r} M={M} N={N}")
+    ldh = (r + 3) // 4 * 4
+    ldb = (r + 7) // 8 * 8
+    rng = np.random.default_rng(70 + r)
+    h = np.zeros((M, ldh), np.float32)
+    h[:, :r] = rng.normal(0, 0.5, (M, r)).astype(np.float32)
+    h[:, r:] = np.nan                         # padding must never be read
+    Bm = normal_bf16((N, r), 0.02, r, "cmB")
+    Bp = np.zeros((N, ldb), np.uint16)
+    Bp[:, :r] = Bm
+    y = normal_bf16((M, N), 1.0, r, "cmy")
+    hg, Bg = f32_to_gpu(h), bf16_to_gpu(Bp)
+    yg = bf16_to_gpu(y)
+    dsl.lora_expand_compensated(hg, Bg, yg, 2.0, r=r)
+    got = bf16_from_gpu(yg)
+    for r0 in (0, 1008, 4096 - 16, 4100 - 37):
+        n = min(64, M - r0)
+        ys = bf16_to_gpu(y[r0:r0 + n])
+        dsl.lora_expand_compensated(hg[r0:r0 + n], Bg, ys, 2.0, r=r)
+        assert np.array_equal(bf16_from_gpu(ys), got[r0:r0 + n]), f"rows {r0}.."
+    rows = sorted(set([0, 15, 16, 2047, 4095, 4096, 4099] + rng.choice(M, 24, replace=False).tolist()))
+    yo, e, ab = oracle.expand_compensated(h[rows, :r], Bm, y[rows], 2.0)
+    check_expand(got[rows], yo, e, ab, y[rows], f"large-M compensated expand r={r}", r=r)
+
+
 # ---------------------------------------------------------------------------
 # multi-adapter shrink + expand in two launches (expand reads the workspace)
 # ---------------------------------------------------------------------------
