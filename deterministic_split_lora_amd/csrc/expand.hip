@@ -15,9 +15,9 @@
 //     n = n_base + 16 (m / 4) + 4 t + (m % 4),
 // so lane (li, g) collects columns n_base + 16 g + 4 t + v, t, v in 0..3 - a
 // contiguous run of 16 - for token li.  Per element, the arithmetic is one
-// matrix-core step over j < 32 (r <= 32) or two (r <= 64) with zero-padded
-// reduction slots, then one fma and one rounding; it does not depend on the
-// tiling, M or the token's neighbours.
+// matrix-core step over j < 32 (r <= 32), two (r <= 64) or four (r <= 128)
+// with zero-padded reduction slots, then one fma and one rounding; it does not
+// depend on the tiling, M or the token's neighbours.
 #include "device.h"
 #include "kernels.h"
 

@@ -1,7 +1,7 @@
 // Split-K LoRA shrink kernels for gfx950.
 //
 // The shrink h = x A^T (paper Eq. 1) is a narrow GEMM: K = hidden size is long,
-// r <= 64 is short.  Split-K (section 2.1, Eq. 3) cuts K into S contiguous
+// r <= 128 is short.  Split-K (section 2.1, Eq. 3) cuts K into S contiguous
 // chunks so S workgroups share one output tile.  A workgroup owns one
 // (16-token row block, split, group of RT 16-wide rank tiles) and W
 // wavefronts; wave w walks k_steps * 32 consecutive k of the split's chunk
