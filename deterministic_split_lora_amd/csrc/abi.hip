@@ -54,12 +54,15 @@ int make_plan(int64_t K, int32_t r, int32_t split_k, lora_shrink_plan_t* pl)
 
 // Rank tiles per shrink workgroup.  Per-element arithmetic does not depend on
 // it; small calls give every 16-wide rank tile its own workgroup (more loads in
-// flight across the chip), large ones keep up to kGroupTiles of a row block's
+// flight across the chip), larger ones keep up to kGroupTiles of a row block's
 // rank tiles together so its x rows are read once (twice above rank 64).
+// Measured on MI355X (cold inputs): together from 256 (row block, split)
+// pairs on (512 x 14336, rank 32: 9.4 against 10.7 us; 512 x 4096, rank 64:
+// 6.3 against 7.0 us), apart below (256 x 4096, rank 64: 5.2 against 6.0 us).
 int group_tiles_for(int64_t M, int32_t split_k, int rank_tiles)
 {
-    const int64_t wgs = ((M + kRowBlock - 1) / kRowBlock) * split_k * rank_tiles;
-    return wgs <= 2048 ? 1 : (rank_tiles < kGroupTiles ? rank_tiles : kGroupTiles);
+    const int64_t pairs = ((M + kRowBlock - 1) / kRowBlock) * split_k;
+    return pairs < 256 ? 1 : (rank_tiles < kGroupTiles ? rank_tiles : kGroupTiles);
 }
 
 // Row blocks per shrink workgroup in the two-pass paths (all rank tiles
@@ -74,11 +77,14 @@ int shrink_tiles_per_wg(int64_t M, int32_t split_k)
     return wgs >= 2048 ? 4 : (wgs >= 512 ? 2 : 1);
 }
 
-// Multi-adapter: 1 or 4 rank tiles per workgroup, by the same rule with M
-// standing in for the (device-side) tile count.
+// Multi-adapter: 1 or 4 rank tiles per workgroup, with M standing in for the
+// (device-side) tile count; the rank tiles stay apart up to 2048 work items
+// (512 tokens x 4096 in runs of 1-64 tokens, 4 adapters of rank 64: one rank
+// tile per workgroup 8.9 us, four 11.1 us).
 int sgmv_group_tiles(int64_t M, int32_t split_k, int32_t r_max)
 {
-    return group_tiles_for(M, split_k, (r_max + 15) / 16) == 1 ? 1 : kGroupTiles;
+    const int64_t items = ((M + kRowBlock - 1) / kRowBlock) * split_k * ((r_max + 15) / 16);
+    return items <= 2048 ? 1 : kGroupTiles;
 }
 
 // Work items of the multi-adapter shrinks (at most M tiles x split_k x
@@ -101,14 +107,17 @@ int launch_status(hipError_t e)
 }
 
 // Row blocks per item of the A-in-registers partial kernel, or 0 when it is
-// not used: it needs short wave chains (shrink_stream_fits) and at least 2048
-// (row block, split) pairs, and takes about 512 items.  Per-element
-// arithmetic does not depend on it.
+// not used: it needs short wave chains (shrink_stream_fits) and at least 1024
+// (row block, split) pairs, and takes one row block per 256 pairs, 4 to 16.
+// Measured on MI355X (cold inputs): 1024 x 8192, rank 64, Split-K 16: 10.0 us
+// against 11.4 us for two row blocks per workgroup; 4096 x 4096, rank 64: 8
+// row blocks 15.0 us, 4 16.1 us; 4096 x 8192, rank 16, Split-K 16: 16 row
+// blocks 18.9 us, 8 20.4 us.  Per-element arithmetic does not depend on it.
 int stream_rows_per_item(int64_t tiles, const lora_shrink_plan_t& pl)
 {
-    if (!shrink_stream_fits(pl.waves, pl.k_steps, pl.rank_tiles) || tiles * pl.split_k < 2048)
+    if (!shrink_stream_fits(pl.waves, pl.k_steps, pl.rank_tiles) || tiles * pl.split_k < 1024)
         return 0;
-    const int64_t R = (tiles * pl.split_k + 511) / 512;
+    const int64_t R = tiles * pl.split_k / 256;
     return R < 4 ? 4 : (R > 16 ? 16 : (int)R);
 }
 

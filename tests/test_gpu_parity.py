@@ -1010,7 +1010,7 @@ def test_shrink_expand_counted_stress_and_graph():
 @pytest.mark.parametrize("M,K,r,S", [(4100, 8192, 64, 16), (4100, 4096, 24, 8), (2100, 16384, 32, 16),
                                      (4100, 1024, 5, 8), (2100, 2048, 37, 16)])
 def test_shrink_stream_rows_bitwise(M, K, r, S):
-    """At M large enough (at least 2048 row block x split pairs, short wave
+    """At M large enough (at least 1024 row block x split pairs, short wave
     chains) for the partial kernel that keeps each wave's A operands in
     registers while it walks several row blocks, every row's h equals that of
     a small call on the same rows (one-tile kernels) bit for bit, and sampled
