@@ -34,15 +34,20 @@ struct ExpandItem {
     int nrows;
 };
 
-__device__ __forceinline__ ExpandItem expand_item(int64_t M, int64_t N)
+__device__ __forceinline__ ExpandItem expand_item_at(uint32_t item, int64_t M, int64_t N)
 {
     ExpandItem q;                                 // 32-bit: the grid is below 2^31
     const uint32_t nblocks = (uint32_t)((N + kExpandCols - 1) / kExpandCols);
-    q.cb = blockIdx.x % nblocks;
-    q.row0 = (int64_t)(blockIdx.x / nblocks) * kRowBlock;
+    q.cb = item % nblocks;
+    q.row0 = (int64_t)(item / nblocks) * kRowBlock;
     const int64_t left = M - q.row0;
     q.nrows = left < kRowBlock ? (int)left : kRowBlock;
     return q;
+}
+
+__device__ __forceinline__ ExpandItem expand_item(int64_t M, int64_t N)
+{
+    return expand_item_at(blockIdx.x, M, N);
 }
 
 // Single adapter: 4 waves of 64 columns per workgroup.
@@ -595,14 +600,26 @@ __global__ __launch_bounds__(256, KS == 4 ? 2 : 4) void k_sgmv_expand_rows(Expan
     y_chunk_store(yc, ys[(tiles - 1) & 1], p.y, p.ld_y, row_base + (int64_t)kRowBlock * (tiles - 1), col0, w_prev);
 }
 
-// KS: matrix-core steps the kernel is built for (1: r_max <= 32, 2: r_max <= 64).
-// COMBINE: the block's h rows are evaluated from the Split-K workspace into
-// LDS first (the first column block also writes them out).
+// KS: matrix-core steps the kernel is built for (1: r_max <= 32, 2: r_max <= 64,
+// 4: r_max <= 128).  COMBINE: the block's h rows are evaluated from the
+// Split-K workspace into LDS first (the first column block also writes them
+// out).  slots: workgroups per (16-token block, column block).  The block's
+// distinct adapters, in order of first appearance, are dealt out to them -
+// workgroup j takes the j-th, (j + slots)-th, ... - so the passes of a block
+// whose tokens carry many adapters (one adapter per decode token) run on
+// different compute units at once instead of one after another; workgroup 0
+// also writes the zero h rows of tokens without an adapter.  Every token
+// still gets exactly one pass of the single-adapter arithmetic.
 template <int KS, bool COMBINE>
-__global__ __launch_bounds__(256) void k_sgmv_expand(ExpandParams p, TreeParams c, int split_k)
+__global__ __launch_bounds__(256) void k_sgmv_expand(ExpandParams p, TreeParams c, int split_k, int slots)
 {
     __shared__ __align__(16) float hs[COMBINE ? kRowBlock * kHTileStride : 1];
-    const ExpandItem q = expand_item(p.M, p.N);
+    // slot slowest: the slot-0 workgroups (the only busy ones where a block
+    // holds one adapter) come first and spread over all XCDs
+    const uint32_t items = gridDim.x / (uint32_t)slots;
+    const int slot = (int)(blockIdx.x / items);
+    const uint32_t item = blockIdx.x - (uint32_t)slot * items;
+    const ExpandItem q = expand_item_at(item, p.M, p.N);
     ExpandLane L = expand_lane(q.row0, q.nrows, q.cb * kExpandCols);
     const bool active = L.n_base < p.N;              // per wave
     int id = -1;
@@ -610,8 +627,28 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(ExpandParams p, TreeParams 
         id = p.ids[L.row];
         id = (id < 0 || id >= p.n_adapters) ? -1 : id;
     }
+    // rows (bit li) of this workgroup's adapters, and of tokens without one;
+    // lanes li and li + 16 g hold the same token, so lanes 0..15 tell all
+    uint32_t mine = 0;
+    if (slots == 1) {
+        mine = (uint32_t)(__ballot(id >= 0) & 0xFFFFull);
+    } else {
+        bool done = id < 0;
+        for (int k = 0;; ++k) {
+            const uint64_t pending = __ballot(!done);
+            if (pending == 0)
+                break;
+            const int a = __shfl(id, __builtin_ctzll(pending));
+            const bool same = !done && id == a;
+            const uint32_t rows = (uint32_t)(__ballot(same) & 0xFFFFull);
+            if (k % slots == slot)
+                mine |= rows;
+            done = done || same;
+        }
+    }
+    const uint32_t none = (uint32_t)(__ballot(L.row_ok && id < 0) & 0xFFFFull);
     ExpandLane Ly = L;
-    Ly.row_ok = L.row_ok && id >= 0;
+    Ly.row_ok = ((mine >> L.li) & 1u) != 0;
     u16x8 yv[2] = {u16x8{0, 0, 0, 0, 0, 0, 0, 0}, u16x8{0, 0, 0, 0, 0, 0, 0, 0}};
     if (active)
         expand_load_y(Ly, p.y, p.ld_y, p.N, yv);
@@ -619,10 +656,11 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(ExpandParams p, TreeParams 
     int64_t ld_hr = p.ld_h;
     if constexpr (COMBINE) {
         const bool write_h = c.h != nullptr && q.cb == 0;
+        const uint32_t rows = mine | (slot == 0 ? none : 0u);
         for (int e = threadIdx.x; e < kRowBlock * p.r_max; e += 256) {
             const int row = e / p.r_max;
             const int col = e - row * p.r_max;
-            if (row < q.nrows) {
+            if (row < q.nrows && ((rows >> row) & 1u)) {
                 const float v = sgmv_h_value(c, q.row0 + row, col, split_k);
                 hs[row * kHTileStride + col] = v;
                 if (write_h)
@@ -771,6 +809,23 @@ static int sgmv_tiles_per_wg(int64_t M, int64_t N, int r_max, bool combine)
     return single > wide ? single : wide;
 }
 
+// Workgroups per (16-token block, column block) of the one-tile multi-adapter
+// expand.  Small grids (decode: at most 512 one-tile workgroups) take enough
+// to bring the grid towards 2048 workgroups, at most 16 (the distinct
+// adapters a block can hold) and at most n_adapters; larger grids keep one,
+// where blocks hold few adapters and extra workgroups cost more than they
+// save.  Measured on MI355X: 32 tokens with 32 rank-64 adapters, N = 4096:
+// 31.8 -> 8.2 us; 512 tokens in runs of 1-64 over 4 adapters, N = 6144, two
+// workgroups per block: 22.9 -> 25.0 us per shrink + expand, so one there.
+static int sgmv_expand_slots(int64_t M, int64_t N, int n_adapters)
+{
+    const int64_t wgs = ((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols);
+    if (wgs < 1 || wgs > 512 || n_adapters < 2)
+        return 1;
+    const int64_t s = 2048 / wgs > 16 ? 16 : 2048 / wgs;
+    return (int)(s < n_adapters ? s : n_adapters);
+}
+
 template <bool COMBINE>
 void launch_sgmv_expand_t(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st, int R = 0)
 {
@@ -785,11 +840,12 @@ void launch_sgmv_expand_t(const ExpandParams& p, const TreeParams& c, int split_
         }
         return;
     }
-    const dim3 grid = expand_grid(p.M, p.N);
+    const int slots = sgmv_expand_slots(p.M, p.N, p.n_adapters);
+    const dim3 grid(expand_grid(p.M, p.N).x * (unsigned)slots);
     switch (expand_steps(p.r_max)) {
-    case 4: hipLaunchKernelGGL((k_sgmv_expand<4, COMBINE>), grid, dim3(256), 0, st, p, c, split_k); break;
-    case 2: hipLaunchKernelGGL((k_sgmv_expand<2, COMBINE>), grid, dim3(256), 0, st, p, c, split_k); break;
-    default: hipLaunchKernelGGL((k_sgmv_expand<1, COMBINE>), grid, dim3(256), 0, st, p, c, split_k); break;
+    case 4: hipLaunchKernelGGL((k_sgmv_expand<4, COMBINE>), grid, dim3(256), 0, st, p, c, split_k, slots); break;
+    case 2: hipLaunchKernelGGL((k_sgmv_expand<2, COMBINE>), grid, dim3(256), 0, st, p, c, split_k, slots); break;
+    default: hipLaunchKernelGGL((k_sgmv_expand<1, COMBINE>), grid, dim3(256), 0, st, p, c, split_k, slots); break;
     }
 }
 

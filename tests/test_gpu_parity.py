@@ -527,6 +527,59 @@ def test_sgmv_ranks_above_64():
         _check_sgmv(c, h, y, rows, f"sgmv r<=128 M={M}")
 
 
+@pytest.mark.parametrize("M,N,r", [(40, 4096, 64), (130, 1032, 16), (48, 2048, 128)])
+def test_sgmv_expand_one_adapter_per_token_bitwise(M, N, r):
+    """Decode-style ids - most tokens with an adapter of their own, some
+    sharing one, some without: every token's y equals the single-adapter
+    lora_expand of its adapter on that row, bit for bit (the blocks' many
+    adapters are dealt out to several workgroups); tokens without an adapter
+    keep y."""
+    t = torch()
+    rng = np.random.default_rng(M + r)
+    n = M
+    ids = np.arange(M, dtype=np.int32)
+    ids[rng.choice(M, M // 5, replace=False)] = -1
+    ids[rng.choice(M, M // 5, replace=False)] = 3
+    ranks = rng.choice([r, max(1, r // 2), 8], n).astype(np.int32)
+    ranks[0] = r
+    ldh = (r + 3) // 4 * 4
+    h = np.zeros((M, ldh), np.float32)
+    h[:, :r] = rng.normal(0, 0.5, (M, r)).astype(np.float32)
+    y = normal_bf16((M, N), 1.0, M, "otpy")
+    Bg, Bs = [], []
+    for a in range(n):
+        ra = int(ranks[a])
+        Bm = normal_bf16((N, ra), 0.02, a, f"otpB{r}")
+        Bp = np.zeros((N, (ra + 7) // 8 * 8), np.uint16)
+        Bp[:, :ra] = Bm
+        Bs.append(Bm)
+        Bg.append(bf16_to_gpu(Bp))
+    scales = rng.choice([0.5, 1.0, 2.0], n).astype(np.float32)
+    Bptr = t.tensor([b.data_ptr() for b in Bg], dtype=t.int64, device="cuda")
+    hg = f32_to_gpu(h)
+    yg = bf16_to_gpu(y)
+    dsl.lora_sgmv_expand(hg, Bptr, t.from_numpy(ranks).cuda(), t.from_numpy(scales).cuda(),
+                         t.from_numpy(ids).cuda(), n, yg, r)
+    got = bf16_from_gpu(yg)
+    none = ids < 0
+    assert np.array_equal(got[none], y[none])
+    for i in range(M):
+        a = int(ids[i])
+        if a < 0:
+            continue
+        ra = int(ranks[a])
+        hs = np.zeros((1, (ra + 3) // 4 * 4), np.float32)
+        hs[0, :ra] = h[i, :ra]
+        ys = bf16_to_gpu(y[i:i + 1])
+        dsl.lora_expand(f32_to_gpu(hs), Bg[a], ys, float(scales[a]), r=ra)
+        assert np.array_equal(bf16_from_gpu(ys), got[i:i + 1]), f"token {i} adapter {a}"
+    pick = [i for i in range(M) if ids[i] == 3][:4]
+    if pick:
+        ra = int(ranks[3])
+        yo, e, ab = oracle.expand(h[pick, :ra], Bs[3], y[pick], float(scales[3]))
+        check_expand(got[pick], yo, e, ab, y[pick], "one adapter per token", r=ra)
+
+
 def test_sgmv_equals_single_adapter_bitwise():
     """All tokens on one adapter: the multi-adapter path must reproduce the
     single-adapter calls bit for bit (same per-token arithmetic)."""
