@@ -20,7 +20,8 @@ Also reported: per-batch-size numbers, the roofline of the dominant kernel
 (the tree + expand kernel of the deterministic pipeline, with the HBM bytes
 the hardware counters recorded for it when its sources are unchanged since),
 two decode bandwidth probes (32 and 128 tokens, each with its own rank-64
-adapter, hidden 8192, multi-adapter shrink), device-copy ceilings at the
+adapter, hidden 8192, multi-adapter shrink), the same decode shapes' expand
+and shrink + expand (N = 4096), device-copy ceilings at the
 probes' sizes, identical-input replay statistics of the deterministic and
 atomic pipelines (1000 launches per batch size), and the CPU oracle timed on
 the host cores.
@@ -719,6 +720,60 @@ def decode_probe(args, M=32):
     return out
 
 
+def decode_expand_probe(args, M=32, N=4096):
+    """Multi-tenant decode, expand side: M tokens, each with its own rank-64
+    adapter (hidden 8192, N = 4096 outputs, Split-K 8), cold cache: the
+    multi-adapter expand alone (h given), and the whole deterministic
+    shrink + expand (lora_sgmv_shrink_expand: partials, then the expand that
+    evaluates the fixed tree).  Algorithmic bytes: every adapter's B once, h,
+    y read and written (expand); plus x and every adapter's A (pipeline)."""
+    import torch
+    import deterministic_split_lora_amd as dsl
+    from synth import normal_bf16
+    dev = torch.device("cuda:0")
+    K, r, S, n = 8192, 64, 8, M
+
+    def g(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    x = normal_bf16((M, K), 1.0, 1, "dprobe_x")
+    y = normal_bf16((M, N), 1.0, 1, "dprobe_y")
+    As = [normal_bf16((r, K), 0.02, 1, f"dprobe_A{a}") for a in range(n)]
+    Bs = [normal_bf16((N, r), 0.02, 1, f"dprobe_B{a}") for a in range(n)]
+    ex_bytes = 2 * r * N * n + 4 * M * N + 4 * M * r
+    sh_bytes = 2 * M * K + 2 * K * r * n + 4 * M * r
+    copies = 1 if args.hot else max(2, math.ceil(ROTATE_BYTES / (ex_bytes + sh_bytes)))
+    ids = torch.arange(M, dtype=torch.int32, device=dev)
+    ranks = torch.full((n,), r, dtype=torch.int32, device=dev)
+    scales = torch.full((n,), SCALE, dtype=torch.float32, device=dev)
+    plan = torch.empty(dsl.lora_sgmv_plan_bytes(M), dtype=torch.uint8, device=dev)
+    dsl.lora_sgmv_plan(ids, n, plan)
+    h0 = torch.randn(M, r, device=dev)
+    sets = []
+    for c in range(copies):
+        Ag, Bg = [g(a) for a in As], [g(b) for b in Bs]
+        sets.append(dict(x=g(x), y=g(y), A=Ag, B=Bg, h=h0.clone(),
+                         Ap=torch.tensor([t.data_ptr() for t in Ag], dtype=torch.int64, device=dev),
+                         Bp=torch.tensor([t.data_ptr() for t in Bg], dtype=torch.int64, device=dev),
+                         ws=torch.empty(dsl.lora_sgmv_workspace_bytes(M, r, S), dtype=torch.uint8, device=dev)))
+    torch.cuda.synchronize()
+
+    def expand(s):
+        dsl.lora_sgmv_expand(s["h"], s["Bp"], ranks, scales, ids, n, s["y"], r)
+
+    def pipeline(s):
+        dsl.lora_sgmv_shrink_expand(s["x"], s["Ap"], K, s["Bp"], ranks, None, scales, ids, n, plan, s["y"], r, S,
+                                    s["ws"])
+
+    out = {"workload": f"{M} tokens, {M} adapters of rank 64 (one per token), hidden 8192 -> N = {N}, "
+                       "Split-K 8, multi-adapter deterministic expand and shrink + expand",
+           "expand_bytes": ex_bytes, "pipeline_bytes": ex_bytes + sh_bytes, "copies": copies}
+    for name, call, byt in (("expand", expand, ex_bytes), ("shrink_expand", pipeline, ex_bytes + sh_bytes)):
+        us = _time_rotating(call, sets, args)
+        out[name] = {"us_per_call": round(us, 3), "GBps": round(byt / us / 1e3, 1),
+                     "pct_hbm_peak": round(100 * byt / us / 1e3 / HBM_PEAK_GBS, 2)}
+    return out
+
+
 def _time_rotating(call, sets, args):
     """us per call: 8 calls on 8 input copies per HIP graph, graphs replayed.
     Under --counters: two eager calls, no timing (returns NaN)."""
@@ -779,6 +834,7 @@ ONLY = {
     "sgmv_prefill": lambda a: sgmv_bench(a, "b5", 4096, 8192, 28672, [8, 16, 32, 64] * 8, 32, 512, 16),
     "decode_probe": lambda a: decode_probe(a, 128),
     "decode_probe32": lambda a: decode_probe(a, 32),
+    "decode_expand": lambda a: {"32": decode_expand_probe(a, 32), "128": decode_expand_probe(a, 128)},
     "batch_sweep": batch_sweep_bench,
     "compensated": compensated_bench,
 }
@@ -816,10 +872,11 @@ def main():
     b = Bench(args)
     res = b.run()
     log("bench: main timing done")
-    probe = wide = roof = floor = extra = replay = None
+    probe = wide = roof = floor = extra = replay = dexp = None
     if not args.no_probe:
         probe = decode_probe(args, 32)
         wide = decode_probe(args, 128)
+        dexp = {"32": decode_expand_probe(args, 32), "128": decode_expand_probe(args, 128)}
         avg = int(res["roofline"]["algorithmic_bytes_per_launch"]) // 2 // 16 * 16
         roof = copy_roofline(args, [avg, probe["bytes"], wide["bytes"], 64 << 20])
         floor = launch_floor(args)
@@ -870,6 +927,7 @@ def main():
         "cpu_baseline": cpu,
         "decode_bandwidth_probe": probe,
         "decode_bandwidth_probe_wide": wide,
+        "decode_expand_probe": dexp,
         "copy_roofline": roof,
         "launch_floor": floor,
         "replay_variability": replay,
