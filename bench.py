@@ -806,9 +806,9 @@ def _time_rotating(call, sets, args):
     return e0.elapsed_time(e1) * 1000 / (replays * per_graph)
 
 
-def cpu_baseline(seconds: float):
-    """The CPU oracle (fp64 C, OpenMP) on the same workload: full steps (four
-    batch sizes, shrink + expand each) repeated for about `seconds`."""
+def _oracle_steps(seconds: float):
+    """Full steps of the CPU oracle (four batch sizes, shrink + expand each)
+    for about `seconds`: (steps, elapsed seconds, threads used)."""
     import oracle
     from synth import single_adapter_case
     cases = {M: single_adapter_case(M, K_HID, RANK, N_OUT, SPLIT, SCALE, seed=0) for M in M_LIST}
@@ -822,9 +822,42 @@ def cpu_baseline(seconds: float):
         el = time.perf_counter() - t0
         if el >= seconds:
             break
-    return {"value": round(el / (n * len(M_LIST)) * 1e6, 1), "unit": "us/call", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{n} full steps (M = 1, 16, 64, 256; fp64 shrink + expand each) in {el:.1f} s"}
+    return n, el, oracle.num_threads()
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(seconds: float):
+    """The CPU oracle (fp64 C, OpenMP over rows) on the same workload, timed
+    on the host's cores for about `seconds`, then on one thread (a child
+    process with OMP_NUM_THREADS=1) for a third of that."""
+    import subprocess
+    n, el, threads = _oracle_steps(seconds)
+    out = {"value": round(el / (n * len(M_LIST)) * 1e6, 1), "unit": "us/call", "cores": threads,
+           "kind": "oracle",
+           "sample": f"{n} full steps (M = 1, 16, 64, 256; fp64 shrink + expand each) in {el:.1f} s",
+           "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    code = ("import json, sys; sys.path.insert(0, %r); import bench; "
+            "print(json.dumps(bench._oracle_steps(%f)))" % (ROOT, seconds / 3))
+    try:
+        res = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
+                             timeout=seconds * 3 + 60)
+        n1, el1, t1 = json.loads(res.stdout.strip().splitlines()[-1])
+        out["single_thread"] = {"value": round(el1 / (n1 * len(M_LIST)) * 1e6, 1), "unit": "us/call",
+                                "threads": t1, "sample": f"{n1} full steps in {el1:.1f} s"}
+    except Exception as exc:                      # the one-thread figure is context only
+        out["single_thread"] = {"error": str(exc)[:200]}
+    return out
 
 
 # Workloads bench.py can time on their own (--only).
