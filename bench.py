@@ -837,27 +837,13 @@ def _cpu_model():
 
 
 def cpu_baseline(seconds: float):
-    """The CPU oracle (fp64 C, OpenMP over rows) on the same workload, timed
-    on the host's cores for about `seconds`, then on one thread (a child
-    process with OMP_NUM_THREADS=1) for a third of that."""
-    import subprocess
+    """The CPU oracle (fp64 C, OpenMP over rows, the host's thread setting) on
+    the same workload, timed for about `seconds`."""
     n, el, threads = _oracle_steps(seconds)
-    out = {"value": round(el / (n * len(M_LIST)) * 1e6, 1), "unit": "us/call", "cores": threads,
-           "kind": "oracle",
-           "sample": f"{n} full steps (M = 1, 16, 64, 256; fp64 shrink + expand each) in {el:.1f} s",
-           "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
-    env = dict(os.environ, OMP_NUM_THREADS="1")
-    code = ("import json, sys; sys.path.insert(0, %r); import bench; "
-            "print(json.dumps(bench._oracle_steps(%f)))" % (ROOT, seconds / 3))
-    try:
-        res = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True,
-                             timeout=seconds * 3 + 60)
-        n1, el1, t1 = json.loads(res.stdout.strip().splitlines()[-1])
-        out["single_thread"] = {"value": round(el1 / (n1 * len(M_LIST)) * 1e6, 1), "unit": "us/call",
-                                "threads": t1, "sample": f"{n1} full steps in {el1:.1f} s"}
-    except Exception as exc:                      # the one-thread figure is context only
-        out["single_thread"] = {"error": str(exc)[:200]}
-    return out
+    return {"value": round(el / (n * len(M_LIST)) * 1e6, 1), "unit": "us/call", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{n} full steps (M = 1, 16, 64, 256; fp64 shrink + expand each) in {el:.1f} s",
+            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
 
 
 # Workloads bench.py can time on their own (--only).
