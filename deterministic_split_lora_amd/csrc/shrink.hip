@@ -458,15 +458,25 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
                     }
                 }
             };
-            bool more = true;
-            while (more) {
+            // whole rounds of NB blocks, then the run's last blocks: the loop
+            // is entered again only after all NB blocks of a round, so the
+            // compiled waits at its head know which loads are in flight (a
+            // round that may stop after any block merged those paths there,
+            // and the head then waited for the loads of the next two blocks)
+            for (; u + NB <= u1;) {
 #pragma unroll
                 for (int q = 0; q < NB; ++q) {
-                    if (more) {                   // uniform
-                        block(xb[q], xb[(q + NB - 1) % NB], kept[q]);
-                        ++k;
-                        more = ++u < u1;
-                    }
+                    block(xb[q], xb[(q + NB - 1) % NB], kept[q]);
+                    ++k;
+                    ++u;
+                }
+            }
+#pragma unroll
+            for (int q = 0; q + 1 < NB; ++q) {
+                if (u < u1) {                     // uniform
+                    block(xb[q], xb[(q + NB - 1) % NB], kept[q]);
+                    ++k;
+                    ++u;
                 }
             }
         }
