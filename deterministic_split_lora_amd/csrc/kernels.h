@@ -97,6 +97,33 @@ __device__ __forceinline__ bool tile_ok(const int32_t* t, int64_t M, int32_t n_a
     return tile_rows_ok(t, M) && t[2] >= 0 && t[2] < n_adapters;
 }
 
+// Per-adapter values (rank, scale) looked up per element by the
+// multi-adapter tree come from an LDS copy of the first kAdapterTable entries
+// of their device arrays, loaded by all threads at kernel start together
+// with the token ids and the workspace slices, instead of one dependent
+// global load after the id; ids from kAdapterTable on read the device array.
+// Callers put a __syncthreads() between table_fill and table_get.
+constexpr int kAdapterTable = 256;
+
+template <typename T>
+__device__ __forceinline__ void table_fill(T* lds, const T* src, int32_t n)
+{
+    if (src == nullptr)
+        return;
+    const int m = n < kAdapterTable ? n : kAdapterTable;
+    for (int t = (int)threadIdx.x; t < m; t += (int)blockDim.x)
+        lds[t] = src[t];
+}
+
+// Entry a (0 <= a < n of table_fill) of src; `none` when src is null.
+template <typename T>
+__device__ __forceinline__ T table_get(const T* lds, const T* src, int a, T none)
+{
+    if (src == nullptr)
+        return none;
+    return a < kAdapterTable ? lds[a] : src[a];
+}
+
 // Single-launch shrink: the per-tile arrival counters and the h it writes.
 struct CounterParams {
     int32_t* counters;              // kMaxRankTiles per row block / plan tile, 0 between calls

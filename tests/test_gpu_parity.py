@@ -67,6 +67,8 @@ SHRINK_CASES = [
     (7, 4096, 65, 1, 1.0, "rank 65, S=1 direct"),
     (2100, 4096, 128, 8, 1.0, "rank 128 at large M: rank groups, one row block per workgroup"),
     (1, 8192, 112, 8, 2.0, "decode rank 112"),
+    (5, 65536, 16, 16, 1.0, "long chains: K = 65536, 16 steps per wave"),
+    (3, 131072, 32, 8, 1.0, "long chains: K = 131072, 64 steps per wave"),
 ]
 
 
@@ -182,6 +184,7 @@ EXPAND_CASES = [
     (1, 16, 4096, 2.0), (16, 16, 4096, 2.0), (64, 16, 4096, 2.0), (256, 16, 4096, 2.0),
     (17, 1, 264, 2.0), (9, 8, 520, 1.0), (33, 24, 1000, 2.0), (5, 40, 4096, 0.5), (20, 64, 6144, 2.0),
     (3, 37, 8, 2.0), (37, 128, 1032, 2.0), (6, 65, 264, 1.0), (300, 100, 2048, 2.0), (1, 128, 4096, 2.0),
+    (3, 64, 65536, 2.0),
 ]
 
 
@@ -504,6 +507,25 @@ def test_sgmv_mixed_ranks_and_invalid_ids():
     c = sgmv_case(M, 2048, 520, ranks, 0, 0, 4, seed=1, tag="mix", ids=ids)
     h, y, _ = _sgmv_gpu(c)
     _check_sgmv(c, h, y, list(range(M)), "sgmv mixed")
+
+
+def test_sgmv_many_adapters():
+    """300 adapters with ranks 1..24, one or a few tokens each, ids spread over
+    the whole range (also past the first 256, whose rank and scale the
+    multi-adapter kernels may look up in a table) and some tokens without an
+    adapter."""
+    rng = np.random.default_rng(300)
+    n = 300
+    ranks = [int(v) for v in rng.integers(1, 25, n)]
+    M = 320
+    ids = rng.permutation(np.concatenate([np.arange(n), rng.integers(250, n, M - n - 8), -np.ones(8)]))
+    ids = ids.astype(np.int32)
+    assert (ids >= 256).sum() > 40
+    c = sgmv_case(M, 1024, 264, ranks, 0, 0, 8, seed=5, tag="many", ids=ids)
+    c.scales[:] = rng.choice([0.5, 1.0, 1.5, 2.0, 3.0], n)      # a scale per adapter
+    _say(f"sgmv many adapters: n={n} M={M}")
+    h, y, _ = _sgmv_gpu(c)
+    _check_sgmv(c, h, y, list(range(M)), "sgmv 300 adapters")
 
 
 def test_sgmv_ranks_above_64():
