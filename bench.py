@@ -837,12 +837,22 @@ def _cpu_model():
 
 
 def cpu_baseline(seconds: float):
-    """The CPU oracle (fp64 C, OpenMP over rows, the host's thread setting) on
-    the same workload, timed for about `seconds`."""
+    """The CPU oracle (fp64 C, OpenMP over rows) on the same workload: timed for
+    about `seconds` with the host's thread setting, then for about a third of
+    that on one thread (set through the OpenMP runtime in this process, then
+    restored)."""
+    import oracle
     n, el, threads = _oracle_steps(seconds)
+    prev = oracle.set_threads(1)
+    try:
+        n1, el1, threads1 = _oracle_steps(seconds / 3)
+    finally:
+        oracle.set_threads(prev)
+    sample = "full steps (M = 1, 16, 64, 256; fp64 shrink + expand each)"
     return {"value": round(el / (n * len(M_LIST)) * 1e6, 1), "unit": "us/call", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{n} full steps (M = 1, 16, 64, 256; fp64 shrink + expand each) in {el:.1f} s",
+            "kind": "oracle", "sample": f"{n} {sample} in {el:.1f} s",
+            "one_thread": {"value": round(el1 / (n1 * len(M_LIST)) * 1e6, 1), "unit": "us/call",
+                           "cores": threads1, "sample": f"{n1} {sample} in {el1:.1f} s"},
             "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
 
 

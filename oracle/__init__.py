@@ -95,6 +95,8 @@ def lib():
         L.oracle_sgmv_expand.argtypes = [_f32p, ctypes.POINTER(_u16p), _i32p, _f32p, _i32p,
                                          ctypes.c_int32, _u16p, _i64, _i64, _i64, _f64p, _u16p, _f64p]
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_threads.restype = ctypes.c_int
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
@@ -266,6 +268,11 @@ def sgmv_expand(h, Bs, ranks, scales, ids, y):
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_threads(n: int) -> int:
+    """Thread count for later calls; returns the previous one."""
+    return int(lib().oracle_set_threads(int(n)))
 
 
 # ----------------------------------------------------------------------------

@@ -355,6 +355,21 @@ void oracle_sgmv_expand(const float* h, const uint16_t* const* B_list, const int
     }
 }
 
+/* Sets the number of OpenMP threads later calls run with (n >= 1) and returns
+   the previous setting, so a timing run can take one thread and restore the
+   host's default afterwards. */
+int oracle_set_threads(int n)
+{
+#ifdef _OPENMP
+    const int prev = omp_get_max_threads();
+    omp_set_num_threads(n > 0 ? n : 1);
+    return prev;
+#else
+    (void)n;
+    return 1;
+#endif
+}
+
 /* Number of OpenMP threads this library runs with (for reporting). */
 int oracle_num_threads(void)
 {
