@@ -250,7 +250,8 @@ class Bench:
             per = {M: self.per_call_us(self.combine_only, (M,), 8, K) for M in two}
             byt = sum(combine_bytes(M, RANK, N_OUT, SPLIT) for M in two)
             cand.append((sum(per.values()), len(two), byt, COMBINE_KERNEL + " (lora_expand_combine: fixed tree "
-                         "over the Split-K workspace + expand; r=16, N=4096, M=" + "/".join(map(str, two)) + ")",
+                         "over the Split-K workspace + expand, 2 waves per workgroup at M <= 4, else 4; r=16, "
+                         "N=4096, M=" + "/".join(map(str, two)) + ")",
                          {str(M): round(u, 3) for M, u in per.items()}))
         us, n, byt, name, per = max(cand, key=lambda c: c[0])
         avg_launch_us = us / n

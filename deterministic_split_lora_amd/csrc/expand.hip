@@ -34,10 +34,10 @@ struct ExpandItem {
     int nrows;
 };
 
-__device__ __forceinline__ ExpandItem expand_item_at(uint32_t item, int64_t M, int64_t N)
+__device__ __forceinline__ ExpandItem expand_item_at(uint32_t item, int64_t M, int64_t N, int cols = kExpandCols)
 {
     ExpandItem q;                                 // 32-bit: the grid is below 2^31
-    const uint32_t nblocks = (uint32_t)((N + kExpandCols - 1) / kExpandCols);
+    const uint32_t nblocks = (uint32_t)((N + cols - 1) / cols);
     q.cb = item % nblocks;
     q.row0 = (int64_t)(item / nblocks) * kRowBlock;
     const int64_t left = M - q.row0;
@@ -298,23 +298,24 @@ __global__ __launch_bounds__(256) void k_expand_comp_rows(ExpandParams p, int R)
 // through a separate kernel.  Same bits as shrink then expand.
 constexpr int kHTileStride = 132;         // floats per LDS row (128 + 4 padding)
 
-template <int KS, int S>
-__global__ __launch_bounds__(256) void k_expand_combine(ExpandParams p, TreeParams c)
+template <int KS, int S, int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_expand_combine(ExpandParams p, TreeParams c)
 {
+    constexpr int kCols = WAVES * 64;
     __shared__ __align__(16) float hs[kRowBlock * kHTileStride];
-    const ExpandItem q = expand_item(p.M, p.N);
+    const ExpandItem q = expand_item_at(blockIdx.x, p.M, p.N, kCols);
     const int64_t row0 = q.row0;
     const int nrows = q.nrows;
     const int r = p.r;
     // y and B first: they do not depend on the workspace
-    ExpandLane L = expand_lane(row0, nrows, q.cb * kExpandCols);
+    ExpandLane L = expand_lane(row0, nrows, q.cb * kCols);
     const bool active = L.n_base < p.N;
     u16x8 yv[2];
     bf16x8 bop[4][KS];
     if (active)
         expand_load<KS>(L, p.y, p.ld_y, p.N, p.B, p.ld_b, r, yv, bop);
     const bool write_h = c.h != nullptr && q.cb == 0;
-    for (int e = threadIdx.x; e < kRowBlock * r; e += 256) {
+    for (int e = threadIdx.x; e < kRowBlock * r; e += kCols) {
         const int row = e / r;
         const int col = e - row * r;
         if (row < nrows) {
@@ -768,26 +769,54 @@ hipError_t launch_expand(const ExpandParams& p, hipStream_t st, int tiles_per_wg
     return hipGetLastError();
 }
 
-template <int KS>
-hipError_t launch_expand_combine_ks(const ExpandParams& p, const TreeParams& c, int S, dim3 grid, hipStream_t st)
+template <int KS, int WAVES>
+hipError_t launch_expand_combine_ks(const ExpandParams& p, const TreeParams& c, int S, hipStream_t st)
 {
+    const dim3 grid((unsigned)(((p.M + kRowBlock - 1) / kRowBlock) * ((p.N + WAVES * 64 - 1) / (WAVES * 64))));
+    const dim3 block(WAVES * 64);
     switch (S) {
-    case 1: hipLaunchKernelGGL((k_expand_combine<KS, 1>), grid, dim3(256), 0, st, p, c); break;
-    case 2: hipLaunchKernelGGL((k_expand_combine<KS, 2>), grid, dim3(256), 0, st, p, c); break;
-    case 4: hipLaunchKernelGGL((k_expand_combine<KS, 4>), grid, dim3(256), 0, st, p, c); break;
-    case 8: hipLaunchKernelGGL((k_expand_combine<KS, 8>), grid, dim3(256), 0, st, p, c); break;
-    default: hipLaunchKernelGGL((k_expand_combine<KS, 16>), grid, dim3(256), 0, st, p, c); break;
+    case 1: hipLaunchKernelGGL((k_expand_combine<KS, 1, WAVES>), grid, block, 0, st, p, c); break;
+    case 2: hipLaunchKernelGGL((k_expand_combine<KS, 2, WAVES>), grid, block, 0, st, p, c); break;
+    case 4: hipLaunchKernelGGL((k_expand_combine<KS, 4, WAVES>), grid, block, 0, st, p, c); break;
+    case 8: hipLaunchKernelGGL((k_expand_combine<KS, 8, WAVES>), grid, block, 0, st, p, c); break;
+    default: hipLaunchKernelGGL((k_expand_combine<KS, 16, WAVES>), grid, block, 0, st, p, c); break;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st)
+template <int KS>
+hipError_t launch_expand_combine_w(const ExpandParams& p, const TreeParams& c, int S, int waves, hipStream_t st)
 {
-    const dim3 grid = expand_grid(p.M, p.N);
+    if (waves == 2)
+        return launch_expand_combine_ks<KS, 2>(p, c, S, st);
+    if (waves == 8)
+        return launch_expand_combine_ks<KS, 8>(p, c, S, st);
+    return launch_expand_combine_ks<KS, 4>(p, c, S, st);
+}
+
+// Waves per workgroup of the tree + expand kernel.  Every column block
+// evaluates its row block's tree again, so narrow blocks pay only where the
+// tree is tiny and wide ones where the grid is large.  Measured on MI355X
+// (cold inputs, N = 4096, Split-K 8, rank 16 unless noted; 2 / 4 / 8 waves):
+// M = 1: 4.55 / 4.70 / 4.74 us; M = 16: 5.02 / 4.85 / 5.14; M = 256: 5.60 /
+// 5.10 / 5.41; M = 1024: 8.78 / 8.31 / 8.18, rank 32: 10.5 / 9.26 / 8.71;
+// M = 4096: 23.3 / 21.2 / 20.8.  The bits do not depend on it.
+static int combine_waves(int64_t M, int64_t N)
+{
+    if (M <= 4)
+        return 2;
+    const int64_t wgs = ((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols);
+    return wgs >= 1024 ? 8 : 4;
+}
+
+hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st, int waves)
+{
+    if (waves == 0)
+        waves = combine_waves(p.M, p.N);
     switch (expand_steps(p.r)) {
-    case 4: return launch_expand_combine_ks<4>(p, c, split_k, grid, st);
-    case 2: return launch_expand_combine_ks<2>(p, c, split_k, grid, st);
-    default: return launch_expand_combine_ks<1>(p, c, split_k, grid, st);
+    case 4: return launch_expand_combine_w<4>(p, c, split_k, waves, st);
+    case 2: return launch_expand_combine_w<2>(p, c, split_k, waves, st);
+    default: return launch_expand_combine_w<1>(p, c, split_k, waves, st);
     }
 }
 
