@@ -223,6 +223,21 @@ bool use_single_launch(int64_t M, int64_t K, int32_t r, int64_t N)
     return M <= 64 && r <= kFusedMaxRank && K * r * 2 <= 32 * 1024;
 }
 
+// Whether lora_shrink_expand's two-launch schedule evaluates the Split-K tree
+// inside the expand.  Every column block evaluates its rows' tree again, so
+// this holds only while column blocks x splits stays small and the h values
+// those re-evaluations produce, M r per column block, stay below 2^19;
+// otherwise the tree kernel writes h once and the tile-walking expand reads
+// it.  Measured on MI355X (N = 4096, Split-K 8, cold inputs; tree in the
+// expand / tree kernel + expand): M = 1024, r = 32, K = 14336: 20.3 / 21.8
+// us; M = 2048: 33.9 / 33.4 us; M = 4096: 59.0 / 56.1 us; M = 2048, r = 64,
+// K = 4096: 29.6 / 24.4 us.  Same bits either way.
+bool tree_in_expand(int64_t M, int32_t r, int64_t N, int32_t split_k)
+{
+    const int64_t nblocks = (N + kExpandCols - 1) / kExpandCols;
+    return nblocks * split_k <= 256 && M * r * nblocks <= (int64_t{1} << 19);
+}
+
 int launch_fused(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a, const uint16_t* B,
                  int64_t ld_b, float* h, int64_t ld_h, uint16_t* y, int64_t ld_y, int64_t M, int32_t r, int64_t N,
                  const lora_shrink_plan_t& pl, float shrink_scale, float expand_scale, void* stream)
@@ -554,7 +569,7 @@ int lora_shrink_expand_launches(int64_t M, int64_t K, int32_t r, int64_t N, int3
         return -LORA_ERR_UNSUPPORTED;
     if (M == 0 || N == 0)
         return 0;
-    return use_single_launch(M, K, r, N) ? 1 : 2;
+    return use_single_launch(M, K, r, N) ? 1 : (tree_in_expand(M, r, N, split_k) ? 2 : 3);
 }
 
 int lora_shrink_expand_fused(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a, const uint16_t* B,
@@ -606,14 +621,12 @@ int lora_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64
     st = lora_shrink_partials(x, ld_x, A, ld_a, M, K, r, split_k, workspace, ws_bytes, stream);
     if (st != LORA_OK)
         return st;
-    // As in lora_sgmv_shrink_expand: the tree goes into the expand only while
-    // column blocks x splits is small (every column block evaluates its rows'
-    // tree again); otherwise the tree kernel writes h once - into the caller's
-    // h, or in place into workspace slice 0 - and the expand reads it.
-    const int64_t nblocks = (N + kExpandCols - 1) / kExpandCols;
+    // Tree in the expand (tree_in_expand), or the tree kernel writing h once -
+    // into the caller's h, or in place into workspace slice 0 - and the expand
+    // reading it (which needs 16-byte h rows).
     float* hh = h ? h : static_cast<float*>(workspace);
     const int64_t ldh = h ? ld_h : r;
-    if (nblocks * split_k <= 256 || !aligned16(hh) || ldh % 4 != 0)
+    if (tree_in_expand(M, r, N, split_k) || !aligned16(hh) || ldh % 4 != 0)
         return lora_expand_combine(workspace, ws_bytes, split_k, shrink_scale, B, ld_b, h, ld_h, y, ld_y, M, r, N,
                                    expand_scale, stream);
     TreeParams t{};

@@ -209,10 +209,11 @@ int lora_shrink_splitk_counted(const uint16_t* x, int64_t ld_x, const uint16_t* 
  * lora_shrink_expand: h and y bit for bit those of lora_shrink_splitk followed
  * by lora_expand, in fewer launches: the two calls above in order on one
  * stream; or (small M and A) the single launch of lora_shrink_expand_fused; or,
- * when ceil(N / 256) * split_k > 256 (every column block re-evaluating the
- * tree would cost more than a launch), the partials, the tree kernel and the
- * expand kernel - without h, h is then kept in workspace slice 0 (when
- * r % 4 == 0).  The workspace content is undefined afterwards.
+ * when ceil(N / 256) * split_k > 256 or M * r * ceil(N / 256) > 2^19 (every
+ * column block re-evaluating the tree would cost more than a launch), the
+ * partials, the tree kernel and the expand kernel - without h, h is then kept
+ * in workspace slice 0 (when r % 4 == 0; with h, when h's rows are 16-byte
+ * aligned).  The workspace content is undefined afterwards.
  *
  * workspace: >= lora_shrink_expand_workspace_bytes(M, r, split_k) bytes =
  * split_k * M * r * 4, also for split_k == 1.  Requirements: those of
@@ -240,8 +241,9 @@ int lora_expand_combine(const void* workspace, size_t workspace_bytes, int32_t s
  * another schedule for them).
  */
 /* Host only: how many kernel launches lora_shrink_expand makes for these sizes
-   (1: the single-launch schedule, 2: partials then tree + expand, 0: nothing
-   to do), or -LORA_ERR_UNSUPPORTED for sizes it rejects. */
+   (1: the single-launch schedule, 2: partials then tree + expand, 3:
+   partials, tree, expand - 2 instead when the h rows do not allow it, see
+   above - 0: nothing to do), or -LORA_ERR_UNSUPPORTED for sizes it rejects. */
 int lora_shrink_expand_launches(int64_t M, int64_t K, int32_t r, int64_t N, int32_t split_k);
 
 int lora_shrink_expand_fused(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a,

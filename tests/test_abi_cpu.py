@@ -318,6 +318,11 @@ def test_shrink_expand_launch_count():
     assert dsl.lora_shrink_expand_launches(65, 1024, 16, 4096, 8) == 2
     assert dsl.lora_shrink_expand_launches(1, 4096, 16, 4096, 8) == 2
     assert dsl.lora_shrink_expand_launches(0, 4096, 16, 4096, 8) == 0
+    # the tree in a kernel of its own: many column blocks x splits, or many h values per column block
+    assert dsl.lora_shrink_expand_launches(300, 2048, 64, 8200, 16) == 3
+    assert dsl.lora_shrink_expand_launches(2100, 1024, 64, 1032, 8) == 3
+    assert dsl.lora_shrink_expand_launches(1024, 14336, 32, 4096, 8) == 2
+    assert dsl.lora_shrink_expand_launches(2048, 14336, 32, 4096, 8) == 3
     assert dsl.lora_shrink_expand_launches(8, 4000, 16, 4096, 8) < 0
 
 

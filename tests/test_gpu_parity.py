@@ -655,7 +655,8 @@ def test_sgmv_prefill_full_size_sampled():
                                        (9, 1024, 33, 520, 4), (2, 16384, 64, 512, 16),
                                        (300, 2048, 64, 8200, 16), (40, 1024, 24, 16384, 8),
                                        (1, 4096, 128, 4096, 8), (20, 1024, 96, 1032, 16),
-                                       (300, 2048, 128, 8200, 16), (33, 2048, 72, 264, 1)])
+                                       (300, 2048, 128, 8200, 16), (33, 2048, 72, 264, 1),
+                                       (2100, 1024, 64, 1032, 8)])
 def test_shrink_expand_fused_bitwise(M, K, r, N, S):
     """Every schedule of the deterministic shrink + expand - lora_shrink_splitk
     then lora_expand (three launches), lora_shrink_partials then
