@@ -906,15 +906,19 @@ int lora_sgmv_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* con
     if (st != LORA_OK)
         return st;
     // Every column block of the expand evaluates its rows' tree again, so the
-    // tree goes into the expand only while column blocks x splits is small;
+    // tree goes into the expand only under the bounds of tree_in_expand;
     // otherwise the tree kernel writes h once (into the caller's h, or in
     // place into workspace slice 0, each element read then written by one
-    // thread) and the expand reads it.  The bits are the same either way.
-    const int64_t nblocks = (N + kExpandCols - 1) / kExpandCols;
+    // thread) and the expand reads it.  Measured on MI355X (cold inputs,
+    // Split-K 8; tree in the expand / tree kernel + expand): 4 rank-64
+    // adapters, N = 6144: M = 128: 14.7 / 15.7 us, M = 256: 17.6 / 17.5 us,
+    // M = 512: 23.6 / 21.6 us; 4 rank-16 adapters, N = 4096, M = 1024: 20.5 /
+    // 22.0 us; one rank-64 adapter per token, N = 4096: 32 tokens 18.8 / 19.7
+    // us.  The bits are the same either way.
     float* hh = h ? h : static_cast<float*>(workspace);
     const int64_t ldh = h ? ld_h : r_max;
     const bool h_readable = aligned16(hh) && ldh % 4 == 0;
-    const bool fuse = nblocks * split_k <= 256 || !h_readable;
+    const bool fuse = tree_in_expand(M, r_max, N, split_k) || !h_readable;
     const TreeParams t = sgmv_tree_params(workspace, M, r_max, fuse ? h : hh, fuse ? ld_h : ldh, token_adapter,
                                           ranks, shrink_scales, n_adapters);
     ExpandParams e{};

@@ -1334,9 +1334,11 @@ def test_sgmv_shrink_expand_bitwise(case):
     """lora_sgmv_shrink_expand gives the h and y bits of lora_sgmv_shrink
     (with the shrink scales) followed by lora_sgmv_expand (with the expand
     scales): tokens without an adapter keep y, ranks below r_max and not a
-    multiple of 8 included; the large cases walk several tiles per expand
-    workgroup, the last one takes the three-launch schedule (with h, and with
-    h kept in the workspace).  Sampled rows agree with the oracle."""
+    multiple of 8 included.  The larger cases take the three-launch schedule
+    (with h, and with h kept in the workspace); a third call, with h rows that
+    are not a multiple of 16 bytes, keeps the tree in the expand, which walks
+    several tiles per workgroup at large M.  Sampled rows agree with the
+    oracle."""
     t = torch()
     if case == "qkv":
         c = sgmv_case(512, 4096, 6144, [64, 64, 64, 64], 1, 64, 8, seed=11, tag="se_q")
@@ -1382,10 +1384,15 @@ def test_sgmv_shrink_expand_bitwise(case):
     dsl.lora_sgmv_shrink_expand(xg, Ap, c.K, Bp, ranks, shg, exg, idg, n, plan, y2, c.r_max, c.split_k, ws2, h=h2)
     y3 = bf16_to_gpu(c.y)
     dsl.lora_sgmv_shrink_expand(xg, Ap, c.K, Bp, ranks, shg, exg, idg, n, plan, y3, c.r_max, c.split_k, ws2)
+    # h rows that are not a multiple of 16 bytes: the tree always goes into the expand
+    h4 = t.full((c.M, c.r_max + 1), float("nan"), dtype=t.float32, device="cuda")[:, :c.r_max]
+    y4 = bf16_to_gpu(c.y)
+    dsl.lora_sgmv_shrink_expand(xg, Ap, c.K, Bp, ranks, shg, exg, idg, n, plan, y4, c.r_max, c.split_k, ws2, h=h4)
     t.cuda.synchronize()
-    assert np.array_equal(f32_bits(h1), f32_bits(h2))
+    assert np.array_equal(f32_bits(h1), f32_bits(h2)) and np.array_equal(f32_bits(h1), f32_bits(h4))
     g1 = bf16_from_gpu(y1)
     assert np.array_equal(g1, bf16_from_gpu(y2)) and np.array_equal(g1, bf16_from_gpu(y3))
+    assert np.array_equal(g1, bf16_from_gpu(y4))
     hh = h2.cpu().numpy()
     rng = np.random.default_rng(5)
     for i in sorted(rng.choice(c.M, min(12, c.M), replace=False).tolist()):
