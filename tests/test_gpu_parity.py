@@ -634,15 +634,59 @@ def test_sgmv_permuting_segments_keeps_token_bits():
     assert np.array_equal(y2, y1[order])
 
 
+def _sgmv_other_schedules(c, h, y, gpu):
+    """lora_sgmv_shrink_expand (the scales as shrink and expand scales) and
+    lora_sgmv_shrink_counted give the h and y bits of the separate shrink and
+    expand that _sgmv_gpu ran."""
+    t = torch()
+    As, Bs = gpu
+    n = len(c.ranks)
+    Ap = t.tensor([a.data_ptr() for a in As], dtype=t.int64, device="cuda")
+    Bp = t.tensor([b.data_ptr() for b in Bs], dtype=t.int64, device="cuda")
+    ranks = t.from_numpy(c.ranks).cuda()
+    scales = t.from_numpy(c.scales).cuda()
+    idg, plan = _build_plan(c.ids, n)
+    xg = bf16_to_gpu(c.x)
+    ws = workspace(dsl.lora_sgmv_workspace_bytes(c.M, c.r_max, c.split_k))
+    h2 = t.full((c.M, c.r_max), float("nan"), dtype=t.float32, device="cuda")
+    y2 = bf16_to_gpu(c.y)
+    dsl.lora_sgmv_shrink_expand(xg, Ap, c.K, Bp, ranks, scales, scales, idg, n, plan, y2, c.r_max, c.split_k, ws,
+                                h=h2)
+    cnt = t.zeros(dsl.lora_sgmv_counter_bytes(c.M) // 4, dtype=t.int32, device="cuda")
+    h3 = t.full((c.M, c.r_max), float("nan"), dtype=t.float32, device="cuda")
+    dsl.lora_sgmv_shrink_counted(xg, Ap, c.K, ranks, scales, n, plan, h3, c.r_max, c.split_k, ws, cnt)
+    t.cuda.synchronize()
+    assert np.array_equal(f32_bits_np(h), f32_bits(h2)), "pipeline h"
+    assert np.array_equal(f32_bits_np(h), f32_bits(h3)), "single-launch shrink h"
+    assert np.array_equal(y, bf16_from_gpu(y2)), "pipeline y"
+
+
 def test_sgmv_prefill_full_size_sampled():
     """32 adapters with ranks cycling 8, 16, 32, 64, x [4096 x 8192], segments
     of 32..512 tokens, B_i [r_i x 28672], S=16, at full size; the oracle checks
-    64 sampled tokens (and untouched rows are checked by value)."""
+    64 sampled tokens (and untouched rows are checked by value).  The shrink +
+    expand pipeline and the single-launch shrink, also timed at this size,
+    give the same bits."""
     c = sgmv_case(4096, 8192, 28672, [8, 16, 32, 64] * 8, 32, 512, 16, seed=0, tag="cfg5")
     _say(f"sgmv prefill 4096x8192 -> 28672, {len(c.segs)} segments")
-    h, y, _ = _sgmv_gpu(c)
+    h, y, gpu = _sgmv_gpu(c)
     rows = sorted(np.random.default_rng(3).choice(4096, 64, replace=False).tolist())
     _check_sgmv(c, h, y, rows, "sgmv prefill")
+    _sgmv_other_schedules(c, h, y, gpu)
+
+
+@pytest.mark.parametrize("M", [32, 128])
+def test_sgmv_decode_probe_shapes(M):
+    """The decode probes' shapes: M tokens, each with its own rank-64 adapter,
+    hidden 8192, Split-K 8, N = 4096.  Sampled rows agree with the oracle; the
+    pipeline and the single-launch shrink give the bits of the separate shrink
+    and expand."""
+    c = sgmv_case(M, 8192, 4096, [64] * M, 0, 0, 8, seed=7, tag=f"dp{M}", ids=np.arange(M, dtype=np.int32))
+    _say(f"sgmv decode probe shape: {M} tokens")
+    h, y, gpu = _sgmv_gpu(c)
+    rows = sorted(np.random.default_rng(M).choice(M, 16, replace=False).tolist())
+    _check_sgmv(c, h, y, rows, f"decode probe {M}")
+    _sgmv_other_schedules(c, h, y, gpu)
 
 
 # ---------------------------------------------------------------------------
