@@ -26,6 +26,9 @@ HIPCC_FLAGS = [
     "-ffp-contract=off",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # only the C ABI (include/lora_det.h) is exported; the kernels' C++
+    # launchers stay inside the library
+    "-fvisibility=hidden",
     "-Wall",
 ]
 

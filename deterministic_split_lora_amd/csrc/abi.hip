@@ -334,9 +334,48 @@ TreeParams sgmv_tree_params(void* workspace, int64_t M, int32_t r_max, float* h,
     return t;
 }
 
+int expand_entry(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b, uint16_t* y, int64_t ld_y,
+                 int64_t M, int32_t r, int64_t N, float scale, bool compensated, void* stream)
+{
+    if (M < 0 || M > kMaxDim || N < 0 || N > kMaxDim)
+        return LORA_ERR_SHAPE;
+    if (r < 1 || r > kMaxRank)
+        return LORA_ERR_UNSUPPORTED;
+    if (N % 8 != 0)
+        return LORA_ERR_UNSUPPORTED;
+    if (((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols) > kMaxGrid)
+        return LORA_ERR_SHAPE;
+    if (M == 0 || N == 0)
+        return LORA_OK;
+    if (!h || !B || !y)
+        return LORA_ERR_NULL;
+    if (ld_h < r || ld_b < r || ld_y < N)
+        return LORA_ERR_SHAPE;
+    if (!aligned16(h) || !aligned16(B) || !aligned16(y) || ld_h % 4 || ld_b % 8 || ld_y % 8)
+        return LORA_ERR_ALIGN;
+    ExpandParams p{};
+    p.h = h;
+    p.ld_h = ld_h;
+    p.B = B;
+    p.ld_b = ld_b;
+    p.y = y;
+    p.ld_y = ld_y;
+    p.M = M;
+    p.N = N;
+    p.r = r;
+    p.r_max = r;
+    p.scale = scale;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    return launch_status(compensated ? launch_expand_compensated(p, st) : launch_expand(p, st));
+}
+
+
 }  // namespace
 
 extern "C" {
+// The library is built with hidden visibility; the entry points below are
+// its exported interface.
+#pragma GCC visibility push(default)
 
 int lora_abi_version(void)
 {
@@ -435,44 +474,6 @@ int lora_shrink_splitk_atomic(const uint16_t* x, int64_t ld_x, const uint16_t* A
                                                       group_tiles_for(M, split_k, pl.rank_tiles), s));
 }
 
-namespace {
-
-int expand_entry(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b, uint16_t* y, int64_t ld_y,
-                 int64_t M, int32_t r, int64_t N, float scale, bool compensated, void* stream)
-{
-    if (M < 0 || M > kMaxDim || N < 0 || N > kMaxDim)
-        return LORA_ERR_SHAPE;
-    if (r < 1 || r > kMaxRank)
-        return LORA_ERR_UNSUPPORTED;
-    if (N % 8 != 0)
-        return LORA_ERR_UNSUPPORTED;
-    if (((M + kRowBlock - 1) / kRowBlock) * ((N + kExpandCols - 1) / kExpandCols) > kMaxGrid)
-        return LORA_ERR_SHAPE;
-    if (M == 0 || N == 0)
-        return LORA_OK;
-    if (!h || !B || !y)
-        return LORA_ERR_NULL;
-    if (ld_h < r || ld_b < r || ld_y < N)
-        return LORA_ERR_SHAPE;
-    if (!aligned16(h) || !aligned16(B) || !aligned16(y) || ld_h % 4 || ld_b % 8 || ld_y % 8)
-        return LORA_ERR_ALIGN;
-    ExpandParams p{};
-    p.h = h;
-    p.ld_h = ld_h;
-    p.B = B;
-    p.ld_b = ld_b;
-    p.y = y;
-    p.ld_y = ld_y;
-    p.M = M;
-    p.N = N;
-    p.r = r;
-    p.r_max = r;
-    p.scale = scale;
-    const hipStream_t st = static_cast<hipStream_t>(stream);
-    return launch_status(compensated ? launch_expand_compensated(p, st) : launch_expand(p, st));
-}
-
-}  // namespace
 
 int lora_expand(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b, uint16_t* y, int64_t ld_y,
                 int64_t M, int32_t r, int64_t N, float scale, void* stream)
@@ -980,4 +981,5 @@ int lora_sgmv_expand(const float* h, int64_t ld_h, const uint16_t* const* B_ptrs
     return launch_status(launch_sgmv_expand(p, static_cast<hipStream_t>(stream)));
 }
 
+#pragma GCC visibility pop
 }  // extern "C"
