@@ -810,6 +810,76 @@ def test_graph_capture_replays_match_eager():
         del junk
 
 
+@pytest.mark.parametrize("M", [300, 2100])
+def test_sgmv_graph_replays(M):
+    """The multi-adapter path captured in a HIP graph - the device-side plan,
+    the shrink + expand pipeline and the single-launch shrink (whose kernel
+    puts its counters back to zero) - replayed several times with eager work
+    and synchronisations in between: every replay gives the eager bits.  At
+    M = 2100 the shrink walks several plan tiles per workgroup with A held in
+    registers."""
+    t = torch()
+    rng = np.random.default_rng(M)
+    ids = np.empty(M, np.int32)
+    pos = 0
+    while pos < M:
+        run = int(rng.integers(1, 200))
+        ids[pos:pos + run] = rng.choice([-1, 0, 1, 2, 3])
+        pos += run
+    c = sgmv_case(M, 1024, 1032, [16, 64, 8, 32], 0, 0, 8, seed=M, tag=f"gr{M}", ids=ids)
+    n = len(c.ranks)
+    As = [bf16_to_gpu(a) for a in c.As]
+    Bs = []
+    for b in c.Bs:
+        bp = np.zeros((c.N, (b.shape[1] + 7) // 8 * 8), np.uint16)
+        bp[:, :b.shape[1]] = b
+        Bs.append(bf16_to_gpu(bp))
+    Ap = t.tensor([a.data_ptr() for a in As], dtype=t.int64, device="cuda")
+    Bp = t.tensor([b.data_ptr() for b in Bs], dtype=t.int64, device="cuda")
+    ranks = t.from_numpy(c.ranks).cuda()
+    scales = t.from_numpy(np.array([0.5, 2.0, 1.0, 3.0], np.float32)).cuda()
+    idg = t.from_numpy(c.ids).cuda()
+    plan = t.zeros(dsl.lora_sgmv_plan_bytes(M), dtype=t.uint8, device="cuda")
+    xg, y0 = bf16_to_gpu(c.x), bf16_to_gpu(c.y)
+    y = y0.clone()
+    ws = workspace(dsl.lora_sgmv_workspace_bytes(M, c.r_max, c.split_k))
+    ws2 = workspace(dsl.lora_sgmv_workspace_bytes(M, c.r_max, c.split_k))
+    cnt = t.zeros(dsl.lora_sgmv_counter_bytes(M) // 4, dtype=t.int32, device="cuda")
+    h = t.empty((M, c.r_max), dtype=t.float32, device="cuda")
+    h2 = t.empty((M, c.r_max), dtype=t.float32, device="cuda")
+
+    def step():
+        dsl.lora_sgmv_plan(idg, n, plan)
+        y.copy_(y0)
+        dsl.lora_sgmv_shrink_expand(xg, Ap, c.K, Bp, ranks, scales, scales, idg, n, plan, y, c.r_max, c.split_k,
+                                    ws, h=h)
+        dsl.lora_sgmv_shrink_counted(xg, Ap, c.K, ranks, scales, n, plan, h2, c.r_max, c.split_k, ws2, cnt)
+    step()
+    t.cuda.synchronize()
+    ref = (f32_bits(h), bf16_from_gpu(y), f32_bits(h2))
+    assert np.array_equal(ref[0], ref[2])
+    side = t.cuda.Stream()
+    side.wait_stream(t.cuda.current_stream())
+    with t.cuda.stream(side):
+        step()
+    t.cuda.current_stream().wait_stream(side)
+    t.cuda.synchronize()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        step()
+    for rep in range(5):
+        h.fill_(float("nan")); h2.fill_(float("nan")); y.zero_(); plan.zero_()
+        junk = t.randn(1 << 20, device="cuda") * 3.0        # eager work between replays
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        got = (f32_bits(h), bf16_from_gpu(y), f32_bits(h2))
+        for a, b in zip(got, ref):
+            assert np.array_equal(a, b), f"replay {rep}"
+        assert int(cnt.abs().sum()) == 0, f"counters left non-zero after replay {rep}"
+        del junk
+
+
 @pytest.mark.parametrize("S", [1, 2, 4, 8, 16])
 def test_expand_combine_on_given_workspace(S):
     """lora_expand_combine on a workspace filled with seeded fp32 values of
