@@ -532,7 +532,7 @@ __global__ __launch_bounds__(W * 64) void k_sgmv_shrink_counted(ShrinkParams p, 
 // one workgroup per compute unit, where each dependent load is latency that
 // no other workgroup hides.  Measured on MI355X after the multi-adapter
 // partials (HIP graphs, cold inputs; 32 and 128 decode tokens, one rank-64
-// adapter each): the tree adds 2.1 and 1.9 us instead of 2.8 and 2.5 us.
+// adapter each): the tree adds 2.1 and 1.9 us instead of 2.7 and 2.5 us.
 // Same arithmetic either way.
 template <int S, bool SGMV, bool TABLE>
 __global__ __launch_bounds__(256) void k_splitk_tree(TreeParams p)
