@@ -298,12 +298,30 @@ __global__ __launch_bounds__(256) void k_expand_comp_rows(ExpandParams p, int R)
 // through a separate kernel.  Same bits as shrink then expand.
 constexpr int kHTileStride = 132;         // floats per LDS row (128 + 4 padding)
 
-template <int KS, int S, int WAVES>
+// XCD: the row blocks are dealt out to the XCDs - workgroup w runs on XCD
+// w % 8 (consecutive workgroups go to different XCDs), and the workgroups of
+// XCD x take row blocks x, x + 8, ... with their column blocks one after
+// another - so a row block's workspace slices are fetched into one L2 instead
+// of every one (B's column blocks are then fetched by every XCD instead).
+// Workgroups past the last row block exit at once.
+template <int KS, int S, int WAVES, bool XCD>
 __global__ __launch_bounds__(WAVES * 64) void k_expand_combine(ExpandParams p, TreeParams c)
 {
     constexpr int kCols = WAVES * 64;
     __shared__ __align__(16) float hs[kRowBlock * kHTileStride];
-    const ExpandItem q = expand_item_at(blockIdx.x, p.M, p.N, kCols);
+    ExpandItem q;
+    if constexpr (XCD) {
+        const uint32_t nblocks = (uint32_t)((p.N + kCols - 1) / kCols);
+        const uint32_t j = blockIdx.x / kXcds;
+        q.cb = j % nblocks;
+        q.row0 = ((int64_t)(j / nblocks) * kXcds + blockIdx.x % kXcds) * kRowBlock;
+        if (q.row0 >= p.M)                           // uniform
+            return;
+        const int64_t left = p.M - q.row0;
+        q.nrows = left < kRowBlock ? (int)left : kRowBlock;
+    } else {
+        q = expand_item_at(blockIdx.x, p.M, p.N, kCols);
+    }
     const int64_t row0 = q.row0;
     const int nrows = q.nrows;
     const int r = p.r;
@@ -769,29 +787,35 @@ hipError_t launch_expand(const ExpandParams& p, hipStream_t st, int tiles_per_wg
     return hipGetLastError();
 }
 
-template <int KS, int WAVES>
+template <int KS, int WAVES, bool XCD>
 hipError_t launch_expand_combine_ks(const ExpandParams& p, const TreeParams& c, int S, hipStream_t st)
 {
-    const dim3 grid((unsigned)(((p.M + kRowBlock - 1) / kRowBlock) * ((p.N + WAVES * 64 - 1) / (WAVES * 64))));
+    int64_t rbs = (p.M + kRowBlock - 1) / kRowBlock;
+    if (XCD)
+        rbs = (rbs + kXcds - 1) / kXcds * kXcds;
+    const dim3 grid((unsigned)(rbs * ((p.N + WAVES * 64 - 1) / (WAVES * 64))));
     const dim3 block(WAVES * 64);
     switch (S) {
-    case 1: hipLaunchKernelGGL((k_expand_combine<KS, 1, WAVES>), grid, block, 0, st, p, c); break;
-    case 2: hipLaunchKernelGGL((k_expand_combine<KS, 2, WAVES>), grid, block, 0, st, p, c); break;
-    case 4: hipLaunchKernelGGL((k_expand_combine<KS, 4, WAVES>), grid, block, 0, st, p, c); break;
-    case 8: hipLaunchKernelGGL((k_expand_combine<KS, 8, WAVES>), grid, block, 0, st, p, c); break;
-    default: hipLaunchKernelGGL((k_expand_combine<KS, 16, WAVES>), grid, block, 0, st, p, c); break;
+    case 1: hipLaunchKernelGGL((k_expand_combine<KS, 1, WAVES, XCD>), grid, block, 0, st, p, c); break;
+    case 2: hipLaunchKernelGGL((k_expand_combine<KS, 2, WAVES, XCD>), grid, block, 0, st, p, c); break;
+    case 4: hipLaunchKernelGGL((k_expand_combine<KS, 4, WAVES, XCD>), grid, block, 0, st, p, c); break;
+    case 8: hipLaunchKernelGGL((k_expand_combine<KS, 8, WAVES, XCD>), grid, block, 0, st, p, c); break;
+    default: hipLaunchKernelGGL((k_expand_combine<KS, 16, WAVES, XCD>), grid, block, 0, st, p, c); break;
     }
     return hipGetLastError();
 }
 
 template <int KS>
-hipError_t launch_expand_combine_w(const ExpandParams& p, const TreeParams& c, int S, int waves, hipStream_t st)
+hipError_t launch_expand_combine_w(const ExpandParams& p, const TreeParams& c, int S, int waves, bool xcd,
+                                   hipStream_t st)
 {
     if (waves == 2)
-        return launch_expand_combine_ks<KS, 2>(p, c, S, st);
+        return launch_expand_combine_ks<KS, 2, false>(p, c, S, st);
     if (waves == 8)
-        return launch_expand_combine_ks<KS, 8>(p, c, S, st);
-    return launch_expand_combine_ks<KS, 4>(p, c, S, st);
+        return xcd ? launch_expand_combine_ks<KS, 8, true>(p, c, S, st)
+                   : launch_expand_combine_ks<KS, 8, false>(p, c, S, st);
+    return xcd ? launch_expand_combine_ks<KS, 4, true>(p, c, S, st)
+               : launch_expand_combine_ks<KS, 4, false>(p, c, S, st);
 }
 
 // Waves per workgroup of the tree + expand kernel.  Every column block
@@ -809,14 +833,20 @@ static int combine_waves(int64_t M, int64_t N)
     return wgs >= 1024 ? 8 : 4;
 }
 
-hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st, int waves)
+hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st, int waves,
+                                 int xcd)
 {
     if (waves == 0)
         waves = combine_waves(p.M, p.N);
+    // Row blocks kept on one XCD from 64 row blocks on.  Measured on MI355X
+    // (cold inputs, N = 4096, Split-K 8; spread over the XCDs / on one):
+    // M = 1024, rank 16: 8.25 / 8.07 us, rank 32: 8.74 / 8.58 us; M = 2048,
+    // rank 16: 12.3 / 11.9 us; below, no gain (M = 256, rank 64: 7.89 / 8.12).
+    const bool rows_on_xcd = waves != 2 && (xcd > 0 || (xcd < 0 && (p.M + kRowBlock - 1) / kRowBlock >= 64));
     switch (expand_steps(p.r)) {
-    case 4: return launch_expand_combine_w<4>(p, c, split_k, waves, st);
-    case 2: return launch_expand_combine_w<2>(p, c, split_k, waves, st);
-    default: return launch_expand_combine_w<1>(p, c, split_k, waves, st);
+    case 4: return launch_expand_combine_w<4>(p, c, split_k, waves, rows_on_xcd, st);
+    case 2: return launch_expand_combine_w<2>(p, c, split_k, waves, rows_on_xcd, st);
+    default: return launch_expand_combine_w<1>(p, c, split_k, waves, rows_on_xcd, st);
     }
 }
 
