@@ -359,11 +359,13 @@ int lora_sgmv_shrink_counted(const uint16_t* x, int64_t ld_x, const uint16_t* co
  * Split-K workspace (the same fixed tree and shrink_scales[a] multiply as
  * lora_sgmv_shrink's second pass, zeros past the adapter's rank), writes it
  * to h when h is not NULL and applies lora_sgmv_expand's update with
- * expand_scales[a]; or (three launches, when ceil(N / 256) * split_k > 256,
- * where every column block re-evaluating the tree would cost more than a
- * launch) the tree kernel, then lora_sgmv_expand's kernel.  Without h the
- * three-launch schedule keeps h in workspace slice 0 (when r_max % 4 == 0,
- * else it takes the two-launch schedule).  Either way h and y are bit for bit
+ * expand_scales[a]; or (three launches, when ceil(N / 256) * split_k > 256
+ * or M * r_max * ceil(N / 256) > 2^19, where every column block re-evaluating
+ * the tree would cost more than a launch) the tree kernel, then
+ * lora_sgmv_expand's kernel.  The three-launch schedule needs 16-byte h rows:
+ * with h, a 16-byte aligned h with ld_h % 4 == 0; without h, it keeps h in
+ * workspace slice 0 (when r_max % 4 == 0); otherwise it takes the two-launch
+ * schedule.  Either way h and y are bit for bit
  * those of lora_sgmv_shrink(scales = shrink_scales) followed by
  * lora_sgmv_expand(scales = expand_scales); either scale array may be NULL
  * (all 1).  Arguments and requirements as for those two calls; h is
