@@ -805,9 +805,18 @@ int lora_sgmv_shrink_counted(const uint16_t* x, int64_t ld_x, const uint16_t* co
     c.h = h;
     c.ld_h = ld_h;
     c.scales = scales;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // large M: plan tiles of one adapter share the A loads, as in the two-pass
+    // shrink before its A-in-registers kernel
+    const int T = r_max <= 16 * kGroupTiles ? shrink_tiles_per_wg(M, split_k) : 1;
+    if (T > 1) {
+        const int64_t bound = (M + T - 1) / T * split_k;
+        return launch_status(
+            launch_sgmv_shrink_counted_multi(p, c, pl.waves, T, (int)(bound < 2048 ? bound : 2048), s));
+    }
     const int gt = sgmv_group_tiles(M, split_k, r_max);
     const int grid = sgmv_grid(M, split_k, r_max, gt);
-    return launch_status(launch_sgmv_shrink_counted(p, c, pl.waves, gt, grid, static_cast<hipStream_t>(stream)));
+    return launch_status(launch_sgmv_shrink_counted(p, c, pl.waves, gt, grid, s));
 }
 
 size_t lora_sgmv_plan_bytes(int64_t M)

@@ -185,6 +185,9 @@ hipError_t launch_shrink_counted(const ShrinkParams& p, const CounterParams& c, 
                                  int group_tiles, hipStream_t st);
 hipError_t launch_sgmv_shrink_counted(const ShrinkParams& p, const CounterParams& c, int waves, int group_tiles,
                                       int grid, hipStream_t st);
+// tiles_per_wg 2 or 4 plan tiles of one adapter per workgroup item, r_max <= 64
+hipError_t launch_sgmv_shrink_counted_multi(const ShrinkParams& p, const CounterParams& c, int waves,
+                                            int tiles_per_wg, int grid, hipStream_t st);
 hipError_t launch_splitk_tree(const TreeParams& p, int split_k, bool sgmv, hipStream_t st);
 hipError_t launch_fill_zero(float* h, int64_t ld_h, int64_t M, int ncols, hipStream_t st);
 

@@ -522,6 +522,75 @@ __global__ __launch_bounds__(W * 64) void k_sgmv_shrink_counted(ShrinkParams p, 
     }
 }
 
+// Large M, single launch: the items of k_sgmv_shrink_partial_multi (up to T
+// consecutive plan tiles of one adapter share the A loads; every rank tile
+// of r_max <= 64 in one workgroup) with the arrival-counter combine of
+// k_sgmv_shrink_counted per tile: partials stored at the coherence point,
+// then per tile one counter add; the split that arrives last evaluates the
+// tile's h (fixed tree, the adapter's shrink scale).  Tiles of tokens without
+// an adapter get zero h rows from their split-0 item.  Same bits as the
+// two-pass multi-adapter shrink.
+template <int RT, int W, int T>
+__global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_counted_multi(ShrinkParams p, CounterParams c)
+{
+    __shared__ float red[red_floats<RT, W>()];
+    __shared__ int flag;
+    const int ntiles = plan_tiles(p.tiles, p.M, p.n_adapters);
+    const uint32_t S = (uint32_t)p.split_k;
+    const uint32_t items = (uint32_t)((ntiles + T - 1) / T) * S;
+    const int32_t* plan = p.tiles + kPlanHeaderInts;
+    for (uint32_t it = blockIdx.x; it < items; it += gridDim.x) {
+        const int s = (int)(it % S);
+        const int c0 = (int)(it / S) * T;
+        const int c1 = c0 + T < ntiles ? c0 + T : ntiles;
+        int j = c0;
+        while (j < c1) {                          // uniform: plan data only
+            const int32_t* t = plan + 3 * j;
+            if (!tile_rows_ok(t, p.M)) {
+                ++j;
+                continue;
+            }
+            if (t[2] < 0 || t[2] >= p.n_adapters) {
+                if (s == 0)
+                    for (int e = threadIdx.x; e < t[1] * p.r_max; e += blockDim.x)
+                        c.h[(t[0] + e / p.r_max) * c.ld_h + e % p.r_max] = 0.0f;
+                ++j;
+                continue;
+            }
+            const int a = t[2];
+            int64_t row0[T];
+            int nrows[T];
+            int n = 0;
+#pragma unroll
+            for (int u = 0; u < T; ++u) {
+                const int32_t* tu = plan + 3 * (j + u);
+                const bool take = n == u && j + u < c1 && tile_ok(tu, p.M, p.n_adapters) && tu[2] == a;
+                row0[u] = take ? tu[0] : t[0];
+                nrows[u] = take ? tu[1] : 0;
+                n += take ? 1 : 0;
+            }
+            const int ra = adapter_rank(p, a);
+            if (ra > 0) {
+                shrink_tiles<RT, W, kToWorkspaceCoherent, T>(p, row0, nrows, p.A_ptrs[a], ra, 0, s, 1.0f, red);
+#pragma unroll
+                for (int u = 0; u < T; ++u) {
+                    if (u < n) {                  // uniform
+                        int32_t* counter = c.counters + (int64_t)(j + u) * kMaxRankTiles;
+                        if (arrived_last(counter, p.split_k, &flag)) {
+                            const float scale = c.scales ? c.scales[a] : 1.0f;
+                            combine_tile(p, row0[u], nrows[u], 0, ra, p.r_max, scale, c.h, c.ld_h);
+                            if (threadIdx.x == 0)
+                                __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        }
+                        __syncthreads();          // flag is reused
+                    }
+                }
+            }
+            j += n;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Second pass of the two-pass shrink: h = scale * tree(ws[0..S-1]).
 // ---------------------------------------------------------------------------
@@ -764,6 +833,40 @@ hipError_t launch_sgmv_shrink_partial_multi(const ShrinkParams& p, int waves, in
         launch_multi_t<2>(p, waves, rank_tiles, dim3((unsigned)grid), true, st);
     else
         launch_multi_t<4>(p, waves, rank_tiles, dim3((unsigned)grid), true, st);
+    return hipGetLastError();
+}
+
+namespace {
+
+template <int RT, int T>
+void launch_counted_multi_rt(const ShrinkParams& p, const CounterParams& c, int waves, dim3 grid, hipStream_t st)
+{
+    constexpr int TS = (RT > 2 && T > 2) ? 2 : T;   // as for the two-pass kernel: registers
+    switch (waves) {
+    case 1: hipLaunchKernelGGL((k_sgmv_shrink_counted_multi<RT, 1, TS>), grid, dim3(64), 0, st, p, c); break;
+    case 2: hipLaunchKernelGGL((k_sgmv_shrink_counted_multi<RT, 2, TS>), grid, dim3(128), 0, st, p, c); break;
+    case 4: hipLaunchKernelGGL((k_sgmv_shrink_counted_multi<RT, 4, TS>), grid, dim3(256), 0, st, p, c); break;
+    default: hipLaunchKernelGGL((k_sgmv_shrink_counted_multi<RT, 8, TS>), grid, dim3(512), 0, st, p, c); break;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_sgmv_shrink_counted_multi(const ShrinkParams& p, const CounterParams& c, int waves,
+                                            int tiles_per_wg, int grid, hipStream_t st)
+{
+    const int rank_tiles = (p.r_max + 15) / 16;
+    if (rank_tiles > kGroupTiles || grid < 1)
+        return hipErrorInvalidValue;
+    const dim3 g((unsigned)grid);
+    if (rank_tiles == 1)
+        tiles_per_wg == 2 ? launch_counted_multi_rt<1, 2>(p, c, waves, g, st)
+                          : launch_counted_multi_rt<1, 4>(p, c, waves, g, st);
+    else if (rank_tiles == 2)
+        tiles_per_wg == 2 ? launch_counted_multi_rt<2, 2>(p, c, waves, g, st)
+                          : launch_counted_multi_rt<2, 4>(p, c, waves, g, st);
+    else
+        launch_counted_multi_rt<4, 2>(p, c, waves, g, st);
     return hipGetLastError();
 }
 
