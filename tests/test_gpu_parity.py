@@ -1130,6 +1130,53 @@ def test_counted_shrinks_stress_repeats():
     assert int(cnt.abs().sum()) == 0 and int(cnt2.abs().sum()) == 0
 
 
+def test_sgmv_counted_large_m_repeats():
+    """The single-launch multi-adapter shrink at a large-M shape (1024 tokens,
+    K = 4096, Split-K 16, short runs of 4 adapters of ranks 64, 16, 37 and 8
+    and of tokens without one, so items mix tiles of several adapters): 200
+    back-to-back launches, each compared bit for bit on the GPU with the
+    two-pass result, and the counters back at zero."""
+    t = torch()
+    rng = np.random.default_rng(93)
+    ids = np.empty(1024, np.int32)
+    pos = 0
+    while pos < 1024:
+        run = int(rng.integers(3, 70))
+        ids[pos:pos + run] = rng.choice([-1, 0, 1, 2, 3])
+        pos += run
+    c = sgmv_case(1024, 4096, 64, [64, 16, 37, 8], 0, 0, 16, seed=94, tag="cs", ids=ids)
+    As = [bf16_to_gpu(a) for a in c.As]
+    Ap = t.tensor([a.data_ptr() for a in As], dtype=t.int64, device="cuda")
+    ranks = t.from_numpy(c.ranks).cuda()
+    scales = t.from_numpy(c.scales).cuda()
+    idg, plan = _build_plan(c.ids, 4)
+    xg = bf16_to_gpu(c.x)
+    ref = t.full((c.M, c.r_max), float("nan"), dtype=t.float32, device="cuda")
+    dsl.lora_sgmv_shrink(xg, Ap, c.K, ranks, scales, idg, 4, plan, ref, c.r_max, c.split_k,
+                         workspace(dsl.lora_sgmv_workspace_bytes(c.M, c.r_max, c.split_k)))
+    ws = workspace(dsl.lora_sgmv_workspace_bytes(c.M, c.r_max, c.split_k))
+    cnt = t.zeros(dsl.lora_sgmv_counter_bytes(c.M) // 4, dtype=t.int32, device="cuda")
+    h = t.empty_like(ref)
+    bad = t.zeros((), dtype=t.int64, device="cuda")
+    for _ in range(200):
+        h.fill_(float("nan"))
+        dsl.lora_sgmv_shrink_counted(xg, Ap, c.K, ranks, scales, 4, plan, h, c.r_max, c.split_k, ws, cnt)
+        bad += (h.view(t.int32) != ref.view(t.int32)).sum()
+    t.cuda.synchronize()
+    assert int(bad) == 0
+    assert int(cnt.abs().sum()) == 0
+    hh = h.cpu().numpy()
+    for i in range(0, c.M, 37):
+        a = int(c.ids[i])
+        if a < 0:
+            assert np.all(hh[i] == 0.0)
+            continue
+        r = int(c.ranks[a])
+        assert np.all(hh[i, r:] == 0.0)
+        check_shrink(hh[i:i + 1, :r], c.x[i:i + 1], c.As[a], float(c.scales[a]),
+                     dsl.lora_shrink_plan(c.K, r, c.split_k), f"large-M counted row {i}")
+
+
 # ---------------------------------------------------------------------------
 # single-launch shrink + expand with arrival counters
 # ---------------------------------------------------------------------------
