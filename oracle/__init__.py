@@ -28,6 +28,18 @@ the tests live in ``tests/test_oracle.py``):
                         h pinned by the paper's midpoint value.
 * ``sgmv_*``          - per-token equality with the single-adapter functions,
                         invalid ids leave rows untouched.
+* ``shrink_bounds``   - hand values on a 2 x 4 case with Pythagorean rows
+                        (norms 5, 13 and 1, 3) and mixed signs (sum|xA| = 22
+                        where the signed sum is 2); exact rationals on random
+                        tiny inputs; the Cauchy-Schwarz chain
+                        |h| <= sum|xA| <= ||x|| ||A|| on random inputs.
+* ``shrink_tolerance``- the same hand case with scale -2 (a transposed outer
+                        product, a lost |scale| or a squared norm all fail).
+* ``bf16_ulp``        - hand values at 1, 2, below 2, the smallest and largest
+                        subnormal, the smallest normal, zero and the largest
+                        finite value; every finite bf16 pattern against the
+                        gap to its successor (computed from the successor's
+                        bits, not from the exponent field).
 * ``expand_compensated`` - exact rational brute force (``exact.py``); the
                         hand-derived cases of tests/golden/compensated_expand.json
                         (where it and the plain expand differ); hi + lo equals h
@@ -280,14 +292,21 @@ def set_threads(n: int) -> int:
 # ----------------------------------------------------------------------------
 def shrink_tolerance(x, A, scale: float = 1.0) -> np.ndarray:
     """Per-element bound for an fp32 shrink: 1e-3 * |scale| * ||x_i||_2 * ||A_j||_2
-    (a Cauchy-Schwarz bound of the dot product, scaled by 1e-3)."""
+    for element (i, j) (token i, rank j): the Cauchy-Schwarz bound of that dot
+    product, scaled by 1e-3.  Shape [M, r]."""
     _, xn, an = shrink_bounds(x, A)
     return 1e-3 * abs(scale) * np.outer(xn, an)
 
 
 def bf16_ulp(bits) -> np.ndarray:
-    """Distance from |v| to the next bf16 value away from zero, v given as bf16 bits."""
-    b = _u16(bits) & np.uint16(0x7FFF)
-    v = bf16_to_f64(b)
-    nxt = bf16_to_f64((b.astype(np.uint32) + 1).astype(np.uint16))
-    return np.abs(nxt - v)
+    """Spacing of the bf16 values in the binade of |v| (v given as bf16 bits),
+    i.e. the distance from |v| to the next bf16 magnitude above it, taken as
+    if the exponent range were unbounded: 2^(E-7) for 2^E <= |v| < 2^(E+1)
+    (8 significant bits), 2^-133 for the subnormals and zero.  At a power of
+    two this is the larger of the two neighbouring gaps, and at the largest
+    finite value it is 2^120 (the gap to the next value is not infinite).
+    NaN for infinities and NaNs."""
+    b = _u16(bits).astype(np.int64) & 0x7FFF
+    e = b >> 7                                    # biased exponent field
+    out = np.where(e == 0, 2.0 ** -133, np.exp2(np.maximum(e, 1) - 127 - 7))
+    return np.where(e == 0xFF, np.nan, out).reshape(np.shape(bits))

@@ -63,18 +63,32 @@ def check_shrink(h_gpu: np.ndarray, x, A, scale: float, plan: dict, what: str = 
     return float(np.max(err / tol)), float(np.max(err / rb))
 
 
+def expand_floor(r):
+    """Coefficient c of the fp32 cancellation floor c 2^-24 (|y| + |s| sum|hb B|).
+
+    The GPU forms acc = sum_{j<r} bf16(h_j) B_jn in fp32 over one, two or four
+    chained matrix-core steps: the products are exact and zero-padded slots add
+    exactly, so with every fp32 addition rounded to nearest, in any order,
+    |acc - sum| <= (r - 1) 2^-24 sum|hb B| to first order.  Then one fused
+    multiply-add v = fl(s acc + y) adds 2^-24 |v|.  Together
+    |v - e| <= r 2^-24 (|y| + |s| sum|hb B|) + O(2^-48); r + 2 keeps the
+    second-order terms inside.  The last rounding, bf16(v), is within half the
+    bf16 spacing at v, which is at most bf16_ulp(o) of the oracle's correctly
+    rounded value o, so |y_gpu - e| <= bf16_ulp(o) + floor."""
+    return np.asarray(r, dtype=np.float64) + 2.0
+
+
 def check_expand(y_gpu: np.ndarray, yo: np.ndarray, e: np.ndarray, absum: np.ndarray, y_in: np.ndarray,
-                 what: str = "", r: int = 64):
-    """|y_gpu - e| <= 1 bf16 ulp of the oracle's rounded value plus the fp32
-    accumulation floor c 2^-24 (|y| + |s| sum|hb B|), c = max(100, r + 36),
-    that matters only under cancellation: r products summed in fp32 over at
-    most four chained matrix-core steps, one fused multiply-add.  Returns the
-    fraction of elements that differ from the oracle's correctly rounded
-    value."""
+                 what: str, r: int):
+    """|y_gpu - e| <= bf16_ulp(o) + (r + 2) 2^-24 (|y| + |s| sum|hb B|) per
+    element (expand_floor); the floor matters only under cancellation.  r is
+    the rank, or an array of per-row ranks broadcast against the rows.
+    Returns the fraction of elements that differ from the oracle's correctly
+    rounded value."""
     got = oracle.bf16_to_f64(y_gpu)
     ulp = oracle.bf16_ulp(yo)
     yv = np.abs(oracle.bf16_to_f64(y_in))
-    floor = max(100, r + 36) * 2.0 ** -24 * (yv + absum)
+    floor = expand_floor(r) * 2.0 ** -24 * (yv + absum)
     err = np.abs(got - e)
     ok = err <= ulp + floor
     assert np.all(ok), f"{what}: expand beyond 1 bf16 ulp at {np.argwhere(~ok)[:5].tolist()}"

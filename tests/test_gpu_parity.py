@@ -353,7 +353,7 @@ def test_batch_invariance_sweep():
     # and the probe rows are right
     check_shrink(ref_h.view(np.float32), probe, A, 1.0, dsl.lora_shrink_plan(K, r, S), "probe")
     yo, e, ab = oracle.expand(ref_h.view(np.float32), B, ybase, 2.0)
-    check_expand(ref_y, yo, e, ab, ybase, "probe expand")
+    check_expand(ref_y, yo, e, ab, ybase, "probe expand", r=r)
 
 
 def test_atomic_variant_varies_on_crafted_input():
@@ -486,7 +486,10 @@ def _check_sgmv(c, h, y, rows, label):
         check_shrink(h[i:i + 1, :r], c.x[i:i + 1], c.As[a], float(c.scales[a]),
                      dsl.lora_shrink_plan(c.K, r, c.split_k), f"{label} row {i}")
     yo, e, ab = oracle.sgmv_expand(h[rows], c.Bs, c.ranks, c.scales, c.ids[rows], c.y[rows])
-    return check_expand(y[rows], yo, e, ab, c.y[rows], label, r=int(c.r_max))
+    ids_r = c.ids[rows]
+    valid = (ids_r >= 0) & (ids_r < len(c.ranks))
+    row_rank = np.where(valid, c.ranks[np.where(valid, ids_r, 0)], 0)[:, None]
+    return check_expand(y[rows], yo, e, ab, c.y[rows], label, r=row_rank)
 
 
 def test_sgmv_fused_qkv_parity():
@@ -898,7 +901,7 @@ def test_expand_combine_on_given_workspace(S):
     want_h = oracle.combine_tree_f32(P, 0.75)
     assert np.array_equal(f32_bits(h), f32_bits_np(want_h))
     yo, e, ab = oracle.expand(want_h, B, y, 2.0)
-    check_expand(bf16_from_gpu(yg), yo, e, ab, y, f"combine S={S}")
+    check_expand(bf16_from_gpu(yg), yo, e, ab, y, f"combine S={S}", r=r)
 
 
 @pytest.mark.parametrize("M,K,r,S", [(1, 4096, 16, 8), (33, 8192, 64, 16), (20, 1024, 8, 8)])
@@ -1348,7 +1351,7 @@ def test_sgmv_expand_large_m_tiles_bitwise():
         assert np.array_equal(bf16_from_gpu(ys), got[sel]), f"adapter {a}"
         pick = sel[rng.choice(len(sel), min(8, len(sel)), replace=False)]
         yo, e, ab = oracle.expand(h[pick, :r], Bs[a], y[pick], float(scales[a]))
-        check_expand(got[pick], yo, e, ab, y[pick], f"sgmv large-M adapter {a}")
+        check_expand(got[pick], yo, e, ab, y[pick], f"sgmv large-M adapter {a}", r=r)
 
 
 # ---------------------------------------------------------------------------

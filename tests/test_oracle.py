@@ -403,3 +403,106 @@ def test_expand_compensated_equals_plain_for_bf16_inputs():
     a, ea, _ = oracle.expand_compensated(h, B, y, 2.0)
     b, eb, _ = oracle.expand(h, B, y, 2.0)
     assert np.array_equal(a, b) and np.array_equal(ea, eb)
+
+
+# ---------------------------------------------------------------------------
+# tolerance helpers: the norms, |x A| sums and bf16 spacing the parity tests
+# compare against (a slip here would silently loosen every GPU check)
+# ---------------------------------------------------------------------------
+def _bf16_exact(vals):
+    return _exact_bf16_bits(np.asarray(vals, dtype=np.float64))
+
+
+def test_shrink_bounds_hand_values():
+    """x rows (3, 4, 0, 0) and (0, 0, 5, 12) have norms 5 and 13; A rows
+    (1, 0, 0, 0) and (0, 2, -2, 1) have norms 1 and 3.  sum_k |x_ik A_jk|:
+    (0,0) 3, (0,1) 8, (1,0) 0, (1,1) |5 * -2| + |12 * 1| = 22, where the signed
+    sum is 2.  Norms over the wrong axis would have length K = 4, not 2."""
+    x = _bf16_exact([[3, 4, 0, 0], [0, 0, 5, 12]])
+    A = _bf16_exact([[1, 0, 0, 0], [0, 2, -2, 1]])
+    absum, xn, an = oracle.shrink_bounds(x, A)
+    assert xn.shape == (2,) and an.shape == (2,) and absum.shape == (2, 2)
+    assert xn.tolist() == [5.0, 13.0]
+    assert an.tolist() == [1.0, 3.0]
+    assert absum.tolist() == [[3.0, 8.0], [0.0, 22.0]]
+    assert oracle.shrink(x, A, 1.0).tolist() == [[3.0, 8.0], [0.0, 2.0]]
+
+
+def test_shrink_tolerance_hand_values():
+    """1e-3 |s| ||x_i|| ||A_j|| with s = -2 on the case above:
+    [[10, 30], [26, 78]] * 1e-3 (the transpose would be [[10, 26], [30, 78]])."""
+    x = _bf16_exact([[3, 4, 0, 0], [0, 0, 5, 12]])
+    A = _bf16_exact([[1, 0, 0, 0], [0, 2, -2, 1]])
+    tol = oracle.shrink_tolerance(x, A, -2.0)
+    want = np.array([[10.0, 30.0], [26.0, 78.0]]) * 1e-3
+    assert tol.shape == (2, 2)
+    assert np.allclose(tol, want, rtol=1e-15, atol=0)
+    # M != r: the shape follows (tokens, ranks)
+    x3 = _bf16_exact([[3, 4, 0, 0], [0, 0, 5, 12], [1, 0, 0, 0]])
+    assert oracle.shrink_tolerance(x3, A, 1.0).shape == (3, 2)
+
+
+@pytest.mark.parametrize("M,K,r,seed", [(2, 8, 3, 0), (3, 24, 2, 1), (1, 64, 4, 2)])
+def test_shrink_bounds_against_exact_rationals(M, K, r, seed):
+    import math
+    x = normal_bf16((M, K), 1.0, seed, "bx")
+    A = normal_bf16((r, K), 0.5, seed, "bA")
+    absum, xn, an = oracle.shrink_bounds(x, A)
+    X = [[exact.bf16_bits_to_fraction(v) for v in row] for row in x]
+    Am = [[exact.bf16_bits_to_fraction(v) for v in row] for row in A]
+    for i in range(M):
+        sq = sum(v * v for v in X[i])
+        assert abs(xn[i] - math.sqrt(float(sq))) <= 2.0 ** -50 * xn[i]
+        for j in range(r):
+            s = sum(abs(X[i][k] * Am[j][k]) for k in range(K))
+            assert abs(Fraction(float(absum[i, j])) - s) <= s * Fraction(K, 2 ** 53)
+    for j in range(r):
+        sq = sum(v * v for v in Am[j])
+        assert abs(an[j] - math.sqrt(float(sq))) <= 2.0 ** -50 * an[j]
+
+
+def test_shrink_bounds_cauchy_schwarz_chain():
+    """|h_ij| <= sum_k |x_ik A_jk| <= ||x_i|| ||A_j|| on random inputs, with
+    the middle inequality strict somewhere (it is not an identity)."""
+    x = normal_bf16((6, 512), 1.0, 3, "cx")
+    A = normal_bf16((5, 512), 0.02, 3, "cA")
+    h = oracle.shrink(x, A, 1.0)
+    absum, xn, an = oracle.shrink_bounds(x, A)
+    cs = np.outer(xn, an)
+    assert np.all(np.abs(h) <= absum * (1 + 1e-12))
+    assert np.all(absum <= cs * (1 + 1e-12))
+    assert np.any(absum < 0.9 * cs) and np.any(np.abs(h) < 0.5 * absum)
+
+
+def test_bf16_ulp_hand_values():
+    cases = {
+        0x3F80: 2.0 ** -7,       # 1.0
+        0xBF80: 2.0 ** -7,       # -1.0: the sign does not matter
+        0x3FFF: 2.0 ** -7,       # 1.9921875, the last value below 2
+        0x4000: 2.0 ** -6,       # 2.0: the gap above a power of two
+        0x0000: 2.0 ** -133,     # +0
+        0x8000: 2.0 ** -133,     # -0
+        0x0001: 2.0 ** -133,     # smallest subnormal
+        0x007F: 2.0 ** -133,     # largest subnormal
+        0x0080: 2.0 ** -133,     # smallest normal 2^-126
+        0x0100: 2.0 ** -132,     # 2^-125
+        0x7F7F: 2.0 ** 120,      # largest finite (2 - 2^-7) 2^127: finite spacing
+        0x3C23: 2.0 ** -14,      # 0.00994873046875 = 163 * 2^-14 (binade [2^-7, 2^-6))
+    }
+    bits = np.array(list(cases), dtype=np.uint16)
+    assert oracle.bf16_ulp(bits).tolist() == list(cases.values())
+    assert np.all(np.isnan(oracle.bf16_ulp(np.array([0x7F80, 0xFF80, 0x7FC0], np.uint16))))
+    # the shape follows the input
+    assert oracle.bf16_ulp(np.zeros((2, 3), np.uint16)).shape == (2, 3)
+
+
+def test_bf16_ulp_is_the_gap_to_the_successor():
+    """For every finite bf16 magnitude below the largest, the spacing equals
+    value(bits + 1) - value(bits), computed from the successor's bit pattern."""
+    b = np.arange(0, 0x7F7F, dtype=np.uint32)            # +0 .. the value below the largest finite
+    val = (b << 16).view(np.float32).astype(np.float64)
+    nxt = ((b + 1) << 16).view(np.float32).astype(np.float64)
+    got = oracle.bf16_ulp(b.astype(np.uint16))
+    assert np.array_equal(got, nxt - val)
+    neg = (b | 0x8000).astype(np.uint16)
+    assert np.array_equal(oracle.bf16_ulp(neg), nxt - val)
