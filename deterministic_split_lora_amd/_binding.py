@@ -22,6 +22,7 @@ LORA_ERR_UNSUPPORTED = 3
 LORA_ERR_ALIGN = 4
 LORA_ERR_WORKSPACE = 5
 LORA_ERR_LAUNCH = 6
+LORA_ERR_SCRATCH = 7
 
 EXPORTED = [
     "lora_abi_version", "lora_status_str", "lora_shrink_plan", "lora_shrink_workspace_bytes",
@@ -31,7 +32,7 @@ EXPORTED = [
     "lora_shrink_expand_fused", "lora_shrink_expand_launches", "lora_shrink_counter_bytes",
     "lora_shrink_splitk_counted", "lora_sgmv_counter_bytes", "lora_sgmv_shrink_counted",
     "lora_shrink_expand_counter_bytes", "lora_shrink_expand_counted", "lora_expand_compensated",
-    "lora_sgmv_shrink_expand",
+    "lora_sgmv_shrink_expand", "lora_shrink_expand_noalloc",
 ]
 
 
@@ -57,7 +58,7 @@ _f32 = ctypes.c_float
 _sz = ctypes.c_size_t
 
 # LORA_DET_ABI_VERSION of include/lora_det.h that these signatures follow.
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 def lib():
@@ -94,6 +95,9 @@ def lib():
         L.lora_shrink_expand.restype = ctypes.c_int
         L.lora_shrink_expand.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32,
                                          _i64, _i32, _f32, _f32, _vp, _sz, _vp]
+        L.lora_shrink_expand_noalloc.restype = ctypes.c_int
+        L.lora_shrink_expand_noalloc.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
+                                                 _i32, _i64, _i32, _f32, _f32, _vp]
         L.lora_shrink_expand_counter_bytes.restype = _sz
         L.lora_shrink_expand_counter_bytes.argtypes = [_i64]
         L.lora_shrink_expand_counted.restype = ctypes.c_int
@@ -308,6 +312,33 @@ def lora_shrink_expand(x, A, B, y, workspace, split_k: int = 8, shrink_scale: fl
                                   shrink_scale, expand_scale, _ptr(workspace), _nbytes(workspace),
                                   _stream(stream, x))
     _check(st, "lora_shrink_expand")
+    return y
+
+
+# LORA_NOALLOC_SCRATCH_BYTES of include/lora_det.h
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def lora_shrink_expand_noalloc(x, A, B, y, split_k: int = 8, shrink_scale: float = 1.0, expand_scale: float = 1.0,
+                               h=None, stream=None):
+    """lora_shrink_expand with the library's fixed scratch buffer as the
+    workspace (nothing allocated); split_k * M * r * 4 must not exceed
+    NOALLOC_SCRATCH_BYTES.  Calls that may overlap on one device race on the
+    buffer."""
+    import torch
+    _dtype(x, torch.bfloat16, "x"); _dtype(A, torch.bfloat16, "A")
+    _dtype(B, torch.bfloat16, "B"); _dtype(y, torch.bfloat16, "y")
+    if h is not None:
+        _dtype(h, torch.float32, "h")
+    M, K = x.shape
+    r = A.shape[0]
+    N = y.shape[1]
+    if y.shape[0] != M:
+        raise ValueError("x and y must have the same number of rows")
+    st = lib().lora_shrink_expand_noalloc(_ptr(x), _ld(x, "x"), _ptr(A), _ld(A, "A"), _ptr(B), _ld(B, "B"),
+                                          _ptr(h), _ld(h, "h") if h is not None else 0, _ptr(y), _ld(y, "y"), M, K,
+                                          r, N, split_k, shrink_scale, expand_scale, _stream(stream, x))
+    _check(st, "lora_shrink_expand_noalloc")
     return y
 
 

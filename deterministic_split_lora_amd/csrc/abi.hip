@@ -7,7 +7,18 @@
 #include "../../include/lora_det.h"
 #include "kernels.h"
 
+#include <atomic>
+#include <mutex>
+
 using namespace lora;
+
+// Fixed Split-K workspace of lora_shrink_expand_noalloc, for callers that
+// cannot allocate: one copy per device, created with the code object and held
+// until the process ends.  In host code the name stands for a host-side
+// handle, never a device address: the device address comes from
+// hipGetSymbolAddress (scratch_for_device) and only that address is passed
+// to kernels.
+static __device__ __align__(256) float scratch[LORA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace {
 
@@ -370,6 +381,39 @@ int expand_entry(const float* h, int64_t ld_h, const uint16_t* B, int64_t ld_b, 
 }
 
 
+// Device address of `scratch` on `dev`, looked up once per device with that
+// device current (hipGetSymbolAddress) and cached; later calls read the cache
+// without a lock.
+constexpr int kScratchMaxDevices = 64;
+std::atomic<void*> g_scratch_addr[kScratchMaxDevices];
+std::mutex g_scratch_lock;
+
+int scratch_for_device(int dev, void** out)
+{
+    if (dev < 0 || dev >= kScratchMaxDevices)
+        return LORA_ERR_LAUNCH;
+    void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        std::lock_guard<std::mutex> guard(g_scratch_lock);
+        p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+        if (p == nullptr) {
+            int prev = -1;
+            if (hipGetDevice(&prev) != hipSuccess)
+                return LORA_ERR_LAUNCH;
+            if (prev != dev && hipSetDevice(dev) != hipSuccess)
+                return LORA_ERR_LAUNCH;
+            const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (prev != dev)
+                (void)hipSetDevice(prev);
+            if (e != hipSuccess || p == nullptr)
+                return LORA_ERR_LAUNCH;
+            g_scratch_addr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return LORA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -392,6 +436,7 @@ const char* lora_status_str(int status)
     case LORA_ERR_ALIGN: return "pointer or leading dimension not 16-byte aligned";
     case LORA_ERR_WORKSPACE: return "workspace or plan buffer too small";
     case LORA_ERR_LAUNCH: return "kernel launch failed";
+    case LORA_ERR_SCRATCH: return "needs more than the library's fixed scratch buffer";
     default: return "unknown status";
     }
 }
@@ -643,6 +688,40 @@ int lora_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64
     if (st != LORA_OK)
         return st;
     return lora_expand(hh, ldh, B, ld_b, y, ld_y, M, r, N, expand_scale, stream);
+}
+
+int lora_shrink_expand_noalloc(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a,
+                               const uint16_t* B, int64_t ld_b, float* h, int64_t ld_h, uint16_t* y,
+                               int64_t ld_y, int64_t M, int64_t K, int32_t r, int64_t N, int32_t split_k,
+                               float shrink_scale, float expand_scale, void* stream)
+{
+    // sizes first: a call the fixed buffer cannot hold is refused before any
+    // HIP call, whatever the pointers
+    if (M < 0 || M > kMaxDim || N < 0 || N > kMaxDim)
+        return LORA_ERR_SHAPE;
+    lora_shrink_plan_t pl;
+    const int st = make_plan(K, r, split_k, &pl);
+    if (st != LORA_OK)
+        return st;
+    const size_t need = workspace_bytes(M, r, split_k);
+    if (need > LORA_NOALLOC_SCRATCH_BYTES)
+        return LORA_ERR_SCRATCH;
+    if (M == 0 || N == 0)
+        return LORA_OK;
+    if (!x || !A || !B || !y)
+        return LORA_ERR_NULL;
+    int dev = -1;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if ((s != nullptr ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev)) != hipSuccess)
+        return LORA_ERR_LAUNCH;
+    void* ws = nullptr;
+    const int sc = scratch_for_device(dev, &ws);
+    if (sc != LORA_OK)
+        return sc;
+    // the two-pass schedules write every workspace element they read, so the
+    // buffer needs no clearing between calls
+    return lora_shrink_expand(x, ld_x, A, ld_a, B, ld_b, h, ld_h, y, ld_y, M, K, r, N, split_k, shrink_scale,
+                              expand_scale, ws, LORA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 size_t lora_shrink_expand_counter_bytes(int64_t M)

@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define LORA_DET_ABI_VERSION 3
+#define LORA_DET_ABI_VERSION 4
 
 enum lora_status {
     LORA_OK = 0,
@@ -71,7 +71,8 @@ enum lora_status {
     LORA_ERR_UNSUPPORTED = 3, /* rank, split count or K divisibility outside the supported set */
     LORA_ERR_ALIGN = 4,       /* pointer or leading dimension breaks the 16-byte rule */
     LORA_ERR_WORKSPACE = 5,   /* workspace or plan buffer smaller than required */
-    LORA_ERR_LAUNCH = 6       /* the HIP runtime refused a kernel launch */
+    LORA_ERR_LAUNCH = 6,      /* the HIP runtime refused a kernel launch */
+    LORA_ERR_SCRATCH = 7      /* lora_shrink_expand_noalloc: more workspace than its fixed buffer */
 };
 
 /* Returns LORA_DET_ABI_VERSION of the built library. */
@@ -256,6 +257,35 @@ int lora_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64
                        uint16_t* y, int64_t ld_y, int64_t M, int64_t K, int32_t r, int64_t N,
                        int32_t split_k, float shrink_scale, float expand_scale,
                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * lora_shrink_expand_noalloc: lora_shrink_expand for callers that cannot
+ * allocate device memory (code being captured into a HIP graph, tight serving
+ * loops, harnesses that forbid allocation).  Same arguments without the
+ * workspace, same launches, same h and y bit for bit.  The Split-K workspace is
+ * a fixed buffer of LORA_NOALLOC_SCRATCH_BYTES inside the library (a static
+ * device array, one per device, created with the library's code object on that
+ * device and held until the process ends); the call allocates nothing.
+ *
+ * Limit: split_k * M * r * 4 <= LORA_NOALLOC_SCRATCH_BYTES (8 MiB: e.g.
+ * M <= 4096 at r = 64, split_k = 8), otherwise LORA_ERR_SCRATCH, checked on the
+ * host before any HIP call.  The first call on a device looks the buffer's
+ * address up (hipGetSymbolAddress, with that device current; LORA_ERR_LAUNCH
+ * if it fails) and caches it.  The device is the stream's (the current device
+ * for a NULL stream).
+ *
+ * Every call on one device uses the same buffer, which keeps the last call's
+ * partials: calls that may overlap on one device (different streams, or
+ * threads enqueueing concurrently) race on it and must be ordered by the
+ * caller.  The buffer needs no clearing: each call writes every element it
+ * later reads.
+ */
+#define LORA_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+int lora_shrink_expand_noalloc(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a,
+                               const uint16_t* B, int64_t ld_b, float* h, int64_t ld_h,
+                               uint16_t* y, int64_t ld_y, int64_t M, int64_t K, int32_t r, int64_t N,
+                               int32_t split_k, float shrink_scale, float expand_scale, void* stream);
 
 /*
  * lora_shrink_expand_counted: the same h and y as lora_shrink_expand in ONE

@@ -36,13 +36,13 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert dsl.lora_abi_version() == 3
+    assert dsl.lora_abi_version() == 4
     seen = set()
-    for s in range(0, 7):
+    for s in range(0, 8):
         t = dsl.lora_status_str(s)
         assert t and t != "unknown status"
         seen.add(t)
-    assert len(seen) == 7
+    assert len(seen) == 8
     assert dsl.lora_status_str(99) == "unknown status"
 
 
@@ -428,3 +428,21 @@ def test_sgmv_shrink_expand_rejects():
     assert call(pb=pb - 4) == B.LORA_ERR_WORKSPACE
     assert call(wsb=wsb - 4) == B.LORA_ERR_WORKSPACE
     assert call(M=0, x=None, ws=None) == B.LORA_OK
+
+
+def test_noalloc_rejects_sizes_beyond_its_scratch_buffer():
+    """split_k * M * r * 4 above the fixed 8 MiB buffer is refused on the host,
+    before any pointer is looked at or any HIP call is made; the limit itself
+    passes the size check (and then fails on the NULL pointers)."""
+    L = dsl.lib()
+    assert B.NOALLOC_SCRATCH_BYTES == 8 << 20
+    args = lambda M, r, S: (None, 4096, None, 4096, None, 64, None, 0, None, 4096, M, 4096, r, 4096, S,
+                            ctypes.c_float(1.0), ctypes.c_float(2.0), None)
+    # 8 * 4096 * 64 * 4 = 8 MiB: fits; one more token does not
+    assert L.lora_shrink_expand_noalloc(*args(4096, 64, 8)) == B.LORA_ERR_NULL
+    assert L.lora_shrink_expand_noalloc(*args(4097, 64, 8)) == B.LORA_ERR_SCRATCH
+    assert L.lora_shrink_expand_noalloc(*args(1 << 20, 16, 16)) == B.LORA_ERR_SCRATCH
+    # the usual shape and plan checks come first
+    assert L.lora_shrink_expand_noalloc(*args(-1, 16, 8)) == B.LORA_ERR_SHAPE
+    assert L.lora_shrink_expand_noalloc(*args(16, 16, 3)) == B.LORA_ERR_UNSUPPORTED
+    assert L.lora_shrink_expand_noalloc(*args(0, 16, 8)) == B.LORA_OK
