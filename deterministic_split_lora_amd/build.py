@@ -40,22 +40,43 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source; always recompiles (a cross-compile, no GPU needed)."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(os.path.dirname(HERE), "include"), *srcs, "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
-    # hipcc's host pass does not know the packed-fp32 feature and says so; that
-    # warning is harmless and filtered here
+    """Compile every source; always recompiles (a cross-compile, no GPU needed).
+    Each source is compiled to an object in parallel, then the objects are
+    linked into the shared library."""
+    from concurrent.futures import ThreadPoolExecutor
+    inc = ["-I", os.path.join(os.path.dirname(HERE), "include")]
+    tag = "%d" % os.getpid()
+    objs = [os.path.join(CSRC, os.path.splitext(s)[0] + ".o.tmp" + tag) for s in SOURCES]
+    compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"]
     noise = "'-packed-fp32-ops' is not a recognized feature"
-    err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + err)
-    if verbose and err.strip():
-        print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
+
+    def run(cmd):
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        # hipcc's host pass does not know the packed-fp32 feature and says so;
+        # that warning is harmless and filtered here
+        return res.returncode, "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+
+    try:
+        jobs = [[hipcc(), *compile_flags, *inc, "-c", os.path.join(CSRC, s), "-o", o]
+                for s, o in zip(SOURCES, objs)]
+        with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
+            results = list(ex.map(run, jobs))
+        errs = "\n".join(e for _, e in results if e.strip())
+        if any(rc != 0 for rc, _ in results):
+            raise RuntimeError("hipcc failed:\n" + errs)
+        if verbose and errs:
+            print(errs, file=sys.stderr)
+        tmp = LIB + ".tmp" + tag
+        rc, err = run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp])
+        if rc != 0:
+            raise RuntimeError("hipcc link failed:\n" + err)
+        os.replace(tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
     return LIB
 
 
