@@ -33,6 +33,7 @@ EXPORTED = [
     "lora_shrink_splitk_counted", "lora_sgmv_counter_bytes", "lora_sgmv_shrink_counted",
     "lora_shrink_expand_counter_bytes", "lora_shrink_expand_counted", "lora_expand_compensated",
     "lora_sgmv_shrink_expand", "lora_shrink_expand_noalloc",
+    "lora_sgmv_shrink_atomic",
 ]
 
 
@@ -95,6 +96,9 @@ def lib():
         L.lora_shrink_expand.restype = ctypes.c_int
         L.lora_shrink_expand.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i32,
                                          _i64, _i32, _f32, _f32, _vp, _sz, _vp]
+        L.lora_sgmv_shrink_atomic.restype = ctypes.c_int
+        L.lora_sgmv_shrink_atomic.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _i32, _vp, _sz, _vp, _i64, _i64, _i64,
+                                              _i32, _i32, _vp]
         L.lora_shrink_expand_noalloc.restype = ctypes.c_int
         L.lora_shrink_expand_noalloc.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64,
                                                  _i32, _i64, _i32, _f32, _f32, _vp]
@@ -465,6 +469,23 @@ def lora_sgmv_shrink_counted(x, A_ptrs, ld_a: int, ranks, scales, n_adapters: in
                                         split_k, _ptr(workspace), _nbytes(workspace), _ptr(counters),
                                         _nbytes(counters), _stream(stream, x))
     _check(st, "lora_sgmv_shrink_counted")
+    return h
+
+
+def lora_sgmv_shrink_atomic(x, A_ptrs, ld_a: int, ranks, scales, n_adapters: int, plan, h, r_max: int,
+                            split_k: int, stream=None):
+    """The nondeterministic contrast: zero h, then the multi-adapter partial
+    kernel adds every split's scaled partial into h with fp32 atomics."""
+    import torch
+    _dtype(x, torch.bfloat16, "x"); _dtype(h, torch.float32, "h")
+    _dtype(A_ptrs, torch.int64, "A_ptrs"); _dtype(ranks, torch.int32, "ranks")
+    if scales is not None:
+        _dtype(scales, torch.float32, "scales")
+    M, K = x.shape
+    st = lib().lora_sgmv_shrink_atomic(_ptr(x), _ld(x, "x"), _ptr(A_ptrs), ld_a, _ptr(ranks), _ptr(scales),
+                                       n_adapters, _ptr(plan), _nbytes(plan), _ptr(h), _ld(h, "h"), M, K, r_max,
+                                       split_k, _stream(stream, x))
+    _check(st, "lora_sgmv_shrink_atomic")
     return h
 
 

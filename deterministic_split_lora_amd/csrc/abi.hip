@@ -132,20 +132,24 @@ int stream_rows_per_item(int64_t tiles, const lora_shrink_plan_t& pl)
     return R < 4 ? 4 : (R > 16 ? 16 : (int)R);
 }
 
-// The Split-K partial kernel of the deterministic two-pass paths.
+// The Split-K partial kernel of the deterministic two-pass paths; with
+// `atomic`, the same kernel and work items for the nondeterministic contrast,
+// each split's scaled partial atomically added into p.out = h.
 hipError_t launch_partials(const ShrinkParams& p, const lora_shrink_plan_t& pl, int64_t M, int32_t split_k,
-                           hipStream_t st)
+                           hipStream_t st, bool atomic = false)
 {
     const int64_t tiles = (M + kRowBlock - 1) / kRowBlock;
     const int R = stream_rows_per_item(tiles, pl);
     if (R > 0)
         return launch_shrink_stream(p, pl.waves, pl.k_steps, pl.rank_tiles, R,
-                                    (int)((tiles + R - 1) / R * split_k), false, st);
+                                    (int)((tiles + R - 1) / R * split_k), false, st, atomic);
     // several row blocks per workgroup hold all rank tiles at once: ranks <= 64
     const int T = pl.rank_tiles <= kGroupTiles ? shrink_tiles_per_wg(M, split_k) : 1;
     if (T > 1)
-        return launch_shrink_partial_multi(p, pl.waves, pl.rank_tiles, T, st);
-    return launch_shrink_partial_ws(p, pl.waves, pl.rank_tiles, group_tiles_for(M, split_k, pl.rank_tiles), st);
+        return launch_shrink_partial_multi(p, pl.waves, pl.rank_tiles, T, st, atomic);
+    const int gt = group_tiles_for(M, split_k, pl.rank_tiles);
+    return atomic ? launch_shrink_partial_atomic(p, pl.waves, pl.rank_tiles, gt, st)
+                  : launch_shrink_partial_ws(p, pl.waves, pl.rank_tiles, gt, st);
 }
 
 // Checks shared by the single-adapter shrinks.
@@ -277,9 +281,13 @@ int launch_fused(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_
 }
 
 // The partial kernel of the multi-adapter two-pass shrink (arguments checked).
+// With `atomic` (the nondeterministic contrast) the same kernel and work items
+// add each split's partial times the adapter's scale into h (`workspace` is
+// then h, with row stride ld_h) instead of storing it.
 int launch_sgmv_partials(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_ptrs, int64_t ld_a,
                          const int32_t* ranks, int32_t n_adapters, const void* plan, int64_t M, int32_t r_max,
-                         const lora_shrink_plan_t& pl, void* workspace, hipStream_t s)
+                         const lora_shrink_plan_t& pl, void* workspace, hipStream_t s, bool atomic = false,
+                         const float* scales = nullptr, int64_t ld_h = 0)
 {
     ShrinkParams p{};
     p.x = x;
@@ -289,8 +297,9 @@ int launch_sgmv_partials(const uint16_t* x, int64_t ld_x, const uint16_t* const*
     p.ranks = ranks;
     p.tiles = static_cast<const int32_t*>(plan);
     p.out = static_cast<float*>(workspace);
-    p.ld_out = r_max;
-    p.split_stride = M * r_max;
+    p.ld_out = atomic ? ld_h : r_max;
+    p.split_stride = atomic ? 0 : M * r_max;
+    p.scales = scales;
     p.M = M;
     p.r = r_max;
     p.r_max = r_max;
@@ -311,17 +320,17 @@ int launch_sgmv_partials(const uint16_t* x, int64_t ld_x, const uint16_t* const*
         const int64_t grid = (est + R - 1) / R * pl.split_k;
         return launch_status(launch_shrink_stream(p, pl.waves, pl.k_steps, ps.rank_tiles, R,
                                                   (int)(grid < 65536 ? grid : 65536 / pl.split_k * pl.split_k),
-                                                  true, s));
+                                                  true, s, atomic));
     }
     const int T = r_max <= 16 * kGroupTiles ? shrink_tiles_per_wg(M, pl.split_k) : 1;
     if (T > 1) {
         const int64_t bound = (M + T - 1) / T * pl.split_k;
         return launch_status(
-            launch_sgmv_shrink_partial_multi(p, pl.waves, T, (int)(bound < 2048 ? bound : 2048), s));
+            launch_sgmv_shrink_partial_multi(p, pl.waves, T, (int)(bound < 2048 ? bound : 2048), s, atomic));
     }
     const int gt = sgmv_group_tiles(M, pl.split_k, r_max);
     const int grid = sgmv_grid(M, pl.split_k, r_max, gt);
-    return launch_status(launch_sgmv_shrink_partial(p, pl.waves, gt, grid, s));
+    return launch_status(launch_sgmv_shrink_partial(p, pl.waves, gt, grid, s, atomic));
 }
 
 // Second pass of the multi-adapter shrink over a [split_k][M][r_max] workspace.
@@ -515,8 +524,8 @@ int lora_shrink_splitk_atomic(const uint16_t* x, int64_t ld_x, const uint16_t* A
     ShrinkParams p = shrink_params(x, ld_x, A, ld_a, M, r, pl, scale);
     p.out = h;
     p.ld_out = ld_h;
-    return launch_status(launch_shrink_partial_atomic(p, pl.waves, pl.rank_tiles,
-                                                      group_tiles_for(M, split_k, pl.rank_tiles), s));
+    p.split_stride = 0;
+    return launch_status(launch_partials(p, pl, M, split_k, s, true));
 }
 
 
@@ -959,6 +968,37 @@ int lora_sgmv_shrink(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_p
         return st;
     const TreeParams t = sgmv_tree_params(workspace, M, r_max, h, ld_h, token_adapter, ranks, scales, n_adapters);
     return launch_status(launch_splitk_tree(t, split_k, true, s));
+}
+
+int lora_sgmv_shrink_atomic(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_ptrs, int64_t ld_a,
+                            const int32_t* ranks, const float* scales, int32_t n_adapters, const void* plan,
+                            size_t plan_bytes, float* h, int64_t ld_h, int64_t M, int64_t K, int32_t r_max,
+                            int32_t split_k, void* stream)
+{
+    if (M < 0 || M > kMaxDim || n_adapters < 1)
+        return LORA_ERR_SHAPE;
+    lora_shrink_plan_t pl;
+    int st = make_plan(K, r_max, split_k, &pl);
+    if (st != LORA_OK)
+        return st;
+    if (!sgmv_items_fit(M, split_k))
+        return LORA_ERR_SHAPE;
+    if (M == 0)
+        return LORA_OK;
+    if (!x || !A_ptrs || !ranks || !plan || !h)
+        return LORA_ERR_NULL;
+    if (ld_x < K || ld_a < K || ld_h < r_max)
+        return LORA_ERR_SHAPE;
+    if (!aligned16(x) || (reinterpret_cast<uintptr_t>(h) & 3u) || !aligned16(plan) || ld_x % 8 || ld_a % 8)
+        return LORA_ERR_ALIGN;
+    if (plan_bytes < lora_sgmv_plan_bytes(M))
+        return LORA_ERR_WORKSPACE;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    st = launch_status(launch_fill_zero(h, ld_h, M, r_max, s));
+    if (st != LORA_OK)
+        return st;
+    return launch_sgmv_partials(x, ld_x, A_ptrs, ld_a, ranks, n_adapters, plan, M, r_max, pl, h, s, true, scales,
+                                ld_h);
 }
 
 int lora_sgmv_shrink_expand(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_ptrs, int64_t ld_a,

@@ -56,6 +56,13 @@ __device__ __forceinline__ void buffer_store_f32(float v, BufferRsrc r, uint32_t
     __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, v), r, (int)byte_offset, 0, 0);
 }
 
+// 4-byte fp32 atomic add through the same kind of resource (a vector memory
+// atomic; used only by the nondeterministic contrast).
+__device__ __forceinline__ void buffer_atomic_add_f32(float v, BufferRsrc r, uint32_t byte_offset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, (int)byte_offset, 0, 0);
+}
+
 // 8 bf16 starting at p of which only the first n exist (n < 8 only at a
 // rank edge that is not a multiple of 8); missing ones read as +0 so that
 // padded reduction slots contribute exact zeros.

@@ -37,6 +37,7 @@ struct ShrinkParams {
     int32_t split_k;
     int32_t n_adapters;             // sgmv
     float scale;
+    const float* scales;            // sgmv atomic contrast: per-adapter scale (may be null: 1)
 };
 
 struct TreeParams {
@@ -168,19 +169,24 @@ hipError_t launch_shrink_partial_direct(const ShrinkParams& p, int waves, int ra
                                         hipStream_t st);
 hipError_t launch_shrink_partial_atomic(const ShrinkParams& p, int waves, int rank_tiles, int group_tiles,
                                         hipStream_t st);
-hipError_t launch_sgmv_shrink_partial(const ShrinkParams& p, int waves, int group_tiles, int grid, hipStream_t st);
+// atomic: the nondeterministic contrast - the same work items, each split's
+// partial times the scale (single adapter: p.scale; sgmv: p.scales[adapter])
+// added to h = p.out (row stride p.ld_out) with fp32 atomics instead of being
+// stored to the workspace.
+hipError_t launch_sgmv_shrink_partial(const ShrinkParams& p, int waves, int group_tiles, int grid, hipStream_t st,
+                                      bool atomic = false);
 // tiles_per_wg 2 or 4: row blocks (plan tiles) per workgroup, all rank tiles together
 hipError_t launch_shrink_partial_multi(const ShrinkParams& p, int waves, int rank_tiles, int tiles_per_wg,
-                                       hipStream_t st);
+                                       hipStream_t st, bool atomic = false);
 hipError_t launch_sgmv_shrink_partial_multi(const ShrinkParams& p, int waves, int tiles_per_wg, int grid,
-                                            hipStream_t st);
+                                            hipStream_t st, bool atomic = false);
 // A-in-registers partial kernel for large M: R row blocks (plan tiles) per
 // workgroup item; usable when shrink_stream_fits (waves 4 or 8, k_steps 1, 2
 // or 4, at most 32 registers of A operands per wave).
 constexpr int kStreamMaxRows = 16;             // row blocks per item, at most
 bool shrink_stream_fits(int waves, int k_steps, int rank_tiles);
 hipError_t launch_shrink_stream(const ShrinkParams& p, int waves, int k_steps, int rank_tiles, int R, int grid,
-                                bool sgmv, hipStream_t st);
+                                bool sgmv, hipStream_t st, bool atomic = false);
 hipError_t launch_shrink_counted(const ShrinkParams& p, const CounterParams& c, int waves, int rank_tiles,
                                  int group_tiles, hipStream_t st);
 hipError_t launch_sgmv_shrink_counted(const ShrinkParams& p, const CounterParams& c, int waves, int group_tiles,

@@ -120,7 +120,7 @@ __global__ __launch_bounds__(W * 64) void k_shrink_partial(ShrinkParams p, int g
 // shrink_tiles); partials and their bits are those of k_shrink_partial.
 // Two 8-wave workgroups per compute unit (4 waves per SIMD, <= 128 VGPRs):
 // one workgroup's loads are in flight while the other runs its trees.
-template <int RT, int W, int T>
+template <int RT, int W, int T, int MODE>
 __global__ __launch_bounds__(W * 64, 4) void k_shrink_partial_multi(ShrinkParams p)
 {
     __shared__ float red[red_floats<RT, W>()];
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(W * 64, 4) void k_shrink_partial_multi(ShrinkParams
         nrows[u] = left <= 0 ? 0 : (left < kRowBlock ? (int)left : kRowBlock);
         row0[u] = nrows[u] > 0 ? r0 : first;      // empty tiles keep a valid base address
     }
-    shrink_tiles<RT, W, kToWorkspace, T>(p, row0, nrows, p.A, p.r, 0, s, 1.0f, red);
+    shrink_tiles<RT, W, MODE, T>(p, row0, nrows, p.A, p.r, 0, s, MODE == kAtomicScaled ? p.scale : 1.0f, red);
 }
 
 // Single launch: the last split of each (row block, rank group) writes h.
@@ -197,7 +197,19 @@ __device__ __forceinline__ int adapter_rank(const ShrinkParams& p, int a)
     return ra < 0 ? 0 : (ra > p.r_max ? p.r_max : ra);
 }
 
-template <int RT, int W>
+// The factor a split's partial is multiplied by before it leaves the
+// workgroup: 1 into the workspace, the adapter's shrink scale for the atomic
+// contrast's direct adds into h.
+template <int MODE>
+__device__ __forceinline__ float sgmv_item_scale(const ShrinkParams& p, int a)
+{
+    if constexpr (MODE == kAtomicScaled)
+        return p.scales ? p.scales[a] : 1.0f;
+    else
+        return 1.0f;
+}
+
+template <int RT, int W, int MODE>
 __global__ __launch_bounds__(W * 64) void k_sgmv_shrink_partial(ShrinkParams p)
 {
     __shared__ float red[red_floats<RT, W>()];
@@ -211,7 +223,8 @@ __global__ __launch_bounds__(W * 64) void k_sgmv_shrink_partial(ShrinkParams p)
         const int col0 = q.grp * 16 * RT;
         if (col0 >= ra)
             continue;
-        shrink_tile<RT, W, kToWorkspace>(p, q.row0, q.nrows, p.A_ptrs[q.a], ra, col0, q.s, 1.0f, red);
+        shrink_tile<RT, W, MODE>(p, q.row0, q.nrows, p.A_ptrs[q.a], ra, col0, q.s, sgmv_item_scale<MODE>(p, q.a),
+                                 red);
     }
 }
 
@@ -220,7 +233,7 @@ __global__ __launch_bounds__(W * 64) void k_sgmv_shrink_partial(ShrinkParams p)
 // goes through shrink_tiles together (tiles of one adapter are consecutive
 // in the plan, so a chunk is usually one stretch).  All rank tiles of r_max
 // in one workgroup.  Same partials, same bits as k_sgmv_shrink_partial.
-template <int RT, int W, int T>
+template <int RT, int W, int T, int MODE>
 __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_partial_multi(ShrinkParams p)
 {
     __shared__ float red[red_floats<RT, W>()];
@@ -253,7 +266,8 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_partial_multi(ShrinkP
             }
             const int ra = adapter_rank(p, a);
             if (ra > 0)
-                shrink_tiles<RT, W, kToWorkspace, T>(p, row0, nrows, p.A_ptrs[a], ra, 0, s, 1.0f, red);
+                shrink_tiles<RT, W, MODE, T>(p, row0, nrows, p.A_ptrs[a], ra, 0, s, sgmv_item_scale<MODE>(p, a),
+                                             red);
             j += n;
         }
     }
@@ -273,7 +287,7 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_partial_multi(ShrinkP
 // stored to the workspace.  What changes is the traffic: A is read once per
 // workgroup instead of once per few row blocks.
 // ---------------------------------------------------------------------------
-template <int RT, int W, int STEPS, bool SGMV>
+template <int RT, int W, int STEPS, bool SGMV, int MODE>
 __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int R)
 {
     // x buffers in rotation: blocks are loaded NB - 1 = 2 ahead (measured on
@@ -381,6 +395,9 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
             }
             const int ra = a < 0 ? 0 : (SGMV ? adapter_rank(p, a) : p.r);
             const int nrt = (ra + 15) / 16 < RT ? (ra + 15) / 16 : RT;
+            // the atomic contrast's factor for the run (loaded once per run)
+            const float run_sc = MODE != kAtomicScaled || ra == 0 ? 1.0f
+                                 : (SGMV ? sgmv_item_scale<MODE>(p, a) : p.scale);
 #pragma unroll
             for (int q = 0; q + 1 < NB; ++q)
                 xload(u + q < u1 ? u + q : u1 - 1, xb[q]);
@@ -443,6 +460,8 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
                             for (int w = 0; w < W; ++w)
                                 v[w] = rb[(w * 16 + erow[q]) * RS + ecol[q]];
                             val = pairwise_tree<W>(v);
+                            if constexpr (MODE == kAtomicScaled)
+                                val = __fmul_rn(val, run_sc);
                         }
                         // the value this slot stored NB blocks ago stays
                         // in its register until here, so no later
@@ -453,8 +472,12 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
                         asm volatile("" : "+v"(kept[q]));
                         kept[q] = val;
                         asm volatile("" : "+v"(kept[q]));
-                        if (mine)
-                            buffer_store_f32(kept[q], ws, voff[q]);
+                        if (mine) {
+                            if constexpr (MODE == kAtomicScaled)
+                                buffer_atomic_add_f32(kept[q], ws, voff[q]);
+                            else
+                                buffer_store_f32(kept[q], ws, voff[q]);
+                        }
                     }
                 }
             };
@@ -727,16 +750,16 @@ void launch_counted_r(const ShrinkParams& p, const CounterParams& c, int waves, 
     }
 }
 
-template <int RT, bool COUNTED>
+template <int RT, bool COUNTED, int MODE = kToWorkspace>
 void launch_sgmv_r(const ShrinkParams& p, const CounterParams& c, int waves, int grid, hipStream_t st)
 {
     dim3 g((unsigned)grid);
-#define LORA_SGMV_LAUNCH(W_)                                                                   \
-    do {                                                                                       \
-        if (COUNTED)                                                                           \
-            hipLaunchKernelGGL((k_sgmv_shrink_counted<RT, W_>), g, dim3(W_ * 64), 0, st, p, c); \
-        else                                                                                   \
-            hipLaunchKernelGGL((k_sgmv_shrink_partial<RT, W_>), g, dim3(W_ * 64), 0, st, p);    \
+#define LORA_SGMV_LAUNCH(W_)                                                                          \
+    do {                                                                                              \
+        if (COUNTED)                                                                                  \
+            hipLaunchKernelGGL((k_sgmv_shrink_counted<RT, W_>), g, dim3(W_ * 64), 0, st, p, c);        \
+        else                                                                                          \
+            hipLaunchKernelGGL((k_sgmv_shrink_partial<RT, W_, MODE>), g, dim3(W_ * 64), 0, st, p);     \
     } while (0)
     switch (waves) {
     case 1: LORA_SGMV_LAUNCH(1); break;
@@ -772,7 +795,7 @@ hipError_t launch_shrink_partial_ws(const ShrinkParams& p, int waves, int rank_t
 
 namespace {
 
-template <int RT, int T>
+template <int RT, int T, int MODE>
 void launch_multi_rt(const ShrinkParams& p, int waves, dim3 grid, bool sgmv, hipStream_t st)
 {
     // the multi-adapter kernel takes at most two tiles with 3-4 rank tiles
@@ -781,9 +804,9 @@ void launch_multi_rt(const ShrinkParams& p, int waves, dim3 grid, bool sgmv, hip
 #define LORA_MULTI(W_)                                                                                    \
     do {                                                                                                  \
         if (sgmv)                                                                                         \
-            hipLaunchKernelGGL((k_sgmv_shrink_partial_multi<RT, W_, TS>), grid, dim3(W_ * 64), 0, st, p); \
+            hipLaunchKernelGGL((k_sgmv_shrink_partial_multi<RT, W_, TS, MODE>), grid, dim3(W_ * 64), 0, st, p); \
         else                                                                                              \
-            hipLaunchKernelGGL((k_shrink_partial_multi<RT, W_, T>), grid, dim3(W_ * 64), 0, st, p);       \
+            hipLaunchKernelGGL((k_shrink_partial_multi<RT, W_, T, MODE>), grid, dim3(W_ * 64), 0, st, p);       \
     } while (0)
     switch (waves) {
     case 1: LORA_MULTI(1); break;
@@ -794,35 +817,45 @@ void launch_multi_rt(const ShrinkParams& p, int waves, dim3 grid, bool sgmv, hip
 #undef LORA_MULTI
 }
 
-template <int T>
-void launch_multi_t(const ShrinkParams& p, int waves, int rank_tiles, dim3 grid, bool sgmv, hipStream_t st)
+template <int T, int MODE>
+void launch_multi_tm(const ShrinkParams& p, int waves, int rank_tiles, dim3 grid, bool sgmv, hipStream_t st)
 {
     if (rank_tiles == 1)
-        launch_multi_rt<1, T>(p, waves, grid, sgmv, st);
+        launch_multi_rt<1, T, MODE>(p, waves, grid, sgmv, st);
     else if (rank_tiles == 2)
-        launch_multi_rt<2, T>(p, waves, grid, sgmv, st);
+        launch_multi_rt<2, T, MODE>(p, waves, grid, sgmv, st);
     else
-        launch_multi_rt<4, T>(p, waves, grid, sgmv, st);
+        launch_multi_rt<4, T, MODE>(p, waves, grid, sgmv, st);
+}
+
+template <int T>
+void launch_multi_t(const ShrinkParams& p, int waves, int rank_tiles, dim3 grid, bool sgmv, bool atomic,
+                    hipStream_t st)
+{
+    if (atomic)
+        launch_multi_tm<T, kAtomicScaled>(p, waves, rank_tiles, grid, sgmv, st);
+    else
+        launch_multi_tm<T, kToWorkspace>(p, waves, rank_tiles, grid, sgmv, st);
 }
 
 }  // namespace
 
 hipError_t launch_shrink_partial_multi(const ShrinkParams& p, int waves, int rank_tiles, int tiles_per_wg,
-                                       hipStream_t st)
+                                       hipStream_t st, bool atomic)
 {
     if (rank_tiles < 1 || rank_tiles > kGroupTiles)
         return hipErrorInvalidValue;
     const int64_t mbs = (p.M + kRowBlock - 1) / kRowBlock;
     const dim3 grid((unsigned)(((mbs + tiles_per_wg - 1) / tiles_per_wg) * p.split_k));
     if (tiles_per_wg == 2)
-        launch_multi_t<2>(p, waves, rank_tiles, grid, false, st);
+        launch_multi_t<2>(p, waves, rank_tiles, grid, false, atomic, st);
     else
-        launch_multi_t<4>(p, waves, rank_tiles, grid, false, st);
+        launch_multi_t<4>(p, waves, rank_tiles, grid, false, atomic, st);
     return hipGetLastError();
 }
 
 hipError_t launch_sgmv_shrink_partial_multi(const ShrinkParams& p, int waves, int tiles_per_wg, int grid,
-                                            hipStream_t st)
+                                            hipStream_t st, bool atomic)
 {
     const int rank_tiles = (p.r_max + 15) / 16;
     if (rank_tiles > kGroupTiles)
@@ -830,9 +863,9 @@ hipError_t launch_sgmv_shrink_partial_multi(const ShrinkParams& p, int waves, in
     // with 3-4 rank tiles, four plan tiles per workgroup do not fit in the
     // 128 registers of two workgroups per compute unit: take two
     if (tiles_per_wg == 2 || rank_tiles > 2)
-        launch_multi_t<2>(p, waves, rank_tiles, dim3((unsigned)grid), true, st);
+        launch_multi_t<2>(p, waves, rank_tiles, dim3((unsigned)grid), true, atomic, st);
     else
-        launch_multi_t<4>(p, waves, rank_tiles, dim3((unsigned)grid), true, st);
+        launch_multi_t<4>(p, waves, rank_tiles, dim3((unsigned)grid), true, atomic, st);
     return hipGetLastError();
 }
 
@@ -872,15 +905,15 @@ hipError_t launch_sgmv_shrink_counted_multi(const ShrinkParams& p, const Counter
 
 namespace {
 
-template <int RT, int W, bool SGMV>
+template <int RT, int W, bool SGMV, int MODE>
 hipError_t launch_stream_rws(const ShrinkParams& p, int steps, int R, dim3 grid, hipStream_t st)
 {
     switch (steps) {
-    case 1: hipLaunchKernelGGL((k_shrink_stream<RT, W, 1, SGMV>), grid, dim3(W * 64), 0, st, p, R); break;
-    case 2: hipLaunchKernelGGL((k_shrink_stream<RT, W, 2, SGMV>), grid, dim3(W * 64), 0, st, p, R); break;
+    case 1: hipLaunchKernelGGL((k_shrink_stream<RT, W, 1, SGMV, MODE>), grid, dim3(W * 64), 0, st, p, R); break;
+    case 2: hipLaunchKernelGGL((k_shrink_stream<RT, W, 2, SGMV, MODE>), grid, dim3(W * 64), 0, st, p, R); break;
     default:
         if constexpr (RT <= 2)
-            hipLaunchKernelGGL((k_shrink_stream<RT, W, 4, SGMV>), grid, dim3(W * 64), 0, st, p, R);
+            hipLaunchKernelGGL((k_shrink_stream<RT, W, 4, SGMV, MODE>), grid, dim3(W * 64), 0, st, p, R);
         else
             return hipErrorInvalidValue;
         break;
@@ -888,11 +921,19 @@ hipError_t launch_stream_rws(const ShrinkParams& p, int steps, int R, dim3 grid,
     return hipGetLastError();
 }
 
-template <int RT, bool SGMV>
-hipError_t launch_stream_r(const ShrinkParams& p, int waves, int steps, int R, dim3 grid, hipStream_t st)
+template <int RT, bool SGMV, int MODE>
+hipError_t launch_stream_rm(const ShrinkParams& p, int waves, int steps, int R, dim3 grid, hipStream_t st)
 {
-    return waves == 8 ? launch_stream_rws<RT, 8, SGMV>(p, steps, R, grid, st)
-                      : launch_stream_rws<RT, 4, SGMV>(p, steps, R, grid, st);
+    return waves == 8 ? launch_stream_rws<RT, 8, SGMV, MODE>(p, steps, R, grid, st)
+                      : launch_stream_rws<RT, 4, SGMV, MODE>(p, steps, R, grid, st);
+}
+
+template <int RT, bool SGMV>
+hipError_t launch_stream_r(const ShrinkParams& p, int waves, int steps, int R, dim3 grid, bool atomic,
+                           hipStream_t st)
+{
+    return atomic ? launch_stream_rm<RT, SGMV, kAtomicScaled>(p, waves, steps, R, grid, st)
+                  : launch_stream_rm<RT, SGMV, kToWorkspace>(p, waves, steps, R, grid, st);
 }
 
 }  // namespace
@@ -906,19 +947,19 @@ bool shrink_stream_fits(int waves, int k_steps, int rank_tiles)
 }
 
 hipError_t launch_shrink_stream(const ShrinkParams& p, int waves, int k_steps, int rank_tiles, int R, int grid,
-                                bool sgmv, hipStream_t st)
+                                bool sgmv, hipStream_t st, bool atomic)
 {
     if (!shrink_stream_fits(waves, k_steps, rank_tiles) || R < 1 || R > kStreamMaxRows || grid < 1)
         return hipErrorInvalidValue;
     const dim3 g((unsigned)grid);
     if (rank_tiles <= 1)
-        return sgmv ? launch_stream_r<1, true>(p, waves, k_steps, R, g, st)
-                    : launch_stream_r<1, false>(p, waves, k_steps, R, g, st);
+        return sgmv ? launch_stream_r<1, true>(p, waves, k_steps, R, g, atomic, st)
+                    : launch_stream_r<1, false>(p, waves, k_steps, R, g, atomic, st);
     if (rank_tiles == 2)
-        return sgmv ? launch_stream_r<2, true>(p, waves, k_steps, R, g, st)
-                    : launch_stream_r<2, false>(p, waves, k_steps, R, g, st);
-    return sgmv ? launch_stream_r<4, true>(p, waves, k_steps, R, g, st)
-                : launch_stream_r<4, false>(p, waves, k_steps, R, g, st);
+        return sgmv ? launch_stream_r<2, true>(p, waves, k_steps, R, g, atomic, st)
+                    : launch_stream_r<2, false>(p, waves, k_steps, R, g, atomic, st);
+    return sgmv ? launch_stream_r<4, true>(p, waves, k_steps, R, g, atomic, st)
+                : launch_stream_r<4, false>(p, waves, k_steps, R, g, atomic, st);
 }
 
 hipError_t launch_shrink_partial_direct(const ShrinkParams& p, int waves, int rank_tiles, int group_tiles,
@@ -948,13 +989,21 @@ hipError_t launch_shrink_counted(const ShrinkParams& p, const CounterParams& c, 
     return hipGetLastError();
 }
 
-hipError_t launch_sgmv_shrink_partial(const ShrinkParams& p, int waves, int group_tiles, int grid, hipStream_t st)
+hipError_t launch_sgmv_shrink_partial(const ShrinkParams& p, int waves, int group_tiles, int grid, hipStream_t st,
+                                      bool atomic)
 {
     const CounterParams none{};
-    if (group_tiles == 1)
-        launch_sgmv_r<1, false>(p, none, waves, grid, st);
-    else
-        launch_sgmv_r<4, false>(p, none, waves, grid, st);
+    if (atomic) {
+        if (group_tiles == 1)
+            launch_sgmv_r<1, false, kAtomicScaled>(p, none, waves, grid, st);
+        else
+            launch_sgmv_r<4, false, kAtomicScaled>(p, none, waves, grid, st);
+    } else {
+        if (group_tiles == 1)
+            launch_sgmv_r<1, false>(p, none, waves, grid, st);
+        else
+            launch_sgmv_r<4, false>(p, none, waves, grid, st);
+    }
     return hipGetLastError();
 }
 

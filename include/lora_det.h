@@ -37,7 +37,7 @@
  * prints, aborts or throws.
  *
  * DETERMINISM.  For the deterministic entry points (everything except
- * lora_shrink_splitk_atomic) each output element's bits depend only on that
+ * lora_shrink_splitk_atomic and lora_sgmv_shrink_atomic) each output element's bits depend only on that
  * token's own input row, the adapter, K, r, split_k and the scale: not on M,
  * on the row's position in the batch, on other rows, on the stream or on
  * timing.  The Split-K plan (lora_shrink_plan) is a function of (K, split_k)
@@ -131,9 +131,11 @@ int lora_shrink_splitk(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64
 /*
  * Atomic Split-K shrink, kept only as the nondeterministic contrast of paper
  * section 4.1: h is zeroed by a fill kernel (the output initialisation the
- * paper counts in its latency), then each split adds scale * P_s into h with
- * hardware fp32 atomic adds, in whatever order the splits finish.  The value
- * agrees with lora_shrink_splitk to rounding; the bits may differ between runs.
+ * paper counts in its latency), then the partial kernel that lora_shrink_splitk
+ * would run for these sizes (same work items and schedule) adds each split's
+ * scale * P_s into h with hardware fp32 atomic adds, in whatever order the
+ * splits finish, instead of storing P_s to a workspace.  The value agrees with
+ * lora_shrink_splitk to rounding; the bits may differ between runs.
  */
 int lora_shrink_splitk_atomic(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a,
                               float* h, int64_t ld_h, int64_t M, int64_t K, int32_t r,
@@ -382,6 +384,23 @@ int lora_sgmv_shrink_counted(const uint16_t* x, int64_t ld_x, const uint16_t* co
                              float* h, int64_t ld_h, int64_t M, int64_t K, int32_t r_max,
                              int32_t split_k, void* workspace, size_t workspace_bytes,
                              int32_t* counters, size_t counter_bytes, void* stream);
+
+/*
+ * lora_sgmv_shrink_atomic: the nondeterministic contrast for the multi-adapter
+ * shrink (the atomic Split-K baseline of paper section 4.1, replayed with the
+ * token-to-adapter mapping as in section 5.2).  h's first r_max columns are
+ * zeroed by a fill kernel, then the partial kernel that lora_sgmv_shrink would
+ * run (same work items, same plan) adds each split's partial times the
+ * adapter's scale (scales[a], NULL = 1) into h with fp32 atomic adds, in
+ * whatever order the splits finish.  Tokens without an adapter, and columns
+ * from the adapter's rank on, stay zero.  No workspace.  Values agree with
+ * lora_sgmv_shrink to rounding; the bits may differ between runs.  Arguments
+ * as for lora_sgmv_shrink (the token ids are read from the plan).
+ */
+int lora_sgmv_shrink_atomic(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_ptrs, int64_t ld_a,
+                            const int32_t* ranks, const float* scales, int32_t n_adapters,
+                            const void* plan, size_t plan_bytes, float* h, int64_t ld_h,
+                            int64_t M, int64_t K, int32_t r_max, int32_t split_k, void* stream);
 
 /*
  * Multi-adapter shrink + expand: the partial kernel of lora_sgmv_shrink, then

@@ -177,6 +177,73 @@ def test_atomic_parity(M, K, r, S):
     check_shrink(h, c.x, c.A, 2.0, dsl.lora_shrink_plan(K, r, S), "atomic", atomic=True)
 
 
+@pytest.mark.parametrize("M,K,r,S", [(1024, 14336, 32, 8), (2100, 4096, 24, 8), (4100, 8192, 64, 16)])
+def test_atomic_parity_large_m_schedules(M, K, r, S):
+    """The atomic contrast runs the partial kernel the deterministic path picks
+    for these sizes - two row blocks per workgroup sharing A (M = 1024,
+    K = 14336), A kept in registers over 4 and 16 row blocks (the others) -
+    with fp32 atomic adds in place of the workspace stores: sampled rows within
+    the atomic rounding bound of the oracle."""
+    _say(f"atomic shrink large M: M={M} K={K} r={r} S={S}")
+    c = single_adapter_case(M, K, r, 0, split_k=S, seed=8)
+    h = run_shrink(c.x, c.A, S, 2.0, atomic=True)
+    rows = np.unique(np.concatenate([np.linspace(0, M - 1, 40).astype(int), [M - 1, M - 2, 15, 16]]))
+    check_shrink(h[rows], c.x[rows], c.A, 2.0, dsl.lora_shrink_plan(K, r, S), "atomic large M", atomic=True)
+
+
+def _sgmv_atomic(c):
+    """lora_sgmv_shrink_atomic on a case: h [M, r_max] (host)."""
+    t = torch()
+    n = len(c.ranks)
+    As = [bf16_to_gpu(a) for a in c.As]
+    Ap = t.tensor([a.data_ptr() for a in As], dtype=t.int64, device="cuda")
+    _, plan = _build_plan(c.ids, n)
+    h = t.full((c.M, c.r_max), float("nan"), dtype=t.float32, device="cuda")
+    dsl.lora_sgmv_shrink_atomic(bf16_to_gpu(c.x), Ap, c.K, t.from_numpy(c.ranks).cuda(),
+                                t.from_numpy(c.scales).cuda(), n, plan, h, c.r_max, c.split_k)
+    t.cuda.synchronize()
+    return h.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", ["qkv", "mixed", "many", "prefill"])
+def test_sgmv_atomic_parity(case):
+    """The multi-adapter atomic contrast (fill, then the multi-adapter partial
+    kernel with atomic adds of each split's partial times the adapter's scale):
+    per token within the atomic rounding bound of the oracle, zero rows for
+    tokens without an adapter, zero columns from the adapter's rank on."""
+    rng = np.random.default_rng(31)
+    if case == "qkv":
+        c = sgmv_case(512, 4096, 8, [64] * 4, 1, 64, 8, seed=0, tag="cfg3")
+        rows = list(range(512))
+    elif case == "mixed":
+        ids = rng.choice([-1, 0, 1, 2, 3, 4, 5, 9], 300).astype(np.int32)
+        ids[100:180] = 3
+        c = sgmv_case(300, 2048, 8, [8, 16, 32, 64, 24, 5], 0, 0, 4, seed=1, tag="mix", ids=ids)
+        rows = list(range(300))
+    elif case == "many":
+        n = 300
+        ranks = [int(v) for v in rng.integers(1, 25, n)]
+        ids = rng.permutation(np.concatenate([np.arange(n), rng.integers(250, n, 12), -np.ones(8)])).astype(np.int32)
+        c = sgmv_case(len(ids), 1024, 8, ranks, 0, 0, 8, seed=5, tag="many", ids=ids)
+        c.scales[:] = rng.choice([0.5, 1.0, 1.5, 2.0, 3.0], n)
+        rows = list(range(len(ids)))
+    else:
+        c = sgmv_case(4096, 8192, 8, [8, 16, 32, 64] * 8, 32, 512, 16, seed=0, tag="b5")
+        rows = sorted(set(np.linspace(0, 4095, 48).astype(int).tolist()) | {0, 4095})
+    _say(f"sgmv atomic {case}: M={c.M} K={c.K} n={len(c.ranks)} S={c.split_k}")
+    h = _sgmv_atomic(c)
+    n = len(c.ranks)
+    for i in rows:
+        a = c.ids[i]
+        if a < 0 or a >= n:
+            assert np.all(h[i] == 0.0), f"{case}: row {i} without adapter"
+            continue
+        r = int(c.ranks[a])
+        assert np.all(h[i, r:] == 0.0), f"{case}: row {i} past rank {r}"
+        check_shrink(h[i:i + 1, :r], c.x[i:i + 1], c.As[a], float(c.scales[a]),
+                     dsl.lora_shrink_plan(c.K, r, c.split_k), f"{case} atomic row {i}", atomic=True)
+
+
 # ---------------------------------------------------------------------------
 # expand parity
 # ---------------------------------------------------------------------------
