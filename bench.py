@@ -56,6 +56,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def steps_per_graph(steps: int) -> int:
+    """Steps captured per HIP graph: the largest divisor of `steps` that is at
+    most STEPS_PER_GRAPH, so that exactly `steps` steps run in whole graphs."""
+    return max(d for d in range(1, STEPS_PER_GRAPH + 1) if steps % d == 0)
+
+
 def shrink_bytes(M, K, r):
     """Algorithmic bytes of a shrink: read x and A once, write h."""
     return 2 * M * K + 2 * K * r + 4 * M * r
@@ -204,7 +210,7 @@ class Bench:
         # the timed steps: the four batch sizes back to back; each HIP graph
         # holds SPG consecutive steps on SPG input copies, replayed K / SPG
         # times, so exactly K steps run in the timed region
-        spg = STEPS_PER_GRAPH if K % STEPS_PER_GRAPH == 0 else 1
+        spg = steps_per_graph(K)
         det_g = self.capture(self.det, M_LIST, spg)
         ms_det = self.time_graphs(det_g, K // spg, max(1, W // spg)) / spg
         del det_g
@@ -245,13 +251,12 @@ class Bench:
             byt = sum(shrink_bytes(M, K_HID, RANK) + expand_bytes(M, RANK, N_OUT) for M in one)
             cand.append((us, len(one), byt, "k_shrink_expand_fused<2,8,8> (lora_shrink_expand_fused: Split-K "
                          "shrink recomputed per 512 columns, fixed trees, expand; r=16, N=4096, M=" +
-                         "/".join(map(str, one)) + ")"))
+                         "/".join(map(str, one)) + ")", None))
         if two:
             per = {M: self.per_call_us(self.combine_only, (M,), 8, K) for M in two}
             byt = sum(combine_bytes(M, RANK, N_OUT, SPLIT) for M in two)
-            cand.append((sum(per.values()), len(two), byt, COMBINE_KERNEL + " (lora_expand_combine: fixed tree "
-                         "over the Split-K workspace + expand, 2 waves per workgroup at M <= 4, else 4; r=16, "
-                         "N=4096, M=" + "/".join(map(str, two)) + ")",
+            cand.append((sum(per.values()), len(two), byt, COMBINE_KERNEL + " (fixed tree over the Split-K "
+                         "workspace + expand; M=" + "/".join(map(str, two)) + ")",
                          {str(M): round(u, 3) for M, u in per.items()}))
         us, n, byt, name, per = max(cand, key=lambda c: c[0])
         avg_launch_us = us / n
@@ -262,8 +267,8 @@ class Bench:
                            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
                            "avg_launch_us": round(avg_launch_us, 3), "launch_us_per_m": per,
                            "algorithmic_bytes_per_launch": avg_bytes,
-                           "timing": "8 back-to-back launches per HIP graph on 8 input copies; a launch's time "
-                                     "includes the gap to the next dispatch"}
+                           "timing": "HIP events over graphs of 8 back-to-back launches: a launch's time includes "
+                                     "the gap to the next dispatch"}
         return res
 
 
@@ -587,7 +592,7 @@ def compensated_bench(args):
     return out
 
 
-def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S):
+def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S, replays=100):
     """Multi-adapter shrink and expand on a prebuilt plan, cold cache.
     Compulsory bytes count only the adapters some token uses, at their own
     rank: shrink 2MK + 2K sum(r) + 4 M r_max (h), expand 4 sum_i r_(a_i) (h)
@@ -655,6 +660,13 @@ def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S):
     def plan_only(st):
         dsl.lora_sgmv_plan(ids_g, n, plan)
 
+    def atomic_shrink(st):
+        dsl.lora_sgmv_shrink_atomic(st["x"], st["Ap"], K, ranks_g, None, n, plan, st["h"], c.r_max, S)
+
+    def atomic_both(st):
+        atomic_shrink(st)
+        expand(st)
+
     out = {"workload": f"M={M}, K={K}, N={N}, {n} adapters of ranks {sorted(set(int(v) for v in c.ranks))}, "
                        f"segments {seg_lo}..{seg_hi} tokens, Split-K {S}",
            "segments": len(c.segs), "touched_adapters": len(touched), "shrink_bytes": sh_bytes,
@@ -663,14 +675,58 @@ def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S):
     for name, call, byt in (("shrink", shrink, sh_bytes), ("shrink_one_launch", shrink_counted, sh_bytes),
                             ("expand", expand, ex_bytes), ("shrink_expand", both, sh_bytes + ex_bytes),
                             ("shrink_expand_pipeline", pipeline, sh_bytes + ex_bytes),
+                            ("atomic_shrink", atomic_shrink, sh_bytes),
+                            ("atomic_shrink_expand", atomic_both, sh_bytes + ex_bytes),
                             ("plan", plan_only, 0)):
         us = _time_rotating(call, sets, args)
         out[name] = {"us": round(us, 3)}
         if byt:
             out[name]["GBps"] = round(byt / us / 1e3, 1)
             out[name]["pct_hbm_peak"] = round(100 * byt / us / 1e3 / HBM_PEAK_GBS, 2)
+    out["det_over_atomic"] = round(out["shrink_expand_pipeline"]["us"] / out["atomic_shrink_expand"]["us"], 4)
+    out["det_shrink_over_atomic_shrink"] = round(out["shrink"]["us"] / out["atomic_shrink"]["us"], 4)
+    st0 = sets[0]
     del sets
     torch.cuda.empty_cache()
+    out["replay"] = sgmv_replay(st0, pipeline, atomic_both, replays)
+    return out
+
+
+def _row_hashes(flat):
+    """64-bit multiplicative hash of each row of an integer tensor's bits."""
+    import torch
+    g = torch.Generator(device=flat.device).manual_seed(1)
+    w = torch.randint(1, 2 ** 62, (flat.shape[1],), generator=g, device=flat.device, dtype=torch.int64) | 1
+    return (flat.to(torch.int64) * w).sum(dim=1)
+
+
+def sgmv_replay(st, det_call, atomic_call, repeats):
+    """Identical-input replay of a multi-adapter shrink + expand: each variant
+    runs `repeats` times on the same inputs (y restored before every call);
+    h is compared bit for bit with the first call's, y by a 64-bit hash of its
+    bits.  Reported per variant: calls whose h (or y) differs from the first."""
+    import torch
+    y0 = st["y"].clone()
+    out = {"repeats": repeats}
+    for name, call in (("deterministic", det_call), ("atomic", atomic_call)):
+        h_first = y_first = None
+        dh = dy = 0
+        hashes = []
+        for i in range(repeats):
+            st["y"].copy_(y0)
+            call(st)
+            hb = st["h"].view(torch.int32)
+            yh = _row_hashes(st["y"].view(torch.int16).reshape(1, -1))
+            if h_first is None:
+                h_first, y_first = hb.clone(), yh.clone()
+            else:
+                dh += int(not torch.equal(hb, h_first))
+                dy += int(not torch.equal(yh, y_first))
+            hashes.append(_row_hashes(hb.reshape(1, -1)))
+        torch.cuda.synchronize()
+        out[name] = {"h_differs": dh, "y_differs": dy, "distinct_h": int(torch.unique(torch.cat(hashes)).numel())}
+    st["y"].copy_(y0)
+    torch.cuda.synchronize()
     return out
 
 
@@ -837,11 +893,62 @@ def _cpu_model():
     return None
 
 
+def _time_cpu(fn, seconds):
+    """Calls of fn for about `seconds` (at least one): (calls, elapsed s)."""
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return n, el
+
+
+def _cpu_config_cases():
+    """The oracle's work per config, as (name, sample description, callable,
+    rows computed per call, rows of the config's call)."""
+    import oracle
+    from synth import single_adapter_case, normal_bf16, sgmv_case
+    out = []
+    c1 = single_adapter_case(8, 1024, 8, 0, split_k=8, scale=1.0, seed=0)
+    out.append(("small_m8_k1024_r8", "whole call (fp64 shrink)", lambda: oracle.shrink(c1.x, c1.A, 1.0), 8, 8))
+    c3 = sgmv_case(512, 4096, 6144, [64] * 4, 1, 64, 8, seed=0, tag="b3")
+
+    def f3():
+        h = oracle.sgmv_shrink(c3.x, c3.As, c3.ranks, None, c3.ids, c3.r_max)
+        oracle.sgmv_expand(h.astype(np.float32), c3.Bs, c3.ranks, c3.scales, c3.ids, c3.y)
+    out.append(("sgmv_m512_k4096_n6144_4x_r64", "whole call (fp64 multi-adapter shrink + expand)", f3, 512, 512))
+    K4, r4, N4 = 14336, 32, 4096
+    probe = normal_bf16((16, K4), 1.0, 0, "probe_x")
+    A4 = normal_bf16((r4, K4), 0.02, 0, "probe_A")
+    B4 = normal_bf16((N4, r4), 0.02, 0, "probe_B")
+    y4 = normal_bf16((16, N4), 1.0, 0, "probe_y")
+
+    def f4():
+        h = oracle.shrink(probe, A4, 1.0)
+        oracle.expand(h.astype(np.float32), B4, y4, SCALE)
+    out.append(("down_k14336_r32_n4096_probe_rows", "the 16 probe rows of the batch sweep (shrink + expand)",
+                f4, 16, 16))
+    c5 = sgmv_case(4096, 8192, 28672, [8, 16, 32, 64] * 8, 32, 512, 16, seed=0, tag="b5")
+    rows = np.arange(0, 4096, 32)
+    x5, ids5, y5 = c5.x[rows], c5.ids[rows], c5.y[rows]
+
+    def f5():
+        h = oracle.sgmv_shrink(x5, c5.As, c5.ranks, None, ids5, c5.r_max)
+        oracle.sgmv_expand(h.astype(np.float32), c5.Bs, c5.ranks, c5.scales, ids5, y5)
+    out.append(("sgmv_prefill_m4096_k8192_n28672", "every 32nd token (128 of 4096; shrink + expand), "
+                "scaled to the whole call", f5, len(rows), 4096))
+    return out
+
+
 def cpu_baseline(seconds: float):
-    """The CPU oracle (fp64 C, OpenMP over rows) on the same workload: timed for
-    about `seconds` with the host's thread setting, then for about a third of
-    that on one thread (set through the OpenMP runtime in this process, then
-    restored)."""
+    """The CPU oracle (fp64 C, OpenMP over rows) on the same workloads: the
+    bench's step (q_proj shape, four batch sizes) timed for about `seconds`
+    with the host's thread setting and for a third of that on one thread (set
+    through the OpenMP runtime in this process, then restored); then each
+    other config's call (sampled rows where the whole call would take long)
+    for about `seconds` / 8 per thread setting, scaled to the whole call."""
     import oracle
     n, el, threads = _oracle_steps(seconds)
     prev = oracle.set_threads(1)
@@ -850,24 +957,165 @@ def cpu_baseline(seconds: float):
     finally:
         oracle.set_threads(prev)
     sample = "full steps (M = 1, 16, 64, 256; fp64 shrink + expand each)"
+    configs = {}
+    for name, what, fn, rows, rows_full in _cpu_config_cases():
+        row = {"sample": what}
+        for label, th in (("all_threads", threads), ("one_thread", 1)):
+            p = oracle.set_threads(th)
+            try:
+                fn()                                   # warm
+                calls, t = _time_cpu(fn, seconds / 8)
+            finally:
+                oracle.set_threads(p)
+            row[label + "_us_per_call"] = round(t / calls * 1e6 * rows_full / rows, 1)
+        configs[name] = row
     return {"value": round(el / (n * len(M_LIST)) * 1e6, 1), "unit": "us/call", "cores": threads,
             "kind": "oracle", "sample": f"{n} {sample} in {el:.1f} s",
             "one_thread": {"value": round(el1 / (n1 * len(M_LIST)) * 1e6, 1), "unit": "us/call",
                            "cores": threads1, "sample": f"{n1} {sample} in {el1:.1f} s"},
-            "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+            "configs": configs, "cpu_model": _cpu_model(), "host_cpus": os.cpu_count()}
+
+
+def _sha256_files(paths):
+    import hashlib
+    h = hashlib.sha256()
+    for f in paths:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def provenance(b):
+    """Where and on what the numbers were taken, and the bitwise evidence:
+    SHA-256 of the headline's seeded inputs and of its deterministic outputs
+    (h fp32 bits and y bf16 bits after one call per batch size on fresh
+    copies), which any run of the same library on the same inputs reproduces."""
+    import hashlib
+    import subprocess
+    import torch
+    import deterministic_split_lora_amd as dsl
+    from synth import single_adapter_case
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        with open("/opt/rocm/.info/version") as fh:
+            rocm = fh.read().strip()
+    except OSError:
+        pass
+    git = None
+    try:
+        git = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True, text=True,
+                             timeout=10).stdout.strip() or None
+    except Exception:
+        pass
+    srcs = sorted(os.path.join("deterministic_split_lora_amd", "csrc", f)
+                  for f in os.listdir(os.path.join(ROOT, "deterministic_split_lora_amd", "csrc")))
+    hin, hout = hashlib.sha256(), hashlib.sha256()
+    dev = torch.device("cuda:0")
+    for M in M_LIST:
+        c = single_adapter_case(M, K_HID, RANK, N_OUT, SPLIT, SCALE, seed=0)
+        for a in (c.x, c.A, c.B, c.y):
+            hin.update(np.ascontiguousarray(a).tobytes())
+        x, A, B, y = (gpu_tensor(a, dev) for a in (c.x, c.A, c.B, c.y))
+        h = torch.empty((M, RANK), dtype=torch.float32, device=dev)
+        ws = torch.empty(dsl.lora_shrink_expand_workspace_bytes(M, RANK, SPLIT), dtype=torch.uint8, device=dev)
+        dsl.lora_shrink_expand(x, A, B, y, ws, SPLIT, 1.0, SCALE, h=h)
+        torch.cuda.synchronize()
+        hout.update(h.view(torch.int32).cpu().numpy().tobytes())
+        hout.update(y.view(torch.int16).cpu().numpy().tobytes())
+    return {"gpu": props.name, "arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
+            "hbm_gib": round(props.total_memory / 2 ** 30, 1), "torch": torch.__version__, "hip": torch.version.hip,
+            "rocm": rocm, "git": git, "library_sha256": _sha256_files([os.path.relpath(dsl.LIBRARY_PATH, ROOT)]),
+            "sources_sha256": _sha256_files(srcs + ["include/lora_det.h"]), "seed": 0,
+            "headline_inputs_sha256": hin.hexdigest(), "headline_outputs_sha256": hout.hexdigest()}
 
 
 # Workloads bench.py can time on their own (--only).
 ONLY = {
     "replay": replay_variability,
-    "sgmv_qkv": lambda a: sgmv_bench(a, "b3", 512, 4096, 6144, [64] * 4, 1, 64, 8),
-    "sgmv_prefill": lambda a: sgmv_bench(a, "b5", 4096, 8192, 28672, [8, 16, 32, 64] * 8, 32, 512, 16),
+    "sgmv_qkv": lambda a: sgmv_bench(a, "b3", 512, 4096, 6144, [64] * 4, 1, 64, 8, replays=200),
+    "sgmv_prefill": lambda a: sgmv_bench(a, "b5", 4096, 8192, 28672, [8, 16, 32, 64] * 8, 32, 512, 16,
+                                         replays=50),
     "decode_probe": lambda a: decode_probe(a, 128),
     "decode_probe32": lambda a: decode_probe(a, 32),
     "decode_expand": lambda a: {"32": decode_expand_probe(a, 32), "128": decode_expand_probe(a, 128)},
     "batch_sweep": batch_sweep_bench,
     "compensated": compensated_bench,
 }
+
+
+def _r(v, nd=3):
+    return None if v is None else round(float(v), nd)
+
+
+def summarize(res, extra, probe, wide, dexp, roof, floor, replay):
+    """The compact view of every measurement, small enough for one stored
+    JSON line: per-config det and atomic microseconds per call with their
+    ratio and HBM share, the decode probes, replay and ceiling figures."""
+    out = {}
+    out["per_m"] = {M: {"det_us": v["det_us"], "atomic_us": v["atomic_us"], "det_over_atomic": v["det_over_atomic"],
+                        "launches": v["det_launches"], "pct_hbm_peak": v["det_pct_hbm_peak"]}
+                    for M, v in res["per_m"].items()}
+    cfg = {}
+    if extra:
+        so = extra["shrink_only_m8_k1024_r8"]
+        cfg["small_m8_k1024_r8_shrink"] = {"det_us": so["det_two_launch_us"], "det_one_launch_us": so["det_one_launch_us"],
+                                           "atomic_us": so["atomic_us"], "det_over_atomic": so["det_over_atomic"]}
+        for key, name in (("sgmv_m512_k4096_n6144_4x_r64", "sgmv_m512_k4096_n6144_4x_r64"),
+                          ("sgmv_prefill_m4096_k8192_n28672_32_adapters", "sgmv_prefill_m4096_k8192_n28672")):
+            e = extra[key]
+            rp = e["replay"]
+            cfg[name] = {"det_us": e["shrink_expand_pipeline"]["us"], "atomic_us": e["atomic_shrink_expand"]["us"],
+                         "det_over_atomic": e["det_over_atomic"],
+                         "pct_hbm_peak": e["shrink_expand_pipeline"]["pct_hbm_peak"],
+                         "shrink_us": e["shrink"]["us"], "shrink_pct": e["shrink"]["pct_hbm_peak"],
+                         "atomic_shrink_us": e["atomic_shrink"]["us"],
+                         "shrink_one_launch_us": e["shrink_one_launch"]["us"],
+                         "expand_us": e["expand"]["us"], "expand_pct": e["expand"]["pct_hbm_peak"],
+                         "plan_us": e["plan"]["us"],
+                         "replay": f"{rp['repeats']} calls: det h/y differ {rp['deterministic']['h_differs']}/"
+                                   f"{rp['deterministic']['y_differs']}, atomic {rp['atomic']['h_differs']}/"
+                                   f"{rp['atomic']['y_differs']} ({rp['atomic']['distinct_h']} distinct h)"}
+        sw = extra["batch_sweep_k14336_r32_n4096"]["points"]
+        cfg["down_k14336_r32_n4096_batch_sweep"] = {
+            "b": {b: [v["det_us"], v["atomic_us"]] for b, v in sw.items()},
+            "columns": "det_us, atomic_us",
+            "det_over_atomic_max": max(v["det_over_atomic"] for v in sw.values()),
+            "pct_hbm_peak_b1024": sw["1024"]["det_pct_hbm_peak"]}
+        qkv = extra["split_sweep"]["decode_qkv_shrink"]
+        cfg["decode_qkv_m1_k3072_3x_r16_split_sweep"] = {
+            S: [qkv[S]["det_two_launch_us"], qkv[S]["det_one_launch_us"], qkv[S]["atomic_us"]]
+            for S in ("1", "2", "4", "8", "16")}
+        cfg["decode_qkv_m1_k3072_3x_r16_split_sweep"]["columns"] = "det two launches, det one launch, atomic (us)"
+        comp = extra["compensated_expand"]
+        cfg["compensated_expand_ratio"] = {k: v["ratio"] for k, v in comp.items() if isinstance(v, dict)}
+    out["configs"] = cfg
+    if probe:
+        out["decode_probe"] = {
+            f"m{M}": {"bytes": p_["bytes"], "us": min(p_["two_launch"]["us_per_call"],
+                                                                      p_["single_launch"]["us_per_call"]),
+                                     "two_launch_us": p_["two_launch"]["us_per_call"],
+                                     "single_launch_us": p_["single_launch"]["us_per_call"],
+                                     "pct_hbm_peak": p_["best_pct_hbm_peak"]}
+            for M, p_ in ((32, probe), (128, wide))}
+        out["decode_expand_probe"] = {m: {"expand_us": v["expand"]["us_per_call"],
+                                          "expand_pct": v["expand"]["pct_hbm_peak"],
+                                          "shrink_expand_us": v["shrink_expand"]["us_per_call"],
+                                          "shrink_expand_pct": v["shrink_expand"]["pct_hbm_peak"]}
+                                      for m, v in dexp.items()}
+        out["copy_ceiling_pct"] = {k: v["pct_hbm_peak"] for k, v in roof.items()}
+        out["launch_floor_us"] = floor
+    if replay:
+        rs = {}
+        for M in M_LIST:
+            r = replay[f"M={M}"]
+            rs[str(M)] = {"det_h": r["deterministic"]["h_fp32"]["differing_comparisons"],
+                          "det_y": r["deterministic"]["y_bf16"]["differing_comparisons"],
+                          "atomic_h": r["atomic"]["h_fp32"]["differing_comparisons"],
+                          "atomic_y": r["atomic"]["y_bf16"]["differing_comparisons"],
+                          "atomic_distinct_h": r["atomic"]["h_fp32"]["distinct_outputs"]}
+        out["replay_q_proj"] = {"calls_per_m": 1000, "differing_of_999": rs}
+    return out
 
 
 def main():
@@ -880,6 +1128,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--no-configs", action="store_true", help="skip the other shapes (sweep, multi-adapter)")
+    ap.add_argument("--detail", help="also write every measurement, in full, to this JSON file")
     ap.add_argument("--only", choices=sorted(ONLY),
                     help="time one workload and print its JSON only (a target for a profiler run)")
     ap.add_argument("--counters", action="store_true",
@@ -902,6 +1151,7 @@ def main():
     b = Bench(args)
     res = b.run()
     log("bench: main timing done")
+    prov = provenance(b)
     probe = wide = roof = floor = extra = replay = dexp = None
     if not args.no_probe:
         probe = decode_probe(args, 32)
@@ -927,7 +1177,8 @@ def main():
         extra["sgmv_prefill_m4096_k8192_n28672_32_adapters"] = ONLY["sgmv_prefill"](args)
         log("bench: sgmv prefill done")
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
-    import torch
+    log("bench: cpu baseline done")
+    summary = summarize(res, extra, probe, wide, dexp, roof, floor, replay)
     out = {
         "metric": METRIC,
         "value": round(res["us_per_call"], 3),
@@ -941,30 +1192,27 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "single-adapter LoRA, q_proj shape of an 8B Llama-3 layer: x [M x 4096], "
-                               "A [16 x 4096], B [4096 x 16], y [M x 4096] bf16, scale 2, Split-K 8, "
-                               "M = 1, 16, 64, 256 per step",
-                   "cache": "hot" if args.hot else f"cold: rotating {b.copies} input copies (>= 1 GiB)",
-                   "timing": "HIP graph replay, HIP events on the launch stream",
-                   "det_pipeline": "lora_shrink_expand (split partials, then tree + expand: 2 launches at every M "
-                                   "of this shape; identical bits to every other schedule)",
-                   "atomic_pipeline": "lora_shrink_splitk_atomic (fill + atomic partials) + lora_expand (3 launches)"},
-        "atomic_us_per_call": round(res["atomic_us_per_call"], 3),
-        "det_two_call_us_per_call": round(res["det_two_call_us_per_call"], 3),
+        "config": {"workload": "q_proj LoRA (8B Llama-3): x [M x 4096], A [16 x 4096], B [4096 x 16], y bf16, "
+                               "s 2, Split-K 8, M 1/16/64/256",
+                   "cache": "hot" if args.hot else f"cold ({b.copies} rotating copies, >= 1 GiB)",
+                   "steps_per_graph": res["steps_per_graph"],
+                   "det": "lora_shrink_expand", "atomic": "fill + atomic partials + lora_expand"},
         "det_over_atomic": round(res["us_per_call"] / res["atomic_us_per_call"], 4),
-        "per_m": res["per_m"],
+        "atomic_us_per_call": round(res["atomic_us_per_call"], 3),
+        "det_three_launch_us_per_call": round(res["det_two_call_us_per_call"], 3),
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
-        "decode_bandwidth_probe": probe,
-        "decode_bandwidth_probe_wide": wide,
-        "decode_expand_probe": dexp,
-        "copy_roofline": roof,
-        "launch_floor": floor,
-        "replay_variability": replay,
-        "other_shapes": extra,
-        "device": torch.cuda.get_device_name(0),
+        "provenance": prov,
     }
-    print(json.dumps(out), flush=True)
+    out.update(summary)
+    if args.detail:
+        detail = dict(out, per_m_detail=res["per_m"], decode_bandwidth_probe=probe, decode_bandwidth_probe_wide=wide,
+                      decode_expand_probe_detail=dexp, copy_roofline=roof, replay_variability=replay,
+                      other_shapes=extra)
+        os.makedirs(os.path.dirname(os.path.abspath(args.detail)), exist_ok=True)
+        with open(args.detail, "w") as fh:
+            json.dump(detail, fh, indent=1)
+    print(json.dumps(out, separators=(",", ":")), flush=True)
 
 
 if __name__ == "__main__":
