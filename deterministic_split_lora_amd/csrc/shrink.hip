@@ -33,28 +33,38 @@ namespace {
 // fixed order).
 //
 // The XCDs of an MI355X each have their own L2, so a partial written by one
-// workgroup must reach the device-wide coherence point before another XCD can
-// read it.  A release fence at agent scope would write back this XCD's entire
-// L2 and an acquire would invalidate it - costly at one pair per workgroup.
-// Instead the partials are moved with agent-scope atomic stores and loads,
-// which the hardware performs at the agent coherence point, and ordering is
-// enforced where the fence would enforce it:
-//   writer: agent-scope stores of its partial; wait until every one of them
-//           has completed (s_waitcnt 0); workgroup barrier; one thread adds 1
-//           to the tile's counter (agent-scope integer atomic).
-//   reader: the workgroup whose add returned split_k - 1 arrived last; only
-//           then does it load the S partials (agent-scope loads), evaluate the
-//           same pairwise tree and multiply as the second-pass kernel, write h
-//           and put the counter back to 0 for the next call.
-// Integer atomics only order the arrivals; the floating-point sum has one
-// fixed order whichever workgroup is last.  No workgroup waits for another.
+// workgroup must reach the device-wide coherence point before another XCD
+// reads it.  The ordering is stated in the memory model, at agent scope:
+//   writer: every thread stores its part of the partial (agent-scope atomic
+//           stores, performed at the coherence point); the workgroup barrier
+//           orders all of them before thread 0's counter add, which is a
+//           RELEASE read-modify-write at agent scope - so every partial store
+//           of the workgroup happens before the add.
+//   reader: the workgroup whose add returned split_k - 1 arrived last.  Its
+//           add read the value of the previous add, which continues the
+//           release sequences of all earlier adds; an ACQUIRE fence at agent
+//           scope after it makes every earlier writer's partial visible; the
+//           barrier then passes that to the workgroup's other threads, which
+//           load the S partials, evaluate the same pairwise tree and multiply
+//           as the second-pass kernel, write h and put the counter back to 0
+//           for the next call (the kernel boundary orders that store before
+//           the next call).
+// On gfx950 the release is an L2 write-back plus a wait for the wave's
+// stores (buffer_wbl2 sc1, s_waitcnt vmcnt(0)) issued by one wave per
+// workgroup, and the acquire an L2 invalidate (buffer_inv sc1) issued only by
+// the last arriver.  Integer atomics only order the arrivals; the
+// floating-point sum has one fixed order whichever workgroup is last.  No
+// workgroup waits for another.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ bool arrived_last(int32_t* counter, int split_k, int* flag)
 {
-    __builtin_amdgcn_s_waitcnt(0);            // this thread's partial stores are complete
     __syncthreads();
-    if (threadIdx.x == 0)
-        *flag = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == split_k - 1)
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        *flag = old;
+    }
     __syncthreads();
     return *flag == split_k - 1;
 }

@@ -34,11 +34,14 @@
 // kSpinLimit polls an expand workgroup gives up, sets the status word and
 // leaves y untouched.
 //
-// Memory ordering across XCDs (each has its own L2): the partials travel with
-// agent-scope stores and loads, which the hardware performs at the
-// device-wide coherence point; a writer's counter add is issued only after its
-// stores have completed (s_waitcnt 0 + barrier), and a reader's loads are
-// issued only after its counter poll has returned S x G (barrier).
+// Memory ordering across XCDs (each has its own L2), at agent scope: the
+// partials travel with agent-scope stores and loads; a shrink workgroup's
+// barrier orders all its partial stores before thread 0's arrival add, a
+// RELEASE read-modify-write; an expand workgroup's thread 0 polls the
+// counter with relaxed loads and, once it reads S x G (a value written by
+// the last of those release adds, whose release sequences the earlier adds
+// continue), issues an ACQUIRE fence at agent scope, so every partial store
+// happens before the barrier that lets the workgroup load the partials.
 #include "device.h"
 #include "kernels.h"
 #include "shrink_tile.h"
@@ -76,10 +79,9 @@ __global__ __launch_bounds__(W * 64) void k_shrink_expand_counted(ShrinkParams p
         const int s = (int)(j % (uint32_t)p.split_k);
         const int grp = (int)(j / (uint32_t)p.split_k);
         shrink_tile<RT, W, kToWorkspaceCoherent>(p, row0, nrows, p.A, p.r, grp * 16 * RT, s, 1.0f, lds);
-        __builtin_amdgcn_s_waitcnt(0);        // this thread's partial stores are complete
-        __syncthreads();
-        if (threadIdx.x == 0)
-            __hip_atomic_fetch_add(arrivals, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();                      // every partial store of the workgroup ...
+        if (threadIdx.x == 0)                 // ... happens before this release
+            __hip_atomic_fetch_add(arrivals, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
 
@@ -103,6 +105,8 @@ __global__ __launch_bounds__(W * 64) void k_shrink_expand_counted(ShrinkParams p
             }
             __builtin_amdgcn_s_sleep(1);
         }
+        if (good)                             // pairs with the producers' release adds
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         ok = good;
         // every expand workgroup of the row block has passed its wait once all
         // of them have departed: then the counters can be reset

@@ -172,13 +172,16 @@ int lora_expand_compensated(const float* h, int64_t ld_h, const uint16_t* B, int
 /*
  * Single-launch deterministic Split-K shrink: the paper's final design
  * (section 4.3, Alg. 1).  Each split's workgroup stores its fp32 partial to
- * the workspace with agent-scope stores (performed at the device-wide
- * coherence point, past the per-XCD L2 caches), waits for them to complete,
- * and adds 1 to its row block's integer counter with an agent-scope atomic;
- * the workgroup that sees split_k - 1 arrived last loads the partials with
- * agent-scope loads, applies the same fixed pairwise tree and scale as
- * lora_shrink_splitk, writes h and resets the counter to 0.  Bit for bit the same h as lora_shrink_splitk, in
- * one launch.  No workgroup waits for another.
+ * the workspace with agent-scope atomic stores; after a workgroup barrier one
+ * thread adds 1 to its row block's integer counter with an agent-scope
+ * RELEASE read-modify-write (so every partial store of the workgroup happens
+ * before the add); the workgroup that sees split_k - 1 arrived last issues an
+ * agent-scope ACQUIRE fence, loads the partials with agent-scope loads,
+ * applies the same fixed pairwise tree and scale as lora_shrink_splitk,
+ * writes h and resets the counter to 0.  Bit for bit the same h as
+ * lora_shrink_splitk, in one launch.  No workgroup waits for another.  On
+ * gfx950 each release writes back the XCD's L2, which makes this path slow
+ * when many workgroups arrive (see lora_sgmv_shrink_counted).
  * counters: int32 [lora_shrink_counter_bytes(M) / 4] (8 per 16-token block, one
  * per 16-wide rank tile of a rank <= 128), 4-byte aligned, ALL ZERO
  * before the first call; every completed call leaves them zero again, so one
@@ -293,10 +296,11 @@ int lora_shrink_expand_noalloc(const uint16_t* x, int64_t ld_x, const uint16_t* 
  * lora_shrink_expand_counted: the same h and y as lora_shrink_expand in ONE
  * launch, with a workspace and a counter buffer.  The grid holds, for each
  * 16-token block, its Split-K shrink workgroups (the partial kernel of
- * lora_shrink_partials, stores made device-visible as in
- * lora_shrink_splitk_counted, then one agent-scope add to the block's arrival
- * counter) followed by its expand workgroups, which load their y tile and B
- * rows, wait until the block's counter shows every partial, then evaluate the
+ * lora_shrink_partials with agent-scope atomic stores, then, after a barrier,
+ * one agent-scope RELEASE add to the block's arrival counter) followed by its
+ * expand workgroups, which load their y tile and B rows, wait until the
+ * block's counter shows every partial, issue an agent-scope ACQUIRE fence,
+ * then evaluate the
  * tree + expand of lora_expand_combine.  The wait is bounded; workgroups are
  * dispatched in increasing id and every shrink workgroup of a block precedes
  * the block's expand workgroups, so the wait ends once they have run.
