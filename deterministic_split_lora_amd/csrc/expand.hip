@@ -305,30 +305,55 @@ __global__ __launch_bounds__(256) void k_expand_comp_rows(ExpandParams p, int R)
 // through a separate kernel.  Same bits as shrink then expand.
 constexpr int kHTileStride = 132;         // floats per LDS row (128 + 4 padding)
 
-// XCD: the row blocks are dealt out to the XCDs - workgroup w runs on XCD
-// w % 8 (consecutive workgroups go to different XCDs), and the workgroups of
-// XCD x take row blocks x, x + 8, ... with their column blocks one after
-// another - so a row block's workspace slices are fetched into one L2 instead
-// of every one (B's column blocks are then fetched by every XCD instead).
+// XR: how the (row block, column block) items meet the XCDs - workgroup w
+// runs on XCD w % 8, consecutive workgroups on different XCDs.
+//   XR = 1: column block fastest, so an XCD takes every eighth column block
+//           of every row block (B is fetched once; every row block's
+//           workspace slices by every XCD);
+//   XR = 8: the workgroups of XCD x take row blocks x, x + 8, ... with their
+//           column blocks one after another (a row block's workspace in one
+//           L2; B by every XCD);
+//   XR = 2: two row groups x four column groups (XCD x takes row blocks
+//           x / 4, x / 4 + 2, ... and column blocks x % 4, x % 4 + 4, ...;
+//           the number of column blocks is a multiple of 4): each workspace
+//           slice and each B column reaches 4 and 2 L2s.
 // Workgroups past the last row block exit at once.
-template <int KS, int S, int WAVES, bool XCD>
+template <int XR>
+__device__ __forceinline__ bool combine_item(const ExpandParams& p, int cols, ExpandItem& q)
+{
+    const uint32_t nblocks = (uint32_t)((p.N + cols - 1) / cols);
+    if constexpr (XR == 1) {
+        q = expand_item_at(blockIdx.x, p.M, p.N, cols);
+    } else {
+        const uint32_t x = blockIdx.x % kXcds;
+        const uint32_t j = blockIdx.x / kXcds;
+        int64_t rb;
+        if constexpr (XR == 8) {
+            q.cb = j % nblocks;
+            rb = (int64_t)(j / nblocks) * kXcds + x;
+        } else {
+            constexpr uint32_t XC = kXcds / XR;   // column groups
+            const uint32_t per = nblocks / XC;    // column blocks of one group
+            q.cb = (x % XC) + XC * (j % per);
+            rb = (int64_t)(j / per) * XR + x / XC;
+        }
+        q.row0 = rb * kRowBlock;
+        if (q.row0 >= p.M)
+            return false;
+        const int64_t left = p.M - q.row0;
+        q.nrows = left < kRowBlock ? (int)left : kRowBlock;
+    }
+    return true;
+}
+
+template <int KS, int S, int WAVES, int XR>
 __global__ __launch_bounds__(WAVES * 64) void k_expand_combine(ExpandParams p, TreeParams c)
 {
     constexpr int kCols = WAVES * 64;
     __shared__ __align__(16) float hs[kRowBlock * kHTileStride];
     ExpandItem q;
-    if constexpr (XCD) {
-        const uint32_t nblocks = (uint32_t)((p.N + kCols - 1) / kCols);
-        const uint32_t j = blockIdx.x / kXcds;
-        q.cb = j % nblocks;
-        q.row0 = ((int64_t)(j / nblocks) * kXcds + blockIdx.x % kXcds) * kRowBlock;
-        if (q.row0 >= p.M)                           // uniform
-            return;
-        const int64_t left = p.M - q.row0;
-        q.nrows = left < kRowBlock ? (int)left : kRowBlock;
-    } else {
-        q = expand_item_at(blockIdx.x, p.M, p.N, kCols);
-    }
+    if (!combine_item<XR>(p, kCols, q))            // uniform
+        return;
     const int64_t row0 = q.row0;
     const int nrows = q.nrows;
     const int r = p.r;
@@ -794,35 +819,37 @@ hipError_t launch_expand(const ExpandParams& p, hipStream_t st, int tiles_per_wg
     return hipGetLastError();
 }
 
-template <int KS, int WAVES, bool XCD>
+template <int KS, int WAVES, int XR>
 hipError_t launch_expand_combine_ks(const ExpandParams& p, const TreeParams& c, int S, hipStream_t st)
 {
     int64_t rbs = (p.M + kRowBlock - 1) / kRowBlock;
-    if (XCD)
-        rbs = (rbs + kXcds - 1) / kXcds * kXcds;
+    if (XR > 1)
+        rbs = (rbs + XR - 1) / XR * XR;
     const dim3 grid((unsigned)(rbs * ((p.N + WAVES * 64 - 1) / (WAVES * 64))));
     const dim3 block(WAVES * 64);
     switch (S) {
-    case 1: hipLaunchKernelGGL((k_expand_combine<KS, 1, WAVES, XCD>), grid, block, 0, st, p, c); break;
-    case 2: hipLaunchKernelGGL((k_expand_combine<KS, 2, WAVES, XCD>), grid, block, 0, st, p, c); break;
-    case 4: hipLaunchKernelGGL((k_expand_combine<KS, 4, WAVES, XCD>), grid, block, 0, st, p, c); break;
-    case 8: hipLaunchKernelGGL((k_expand_combine<KS, 8, WAVES, XCD>), grid, block, 0, st, p, c); break;
-    default: hipLaunchKernelGGL((k_expand_combine<KS, 16, WAVES, XCD>), grid, block, 0, st, p, c); break;
+    case 1: hipLaunchKernelGGL((k_expand_combine<KS, 1, WAVES, XR>), grid, block, 0, st, p, c); break;
+    case 2: hipLaunchKernelGGL((k_expand_combine<KS, 2, WAVES, XR>), grid, block, 0, st, p, c); break;
+    case 4: hipLaunchKernelGGL((k_expand_combine<KS, 4, WAVES, XR>), grid, block, 0, st, p, c); break;
+    case 8: hipLaunchKernelGGL((k_expand_combine<KS, 8, WAVES, XR>), grid, block, 0, st, p, c); break;
+    default: hipLaunchKernelGGL((k_expand_combine<KS, 16, WAVES, XR>), grid, block, 0, st, p, c); break;
     }
     return hipGetLastError();
 }
 
 template <int KS>
-hipError_t launch_expand_combine_w(const ExpandParams& p, const TreeParams& c, int S, int waves, bool xcd,
+hipError_t launch_expand_combine_w(const ExpandParams& p, const TreeParams& c, int S, int waves, int xr,
                                    hipStream_t st)
 {
     if (waves == 2)
-        return launch_expand_combine_ks<KS, 2, false>(p, c, S, st);
+        return launch_expand_combine_ks<KS, 2, 1>(p, c, S, st);
     if (waves == 8)
-        return xcd ? launch_expand_combine_ks<KS, 8, true>(p, c, S, st)
-                   : launch_expand_combine_ks<KS, 8, false>(p, c, S, st);
-    return xcd ? launch_expand_combine_ks<KS, 4, true>(p, c, S, st)
-               : launch_expand_combine_ks<KS, 4, false>(p, c, S, st);
+        return xr == 8 ? launch_expand_combine_ks<KS, 8, 8>(p, c, S, st)
+                       : (xr == 2 ? launch_expand_combine_ks<KS, 8, 2>(p, c, S, st)
+                                  : launch_expand_combine_ks<KS, 8, 1>(p, c, S, st));
+    return xr == 8 ? launch_expand_combine_ks<KS, 4, 8>(p, c, S, st)
+                   : (xr == 2 ? launch_expand_combine_ks<KS, 4, 2>(p, c, S, st)
+                              : launch_expand_combine_ks<KS, 4, 1>(p, c, S, st));
 }
 
 // Waves per workgroup of the tree + expand kernel.  Every column block
@@ -849,11 +876,21 @@ hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int
     // (cold inputs, N = 4096, Split-K 8; spread over the XCDs / on one):
     // M = 1024, rank 16: 8.25 / 8.07 us, rank 32: 8.74 / 8.58 us; M = 2048,
     // rank 16: 12.3 / 11.9 us; below, no gain (M = 256, rank 64: 7.89 / 8.12).
-    const bool rows_on_xcd = waves != 2 && (xcd > 0 || (xcd < 0 && (p.M + kRowBlock - 1) / kRowBlock >= 64));
+    // Between, two row groups x four column groups (XR = 2) where the column
+    // blocks split evenly.
+    const int64_t rbs = (p.M + kRowBlock - 1) / kRowBlock;
+    const int64_t nblocks = (p.N + waves * 64 - 1) / (waves * 64);
+    int xr = 1;
+    if (waves != 2) {
+        if (xcd == 8 || (xcd < 0 && rbs >= 64))
+            xr = 8;
+        else if ((xcd == 2 || (xcd < 0 && rbs >= 8)) && nblocks % (kXcds / 2) == 0)
+            xr = 2;
+    }
     switch (expand_steps(p.r)) {
-    case 4: return launch_expand_combine_w<4>(p, c, split_k, waves, rows_on_xcd, st);
-    case 2: return launch_expand_combine_w<2>(p, c, split_k, waves, rows_on_xcd, st);
-    default: return launch_expand_combine_w<1>(p, c, split_k, waves, rows_on_xcd, st);
+    case 4: return launch_expand_combine_w<4>(p, c, split_k, waves, xr, st);
+    case 2: return launch_expand_combine_w<2>(p, c, split_k, waves, xr, st);
+    default: return launch_expand_combine_w<1>(p, c, split_k, waves, xr, st);
     }
 }
 

@@ -202,8 +202,10 @@ hipError_t launch_fill_zero(float* h, int64_t ld_h, int64_t M, int ncols, hipStr
 hipError_t launch_expand(const ExpandParams& p, hipStream_t st, int tiles_per_wg = 0);
 hipError_t launch_expand_compensated(const ExpandParams& p, hipStream_t st, int tiles_per_wg = 0);
 // waves: 2, 4 or 8 waves (128, 256 or 512 columns) per workgroup, 0 = the
-// default rule; xcd: 1 keeps each row block's workgroups on one XCD, 0 does
-// not, -1 = the default rule (any choice gives the same bits).
+// default rule; xcd: how items meet the XCDs - 8 keeps each row block's
+// workgroups on one XCD, 2 splits the XCDs into two row groups x four column
+// groups, 1 spreads a row block's column blocks over all XCDs, -1 = the
+// default rule (any choice gives the same bits).
 hipError_t launch_expand_combine(const ExpandParams& p, const TreeParams& c, int split_k, hipStream_t st,
                                  int waves = 0, int xcd = -1);
 hipError_t launch_sgmv_expand(const ExpandParams& p, hipStream_t st, int tiles_per_wg = 0);

@@ -359,9 +359,10 @@ def test_repeat_1000_bitwise():
 def test_batch_invariance_sweep():
     """16 probe rows of the MLP down-projection shape (K=14336, r=32, N=4096,
     S=8) placed at random positions among N(0,1) filler rows in batches of
-    1, 2, 4, ..., 1024 tokens (four layouts per size, the first launched 1000
-    times): every probe row's h (fp32 bits) and y (bf16 bits) must be
-    identical across repeats, positions and batch sizes."""
+    1, 2, 4, ..., 1024 tokens (20 layouts per size - fresh filler rows and
+    fresh probe positions each - the first launched 1000 times): every probe
+    row's h (fp32 bits) and y (bf16 bits) must be identical across repeats,
+    positions, neighbours and batch sizes."""
     t = torch()
     K, r, N, S, P = 14336, 32, 4096, 8, 16
     probe = normal_bf16((P, K), 1.0, 0, "probe_x")
@@ -372,7 +373,7 @@ def test_batch_invariance_sweep():
     ref_h = ref_y = None
     rng = np.random.default_rng(0)
     for b in [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1024]:
-        for layout in range(4):
+        for layout in range(20):
             # which probe rows go in this batch and where
             groups = [list(range(i, i + b)) for i in range(0, P, b)] if b < P else [list(range(P))]
             for grp in groups:
@@ -423,11 +424,13 @@ def test_batch_invariance_sweep():
     check_expand(ref_y, yo, e, ab, ybase, "probe expand", r=r)
 
 
-def test_atomic_variant_varies_on_crafted_input():
+def test_atomic_variant_varies_on_crafted_input(record_property):
     """The atomic variant's result depends on the order its splits land.  With
     P = (2^100, 1, -2^100, 1, 0...) every order gives 0, 1 or 2.  The
-    deterministic path gives 0 every time.  Reports how many distinct atomic
-    results 2000 launches produced."""
+    deterministic path gives 0 every time.  Reports (prints and records as a
+    test property) the distinct atomic results 2000 launches produced and how
+    often each occurred; how many appear depends on scheduling, so no count
+    is asserted."""
     t = torch()
     K, S, r = 1024, 8, 8
     two50, one = 0x5880, 0x3F80
@@ -446,9 +449,11 @@ def test_atomic_variant_varies_on_crafted_input():
     D = t.stack(det).cpu().numpy()
     Aa = t.stack(atom).cpu().numpy()
     assert np.all(D == 0.0)
-    vals_seen = sorted(set(Aa.reshape(-1).tolist()))
-    assert set(vals_seen) <= {0.0, 1.0, 2.0}
-    _say(f"  atomic results seen over 2000 launches x {r} columns: {vals_seen}")
+    vals, counts = np.unique(Aa.reshape(-1), return_counts=True)
+    seen = {float(v): int(n) for v, n in zip(vals, counts)}
+    assert set(seen) <= {0.0, 1.0, 2.0}
+    record_property("atomic_results_seen", seen)
+    _say(f"  atomic results over 2000 launches x {r} columns (value: count): {seen}; deterministic: 0 every time")
 
 
 # ---------------------------------------------------------------------------
