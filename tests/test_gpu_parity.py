@@ -483,7 +483,8 @@ def _build_plan(ids, n):
     return idg, plan
 
 
-@pytest.mark.parametrize("case", ["segments", "singletons", "invalid", "long", "one_adapter", "large"])
+@pytest.mark.parametrize("case", ["segments", "singletons", "invalid", "long", "one_adapter", "large",
+                                  "runs_across_passes", "pass_edges", "one_run_8193"])
 def test_sgmv_plan_tiles(case):
     rng = np.random.default_rng(zlib.crc32(case.encode()))
     if case == "segments":
@@ -496,6 +497,15 @@ def test_sgmv_plan_tiles(case):
         ids, n = segments_to_ids(5000, [(s, l, a) for s, l, a in _segs(5000, 32, 512, 32, rng)]), 32
     elif case == "one_adapter":
         ids, n = np.zeros(1025, np.int32), 1
+    elif case == "runs_across_passes":     # runs of 1000-9000 tokens over the 8192-token passes
+        ids, n = segments_to_ids(30000, [(s, l, a) for s, l, a in _segs(30000, 1000, 9000, 3, rng)]), 3
+    elif case == "pass_edges":             # run changes right at and next to the pass boundaries
+        ids = np.zeros(16390, np.int32)
+        for cut in (8190, 8191, 8192, 8193, 16383, 16384, 16385):
+            ids[cut:] += 1
+        ids, n = ids % 3, 3
+    elif case == "one_run_8193":
+        ids, n = np.full(8193, 2, np.int32), 3
     else:
         ids, n = rng.integers(0, 2, 20000).astype(np.int32), 2
     _say(f"plan {case}: M={len(ids)}")
