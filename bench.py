@@ -730,24 +730,29 @@ def sgmv_replay(st, det_call, atomic_call, repeats):
     return out
 
 
-def decode_probe(args, M=32):
-    """M decode tokens, each with its own rank-64 adapter, hidden 8192, Split-K 8:
-    the multi-adapter deterministic shrink (partials + fixed tree) on a prebuilt
-    plan, cold cache.  Algorithmic bytes: x, every adapter's A once, h."""
+def decode_probe(args, M=32, mixed=False):
+    """M decode tokens, each with its own adapter, hidden 8192, Split-K 8: the
+    multi-adapter deterministic shrink (partials + fixed tree) on a prebuilt
+    plan, cold cache, against the atomic contrast (zero h + the same partial
+    kernel with fp32 atomic adds).  Adapters of rank 64, or with `mixed` the
+    prefill workload's pool (ranks cycling 8, 16, 32, 64).  Algorithmic bytes:
+    x, every adapter's A once at its own rank, h at each token's rank."""
     import torch
     import deterministic_split_lora_amd as dsl
     from synth import normal_bf16
     dev = torch.device("cuda:0")
-    K, r, S, n = 8192, 64, 8, M
+    K, S, n = 8192, 8, M
+    rk = [(8, 16, 32, 64)[a % 4] if mixed else 64 for a in range(n)]
+    r = max(rk)
 
     def g(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
     x = normal_bf16((M, K), 1.0, 0, "probe_x")
-    As = [normal_bf16((r, K), 0.02, 0, f"probe_A{a}") for a in range(n)]
-    byt = 2 * M * K + 2 * K * r * n + 4 * M * r
+    As = [normal_bf16((rk[a], K), 0.02, 0, f"probe_A{a}") for a in range(n)]
+    byt = 2 * M * K + 2 * K * sum(rk) + 4 * sum(rk)
     copies = 1 if args.hot else max(2, math.ceil(ROTATE_BYTES / byt))
     ids = torch.arange(M, dtype=torch.int32, device=dev)
-    ranks = torch.full((n,), r, dtype=torch.int32, device=dev)
+    ranks = torch.tensor(rk, dtype=torch.int32, device=dev)
     plan = torch.empty(dsl.lora_sgmv_plan_bytes(M), dtype=torch.uint8, device=dev)
     dsl.lora_sgmv_plan(ids, n, plan)
     sets = []
@@ -766,14 +771,19 @@ def decode_probe(args, M=32):
     def counted(s):
         dsl.lora_sgmv_shrink_counted(s["x"], s["Ap"], K, ranks, None, n, plan, s["h"], r, S, s["ws"], cnt)
 
-    out = {"workload": f"{M} tokens x hidden 8192, {M} adapters of rank 64 (one per token), Split-K 8, "
+    def atomic(s):
+        dsl.lora_sgmv_shrink_atomic(s["x"], s["Ap"], K, ranks, None, n, plan, s["h"], r, S)
+
+    pool = "ranks cycling 8, 16, 32, 64" if mixed else "rank 64"
+    out = {"workload": f"{M} tokens x hidden 8192, {M} adapters of {pool} (one per token), Split-K 8, "
                        "multi-adapter deterministic shrink", "bytes": byt, "copies": copies}
-    for name, call in (("two_launch", two_launch), ("single_launch", counted)):
+    for name, call in (("two_launch", two_launch), ("single_launch", counted), ("atomic", atomic)):
         us = _time_rotating(call, sets, args)
         out[name] = {"us_per_call": round(us, 3), "GBps": round(byt / us / 1e3, 1),
                      "pct_hbm_peak": round(100 * byt / us / 1e3 / HBM_PEAK_GBS, 2)}
     best = min(out["two_launch"]["us_per_call"], out["single_launch"]["us_per_call"])
     out["best_pct_hbm_peak"] = round(100 * byt / best / 1e3 / HBM_PEAK_GBS, 2)
+    out["det_over_atomic"] = round(best / out["atomic"]["us_per_call"], 4)
     return out
 
 
@@ -1038,6 +1048,7 @@ ONLY = {
                                          replays=50),
     "decode_probe": lambda a: decode_probe(a, 128),
     "decode_probe32": lambda a: decode_probe(a, 32),
+    "decode_probe32_mixed": lambda a: decode_probe(a, 32, mixed=True),
     "decode_expand": lambda a: {"32": decode_expand_probe(a, 32), "128": decode_expand_probe(a, 128)},
     "batch_sweep": batch_sweep_bench,
     "compensated": compensated_bench,
@@ -1048,7 +1059,7 @@ def _r(v, nd=3):
     return None if v is None else round(float(v), nd)
 
 
-def summarize(res, extra, probe, wide, dexp, roof, floor, replay):
+def summarize(res, extra, probe, mixed, wide, dexp, roof, floor, replay):
     """The compact view of every measurement, small enough for one stored
     JSON line: per-config det and atomic microseconds per call with their
     ratio and HBM share, the decode probes, replay and ceiling figures."""
@@ -1092,12 +1103,14 @@ def summarize(res, extra, probe, wide, dexp, roof, floor, replay):
     out["configs"] = cfg
     if probe:
         out["decode_probe"] = {
-            f"m{M}": {"bytes": p_["bytes"], "us": min(p_["two_launch"]["us_per_call"],
+            M: {"bytes": p_["bytes"], "us": min(p_["two_launch"]["us_per_call"],
                                                                       p_["single_launch"]["us_per_call"]),
                                      "two_launch_us": p_["two_launch"]["us_per_call"],
                                      "single_launch_us": p_["single_launch"]["us_per_call"],
+                                     "atomic_us": p_["atomic"]["us_per_call"],
+                                     "det_over_atomic": p_["det_over_atomic"],
                                      "pct_hbm_peak": p_["best_pct_hbm_peak"]}
-            for M, p_ in ((32, probe), (128, wide))}
+            for M, p_ in (("m32", probe), ("m32_mixed_ranks", mixed), ("m128", wide))}
         out["decode_expand_probe"] = {m: {"expand_us": v["expand"]["us_per_call"],
                                           "expand_pct": v["expand"]["pct_hbm_peak"],
                                           "shrink_expand_us": v["shrink_expand"]["us_per_call"],
@@ -1152,9 +1165,10 @@ def main():
     res = b.run()
     log("bench: main timing done")
     prov = provenance(b)
-    probe = wide = roof = floor = extra = replay = dexp = None
+    probe = wide = mixed = roof = floor = extra = replay = dexp = None
     if not args.no_probe:
         probe = decode_probe(args, 32)
+        mixed = decode_probe(args, 32, mixed=True)
         wide = decode_probe(args, 128)
         dexp = {"32": decode_expand_probe(args, 32), "128": decode_expand_probe(args, 128)}
         avg = int(res["roofline"]["algorithmic_bytes_per_launch"]) // 2 // 16 * 16
@@ -1178,7 +1192,7 @@ def main():
         log("bench: sgmv prefill done")
     cpu = None if args.no_cpu else cpu_baseline(args.cpu_seconds)
     log("bench: cpu baseline done")
-    summary = summarize(res, extra, probe, wide, dexp, roof, floor, replay)
+    summary = summarize(res, extra, probe, mixed, wide, dexp, roof, floor, replay)
     out = {
         "metric": METRIC,
         "value": round(res["us_per_call"], 3),
@@ -1206,7 +1220,8 @@ def main():
     }
     out.update(summary)
     if args.detail:
-        detail = dict(out, per_m_detail=res["per_m"], decode_bandwidth_probe=probe, decode_bandwidth_probe_wide=wide,
+        detail = dict(out, per_m_detail=res["per_m"], decode_bandwidth_probe=probe, decode_bandwidth_probe_mixed=mixed,
+                      decode_bandwidth_probe_wide=wide,
                       decode_expand_probe_detail=dexp, copy_roofline=roof, replay_variability=replay,
                       other_shapes=extra)
         os.makedirs(os.path.dirname(os.path.abspath(args.detail)), exist_ok=True)

@@ -43,6 +43,24 @@
  * timing.  The Split-K plan (lora_shrink_plan) is a function of (K, split_k)
  * alone.
  *
+ * SIGNATURE NOTES, for callers used to other LoRA kernel interfaces:
+ *   - A is [r][K] and B is [N][r] (Eq. 1's orientation), not K x r and r x N:
+ *     a caller holding A as [K][r] passes its transpose.  Both operands of
+ *     every matrix-core step are then contiguous along the reduced dimension.
+ *   - The multi-adapter shrinks take a device plan made by lora_sgmv_plan
+ *     from the per-token adapter ids (tiles of at most 16 consecutive tokens
+ *     with one adapter), not the ids alone; build it once per batch and reuse
+ *     it for every layer.  lora_sgmv_shrink_counted and
+ *     lora_sgmv_shrink_atomic read the ids only through the plan; the
+ *     expands read token_adapter directly.
+ *   - Adapters are passed as device arrays of A and B addresses, with one
+ *     leading dimension ld_a for every A and every B_a packed as
+ *     [N][r_a rounded up to 8], plus device arrays of ranks and
+ *     (optionally) scales.
+ *   - Split-K workspaces, counters and plans are caller buffers whose sizes
+ *     the *_bytes functions return; every entry point takes leading
+ *     dimensions and a stream.
+ *
  * SUPPORTED (otherwise LORA_ERR_UNSUPPORTED / LORA_ERR_ALIGN):
  *   1 <= r <= 128 (lora_shrink_expand_fused: r <= 64);  split_k in {1, 2, 4, 8, 16};
  *   K % (32 * split_k) == 0;
