@@ -258,18 +258,28 @@ class Bench:
             cand.append((sum(per.values()), len(two), byt, COMBINE_KERNEL + " (fixed tree over the Split-K "
                          "workspace + expand; M=" + "/".join(map(str, two)) + ")",
                          {str(M): round(u, 3) for M, u in per.items()}))
-        us, n, byt, name, per = max(cand, key=lambda c: c[0])
-        avg_launch_us = us / n
-        avg_bytes = byt / n
-        ach = avg_bytes / avg_launch_us / 1e3
-        traffic = recorded_traffic(COMBINE_KERNEL, two) if name.startswith(COMBINE_KERNEL) else None
-        res["roofline"] = {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic,
-                           "avg_launch_us": round(avg_launch_us, 3), "launch_us_per_m": per,
-                           "algorithmic_bytes_per_launch": avg_bytes,
-                           "timing": "HIP events over graphs of 8 back-to-back launches: a launch's time includes "
-                                     "the gap to the next dispatch"}
+        res["roofline"] = pick_roofline(cand, lambda name: recorded_traffic(COMBINE_KERNEL, two)
+                                        if name.startswith(COMBINE_KERNEL) else None)
         return res
+
+
+def pick_roofline(cand, traffic_for):
+    """The roofline object for the dominant kernel of the step.  `cand` holds
+    one (total us, launches, total algorithmic bytes, kernel name, per-M us or
+    None) tuple per kernel the step launches; the one with the most time is
+    the dominant kernel; achieved = its algorithmic bytes per launch over its
+    mean launch time; traffic_for(name) gives the counter-based HBM bytes per
+    launch, or None."""
+    us, n, byt, name, per = max(cand, key=lambda c: c[0])
+    avg_launch_us = us / n
+    avg_bytes = byt / n
+    ach = avg_bytes / avg_launch_us / 1e3
+    return {"kernel": name, "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic_for(name),
+            "avg_launch_us": round(avg_launch_us, 3), "launch_us_per_m": per,
+            "algorithmic_bytes_per_launch": avg_bytes,
+            "timing": "HIP events over graphs of 8 back-to-back launches: a launch's time includes "
+                      "the gap to the next dispatch"}
 
 
 COMBINE_KERNEL = "k_expand_combine<1,8>"
