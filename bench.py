@@ -602,7 +602,7 @@ def compensated_bench(args):
     return out
 
 
-def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S, replays=100):
+def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S, replays=100, ids=None):
     """Multi-adapter shrink and expand on a prebuilt plan, cold cache.
     Compulsory bytes count only the adapters some token uses, at their own
     rank: shrink 2MK + 2K sum(r) + 4 M r_max (h), expand 4 sum_i r_(a_i) (h)
@@ -611,7 +611,7 @@ def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S, replays=100):
     import torch
     import deterministic_split_lora_amd as dsl
     from synth import sgmv_case
-    c = sgmv_case(M, K, N, ranks, seg_lo, seg_hi, S, seed=0, tag=label)
+    c = sgmv_case(M, K, N, ranks, seg_lo, seg_hi, S, seed=0, tag=label, ids=ids)
     dev = torch.device("cuda:0")
     n = len(c.ranks)
     valid = (c.ids >= 0) & (c.ids < n)
@@ -677,8 +677,10 @@ def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S, replays=100):
         atomic_shrink(st)
         expand(st)
 
+    layout = (f"segments {seg_lo}..{seg_hi} tokens" if ids is None
+              else "ids drawn per token (interleaved, as decode tokens of many requests)")
     out = {"workload": f"M={M}, K={K}, N={N}, {n} adapters of ranks {sorted(set(int(v) for v in c.ranks))}, "
-                       f"segments {seg_lo}..{seg_hi} tokens, Split-K {S}",
+                       f"{layout}, Split-K {S}",
            "segments": len(c.segs), "touched_adapters": len(touched), "shrink_bytes": sh_bytes,
            "expand_bytes": ex_bytes, "workspace_bytes": 8 * S * M * c.r_max,
            "copies": {"x_A": copies_sh, "y_B_h": copies_ex}}
@@ -1054,6 +1056,8 @@ def provenance(b):
 ONLY = {
     "replay": replay_variability,
     "sgmv_qkv": lambda a: sgmv_bench(a, "b3", 512, 4096, 6144, [64] * 4, 1, 64, 8, replays=200),
+    "sgmv_interleaved": lambda a: sgmv_bench(a, "b3i", 512, 4096, 6144, [64] * 4, 0, 0, 8, replays=50,
+                                             ids=np.random.default_rng(7).integers(0, 4, 512).astype(np.int32)),
     "sgmv_prefill": lambda a: sgmv_bench(a, "b5", 4096, 8192, 28672, [8, 16, 32, 64] * 8, 32, 512, 16,
                                          replays=50),
     "decode_probe": lambda a: decode_probe(a, 128),
@@ -1083,6 +1087,7 @@ def summarize(res, extra, probe, mixed, wide, dexp, roof, floor, replay):
         cfg["small_m8_k1024_r8_shrink"] = {"det_us": so["det_two_launch_us"], "det_one_launch_us": so["det_one_launch_us"],
                                            "atomic_us": so["atomic_us"], "det_over_atomic": so["det_over_atomic"]}
         for key, name in (("sgmv_m512_k4096_n6144_4x_r64", "sgmv_m512_k4096_n6144_4x_r64"),
+                          ("sgmv_m512_k4096_n6144_4x_r64_interleaved", "sgmv_m512_k4096_n6144_4x_r64_interleaved"),
                           ("sgmv_prefill_m4096_k8192_n28672_32_adapters", "sgmv_prefill_m4096_k8192_n28672")):
             e = extra[key]
             rp = e["replay"]
@@ -1197,6 +1202,7 @@ def main():
         extra["compensated_expand"] = compensated_bench(args)
         log("bench: compensated expand done")
         extra["sgmv_m512_k4096_n6144_4x_r64"] = ONLY["sgmv_qkv"](args)
+        extra["sgmv_m512_k4096_n6144_4x_r64_interleaved"] = ONLY["sgmv_interleaved"](args)
         log("bench: sgmv 512 done")
         extra["sgmv_prefill_m4096_k8192_n28672_32_adapters"] = ONLY["sgmv_prefill"](args)
         log("bench: sgmv prefill done")

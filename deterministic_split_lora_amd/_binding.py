@@ -59,7 +59,7 @@ _f32 = ctypes.c_float
 _sz = ctypes.c_size_t
 
 # LORA_DET_ABI_VERSION of include/lora_det.h that these signatures follow.
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 
 def lib():

@@ -911,7 +911,7 @@ size_t lora_sgmv_plan_bytes(int64_t M)
 {
     if (M < 0 || M > kMaxDim)
         return 0;
-    return (size_t)kPlanHeaderInts * 4 + (size_t)12 * (size_t)M;
+    return (size_t)kPlanHeaderInts * 4 + (size_t)kPlanTileInts * 4 * (size_t)M;
 }
 
 int lora_sgmv_plan(const int32_t* token_adapter, int64_t M, int32_t n_adapters, void* plan,

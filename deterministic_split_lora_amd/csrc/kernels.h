@@ -13,10 +13,15 @@ constexpr int kGroupTiles = 4;               // rank tiles one shrink workgroup 
 constexpr int kFusedMaxRank = 64;            // rank bound of the single-launch recompute kernel
 
 // Plan buffer: int32 header [ntiles, M, n_adapters, magic], then ntiles
-// triples (first token, token count 1..16, adapter id or -1 for tokens
-// without an adapter).
+// entries of kPlanTileInts: first token row0, span 1..16, adapter id (-1 for
+// tokens without an adapter), row mask.  The tile's tokens are the rows
+// row0 + i (i < span) whose mask bit i is set; the other rows of the span
+// belong to other tiles (a 16-token block holding several adapters gives one
+// tile per adapter).
 constexpr int kPlanHeaderInts = 4;
-constexpr int32_t kPlanMagic = 0x4C6F5241;   // "LoRA"
+constexpr int kPlanTileInts = 4;
+constexpr int32_t kPlanMagic = 0x4C6F5242;   // "LoRB"
+constexpr uint32_t kFullMask = 0xFFFFu;
 
 struct ShrinkParams {
     const uint16_t* x;
@@ -85,10 +90,21 @@ __device__ __forceinline__ int plan_tiles(const int32_t* plan, int64_t M, int32_
     return n < 0 ? 0 : (n > M ? (int)M : n);
 }
 
-// A tile entry covers 1..16 rows inside [0, M) ...
+// A tile entry spans 1..16 rows inside [0, M) ...
 __device__ __forceinline__ bool tile_rows_ok(const int32_t* t, int64_t M)
 {
     return t[0] >= 0 && t[1] >= 1 && t[1] <= kRowBlock && (int64_t)t[0] + t[1] <= M;
+}
+
+// ... of which the rows whose mask bit is set are the tile's
+__device__ __forceinline__ uint32_t tile_mask(const int32_t* t)
+{
+    return (uint32_t)t[3] & ((1u << t[1]) - 1u);
+}
+
+__device__ __forceinline__ bool row_in(uint32_t mask, int row)
+{
+    return (mask >> row) & 1u;
 }
 
 // ... and is computed on only if it also names a valid adapter (tiles of

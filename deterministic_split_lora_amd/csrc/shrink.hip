@@ -69,14 +69,17 @@ __device__ __forceinline__ bool arrived_last(int32_t* counter, int split_k, int*
     return *flag == split_k - 1;
 }
 
-// h rows row0 .. row0+nrows-1, columns [c0, c_zero): scale * tree over the S
-// workspace slices for columns below c_data, zeros from c_data on.
-__device__ __forceinline__ void combine_tile(const ShrinkParams& p, int64_t row0, int nrows, int c0, int c_data,
-                                             int c_zero, float scale, float* h, int64_t ld_h)
+// h rows row0 + i (i < nrows, bit i of mask set), columns [c0, c_zero):
+// scale * tree over the S workspace slices for columns below c_data, zeros
+// from c_data on.
+__device__ __forceinline__ void combine_tile(const ShrinkParams& p, int64_t row0, int nrows, uint32_t mask, int c0,
+                                             int c_data, int c_zero, float scale, float* h, int64_t ld_h)
 {
     const int ncols = c_zero - c0;
     for (int e = threadIdx.x; e < nrows * ncols; e += blockDim.x) {
         const int row = e / ncols;
+        if (!row_in(mask, row))
+            continue;
         const int col = c0 + (e - row * ncols);
         float val = 0.0f;
         if (col < c_data) {
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(W * 64) void k_shrink_partial(ShrinkParams p, int g
 {
     __shared__ float red[red_floats<RT, W>()];
     const SingleItem q = single_item(p, groups);
-    shrink_tile<RT, W, MODE>(p, q.row0, q.nrows, p.A, p.r, q.grp * 16 * RT, q.s, p.scale, red);
+    shrink_tile<RT, W, MODE>(p, q.row0, q.nrows, kFullMask, p.A, p.r, q.grp * 16 * RT, q.s, p.scale, red);
 }
 
 // Large M: T consecutive row blocks per workgroup, all rank tiles together,
@@ -139,14 +142,17 @@ __global__ __launch_bounds__(W * 64, 4) void k_shrink_partial_multi(ShrinkParams
     const int64_t first = (int64_t)(blockIdx.x / S) * T * kRowBlock;
     int64_t row0[T];
     int nrows[T];
+    uint32_t mask[T];
 #pragma unroll
     for (int u = 0; u < T; ++u) {
         const int64_t r0 = first + (int64_t)u * kRowBlock;
         const int64_t left = p.M - r0;
         nrows[u] = left <= 0 ? 0 : (left < kRowBlock ? (int)left : kRowBlock);
         row0[u] = nrows[u] > 0 ? r0 : first;      // empty tiles keep a valid base address
+        mask[u] = kFullMask;
     }
-    shrink_tiles<RT, W, MODE, T>(p, row0, nrows, p.A, p.r, 0, s, MODE == kAtomicScaled ? p.scale : 1.0f, red);
+    shrink_tiles<RT, W, MODE, T>(p, row0, nrows, mask, p.A, p.r, 0, s, MODE == kAtomicScaled ? p.scale : 1.0f,
+                                 red);
 }
 
 // Single launch: the last split of each (row block, rank group) writes h.
@@ -159,11 +165,11 @@ __global__ __launch_bounds__(W * 64) void k_shrink_counted(ShrinkParams p, Count
     const int64_t row0 = q.row0;
     const int nrows = q.nrows;
     const int col0 = q.grp * 16 * RT;
-    shrink_tile<RT, W, kToWorkspaceCoherent>(p, row0, nrows, p.A, p.r, col0, q.s, 1.0f, red);
+    shrink_tile<RT, W, kToWorkspaceCoherent>(p, row0, nrows, kFullMask, p.A, p.r, col0, q.s, 1.0f, red);
     int32_t* counter = c.counters + q.mb * kMaxRankTiles + q.grp;
     if (arrived_last(counter, p.split_k, &flag)) {
         const int cend = col0 + 16 * RT < p.r ? col0 + 16 * RT : p.r;
-        combine_tile(p, row0, nrows, col0, cend, cend, p.scale, c.h, c.ld_h);
+        combine_tile(p, row0, nrows, kFullMask, col0, cend, cend, p.scale, c.h, c.ld_h);
         if (threadIdx.x == 0)
             __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -178,6 +184,7 @@ __global__ __launch_bounds__(W * 64) void k_shrink_counted(ShrinkParams p, Count
 struct SgmvItem {
     int64_t row0;
     int nrows;
+    uint32_t mask;   // the tile's rows among row0 .. row0 + nrows - 1
     int a;           // adapter, -1 for tokens without one
     int s;
     int grp;
@@ -193,10 +200,11 @@ __device__ __forceinline__ SgmvItem sgmv_item(const ShrinkParams& p, uint32_t it
     const uint32_t rest = it / S;
     q.grp = (int)(rest % (uint32_t)groups);
     q.tile = (int)(rest / (uint32_t)groups);
-    const int32_t* t = p.tiles + kPlanHeaderInts + 3 * q.tile;
+    const int32_t* t = p.tiles + kPlanHeaderInts + kPlanTileInts * q.tile;
     q.ok = tile_rows_ok(t, p.M) && t[2] >= -1 && t[2] < p.n_adapters;
     q.row0 = t[0];
     q.nrows = t[1];
+    q.mask = q.ok ? tile_mask(t) : 0u;
     q.a = t[2];
     return q;
 }
@@ -233,8 +241,8 @@ __global__ __launch_bounds__(W * 64) void k_sgmv_shrink_partial(ShrinkParams p)
         const int col0 = q.grp * 16 * RT;
         if (col0 >= ra)
             continue;
-        shrink_tile<RT, W, MODE>(p, q.row0, q.nrows, p.A_ptrs[q.a], ra, col0, q.s, sgmv_item_scale<MODE>(p, q.a),
-                                 red);
+        shrink_tile<RT, W, MODE>(p, q.row0, q.nrows, q.mask, p.A_ptrs[q.a], ra, col0, q.s,
+                                 sgmv_item_scale<MODE>(p, q.a), red);
     }
 }
 
@@ -257,7 +265,7 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_partial_multi(ShrinkP
         const int c1 = c0 + T < ntiles ? c0 + T : ntiles;
         int j = c0;
         while (j < c1) {                          // uniform: plan data only
-            const int32_t* t = plan + 3 * j;
+            const int32_t* t = plan + kPlanTileInts * j;
             if (!tile_ok(t, p.M, p.n_adapters)) {
                 ++j;
                 continue;
@@ -265,19 +273,21 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_partial_multi(ShrinkP
             const int a = t[2];
             int64_t row0[T];
             int nrows[T];
+            uint32_t mask[T];
             int n = 0;
 #pragma unroll
             for (int u = 0; u < T; ++u) {
-                const int32_t* tu = plan + 3 * (j + u);
+                const int32_t* tu = plan + kPlanTileInts * (j + u);
                 const bool take = n == u && j + u < c1 && tile_ok(tu, p.M, p.n_adapters) && tu[2] == a;
                 row0[u] = take ? tu[0] : t[0];
                 nrows[u] = take ? tu[1] : 0;
+                mask[u] = take ? tile_mask(tu) : 0u;
                 n += take ? 1 : 0;
             }
             const int ra = adapter_rank(p, a);
             if (ra > 0)
-                shrink_tiles<RT, W, MODE, T>(p, row0, nrows, p.A_ptrs[a], ra, 0, s, sgmv_item_scale<MODE>(p, a),
-                                             red);
+                shrink_tiles<RT, W, MODE, T>(p, row0, nrows, mask, p.A_ptrs[a], ra, 0, s,
+                                             sgmv_item_scale<MODE>(p, a), red);
             j += n;
         }
     }
@@ -306,7 +316,7 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
     constexpr int NB = 3;
     constexpr int RS = 16 * RT + 4;               // padded LDS row stride (floats)
     __shared__ __align__(16) float red[2][W * 16 * RS];
-    __shared__ int32_t tl[3 * kStreamMaxRows];    // the item's plan entries
+    __shared__ int32_t tl[kPlanTileInts * kStreamMaxRows];   // the item's plan entries
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int li = lane & 15;
@@ -315,23 +325,26 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
     const int64_t ntiles = SGMV ? plan_tiles(p.tiles, p.M, p.n_adapters) : (p.M + kRowBlock - 1) / kRowBlock;
     const uint32_t S = (uint32_t)p.split_k;
     const uint32_t items = (uint32_t)((ntiles + R - 1) / R) * S;
-    // tile j (the item's u-th): first row, row count (0: nothing to compute)
-    // and adapter; plan entries come from LDS, so reading them never waits
-    // for the x loads in flight
-    auto tile = [&](int64_t j, int u, int64_t& row0, int& nrows, int& a) {
+    // tile j (the item's u-th): first row, row span (0: nothing to compute),
+    // adapter and row mask; plan entries come from LDS, so reading them never
+    // waits for the x loads in flight
+    auto tile = [&](int64_t j, int u, int64_t& row0, int& nrows, int& a, uint32_t& msk) {
         if constexpr (SGMV) {
             // uniform by construction: scalar registers
-            const int32_t t[3] = {__builtin_amdgcn_readfirstlane(tl[3 * u]),
-                                  __builtin_amdgcn_readfirstlane(tl[3 * u + 1]),
-                                  __builtin_amdgcn_readfirstlane(tl[3 * u + 2])};
+            const int32_t t[kPlanTileInts] = {__builtin_amdgcn_readfirstlane(tl[kPlanTileInts * u]),
+                                              __builtin_amdgcn_readfirstlane(tl[kPlanTileInts * u + 1]),
+                                              __builtin_amdgcn_readfirstlane(tl[kPlanTileInts * u + 2]),
+                                              __builtin_amdgcn_readfirstlane(tl[kPlanTileInts * u + 3])};
             const bool ok = tile_ok(t, p.M, p.n_adapters);
             row0 = ok ? t[0] : 0;
             nrows = ok ? t[1] : 0;
             a = ok ? t[2] : -1;
+            msk = ok ? tile_mask(t) : 0u;
         } else {
             row0 = j * kRowBlock;
             nrows = p.M - row0 < kRowBlock ? (int)(p.M - row0) : kRowBlock;
             a = 0;
+            msk = kFullMask;
         }
     };
     // this thread's elements of a block's 16 x 16 RT partial tile: row, column
@@ -364,8 +377,8 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
         const int cnt = ntiles - c0 < R ? (int)(ntiles - c0) : R;
         if constexpr (SGMV) {
             __syncthreads();                      // the previous item's entries are no longer read
-            if ((int)threadIdx.x < 3 * cnt)
-                tl[threadIdx.x] = plan[3 * c0 + threadIdx.x];
+            if ((int)threadIdx.x < kPlanTileInts * cnt)
+                tl[threadIdx.x] = plan[kPlanTileInts * c0 + threadIdx.x];
             __syncthreads();
         }
         // reduction slots 8g..8g+7 of step t hold k = kbase + 32 t + (0..7)
@@ -373,7 +386,8 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
         auto xload = [&](int u, bf16x8 (&dst)[STEPS]) {
             int64_t row0;
             int nrows, a;
-            tile(c0 + u, u, row0, nrows, a);
+            uint32_t msk;
+            tile(c0 + u, u, row0, nrows, a, msk);
             const uint16_t* xp = p.x + (row0 + (li < nrows ? li : 0)) * p.ld_x + kbase;
 #pragma unroll
             for (int t = 0; t < STEPS; ++t)
@@ -389,13 +403,15 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
         while (u < cnt) {
             int64_t row0;
             int nrows, a;
-            tile(c0 + u, u, row0, nrows, a);      // uniform: plan data only
+            uint32_t msk;
+            tile(c0 + u, u, row0, nrows, a, msk); // uniform: plan data only
             int u1 = u + 1;
             if constexpr (SGMV) {
                 while (u1 < cnt) {
                     int64_t r1;
                     int n1, a1;
-                    tile(c0 + u1, u1, r1, n1, a1);
+                    uint32_t m1;
+                    tile(c0 + u1, u1, r1, n1, a1, m1);
                     if (a1 != a)
                         break;
                     ++u1;
@@ -435,7 +451,7 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
             // loads in flight.
             auto block = [&](const bf16x8 (&xc)[STEPS], bf16x8 (&xn)[STEPS], float (&kept)[EPT]) {
                 xload(u + NB - 1 < u1 ? u + NB - 1 : u1 - 1, xn);   // unconditional: no branch-dependent buffer
-                tile(c0 + u, u, row0, nrows, a);
+                tile(c0 + u, u, row0, nrows, a, msk);
                 const bool on = nrows > 0 && ra > 0;
                 float* rb = red[k & 1];
                 f32x4 acc[RT];
@@ -462,7 +478,7 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
                                                       (uint32_t)(16 * p.ld_out * 4));
 #pragma unroll
                     for (int q = 0; q < EPT; ++q) {
-                        const bool mine = erow[q] < nrows && ecol[q] < ncols;
+                        const bool mine = erow[q] < nrows && row_in(msk, erow[q]) && ecol[q] < ncols;
                         float val = 0.0f;
                         if (mine) {
                             float v[W];
@@ -534,20 +550,22 @@ __global__ __launch_bounds__(W * 64) void k_sgmv_shrink_counted(ShrinkParams p, 
         if (q.a < 0) {
             if (q.s == 0 && q.grp == 0)
                 for (int e = threadIdx.x; e < q.nrows * p.r_max; e += blockDim.x)
-                    c.h[(q.row0 + e / p.r_max) * c.ld_h + e % p.r_max] = 0.0f;
+                    if (row_in(q.mask, e / p.r_max))
+                        c.h[(q.row0 + e / p.r_max) * c.ld_h + e % p.r_max] = 0.0f;
             continue;
         }
         const int ra = adapter_rank(p, q.a);
         const int col0 = q.grp * 16 * RT;
         if (col0 >= ra)
             continue;
-        shrink_tile<RT, W, kToWorkspaceCoherent>(p, q.row0, q.nrows, p.A_ptrs[q.a], ra, col0, q.s, 1.0f, red);
+        shrink_tile<RT, W, kToWorkspaceCoherent>(p, q.row0, q.nrows, q.mask, p.A_ptrs[q.a], ra, col0, q.s, 1.0f,
+                                                 red);
         int32_t* counter = c.counters + (int64_t)q.tile * kMaxRankTiles + q.grp;
         if (arrived_last(counter, p.split_k, &flag)) {
             const float scale = c.scales ? c.scales[q.a] : 1.0f;
             const int cend = col0 + 16 * RT < ra ? col0 + 16 * RT : ra;
             const int czero = cend == ra ? p.r_max : cend;
-            combine_tile(p, q.row0, q.nrows, col0, cend, czero, scale, c.h, c.ld_h);
+            combine_tile(p, q.row0, q.nrows, q.mask, col0, cend, czero, scale, c.h, c.ld_h);
             if (threadIdx.x == 0)
                 __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -578,40 +596,46 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_counted_multi(ShrinkP
         const int c1 = c0 + T < ntiles ? c0 + T : ntiles;
         int j = c0;
         while (j < c1) {                          // uniform: plan data only
-            const int32_t* t = plan + 3 * j;
+            const int32_t* t = plan + kPlanTileInts * j;
             if (!tile_rows_ok(t, p.M)) {
                 ++j;
                 continue;
             }
             if (t[2] < 0 || t[2] >= p.n_adapters) {
-                if (s == 0)
+                if (s == 0) {
+                    const uint32_t m = tile_mask(t);
                     for (int e = threadIdx.x; e < t[1] * p.r_max; e += blockDim.x)
-                        c.h[(t[0] + e / p.r_max) * c.ld_h + e % p.r_max] = 0.0f;
+                        if (row_in(m, e / p.r_max))
+                            c.h[(t[0] + e / p.r_max) * c.ld_h + e % p.r_max] = 0.0f;
+                }
                 ++j;
                 continue;
             }
             const int a = t[2];
             int64_t row0[T];
             int nrows[T];
+            uint32_t mask[T];
             int n = 0;
 #pragma unroll
             for (int u = 0; u < T; ++u) {
-                const int32_t* tu = plan + 3 * (j + u);
+                const int32_t* tu = plan + kPlanTileInts * (j + u);
                 const bool take = n == u && j + u < c1 && tile_ok(tu, p.M, p.n_adapters) && tu[2] == a;
                 row0[u] = take ? tu[0] : t[0];
                 nrows[u] = take ? tu[1] : 0;
+                mask[u] = take ? tile_mask(tu) : 0u;
                 n += take ? 1 : 0;
             }
             const int ra = adapter_rank(p, a);
             if (ra > 0) {
-                shrink_tiles<RT, W, kToWorkspaceCoherent, T>(p, row0, nrows, p.A_ptrs[a], ra, 0, s, 1.0f, red);
+                shrink_tiles<RT, W, kToWorkspaceCoherent, T>(p, row0, nrows, mask, p.A_ptrs[a], ra, 0, s, 1.0f,
+                                                             red);
 #pragma unroll
                 for (int u = 0; u < T; ++u) {
                     if (u < n) {                  // uniform
                         int32_t* counter = c.counters + (int64_t)(j + u) * kMaxRankTiles;
                         if (arrived_last(counter, p.split_k, &flag)) {
                             const float scale = c.scales ? c.scales[a] : 1.0f;
-                            combine_tile(p, row0[u], nrows[u], 0, ra, p.r_max, scale, c.h, c.ld_h);
+                            combine_tile(p, row0[u], nrows[u], mask[u], 0, ra, p.r_max, scale, c.h, c.ld_h);
                             if (threadIdx.x == 0)
                                 __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                         }

@@ -42,8 +42,8 @@ __device__ __forceinline__ void shrink_store(const ShrinkParams& p, int64_t row0
 }
 
 template <int RT, int W, int MODE>
-__device__ __forceinline__ void wave_tree_store(const ShrinkParams& p, int64_t row0, int nrows, int rg, int col0,
-                                                int s, float scale, float* red, const f32x4 (&acc)[RT]);
+__device__ __forceinline__ void wave_tree_store(const ShrinkParams& p, int64_t row0, int nrows, uint32_t mask, int rg,
+                                                int col0, int s, float scale, float* red, const f32x4 (&acc)[RT]);
 
 // The matrix-core chains of one wave: T row tiles (x row pointers xp[u]) times
 // NRT rank tiles (A row pointers ap[rt]), `steps` steps of 32 k from the
@@ -138,16 +138,18 @@ __device__ __forceinline__ void mfma_dispatch(int nrt, const uint16_t* const (&x
     }
 }
 
-// T row tiles (row0[u], nrows[u]; a tile with nrows 0 is skipped) that share
-// one adapter, split s and rank columns col0 .. col0 + 16 RT - 1 (those below
-// r): every (tile, rank tile) accumulator gets its chain over the wave's k
-// range, the A loads shared by the T tiles, then the wave tree and the store.
-// Per element the arithmetic depends only on (K, split_k): the tiles a
-// workgroup holds and the rank tiles grouped with it change no bit.
+// T row tiles (rows row0[u] + i for i < nrows[u] with bit i of mask[u] set;
+// a tile with nrows 0 is skipped) that share one adapter, split s and rank
+// columns col0 .. col0 + 16 RT - 1 (those below r): every (tile, rank tile)
+// accumulator gets its chain over the wave's k range, the A loads shared by
+// the T tiles, then the wave tree and the store of the tile's rows.  Per
+// element the arithmetic depends only on (K, split_k): the tiles a workgroup
+// holds, the rank tiles grouped with it and the other rows of its tile change
+// no bit.
 template <int RT, int W, int MODE, int T>
 __device__ __forceinline__ void shrink_tiles(const ShrinkParams& p, const int64_t (&row0)[T], const int (&nrows)[T],
-                                             const uint16_t* __restrict__ A, int r, int col0, int s, float scale,
-                                             float* red)
+                                             const uint32_t (&mask)[T], const uint16_t* __restrict__ A, int r,
+                                             int col0, int s, float scale, float* red)
 {
     constexpr int G = T == 1 ? 4 : 2;
     const int wave = threadIdx.x >> 6;
@@ -164,8 +166,8 @@ __device__ __forceinline__ void shrink_tiles(const ShrinkParams& p, const int64_
     bool full = true;                        // every tile has 16 rows (uniform)
 #pragma unroll
     for (int u = 0; u < T; ++u) {
-        x_ok[u] = li < nrows[u];
-        full = full && (nrows[u] == kRowBlock || nrows[u] == 0);
+        x_ok[u] = li < nrows[u] && row_in(mask[u], li);
+        full = full && ((nrows[u] == kRowBlock && mask[u] == kFullMask) || nrows[u] == 0);
         xp[u] = p.x + (row0[u] + (x_ok[u] ? li : 0)) * p.ld_x + kbase;
     }
     const uint16_t* ap[RT];
@@ -194,27 +196,28 @@ __device__ __forceinline__ void shrink_tiles(const ShrinkParams& p, const int64_
 #pragma unroll
     for (int u = 0; u < T; ++u)
         if (nrows[u] > 0)                         // uniform across the workgroup
-            wave_tree_store<RT, W, MODE>(p, row0[u], nrows[u], rg, col0, s, scale, red, acc[u]);
+            wave_tree_store<RT, W, MODE>(p, row0[u], nrows[u], mask[u], rg, col0, s, scale, red, acc[u]);
 }
 
-// One work item: rows row0 .. row0+nrows-1, split s, rank columns col0 ..
-// col0 + 16 RT - 1 (those below r).  A is the adapter's row 0.
+// One work item: rows row0 .. row0+nrows-1 (those in mask), split s, rank
+// columns col0 .. col0 + 16 RT - 1 (those below r).  A is the adapter's row 0.
 template <int RT, int W, int MODE>
-__device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0, int nrows,
+__device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0, int nrows, uint32_t mask,
                                             const uint16_t* __restrict__ A, int r, int col0, int s, float scale,
                                             float* red)
 {
     const int64_t rows[1] = {row0};
     const int n[1] = {nrows};
-    shrink_tiles<RT, W, MODE, 1>(p, rows, n, A, r, col0, s, scale, red);
+    const uint32_t m[1] = {mask};
+    shrink_tiles<RT, W, MODE, 1>(p, rows, n, m, A, r, col0, s, scale, red);
 }
 
 // acc[rt][v] is the wave's sum for token row 4g+v, rank column col0 + 16 rt + li:
 // with W waves, the W wave sums meet in LDS and are added along the fixed
 // pairwise tree; then the split's partial is stored.
 template <int RT, int W, int MODE>
-__device__ __forceinline__ void wave_tree_store(const ShrinkParams& p, int64_t row0, int nrows, int rg, int col0,
-                                                int s, float scale, float* red, const f32x4 (&acc)[RT])
+__device__ __forceinline__ void wave_tree_store(const ShrinkParams& p, int64_t row0, int nrows, uint32_t mask, int rg,
+                                                int col0, int s, float scale, float* red, const f32x4 (&acc)[RT])
 {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -226,7 +229,7 @@ __device__ __forceinline__ void wave_tree_store(const ShrinkParams& p, int64_t r
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int row = 4 * g + v, col = rt * 16 + li;
-                if (row < nrows && col < rg)
+                if (row < nrows && row_in(mask, row) && col < rg)
                     shrink_store<MODE>(p, row0, s, row, col0 + col, acc[rt][v], scale);
             }
     } else {
@@ -241,7 +244,7 @@ __device__ __forceinline__ void wave_tree_store(const ShrinkParams& p, int64_t r
         for (int e = threadIdx.x; e < 16 * 16 * RT; e += W * kWave) {
             const int row = e / (16 * RT);
             const int col = e - row * (16 * RT);
-            if (row < nrows && col < ncols) {
+            if (row < nrows && row_in(mask, row) && col < ncols) {
                 float v[W];
 #pragma unroll
                 for (int w = 0; w < W; ++w)

@@ -78,7 +78,7 @@ __global__ __launch_bounds__(W * 64) void k_shrink_expand_counted(ShrinkParams p
     if (j < (uint32_t)q.producers) {
         const int s = (int)(j % (uint32_t)p.split_k);
         const int grp = (int)(j / (uint32_t)p.split_k);
-        shrink_tile<RT, W, kToWorkspaceCoherent>(p, row0, nrows, p.A, p.r, grp * 16 * RT, s, 1.0f, lds);
+        shrink_tile<RT, W, kToWorkspaceCoherent>(p, row0, nrows, kFullMask, p.A, p.r, grp * 16 * RT, s, 1.0f, lds);
         __syncthreads();                      // every partial store of the workgroup ...
         if (threadIdx.x == 0)                 // ... happens before this release
             __hip_atomic_fetch_add(arrivals, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);

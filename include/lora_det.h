@@ -80,7 +80,7 @@
 extern "C" {
 #endif
 
-#define LORA_DET_ABI_VERSION 4
+#define LORA_DET_ABI_VERSION 5
 
 enum lora_status {
     LORA_OK = 0,
@@ -360,16 +360,20 @@ int lora_shrink_expand_counted(const uint16_t* x, int64_t ld_x, const uint16_t* 
  * single-adapter call with that token's adapter.
  * ------------------------------------------------------------------------- */
 
-/* Bytes of the plan buffer for M tokens: 16 + 12 * M. */
+/* Bytes of the plan buffer for M tokens: 16 + 16 * M. */
 size_t lora_sgmv_plan_bytes(int64_t M);
 
 /*
  * Builds the work list from the per-token ids, on the device and without a
- * host synchronisation: tokens are grouped into runs of equal id, each run is
- * cut into tiles of at most 16 consecutive tokens (tiles of tokens without a
- * valid adapter are kept, marked -1).  One launch of one workgroup.  The plan buffer (16-byte aligned) is
- * opaque; it stays valid for later sgmv calls with the same ids, M and
- * n_adapters and may be reused by both sgmv_shrink and sgmv_expand.
+ * host synchronisation: tiles of up to 16 tokens with one adapter, either
+ * runs of equal id cut into pieces of at most 16 consecutive tokens, or (up
+ * to 4096 tokens, where the runs give at least two tiles per 16-token block
+ * and this gives fewer, e.g. for interleaved ids) one tile per distinct id of
+ * each aligned 16-token block, masked to its tokens.
+ * Tokens without a valid adapter get tiles marked -1.  The tiling changes no
+ * output bit.  One launch of one workgroup.  The plan buffer (16-byte
+ * aligned) is opaque; it stays valid for later sgmv calls with the same ids,
+ * M and n_adapters and may be reused by both sgmv_shrink and sgmv_expand.
  */
 int lora_sgmv_plan(const int32_t* token_adapter, int64_t M, int32_t n_adapters,
                    void* plan, size_t plan_bytes, void* stream);

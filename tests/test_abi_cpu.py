@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert dsl.lora_abi_version() == 4
+    assert dsl.lora_abi_version() == 5
     seen = set()
     for s in range(0, 8):
         t = dsl.lora_status_str(s)
@@ -85,7 +85,7 @@ def test_workspace_and_plan_sizes():
     assert dsl.lora_shrink_workspace_bytes(256, 16, 3) == 0
     assert dsl.lora_sgmv_workspace_bytes(512, 64, 8) == 8 * 512 * 64 * 4
     assert dsl.lora_sgmv_workspace_bytes(512, 64, 1) == 512 * 64 * 4
-    assert dsl.lora_sgmv_plan_bytes(512) == 16 + 12 * 512
+    assert dsl.lora_sgmv_plan_bytes(512) == 16 + 16 * 512
     assert dsl.lora_sgmv_plan_bytes(-3) == 0
 
 

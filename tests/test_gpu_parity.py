@@ -460,6 +460,11 @@ def test_atomic_variant_varies_on_crafted_input(record_property):
 # multi-adapter
 # ---------------------------------------------------------------------------
 def _plan_reference(ids, n):
+    """The plan's tiles (first row, row span, adapter, row mask): runs of equal
+    id cut into pieces of 16 in token order, or - up to 4096 tokens, where the
+    runs make at least two tiles per 16-token block and the blocks strictly
+    fewer - one tile per distinct id of each aligned block, ordered by adapter
+    (-1 first) and then block."""
     tiles = []
     M = len(ids)
     i = 0
@@ -469,8 +474,22 @@ def _plan_reference(ids, n):
         while j < M and norm[j] == norm[i]:
             j += 1
         for s in range(i, j, 16):
-            tiles.append((s, min(16, j - s), norm[i]))
+            c = min(16, j - s)
+            tiles.append((s, c, norm[i], (1 << c) - 1))
         i = j
+    if M <= 4096 and n < 2 ** 22 and len(tiles) >= 2 * ((M + 15) // 16):
+        pairs = []
+        for b in range((M + 15) // 16):
+            r0, c = 16 * b, min(16, M - 16 * b)
+            seen = []
+            for q in range(c):
+                if norm[r0 + q] not in seen:
+                    seen.append(norm[r0 + q])
+            for a in seen:
+                mask = sum(1 << q for q in range(c) if norm[r0 + q] == a)
+                pairs.append((a, b, (r0, c, a, mask)))
+        if len(pairs) < len(tiles):
+            return [e[2] for e in sorted(pairs, key=lambda e: (e[0], e[1]))]
     return tiles
 
 
@@ -484,7 +503,8 @@ def _build_plan(ids, n):
 
 
 @pytest.mark.parametrize("case", ["segments", "singletons", "invalid", "long", "one_adapter", "large",
-                                  "runs_across_passes", "pass_edges", "one_run_8193"])
+                                  "runs_across_passes", "pass_edges", "one_run_8193", "interleaved",
+                                  "interleaved_4096", "interleaved_4097", "one_per_token_tie", "ragged_blocks"])
 def test_sgmv_plan_tiles(case):
     rng = np.random.default_rng(zlib.crc32(case.encode()))
     if case == "segments":
@@ -506,6 +526,16 @@ def test_sgmv_plan_tiles(case):
         ids, n = ids % 3, 3
     elif case == "one_run_8193":
         ids, n = np.full(8193, 2, np.int32), 3
+    elif case == "interleaved":            # decode tokens of many requests over 4 adapters: block tiles
+        ids, n = (np.arange(512) % 4).astype(np.int32), 4
+    elif case == "interleaved_4096":       # the largest batch the block tiling considers
+        ids, n = rng.integers(-1, 9, 4096).astype(np.int32), 8
+    elif case == "interleaved_4097":       # one token more: runs only
+        ids, n = rng.integers(-1, 9, 4097).astype(np.int32), 8
+    elif case == "one_per_token_tie":      # as many block pairs as runs: runs
+        ids, n = np.arange(40, dtype=np.int32), 40
+    elif case == "ragged_blocks":          # a partial last block, ids outside the range
+        ids, n = rng.choice([-3, 0, 1, 5, 9], 999).astype(np.int32), 6
     else:
         ids, n = rng.integers(0, 2, 20000).astype(np.int32), 2
     _say(f"plan {case}: M={len(ids)}")
@@ -514,7 +544,7 @@ def test_sgmv_plan_tiles(case):
     raw = plan.cpu().numpy().view(np.int32)
     ref = _plan_reference(ids.tolist(), n)
     assert raw[0] == len(ref) and raw[1] == len(ids) and raw[2] == n
-    got = [tuple(raw[4 + 3 * k: 7 + 3 * k]) for k in range(raw[0])]
+    got = [tuple(int(v) for v in raw[4 + 4 * k: 8 + 4 * k]) for k in range(raw[0])]
     assert got == ref
 
 
@@ -703,6 +733,67 @@ def test_sgmv_equals_single_adapter_bitwise():
         t.cuda.synchronize()
         assert np.array_equal(f32_bits(hs), f32_bits_np(h[:, :r]))
         assert np.array_equal(bf16_from_gpu(ys), y)
+
+
+@pytest.mark.parametrize("case", ["cycling", "random_invalid", "stream", "counted_multi"])
+def test_sgmv_block_tiles_bitwise(case):
+    """Interleaved ids, for which the plan makes one masked tile per adapter
+    and 16-token block: every token's h and y bits equal those of the
+    single-adapter shrink and expand run on that adapter's tokens alone (the
+    tiling changes no bit), tokens without an adapter get zero h and keep y,
+    the pipeline and the single-launch shrink agree bit for bit, and the
+    atomic contrast stays within its rounding bound."""
+    t = torch()
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
+    if case == "cycling":                  # decode-like: every block holds all four adapters
+        c = sgmv_case(512, 4096, 1024, [16, 64, 32, 8], 0, 0, 8, seed=41, tag="bt_c",
+                      ids=(np.arange(512) % 4).astype(np.int32))
+    elif case == "random_invalid":         # partial last block, ids outside the range, rank 128
+        c = sgmv_case(300, 2048, 520, [5, 16, 37, 64, 128], 0, 0, 16, seed=42, tag="bt_r",
+                      ids=rng.choice([-2, 0, 1, 2, 3, 4, 7], 300).astype(np.int32))
+    elif case == "stream":                 # many tiles: the A-in-registers partial kernel
+        c = sgmv_case(4096, 1024, 264, [8, 16, 32, 64] * 2, 0, 0, 4, seed=43, tag="bt_s",
+                      ids=rng.integers(-1, 8, 4096).astype(np.int32))
+    else:                                  # large items of the single-launch multi-adapter shrink
+        c = sgmv_case(2048, 4096, 264, [16, 64, 32, 8], 0, 0, 8, seed=44, tag="bt_m",
+                      ids=rng.integers(0, 4, 2048).astype(np.int32))
+    n = len(c.ranks)
+    _say(f"sgmv block tiles {case}: M={c.M} K={c.K} n={n} S={c.split_k}")
+    ref = _plan_reference(c.ids.tolist(), n)
+    assert any(tl[3] != (1 << tl[1]) - 1 for tl in ref), "the case must take the block tiling"
+    _, plan = _build_plan(c.ids, n)
+    raw = plan.cpu().numpy().view(np.int32)
+    assert [tuple(int(v) for v in raw[4 + 4 * k: 8 + 4 * k]) for k in range(raw[0])] == ref
+    h, y, gpu = _sgmv_gpu(c)
+    _sgmv_other_schedules(c, h, y, gpu)
+    As, Bs = gpu
+    for a in range(n):
+        rows = np.nonzero(c.ids == a)[0]
+        if len(rows) == 0:
+            continue
+        r, S = int(c.ranks[a]), c.split_k
+        xs = bf16_to_gpu(c.x[rows])
+        # rows padded to a multiple of 4 floats: the expand reads h with 16-byte loads
+        hs = t.empty((len(rows), (r + 3) // 4 * 4), dtype=t.float32, device="cuda")[:, :r]
+        dsl.lora_shrink_splitk(xs, As[a], hs, workspace(dsl.lora_shrink_workspace_bytes(len(rows), r, S)), S,
+                               float(c.scales[a]))
+        ys = bf16_to_gpu(c.y[rows])
+        dsl.lora_expand(hs, Bs[a], ys, float(c.scales[a]), r=r)
+        t.cuda.synchronize()
+        assert np.array_equal(f32_bits(hs), f32_bits_np(h[rows, :r])), f"{case}: h of adapter {a}"
+        assert np.array_equal(bf16_from_gpu(ys), y[rows]), f"{case}: y of adapter {a}"
+    none = np.nonzero((c.ids < 0) | (c.ids >= n))[0]
+    assert np.all(h[none] == 0.0) and np.array_equal(y[none], c.y[none])
+    ha = _sgmv_atomic(c)
+    for i in sorted(rng.choice(c.M, 24, replace=False).tolist()):
+        a = int(c.ids[i])
+        if a < 0 or a >= n:
+            assert np.all(ha[i] == 0.0)
+            continue
+        r = int(c.ranks[a])
+        check_shrink(ha[i:i + 1, :r], c.x[i:i + 1], c.As[a], float(c.scales[a]),
+                     dsl.lora_shrink_plan(c.K, r, c.split_k), f"{case} atomic row {i}", atomic=True)
+    _check_sgmv(c, h, y, sorted(rng.choice(c.M, 12, replace=False).tolist()), f"block tiles {case}")
 
 
 def test_sgmv_permuting_segments_keeps_token_bits():
