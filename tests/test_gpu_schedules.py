@@ -235,3 +235,88 @@ def test_sgmv_batch_invariance_every_row_block_count(label, K, N, ranks, S, seg,
                      f"{label} probe {j} h")
         yo, e, ab = oracle.expand(hh[j:j + 1, :r], Bs[a], ybase[j:j + 1], float(ex_np[a]))
         check_expand(yy[j:j + 1], yo, e, ab, ybase[j:j + 1], f"{label} probe {j} y", r=r)
+
+
+@pytest.mark.parametrize("multi", [False, True])
+def test_offsets_beyond_32_bits(multi):
+    """Batches whose x holds more than 2^31 elements (524 293 tokens x 4096):
+    every element offset past 2^31 must be formed in 64 bits.  Probe rows
+    placed at the start, the middle and the last rows (past 2^31 / K) of the
+    batch give the h and y bits of the probe rows computed alone, through the
+    fused entry point and the separate calls (single adapter), or through the
+    multi-adapter pipeline (two adapters in alternating segments of 4096
+    tokens); the probe rows computed alone are checked against the oracle."""
+    t = torch()
+    M, K, r, N, S = (1 << 19) + 5, 4096, 16, 1024, 8
+    assert M * K > 2 ** 31
+    probe = normal_bf16((P, K), 1.0, 7, "big_x")
+    ybase = normal_bf16((P, N), 1.0, 7, "big_y")
+    n = 2 if multi else 1
+    As = [normal_bf16((r, K), 0.02, 7 + a, "big_A") for a in range(n)]
+    Bs = [normal_bf16((N, r), 0.02, 7 + a, "big_B") for a in range(n)]
+    Ag, Bg = [bf16_to_gpu(a) for a in As], [bf16_to_gpu(b) for b in Bs]
+    xp, yp = bf16_to_gpu(probe), bf16_to_gpu(ybase)
+    pos = np.array([0, 1, 2, 3, 4095, 4096, 262144, 262145, M // 2, M - 9, M - 8, M - 5, M - 4, M - 3, M - 2,
+                    M - 1], dtype=np.int64)
+    ids_np = ((np.arange(M) // 4096) % n).astype(np.int32)
+    pid = ids_np[pos]
+    _say(f"offsets past 2^31: M={M} K={K} multi={multi}")
+    # the probe rows alone
+    h0 = t.zeros((P, r), dtype=t.float32, device="cuda")
+    y0 = yp.clone()
+    for a in range(n):
+        sel = np.nonzero(pid == a)[0]
+        if len(sel) == 0:
+            continue
+        sg = t.from_numpy(sel).cuda()
+        ha = t.empty((len(sel), r), dtype=t.float32, device="cuda")
+        dsl.lora_shrink_splitk(xp[sg].contiguous(), Ag[a], ha,
+                               t.empty(dsl.lora_shrink_workspace_bytes(len(sel), r, S), dtype=t.uint8,
+                                       device="cuda"), S, 1.0)
+        ya = yp[sg].contiguous()
+        dsl.lora_expand(ha, Bg[a], ya, 2.0)
+        h0[sg] = ha
+        y0[sg] = ya
+    ref_h, ref_y = h0.view(t.int32).clone(), y0.view(t.int16).clone()
+
+    gen = t.Generator(device="cuda")
+    gen.manual_seed(11)
+    x = _filler(gen, M, K)
+    y = _filler(gen, M, N)
+    pg = t.from_numpy(pos).cuda()
+    x[pg] = xp
+    h = t.empty((M, r), dtype=t.float32, device="cuda")
+    if multi:
+        Ap = t.tensor([a.data_ptr() for a in Ag], dtype=t.int64, device="cuda")
+        Bp = t.tensor([b.data_ptr() for b in Bg], dtype=t.int64, device="cuda")
+        rk = t.full((n,), r, dtype=t.int32, device="cuda")
+        ids = t.from_numpy(ids_np).cuda()
+        plan = t.zeros(dsl.lora_sgmv_plan_bytes(M), dtype=t.uint8, device="cuda")
+        dsl.lora_sgmv_plan(ids, n, plan)
+        ws = t.empty(dsl.lora_sgmv_workspace_bytes(M, r, S), dtype=t.uint8, device="cuda")
+        y[pg] = yp
+        dsl.lora_sgmv_shrink_expand(x, Ap, K, Bp, rk, None, t.full((n,), 2.0, device="cuda"), ids, n, plan, y, r,
+                                    S, ws, h=h)
+        t.cuda.synchronize()
+        assert t.equal(h[pg].view(t.int32), ref_h) and t.equal(y[pg].view(t.int16), ref_y), "pipeline"
+    else:
+        ws = t.empty(max(dsl.lora_shrink_expand_workspace_bytes(M, r, S), dsl.lora_shrink_workspace_bytes(M, r, S)),
+                     dtype=t.uint8, device="cuda")
+        y[pg] = yp
+        dsl.lora_shrink_expand(x, Ag[0], Bg[0], y, ws, S, 1.0, 2.0, h=h)
+        t.cuda.synchronize()
+        assert t.equal(h[pg].view(t.int32), ref_h) and t.equal(y[pg].view(t.int16), ref_y), "shrink_expand"
+        y[pg] = yp
+        dsl.lora_shrink_splitk(x, Ag[0], h, ws, S, 1.0)
+        dsl.lora_expand(h, Bg[0], y, 2.0)
+        t.cuda.synchronize()
+        assert t.equal(h[pg].view(t.int32), ref_h) and t.equal(y[pg].view(t.int16), ref_y), "separate calls"
+    del x, y, h, ws
+    t.cuda.empty_cache()
+    h_ref = ref_h.cpu().numpy().view(np.float32)
+    y_ref = bf16_from_gpu(y0)
+    for a in range(n):
+        sel = np.nonzero(pid == a)[0]
+        check_shrink(h_ref[sel], probe[sel], As[a], 1.0, dsl.lora_shrink_plan(K, r, S), f"big probe h a={a}")
+        yo, e, ab = oracle.expand(h_ref[sel], Bs[a], ybase[sel], 2.0)
+        check_expand(y_ref[sel], yo, e, ab, ybase[sel], f"big probe y a={a}", r=r)
