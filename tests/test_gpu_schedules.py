@@ -239,16 +239,17 @@ def test_sgmv_batch_invariance_every_row_block_count(label, K, N, ranks, S, seg,
 
 @pytest.mark.parametrize("multi", [False, True])
 def test_offsets_beyond_32_bits(multi):
-    """Batches whose x holds more than 2^31 elements (524 293 tokens x 4096):
-    every element offset past 2^31 must be formed in 64 bits.  Probe rows
+    """Batches whose x and y each hold more than 2^31 elements (524 293 tokens
+    x 4096 in, x 4104 out): every element offset past 2^31 must be formed in
+    64 bits.  Probe rows
     placed at the start, the middle and the last rows (past 2^31 / K) of the
     batch give the h and y bits of the probe rows computed alone, through the
     fused entry point and the separate calls (single adapter), or through the
     multi-adapter pipeline (two adapters in alternating segments of 4096
     tokens); the probe rows computed alone are checked against the oracle."""
     t = torch()
-    M, K, r, N, S = (1 << 19) + 5, 4096, 16, 1024, 8
-    assert M * K > 2 ** 31
+    M, K, r, N, S = (1 << 19) + 5, 4096, 16, 4104, 8
+    assert M * K > 2 ** 31 and M * N > 2 ** 31
     probe = normal_bf16((P, K), 1.0, 7, "big_x")
     ybase = normal_bf16((P, N), 1.0, 7, "big_y")
     n = 2 if multi else 1
