@@ -986,22 +986,25 @@ def test_graph_capture_replays_match_eager():
         del junk
 
 
-@pytest.mark.parametrize("M", [300, 2100])
-def test_sgmv_graph_replays(M):
+@pytest.mark.parametrize("M,interleaved", [(300, False), (2100, False), (700, True)])
+def test_sgmv_graph_replays(M, interleaved):
     """The multi-adapter path captured in a HIP graph - the device-side plan,
     the shrink + expand pipeline and the single-launch shrink (whose kernel
     puts its counters back to zero) - replayed several times with eager work
     and synchronisations in between: every replay gives the eager bits.  At
     M = 2100 the shrink walks several plan tiles per workgroup with A held in
-    registers."""
+    registers; with interleaved ids the plan takes the block tiling (its sort
+    included in the graph)."""
     t = torch()
     rng = np.random.default_rng(M)
     ids = np.empty(M, np.int32)
     pos = 0
     while pos < M:
-        run = int(rng.integers(1, 200))
+        run = 1 if interleaved else int(rng.integers(1, 200))
         ids[pos:pos + run] = rng.choice([-1, 0, 1, 2, 3])
         pos += run
+    if interleaved:
+        assert any(tl[3] != (1 << tl[1]) - 1 for tl in _plan_reference(ids.tolist(), 4))
     c = sgmv_case(M, 1024, 1032, [16, 64, 8, 32], 0, 0, 8, seed=M, tag=f"gr{M}", ids=ids)
     n = len(c.ranks)
     As = [bf16_to_gpu(a) for a in c.As]
