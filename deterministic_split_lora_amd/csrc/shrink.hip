@@ -326,20 +326,16 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
     const uint32_t S = (uint32_t)p.split_k;
     const uint32_t items = (uint32_t)((ntiles + R - 1) / R) * S;
     // tile j (the item's u-th): first row, row span (0: nothing to compute),
-    // adapter and row mask; plan entries come from LDS, so reading them never
-    // waits for the x loads in flight
+    // adapter and row mask; plan entries come from LDS, checked once when the
+    // item's entries are staged, so reading them never waits for the x loads
+    // in flight and costs no scalar work per block
     auto tile = [&](int64_t j, int u, int64_t& row0, int& nrows, int& a, uint32_t& msk) {
         if constexpr (SGMV) {
             // uniform by construction: scalar registers
-            const int32_t t[kPlanTileInts] = {__builtin_amdgcn_readfirstlane(tl[kPlanTileInts * u]),
-                                              __builtin_amdgcn_readfirstlane(tl[kPlanTileInts * u + 1]),
-                                              __builtin_amdgcn_readfirstlane(tl[kPlanTileInts * u + 2]),
-                                              __builtin_amdgcn_readfirstlane(tl[kPlanTileInts * u + 3])};
-            const bool ok = tile_ok(t, p.M, p.n_adapters);
-            row0 = ok ? t[0] : 0;
-            nrows = ok ? t[1] : 0;
-            a = ok ? t[2] : -1;
-            msk = ok ? tile_mask(t) : 0u;
+            row0 = __builtin_amdgcn_readfirstlane(tl[kPlanTileInts * u]);
+            nrows = __builtin_amdgcn_readfirstlane(tl[kPlanTileInts * u + 1]);
+            a = __builtin_amdgcn_readfirstlane(tl[kPlanTileInts * u + 2]);
+            msk = (uint32_t)__builtin_amdgcn_readfirstlane(tl[kPlanTileInts * u + 3]);
         } else {
             row0 = j * kRowBlock;
             nrows = p.M - row0 < kRowBlock ? (int)(p.M - row0) : kRowBlock;
@@ -377,8 +373,16 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
         const int cnt = ntiles - c0 < R ? (int)(ntiles - c0) : R;
         if constexpr (SGMV) {
             __syncthreads();                      // the previous item's entries are no longer read
-            if ((int)threadIdx.x < kPlanTileInts * cnt)
-                tl[threadIdx.x] = plan[kPlanTileInts * c0 + threadIdx.x];
+            if ((int)threadIdx.x < cnt) {         // one tile per thread, checked and normalised
+                const int32_t* src = plan + kPlanTileInts * (c0 + threadIdx.x);
+                const int32_t t[kPlanTileInts] = {src[0], src[1], src[2], src[3]};
+                const bool ok = tile_ok(t, p.M, p.n_adapters);
+                int32_t* d = tl + kPlanTileInts * threadIdx.x;
+                d[0] = ok ? t[0] : 0;
+                d[1] = ok ? t[1] : 0;
+                d[2] = ok ? t[2] : -1;
+                d[3] = ok ? (int32_t)tile_mask(t) : 0;
+            }
             __syncthreads();
         }
         // reduction slots 8g..8g+7 of step t hold k = kbase + 32 t + (0..7)
