@@ -387,7 +387,7 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
         }
         // reduction slots 8g..8g+7 of step t hold k = kbase + 32 t + (0..7)
         const int64_t kbase = (int64_t)s * p.k_chunk + (int64_t)wave * STEPS * kKStep + g * 8;
-        auto xload = [&](int u, bf16x8 (&dst)[STEPS]) {
+        auto xload = [&](int u, u32x4 (&dst)[STEPS]) {
             int64_t row0;
             int nrows, a;
             uint32_t msk;
@@ -395,9 +395,11 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
             const uint16_t* xp = p.x + (row0 + (li < nrows ? li : 0)) * p.ld_x + kbase;
 #pragma unroll
             for (int t = 0; t < STEPS; ++t)
-                dst[t] = load_bf16x8(xp + t * kKStep);
+                dst[t] = *(const global_u32x4*)(xp + t * kKStep);
         };
-        bf16x8 xb[NB][STEPS];
+        // x operands held as raw 32-bit words until the matrix-core step: moves
+        // of 8 x bf16 vectors between registers compiled to per-half shuffles
+        u32x4 xb[NB][STEPS];
         bf16x8 aop[STEPS][RT];
         // runs of blocks with one adapter: the run's first two x blocks and
         // its A chunk are loaded at the start of the run and waited for there,
@@ -453,7 +455,7 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
             // that every buffer is known to have landed once its block is
             // done and its registers can be reused without draining the
             // loads in flight.
-            auto block = [&](const bf16x8 (&xc)[STEPS], bf16x8 (&xn)[STEPS], float (&kept)[EPT]) {
+            auto block = [&](const u32x4 (&xc)[STEPS], u32x4 (&xn)[STEPS], float (&kept)[EPT]) {
                 xload(u + NB - 1 < u1 ? u + NB - 1 : u1 - 1, xn);   // unconditional: no branch-dependent buffer
                 tile(c0 + u, u, row0, nrows, a, msk);
                 const bool on = nrows > 0 && ra > 0;
@@ -464,7 +466,7 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
                     acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int t = 0; t < STEPS; ++t)
-                        acc[rt] = mfma_16x16x32(xc[t], aop[t][rt], acc[rt]);
+                        acc[rt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, xc[t]), aop[t][rt], acc[rt]);
                 }
                 if (on) {
 #pragma unroll
