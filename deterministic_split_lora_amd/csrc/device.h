@@ -180,9 +180,17 @@ __device__ __forceinline__ void expand_load_y(const ExpandLane& L, const uint16_
 }
 
 // This lane's B operand rows (KS steps of 32 over r; zeros past r and N).
-template <int KS>
-__device__ __forceinline__ void expand_load_b(const ExpandLane& L, int64_t N, const uint16_t* __restrict__ B,
-                                              int64_t ld_b, int r, bf16x8 (&bop)[4][KS])
+// Rows of B hold ld_b >= r elements with ld_b a multiple of 8 (checked by
+// every entry point), so the 8 elements from any j0 < r (j0 a multiple of 8)
+// lie inside the row: each operand is one full 16-byte load, and only for a
+// rank that is not a multiple of 8 are the elements from r on cleared
+// afterwards (EDGE; the choice is uniform and made once, so the common case
+// is one straight run of loads).  These kernels are latency-bound:
+// per-element partial loads made their code a third longer and the step
+// slower.
+template <int KS, bool EDGE>
+__device__ __forceinline__ void expand_load_b_run(const ExpandLane& L, int64_t N, const uint16_t* __restrict__ B,
+                                                  int64_t ld_b, int r, bf16x8 (&bop)[4][KS])
 {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -191,9 +199,26 @@ __device__ __forceinline__ void expand_load_b(const ExpandLane& L, int64_t N, co
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int j0 = ks * kKStep + 8 * L.g;
-            bop[t][ks] = (n_ok && j0 < r) ? load_bf16x8_partial(B + n * ld_b + j0, r - j0) : bf16x8_zero();
+            u32x4 v = (n_ok && j0 < r) ? *(const global_u32x4*)(B + n * ld_b + j0) : u32x4{0u, 0u, 0u, 0u};
+            if constexpr (EDGE) {
+                const int rem = r - j0;
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    v[d] &= (2 * d < rem ? 0x0000FFFFu : 0u) | (2 * d + 1 < rem ? 0xFFFF0000u : 0u);
+            }
+            bop[t][ks] = __builtin_bit_cast(bf16x8, v);
         }
     }
+}
+
+template <int KS>
+__device__ __forceinline__ void expand_load_b(const ExpandLane& L, int64_t N, const uint16_t* __restrict__ B,
+                                              int64_t ld_b, int r, bf16x8 (&bop)[4][KS])
+{
+    if ((r & 7) == 0)                              // uniform
+        expand_load_b_run<KS, false>(L, N, B, ld_b, r, bop);
+    else
+        expand_load_b_run<KS, true>(L, N, B, ld_b, r, bop);
 }
 
 // Loads this lane's 16 y values and its B operand rows.
