@@ -121,6 +121,19 @@ __device__ __forceinline__ bf16x8 load_h_as_bf16(const float* hp, int j0, int r)
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// The same for j0 + 8 <= r: two 16-byte loads, no per-element checks.
+__device__ __forceinline__ bf16x8 load_h_as_bf16_whole(const float* hp)
+{
+    const float4 a = *reinterpret_cast<const float4*>(hp);
+    const float4 b = *reinterpret_cast<const float4*>(hp + 4);
+    const float f[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    u16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        v[e] = f32_to_bf16_bits(f[e]);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 // ---------------------------------------------------------------------------
 // Expand tile, shared by every kernel that expands (so the per-element
 // arithmetic is literally the same code): a wavefront owns 16 tokens x 64
@@ -282,10 +295,18 @@ __device__ __forceinline__ void expand_finish(const ExpandLane& L, uint16_t* y, 
                                               const u16x8 (&yv)[2], const bf16x8 (&bop)[4][KS])
 {
     bf16x8 hb[KS];
+    if ((r & 7) == 0) {                            // uniform: whole groups of 8 columns
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-        const int j0 = ks * kKStep + 8 * L.g;
-        hb[ks] = (L.row_ok && j0 < r) ? load_h_as_bf16(hrows + L.li * ld_hr + j0, j0, r) : bf16x8_zero();
+        for (int ks = 0; ks < KS; ++ks) {
+            const int j0 = ks * kKStep + 8 * L.g;
+            hb[ks] = (L.row_ok && j0 < r) ? load_h_as_bf16_whole(hrows + L.li * ld_hr + j0) : bf16x8_zero();
+        }
+    } else {
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int j0 = ks * kKStep + 8 * L.g;
+            hb[ks] = (L.row_ok && j0 < r) ? load_h_as_bf16(hrows + L.li * ld_hr + j0, j0, r) : bf16x8_zero();
+        }
     }
     expand_mma_store<KS>(L, y, ld_y, N, hb, scale, yv, bop);
 }
