@@ -120,12 +120,13 @@ __device__ __forceinline__ SingleItem single_item(const ShrinkParams& p, int gro
     return q;
 }
 
-template <int RT, int W, int MODE>
+// KST: the wave chain length when it is 1, 2 or 4 (0: read from p.k_steps).
+template <int RT, int W, int MODE, int KST>
 __global__ __launch_bounds__(W * 64) void k_shrink_partial(ShrinkParams p, int groups)
 {
     __shared__ float red[red_floats<RT, W>()];
     const SingleItem q = single_item(p, groups);
-    shrink_tile<RT, W, MODE>(p, q.row0, q.nrows, kFullMask, p.A, p.r, q.grp * 16 * RT, q.s, p.scale, red);
+    shrink_tile<RT, W, MODE, KST>(p, q.row0, q.nrows, kFullMask, p.A, p.r, q.grp * 16 * RT, q.s, p.scale, red);
 }
 
 // Large M: T consecutive row blocks per workgroup, all rank tiles together,
@@ -227,7 +228,7 @@ __device__ __forceinline__ float sgmv_item_scale(const ShrinkParams& p, int a)
         return 1.0f;
 }
 
-template <int RT, int W, int MODE>
+template <int RT, int W, int MODE, int KST>
 __global__ __launch_bounds__(W * 64) void k_sgmv_shrink_partial(ShrinkParams p)
 {
     __shared__ float red[red_floats<RT, W>()];
@@ -241,8 +242,8 @@ __global__ __launch_bounds__(W * 64) void k_sgmv_shrink_partial(ShrinkParams p)
         const int col0 = q.grp * 16 * RT;
         if (col0 >= ra)
             continue;
-        shrink_tile<RT, W, MODE>(p, q.row0, q.nrows, q.mask, p.A_ptrs[q.a], ra, col0, q.s,
-                                 sgmv_item_scale<MODE>(p, q.a), red);
+        shrink_tile<RT, W, MODE, KST>(p, q.row0, q.nrows, q.mask, p.A_ptrs[q.a], ra, col0, q.s,
+                                      sgmv_item_scale<MODE>(p, q.a), red);
     }
 }
 
@@ -743,7 +744,13 @@ inline dim3 single_grid(const ShrinkParams& p, int groups)
 template <int MODE, int RT, int W>
 void launch_partial_rw(const ShrinkParams& p, int groups, hipStream_t st)
 {
-    hipLaunchKernelGGL((k_shrink_partial<RT, W, MODE>), single_grid(p, groups), dim3(W * 64), 0, st, p, groups);
+    const dim3 g = single_grid(p, groups);
+    switch (p.k_steps) {
+    case 1: hipLaunchKernelGGL((k_shrink_partial<RT, W, MODE, 1>), g, dim3(W * 64), 0, st, p, groups); break;
+    case 2: hipLaunchKernelGGL((k_shrink_partial<RT, W, MODE, 2>), g, dim3(W * 64), 0, st, p, groups); break;
+    case 4: hipLaunchKernelGGL((k_shrink_partial<RT, W, MODE, 4>), g, dim3(W * 64), 0, st, p, groups); break;
+    default: hipLaunchKernelGGL((k_shrink_partial<RT, W, MODE, 0>), g, dim3(W * 64), 0, st, p, groups); break;
+    }
 }
 
 template <int MODE, int RT>
@@ -798,8 +805,12 @@ void launch_sgmv_r(const ShrinkParams& p, const CounterParams& c, int waves, int
     do {                                                                                              \
         if (COUNTED)                                                                                  \
             hipLaunchKernelGGL((k_sgmv_shrink_counted<RT, W_>), g, dim3(W_ * 64), 0, st, p, c);        \
+        else if (p.k_steps == 2)                                                                      \
+            hipLaunchKernelGGL((k_sgmv_shrink_partial<RT, W_, MODE, 2>), g, dim3(W_ * 64), 0, st, p);  \
+        else if (p.k_steps == 4)                                                                      \
+            hipLaunchKernelGGL((k_sgmv_shrink_partial<RT, W_, MODE, 4>), g, dim3(W_ * 64), 0, st, p);  \
         else                                                                                          \
-            hipLaunchKernelGGL((k_sgmv_shrink_partial<RT, W_, MODE>), g, dim3(W_ * 64), 0, st, p);     \
+            hipLaunchKernelGGL((k_sgmv_shrink_partial<RT, W_, MODE, 0>), g, dim3(W_ * 64), 0, st, p);  \
     } while (0)
     switch (waves) {
     case 1: LORA_SGMV_LAUNCH(1); break;

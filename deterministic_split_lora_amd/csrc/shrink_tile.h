@@ -93,11 +93,24 @@ __device__ __forceinline__ void mfma_group(const uint16_t* const (&xp)[T], const
                 acc[u][rt] = mfma_16x16x32(xa[q][u], b[q][rt], acc[u][rt]);
 }
 
-template <int NRT, int RT, int T, int G, bool MASK>
+// KST > 0: the chain length is known at compile time (it must equal
+// `steps`), so only the groups it takes are compiled - the same groups, in the
+// same order, as the run-time path; these latency-bound kernels run faster
+// with less code.
+template <int NRT, int RT, int T, int G, bool MASK, int KST = 0>
 __device__ __forceinline__ void mfma_chains(const uint16_t* const (&xp)[T], const bool (&x_ok)[T],
                                             const uint16_t* const (&ap)[RT], const bool (&a_ok)[RT], int steps,
                                             f32x4 (&acc)[T][RT])
 {
+    if constexpr (KST > 0) {
+        constexpr int full = KST / G * G;
+#pragma unroll
+        for (int t = 0; t < full; t += G)
+            mfma_group<NRT, RT, T, G, MASK>(xp, x_ok, ap, a_ok, t, acc);
+        if constexpr (KST - full > 0)
+            mfma_group<NRT, RT, T, KST - full, MASK>(xp, x_ok, ap, a_ok, full, acc);
+        return;
+    }
     int t = 0;
     for (; t + G <= steps; t += G)
         mfma_group<NRT, RT, T, G, MASK>(xp, x_ok, ap, a_ok, t, acc);
@@ -119,21 +132,21 @@ __device__ __forceinline__ void mfma_chains(const uint16_t* const (&xp)[T], cons
 }
 
 // The chains for nrt (1 .. RT) active rank tiles.
-template <int RT, int T, int G, bool MASK>
+template <int RT, int T, int G, bool MASK, int KST = 0>
 __device__ __forceinline__ void mfma_dispatch(int nrt, const uint16_t* const (&xp)[T], const bool (&x_ok)[T],
                                               const uint16_t* const (&ap)[RT], const bool (&a_ok)[RT], int steps,
                                               f32x4 (&acc)[T][RT])
 {
     if (nrt >= RT)
-        mfma_chains<RT, RT, T, G, MASK>(xp, x_ok, ap, a_ok, steps, acc);
+        mfma_chains<RT, RT, T, G, MASK, KST>(xp, x_ok, ap, a_ok, steps, acc);
     else if constexpr (RT >= 2) {
         if (nrt == 1)
-            mfma_chains<1, RT, T, G, MASK>(xp, x_ok, ap, a_ok, steps, acc);
+            mfma_chains<1, RT, T, G, MASK, KST>(xp, x_ok, ap, a_ok, steps, acc);
         else if constexpr (RT >= 3) {
             if (nrt == 2)
-                mfma_chains<2, RT, T, G, MASK>(xp, x_ok, ap, a_ok, steps, acc);
+                mfma_chains<2, RT, T, G, MASK, KST>(xp, x_ok, ap, a_ok, steps, acc);
             else if constexpr (RT >= 4)
-                mfma_chains<3, RT, T, G, MASK>(xp, x_ok, ap, a_ok, steps, acc);
+                mfma_chains<3, RT, T, G, MASK, KST>(xp, x_ok, ap, a_ok, steps, acc);
         }
     }
 }
@@ -146,7 +159,7 @@ __device__ __forceinline__ void mfma_dispatch(int nrt, const uint16_t* const (&x
 // element the arithmetic depends only on (K, split_k): the tiles a workgroup
 // holds, the rank tiles grouped with it and the other rows of its tile change
 // no bit.
-template <int RT, int W, int MODE, int T>
+template <int RT, int W, int MODE, int T, int KST = 0>
 __device__ __forceinline__ void shrink_tiles(const ShrinkParams& p, const int64_t (&row0)[T], const int (&nrows)[T],
                                              const uint32_t (&mask)[T], const uint16_t* __restrict__ A, int r,
                                              int col0, int s, float scale, float* red)
@@ -156,7 +169,7 @@ __device__ __forceinline__ void shrink_tiles(const ShrinkParams& p, const int64_
     const int lane = threadIdx.x & 63;
     const int li = lane & 15;
     const int g = lane >> 4;
-    const int steps = p.k_steps;
+    const int steps = KST > 0 ? KST : p.k_steps;
     const int rg = r - col0;                 // rank columns left from col0
 
     // Reduction slots 8g..8g+7 of step t hold k = kbase + 32 t + (0..7).
@@ -190,9 +203,9 @@ __device__ __forceinline__ void shrink_tiles(const ShrinkParams& p, const int64_
     // several-tile kernels are register-bound and see full tiles almost only)
     const int nrt = (rg + 15) / 16 < RT ? (rg + 15) / 16 : RT;
     if (T > 1 || (full && rg >= 16 * nrt))
-        mfma_dispatch<RT, T, G, false>(nrt, xp, x_ok, ap, a_ok, steps, acc);
+        mfma_dispatch<RT, T, G, false, KST>(nrt, xp, x_ok, ap, a_ok, steps, acc);
     else if constexpr (T == 1)
-        mfma_dispatch<RT, T, G, true>(nrt, xp, x_ok, ap, a_ok, steps, acc);
+        mfma_dispatch<RT, T, G, true, KST>(nrt, xp, x_ok, ap, a_ok, steps, acc);
 #pragma unroll
     for (int u = 0; u < T; ++u)
         if (nrows[u] > 0)                         // uniform across the workgroup
@@ -201,7 +214,7 @@ __device__ __forceinline__ void shrink_tiles(const ShrinkParams& p, const int64_
 
 // One work item: rows row0 .. row0+nrows-1 (those in mask), split s, rank
 // columns col0 .. col0 + 16 RT - 1 (those below r).  A is the adapter's row 0.
-template <int RT, int W, int MODE>
+template <int RT, int W, int MODE, int KST = 0>
 __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0, int nrows, uint32_t mask,
                                             const uint16_t* __restrict__ A, int r, int col0, int s, float scale,
                                             float* red)
@@ -209,7 +222,7 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0,
     const int64_t rows[1] = {row0};
     const int n[1] = {nrows};
     const uint32_t m[1] = {mask};
-    shrink_tiles<RT, W, MODE, 1>(p, rows, n, m, A, r, col0, s, scale, red);
+    shrink_tiles<RT, W, MODE, 1, KST>(p, rows, n, m, A, r, col0, s, scale, red);
 }
 
 // acc[rt][v] is the wave's sum for token row 4g+v, rank column col0 + 16 rt + li:
