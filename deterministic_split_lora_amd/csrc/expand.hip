@@ -346,6 +346,15 @@ __device__ __forceinline__ bool combine_item(const ExpandParams& p, int cols, Ex
     return true;
 }
 
+// floor(a / r) for 0 <= a < 4096 and 1 <= r <= 128 from the hardware
+// reciprocal of r: with a = q r + m, (a + 1/2) / r lies at least 1/(2r)
+// >= 1/256 from both q and q + 1, and the product's error (a few ulp of a
+// value below 4096, under 1e-3) cannot carry it across either
+__device__ __forceinline__ int div_small(int a, float rcp_r)
+{
+    return (int)(((float)a + 0.5f) * rcp_r);
+}
+
 template <int KS, int S, int WAVES, int XR>
 __global__ __launch_bounds__(WAVES * 64) void k_expand_combine(ExpandParams p, TreeParams c)
 {
@@ -365,9 +374,22 @@ __global__ __launch_bounds__(WAVES * 64) void k_expand_combine(ExpandParams p, T
     if (active)
         expand_load<KS>(L, p.y, p.ld_y, p.N, p.B, p.ld_b, r, yv, bop);
     const bool write_h = c.h != nullptr && q.cb == 0;
-    for (int e = threadIdx.x; e < kRowBlock * r; e += kCols) {
-        const int row = e / r;
-        const int col = e - row * r;
+    // nrows x r tile elements over the workgroup's threads, the passes
+    // unrolled to their compile-time bound so that every pass's workspace
+    // loads are in flight together; (row, col) advance by kCols elements
+    // per pass without a division
+    constexpr int kPasses = (kRowBlock * 32 * KS + kCols - 1) / kCols;
+    const float rcp_r = __builtin_amdgcn_rcpf((float)r);
+    const int drow = div_small(kCols, rcp_r);
+    const int dcol = kCols - drow * r;
+    int row = div_small((int)threadIdx.x, rcp_r);
+    int col = (int)threadIdx.x - row * r;
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass, row += drow, col += dcol) {
+        if (col >= r) {
+            col -= r;
+            ++row;
+        }
         if (row < nrows) {
             float v[S];
             const float* w = c.ws + (row0 + row) * c.ldw + col;
@@ -651,6 +673,48 @@ __global__ __launch_bounds__(256, KS == 4 ? 2 : 4) void k_sgmv_expand_rows(Expan
     y_chunk_store(yc, ys[(tiles - 1) & 1], p.y, p.ld_y, row_base + (int64_t)kRowBlock * (tiles - 1), col0, w_prev);
 }
 
+// The 16-row h tile of a block, rows of `rows` only, from the Split-K
+// workspace into LDS (and out to c.h when write_h): the row's shrink scale
+// times the tree over the S slices below its rank, zeros from there to
+// r_max.  Lane li of each wave holds row li's rank and scale.  Every column
+// below r_max of a row below M lies in the workspace, so the loads are
+// issued without waiting for the rank, and the passes over the tile are
+// unrolled to their compile-time bound (r_max <= 32 KS) so that all of a
+// thread's loads are in flight together.
+template <int S, int KS>
+__device__ __forceinline__ void sgmv_h_tile(const TreeParams& c, int64_t row0, uint32_t rows, int ra_l, float sc_l,
+                                            bool write_h, float* hs)
+{
+    constexpr int kPasses = kRowBlock * 32 * KS / 256;
+    const int r_max = c.ncols;
+    const float rcp_r = __builtin_amdgcn_rcpf((float)r_max);
+    const int drow = div_small(256, rcp_r);
+    const int dcol = 256 - drow * r_max;
+    int row = div_small((int)threadIdx.x, rcp_r);
+    int col = (int)threadIdx.x - row * r_max;
+#pragma unroll
+    for (int pass = 0; pass < kPasses; ++pass, row += drow, col += dcol) {
+        if (col >= r_max) {
+            col -= r_max;
+            ++row;
+        }
+        const int ra = __shfl(ra_l, row & 15);
+        const float sc = __shfl(sc_l, row & 15);
+        if (row < kRowBlock && ((rows >> row) & 1u)) {
+            const float* w = c.ws + (row0 + row) * c.ldw + col;
+            float v[S];
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+                v[s] = w[(int64_t)s * c.split_stride];
+            const float t = pairwise_tree<S>(v);
+            const float hv = col < ra ? __fmul_rn(t, sc) : 0.0f;
+            hs[row * kHTileStride + col] = hv;
+            if (write_h)
+                c.h[(row0 + row) * c.ld_h + col] = hv;
+        }
+    }
+}
+
 // KS: matrix-core steps the kernel is built for (1: r_max <= 32, 2: r_max <= 64,
 // 4: r_max <= 128).  COMBINE: the block's h rows are evaluated from the
 // Split-K workspace into LDS first (the first column block also writes them
@@ -698,6 +762,14 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(ExpandParams p, TreeParams 
         }
     }
     const uint32_t none = (uint32_t)(__ballot(L.row_ok && id < 0) & 0xFFFFull);
+    // the h tile's per-row rank and shrink scale, lane li for row li
+    int ra_l = 0;
+    float sc_l = 0.0f;
+    if (COMBINE && id >= 0) {
+        ra_l = c.ranks[id];
+        ra_l = ra_l < 0 ? 0 : (ra_l > c.ncols ? c.ncols : ra_l);
+        sc_l = c.scales ? c.scales[id] : 1.0f;
+    }
     ExpandLane Ly = L;
     Ly.row_ok = ((mine >> L.li) & 1u) != 0;
     u16x8 yv[2] = {u16x8{0, 0, 0, 0, 0, 0, 0, 0}, u16x8{0, 0, 0, 0, 0, 0, 0, 0}};
@@ -708,15 +780,12 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(ExpandParams p, TreeParams 
     if constexpr (COMBINE) {
         const bool write_h = c.h != nullptr && q.cb == 0;
         const uint32_t rows = mine | (slot == 0 ? none : 0u);
-        for (int e = threadIdx.x; e < kRowBlock * p.r_max; e += 256) {
-            const int row = e / p.r_max;
-            const int col = e - row * p.r_max;
-            if (row < q.nrows && ((rows >> row) & 1u)) {
-                const float v = sgmv_h_value(c, q.row0 + row, col, split_k);
-                hs[row * kHTileStride + col] = v;
-                if (write_h)
-                    c.h[(q.row0 + row) * c.ld_h + col] = v;
-            }
+        switch (split_k) {
+        case 1: sgmv_h_tile<1, KS>(c, q.row0, rows, ra_l, sc_l, write_h, hs); break;
+        case 2: sgmv_h_tile<2, KS>(c, q.row0, rows, ra_l, sc_l, write_h, hs); break;
+        case 4: sgmv_h_tile<4, KS>(c, q.row0, rows, ra_l, sc_l, write_h, hs); break;
+        case 8: sgmv_h_tile<8, KS>(c, q.row0, rows, ra_l, sc_l, write_h, hs); break;
+        default: sgmv_h_tile<16, KS>(c, q.row0, rows, ra_l, sc_l, write_h, hs); break;
         }
         __syncthreads();
         hrows = hs;
