@@ -346,15 +346,6 @@ __device__ __forceinline__ bool combine_item(const ExpandParams& p, int cols, Ex
     return true;
 }
 
-// floor(a / r) for 0 <= a < 4096 and 1 <= r <= 128 from the hardware
-// reciprocal of r: with a = q r + m, (a + 1/2) / r lies at least 1/(2r)
-// >= 1/256 from both q and q + 1, and the product's error (a few ulp of a
-// value below 4096, under 1e-3) cannot carry it across either
-__device__ __forceinline__ int div_small(int a, float rcp_r)
-{
-    return (int)(((float)a + 0.5f) * rcp_r);
-}
-
 template <int KS, int S, int WAVES, int XR>
 __global__ __launch_bounds__(WAVES * 64) void k_expand_combine(ExpandParams p, TreeParams c)
 {

@@ -114,6 +114,15 @@ __device__ __forceinline__ bool tile_ok(const int32_t* t, int64_t M, int32_t n_a
     return tile_rows_ok(t, M) && t[2] >= 0 && t[2] < n_adapters;
 }
 
+// floor(a / r) for 0 <= a < 4096 and 1 <= r <= 128 from the hardware
+// reciprocal of r: with a = q r + m, (a + 1/2) / r lies at least 1/(2r)
+// >= 1/256 from both q and q + 1, and the product's error (a few ulp of a
+// value below 4096, under 1e-3) cannot carry it across either
+__device__ __forceinline__ int div_small(int a, float rcp_r)
+{
+    return (int)(((float)a + 0.5f) * rcp_r);
+}
+
 // Per-adapter values (rank, scale) looked up per element by the
 // multi-adapter tree come from an LDS copy of the first kAdapterTable entries
 // of their device arrays, loaded by all threads at kernel start together

@@ -667,15 +667,20 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_counted_multi(ShrinkP
 // partials (HIP graphs, cold inputs; 32 and 128 decode tokens, one rank-64
 // adapter each): the tree adds 2.1 and 1.9 us instead of 2.7 and 2.5 us.
 // Same arithmetic either way.
+//
+// Each workgroup takes rows_per_wg = 256 / ncols whole rows, thread t
+// column t % ncols of row t / ncols (the quotient from the hardware
+// reciprocal, exact in this range): no 64-bit division ahead of the loads.
 template <int S, bool SGMV, bool TABLE>
-__global__ __launch_bounds__(256) void k_splitk_tree(TreeParams p)
+__global__ __launch_bounds__(256) void k_splitk_tree(TreeParams p, int rows_per_wg)
 {
-    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const bool live = e < p.M * p.ncols;
+    const int tr = div_small((int)threadIdx.x, __builtin_amdgcn_rcpf((float)p.ncols));
+    const int j = (int)threadIdx.x - tr * p.ncols;
+    const int64_t i0 = (int64_t)blockIdx.x * rows_per_wg + tr;
+    const bool live = tr < rows_per_wg && i0 < p.M;
     if (!TABLE && !live)
         return;
-    const int64_t i = live ? e / p.ncols : 0;
-    const int j = (int)(e - i * p.ncols);
+    const int64_t i = live ? i0 : 0;
     float scale = p.scale;
     bool zero = false;
     float v[S];
@@ -821,17 +826,23 @@ void launch_sgmv_r(const ShrinkParams& p, const CounterParams& c, int waves, int
 #undef LORA_SGMV_LAUNCH
 }
 
+// Whole rows of the tree kernel per 256-thread workgroup (ncols <= kMaxRank).
+inline int tree_rows_per_wg(int ncols)
+{
+    return 256 / ncols;
+}
+
 template <bool SGMV, bool TABLE>
 hipError_t launch_tree_t(const TreeParams& p, int S, hipStream_t st)
 {
-    const int64_t n = p.M * p.ncols;
-    dim3 grid((unsigned)((n + 255) / 256)), block(256);
+    const int rows = tree_rows_per_wg(p.ncols);
+    dim3 grid((unsigned)((p.M + rows - 1) / rows)), block(256);
     switch (S) {
-    case 1: hipLaunchKernelGGL((k_splitk_tree<1, SGMV, TABLE>), grid, block, 0, st, p); break;
-    case 2: hipLaunchKernelGGL((k_splitk_tree<2, SGMV, TABLE>), grid, block, 0, st, p); break;
-    case 4: hipLaunchKernelGGL((k_splitk_tree<4, SGMV, TABLE>), grid, block, 0, st, p); break;
-    case 8: hipLaunchKernelGGL((k_splitk_tree<8, SGMV, TABLE>), grid, block, 0, st, p); break;
-    default: hipLaunchKernelGGL((k_splitk_tree<16, SGMV, TABLE>), grid, block, 0, st, p); break;
+    case 1: hipLaunchKernelGGL((k_splitk_tree<1, SGMV, TABLE>), grid, block, 0, st, p, rows); break;
+    case 2: hipLaunchKernelGGL((k_splitk_tree<2, SGMV, TABLE>), grid, block, 0, st, p, rows); break;
+    case 4: hipLaunchKernelGGL((k_splitk_tree<4, SGMV, TABLE>), grid, block, 0, st, p, rows); break;
+    case 8: hipLaunchKernelGGL((k_splitk_tree<8, SGMV, TABLE>), grid, block, 0, st, p, rows); break;
+    default: hipLaunchKernelGGL((k_splitk_tree<16, SGMV, TABLE>), grid, block, 0, st, p, rows); break;
     }
     return hipGetLastError();
 }
@@ -1073,7 +1084,7 @@ hipError_t launch_splitk_tree(const TreeParams& p, int split_k, bool sgmv, hipSt
     if (!sgmv)
         return launch_tree_t<false, false>(p, split_k, st);
     // adapter tables for grids of at most one workgroup per compute unit
-    const int64_t wgs = (p.M * p.ncols + 255) / 256;
+    const int64_t wgs = (p.M + tree_rows_per_wg(p.ncols) - 1) / tree_rows_per_wg(p.ncols);
     return wgs <= 256 ? launch_tree_t<true, true>(p, split_k, st) : launch_tree_t<true, false>(p, split_k, st);
 }
 
