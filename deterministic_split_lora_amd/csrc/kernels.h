@@ -79,21 +79,34 @@ struct ExpandParams {
     float scale;
 };
 
+// The four ints of the plan header or of a tile entry, read together and
+// tested without short-circuit branches: tested one by one with && and ||,
+// they were loaded one after another, each a scalar round trip ahead of the
+// work; read at once, the four loads merge into one.
+struct PlanInts {
+    int32_t v[4];
+};
+
+__device__ __forceinline__ PlanInts load_plan_ints(const int32_t* p)
+{
+    return PlanInts{{p[0], p[1], p[2], p[3]}};
+}
+
 // Number of tiles of a plan buffer, or 0 when the buffer was not built by
 // lora_sgmv_plan for these M and n_adapters (the kernels then do nothing
 // rather than follow stale entries).
 __device__ __forceinline__ int plan_tiles(const int32_t* plan, int64_t M, int32_t n_adapters)
 {
-    if (plan[3] != kPlanMagic || plan[1] != (int32_t)M || plan[2] != n_adapters)
-        return 0;
-    const int n = plan[0];
-    return n < 0 ? 0 : (n > M ? (int)M : n);
+    const PlanInts h = load_plan_ints(plan);
+    const bool ok = (h.v[3] == kPlanMagic) & (h.v[1] == (int32_t)M) & (h.v[2] == n_adapters);
+    const int n = h.v[0];
+    return !ok || n < 0 ? 0 : (n > M ? (int)M : n);
 }
 
 // A tile entry spans 1..16 rows inside [0, M) ...
 __device__ __forceinline__ bool tile_rows_ok(const int32_t* t, int64_t M)
 {
-    return t[0] >= 0 && t[1] >= 1 && t[1] <= kRowBlock && (int64_t)t[0] + t[1] <= M;
+    return (t[0] >= 0) & (t[1] >= 1) & (t[1] <= kRowBlock) & ((int64_t)t[0] + t[1] <= M);
 }
 
 // ... of which the rows whose mask bit is set are the tile's
@@ -111,7 +124,7 @@ __device__ __forceinline__ bool row_in(uint32_t mask, int row)
 // tokens without an adapter carry -1).
 __device__ __forceinline__ bool tile_ok(const int32_t* t, int64_t M, int32_t n_adapters)
 {
-    return tile_rows_ok(t, M) && t[2] >= 0 && t[2] < n_adapters;
+    return tile_rows_ok(t, M) & (t[2] >= 0) & (t[2] < n_adapters);
 }
 
 // floor(a / r) for 0 <= a < 4096 and 1 <= r <= 128 from the hardware

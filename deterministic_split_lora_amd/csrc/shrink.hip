@@ -201,8 +201,9 @@ __device__ __forceinline__ SgmvItem sgmv_item(const ShrinkParams& p, uint32_t it
     const uint32_t rest = it / S;
     q.grp = (int)(rest % (uint32_t)groups);
     q.tile = (int)(rest / (uint32_t)groups);
-    const int32_t* t = p.tiles + kPlanHeaderInts + kPlanTileInts * q.tile;
-    q.ok = tile_rows_ok(t, p.M) && t[2] >= -1 && t[2] < p.n_adapters;
+    const PlanInts e = load_plan_ints(p.tiles + kPlanHeaderInts + kPlanTileInts * q.tile);
+    const int32_t* t = e.v;
+    q.ok = tile_rows_ok(t, p.M) & (t[2] >= -1) & (t[2] < p.n_adapters);
     q.row0 = t[0];
     q.nrows = t[1];
     q.mask = q.ok ? tile_mask(t) : 0u;
@@ -238,12 +239,15 @@ __global__ __launch_bounds__(W * 64) void k_sgmv_shrink_partial(ShrinkParams p)
         const SgmvItem q = sgmv_item(p, it, groups);
         if (!q.ok || q.a < 0)                     // uniform across the workgroup
             continue;
+        // the adapter's weight pointer is read together with its rank, not
+        // after the rank test (one dependent round trip less per item)
+        const uint16_t* Aa = p.A_ptrs[q.a];
         const int ra = adapter_rank(p, q.a);
         const int col0 = q.grp * 16 * RT;
         if (col0 >= ra)
             continue;
-        shrink_tile<RT, W, MODE, KST>(p, q.row0, q.nrows, q.mask, p.A_ptrs[q.a], ra, col0, q.s,
-                                      sgmv_item_scale<MODE>(p, q.a), red);
+        shrink_tile<RT, W, MODE, KST>(p, q.row0, q.nrows, q.mask, Aa, ra, col0, q.s, sgmv_item_scale<MODE>(p, q.a),
+                                      red);
     }
 }
 
@@ -266,7 +270,8 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_partial_multi(ShrinkP
         const int c1 = c0 + T < ntiles ? c0 + T : ntiles;
         int j = c0;
         while (j < c1) {                          // uniform: plan data only
-            const int32_t* t = plan + kPlanTileInts * j;
+            const PlanInts et = load_plan_ints(plan + kPlanTileInts * j);
+            const int32_t* t = et.v;
             if (!tile_ok(t, p.M, p.n_adapters)) {
                 ++j;
                 continue;
@@ -278,17 +283,20 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_partial_multi(ShrinkP
             int n = 0;
 #pragma unroll
             for (int u = 0; u < T; ++u) {
-                const int32_t* tu = plan + kPlanTileInts * (j + u);
+                PlanInts eu{{0, 0, -1, 0}};
+                if (j + u < c1)
+                    eu = load_plan_ints(plan + kPlanTileInts * (j + u));
+                const int32_t* tu = eu.v;
                 const bool take = n == u && j + u < c1 && tile_ok(tu, p.M, p.n_adapters) && tu[2] == a;
                 row0[u] = take ? tu[0] : t[0];
                 nrows[u] = take ? tu[1] : 0;
                 mask[u] = take ? tile_mask(tu) : 0u;
                 n += take ? 1 : 0;
             }
+            const uint16_t* Aa = p.A_ptrs[a];            // with the rank, not after its test
             const int ra = adapter_rank(p, a);
-            if (ra > 0)
-                shrink_tiles<RT, W, MODE, T>(p, row0, nrows, mask, p.A_ptrs[a], ra, 0, s,
-                                             sgmv_item_scale<MODE>(p, a), red);
+                if (ra > 0)
+                shrink_tiles<RT, W, MODE, T>(p, row0, nrows, mask, Aa, ra, 0, s, sgmv_item_scale<MODE>(p, a), red);
             j += n;
         }
     }
@@ -375,8 +383,8 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
         if constexpr (SGMV) {
             __syncthreads();                      // the previous item's entries are no longer read
             if ((int)threadIdx.x < cnt) {         // one tile per thread, checked and normalised
-                const int32_t* src = plan + kPlanTileInts * (c0 + threadIdx.x);
-                const int32_t t[kPlanTileInts] = {src[0], src[1], src[2], src[3]};
+                const PlanInts e = load_plan_ints(plan + kPlanTileInts * (c0 + threadIdx.x));
+                const int32_t* t = e.v;
                 const bool ok = tile_ok(t, p.M, p.n_adapters);
                 int32_t* d = tl + kPlanTileInts * threadIdx.x;
                 d[0] = ok ? t[0] : 0;
@@ -426,6 +434,8 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
             } else {
                 u1 = cnt;
             }
+            // the weight pointer with the rank, not after the rank test
+            const uint16_t* A = SGMV ? (a < 0 ? nullptr : p.A_ptrs[a]) : p.A;
             const int ra = a < 0 ? 0 : (SGMV ? adapter_rank(p, a) : p.r);
             const int nrt = (ra + 15) / 16 < RT ? (ra + 15) / 16 : RT;
             // the atomic contrast's factor for the run (loaded once per run)
@@ -435,7 +445,6 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
             for (int q = 0; q + 1 < NB; ++q)
                 xload(u + q < u1 ? u + q : u1 - 1, xb[q]);
             if (ra > 0) {
-                const uint16_t* A = SGMV ? p.A_ptrs[a] : p.A;
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
                     if (rt < nrt) {
@@ -603,7 +612,8 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_counted_multi(ShrinkP
         const int c1 = c0 + T < ntiles ? c0 + T : ntiles;
         int j = c0;
         while (j < c1) {                          // uniform: plan data only
-            const int32_t* t = plan + kPlanTileInts * j;
+            const PlanInts et = load_plan_ints(plan + kPlanTileInts * j);
+            const int32_t* t = et.v;
             if (!tile_rows_ok(t, p.M)) {
                 ++j;
                 continue;
@@ -625,7 +635,10 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_counted_multi(ShrinkP
             int n = 0;
 #pragma unroll
             for (int u = 0; u < T; ++u) {
-                const int32_t* tu = plan + kPlanTileInts * (j + u);
+                PlanInts eu{{0, 0, -1, 0}};
+                if (j + u < c1)
+                    eu = load_plan_ints(plan + kPlanTileInts * (j + u));
+                const int32_t* tu = eu.v;
                 const bool take = n == u && j + u < c1 && tile_ok(tu, p.M, p.n_adapters) && tu[2] == a;
                 row0[u] = take ? tu[0] : t[0];
                 nrows[u] = take ? tu[1] : 0;
