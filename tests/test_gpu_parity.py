@@ -876,7 +876,9 @@ def test_sgmv_decode_probe_shapes(M):
                                        (300, 2048, 64, 8200, 16), (40, 1024, 24, 16384, 8),
                                        (1, 4096, 128, 4096, 8), (20, 1024, 96, 1032, 16),
                                        (300, 2048, 128, 8200, 16), (33, 2048, 72, 264, 1),
-                                       (2100, 1024, 64, 1032, 8)])
+                                       (2100, 1024, 64, 1032, 8), (17, 2048, 32, 1544, 8),
+                                       (1, 2048, 20, 3000, 8), (33, 2048, 16, 1024, 8), (1, 4096, 5, 1032, 8),
+                                       (250, 4096, 16, 2056, 8)])
 def test_shrink_expand_fused_bitwise(M, K, r, N, S):
     """Every schedule of the deterministic shrink + expand - lora_shrink_splitk
     then lora_expand (three launches), lora_shrink_partials then
