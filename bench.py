@@ -107,6 +107,9 @@ class Bench:
                 s[M] = dict(x=g(b.x), A=g(b.A), B=g(b.B), y=g(b.y),
                             h=torch.empty((M, RANK), dtype=torch.float32, device=self.dev),
                             ws=torch.empty(self.ws_bytes[M], dtype=torch.uint8, device=self.dev),
+                            # the single-launch shrink's own zeroed workspace of tagged slots
+                            cws=torch.zeros(dsl.lora_counted_workspace_bytes(M, RANK, SPLIT), dtype=torch.uint8,
+                                            device=self.dev),
                             cnt=torch.zeros(max(1, dsl.lora_shrink_counter_bytes(M) // 4), dtype=torch.int32,
                                             device=self.dev))
             self.sets.append(s)
@@ -131,7 +134,7 @@ class Bench:
     def det_counted(self, s, M):
         """Single-launch counted shrink, then expand (2 launches)."""
         d = self.dsl
-        d.lora_shrink_splitk_counted(s["x"], s["A"], s["h"], s["ws"], s["cnt"], SPLIT, 1.0)
+        d.lora_shrink_splitk_counted(s["x"], s["A"], s["h"], s["cws"], s["cnt"], SPLIT, 1.0)
         d.lora_expand(s["h"], s["B"], s["y"], SCALE)
 
     def det_counted_one_launch(self, s, M):
@@ -474,14 +477,15 @@ def shrink_only_bench(args):
     copies = max(8, math.ceil(ROTATE_BYTES / 64 / per))
     sets = [dict(x=gpu_tensor(c.x, dev), A=gpu_tensor(c.A, dev),
                  h=torch.empty((M, r), dtype=torch.float32, device=dev),
-                 ws=torch.empty(dsl.lora_shrink_workspace_bytes(M, r, S), dtype=torch.uint8, device=dev))
+                 ws=torch.empty(dsl.lora_shrink_workspace_bytes(M, r, S), dtype=torch.uint8, device=dev),
+                 cws=torch.zeros(dsl.lora_counted_workspace_bytes(M, r, S), dtype=torch.uint8, device=dev))
             for _ in range(copies)]
     cnt = torch.zeros(dsl.lora_shrink_counter_bytes(M) // 4, dtype=torch.int32, device=dev)
     out = {"workload": "shrink only: x [8 x 1024], A [8 x 1024] bf16, Split-K 8, scale 1",
            "bytes": shrink_bytes(M, K, r), "copies": copies}
     calls = {
         "det_two_launch": lambda st: dsl.lora_shrink_splitk(st["x"], st["A"], st["h"], st["ws"], S, 1.0),
-        "det_one_launch": lambda st: dsl.lora_shrink_splitk_counted(st["x"], st["A"], st["h"], st["ws"], cnt, S,
+        "det_one_launch": lambda st: dsl.lora_shrink_splitk_counted(st["x"], st["A"], st["h"], st["cws"], cnt, S,
                                                                     1.0),
         "atomic": lambda st: dsl.lora_shrink_splitk_atomic(st["x"], st["A"], st["h"], S, 1.0),
     }
@@ -549,7 +553,8 @@ def split_sweep_bench(args):
     c = single_adapter_case(1, K, r, 0, split_k=8, scale=1.0, seed=0)
     copies = 256
     sets = [dict(x=gpu_tensor(c.x, dev), A=gpu_tensor(c.A, dev), h=torch.empty((1, r), device=dev),
-                 ws=torch.empty(dsl.lora_shrink_workspace_bytes(1, r, 16), dtype=torch.uint8, device=dev))
+                 ws=torch.empty(dsl.lora_shrink_workspace_bytes(1, r, 16), dtype=torch.uint8, device=dev),
+                 cws=torch.zeros(dsl.lora_counted_workspace_bytes(1, r, 16), dtype=torch.uint8, device=dev))
             for _ in range(copies)]
     cnt = torch.zeros(dsl.lora_shrink_counter_bytes(1) // 4, dtype=torch.int32, device=dev)
     qkv = {"workload": "decode shrink, 1 token, hidden 3072, 3 fused QKV slices of rank 16 (A stacked: r = 48)"}
@@ -558,7 +563,7 @@ def split_sweep_bench(args):
         row["det_two_launch_us"] = round(_time_rotating(
             lambda st, S=S: dsl.lora_shrink_splitk(st["x"], st["A"], st["h"], st["ws"], S, 1.0), sets, args), 3)
         row["det_one_launch_us"] = round(_time_rotating(
-            lambda st, S=S: dsl.lora_shrink_splitk_counted(st["x"], st["A"], st["h"], st["ws"], cnt, S, 1.0), sets,
+            lambda st, S=S: dsl.lora_shrink_splitk_counted(st["x"], st["A"], st["h"], st["cws"], cnt, S, 1.0), sets,
             args), 3)
         row["atomic_us"] = round(_time_rotating(
             lambda st, S=S: dsl.lora_shrink_splitk_atomic(st["x"], st["A"], st["h"], S, 1.0), sets, args), 3)
@@ -661,7 +666,9 @@ def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S, replays=100, ids=
                          Bp=torch.tensor([b.data_ptr() for b in Bs], dtype=torch.int64, device=dev),
                          h=hs[i % copies_ex],
                          ws=torch.empty(dsl.lora_sgmv_workspace_bytes(M, c.r_max, S), dtype=torch.uint8,
-                                        device=dev)))
+                                        device=dev),
+                         cws=torch.zeros(dsl.lora_counted_workspace_bytes(M, c.r_max, S), dtype=torch.uint8,
+                                         device=dev)))
     torch.cuda.synchronize()
 
     def shrink(st):
@@ -669,7 +676,7 @@ def sgmv_bench(args, label, M, K, N, ranks, seg_lo, seg_hi, S, replays=100, ids=
 
     def shrink_counted(st):
         dsl.lora_sgmv_shrink_counted(st["x"], st["Ap"], K, ranks_g, None, n, plan, st["h"], c.r_max, S,
-                                     st["ws"], cnt)
+                                     st["cws"], cnt)
 
     def expand(st):
         dsl.lora_sgmv_expand(st["h"], st["Bp"], ranks_g, scales_g, ids_g, n, st["y"], c.r_max)
@@ -787,7 +794,8 @@ def decode_probe(args, M=32, mixed=False):
         Ag = [g(a) for a in As]
         sets.append(dict(x=g(x), A=Ag, Ap=torch.tensor([t.data_ptr() for t in Ag], dtype=torch.int64, device=dev),
                          h=torch.empty((M, r), dtype=torch.float32, device=dev),
-                         ws=torch.empty(dsl.lora_sgmv_workspace_bytes(M, r, S), dtype=torch.uint8, device=dev)))
+                         ws=torch.empty(dsl.lora_sgmv_workspace_bytes(M, r, S), dtype=torch.uint8, device=dev),
+                         cws=torch.zeros(dsl.lora_counted_workspace_bytes(M, r, S), dtype=torch.uint8, device=dev)))
     torch.cuda.synchronize()
 
     cnt = torch.zeros(dsl.lora_sgmv_counter_bytes(M) // 4, dtype=torch.int32, device=dev)
@@ -796,7 +804,7 @@ def decode_probe(args, M=32, mixed=False):
         dsl.lora_sgmv_shrink(s["x"], s["Ap"], K, ranks, None, ids, n, plan, s["h"], r, S, s["ws"])
 
     def counted(s):
-        dsl.lora_sgmv_shrink_counted(s["x"], s["Ap"], K, ranks, None, n, plan, s["h"], r, S, s["ws"], cnt)
+        dsl.lora_sgmv_shrink_counted(s["x"], s["Ap"], K, ranks, None, n, plan, s["h"], r, S, s["cws"], cnt)
 
     def atomic(s):
         dsl.lora_sgmv_shrink_atomic(s["x"], s["Ap"], K, ranks, None, n, plan, s["h"], r, S)
@@ -1081,6 +1089,8 @@ ONLY = {
     "decode_expand": lambda a: {"32": decode_expand_probe(a, 32), "128": decode_expand_probe(a, 128)},
     "batch_sweep": batch_sweep_bench,
     "compensated": compensated_bench,
+    "small_shrink": shrink_only_bench,
+    "split_sweep": split_sweep_bench,
 }
 
 

@@ -13,5 +13,5 @@ from ._binding import (  # noqa: F401
     lora_shrink_expand_fused, lora_shrink_expand_launches, lora_shrink_counter_bytes, lora_shrink_splitk_counted,
     lora_sgmv_counter_bytes, lora_sgmv_shrink_counted, lora_shrink_expand_counter_bytes, lora_shrink_expand_counted,
     lora_expand_compensated, lora_sgmv_shrink_expand, lora_shrink_expand_noalloc, NOALLOC_SCRATCH_BYTES,
-    lora_sgmv_shrink_atomic,
+    lora_sgmv_shrink_atomic, lora_counted_workspace_bytes,
 )

@@ -33,7 +33,7 @@ EXPORTED = [
     "lora_shrink_splitk_counted", "lora_sgmv_counter_bytes", "lora_sgmv_shrink_counted",
     "lora_shrink_expand_counter_bytes", "lora_shrink_expand_counted", "lora_expand_compensated",
     "lora_sgmv_shrink_expand", "lora_shrink_expand_noalloc",
-    "lora_sgmv_shrink_atomic",
+    "lora_sgmv_shrink_atomic", "lora_counted_workspace_bytes",
 ]
 
 
@@ -59,7 +59,7 @@ _f32 = ctypes.c_float
 _sz = ctypes.c_size_t
 
 # LORA_DET_ABI_VERSION of include/lora_det.h that these signatures follow.
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 def lib():
@@ -109,6 +109,8 @@ def lib():
                                                  _i32, _i64, _i32, _f32, _f32, _vp, _sz, _vp, _sz, _vp]
         L.lora_shrink_counter_bytes.restype = _sz
         L.lora_shrink_counter_bytes.argtypes = [_i64]
+        L.lora_counted_workspace_bytes.restype = _sz
+        L.lora_counted_workspace_bytes.argtypes = [_i64, _i32, _i32]
         L.lora_sgmv_counter_bytes.restype = _sz
         L.lora_sgmv_counter_bytes.argtypes = [_i64]
         L.lora_shrink_splitk_counted.restype = ctypes.c_int
@@ -236,13 +238,18 @@ def lora_shrink_counter_bytes(M: int) -> int:
     return int(lib().lora_shrink_counter_bytes(M))
 
 
+def lora_counted_workspace_bytes(M: int, r_max: int, split_k: int) -> int:
+    return int(lib().lora_counted_workspace_bytes(M, r_max, split_k))
+
+
 def lora_sgmv_counter_bytes(M: int) -> int:
     return int(lib().lora_sgmv_counter_bytes(M))
 
 
 def lora_shrink_splitk_counted(x, A, h, workspace, counters, split_k: int = 8, scale: float = 1.0, stream=None):
-    """Single-launch deterministic shrink; counters: zero-initialised int32 GPU tensor
-    of lora_shrink_counter_bytes(M) / 4 elements (left zero)."""
+    """Single-launch deterministic shrink.  workspace: zero-initialised GPU buffer of
+    lora_counted_workspace_bytes(M, r, split_k) bytes, counters: zero-initialised
+    int32 GPU tensor of lora_shrink_counter_bytes(M) / 4 elements (both left zero)."""
     import torch
     _dtype(x, torch.bfloat16, "x"); _dtype(A, torch.bfloat16, "A"); _dtype(h, torch.float32, "h")
     if counters is not None:

@@ -796,6 +796,12 @@ int lora_shrink_expand_counted(const uint16_t* x, int64_t ld_x, const uint16_t* 
     return launch_status(launch_shrink_expand_counted(sp, ep, t, q, pl.waves, gt, static_cast<hipStream_t>(stream)));
 }
 
+size_t lora_counted_workspace_bytes(int64_t M, int32_t r_max, int32_t split_k)
+{
+    const size_t w = workspace_bytes(M, r_max, split_k);
+    return w > SIZE_MAX / 2 ? 0 : 2 * w;
+}
+
 size_t lora_shrink_counter_bytes(int64_t M)
 {
     if (M < 0 || M > kMaxDim)
@@ -824,7 +830,7 @@ int lora_shrink_splitk_counted(const uint16_t* x, int64_t ld_x, const uint16_t* 
         return LORA_ERR_NULL;
     if (!aligned16(workspace) || (reinterpret_cast<uintptr_t>(counters) & 3u))
         return LORA_ERR_ALIGN;
-    if (ws_bytes < workspace_bytes(M, r, split_k) || counter_bytes < lora_shrink_counter_bytes(M))
+    if (ws_bytes < lora_counted_workspace_bytes(M, r, split_k) || counter_bytes < lora_shrink_counter_bytes(M))
         return LORA_ERR_WORKSPACE;
     p.out = static_cast<float*>(workspace);
     p.ld_out = r;
@@ -867,7 +873,7 @@ int lora_sgmv_shrink_counted(const uint16_t* x, int64_t ld_x, const uint16_t* co
     if (!aligned16(x) || (reinterpret_cast<uintptr_t>(h) & 3u) || !aligned16(plan) || !aligned16(workspace) ||
         (reinterpret_cast<uintptr_t>(counters) & 3u) || ld_x % 8 || ld_a % 8)
         return LORA_ERR_ALIGN;
-    if (plan_bytes < lora_sgmv_plan_bytes(M) || ws_bytes < workspace_bytes(M, r_max, split_k) ||
+    if (plan_bytes < lora_sgmv_plan_bytes(M) || ws_bytes < lora_counted_workspace_bytes(M, r_max, split_k) ||
         counter_bytes < lora_sgmv_counter_bytes(M))
         return LORA_ERR_WORKSPACE;
     ShrinkParams p{};

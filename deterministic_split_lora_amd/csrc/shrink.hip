@@ -33,61 +33,33 @@ namespace {
 // fixed order).
 //
 // The XCDs of an MI355X each have their own L2, so a partial written by one
-// workgroup must reach the device-wide coherence point before another XCD
-// reads it.  The ordering is stated in the memory model, at agent scope:
-//   writer: every thread stores its part of the partial (agent-scope atomic
-//           stores, performed at the coherence point); the workgroup barrier
-//           orders all of them before thread 0's counter add, which is a
-//           RELEASE read-modify-write at agent scope - so every partial store
-//           of the workgroup happens before the add.
-//   reader: the workgroup whose add returned split_k - 1 arrived last.  Its
-//           add read the value of the previous add, which continues the
-//           release sequences of all earlier adds; an ACQUIRE fence at agent
-//           scope after it makes every earlier writer's partial visible; the
-//           barrier then passes that to the workgroup's other threads, which
-//           load the S partials, evaluate the same pairwise tree and multiply
-//           as the second-pass kernel, write h and put the counter back to 0
-//           for the next call (the kernel boundary orders that store before
-//           the next call).
-// On gfx950 the release is an L2 write-back plus a wait for the wave's
-// stores (buffer_wbl2 sc1, s_waitcnt vmcnt(0)) issued by one wave per
-// workgroup, and the acquire an L2 invalidate (buffer_inv sc1) issued only by
-// the last arriver.  Integer atomics only order the arrivals; the
-// floating-point sum has one fixed order whichever workgroup is last.  No
-// workgroup waits for another.
+// workgroup must reach the device-wide coherence point before a workgroup on
+// another XCD reads it.  Ordering the partial stores before an arrival
+// counter would take a release at agent scope, which on gfx950 writes back
+// the XCD's L2 (buffer_wbl2) once per arriving workgroup; those write-backs
+// queue per XCD and made the multi-adapter single launch ~4x slower than the
+// two passes.  Instead each partial travels in a tagged 64-bit slot
+// (tagged_tree): the reader checks every slot's own tag, so nothing but
+// per-location coherence is needed.
+//
+// Every workgroup of a (row block or plan tile, rank group) makes one relaxed
+// integer add to its counter when it STARTS the item; the add's result comes
+// back while the workgroup streams its operands.  The one whose add returned
+// split_k - 1 started last (its add also put the counter back to 0): it keeps
+// its own partial in LDS and waits for the other split_k - 1 slots.  Those belong to workgroups
+// that already made their add, so they are resident and finish their item
+// without waiting for anyone; the wait always ends.  The floating-point sum
+// has one fixed order whichever workgroup combines.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bool arrived_last(int32_t* counter, int split_k, int* flag)
+// The arrival is a wrapping increment (old >= split_k - 1 ? 0 : old + 1),
+// so the add that returns split_k - 1 also puts the counter back to 0 for the
+// next call.  (An integer fetch-add here is rewritten by the compiler into a
+// wave-wide add whose result it waits for at once; the increment's result is
+// waited for only where it is used, after the partial.)
+__device__ __forceinline__ int arrival_add(int32_t* counter, int split_k)
 {
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int old = __hip_atomic_fetch_add(counter, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == split_k - 1)
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        *flag = old;
-    }
-    __syncthreads();
-    return *flag == split_k - 1;
-}
-
-// h rows row0 + i (i < nrows, bit i of mask set), columns [c0, c_zero):
-// scale * tree over the S workspace slices for columns below c_data, zeros
-// from c_data on.
-__device__ __forceinline__ void combine_tile(const ShrinkParams& p, int64_t row0, int nrows, uint32_t mask, int c0,
-                                             int c_data, int c_zero, float scale, float* h, int64_t ld_h)
-{
-    const int ncols = c_zero - c0;
-    for (int e = threadIdx.x; e < nrows * ncols; e += blockDim.x) {
-        const int row = e / ncols;
-        if (!row_in(mask, row))
-            continue;
-        const int col = c0 + (e - row * ncols);
-        float val = 0.0f;
-        if (col < c_data) {
-            const float* w = p.out + (row0 + row) * p.ld_out + col;
-            val = __fmul_rn(split_tree(w, p.split_stride, p.split_k), scale);
-        }
-        h[(row0 + row) * ld_h + col] = val;
-    }
+    return (int)__builtin_amdgcn_atomic_inc32(reinterpret_cast<uint32_t*>(counter), (uint32_t)(split_k - 1),
+                                              __ATOMIC_RELAXED, "agent");
 }
 
 // ---------------------------------------------------------------------------
@@ -156,24 +128,27 @@ __global__ __launch_bounds__(W * 64, 4) void k_shrink_partial_multi(ShrinkParams
                                  red);
 }
 
-// Single launch: the last split of each (row block, rank group) writes h.
-template <int RT, int W>
+// Single launch: the split that starts last in each (row block, rank group)
+// writes h.
+template <int RT, int W, int KST>
 __global__ __launch_bounds__(W * 64) void k_shrink_counted(ShrinkParams p, CounterParams c, int groups)
 {
     __shared__ float red[red_floats<RT, W>()];
+    __shared__ float own[16 * 16 * RT];
     __shared__ int flag;
     const SingleItem q = single_item(p, groups);
-    const int64_t row0 = q.row0;
-    const int nrows = q.nrows;
     const int col0 = q.grp * 16 * RT;
-    shrink_tile<RT, W, kToWorkspaceCoherent>(p, row0, nrows, kFullMask, p.A, p.r, col0, q.s, 1.0f, red);
     int32_t* counter = c.counters + q.mb * kMaxRankTiles + q.grp;
-    if (arrived_last(counter, p.split_k, &flag)) {
-        const int cend = col0 + 16 * RT < p.r ? col0 + 16 * RT : p.r;
-        combine_tile(p, row0, nrows, kFullMask, col0, cend, cend, p.scale, c.h, c.ld_h);
-        if (threadIdx.x == 0)
-            __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    int arrived = 0;
+    if (threadIdx.x == 0)
+        arrived = arrival_add(counter, p.split_k);
+    shrink_tile<RT, W, kToLds, KST>(p, q.row0, q.nrows, kFullMask, p.A, p.r, col0, q.s, 1.0f, red, own);
+    if (threadIdx.x == 0)
+        flag = arrived;
+    __syncthreads();
+    const bool last = flag == p.split_k - 1;
+    const int cend = col0 + 16 * RT < p.r ? col0 + 16 * RT : p.r;
+    tagged_finish<RT, 8>(p, q.row0, q.nrows, kFullMask, col0, cend, cend, q.s, last, p.scale, own, c.h, c.ld_h);
 }
 
 // ---------------------------------------------------------------------------
@@ -548,14 +523,15 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
     }
 }
 
-// Single launch: the last split of each (tile, rank group) writes its h
-// columns; the group holding the adapter's last rank column also zeroes the
-// columns from the rank up to r_max; tiles of tokens without an adapter are
-// zeroed by their (split 0, group 0) workgroup.
-template <int RT, int W>
+// Single launch: the split that starts last in each (tile, rank group)
+// writes its h columns; the group holding the adapter's last rank column
+// also zeroes the columns from the rank up to r_max; tiles of tokens without
+// an adapter are zeroed by their (split 0, group 0) workgroup.
+template <int RT, int W, int KST>
 __global__ __launch_bounds__(W * 64) void k_sgmv_shrink_counted(ShrinkParams p, CounterParams c)
 {
     __shared__ float red[red_floats<RT, W>()];
+    __shared__ float own[16 * 16 * RT];
     __shared__ int flag;
     const int groups = (p.r_max + 16 * RT - 1) / (16 * RT);
     const uint32_t items = (uint32_t)plan_tiles(p.tiles, p.M, p.n_adapters) * p.split_k * groups;
@@ -570,38 +546,43 @@ __global__ __launch_bounds__(W * 64) void k_sgmv_shrink_counted(ShrinkParams p, 
                         c.h[(q.row0 + e / p.r_max) * c.ld_h + e % p.r_max] = 0.0f;
             continue;
         }
+        const uint16_t* Aa = p.A_ptrs[q.a];
         const int ra = adapter_rank(p, q.a);
         const int col0 = q.grp * 16 * RT;
         if (col0 >= ra)
             continue;
-        shrink_tile<RT, W, kToWorkspaceCoherent>(p, q.row0, q.nrows, q.mask, p.A_ptrs[q.a], ra, col0, q.s, 1.0f,
-                                                 red);
         int32_t* counter = c.counters + (int64_t)q.tile * kMaxRankTiles + q.grp;
-        if (arrived_last(counter, p.split_k, &flag)) {
-            const float scale = c.scales ? c.scales[q.a] : 1.0f;
-            const int cend = col0 + 16 * RT < ra ? col0 + 16 * RT : ra;
-            const int czero = cend == ra ? p.r_max : cend;
-            combine_tile(p, q.row0, q.nrows, q.mask, col0, cend, czero, scale, c.h, c.ld_h);
-            if (threadIdx.x == 0)
-                __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        __syncthreads();                          // flag is reused by the next item
+        int arrived = 0;
+        if (threadIdx.x == 0)
+            arrived = arrival_add(counter, p.split_k);
+        shrink_tile<RT, W, kToLds, KST>(p, q.row0, q.nrows, q.mask, Aa, ra, col0, q.s, 1.0f, red, own);
+        if (threadIdx.x == 0)
+            flag = arrived;
+        __syncthreads();
+        const bool last = flag == p.split_k - 1;
+        const float scale = last && c.scales ? c.scales[q.a] : 1.0f;
+        const int cend = col0 + 16 * RT < ra ? col0 + 16 * RT : ra;
+        const int czero = cend == ra ? p.r_max : cend;
+        tagged_finish<RT, 4>(p, q.row0, q.nrows, q.mask, col0, cend, czero, q.s, last, scale, own, c.h, c.ld_h);
+        __syncthreads();                          // own and flag are reused by the next item
     }
 }
 
 // Large M, single launch: the items of k_sgmv_shrink_partial_multi (up to T
 // consecutive plan tiles of one adapter share the A loads; every rank tile
 // of r_max <= 64 in one workgroup) with the arrival-counter combine of
-// k_sgmv_shrink_counted per tile: partials stored at the coherence point,
-// then per tile one counter add; the split that arrives last evaluates the
-// tile's h (fixed tree, the adapter's shrink scale).  Tiles of tokens without
+// k_sgmv_shrink_counted per tile: one counter add per tile when the item
+// starts, partials kept in LDS, then stored to tagged slots; the split that
+// started last evaluates the tile's h (fixed tree, the adapter's shrink
+// scale).  Tiles of tokens without
 // an adapter get zero h rows from their split-0 item.  Same bits as the
 // two-pass multi-adapter shrink.
 template <int RT, int W, int T>
 __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_counted_multi(ShrinkParams p, CounterParams c)
 {
     __shared__ float red[red_floats<RT, W>()];
-    __shared__ int flag;
+    __shared__ float own[T * 16 * 16 * RT];
+    __shared__ int flag[T];
     const int ntiles = plan_tiles(p.tiles, p.M, p.n_adapters);
     const uint32_t S = (uint32_t)p.split_k;
     const uint32_t items = (uint32_t)((ntiles + T - 1) / T) * S;
@@ -647,21 +628,23 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_counted_multi(ShrinkP
             }
             const int ra = adapter_rank(p, a);
             if (ra > 0) {
-                shrink_tiles<RT, W, kToWorkspaceCoherent, T>(p, row0, nrows, mask, p.A_ptrs[a], ra, 0, s, 1.0f,
-                                                             red);
+                int arrived = 0;
+                if ((int)threadIdx.x < n)
+                    arrived = arrival_add(c.counters + (int64_t)(j + (int)threadIdx.x) * kMaxRankTiles, p.split_k);
+                shrink_tiles<RT, W, kToLds, T>(p, row0, nrows, mask, p.A_ptrs[a], ra, 0, s, 1.0f, red, own);
+                if ((int)threadIdx.x < n)
+                    flag[threadIdx.x] = arrived;
+                __syncthreads();
 #pragma unroll
                 for (int u = 0; u < T; ++u) {
                     if (u < n) {                  // uniform
-                        int32_t* counter = c.counters + (int64_t)(j + u) * kMaxRankTiles;
-                        if (arrived_last(counter, p.split_k, &flag)) {
-                            const float scale = c.scales ? c.scales[a] : 1.0f;
-                            combine_tile(p, row0[u], nrows[u], mask[u], 0, ra, p.r_max, scale, c.h, c.ld_h);
-                            if (threadIdx.x == 0)
-                                __hip_atomic_store(counter, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                        }
-                        __syncthreads();          // flag is reused
+                        const bool last = flag[u] == p.split_k - 1;
+                        const float scale = last && c.scales ? c.scales[a] : 1.0f;
+                        tagged_finish<RT, 4>(p, row0[u], nrows[u], mask[u], 0, ra < 16 * RT ? ra : 16 * RT, p.r_max,
+                                          s, last, scale, own + u * 16 * 16 * RT, c.h, c.ld_h);
                     }
                 }
+                __syncthreads();                  // own and flag are reused
             }
             j += n;
         }
@@ -801,7 +784,13 @@ hipError_t launch_partial(const ShrinkParams& p, int waves, int rank_tiles, int 
 template <int RT, int W>
 void launch_counted_rw(const ShrinkParams& p, const CounterParams& c, int groups, hipStream_t st)
 {
-    hipLaunchKernelGGL((k_shrink_counted<RT, W>), single_grid(p, groups), dim3(W * 64), 0, st, p, c, groups);
+    const dim3 g = single_grid(p, groups);
+    switch (p.k_steps) {
+    case 1: hipLaunchKernelGGL((k_shrink_counted<RT, W, 1>), g, dim3(W * 64), 0, st, p, c, groups); break;
+    case 2: hipLaunchKernelGGL((k_shrink_counted<RT, W, 2>), g, dim3(W * 64), 0, st, p, c, groups); break;
+    case 4: hipLaunchKernelGGL((k_shrink_counted<RT, W, 4>), g, dim3(W * 64), 0, st, p, c, groups); break;
+    default: hipLaunchKernelGGL((k_shrink_counted<RT, W, 0>), g, dim3(W * 64), 0, st, p, c, groups); break;
+    }
 }
 
 template <int RT>
@@ -821,8 +810,12 @@ void launch_sgmv_r(const ShrinkParams& p, const CounterParams& c, int waves, int
     dim3 g((unsigned)grid);
 #define LORA_SGMV_LAUNCH(W_)                                                                          \
     do {                                                                                              \
-        if (COUNTED)                                                                                  \
-            hipLaunchKernelGGL((k_sgmv_shrink_counted<RT, W_>), g, dim3(W_ * 64), 0, st, p, c);        \
+        if (COUNTED && p.k_steps == 2)                                                                \
+            hipLaunchKernelGGL((k_sgmv_shrink_counted<RT, W_, 2>), g, dim3(W_ * 64), 0, st, p, c);     \
+        else if (COUNTED && p.k_steps == 4)                                                           \
+            hipLaunchKernelGGL((k_sgmv_shrink_counted<RT, W_, 4>), g, dim3(W_ * 64), 0, st, p, c);     \
+        else if (COUNTED)                                                                             \
+            hipLaunchKernelGGL((k_sgmv_shrink_counted<RT, W_, 0>), g, dim3(W_ * 64), 0, st, p, c);     \
         else if (p.k_steps == 2)                                                                      \
             hipLaunchKernelGGL((k_sgmv_shrink_partial<RT, W_, MODE, 2>), g, dim3(W_ * 64), 0, st, p);  \
         else if (p.k_steps == 4)                                                                      \

@@ -10,7 +10,13 @@
 
 namespace lora {
 
-enum ShrinkMode { kToWorkspace = 0, kToOutputScaled = 1, kAtomicScaled = 2, kToWorkspaceCoherent = 3 };
+enum ShrinkMode {
+    kToWorkspace = 0,
+    kToOutputScaled = 1,
+    kAtomicScaled = 2,
+    kToWorkspaceCoherent = 3,
+    kToLds = 4                              // the split's partial into an LDS tile (single-launch combine)
+};
 
 // Agent-scope atomic store / load: performed at the device-wide coherence
 // point, past the per-XCD L2 caches (used for the single-launch combine).
@@ -43,7 +49,8 @@ __device__ __forceinline__ void shrink_store(const ShrinkParams& p, int64_t row0
 
 template <int RT, int W, int MODE>
 __device__ __forceinline__ void wave_tree_store(const ShrinkParams& p, int64_t row0, int nrows, uint32_t mask, int rg,
-                                                int col0, int s, float scale, float* red, const f32x4 (&acc)[RT]);
+                                                int col0, int s, float scale, float* red, const f32x4 (&acc)[RT],
+                                                float* own);
 
 // The matrix-core chains of one wave: T row tiles (x row pointers xp[u]) times
 // NRT rank tiles (A row pointers ap[rt]), `steps` steps of 32 k from the
@@ -159,10 +166,12 @@ __device__ __forceinline__ void mfma_dispatch(int nrt, const uint16_t* const (&x
 // element the arithmetic depends only on (K, split_k): the tiles a workgroup
 // holds, the rank tiles grouped with it and the other rows of its tile change
 // no bit.
+// MODE kToLds: tile u's partial goes to own[(u * 16 + row) * 16 RT + column -
+// col0] instead of memory.
 template <int RT, int W, int MODE, int T, int KST = 0>
 __device__ __forceinline__ void shrink_tiles(const ShrinkParams& p, const int64_t (&row0)[T], const int (&nrows)[T],
                                              const uint32_t (&mask)[T], const uint16_t* __restrict__ A, int r,
-                                             int col0, int s, float scale, float* red)
+                                             int col0, int s, float scale, float* red, float* own = nullptr)
 {
     constexpr int G = T == 1 ? 4 : 2;
     const int wave = threadIdx.x >> 6;
@@ -209,7 +218,8 @@ __device__ __forceinline__ void shrink_tiles(const ShrinkParams& p, const int64_
 #pragma unroll
     for (int u = 0; u < T; ++u)
         if (nrows[u] > 0)                         // uniform across the workgroup
-            wave_tree_store<RT, W, MODE>(p, row0[u], nrows[u], mask[u], rg, col0, s, scale, red, acc[u]);
+            wave_tree_store<RT, W, MODE>(p, row0[u], nrows[u], mask[u], rg, col0, s, scale, red, acc[u],
+                                         MODE == kToLds ? own + u * 16 * 16 * RT : nullptr);
 }
 
 // One work item: rows row0 .. row0+nrows-1 (those in mask), split s, rank
@@ -217,12 +227,12 @@ __device__ __forceinline__ void shrink_tiles(const ShrinkParams& p, const int64_
 template <int RT, int W, int MODE, int KST = 0>
 __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0, int nrows, uint32_t mask,
                                             const uint16_t* __restrict__ A, int r, int col0, int s, float scale,
-                                            float* red)
+                                            float* red, float* own = nullptr)
 {
     const int64_t rows[1] = {row0};
     const int n[1] = {nrows};
     const uint32_t m[1] = {mask};
-    shrink_tiles<RT, W, MODE, 1, KST>(p, rows, n, m, A, r, col0, s, scale, red);
+    shrink_tiles<RT, W, MODE, 1, KST>(p, rows, n, m, A, r, col0, s, scale, red, own);
 }
 
 // acc[rt][v] is the wave's sum for token row 4g+v, rank column col0 + 16 rt + li:
@@ -230,7 +240,8 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t row0,
 // pairwise tree; then the split's partial is stored.
 template <int RT, int W, int MODE>
 __device__ __forceinline__ void wave_tree_store(const ShrinkParams& p, int64_t row0, int nrows, uint32_t mask, int rg,
-                                                int col0, int s, float scale, float* red, const f32x4 (&acc)[RT])
+                                                int col0, int s, float scale, float* red, const f32x4 (&acc)[RT],
+                                                float* own)
 {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -242,8 +253,12 @@ __device__ __forceinline__ void wave_tree_store(const ShrinkParams& p, int64_t r
 #pragma unroll
             for (int v = 0; v < 4; ++v) {
                 const int row = 4 * g + v, col = rt * 16 + li;
-                if (row < nrows && row_in(mask, row) && col < rg)
-                    shrink_store<MODE>(p, row0, s, row, col0 + col, acc[rt][v], scale);
+                if (row < nrows && row_in(mask, row) && col < rg) {
+                    if constexpr (MODE == kToLds)
+                        own[row * 16 * RT + col] = acc[rt][v];
+                    else
+                        shrink_store<MODE>(p, row0, s, row, col0 + col, acc[rt][v], scale);
+                }
             }
     } else {
         constexpr int RS = 16 * RT + 4;          // padded LDS row stride (floats)
@@ -262,7 +277,10 @@ __device__ __forceinline__ void wave_tree_store(const ShrinkParams& p, int64_t r
 #pragma unroll
                 for (int w = 0; w < W; ++w)
                     v[w] = red[(w * 16 + row) * RS + col];
-                shrink_store<MODE>(p, row0, s, row, col0 + col, pairwise_tree<W>(v), scale);
+                if constexpr (MODE == kToLds)
+                    own[e] = pairwise_tree<W>(v);
+                else
+                    shrink_store<MODE>(p, row0, s, row, col0 + col, pairwise_tree<W>(v), scale);
             }
         }
         __syncthreads();                          // LDS is reused by the next item
@@ -297,6 +315,164 @@ __device__ __forceinline__ float split_tree(const float* w, int64_t split_stride
     case 4: return tree_of_splits<4>(w, split_stride);
     case 8: return tree_of_splits<8>(w, split_stride);
     default: return tree_of_splits<16>(w, split_stride);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tagged workspace slots of the single-launch shrinks.  A slot is one 64-bit
+// word: the fp32 partial in the low half and a tag in the high half (1: this
+// call's partial, 0: consumed).  Slots are written and read only with
+// agent-scope atomic stores and loads of the whole word, so a reader that
+// sees the tag 1 sees the partial stored with it (single-copy atomicity of an
+// aligned 64-bit atomic), and by per-location coherence it eventually sees
+// the store, whichever XCD made it.  No ordering between different
+// locations is needed - no release or acquire, hence no L2 write-back or
+// invalidate - because every slot carries its own evidence of being written.
+// The combining workgroup clears each slot it consumed; the kernel boundary
+// orders those clears before the next call's stores.
+// ---------------------------------------------------------------------------
+constexpr uint32_t kSlotWritten = 1u;
+// Polls per slot before a reader gives up (each a memory round trip: about a
+// quarter of a second in all).  A writer that has made its arrival add is
+// resident and finishes its item without waiting for anyone, and the reader
+// started last, so no correct launch comes near this.
+constexpr uint32_t kSlotSpinLimit = 1u << 18;
+
+__device__ __forceinline__ void slot_store(uint64_t* slot, float v)
+{
+    const uint64_t w = ((uint64_t)kSlotWritten << 32) | (uint64_t)__builtin_bit_cast(uint32_t, v);
+    __hip_atomic_store(slot, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t slot_load(uint64_t* slot)
+{
+    return __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void slot_clear(uint64_t* slot)
+{
+    __hip_atomic_store(slot, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool slot_written(uint64_t w)
+{
+    return (uint32_t)(w >> 32) == kSlotWritten;
+}
+
+__device__ __forceinline__ float slot_value(uint64_t w)
+{
+    return __builtin_bit_cast(float, (uint32_t)w);
+}
+
+// Fixed pairwise tree over the S partials of one element: split s_own's from
+// `own` (the combining workgroup's own partial, never stored), the others
+// from their tagged slots w[s * stride], each read until written and then
+// cleared.  False (and the slots left as they are) if a slot never showed
+// its partial.
+// Slots are polled in groups of GMAX (4 or 8): each poll loads the group's
+// missing slots at once.  Fewer loads in flight per thread keep the register
+// count, and with it the occupancy, close to the two-pass partial kernel's;
+// more cut the round trips of the last workgroup.
+template <int S, int GMAX>
+__device__ __forceinline__ bool tagged_tree(uint64_t* w, int64_t stride, int s_own, float own, float& out)
+{
+    constexpr int G = S < GMAX ? S : GMAX;
+    float v[S];
+#pragma unroll
+    for (int g0 = 0; g0 < S; g0 += G) {
+        const int d = s_own - g0;
+        uint32_t pending = ((1u << G) - 1u) & ~((unsigned)d < (unsigned)G ? 1u << d : 0u);
+        for (uint32_t n = 0; pending != 0u && n < kSlotSpinLimit; ++n) {
+            if (n > 0)
+                __builtin_amdgcn_s_sleep(2);
+            uint64_t t[G];
+#pragma unroll
+            for (int q = 0; q < G; ++q)
+                t[q] = ((pending >> q) & 1u) ? slot_load(w + (int64_t)(g0 + q) * stride) : 0;
+#pragma unroll
+            for (int q = 0; q < G; ++q)
+                if (((pending >> q) & 1u) && slot_written(t[q])) {
+                    v[g0 + q] = slot_value(t[q]);
+                    pending &= ~(1u << q);
+                }
+        }
+        if (pending != 0u)
+            return false;
+    }
+    // the own split's slot was not written in this call and still reads 0,
+    // so clearing it too changes nothing
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        v[s] = s == s_own ? own : v[s];
+        slot_clear(w + (int64_t)s * stride);
+    }
+    out = pairwise_tree<S>(v);
+    return true;
+}
+
+// Sixteen splits as two trees of eight added at the end - the same sum as
+// the 16-way pairwise tree, whose top level is exactly that add - so that no
+// thread holds more than eight partials.
+template <int GMAX>
+__device__ __forceinline__ bool tagged_split_tree(uint64_t* w, int64_t stride, int split_k, int s_own, float own,
+                                                  float& out)
+{
+    switch (split_k) {
+    case 1: out = own; return true;
+    case 2: return tagged_tree<2, GMAX>(w, stride, s_own, own, out);
+    case 4: return tagged_tree<4, GMAX>(w, stride, s_own, own, out);
+    case 8: return tagged_tree<8, GMAX>(w, stride, s_own, own, out);
+    default: {
+        float lo, hi;
+        if (!tagged_tree<8, GMAX>(w, stride, s_own, own, lo) ||
+            !tagged_tree<8, GMAX>(w + 8 * stride, stride, s_own - 8, own, hi))
+            return false;
+        out = __fadd_rn(lo, hi);
+        return true;
+    }
+    }
+}
+
+// After shrink_tile<kToLds>: the tile's rows row0 + i (i < nrows, in mask) and
+// columns [c0, c_data) are in own[i * 16 RT + column - c0].  A workgroup that
+// did not arrive last stores them to its split's tagged slots
+// (ws[s * split_stride + row * ld_out + column], 64-bit words); the last one
+// evaluates h = scale * tree over the S partials for those columns and writes
+// zeros for columns [c_data, c_zero).  A slot that never shows its partial
+// (no correct launch) gives NaN in h.
+template <int RT, int GMAX>
+__device__ __forceinline__ void tagged_finish(const ShrinkParams& p, int64_t row0, int nrows, uint32_t mask, int c0,
+                                              int c_data, int c_zero, int s, bool last, float scale,
+                                              const float* own, float* h, int64_t ld_h)
+{
+    uint64_t* ws = reinterpret_cast<uint64_t*>(p.out);
+    if (!last) {
+        const int ncols = c_data - c0;
+        for (int e = threadIdx.x; e < nrows * ncols; e += blockDim.x) {
+            const int row = e / ncols;
+            const int col = e - row * ncols;
+            if (row_in(mask, row))
+                slot_store(ws + (int64_t)s * p.split_stride + (row0 + row) * p.ld_out + c0 + col,
+                           own[row * 16 * RT + col]);
+        }
+        return;
+    }
+    const int ncols = c_zero - c0;
+    for (int e = threadIdx.x; e < nrows * ncols; e += blockDim.x) {
+        const int row = e / ncols;
+        if (!row_in(mask, row))
+            continue;
+        const int col = c0 + (e - row * ncols);
+        float val = 0.0f;
+        if (col < c_data) {
+            float t;
+            if (tagged_split_tree<GMAX>(ws + (row0 + row) * p.ld_out + col, p.split_stride, p.split_k, s,
+                                  own[row * 16 * RT + col - c0], t))
+                val = __fmul_rn(t, scale);
+            else
+                val = __builtin_nanf("");
+        }
+        h[(row0 + row) * ld_h + col] = val;
     }
 }
 

@@ -80,7 +80,7 @@
 extern "C" {
 #endif
 
-#define LORA_DET_ABI_VERSION 5
+#define LORA_DET_ABI_VERSION 6
 
 enum lora_status {
     LORA_OK = 0,
@@ -189,24 +189,36 @@ int lora_expand_compensated(const float* h, int64_t ld_h, const uint16_t* B, int
 
 /*
  * Single-launch deterministic Split-K shrink: the paper's final design
- * (section 4.3, Alg. 1).  Each split's workgroup stores its fp32 partial to
- * the workspace with agent-scope atomic stores; after a workgroup barrier one
- * thread adds 1 to its row block's integer counter with an agent-scope
- * RELEASE read-modify-write (so every partial store of the workgroup happens
- * before the add); the workgroup that sees split_k - 1 arrived last issues an
- * agent-scope ACQUIRE fence, loads the partials with agent-scope loads,
- * applies the same fixed pairwise tree and scale as lora_shrink_splitk,
- * writes h and resets the counter to 0.  Bit for bit the same h as
- * lora_shrink_splitk, in one launch.  No workgroup waits for another.  On
- * gfx950 each release writes back the XCD's L2, which makes this path slow
- * when many workgroups arrive (see lora_sgmv_shrink_counted).
+ * (section 4.3, Alg. 1 - per-tile arrival counters, the partials combined
+ * inside the same launch).  Each split's workgroup adds 1 to its row block's
+ * integer counter (agent-scope relaxed read-modify-write) when it starts, then
+ * computes its fp32 partial.  The workgroup whose add returned split_k - 1
+ * started last: it resets the counter to 0, keeps its own partial and reads
+ * the other split_k - 1 from the workspace, then applies the same fixed
+ * pairwise tree and scale as lora_shrink_splitk and writes h.  Bit for bit
+ * the same h as lora_shrink_splitk, in one launch.
+ * The partials move in TAGGED 64-bit workspace slots: low half the fp32
+ * value, high half 1 once written, put back to 0 by the workgroup that
+ * consumed it.  Writers store and the combining workgroup loads whole slots
+ * with agent-scope atomic stores and loads, and waits until each slot shows
+ * its tag: per-location coherence suffices, so no release or acquire is
+ * issued (on gfx950 an agent-scope release writes back the XCD's L2).  The
+ * combining workgroup waits only for workgroups that have already made their
+ * add, which are resident and wait for nobody, so every wait ends; a slot
+ * that never showed its partial (no correct launch) would give NaN in h.
+ * workspace: lora_counted_workspace_bytes(M, r, split_k) bytes, 16-byte
+ * aligned, ALL ZERO before the first call and left zero by every completed
+ * call; it is this entry point's own (the two-pass entry points write other
+ * values into a workspace).  Slot (s, i, j) is the 64-bit word
+ * s * M * r + i * r + j.
  * counters: int32 [lora_shrink_counter_bytes(M) / 4] (8 per 16-token block, one
  * per 16-wide rank tile of a rank <= 128), 4-byte aligned, ALL ZERO
  * before the first call; every completed call leaves them zero again, so one
- * zero-initialised buffer serves any number of calls on one stream (not
- * concurrent calls).  workspace as for lora_shrink_splitk.  split_k == 1 needs
- * neither workspace nor counters.
+ * zero-initialised pair of buffers serves any number of calls on one stream
+ * (not concurrent calls).  split_k == 1 needs neither workspace nor counters.
  */
+size_t lora_counted_workspace_bytes(int64_t M, int32_t r_max, int32_t split_k);
+
 size_t lora_shrink_counter_bytes(int64_t M);
 
 int lora_shrink_splitk_counted(const uint16_t* x, int64_t ld_x, const uint16_t* A, int64_t ld_a,
@@ -396,9 +408,12 @@ int lora_sgmv_shrink(const uint16_t* x, int64_t ld_x, const uint16_t* const* A_p
 
 /*
  * Multi-adapter single-launch shrink: lora_sgmv_shrink's result (same bits) in
- * one launch with the completion-counter combine of lora_shrink_splitk_counted,
- * one counter per plan tile.  The plan must come from lora_sgmv_plan with the
- * same M and n_adapters (token ids are read from the plan).
+ * one launch with the tagged-slot combine of lora_shrink_splitk_counted,
+ * one counter per plan tile and rank group.  The plan must come from
+ * lora_sgmv_plan with the same M and n_adapters (token ids are read from the
+ * plan).
+ * workspace: lora_counted_workspace_bytes(M, r_max, split_k) bytes, all zero
+ * before the first call, left zero, not shared with other entry points.
  * counters: int32 [lora_sgmv_counter_bytes(M) / 4] (8 per possible tile), all
  * zero before the first call, left zero.
  */

@@ -41,6 +41,14 @@ def workspace(nbytes: int):
     return t.empty(max(int(nbytes), 16), dtype=t.uint8, device="cuda")
 
 
+def counted_workspace(M: int, r_max: int, split_k: int):
+    """The single-launch shrinks' own workspace of tagged slots: zero before
+    the first call (and left zero by every call)."""
+    import deterministic_split_lora_amd as dsl
+    t = torch()
+    return t.zeros(max(int(dsl.lora_counted_workspace_bytes(M, r_max, split_k)), 16), dtype=t.uint8, device="cuda")
+
+
 def check_shrink(h_gpu: np.ndarray, x, A, scale: float, plan: dict, what: str = "", atomic: bool = False):
     """Two bounds, both per element:
     * the stated tolerance: |h - ref| <= 1e-3 |scale| ||x_i|| ||A_j||;

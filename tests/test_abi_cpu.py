@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_status_strings():
-    assert dsl.lora_abi_version() == 5
+    assert dsl.lora_abi_version() == 6
     seen = set()
     for s in range(0, 8):
         t = dsl.lora_status_str(s)
@@ -332,7 +332,9 @@ def test_counted_rejects():
     assert dsl.lora_shrink_counter_bytes(1) == 32
     assert dsl.lora_shrink_counter_bytes(33) == 96
     assert dsl.lora_sgmv_counter_bytes(33) == 1056
-    wsb = dsl.lora_shrink_workspace_bytes(4, 16, 8)
+    # tagged 64-bit slots: twice the two-pass workspace
+    wsb = dsl.lora_counted_workspace_bytes(4, 16, 8)
+    assert wsb == 2 * dsl.lora_shrink_workspace_bytes(4, 16, 8)
 
     def call(**kw):
         a = dict(x=FAKE, ld_x=4096, A=FAKE, ld_a=4096, h=FAKE, ld_h=16, M=4, K=4096, r=16, S=8, scale=1.0,
@@ -346,10 +348,11 @@ def test_counted_rejects():
     assert call(cnt=FAKE + 2) == B.LORA_ERR_ALIGN
     assert call(cb=0) == B.LORA_ERR_WORKSPACE
     assert call(wsb=wsb - 4) == B.LORA_ERR_WORKSPACE
+    assert call(wsb=dsl.lora_shrink_workspace_bytes(4, 16, 8)) == B.LORA_ERR_WORKSPACE
     assert call(S=5) == B.LORA_ERR_UNSUPPORTED
     assert call(M=0, x=None, cnt=None) == B.LORA_OK
     pb = dsl.lora_sgmv_plan_bytes(64)
-    wsg = dsl.lora_sgmv_workspace_bytes(64, 64, 8)
+    wsg = dsl.lora_counted_workspace_bytes(64, 64, 8)
 
     def sg(**kw):
         a = dict(x=FAKE, ld_x=4096, Ap=FAKE, ld_a=4096, ranks=FAKE, scales=None, n=4, plan=FAKE, pb=pb, h=FAKE,
@@ -361,6 +364,7 @@ def test_counted_rejects():
     assert sg(cnt=None) == B.LORA_ERR_NULL
     assert sg(plan=None) == B.LORA_ERR_NULL
     assert sg(cb=1020) == B.LORA_ERR_WORKSPACE
+    assert sg(wsb=dsl.lora_sgmv_workspace_bytes(64, 64, 8)) == B.LORA_ERR_WORKSPACE
     assert sg(n=0) == B.LORA_ERR_SHAPE
     assert sg(cnt=FAKE + 1) == B.LORA_ERR_ALIGN
     assert sg(M=0, x=None) == B.LORA_OK
@@ -427,6 +431,7 @@ def test_sgmv_shrink_expand_rejects():
     assert call(y=FAKE_MIS) == B.LORA_ERR_ALIGN
     assert call(pb=pb - 4) == B.LORA_ERR_WORKSPACE
     assert call(wsb=wsb - 4) == B.LORA_ERR_WORKSPACE
+    assert call(wsb=dsl.lora_shrink_workspace_bytes(4, 16, 8)) == B.LORA_ERR_WORKSPACE
     assert call(M=0, x=None, ws=None) == B.LORA_OK
 
 

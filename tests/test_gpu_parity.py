@@ -14,8 +14,8 @@ import pytest
 import deterministic_split_lora_amd as dsl
 import oracle
 from synth import integer_bf16, normal_bf16, single_adapter_case, sgmv_case, segments_to_ids
-from tests.helpers import (bf16_from_gpu, bf16_to_gpu, check_expand, check_shrink, f32_bits, f32_to_gpu,
-                           gpu_available, torch, workspace)
+from tests.helpers import (bf16_from_gpu, bf16_to_gpu, check_expand, check_shrink, counted_workspace, f32_bits,
+                           f32_to_gpu, gpu_available, torch, workspace)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs a GPU")]
@@ -830,7 +830,8 @@ def _sgmv_other_schedules(c, h, y, gpu):
                                 h=h2)
     cnt = t.zeros(dsl.lora_sgmv_counter_bytes(c.M) // 4, dtype=t.int32, device="cuda")
     h3 = t.full((c.M, c.r_max), float("nan"), dtype=t.float32, device="cuda")
-    dsl.lora_sgmv_shrink_counted(xg, Ap, c.K, ranks, scales, n, plan, h3, c.r_max, c.split_k, ws, cnt)
+    dsl.lora_sgmv_shrink_counted(xg, Ap, c.K, ranks, scales, n, plan, h3, c.r_max, c.split_k,
+                                 counted_workspace(c.M, c.r_max, c.split_k), cnt)
     t.cuda.synchronize()
     assert np.array_equal(f32_bits_np(h), f32_bits(h2)), "pipeline h"
     assert np.array_equal(f32_bits_np(h), f32_bits(h3)), "single-launch shrink h"
@@ -1024,7 +1025,7 @@ def test_sgmv_graph_replays(M, interleaved):
     xg, y0 = bf16_to_gpu(c.x), bf16_to_gpu(c.y)
     y = y0.clone()
     ws = workspace(dsl.lora_sgmv_workspace_bytes(M, c.r_max, c.split_k))
-    ws2 = workspace(dsl.lora_sgmv_workspace_bytes(M, c.r_max, c.split_k))
+    ws2 = counted_workspace(M, c.r_max, c.split_k)
     cnt = t.zeros(dsl.lora_sgmv_counter_bytes(M) // 4, dtype=t.int32, device="cuda")
     h = t.empty((M, c.r_max), dtype=t.float32, device="cuda")
     h2 = t.empty((M, c.r_max), dtype=t.float32, device="cuda")
@@ -1163,7 +1164,7 @@ def test_shrink_counted_bitwise(M, K, r, S):
     h1 = t.empty((M, r), dtype=t.float32, device="cuda")
     dsl.lora_shrink_splitk(xg, Ag, h1, ws if S > 1 else None, S, 2.0)
     cnt = t.zeros(max(1, dsl.lora_shrink_counter_bytes(M) // 4), dtype=t.int32, device="cuda")
-    ws2 = workspace(dsl.lora_shrink_workspace_bytes(M, r, S))
+    ws2 = counted_workspace(M, r, S)
     outs = []
     for rep in range(20):
         h2 = t.full((M, r), float("nan"), dtype=t.float32, device="cuda")
@@ -1182,7 +1183,7 @@ def test_shrink_counted_in_graph_replays():
     M, K, r, S = 48, 4096, 16, 8
     c = single_adapter_case(M, K, r, 0, split_k=S, seed=8)
     xg, Ag = bf16_to_gpu(c.x), bf16_to_gpu(c.A)
-    ws = workspace(dsl.lora_shrink_workspace_bytes(M, r, S))
+    ws = counted_workspace(M, r, S)
     cnt = t.zeros(dsl.lora_shrink_counter_bytes(M) // 4, dtype=t.int32, device="cuda")
     h = t.empty((M, r), dtype=t.float32, device="cuda")
     dsl.lora_shrink_splitk_counted(xg, Ag, h, ws, cnt, S, 1.0)
@@ -1249,7 +1250,7 @@ def test_sgmv_counted_bitwise(case):
     ws = workspace(dsl.lora_sgmv_workspace_bytes(c.M, c.r_max, c.split_k))
     dsl.lora_sgmv_shrink(xg, Ap, c.K, ranks, scales, idg, n, plan, h1, c.r_max, c.split_k, ws)
     cnt = t.zeros(dsl.lora_sgmv_counter_bytes(c.M) // 4, dtype=t.int32, device="cuda")
-    ws2 = workspace(dsl.lora_sgmv_workspace_bytes(c.M, c.r_max, c.split_k))
+    ws2 = counted_workspace(c.M, c.r_max, c.split_k)
     hs = []
     for rep in range(5):
         h2 = t.full((c.M, c.r_max), float("nan"), dtype=t.float32, device="cuda")
@@ -1282,7 +1283,7 @@ def test_counted_shrinks_stress_repeats():
     xg, Ag = bf16_to_gpu(c.x), bf16_to_gpu(c.A)
     ref = t.empty((M, r), dtype=t.float32, device="cuda")
     dsl.lora_shrink_splitk(xg, Ag, ref, workspace(dsl.lora_shrink_workspace_bytes(M, r, S)), S, 1.0)
-    ws = workspace(dsl.lora_shrink_workspace_bytes(M, r, S))
+    ws = counted_workspace(M, r, S)
     cnt = t.zeros(dsl.lora_shrink_counter_bytes(M) // 4, dtype=t.int32, device="cuda")
     h = t.empty_like(ref)
     bad = t.zeros((), dtype=t.int64, device="cuda")
@@ -1299,7 +1300,7 @@ def test_counted_shrinks_stress_repeats():
     ref2 = t.empty((32, 64), dtype=t.float32, device="cuda")
     dsl.lora_sgmv_shrink(x2, Ap, 8192, ranks, None, idg, 32, plan, ref2, 64, 8,
                          workspace(dsl.lora_sgmv_workspace_bytes(32, 64, 8)))
-    ws2 = workspace(dsl.lora_sgmv_workspace_bytes(32, 64, 8))
+    ws2 = counted_workspace(32, 64, 8)
     cnt2 = t.zeros(dsl.lora_sgmv_counter_bytes(32) // 4, dtype=t.int32, device="cuda")
     h2 = t.empty_like(ref2)
     for _ in range(500):
@@ -1335,7 +1336,7 @@ def test_sgmv_counted_large_m_repeats():
     ref = t.full((c.M, c.r_max), float("nan"), dtype=t.float32, device="cuda")
     dsl.lora_sgmv_shrink(xg, Ap, c.K, ranks, scales, idg, 4, plan, ref, c.r_max, c.split_k,
                          workspace(dsl.lora_sgmv_workspace_bytes(c.M, c.r_max, c.split_k)))
-    ws = workspace(dsl.lora_sgmv_workspace_bytes(c.M, c.r_max, c.split_k))
+    ws = counted_workspace(c.M, c.r_max, c.split_k)
     cnt = t.zeros(dsl.lora_sgmv_counter_bytes(c.M) // 4, dtype=t.int32, device="cuda")
     h = t.empty_like(ref)
     bad = t.zeros((), dtype=t.int64, device="cuda")
@@ -1552,7 +1553,8 @@ def test_fused_qkv_decode_slices(S):
         dsl.lora_shrink_splitk(xg, Ag, h48, ws if S > 1 else None, S, 1.0)
         cnt = t.zeros(dsl.lora_shrink_counter_bytes(M) // 4, dtype=t.int32, device="cuda")
         h1 = t.full((M, 48), float("nan"), dtype=t.float32, device="cuda")
-        dsl.lora_shrink_splitk_counted(xg, Ag, h1, ws if S > 1 else None, cnt if S > 1 else None, S, 1.0)
+        dsl.lora_shrink_splitk_counted(xg, Ag, h1, counted_workspace(M, 48, S) if S > 1 else None,
+                                       cnt if S > 1 else None, S, 1.0)
         ha = t.full((M, 48), float("nan"), dtype=t.float32, device="cuda")
         dsl.lora_shrink_splitk_atomic(xg, Ag, ha, S, 1.0)
         slices = []
