@@ -1053,6 +1053,13 @@ def provenance(b):
                              timeout=10).stdout.strip() or None
     except Exception:
         pass
+    if git is None:
+        # a copy of the tree without its history: the revision the library was built from
+        try:
+            with open(os.path.join(os.path.dirname(dsl.LIBRARY_PATH), "build_revision.txt")) as f:
+                git = f.read().strip() or None
+        except OSError:
+            pass
     srcs = sorted(os.path.join("deterministic_split_lora_amd", "csrc", f)
                   for f in os.listdir(os.path.join(ROOT, "deterministic_split_lora_amd", "csrc")))
     hin, hout = hashlib.sha256(), hashlib.sha256()

@@ -39,6 +39,25 @@ def hipcc() -> str:
     return p if os.path.exists(p) else "hipcc"
 
 
+def _record_revision() -> None:
+    """Writes the git revision of the sources next to the library (with
+    "-dirty" when tracked files differ from it), so a copy of the tree without
+    its history still says what the library was built from.  No git: no file."""
+    import subprocess
+    root = os.path.dirname(HERE)
+    path = os.path.join(HERE, "build_revision.txt")
+    try:
+        rev = subprocess.run(["git", "-C", root, "rev-parse", "HEAD"], capture_output=True, text=True,
+                             timeout=10).stdout.strip()
+        dirty = subprocess.run(["git", "-C", root, "status", "--porcelain", "--untracked-files=no"],
+                               capture_output=True, text=True, timeout=10).stdout.strip()
+    except (OSError, subprocess.SubprocessError):
+        return
+    if rev:
+        with open(path, "w") as f:
+            f.write(rev + ("-dirty" if dirty else "") + "\n")
+
+
 def build(verbose: bool = False) -> str:
     """Compile every source; always recompiles (a cross-compile, no GPU needed).
     Each source is compiled to an object in parallel, then the objects are
@@ -73,6 +92,7 @@ def build(verbose: bool = False) -> str:
         if rc != 0:
             raise RuntimeError("hipcc link failed:\n" + err)
         os.replace(tmp, LIB)
+        _record_revision()
     finally:
         for o in objs:
             if os.path.exists(o):

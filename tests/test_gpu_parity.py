@@ -1152,11 +1152,11 @@ def test_batch_invariance_across_schedule_switch():
                                      (4100, 2048, 16, 8), (2000, 1024, 24, 16), (37, 4096, 128, 8),
                                      (2100, 1024, 100, 8)])
 def test_shrink_counted_bitwise(M, K, r, S):
-    """lora_shrink_splitk_counted (one launch, the last-arriving split
+    """lora_shrink_splitk_counted (one launch, the split that starts last
     combines, one row block per workgroup) gives lora_shrink_splitk's bits
     (which shares A loads between 2 or 4 row blocks per workgroup at the
-    larger M here), leaves its counters at zero, and repeats bit for bit on
-    the same counters."""
+    larger M here), leaves its counters and its tagged workspace at zero, and
+    repeats bit for bit on the same buffers."""
     t = torch()
     c = single_adapter_case(M, K, r, 0, split_k=S, seed=31 + M)
     xg, Ag = bf16_to_gpu(c.x), bf16_to_gpu(c.A)
@@ -1175,6 +1175,9 @@ def test_shrink_counted_bitwise(M, K, r, S):
     for h2 in outs:
         assert np.array_equal(f32_bits(h2), ref)
     assert int(cnt.abs().sum()) == 0
+    # every tagged slot written was consumed and cleared by its combining workgroup
+    if S > 1:
+        assert int(ws2.count_nonzero()) == 0
     check_shrink(outs[0].cpu().numpy(), c.x, c.A, 2.0, dsl.lora_shrink_plan(K, r, S), "counted")
 
 
@@ -1260,6 +1263,7 @@ def test_sgmv_counted_bitwise(case):
     for h2 in hs:
         assert np.array_equal(f32_bits(h2), f32_bits(h1))
     assert int(cnt.abs().sum()) == 0
+    assert int(ws2.count_nonzero()) == 0          # every written slot consumed and cleared
     hh = hs[0].cpu().numpy()
     for i in range(0, c.M, max(1, c.M // 40)):
         a = int(c.ids[i])
