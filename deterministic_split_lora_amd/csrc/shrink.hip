@@ -129,9 +129,10 @@ __global__ __launch_bounds__(W * 64, 4) void k_shrink_partial_multi(ShrinkParams
 }
 
 // Single launch: the split that starts last in each (row block, rank group)
-// writes h.
+// writes h.  Occupancy hint as for k_sgmv_shrink_counted.
 template <int RT, int W, int KST>
-__global__ __launch_bounds__(W * 64) void k_shrink_counted(ShrinkParams p, CounterParams c, int groups)
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 && KST > 0 && W >= 4 ? 8 : 1, 8)))
+void k_shrink_counted(ShrinkParams p, CounterParams c, int groups)
 {
     __shared__ float red[red_floats<RT, W>()];
     __shared__ float own[16 * 16 * RT];
@@ -527,8 +528,15 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
 // writes its h columns; the group holding the adapter's last rank column
 // also zeroes the columns from the rank up to r_max; tiles of tokens without
 // an adapter are zeroed by their (split 0, group 0) workgroup.
+// Eight waves per SIMD for the one-rank-tile kernels with compile-time
+// chains, as the two-pass partial kernel gets: the poll loops would otherwise
+// raise the scalar register count past that occupancy (the compiler keeps the
+// excess in vector-register lanes; the other variants would spill to memory).
+// Measured on MI355X, 32 decode tokens with one rank-64 adapter each: 15.9 ->
+// 13.2 us.
 template <int RT, int W, int KST>
-__global__ __launch_bounds__(W * 64) void k_sgmv_shrink_counted(ShrinkParams p, CounterParams c)
+__global__ __launch_bounds__(W * 64) __attribute__((amdgpu_waves_per_eu(RT == 1 && KST > 0 && W >= 4 ? 8 : 1, 8)))
+void k_sgmv_shrink_counted(ShrinkParams p, CounterParams c)
 {
     __shared__ float red[red_floats<RT, W>()];
     __shared__ float own[16 * 16 * RT];
