@@ -88,14 +88,20 @@ int shrink_tiles_per_wg(int64_t M, int32_t split_k)
     return wgs >= 2048 ? 4 : (wgs >= 512 ? 2 : 1);
 }
 
-// Multi-adapter: 1 or 4 rank tiles per workgroup, with M standing in for the
-// (device-side) tile count; the rank tiles stay apart up to 2048 work items
-// (512 tokens x 4096 in runs of 1-64 tokens, 4 adapters of rank 64: one rank
-// tile per workgroup 8.9 us, four 11.1 us).
+// Multi-adapter: 1, 2 or 4 rank tiles per workgroup, with M standing in for
+// the (device-side) tile count.  Up to 512 work items every rank tile has its
+// own workgroup (memory parallelism: 32 decode tokens with one rank-64 adapter
+// each are 1024 items once the plan has one tile per token); up to 2048, two
+// rank tiles share their x loads, so that the grid fits in one round of
+// residency (4 eight-wave workgroups per compute unit); beyond that four.
+// Measured on MI355X, 512 tokens x 4096, 4 adapters of rank 64 (~1440 items
+// with one rank tile per workgroup): two-pass shrink 10.8 -> 10.6 us,
+// single-launch shrink 15.1 -> 12.4 us; with ids drawn per token 16.8 -> 15.4
+// and 30.1 -> 22.9 us; four rank tiles per workgroup were slower (11.1 us).
 int sgmv_group_tiles(int64_t M, int32_t split_k, int32_t r_max)
 {
     const int64_t items = ((M + kRowBlock - 1) / kRowBlock) * split_k * ((r_max + 15) / 16);
-    return items <= 2048 ? 1 : kGroupTiles;
+    return items <= 512 ? 1 : (items <= 2048 ? 2 : kGroupTiles);
 }
 
 // Work items of the multi-adapter shrinks (at most M tiles x split_k x

@@ -200,7 +200,7 @@ struct FusedParams {
     float expand_scale;
 };
 
-// group_tiles: rank tiles per workgroup (1 .. rank_tiles; the sgmv kernels take 1 or 4).
+// group_tiles: rank tiles per workgroup (1 .. rank_tiles; the sgmv kernels take 1, 2 or 4).
 hipError_t launch_shrink_partial_ws(const ShrinkParams& p, int waves, int rank_tiles, int group_tiles,
                                     hipStream_t st);
 hipError_t launch_shrink_partial_direct(const ShrinkParams& p, int waves, int rank_tiles, int group_tiles,

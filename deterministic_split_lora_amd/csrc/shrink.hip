@@ -1072,11 +1072,15 @@ hipError_t launch_sgmv_shrink_partial(const ShrinkParams& p, int waves, int grou
     if (atomic) {
         if (group_tiles == 1)
             launch_sgmv_r<1, false, kAtomicScaled>(p, none, waves, grid, st);
+        else if (group_tiles == 2)
+            launch_sgmv_r<2, false, kAtomicScaled>(p, none, waves, grid, st);
         else
             launch_sgmv_r<4, false, kAtomicScaled>(p, none, waves, grid, st);
     } else {
         if (group_tiles == 1)
             launch_sgmv_r<1, false>(p, none, waves, grid, st);
+        else if (group_tiles == 2)
+            launch_sgmv_r<2, false>(p, none, waves, grid, st);
         else
             launch_sgmv_r<4, false>(p, none, waves, grid, st);
     }
@@ -1088,6 +1092,8 @@ hipError_t launch_sgmv_shrink_counted(const ShrinkParams& p, const CounterParams
 {
     if (group_tiles == 1)
         launch_sgmv_r<1, true>(p, c, waves, grid, st);
+    else if (group_tiles == 2)
+        launch_sgmv_r<2, true>(p, c, waves, grid, st);
     else
         launch_sgmv_r<4, true>(p, c, waves, grid, st);
     return hipGetLastError();
