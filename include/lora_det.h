@@ -60,6 +60,10 @@
  *   - Split-K workspaces, counters and plans are caller buffers whose sizes
  *     the *_bytes functions return; every entry point takes leading
  *     dimensions and a stream.
+ *   - The single-launch shrinks (lora_shrink_splitk_counted,
+ *     lora_sgmv_shrink_counted) take a workspace of their own, twice the
+ *     two-pass size (lora_counted_workspace_bytes), zero before the first
+ *     call and left zero by every call.
  *
  * SUPPORTED (otherwise LORA_ERR_UNSUPPORTED / LORA_ERR_ALIGN):
  *   1 <= r <= 128 (lora_shrink_expand_fused: r <= 64);  split_k in {1, 2, 4, 8, 16};
