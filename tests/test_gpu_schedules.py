@@ -11,7 +11,9 @@ batch-invariance experiment of the pages (the same row gives the same bits
 whatever batch it is part of) is therefore run here at every row-block count
 from 1 up to past the last switch for each workload shape: 16 probe rows at
 fresh random positions among N(0,1) filler rows, every probe's h (fp32 bits)
-and y (bf16 bits) compared with those of the probe rows computed alone.  The
+and y (bf16 bits) compared with those of the probe rows computed alone - also
+for the single-launch shrinks, whose tagged workspace and counters must be
+back at zero after every batch size.  The
 batch size M runs through 1..5, 64, 65 and one ragged M per row-block count
 (M = 16 b - (7 b mod 16)), so every rule of the form "M below / at least a
 bound" is seen from both sides.  The probe rows computed alone are checked
@@ -88,7 +90,10 @@ def test_batch_invariance_every_row_block_count(label, K, r, N, S, last, record_
     H = t.empty((Mmax, r), dtype=t.float32, device="cuda")
     ws = t.empty(max(dsl.lora_shrink_expand_workspace_bytes(Mmax, r, S),
                      dsl.lora_shrink_workspace_bytes(Mmax, r, S)), dtype=t.uint8, device="cuda")
-    bad = t.zeros((len(Ms), 2), dtype=t.int64, device="cuda")
+    # the single-launch shrink's own buffers (tagged slots and counters, zero between calls)
+    cws = t.zeros(dsl.lora_counted_workspace_bytes(Mmax, r, S), dtype=t.uint8, device="cuda")
+    cnt = t.zeros(dsl.lora_shrink_counter_bytes(Mmax) // 4, dtype=t.int32, device="cuda")
+    bad = t.zeros((len(Ms), 3), dtype=t.int64, device="cuda")
     rng = np.random.default_rng(seed)
     launches = {}
     for i, M in enumerate(Ms):
@@ -107,14 +112,19 @@ def test_batch_invariance_every_row_block_count(label, K, r, N, S, last, record_
         dsl.lora_shrink_splitk(x, Ag, h, ws, S, 1.0)
         dsl.lora_expand(h, Bg, y, 2.0)
         bad[i, 1] += (h[pos].view(t.int32) != ref_h[which]).sum() + (y[pos].view(t.int16) != ref_y[which]).sum()
+        # lora_shrink_splitk_counted: one launch, the split that starts last combines
+        h.fill_(float("nan"))
+        dsl.lora_shrink_splitk_counted(x, Ag, h, cws, cnt, S, 1.0)
+        bad[i, 2] += (h[pos].view(t.int32) != ref_h[which]).sum()
         x[pos] = saved
         nl = dsl.lora_shrink_expand_launches(M, K, r, N, S)
         launches[nl] = launches.get(nl, 0) + 1
     t.cuda.synchronize()
     b = bad.cpu().numpy()
-    wrong = [(Ms[i], int(b[i, 0]), int(b[i, 1])) for i in range(len(Ms)) if b[i].any()]
+    wrong = [(Ms[i], int(b[i, 0]), int(b[i, 1]), int(b[i, 2])) for i in range(len(Ms)) if b[i].any()]
     record_property("launch_counts_seen", launches)
-    assert not wrong, f"{label}: probe bits changed at (M, shrink_expand, splitk+expand) {wrong[:10]}"
+    assert not wrong, f"{label}: probe bits changed at (M, shrink_expand, splitk+expand, counted) {wrong[:10]}"
+    assert int(cnt.abs().sum()) == 0 and int(cws.count_nonzero()) == 0
     _say(f"  {len(Ms)} batch sizes identical; launches seen {launches}")
 
     # and the probe rows are right
@@ -194,7 +204,9 @@ def test_sgmv_batch_invariance_every_row_block_count(label, K, N, ranks, S, seg,
     H = t.zeros((Mmax, r_max), dtype=t.float32, device="cuda")
     ws = t.empty(dsl.lora_sgmv_workspace_bytes(Mmax, r_max, S), dtype=t.uint8, device="cuda")
     plan = t.zeros(dsl.lora_sgmv_plan_bytes(Mmax), dtype=t.uint8, device="cuda")
-    bad = t.zeros((len(Ms), 2), dtype=t.int64, device="cuda")
+    cws = t.zeros(dsl.lora_counted_workspace_bytes(Mmax, r_max, S), dtype=t.uint8, device="cuda")
+    cnt = t.zeros(dsl.lora_sgmv_counter_bytes(Mmax) // 4, dtype=t.int32, device="cuda")
+    bad = t.zeros((len(Ms), 3), dtype=t.int64, device="cuda")
 
     def differ(h, y, pos, which):
         hp = t.where(cols[which], h[pos], 0.0).view(t.int32)
@@ -218,11 +230,16 @@ def test_sgmv_batch_invariance_every_row_block_count(label, K, N, ranks, S, seg,
         dsl.lora_sgmv_shrink(x, Ap, K, rk, sh, ids, n, plan, h, r_max, S, ws)
         dsl.lora_sgmv_expand(h, Bp, rk, ex, ids, n, y, r_max)
         bad[i, 1] += differ(h, y, pos, which)
+        # lora_sgmv_shrink_counted: one launch (h only)
+        h.fill_(float("nan"))
+        dsl.lora_sgmv_shrink_counted(x, Ap, K, rk, sh, n, plan, h, r_max, S, cws, cnt)
+        bad[i, 2] += (t.where(cols[which], h[pos], 0.0).view(t.int32) != ref_h[which]).sum()
         x[pos], ids[pos] = saved_x, saved_id
     t.cuda.synchronize()
     b = bad.cpu().numpy()
-    wrong = [(Ms[i], int(b[i, 0]), int(b[i, 1])) for i in range(len(Ms)) if b[i].any()]
-    assert not wrong, f"{label}: probe bits changed at (M, shrink_expand, shrink+expand) {wrong[:10]}"
+    wrong = [(Ms[i], int(b[i, 0]), int(b[i, 1]), int(b[i, 2])) for i in range(len(Ms)) if b[i].any()]
+    assert not wrong, f"{label}: probe bits changed at (M, shrink_expand, shrink+expand, counted) {wrong[:10]}"
+    assert int(cnt.abs().sum()) == 0 and int(cws.count_nonzero()) == 0
     _say(f"  {len(Ms)} batch sizes identical")
 
     # and the probe rows are right
