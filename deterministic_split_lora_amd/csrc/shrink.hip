@@ -158,6 +158,25 @@ void k_shrink_counted(ShrinkParams p, CounterParams c, int groups)
 // count and leaves the loop together.  Items of rank groups beyond the tile's
 // adapter rank are skipped.
 // ---------------------------------------------------------------------------
+// The plan and the adapter tables (weight pointers, ranks, scales) are never
+// written by a kernel.  Read through the constant address space, their
+// wave-uniform loads are scalar loads in every kernel; in the single-launch
+// kernels the compiler otherwise cannot prove them unchanged past the
+// kernel's own stores and reads them with vector loads, and its wait for
+// those (the counter retires in order) then also waits for the arrival add
+// issued just before the first operand load.
+template <typename T>
+__device__ __forceinline__ T table_load(const T* t, int i)
+{
+    return ((const __attribute__((address_space(4))) T*)t)[i];
+}
+
+// A plan tile entry (wave-uniform), through the scalar cache.
+__device__ __forceinline__ PlanInts plan_entry(const int32_t* e)
+{
+    return PlanInts{{table_load(e, 0), table_load(e, 1), table_load(e, 2), table_load(e, 3)}};
+}
+
 struct SgmvItem {
     int64_t row0;
     int nrows;
@@ -177,7 +196,7 @@ __device__ __forceinline__ SgmvItem sgmv_item(const ShrinkParams& p, uint32_t it
     const uint32_t rest = it / S;
     q.grp = (int)(rest % (uint32_t)groups);
     q.tile = (int)(rest / (uint32_t)groups);
-    const PlanInts e = load_plan_ints(p.tiles + kPlanHeaderInts + kPlanTileInts * q.tile);
+    const PlanInts e = plan_entry(p.tiles + kPlanHeaderInts + kPlanTileInts * q.tile);
     const int32_t* t = e.v;
     q.ok = tile_rows_ok(t, p.M) & (t[2] >= -1) & (t[2] < p.n_adapters);
     q.row0 = t[0];
@@ -187,9 +206,14 @@ __device__ __forceinline__ SgmvItem sgmv_item(const ShrinkParams& p, uint32_t it
     return q;
 }
 
+__device__ __forceinline__ const uint16_t* adapter_weights(const ShrinkParams& p, int a)
+{
+    return table_load(p.A_ptrs, a);
+}
+
 __device__ __forceinline__ int adapter_rank(const ShrinkParams& p, int a)
 {
-    int ra = p.ranks[a];
+    int ra = table_load(p.ranks, a);
     return ra < 0 ? 0 : (ra > p.r_max ? p.r_max : ra);
 }
 
@@ -200,7 +224,7 @@ template <int MODE>
 __device__ __forceinline__ float sgmv_item_scale(const ShrinkParams& p, int a)
 {
     if constexpr (MODE == kAtomicScaled)
-        return p.scales ? p.scales[a] : 1.0f;
+        return p.scales ? table_load(p.scales, a) : 1.0f;
     else
         return 1.0f;
 }
@@ -217,7 +241,7 @@ __global__ __launch_bounds__(W * 64) void k_sgmv_shrink_partial(ShrinkParams p)
             continue;
         // the adapter's weight pointer is read together with its rank, not
         // after the rank test (one dependent round trip less per item)
-        const uint16_t* Aa = p.A_ptrs[q.a];
+        const uint16_t* Aa = adapter_weights(p, q.a);
         const int ra = adapter_rank(p, q.a);
         const int col0 = q.grp * 16 * RT;
         if (col0 >= ra)
@@ -246,7 +270,7 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_partial_multi(ShrinkP
         const int c1 = c0 + T < ntiles ? c0 + T : ntiles;
         int j = c0;
         while (j < c1) {                          // uniform: plan data only
-            const PlanInts et = load_plan_ints(plan + kPlanTileInts * j);
+            const PlanInts et = plan_entry(plan + kPlanTileInts * j);
             const int32_t* t = et.v;
             if (!tile_ok(t, p.M, p.n_adapters)) {
                 ++j;
@@ -261,7 +285,7 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_partial_multi(ShrinkP
             for (int u = 0; u < T; ++u) {
                 PlanInts eu{{0, 0, -1, 0}};
                 if (j + u < c1)
-                    eu = load_plan_ints(plan + kPlanTileInts * (j + u));
+                    eu = plan_entry(plan + kPlanTileInts * (j + u));
                 const int32_t* tu = eu.v;
                 const bool take = n == u && j + u < c1 && tile_ok(tu, p.M, p.n_adapters) && tu[2] == a;
                 row0[u] = take ? tu[0] : t[0];
@@ -269,7 +293,7 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_partial_multi(ShrinkP
                 mask[u] = take ? tile_mask(tu) : 0u;
                 n += take ? 1 : 0;
             }
-            const uint16_t* Aa = p.A_ptrs[a];            // with the rank, not after its test
+            const uint16_t* Aa = adapter_weights(p, a);  // with the rank, not after its test
             const int ra = adapter_rank(p, a);
                 if (ra > 0)
                 shrink_tiles<RT, W, MODE, T>(p, row0, nrows, mask, Aa, ra, 0, s, sgmv_item_scale<MODE>(p, a), red);
@@ -411,7 +435,7 @@ __global__ __launch_bounds__(W * 64, 2) void k_shrink_stream(ShrinkParams p, int
                 u1 = cnt;
             }
             // the weight pointer with the rank, not after the rank test
-            const uint16_t* A = SGMV ? (a < 0 ? nullptr : p.A_ptrs[a]) : p.A;
+            const uint16_t* A = SGMV ? (a < 0 ? nullptr : adapter_weights(p, a)) : p.A;
             const int ra = a < 0 ? 0 : (SGMV ? adapter_rank(p, a) : p.r);
             const int nrt = (ra + 15) / 16 < RT ? (ra + 15) / 16 : RT;
             // the atomic contrast's factor for the run (loaded once per run)
@@ -554,7 +578,7 @@ void k_sgmv_shrink_counted(ShrinkParams p, CounterParams c)
                         c.h[(q.row0 + e / p.r_max) * c.ld_h + e % p.r_max] = 0.0f;
             continue;
         }
-        const uint16_t* Aa = p.A_ptrs[q.a];
+        const uint16_t* Aa = adapter_weights(p, q.a);
         const int ra = adapter_rank(p, q.a);
         const int col0 = q.grp * 16 * RT;
         if (col0 >= ra)
@@ -568,7 +592,7 @@ void k_sgmv_shrink_counted(ShrinkParams p, CounterParams c)
             flag = arrived;
         __syncthreads();
         const bool last = flag == p.split_k - 1;
-        const float scale = last && c.scales ? c.scales[q.a] : 1.0f;
+        const float scale = last && c.scales ? table_load(c.scales, q.a) : 1.0f;
         const int cend = col0 + 16 * RT < ra ? col0 + 16 * RT : ra;
         const int czero = cend == ra ? p.r_max : cend;
         tagged_finish<RT, 4>(p, q.row0, q.nrows, q.mask, col0, cend, czero, q.s, last, scale, own, c.h, c.ld_h);
@@ -601,7 +625,7 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_counted_multi(ShrinkP
         const int c1 = c0 + T < ntiles ? c0 + T : ntiles;
         int j = c0;
         while (j < c1) {                          // uniform: plan data only
-            const PlanInts et = load_plan_ints(plan + kPlanTileInts * j);
+            const PlanInts et = plan_entry(plan + kPlanTileInts * j);
             const int32_t* t = et.v;
             if (!tile_rows_ok(t, p.M)) {
                 ++j;
@@ -626,7 +650,7 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_counted_multi(ShrinkP
             for (int u = 0; u < T; ++u) {
                 PlanInts eu{{0, 0, -1, 0}};
                 if (j + u < c1)
-                    eu = load_plan_ints(plan + kPlanTileInts * (j + u));
+                    eu = plan_entry(plan + kPlanTileInts * (j + u));
                 const int32_t* tu = eu.v;
                 const bool take = n == u && j + u < c1 && tile_ok(tu, p.M, p.n_adapters) && tu[2] == a;
                 row0[u] = take ? tu[0] : t[0];
@@ -639,7 +663,8 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_counted_multi(ShrinkP
                 int arrived = 0;
                 if ((int)threadIdx.x < n)
                     arrived = arrival_add(c.counters + (int64_t)(j + (int)threadIdx.x) * kMaxRankTiles, p.split_k);
-                shrink_tiles<RT, W, kToLds, T>(p, row0, nrows, mask, p.A_ptrs[a], ra, 0, s, 1.0f, red, own);
+                shrink_tiles<RT, W, kToLds, T>(p, row0, nrows, mask, adapter_weights(p, a), ra, 0, s, 1.0f, red,
+                                               own);
                 if ((int)threadIdx.x < n)
                     flag[threadIdx.x] = arrived;
                 __syncthreads();
@@ -647,7 +672,7 @@ __global__ __launch_bounds__(W * 64, 4) void k_sgmv_shrink_counted_multi(ShrinkP
                 for (int u = 0; u < T; ++u) {
                     if (u < n) {                  // uniform
                         const bool last = flag[u] == p.split_k - 1;
-                        const float scale = last && c.scales ? c.scales[a] : 1.0f;
+                        const float scale = last && c.scales ? table_load(c.scales, a) : 1.0f;
                         tagged_finish<RT, 4>(p, row0[u], nrows[u], mask[u], 0, ra < 16 * RT ? ra : 16 * RT, p.r_max,
                                           s, last, scale, own + u * 16 * 16 * RT, c.h, c.ld_h);
                     }
