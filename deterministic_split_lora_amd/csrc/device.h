@@ -496,6 +496,18 @@ __device__ __forceinline__ void hb_from_tile(const ExpandLane& L, const uint16_t
     }
 }
 
+// Tables the kernels only read (plan entries, adapter weight pointers,
+// ranks, scales), at a wave-uniform index, through the constant address
+// space: scalar loads, also in kernels whose own stores keep the compiler from
+// proving the tables unchanged.  It would otherwise use vector loads, whose
+// wait (the vector-memory counter retires in order) also covers every older
+// load or atomic of the wave.
+template <typename T>
+__device__ __forceinline__ T table_load(const T* t, int i)
+{
+    return ((const __attribute__((address_space(4))) T*)t)[i];
+}
+
 // Fixed pairwise tree over N values: v[0]+v[1], v[2]+v[3], ... then the same on
 // the results, level by level; every add is one fp32 rounding.  N is a power
 // of two.  The result is left in v[0].

@@ -415,9 +415,9 @@ template <int KS>
 __device__ __forceinline__ void sgmv_pass(const ExpandParams& p, const ExpandLane& L, const float* hrows,
                                           int64_t ld_hr, int a, const u16x8 (&yv)[2])
 {
-    int ra = p.ranks[a];
+    int ra = table_load(p.ranks, a);
     ra = ra < 0 ? 0 : (ra > p.r_max ? p.r_max : ra);
-    const float scale = p.scales ? p.scales[a] : 1.0f;
+    const float scale = p.scales ? table_load(p.scales, a) : 1.0f;
     const int64_t ld_b = (ra + 7) & ~7;
     u16x8 unused[2];
     ExpandLane Lb = L;
@@ -426,7 +426,7 @@ __device__ __forceinline__ void sgmv_pass(const ExpandParams& p, const ExpandLan
     auto pass = [&](auto steps) {
         constexpr int K2 = decltype(steps)::value;
         bf16x8 bop[4][K2];
-        expand_load<K2>(Lb, p.y, p.ld_y, p.N, p.B_ptrs[a], ld_b, ra, unused, bop);
+        expand_load<K2>(Lb, p.y, p.ld_y, p.N, table_load(p.B_ptrs, a), ld_b, ra, unused, bop);
         expand_finish<K2>(L, p.y, p.ld_y, p.N, hrows, ld_hr, ra, scale, yv, bop);
     };
     const int need = expand_steps(ra);
@@ -596,13 +596,13 @@ __global__ __launch_bounds__(256, KS == 4 ? 2 : 4) void k_sgmv_expand_rows(Expan
                 const uint64_t pending = __ballot(!done);
                 if (pending == 0)
                     break;
-                const int a = __shfl(lid, __builtin_ctzll(pending));    // wave-uniform
+                const int a = __builtin_amdgcn_readfirstlane(__shfl(lid, __builtin_ctzll(pending)));
                 if (a != cur) {
                     cur = a;
-                    ra = p.ranks[a];
+                    ra = table_load(p.ranks, a);
                     ra = ra < 0 ? 0 : (ra > p.r_max ? p.r_max : ra);
-                    scale = p.scales ? p.scales[a] : 1.0f;
-                    expand_load_b<KS>(L, p.N, p.B_ptrs[a], (ra + 7) & ~7, ra, bop);
+                    scale = p.scales ? table_load(p.scales, a) : 1.0f;
+                    expand_load_b<KS>(L, p.N, table_load(p.B_ptrs, a), (ra + 7) & ~7, ra, bop);
                 }
                 const bool mine = !done && lid == a;
                 ExpandLane La = L;
@@ -789,7 +789,7 @@ __global__ __launch_bounds__(256) void k_sgmv_expand(ExpandParams p, TreeParams 
         const uint64_t pending = __ballot(!done);
         if (pending == 0)
             break;
-        const int a = __shfl(id, __builtin_ctzll(pending));     // wave-uniform
+        const int a = __builtin_amdgcn_readfirstlane(__shfl(id, __builtin_ctzll(pending)));
         const bool mine = !done && id == a;
         ExpandLane La = L;
         La.row_ok = mine;

@@ -158,20 +158,9 @@ void k_shrink_counted(ShrinkParams p, CounterParams c, int groups)
 // count and leaves the loop together.  Items of rank groups beyond the tile's
 // adapter rank are skipped.
 // ---------------------------------------------------------------------------
-// The plan and the adapter tables (weight pointers, ranks, scales) are never
-// written by a kernel.  Read through the constant address space, their
-// wave-uniform loads are scalar loads in every kernel; in the single-launch
-// kernels the compiler otherwise cannot prove them unchanged past the
-// kernel's own stores and reads them with vector loads, and its wait for
-// those (the counter retires in order) then also waits for the arrival add
-// issued just before the first operand load.
-template <typename T>
-__device__ __forceinline__ T table_load(const T* t, int i)
-{
-    return ((const __attribute__((address_space(4))) T*)t)[i];
-}
-
-// A plan tile entry (wave-uniform), through the scalar cache.
+// A plan tile entry (wave-uniform) through the scalar cache (table_load): in
+// the single-launch kernels a vector load's wait would also wait for the
+// arrival add issued before the first operand load.
 __device__ __forceinline__ PlanInts plan_entry(const int32_t* e)
 {
     return PlanInts{{table_load(e, 0), table_load(e, 1), table_load(e, 2), table_load(e, 3)}};
