@@ -415,7 +415,11 @@ __device__ __forceinline__ HStageSlot h_stage_slot(int r)
     return s;
 }
 
-// The slot's HC h values (zeros past r and for rows outside the tile) ...
+// The slot's HC h values as stored (zeros for rows outside the tile; the
+// columns from r on are cleared by h_put / h_put_comp).  Nothing here uses
+// the loaded values, so the loads stay in flight until the tile is put into
+// LDS - a prefetch of the next tile is not waited for at once (a wait for it
+// would also wait for every older load of the wave).
 template <int HC>
 __device__ __forceinline__ void h_load(const HStageSlot& s, const float* h, int64_t ld_h, int64_t row0, int nrows,
                                        int r, float (&f)[HC])
@@ -428,36 +432,36 @@ __device__ __forceinline__ void h_load(const HStageSlot& s, const float* h, int6
     const float* hp = h + (row0 + s.row) * ld_h + s.col;
     const float4 v = *reinterpret_cast<const float4*>(hp);
     f[0] = v.x;
-    f[1] = s.col + 1 < r ? v.y : 0.f;
-    f[2] = s.col + 2 < r ? v.z : 0.f;
-    f[3] = s.col + 3 < r ? v.w : 0.f;
+    f[1] = v.y;
+    f[2] = v.z;
+    f[3] = v.w;
     if constexpr (HC == 8) {
         if (s.col + 4 < r) {
             const float4 w = *reinterpret_cast<const float4*>(hp + 4);
             f[4] = w.x;
-            f[5] = s.col + 5 < r ? w.y : 0.f;
-            f[6] = s.col + 6 < r ? w.z : 0.f;
-            f[7] = s.col + 7 < r ? w.w : 0.f;
+            f[5] = w.y;
+            f[6] = w.z;
+            f[7] = w.w;
         }
     }
 }
 
-// ... and their bf16 roundings put into the LDS tile.
+// ... and their bf16 roundings put into the LDS tile, zeros from column r on.
 template <int HC>
-__device__ __forceinline__ void h_put(const HStageSlot& s, const float (&f)[HC], uint16_t* tile)
+__device__ __forceinline__ void h_put(const HStageSlot& s, const float (&f)[HC], int r, uint16_t* tile)
 {
     if (!s.on)
         return;
     uint16_t* d = tile + s.row * kHbStride + s.col;
 #pragma unroll
     for (int e = 0; e < HC; ++e)
-        d[e] = f32_to_bf16_bits(f[e]);
+        d[e] = f32_to_bf16_bits(s.col + e < r ? f[e] : 0.f);
 }
 
 // ... or, for the compensated expand, the hi and lo halves of each value put
 // into two LDS tiles.
 template <int HC>
-__device__ __forceinline__ void h_put_comp(const HStageSlot& s, const float (&f)[HC], uint16_t* hi_tile,
+__device__ __forceinline__ void h_put_comp(const HStageSlot& s, const float (&f)[HC], int r, uint16_t* hi_tile,
                                            uint16_t* lo_tile)
 {
     if (!s.on)
@@ -467,7 +471,7 @@ __device__ __forceinline__ void h_put_comp(const HStageSlot& s, const float (&f)
 #pragma unroll
     for (int e = 0; e < HC; ++e) {
         uint16_t vh, vl;
-        split_hi_lo(f[e], vh, vl);
+        split_hi_lo(s.col + e < r ? f[e] : 0.f, vh, vl);
         dh[e] = vh;
         dl[e] = vl;
     }

@@ -197,7 +197,7 @@ __global__ __launch_bounds__(256) void k_expand_rows(ExpandParams p, int R)
     y_chunk_load(yc, p.y, p.ld_y, row_base, col0, ok, g);
     h_load(slot, p.h, p.ld_h, row_base, nr, p.r, f);
     y_chunk_put(yc, g, ys[0]);
-    h_put(slot, f, hs[0]);
+    h_put(slot, f, p.r, hs[0]);
     __syncthreads();
     for (int i = 0; i < tiles; ++i) {
         const int64_t row0 = row_base + (int64_t)kRowBlock * i;
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256) void k_expand_rows(ExpandParams p, int R)
         }
         if (next) {
             y_chunk_put(yc, g, ys[(i + 1) & 1]);
-            h_put(slot, f, hs[(i + 1) & 1]);
+            h_put(slot, f, p.r, hs[(i + 1) & 1]);
         }
         __syncthreads();
         if (next) {
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(256) void k_expand_comp_rows(ExpandParams p, int R)
     y_chunk_load(yc, p.y, p.ld_y, row_base, col0, ok, g);
     h_load(slot, p.h, p.ld_h, row_base, nr, p.r, f);
     y_chunk_put(yc, g, ys[0]);
-    h_put_comp(slot, f, hs[0], hl[0]);
+    h_put_comp(slot, f, p.r, hs[0], hl[0]);
     __syncthreads();
     for (int i = 0; i < tiles; ++i) {
         const int64_t row0 = row_base + (int64_t)kRowBlock * i;
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(256) void k_expand_comp_rows(ExpandParams p, int R)
         }
         if (next) {
             y_chunk_put(yc, g, ys[(i + 1) & 1]);
-            h_put_comp(slot, f, hs[(i + 1) & 1], hl[(i + 1) & 1]);
+            h_put_comp(slot, f, p.r, hs[(i + 1) & 1], hl[(i + 1) & 1]);
         }
         __syncthreads();
         if (next) {
@@ -563,7 +563,7 @@ __global__ __launch_bounds__(256, KS == 4 ? 2 : 4) void k_sgmv_expand_rows(Expan
         if constexpr (COMBINE)
             h_tree(slot, c, r0, nrows, p.r_max, split_k, write_h, f);
         y_chunk_put(yc, g, ys[b]);
-        h_put(slot, f, hs[b]);
+        h_put(slot, f, p.r_max, hs[b]);
         return (unsigned)valid(ca[0]) | (unsigned)valid(ca[1]) << 1;
     };
     int id;
