@@ -390,6 +390,11 @@ size_t lora_sgmv_plan_bytes(int64_t M);
  * output bit.  One launch of one workgroup.  The plan buffer (16-byte
  * aligned) is opaque; it stays valid for later sgmv calls with the same ids,
  * M and n_adapters and may be reused by both sgmv_shrink and sgmv_expand.
+ * Its header records M and n_adapters. A multi-adapter shrink given a plan
+ * made for other values processes no tile, so none of the stale entries is
+ * followed. Its h is then not computed: the single launch leaves h as it
+ * was, and the two-pass shrink's second pass reads whatever the workspace
+ * holds.
  */
 int lora_sgmv_plan(const int32_t* token_adapter, int64_t M, int32_t n_adapters,
                    void* plan, size_t plan_bytes, void* stream);

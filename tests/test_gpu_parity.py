@@ -1276,6 +1276,41 @@ def test_sgmv_counted_bitwise(case):
                      dsl.lora_shrink_plan(c.K, r, c.split_k), f"{case} row {i}")
 
 
+def test_sgmv_plan_of_other_batch_processes_nothing():
+    """A plan used with another M or n_adapters than it was built for is
+    recognised by its header, and the multi-adapter shrinks then process no
+    tile, so none of its entries (which may point past the batch) is
+    followed. The single launch leaves h, its tagged workspace and its
+    counters as they were. The two-pass shrink's partial kernel leaves its
+    workspace untouched."""
+    t = torch()
+    c = sgmv_case(64, 2048, 64, [16, 32, 16], 0, 0, 8, seed=9, tag="pl",
+                  ids=(np.arange(64) % 3).astype(np.int32))
+    n = len(c.ranks)
+    As = [bf16_to_gpu(a) for a in c.As]
+    Ap = t.tensor([a.data_ptr() for a in As], dtype=t.int64, device="cuda")
+    ranks = t.from_numpy(c.ranks).cuda()
+    scales = t.from_numpy(c.scales).cuda()
+    xg = bf16_to_gpu(c.x)
+    _, plan = _build_plan(c.ids, n)                     # built for M = 64, n_adapters = 3
+    m = 16
+    for n_used, what in ((n, "other M"), (n - 1, "other n_adapters and M")):
+        h = t.full((m, c.r_max), 7.0, dtype=t.float32, device="cuda")
+        cws = counted_workspace(m, c.r_max, c.split_k)
+        cnt = t.zeros(dsl.lora_sgmv_counter_bytes(m) // 4, dtype=t.int32, device="cuda")
+        dsl.lora_sgmv_shrink_counted(xg[:m], Ap, c.K, ranks, scales, n_used, plan, h, c.r_max, c.split_k, cws, cnt)
+        t.cuda.synchronize()
+        assert bool((h == 7.0).all()), what
+        assert int(cnt.abs().sum()) == 0, what
+        assert int(cws.count_nonzero()) == 0, what
+    ws = t.full((dsl.lora_sgmv_workspace_bytes(m, c.r_max, c.split_k),), 0x5A, dtype=t.uint8, device="cuda")
+    idg = t.from_numpy(np.ascontiguousarray(c.ids[:m])).cuda()
+    h = t.zeros((m, c.r_max), dtype=t.float32, device="cuda")
+    dsl.lora_sgmv_shrink(xg[:m], Ap, c.K, ranks, scales, idg, n, plan, h, c.r_max, c.split_k, ws)
+    t.cuda.synchronize()
+    assert bool((ws == 0x5A).all())
+
+
 def test_counted_shrinks_stress_repeats():
     """Back-to-back launches of the single-launch shrinks (single adapter and
     32 one-token adapters of rank 64), each compared bit for bit on the GPU
